@@ -57,6 +57,7 @@ def quantize(w):
     """Quantize a float32 array (any shape; flattened row-major).
 
     Returns (codes uint8 [ceil(n/2)], absmax float32 [ceil(n/64)]).
+    Blocks are processed in batches, each element exactly as stated above.
     """
     w = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
     if not np.all(np.isfinite(w)):
@@ -64,19 +65,23 @@ def quantize(w):
     n = w.size
     nblocks = (n + BLOCK - 1) // BLOCK
     mids = midpoints()
-    codes = np.empty(n, dtype=np.uint8)
-    absmax = np.empty(nblocks, dtype=np.float32)
-    for b in range(nblocks):
-        blk = w[b * BLOCK:(b + 1) * BLOCK]
-        a = np.float32(np.max(np.abs(blk)))
-        absmax[b] = a
-        if a == 0:
-            codes[b * BLOCK:(b + 1) * BLOCK] = 7
-            continue
-        x = (blk / a).astype(np.float32)          # float32 / float32 -> float32
-        # code = how many thresholds lie strictly below x
-        codes[b * BLOCK:(b + 1) * BLOCK] = (x[:, None] > mids[None, :]).sum(axis=1)
-    return pack(codes), absmax
+    padded = np.zeros(nblocks * BLOCK, np.float32)
+    padded[:n] = w
+    blocks = padded.reshape(nblocks, BLOCK)
+    absmax = np.max(np.abs(blocks), axis=1).astype(np.float32)
+    codes = np.empty((nblocks, BLOCK), dtype=np.uint8)
+    step = 8192
+    for b0 in range(0, nblocks, step):
+        blk = blocks[b0:b0 + step]
+        a = absmax[b0:b0 + step]
+        safe = np.where(a == 0, np.float32(1), a)
+        x = (blk / safe[:, None]).astype(np.float32)      # float32 / float32
+        c = np.zeros(blk.shape, dtype=np.uint8)
+        for m in mids:                                     # count thresholds below x
+            c += (x > m)
+        c[a == 0] = 7                                      # all-zero block: exact zero
+        codes[b0:b0 + step] = c
+    return pack(codes.reshape(-1)[:n]), absmax
 
 
 def pack(codes):
