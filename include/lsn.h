@@ -1,0 +1,246 @@
+/*
+ * liblsn -- layer-streamed LoRA training over a frozen NF4 decoder base on one
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes, no C++ or
+ * framework types.
+ *
+ * The method (web pages on the "Soup" fine-tuning CLI):
+ *   - "Soup: Fine-Tune an 8B Model on a 4 GB GPU" (lucaberton.com), section
+ *     "The Core Idea: Layer Streaming": the frozen base stays in CPU RAM or on
+ *     NVMe; on a dedicated stream one decoder layer at a time is copied into
+ *     VRAM as forward or backward needs it; peak VRAM is one layer plus the
+ *     adapter; the streamed base may be NF4; only the LoRA adapter trains; for
+ *     DPO the reference model is the same base with adapters disabled.
+ *   - "Show HN: Fine-tune an 8B model on a 4 GB laptop GPU" (elseif.net),
+ *     first paragraph: policy log-probs with the adapter on, reference
+ *     log-probs with it off, from the same streamed base; results bit-exact
+ *     against a non-streamed run.
+ *   - axbrief.com article, "Beyond Memory: The Layer Streaming Breakthrough":
+ *     streamed results are bit-exact with resident execution.
+ *
+ * Conventions
+ *   - Every call returns lsn_status; nothing throws across the ABI.
+ *   - "device pointer" = memory on the context's GPU (the caller allocates it,
+ *     e.g. with PyTorch); "host pointer" = ordinary CPU memory, copied before
+ *     the call returns and never retained.
+ *   - All device work is enqueued on the context's compute stream and the
+ *     call returns before it completes.  The library's own copy stream is
+ *     ordered against it only through events.  lsn_sync() waits and reports
+ *     asynchronous HIP errors.
+ *   - The library never allocates device memory: lsn_create carves every
+ *     device buffer out of ONE caller-owned workspace of lsn_workspace_bytes().
+ *     It owns the pinned host copy of the frozen base (hipHostMalloc) and any
+ *     file handle.
+ *   - Argument errors return LSN_ERR_INVALID with nothing enqueued.  A HIP
+ *     failure returns LSN_ERR_HIP and poisons the context: later calls return
+ *     LSN_ERR_STATE.  lsn_last_error() gives a message.
+ *   - Weights are stored as W^T = [out, in] row-major (the causal-LM layout),
+ *     so a projection is y = x W = x (W^T)^T with x [T, in], y [T, out].
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - A context is not thread-safe; use one per device and per thread.
+ */
+#ifndef LSN_H
+#define LSN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lsn_ctx lsn_ctx;
+
+typedef enum {
+  LSN_OK = 0,
+  LSN_ERR_INVALID = 1, /* bad argument; nothing enqueued */
+  LSN_ERR_NOFIT = 2,   /* workspace (or the configured budget) too small */
+  LSN_ERR_HIP = 3,     /* HIP runtime failure; context poisoned */
+  LSN_ERR_IO = 4,      /* file source read failure; context poisoned */
+  LSN_ERR_STATE = 5    /* call out of order, or context poisoned */
+} lsn_status;
+
+/* where the frozen base lives during training */
+enum { LSN_RESIDENT = 0, LSN_STREAM_HOST = 1, LSN_STREAM_FILE = 2 };
+/* pass kinds: forward visits layers 0..L-1, backward L-1..0 */
+enum { LSN_PASS_FWD = 0, LSN_PASS_BWD = 1 };
+/* projections of a decoder layer, in record order */
+enum { LSN_Q = 0, LSN_K = 1, LSN_V = 2, LSN_O = 3, LSN_GATE = 4, LSN_UP = 5, LSN_DOWN = 6 };
+
+typedef struct {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  int32_t tied_embeddings; /* 1: the LM head is the embedding table */
+  float rms_eps, rope_theta;
+  int32_t lora_rank;       /* 1..16 */
+  float lora_alpha;        /* LoRA scale s = alpha / rank */
+  uint32_t lora_targets;   /* bit p set = projection p carries an adapter */
+  int32_t max_tokens;      /* upper bound of n_seq * seq_len per pass */
+  int32_t max_seq_len;     /* upper bound of seq_len */
+  int32_t mode;            /* LSN_RESIDENT | LSN_STREAM_HOST | LSN_STREAM_FILE */
+  const char* store_path;  /* LSN_STREAM_FILE: file that holds the layer records */
+  uint64_t vram_budget;    /* 0 = none; else lsn_create refuses a larger workspace */
+} lsn_config;
+
+/* ---------------------------------------------------------------------------
+ * NF4 host codec (no context).  The pages name the format only ("Soup:
+ * Fine-Tune an 8B Model on a 4 GB GPU", "The Core Idea: Layer Streaming":
+ * the streamed base optionally quantized to NF4, about four times smaller).
+ * Format used: 16 normal-quantile levels with an exact zero, scaled to
+ * [-1, 1]; blocks of 64 consecutive elements of the flattened W^T, one fp32
+ * absmax per block; code = number of fp32 midpoints strictly below
+ * fl32(w / absmax); an all-zero block stores absmax 0 and code 7; two codes
+ * per byte, even element in the low nibble (odd n pads a zero nibble).
+ * ------------------------------------------------------------------------- */
+/* out16: host, 16 floats, ascending (-1 .. 1, entry 7 is 0). */
+lsn_status lsn_nf4_codebook(float* out16);
+/* w: host [n] fp32 (finite, else LSN_ERR_INVALID); codes: host [(n+1)/2];
+ * absmax: host [(n+63)/64].  Multithreaded; deterministic. */
+lsn_status lsn_nf4_quantize(const float* w, uint64_t n, uint8_t* codes, float* absmax);
+/* host inverse: w[e] = fl32(level[code_e] * absmax[e/64]). */
+lsn_status lsn_nf4_dequantize_host(const uint8_t* codes, const float* absmax, uint64_t n, float* w);
+
+/* ---------------------------------------------------------------------------
+ * Device NF4 dequantization (all pointers device).  out_bf16 = 0: fp32
+ * output fl32(level * absmax), bit-equal to the host codec; 1: that value
+ * rounded to bf16 (what the GEMMs feed the matrix cores).  n % 8 == 0.
+ * ------------------------------------------------------------------------- */
+lsn_status lsn_nf4_dequant(const uint8_t* codes, const float* absmax, uint64_t n, void* out,
+                           int32_t out_bf16, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Single NF4 projection with a LoRA branch, stateless (the frozen linear of
+ * "only the adapter trains", page "Soup: Fine-Tune an 8B Model on a 4 GB GPU",
+ * "The Core Idea: Layer Streaming"; formula y = x W + s (x A) B).
+ * All pointers device.  W^T codes [N*K/2] + absmax [N*K/64] as the codec
+ * writes them; X bf16 [M, K]; A fp32 [K, r]; B fp32 [r, N] (A = B = NULL or
+ * r = 0: no adapter); Y fp32 [M, N].  K % 16 == 0, N % 8 == 0, r <= 16.
+ * scratch: device, >= lsn_nf4_linear_scratch_bytes().
+ * bwd: dY bf16 [M, N] -> dX fp32 [M, K] (overwritten), dA fp32 [K, r] and
+ * dB fp32 [r, N] (overwritten; may be NULL when r = 0).  The base gets no
+ * gradient.
+ * ------------------------------------------------------------------------- */
+lsn_status lsn_nf4_linear_scratch_bytes(int32_t M, int32_t K, int32_t N, int32_t r,
+                                        uint64_t* bytes);
+lsn_status lsn_nf4_linear_fwd(const uint8_t* codes, const float* absmax, int32_t M, int32_t K,
+                              int32_t N, const uint16_t* X, const float* A, const float* B,
+                              int32_t r, float s, float* Y, void* scratch, uint64_t scratch_bytes,
+                              void* hip_stream);
+lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t M, int32_t K,
+                              int32_t N, const uint16_t* X, const float* A, const float* B,
+                              int32_t r, float s, const uint16_t* dY, float* dX, float* dA,
+                              float* dB, void* scratch, uint64_t scratch_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Context lifecycle.
+ * ------------------------------------------------------------------------- */
+/* Device bytes the context needs for cfg (records or slots, head tables,
+ * adapters and gradients, one layer's activations at max_tokens). */
+lsn_status lsn_workspace_bytes(const lsn_config* cfg, uint64_t* bytes);
+/* dev_ws: device, ws_bytes >= lsn_workspace_bytes (else LSN_ERR_NOFIT, the
+ * pre-flight refusal of a run that will not fit: page "Soup: Fine-Tune an 8B
+ * Model on a 4 GB GPU", "A Practical Quick Start").  hip_stream: the compute
+ * stream (hipStream_t, may be 0).  The workspace stays owned by the caller and
+ * must outlive the context. */
+lsn_status lsn_create(const lsn_config* cfg, void* dev_ws, uint64_t ws_bytes, void* hip_stream,
+                      lsn_ctx** out);
+void lsn_destroy(lsn_ctx* ctx);
+const char* lsn_last_error(const lsn_ctx* ctx);
+lsn_status lsn_sync(lsn_ctx* ctx);
+/* bytes of one layer record (NF4 codes + absmax + norm gains), 4 KiB aligned */
+lsn_status lsn_record_bytes(const lsn_ctx* ctx, uint64_t* bytes);
+
+/* ---------------------------------------------------------------------------
+ * Frozen base (page "Soup: Fine-Tune an 8B Model on a 4 GB GPU", "The Core
+ * Idea: Layer Streaming": the frozen base is kept in CPU RAM or on NVMe).
+ * Host pointers; copied into the library's pinned store (and, in
+ * LSN_RESIDENT mode, into the device record).  codes[p]/absmax[p] as
+ * lsn_nf4_quantize writes them for W_p^T; norms bf16 [hidden].
+ * LSN_STREAM_FILE: the record is written to store_path at its offset.
+ * ------------------------------------------------------------------------- */
+lsn_status lsn_load_layer_nf4(lsn_ctx* ctx, int32_t layer, const uint8_t* const* codes,
+                              const float* const* absmax, const uint16_t* attn_norm_bf16,
+                              const uint16_t* mlp_norm_bf16);
+/* embed, lm_head: host bf16 [vocab, hidden] (lm_head NULL when tied);
+ * final_norm: host bf16 [hidden].  Kept resident on the device. */
+lsn_status lsn_load_head(lsn_ctx* ctx, const uint16_t* embed_bf16, const uint16_t* lm_head_bf16,
+                         const uint16_t* final_norm_bf16);
+
+/* ---------------------------------------------------------------------------
+ * Adapters: fp32 masters and gradients live in the workspace.  Host pointers.
+ * A [K, r], B [r, N] of projection proj of layer; proj must be a target.
+ * ------------------------------------------------------------------------- */
+lsn_status lsn_set_lora(lsn_ctx* ctx, int32_t layer, int32_t proj, const float* A, const float* B);
+/* any output may be NULL */
+lsn_status lsn_get_lora(lsn_ctx* ctx, int32_t layer, int32_t proj, float* A, float* B, float* dA,
+                        float* dB);
+/* 0: forward skips every low-rank branch (the DPO reference model, page
+ * "Show HN: Fine-tune an 8B model on a 4 GB laptop GPU", first paragraph);
+ * 1: branches on.  Backward requires 1. */
+lsn_status lsn_set_adapter_enabled(lsn_ctx* ctx, int32_t enabled);
+lsn_status lsn_zero_grads(lsn_ctx* ctx);
+/* theta -= lr * grad for every adapter matrix (plain SGD). */
+lsn_status lsn_sgd_step(lsn_ctx* ctx, float lr);
+
+/* ---------------------------------------------------------------------------
+ * A pass over the stack.  begin_pass fixes the layer order (FWD 0..L-1, BWD
+ * L-1..0) and, when streaming, starts copying the first two layer records
+ * into the two device slots on the copy stream.  Each forward_layer /
+ * backward_layer must name the next layer of the pass (else LSN_ERR_STATE);
+ * it waits for its record, runs, frees the slot and queues the copy of the
+ * layer two ahead.  A record already in a slot is reused, not copied again.
+ * n_seq sequences of seq_len tokens each, back to back (T = n_seq*seq_len).
+ * ------------------------------------------------------------------------- */
+lsn_status lsn_begin_pass(lsn_ctx* ctx, int32_t kind, int32_t n_seq, int32_t seq_len);
+/* tokens: device int32 [T]; h0: device fp32 [T, hidden] = embedding rows. */
+lsn_status lsn_embed(lsn_ctx* ctx, const int32_t* tokens, float* h0);
+/* h_in, h_out: device fp32 [T, hidden] (may alias).  One decoder layer:
+ * RMSNorm, q/k/v (+LoRA), RoPE, causal GQA attention, o (+LoRA) + residual,
+ * RMSNorm, SwiGLU MLP (+LoRA) + residual. */
+lsn_status lsn_forward_layer(lsn_ctx* ctx, int32_t layer, const float* h_in, float* h_out);
+/* Recomputes the layer from its saved input, then back-propagates:
+ * dh_in = d loss / d h_in (may alias dh_out), and adds the adapter
+ * gradients of this layer into the context's gradient buffers.  The base
+ * gets no gradient (page "Soup: ...", "The Core Idea: Layer Streaming": the
+ * backward re-reads each layer). */
+lsn_status lsn_backward_layer(lsn_ctx* ctx, int32_t layer, const float* h_in_saved,
+                              const float* dh_out, float* dh_in);
+
+/* ---------------------------------------------------------------------------
+ * LM head.  h: device fp32 [T, hidden]; targets: device int32 [T] (a negative
+ * target gives logp 0); logp: device fp32 [T] = log softmax(RMSNorm(h) W_lm^T)
+ * at the target, over the vocabulary in chunks (online max / sum).
+ * lm_head_backward must follow the lm_head_logprobs call on the same h:
+ * dh (device fp32 [T, hidden], overwritten) from dlogp (device fp32 [T]).
+ * ------------------------------------------------------------------------- */
+lsn_status lsn_lm_head_logprobs(lsn_ctx* ctx, const float* h, const int32_t* targets, float* logp);
+lsn_status lsn_lm_head_backward(lsn_ctx* ctx, const float* h, const int32_t* targets,
+                                const float* dlogp, float* dh);
+
+/* ---------------------------------------------------------------------------
+ * Losses (device pointers).
+ * SFT: loss[0] = -mean of logp over positions with target >= 0;
+ *      dlogp = -1/count there, 0 elsewhere.
+ * DPO on one pair laid out as two sequences (chosen, rejected) of seq_len:
+ *      pc, pr (policy) and rc, rr (reference) = sums of logp over response
+ *      targets (positions prompt_len-1 .. seq_len-2 of each sequence);
+ *      z = beta((pc - rc) - (pr - rr)); out[0] = -log sigmoid(z), out[1] = z,
+ *      out[2..5] = pc, pr, rc, rr; dlogp_pol = -+ beta sigmoid(-z) on the
+ *      chosen / rejected response positions, 0 elsewhere.  The reference
+ *      log-probs come from the same base with the adapter off (page "Show HN:
+ *      Fine-tune an 8B model on a 4 GB laptop GPU", first paragraph).
+ * ------------------------------------------------------------------------- */
+lsn_status lsn_sft_loss(lsn_ctx* ctx, const float* logp, const int32_t* targets, int32_t n,
+                        float* loss, float* dlogp);
+lsn_status lsn_dpo_loss(lsn_ctx* ctx, const float* logp_pol, const float* logp_ref,
+                        int32_t seq_len, int32_t prompt_len, float beta, float* out6,
+                        float* dlogp_pol);
+
+/* Counters since lsn_create: layer records copied host->device, bytes copied
+ * host->device by the scheduler, and workspace bytes carved.  Any may be NULL. */
+lsn_status lsn_stats(const lsn_ctx* ctx, uint64_t* layer_loads, uint64_t* bytes_h2d,
+                     uint64_t* ws_bytes);
+/* The copy stream (hipStream_t) the scheduler uses, for timing its copies. */
+lsn_status lsn_copy_stream(const lsn_ctx* ctx, void** hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSN_H */

@@ -1,0 +1,45 @@
+// Internal interface of the MFMA GEMM (see gemm.hip for the operand forms).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lsn {
+
+enum { A_BF16_K = 0, A_BF16_R = 1, A_F32_K = 2 };
+enum { B_BF16_K = 0, B_BF16_R = 1, B_NF4_K = 2, B_NF4_R = 3 };
+enum { C_F32 = 0, C_F32_ACC = 1, C_F32_RES = 2, C_BF16 = 3 };
+
+struct GemmParams {
+  int M = 0, N = 0, K = 0;
+  const void* A = nullptr;
+  int64_t lda = 0;
+  const void* B = nullptr;  // bf16 matrix, or NF4 codes of W^T [rows, rowlen]
+  int64_t ldb = 0;
+  const float* absmax = nullptr;  // NF4 only: one float per 64 elements of W^T
+  int64_t rowlen = 0;             // NF4 only: row length of W^T
+  // batch index z = blockIdx.z split as (z / zdiv, z % zdiv); B uses the inner
+  // index divided by grpB (grouped key/value heads)
+  int zdiv = 1, grpB = 1;
+  int64_t sA_o = 0, sA_i = 0, sB_o = 0, sB_i = 0, sC_o = 0, sC_i = 0;
+  // the reduction runs over nseg segments of K each; segment s shifts A and B
+  int nseg = 1;
+  int64_t sA_seg = 0, sB_seg = 0;
+  // low-rank extension (bf16, k-contiguous, kext a multiple of 16)
+  const uint16_t* Aext = nullptr;
+  int64_t ldae = 0;
+  const uint16_t* Bext = nullptr;
+  int64_t ldbe = 0;
+  int kext = 0;
+  // output
+  void* C = nullptr;
+  int64_t ldc = 0;
+  const float* R = nullptr;  // residual for C_F32_RES
+  int64_t ldr = 0;
+  float alpha = 1.f;
+  int cmode = C_F32;
+  float levels[16] = {};  // NF4 code levels
+};
+
+hipError_t gemm(const GemmParams& p, int opa, int opb, int batch, hipStream_t s);
+
+}  // namespace lsn

@@ -1,0 +1,434 @@
+// bf16 MFMA GEMM for gfx950 with on-the-fly NF4 dequantization.
+//
+//   C[m, n] (op)= alpha * sum_k A(m, k) * B(n, k)   (+ LoRA extension, below)
+//
+// Both operands reach the matrix cores as bf16 with fp32 accumulation
+// (v_mfma_f32_32x32x16_bf16).  Each operand comes through a loader that
+// stages a 64-deep K slice into LDS, always k-contiguous per row, so the
+// fragment reads are 16-byte ds_read_b128:
+//   A_BF16_K  A(m,k) = A[m*lda + k]            (bf16, rows k-contiguous)
+//   A_BF16_R  A(m,k) = A[k*lda + m]            (bf16, transposed storage)
+//   A_F32_K   A(m,k) = bf16(A[m*lda + k])      (fp32 source rounded on load)
+//   B_BF16_K  B(n,k) = B[n*ldb + k]
+//   B_BF16_R  B(n,k) = B[k*ldb + n]
+//   B_NF4_K   B(n,k) = bf16(level[code(e)] * absmax[e/64]),  e = n*rowlen + k
+//   B_NF4_R   B(n,k) = same with e = k*rowlen + n   (transposed use, dX = dY W)
+// NF4 codes are packed two per byte, even element in the low nibble; the
+// dequantized value is the float32 product rounded once to bf16.
+//
+// The stored weight is W^T = [out, in] row-major, so the forward projection
+// y = x W is (A_BF16_K, B_NF4_K) and the input gradient dx = dy W^T is
+// (A_*_K, B_NF4_R).
+//
+// LoRA extension: with kext > 0 the reduction continues over kext extra
+// columns taken straight from two bf16 matrices Aext [M, kext] and
+// Bext [N, kext].  With Aext = bf16(s * x A) and Bext = B^T this adds
+// s (x A) B inside the same accumulators (the low-rank branch of the
+// adapted projection); several adapted projections that share one GEMM use a
+// block layout (each projection's rows of Bext are zero outside its slot).
+//
+// Determinism: every output element is reduced by one lane in a fixed order,
+// so results do not depend on scheduling, and they do not depend on where the
+// weights live (a streamed slot or a resident record): the kernel only sees
+// byte offsets inside the record.
+#include "common.h"
+#include "gemm.h"
+#include <type_traits>
+
+namespace lsn {
+
+constexpr int BK = 64;        // K depth staged per iteration
+constexpr int PITCH = 72;     // LDS row pitch in bf16 (64 + 8 pad: conflict-free b128 reads)
+constexpr int NTHREADS = 256; // 4 waves, arranged 2 x 2 over the tile
+
+// ---------------------------------------------------------------------------
+// NF4 dequantization of one 32-bit code word (8 elements) to 4 packed bf16x2
+// ---------------------------------------------------------------------------
+LSN_DEV u32x4 nf4_dequant8(uint32_t w, float a, const float* lv) {
+  u32x4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float lo = lv[(w >> (8 * p)) & 15u] * a;
+    const float hi = lv[(w >> (8 * p + 4)) & 15u] * a;
+    r[p] = pack_bf16x2(lo, hi);
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// operand loaders: prefetch(kt) issues global loads into registers,
+// store(lds) converts and writes the 64-deep slice to LDS as [row][k].
+// ---------------------------------------------------------------------------
+template <int ROWS>
+struct LoadBf16K {  // rows k-contiguous bf16
+  static constexpr int CH = ROWS * 8 / NTHREADS;  // 16-byte chunks per thread
+  u32x4 v[CH];
+  LSN_DEV void prefetch(const uint16_t* base, int64_t ld, int row0, int nrows, int k0, int K) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = threadIdx.x + i * NTHREADS;
+      const int r = c >> 3, kc = (c & 7) * 8;
+      const int row = row0 + r, k = k0 + kc;
+      if (row < nrows && k < K)
+        v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)row * ld + k);
+      else
+        v[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+  LSN_DEV void store(uint16_t* lds) const {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = threadIdx.x + i * NTHREADS;
+      *reinterpret_cast<u32x4*>(lds + (c >> 3) * PITCH + (c & 7) * 8) = v[i];
+    }
+  }
+};
+
+template <int ROWS>
+struct LoadF32K {  // fp32 rows, rounded to bf16 on the way to LDS
+  static constexpr int CH = ROWS * 8 / NTHREADS;
+  f32x4 v[CH][2];
+  LSN_DEV void prefetch(const float* base, int64_t ld, int row0, int nrows, int k0, int K) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = threadIdx.x + i * NTHREADS;
+      const int r = c >> 3, kc = (c & 7) * 8;
+      const int row = row0 + r, k = k0 + kc;
+      if (row < nrows && k < K) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(base + (int64_t)row * ld + k);
+        v[i][0] = p[0];
+        v[i][1] = p[1];
+      } else {
+        v[i][0] = f32x4{0, 0, 0, 0};
+        v[i][1] = f32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  LSN_DEV void store(uint16_t* lds) const {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = threadIdx.x + i * NTHREADS;
+      u32x4 o;
+      o[0] = pack_bf16x2(v[i][0][0], v[i][0][1]);
+      o[1] = pack_bf16x2(v[i][0][2], v[i][0][3]);
+      o[2] = pack_bf16x2(v[i][1][0], v[i][1][1]);
+      o[3] = pack_bf16x2(v[i][1][2], v[i][1][3]);
+      *reinterpret_cast<u32x4*>(lds + (c >> 3) * PITCH + (c & 7) * 8) = o;
+    }
+  }
+};
+
+template <int ROWS>
+struct LoadBf16R {  // element (row, k) at base[k*ld + row]; 8x8 register transpose
+  static_assert(ROWS <= NTHREADS, "one 8x8 task per thread at most");
+  u32x4 v[8];
+  bool active;
+  LSN_DEV void prefetch(const uint16_t* base, int64_t ld, int row0, int nrows, int k0, int K) {
+    const int t = threadIdx.x;
+    active = t < ROWS;  // ROWS/8 row groups x 8 k groups
+    if (!active) return;
+    const int rg = t >> 3, kg = t & 7;
+    const int row = row0 + rg * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = k0 + kg * 8 + i;
+      if (row < nrows && k < K)
+        v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)k * ld + row);
+      else
+        v[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+  LSN_DEV void store(uint16_t* lds) const {
+    if (!active) return;
+    const int t = threadIdx.x;
+    const int rg = t >> 3, kg = t & 7;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // output row rg*8 + j holds k = kg*8 .. +7
+      u32x4 o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t x = v[2 * p][j >> 1], y = v[2 * p + 1][j >> 1];
+        o[p] = (j & 1) ? __builtin_amdgcn_perm(y, x, 0x07060302u)
+                       : __builtin_amdgcn_perm(y, x, 0x05040100u);
+      }
+      *reinterpret_cast<u32x4*>(lds + (rg * 8 + j) * PITCH + kg * 8) = o;
+    }
+  }
+};
+
+template <int ROWS>
+struct LoadNf4K {  // B(n,k) from W^T[n, k] (forward); one code word = 8 k
+  static constexpr int CH = ROWS * 8 / NTHREADS;
+  uint32_t code[CH];
+  float amax[CH];
+  LSN_DEV void prefetch(const uint8_t* codes, const float* absmax, int64_t rowlen, int row0,
+                        int nrows, int k0, int K) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = threadIdx.x + i * NTHREADS;
+      const int r = c >> 3, kc = (c & 7) * 8;
+      const int row = row0 + r, k = k0 + kc;
+      if (row < nrows && k < K) {
+        const int64_t e = (int64_t)row * rowlen + k;
+        code[i] = *reinterpret_cast<const uint32_t*>(codes + (e >> 1));
+        amax[i] = absmax[e >> 6];
+      } else {
+        code[i] = 0x77777777u;  // level 7 is exactly 0
+        amax[i] = 0.f;
+      }
+    }
+  }
+  LSN_DEV void store(uint16_t* lds, const float* lv) const {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = threadIdx.x + i * NTHREADS;
+      *reinterpret_cast<u32x4*>(lds + (c >> 3) * PITCH + (c & 7) * 8) =
+          nf4_dequant8(code[i], amax[i], lv);
+    }
+  }
+};
+
+template <int ROWS>
+struct LoadNf4R {  // B(n,k) from W^T[k, n] (input gradient); task = 4 k x 8 n
+  static constexpr int TASKS = ROWS * 2;  // 16 k-groups x ROWS/8 n-groups
+  static_assert(TASKS <= NTHREADS, "one task per thread at most");
+  uint32_t code[4];
+  float amax[4];
+  bool active;
+  LSN_DEV void prefetch(const uint8_t* codes, const float* absmax, int64_t rowlen, int row0,
+                        int nrows, int k0, int K) {
+    const int t = threadIdx.x;
+    active = t < TASKS;
+    if (!active) return;
+    const int ng = t % (ROWS / 8), kg = t / (ROWS / 8);
+    const int n = row0 + ng * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = k0 + kg * 4 + i;
+      if (n < nrows && k < K) {
+        const int64_t e = (int64_t)k * rowlen + n;
+        code[i] = *reinterpret_cast<const uint32_t*>(codes + (e >> 1));
+        amax[i] = absmax[e >> 6];
+      } else {
+        code[i] = 0x77777777u;
+        amax[i] = 0.f;
+      }
+    }
+  }
+  LSN_DEV void store(uint16_t* lds, const float* lv) const {
+    if (!active) return;
+    const int t = threadIdx.x;
+    const int ng = t % (ROWS / 8), kg = t / (ROWS / 8);
+    float w[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[i][j] = lv[(code[i] >> (4 * j)) & 15u] * amax[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // LDS row n = ng*8 + j, k = kg*4 .. +3
+      u32x2 o;
+      o[0] = pack_bf16x2(w[0][j], w[1][j]);
+      o[1] = pack_bf16x2(w[2][j], w[3][j]);
+      *reinterpret_cast<u32x2*>(lds + (ng * 8 + j) * PITCH + kg * 4) = o;
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// kernel
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int OPA, int OPB>
+__global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
+  constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM >= 1 && TN >= 1, "tile too small");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * PITCH];
+  __shared__ float sLv[16];
+
+  // ---- tile coordinates (XCD-aware: consecutive ids land on one XCD) ----
+  const int mt = (p.M + BM - 1) / BM;
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int per = nblk / 8, rem = nblk % 8, x = b % 8;
+  const int id = x * per + min(x, rem) + b / 8;
+  const int m0 = (id % mt) * BM, n0 = (id / mt) * BN;
+
+  const int z = blockIdx.z;
+  const int zo = z / p.zdiv, zi = z % p.zdiv;
+  const int64_t offA = zo * p.sA_o + zi * p.sA_i;
+  const int64_t offB = zo * p.sB_o + (zi / p.grpB) * p.sB_i;
+  const int64_t offC = zo * p.sC_o + zi * p.sC_i;
+
+  if (threadIdx.x < 16) sLv[threadIdx.x] = p.levels[threadIdx.x];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // loaders
+  using LA = typename std::conditional<
+      OPA == A_BF16_K, LoadBf16K<BM>,
+      typename std::conditional<OPA == A_F32_K, LoadF32K<BM>, LoadBf16R<BM>>::type>::type;
+  using LB = typename std::conditional<
+      OPB == B_BF16_K, LoadBf16K<BN>,
+      typename std::conditional<
+          OPB == B_BF16_R, LoadBf16R<BN>,
+          typename std::conditional<OPB == B_NF4_K, LoadNf4K<BN>, LoadNf4R<BN>>::type>::type>::
+      type;
+  LA la;
+  LB lb;
+
+  const int nkt = (p.K + BK - 1) / BK;
+  const int total = nkt * p.nseg;
+
+  auto prefetch = [&](int it) {
+    const int seg = it / nkt, k0 = (it % nkt) * BK;
+    if constexpr (OPA == A_F32_K)
+      la.prefetch(reinterpret_cast<const float*>(p.A) + offA + seg * p.sA_seg, p.lda, m0, p.M,
+                  k0, p.K);
+    else
+      la.prefetch(reinterpret_cast<const uint16_t*>(p.A) + offA + seg * p.sA_seg, p.lda, m0,
+                  p.M, k0, p.K);
+    if constexpr (OPB == B_NF4_K || OPB == B_NF4_R)
+      lb.prefetch(reinterpret_cast<const uint8_t*>(p.B), p.absmax, p.rowlen, n0, p.N, k0, p.K);
+    else
+      lb.prefetch(reinterpret_cast<const uint16_t*>(p.B) + offB + seg * p.sB_seg, p.ldb, n0,
+                  p.N, k0, p.K);
+  };
+  auto store = [&](int buf) {
+    la.store(sA[buf]);
+    if constexpr (OPB == B_NF4_K || OPB == B_NF4_R)
+      lb.store(sB[buf], sLv);
+    else
+      lb.store(sB[buf]);
+  };
+
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  if (total > 0) {
+    prefetch(0);
+    __syncthreads();  // sLv visible
+    store(0);
+    __syncthreads();
+    for (int it = 0; it < total; ++it) {
+      const int cur = it & 1;
+      if (it + 1 < total) prefetch(it + 1);
+      const uint16_t* a_base = sA[cur] + (wm * WTM + lr) * PITCH + lk;
+      const uint16_t* b_base = sB[cur] + (wn * WTN + lr) * PITCH + lk;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 af[TM], bfr[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          af[i] = *reinterpret_cast<const bf16x8*>(a_base + i * 32 * PITCH + kk * 16);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8*>(b_base + j * 32 * PITCH + kk * 16);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+      if (it + 1 < total) store(cur ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- LoRA extension: extra k columns read directly as fragments ----
+  if (p.kext > 0) {
+    for (int e0 = 0; e0 < p.kext; e0 += 16) {
+      bf16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm * WTM + i * 32 + lr;
+        if (m < p.M)
+          af[i] = *reinterpret_cast<const bf16x8*>(p.Aext + (int64_t)m * p.ldae + e0 + lk);
+        else
+          af[i] = bf16x8{};
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WTN + j * 32 + lr;
+        if (n < p.N)
+          bfr[j] = *reinterpret_cast<const bf16x8*>(p.Bext + (int64_t)n * p.ldbe + e0 + lk);
+        else
+          bfr[j] = bf16x8{};
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: lane holds column lr, rows (e/4)*8 + (lane/32)*4 + e%4 ----
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * WTN + j * 32 + lr;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        if (m >= p.M) continue;
+        const float v = p.alpha * acc[i][j][e];
+        const int64_t o = offC + (int64_t)m * p.ldc + n;
+        switch (p.cmode) {
+          case C_F32: reinterpret_cast<float*>(p.C)[o] = v; break;
+          case C_F32_ACC: reinterpret_cast<float*>(p.C)[o] += v; break;
+          case C_F32_RES:
+            reinterpret_cast<float*>(p.C)[o] = p.R[offC + (int64_t)m * p.ldr + n] + v;
+            break;
+          default: reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16_bits(v); break;
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host launcher
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int OPA, int OPB>
+static hipError_t launch_t(const GemmParams& p, int batch, hipStream_t s) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, OPA, OPB>), dim3(tiles, 1, batch), dim3(NTHREADS), 0,
+                     s, p);
+  return hipGetLastError();
+}
+
+template <int OPA, int OPB>
+static hipError_t launch_tiles(const GemmParams& p, int batch, hipStream_t s) {
+  // Large problems take the 256 x 128 tile (each dequantized weight feeds 256
+  // rows); small ones trade reuse for enough workgroups to fill 256 CUs.
+  const int64_t t256 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128) * batch;
+  const int64_t t128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) * batch;
+  if (p.M >= 256 && t256 >= 192) return launch_t<256, 128, OPA, OPB>(p, batch, s);
+  if (p.M >= 128 && t128 >= 128) return launch_t<128, 128, OPA, OPB>(p, batch, s);
+  return launch_t<64, 64, OPA, OPB>(p, batch, s);
+}
+
+hipError_t gemm(const GemmParams& p, int opa, int opb, int batch, hipStream_t s) {
+  if (p.M <= 0 || p.N <= 0 || batch <= 0) return hipSuccess;
+#define LSN_CASE(A_, B_) \
+  if (opa == A_ && opb == B_) return launch_tiles<A_, B_>(p, batch, s);
+  LSN_CASE(A_BF16_K, B_NF4_K)
+  LSN_CASE(A_BF16_K, B_NF4_R)
+  LSN_CASE(A_F32_K, B_NF4_R)
+  LSN_CASE(A_BF16_K, B_BF16_K)
+  LSN_CASE(A_BF16_K, B_BF16_R)
+  LSN_CASE(A_BF16_R, B_BF16_R)
+#undef LSN_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lsn

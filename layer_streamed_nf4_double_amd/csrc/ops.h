@@ -1,0 +1,50 @@
+// Launchers of the per-layer kernels (ops.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lsn {
+void rmsnorm_fwd(const float* h, const uint16_t* g, int T, int H, float eps, uint16_t* y,
+                 float* rstd, hipStream_t s);
+void rmsnorm_bwd(const float* h, const uint16_t* g, const float* rstd, const float* dy,
+                 const float* dres, int T, int H, float* out, hipStream_t s);
+void rope_fwd(const float* qkv, uint16_t* out, int T, int S, int nq, int nkv, int d, float theta,
+              hipStream_t s);
+void rope_bwd(float* dqkv, uint16_t* outb, int T, int S, int nq, int nkv, int d, float theta,
+              hipStream_t s);
+void softmax_causal(const float* sc, float* Pf, uint16_t* Pb, int S, int64_t rows, hipStream_t s);
+void softmax_bwd(const float* Pf, const float* dP, uint16_t* dS, int S, int64_t rows,
+                 hipStream_t s);
+void swiglu_fwd(const float* gu, uint16_t* a, int T, int F, hipStream_t s);
+void swiglu_bwd(const float* gu, const float* da, uint16_t* dgu, float* dguf, int T, int F,
+                hipStream_t s);
+void embed(const int32_t* tok, const uint16_t* table, int T, int H, float* h, hipStream_t s);
+void skinny_bf16(const uint16_t* X, int64_t ldx, const float* W, int64_t sk, int64_t sj, int M,
+                 int K, int r, float* out, uint16_t* ext, int64_t ldext, float scale,
+                 hipStream_t s);
+void skinny_f32(const float* X, int64_t ldx, const float* W, int64_t sk, int64_t sj, int M, int K,
+                int r, float* out, uint16_t* ext, int64_t ldext, float scale, hipStream_t s);
+void lora_dA_bf16(const uint16_t* X, int64_t ldx, const float* U, int M, int K, int r, float sc,
+                  float* dA, hipStream_t s);
+void lora_dB_f32(const float* T, const float* DY, int64_t ldy, int M, int N, int r, float sc,
+                 float* dB, hipStream_t s);
+void lora_dB_bf16(const float* T, const uint16_t* DY, int64_t ldy, int M, int N, int r, float sc,
+                  float* dB, hipStream_t s);
+void lora_ext(const float* W, int64_t srow, int64_t sj, int R, int r, uint16_t* out, int64_t ld,
+              int c0, hipStream_t s);
+void lse_chunk(const float* logits, int T, int Vc, int v0, const int32_t* tgt, float* run_m,
+               float* run_s, float* tlogit, int first, hipStream_t s);
+void lse_final(const float* run_m, const float* run_s, const float* tlogit, const int32_t* tgt,
+               int T, float* logp, float* lse, hipStream_t s);
+void dlogits(const float* logits, int T, int Vc, int v0, const float* lse, const int32_t* tgt,
+             const float* dlogp, uint16_t* out, hipStream_t s);
+void sft_loss(const float* logp, const int32_t* tgt, int n, float* loss, float* dlogp,
+              hipStream_t s);
+void dpo_loss(const float* lp, const float* lr, int S, int P, float beta, float* out,
+              float* dlogp, hipStream_t s);
+void sgd(float* p, const float* g, float lr, int64_t n, hipStream_t s);
+void fill_u32(void* p, uint32_t v, int64_t n, hipStream_t s);
+void f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
+void nf4_dequant(const uint8_t* codes, const float* absmax, int64_t n, const float* levels,
+                 float* of32, uint16_t* obf, hipStream_t s);
+}  // namespace lsn

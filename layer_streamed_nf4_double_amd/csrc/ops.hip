@@ -1,0 +1,582 @@
+// Per-layer kernels around the GEMMs: RMSNorm, RoPE, causal softmax, SwiGLU,
+// embedding gather, LoRA skinny products and gradients, the vocabulary-chunk
+// log-softmax, losses, SGD, NF4 dequantization and small converters.
+//
+// Every reduction runs in a fixed order (one owner thread, or a fixed
+// butterfly + fixed cross-wave order), with no atomics, so a run is
+// bit-reproducible and independent of where the weights live.
+#include "common.h"
+#include "ops.h"
+
+namespace lsn {
+
+// ---------------------------------------------------------------------------
+// RMSNorm: y = g * h / sqrt(mean(h^2) + eps); one block per row
+// ---------------------------------------------------------------------------
+__global__ void rmsnorm_fwd_k(const float* __restrict__ h, const uint16_t* __restrict__ g, int H,
+                              float eps, uint16_t* __restrict__ y, float* __restrict__ rstd) {
+  __shared__ float red[16];
+  const int64_t row = blockIdx.x;
+  const float* x = h + row * H;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) ss += x[i] * x[i];
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  if (threadIdx.x == 0) rstd[row] = r;
+  for (int i = threadIdx.x; i < H; i += blockDim.x)
+    y[row * H + i] = f32_to_bf16_bits(bf16_to_f32(g[i]) * (x[i] * r));
+}
+
+// out = dres + rstd*(g dy) - rstd^3/H * h * sum(g dy h)
+__global__ void rmsnorm_bwd_k(const float* __restrict__ h, const uint16_t* __restrict__ g,
+                              const float* __restrict__ rstd, const float* __restrict__ dy,
+                              const float* dres, int H, float* out) {
+  __shared__ float red[16];
+  const int64_t row = blockIdx.x;
+  const float* x = h + row * H;
+  const float* d = dy + row * H;
+  float dot = 0.f;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) dot += bf16_to_f32(g[i]) * d[i] * x[i];
+  dot = block_sum(dot, red);
+  const float r = rstd[row];
+  const float c = r * r * r * dot / (float)H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) {
+    const float v = r * bf16_to_f32(g[i]) * d[i] - c * x[i];
+    out[row * H + i] = (dres ? dres[row * H + i] : 0.f) + v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RoPE (rotate-half) on the fused q|k|v rows.  Position = token % S.
+// fwd: fp32 q,k,v -> bf16 rotated q, k and plain v.
+// bwd: fp32 dq,dk,dv rotated back in place (fp32) + bf16 copy of all three.
+// ---------------------------------------------------------------------------
+LSN_DEV void rope_angle(int pos, int j, int d, float theta, float* c, float* s) {
+  const float inv = powf(theta, -2.0f * (float)j / (float)d);
+  sincosf((float)pos * inv, s, c);
+}
+
+__global__ void rope_fwd_k(const float* __restrict__ qkv, uint16_t* __restrict__ out, int S,
+                           int nq, int nkv, int d, float theta) {
+  const int64_t t = blockIdx.x;
+  const int pos = (int)(t % S);
+  const int W = (nq + 2 * nkv) * d;
+  const int half = d / 2;
+  const float* x = qkv + t * W;
+  uint16_t* y = out + t * W;
+  const int nrot = (nq + nkv) * half;  // rotated pairs
+  for (int i = threadIdx.x; i < nrot; i += blockDim.x) {
+    const int head = i / half, j = i % half;
+    float c, s;
+    rope_angle(pos, j, d, theta, &c, &s);
+    const float x1 = x[head * d + j], x2 = x[head * d + j + half];
+    y[head * d + j] = f32_to_bf16_bits(x1 * c - x2 * s);
+    y[head * d + j + half] = f32_to_bf16_bits(x2 * c + x1 * s);
+  }
+  for (int i = threadIdx.x; i < nkv * d; i += blockDim.x) {
+    const int o = (nq + nkv) * d + i;
+    y[o] = f32_to_bf16_bits(x[o]);
+  }
+}
+
+__global__ void rope_bwd_k(float* __restrict__ dqkv, uint16_t* __restrict__ outb, int S, int nq,
+                           int nkv, int d, float theta) {
+  const int64_t t = blockIdx.x;
+  const int pos = (int)(t % S);
+  const int W = (nq + 2 * nkv) * d;
+  const int half = d / 2;
+  float* x = dqkv + t * W;
+  uint16_t* y = outb + t * W;
+  const int nrot = (nq + nkv) * half;
+  for (int i = threadIdx.x; i < nrot; i += blockDim.x) {
+    const int head = i / half, j = i % half;
+    float c, s;
+    rope_angle(pos, j, d, theta, &c, &s);
+    const float d1 = x[head * d + j], d2 = x[head * d + j + half];
+    const float r1 = d1 * c + d2 * s, r2 = d2 * c - d1 * s;
+    x[head * d + j] = r1;
+    x[head * d + j + half] = r2;
+    y[head * d + j] = f32_to_bf16_bits(r1);
+    y[head * d + j + half] = f32_to_bf16_bits(r2);
+  }
+  for (int i = threadIdx.x; i < nkv * d; i += blockDim.x) {
+    const int o = (nq + nkv) * d + i;
+    y[o] = f32_to_bf16_bits(x[o]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// causal softmax over rows of [Z, S, S] scores (already scaled); one wave
+// per row.  Writes P in fp32 and bf16, zeros above the diagonal.
+// ---------------------------------------------------------------------------
+__global__ void softmax_causal_k(const float* __restrict__ sc, float* __restrict__ Pf,
+                                 uint16_t* __restrict__ Pb, int S, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int i = (int)(row % S);
+  const float* x = sc + row * S;
+  float m = -INFINITY;
+  for (int j = lane; j <= i; j += 64) m = fmaxf(m, x[j]);
+  m = wave_max(m);
+  float sum = 0.f;
+  for (int j = lane; j <= i; j += 64) sum += expf(x[j] - m);
+  sum = wave_sum(sum);
+  const float inv = 1.0f / sum;
+  for (int j = lane; j < S; j += 64) {
+    const float p = (j <= i) ? expf(x[j] - m) * inv : 0.f;
+    Pf[row * S + j] = p;
+    Pb[row * S + j] = f32_to_bf16_bits(p);
+  }
+}
+
+// dS = P * (dP - sum_j dP*P) -> bf16; one wave per row
+__global__ void softmax_bwd_k(const float* __restrict__ Pf, const float* __restrict__ dP,
+                              uint16_t* __restrict__ dS, int S, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int i = (int)(row % S);
+  const float* p = Pf + row * S;
+  const float* g = dP + row * S;
+  float dot = 0.f;
+  for (int j = lane; j <= i; j += 64) dot += p[j] * g[j];
+  dot = wave_sum(dot);
+  for (int j = lane; j < S; j += 64)
+    dS[row * S + j] = f32_to_bf16_bits((j <= i) ? p[j] * (g[j] - dot) : 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU on the fused gate|up rows [T, 2F]
+// ---------------------------------------------------------------------------
+LSN_DEV float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+__global__ void swiglu_fwd_k(const float* __restrict__ gu, uint16_t* __restrict__ a, int F,
+                             int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int64_t t = i / F, f = i % F;
+  const float g = gu[t * 2 * F + f], u = gu[t * 2 * F + F + f];
+  a[i] = f32_to_bf16_bits(g * sigm(g) * u);
+}
+
+// dg = da * u * silu'(g), du = da * silu(g) -> bf16 [T, 2F] (+ fp32 copy)
+__global__ void swiglu_bwd_k(const float* __restrict__ gu, const float* __restrict__ da,
+                             uint16_t* __restrict__ dgu, float* __restrict__ dguf, int F,
+                             int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int64_t t = i / F, f = i % F;
+  const float g = gu[t * 2 * F + f], u = gu[t * 2 * F + F + f];
+  const float s = sigm(g);
+  const float dg = da[i] * u * (s * (1.0f + g * (1.0f - s)));
+  const float du = da[i] * (g * s);
+  dgu[t * 2 * F + f] = f32_to_bf16_bits(dg);
+  dgu[t * 2 * F + F + f] = f32_to_bf16_bits(du);
+  if (dguf) {
+    dguf[t * 2 * F + f] = dg;
+    dguf[t * 2 * F + F + f] = du;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// embedding rows (bf16 table) -> fp32
+// ---------------------------------------------------------------------------
+__global__ void embed_k(const int32_t* __restrict__ tok, const uint16_t* __restrict__ table,
+                        int H, float* __restrict__ h) {
+  const int64_t t = blockIdx.x;
+  const int64_t v = tok[t];
+  for (int i = threadIdx.x; i < H; i += blockDim.x) h[t * H + i] = bf16_to_f32(table[v * H + i]);
+}
+
+// ---------------------------------------------------------------------------
+// LoRA skinny products (r <= 16)
+//   out[m, j] = sum_k X(m, k) * W(k, j),  W(k, j) = Wp[k*sk + j*sj]
+// 16 rows per block, 256 threads = 16 rows x 16 ranks; K in chunks of 64
+// staged through LDS; each output summed by one thread in k order.
+// Optional bf16(scale * out) copy into ext[m*ldext + j].
+// ---------------------------------------------------------------------------
+template <typename TX>
+__global__ void skinny_k(const TX* __restrict__ X, int64_t ldx, const float* __restrict__ Wp,
+                         int64_t sk, int64_t sj, int M, int K, int r, float* __restrict__ out,
+                         uint16_t* __restrict__ ext, int64_t ldext, float scale) {
+  __shared__ float sx[16][65];
+  __shared__ float sw[64][17];
+  const int m0 = blockIdx.x * 16;
+  const int tr = threadIdx.x >> 4, tj = threadIdx.x & 15;
+  float acc = 0.f;
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    for (int i = threadIdx.x; i < 16 * 64; i += 256) {
+      const int rr = i >> 6, kk = i & 63;
+      const int m = m0 + rr, k = k0 + kk;
+      float v = 0.f;
+      if (m < M && k < K) {
+        if constexpr (sizeof(TX) == 2)
+          v = bf16_to_f32(X[(int64_t)m * ldx + k]);
+        else
+          v = X[(int64_t)m * ldx + k];
+      }
+      sx[rr][kk] = v;
+    }
+    for (int i = threadIdx.x; i < 64 * 16; i += 256) {
+      const int kk = i >> 4, j = i & 15;
+      const int k = k0 + kk;
+      sw[kk][j] = (k < K && j < r) ? Wp[(int64_t)k * sk + (int64_t)j * sj] : 0.f;
+    }
+    __syncthreads();
+    const int kn = min(64, K - k0);
+    for (int kk = 0; kk < kn; ++kk) acc += sx[tr][kk] * sw[kk][tj];
+    __syncthreads();
+  }
+  const int m = m0 + tr;
+  if (m < M && tj < r) {
+    out[(int64_t)m * r + tj] = acc;
+    if (ext) ext[(int64_t)m * ldext + tj] = f32_to_bf16_bits(scale * acc);
+  }
+  if (m < M && ext && tj >= r) ext[(int64_t)m * ldext + tj] = 0;  // pad ranks to 16
+}
+
+// dA[k, j] += s * sum_m X[m, k] * U[m, j]   (one thread per k, all r ranks)
+template <typename TX>
+__global__ void lora_dA_k(const TX* __restrict__ X, int64_t ldx, const float* __restrict__ U,
+                          int M, int K, int r, float s, float* __restrict__ dA) {
+  __shared__ float su[256][16];
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  for (int m0 = 0; m0 < M; m0 += 256) {
+    const int mn = min(256, M - m0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < 256 * 16; i += blockDim.x) {
+      const int mm = i >> 4, j = i & 15;
+      su[mm][j] = (mm < mn && j < r) ? U[(int64_t)(m0 + mm) * r + j] : 0.f;
+    }
+    __syncthreads();
+    if (k < K) {
+      for (int mm = 0; mm < mn; ++mm) {
+        float x;
+        if constexpr (sizeof(TX) == 2)
+          x = bf16_to_f32(X[(int64_t)(m0 + mm) * ldx + k]);
+        else
+          x = X[(int64_t)(m0 + mm) * ldx + k];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] += x * su[mm][j];
+      }
+    }
+  }
+  if (k < K)
+    for (int j = 0; j < r; ++j) dA[(int64_t)k * r + j] += s * acc[j];
+}
+
+// dB[j, n] += s * sum_m T[m, j] * DY[m, n]   (one thread per n, all r ranks)
+template <typename TY>
+__global__ void lora_dB_k(const float* __restrict__ T, const TY* __restrict__ DY, int64_t ldy,
+                          int M, int N, int r, float s, float* __restrict__ dB) {
+  __shared__ float st[256][16];
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  for (int m0 = 0; m0 < M; m0 += 256) {
+    const int mn = min(256, M - m0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < 256 * 16; i += blockDim.x) {
+      const int mm = i >> 4, j = i & 15;
+      st[mm][j] = (mm < mn && j < r) ? T[(int64_t)(m0 + mm) * r + j] : 0.f;
+    }
+    __syncthreads();
+    if (n < N) {
+      for (int mm = 0; mm < mn; ++mm) {
+        float y;
+        if constexpr (sizeof(TY) == 2)
+          y = bf16_to_f32(DY[(int64_t)(m0 + mm) * ldy + n]);
+        else
+          y = DY[(int64_t)(m0 + mm) * ldy + n];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] += st[mm][j] * y;
+      }
+    }
+  }
+  if (n < N)
+    for (int j = 0; j < r; ++j) dB[(int64_t)j * N + n] += s * acc[j];
+}
+
+// out[row*ld + c0 + j] = bf16(W(row, j)), W(row, j) = Wp[row*srow + j*sj], j < 16
+// (zero for j >= r); rows [0, R)
+__global__ void lora_ext_k(const float* __restrict__ Wp, int64_t srow, int64_t sj, int R, int r,
+                           uint16_t* __restrict__ out, int64_t ld, int c0) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)R * 16) return;
+  const int64_t row = i >> 4;
+  const int j = (int)(i & 15);
+  out[row * ld + c0 + j] = (j < r) ? f32_to_bf16_bits(Wp[row * srow + (int64_t)j * sj]) : 0;
+}
+
+// ---------------------------------------------------------------------------
+// vocabulary-chunk log-softmax (online max / sum) and target gather
+// ---------------------------------------------------------------------------
+__global__ void lse_chunk_k(const float* __restrict__ logits, int Vc, int v0,
+                            const int32_t* __restrict__ tgt, float* __restrict__ run_m,
+                            float* __restrict__ run_s, float* __restrict__ tlogit, int first) {
+  __shared__ float red[16];
+  const int64_t t = blockIdx.x;
+  const float* x = logits + t * Vc;
+  float m = -INFINITY;
+  for (int i = threadIdx.x; i < Vc; i += blockDim.x) m = fmaxf(m, x[i]);
+  m = block_max(m, red);
+  float s = 0.f;
+  for (int i = threadIdx.x; i < Vc; i += blockDim.x) s += expf(x[i] - m);
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) {
+    const int y = tgt[t];
+    if (first) {
+      run_m[t] = m;
+      run_s[t] = s;
+      tlogit[t] = 0.f;
+    } else {
+      const float om = run_m[t], os = run_s[t];
+      const float nm = fmaxf(om, m);
+      run_s[t] = os * expf(om - nm) + s * expf(m - nm);
+      run_m[t] = nm;
+    }
+    if (y >= v0 && y < v0 + Vc) tlogit[t] = x[y - v0];
+  }
+}
+
+__global__ void lse_final_k(const float* __restrict__ run_m, const float* __restrict__ run_s,
+                            const float* __restrict__ tlogit, const int32_t* __restrict__ tgt,
+                            int T, float* __restrict__ logp, float* __restrict__ lse) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const float l = run_m[t] + logf(run_s[t]);
+  lse[t] = l;
+  logp[t] = (tgt[t] >= 0) ? tlogit[t] - l : 0.f;
+}
+
+// dlogits = dlogp * (onehot(y) - exp(l - lse)) -> bf16 [T, Vc]
+__global__ void dlogits_k(const float* __restrict__ logits, int Vc, int v0,
+                          const float* __restrict__ lse, const int32_t* __restrict__ tgt,
+                          const float* __restrict__ dlogp, uint16_t* __restrict__ out) {
+  const int64_t t = blockIdx.y;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= Vc) return;
+  const int y = tgt[t];
+  float g = 0.f;
+  if (y >= 0) {
+    const float p = expf(logits[t * Vc + i] - lse[t]);
+    g = dlogp[t] * (((v0 + i) == y ? 1.f : 0.f) - p);
+  }
+  out[t * Vc + i] = f32_to_bf16_bits(g);
+}
+
+// ---------------------------------------------------------------------------
+// losses (single block, fixed-order reductions)
+// ---------------------------------------------------------------------------
+__global__ void sft_loss_k(const float* __restrict__ logp, const int32_t* __restrict__ tgt, int n,
+                           float* __restrict__ loss, float* __restrict__ dlogp) {
+  __shared__ float red[16];
+  float s = 0.f, c = 0.f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x)
+    if (tgt[i] >= 0) {
+      s += logp[i];
+      c += 1.f;
+    }
+  s = block_sum(s, red);
+  c = block_sum(c, red);
+  if (threadIdx.x == 0) loss[0] = -s / c;
+  const float g = -1.0f / c;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) dlogp[i] = (tgt[i] >= 0) ? g : 0.f;
+}
+
+__global__ void dpo_loss_k(const float* __restrict__ lp, const float* __restrict__ lr, int S,
+                           int P, float beta, float* __restrict__ out,
+                           float* __restrict__ dlogp) {
+  __shared__ float red[16];
+  float v[4] = {0.f, 0.f, 0.f, 0.f};  // pc, pr, rc, rr
+  for (int i = threadIdx.x; i < 2 * S; i += blockDim.x) {
+    const int seq = i / S, pos = i % S;
+    if (pos >= P - 1 && pos <= S - 2) {
+      v[seq] += lp[i];
+      v[2 + seq] += lr[i];
+    }
+  }
+  for (int q = 0; q < 4; ++q) v[q] = block_sum(v[q], red);
+  const float z = beta * ((v[0] - v[2]) - (v[1] - v[3]));
+  // -log sigmoid(z) = softplus(-z), stable form
+  const float loss = fmaxf(-z, 0.f) + log1pf(expf(-fabsf(z)));
+  const float g = beta / (1.0f + expf(z));  // beta * sigmoid(-z)
+  if (threadIdx.x == 0) {
+    out[0] = loss;
+    out[1] = z;
+    out[2] = v[0];
+    out[3] = v[1];
+    out[4] = v[2];
+    out[5] = v[3];
+  }
+  for (int i = threadIdx.x; i < 2 * S; i += blockDim.x) {
+    const int seq = i / S, pos = i % S;
+    dlogp[i] = (pos >= P - 1 && pos <= S - 2) ? (seq == 0 ? -g : g) : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// small utilities
+// ---------------------------------------------------------------------------
+__global__ void sgd_k(float* __restrict__ p, const float* __restrict__ g, float lr, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] -= lr * g[i];
+}
+
+__global__ void fill_k(uint32_t* __restrict__ p, uint32_t v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void f32_to_bf16_k(const float* __restrict__ x, uint16_t* __restrict__ y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = f32_to_bf16_bits(x[i]);
+}
+
+// NF4 -> fp32 (bit-equal to the host codec) or bf16; 8 elements per thread
+struct Levels {
+  float v[16];
+};
+__global__ void nf4_dequant_k(const uint32_t* __restrict__ codes, const float* __restrict__ absmax,
+                              int64_t nwords, Levels lv, float* __restrict__ of32,
+                              u32x4* __restrict__ obf) {
+  __shared__ float sl[16];
+  if (threadIdx.x < 16) sl[threadIdx.x] = lv.v[threadIdx.x];
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nwords) return;
+  const uint32_t w = codes[i];
+  const float a = absmax[i >> 3];
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = sl[(w >> (4 * j)) & 15u] * a;
+  if (of32) {
+    f32x4* o = reinterpret_cast<f32x4*>(of32 + i * 8);
+    o[0] = f32x4{v[0], v[1], v[2], v[3]};
+    o[1] = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    obf[i] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7])};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static inline unsigned nb(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
+
+void rmsnorm_fwd(const float* h, const uint16_t* g, int T, int H, float eps, uint16_t* y,
+                 float* rstd, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_fwd_k, dim3(T), dim3(256), 0, s, h, g, H, eps, y, rstd);
+}
+void rmsnorm_bwd(const float* h, const uint16_t* g, const float* rstd, const float* dy,
+                 const float* dres, int T, int H, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_bwd_k, dim3(T), dim3(256), 0, s, h, g, rstd, dy, dres, H, out);
+}
+void rope_fwd(const float* qkv, uint16_t* out, int T, int S, int nq, int nkv, int d, float theta,
+              hipStream_t s) {
+  hipLaunchKernelGGL(rope_fwd_k, dim3(T), dim3(256), 0, s, qkv, out, S, nq, nkv, d, theta);
+}
+void rope_bwd(float* dqkv, uint16_t* outb, int T, int S, int nq, int nkv, int d, float theta,
+              hipStream_t s) {
+  hipLaunchKernelGGL(rope_bwd_k, dim3(T), dim3(256), 0, s, dqkv, outb, S, nq, nkv, d, theta);
+}
+void softmax_causal(const float* sc, float* Pf, uint16_t* Pb, int S, int64_t rows,
+                    hipStream_t s) {
+  hipLaunchKernelGGL(softmax_causal_k, dim3(nb(rows, 4)), dim3(256), 0, s, sc, Pf, Pb, S, rows);
+}
+void softmax_bwd(const float* Pf, const float* dP, uint16_t* dS, int S, int64_t rows,
+                 hipStream_t s) {
+  hipLaunchKernelGGL(softmax_bwd_k, dim3(nb(rows, 4)), dim3(256), 0, s, Pf, dP, dS, S, rows);
+}
+void swiglu_fwd(const float* gu, uint16_t* a, int T, int F, hipStream_t s) {
+  const int64_t n = (int64_t)T * F;
+  hipLaunchKernelGGL(swiglu_fwd_k, dim3(nb(n, 256)), dim3(256), 0, s, gu, a, F, n);
+}
+void swiglu_bwd(const float* gu, const float* da, uint16_t* dgu, float* dguf, int T, int F,
+                hipStream_t s) {
+  const int64_t n = (int64_t)T * F;
+  hipLaunchKernelGGL(swiglu_bwd_k, dim3(nb(n, 256)), dim3(256), 0, s, gu, da, dgu, dguf, F, n);
+}
+void embed(const int32_t* tok, const uint16_t* table, int T, int H, float* h, hipStream_t s) {
+  hipLaunchKernelGGL(embed_k, dim3(T), dim3(256), 0, s, tok, table, H, h);
+}
+void skinny_bf16(const uint16_t* X, int64_t ldx, const float* W, int64_t sk, int64_t sj, int M,
+                 int K, int r, float* out, uint16_t* ext, int64_t ldext, float scale,
+                 hipStream_t s) {
+  hipLaunchKernelGGL(skinny_k<uint16_t>, dim3(nb(M, 16)), dim3(256), 0, s, X, ldx, W, sk, sj, M,
+                     K, r, out, ext, ldext, scale);
+}
+void skinny_f32(const float* X, int64_t ldx, const float* W, int64_t sk, int64_t sj, int M, int K,
+                int r, float* out, uint16_t* ext, int64_t ldext, float scale, hipStream_t s) {
+  hipLaunchKernelGGL(skinny_k<float>, dim3(nb(M, 16)), dim3(256), 0, s, X, ldx, W, sk, sj, M, K,
+                     r, out, ext, ldext, scale);
+}
+void lora_dA_bf16(const uint16_t* X, int64_t ldx, const float* U, int M, int K, int r, float sc,
+                  float* dA, hipStream_t s) {
+  hipLaunchKernelGGL(lora_dA_k<uint16_t>, dim3(nb(K, 256)), dim3(256), 0, s, X, ldx, U, M, K, r,
+                     sc, dA);
+}
+void lora_dB_f32(const float* T, const float* DY, int64_t ldy, int M, int N, int r, float sc,
+                 float* dB, hipStream_t s) {
+  hipLaunchKernelGGL(lora_dB_k<float>, dim3(nb(N, 256)), dim3(256), 0, s, T, DY, ldy, M, N, r, sc,
+                     dB);
+}
+void lora_dB_bf16(const float* T, const uint16_t* DY, int64_t ldy, int M, int N, int r, float sc,
+                  float* dB, hipStream_t s) {
+  hipLaunchKernelGGL(lora_dB_k<uint16_t>, dim3(nb(N, 256)), dim3(256), 0, s, T, DY, ldy, M, N, r,
+                     sc, dB);
+}
+void lora_ext(const float* W, int64_t srow, int64_t sj, int R, int r, uint16_t* out, int64_t ld,
+              int c0, hipStream_t s) {
+  hipLaunchKernelGGL(lora_ext_k, dim3(nb((int64_t)R * 16, 256)), dim3(256), 0, s, W, srow, sj, R,
+                     r, out, ld, c0);
+}
+void lse_chunk(const float* logits, int T, int Vc, int v0, const int32_t* tgt, float* run_m,
+               float* run_s, float* tlogit, int first, hipStream_t s) {
+  hipLaunchKernelGGL(lse_chunk_k, dim3(T), dim3(256), 0, s, logits, Vc, v0, tgt, run_m, run_s,
+                     tlogit, first);
+}
+void lse_final(const float* run_m, const float* run_s, const float* tlogit, const int32_t* tgt,
+               int T, float* logp, float* lse, hipStream_t s) {
+  hipLaunchKernelGGL(lse_final_k, dim3(nb(T, 256)), dim3(256), 0, s, run_m, run_s, tlogit, tgt, T,
+                     logp, lse);
+}
+void dlogits(const float* logits, int T, int Vc, int v0, const float* lse, const int32_t* tgt,
+             const float* dlogp, uint16_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(dlogits_k, dim3(nb(Vc, 256), T), dim3(256), 0, s, logits, Vc, v0, lse, tgt,
+                     dlogp, out);
+}
+void sft_loss(const float* logp, const int32_t* tgt, int n, float* loss, float* dlogp,
+              hipStream_t s) {
+  hipLaunchKernelGGL(sft_loss_k, dim3(1), dim3(1024), 0, s, logp, tgt, n, loss, dlogp);
+}
+void dpo_loss(const float* lp, const float* lr, int S, int P, float beta, float* out,
+              float* dlogp, hipStream_t s) {
+  hipLaunchKernelGGL(dpo_loss_k, dim3(1), dim3(1024), 0, s, lp, lr, S, P, beta, out, dlogp);
+}
+void sgd(float* p, const float* g, float lr, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(sgd_k, dim3(nb(n, 256)), dim3(256), 0, s, p, g, lr, n);
+}
+void fill_u32(void* p, uint32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(fill_k, dim3(nb(n, 256)), dim3(256), 0, s, (uint32_t*)p, v, n);
+}
+void f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(f32_to_bf16_k, dim3(nb(n, 256)), dim3(256), 0, s, x, y, n);
+}
+void nf4_dequant(const uint8_t* codes, const float* absmax, int64_t n, const float* levels,
+                 float* of32, uint16_t* obf, hipStream_t s) {
+  Levels lv;
+  for (int i = 0; i < 16; ++i) lv.v[i] = levels[i];
+  const int64_t nw = n / 8;
+  hipLaunchKernelGGL(nf4_dequant_k, dim3(nb(nw, 256)), dim3(256), 0, s, (const uint32_t*)codes,
+                     absmax, nw, lv, of32, (u32x4*)obf);
+}
+
+}  // namespace lsn

@@ -1,0 +1,1123 @@
+// liblsn runtime: context, workspace carving, pinned host store, the
+// double-buffered layer stream scheduler, layer orchestration and the C ABI.
+//
+// The mechanism ("Soup: Fine-Tune an 8B Model on a 4 GB GPU", section "The Core
+// Idea: Layer Streaming"): the frozen base stays in host RAM (here: one pinned
+// arena, or a file) and is copied to the GPU one decoder layer at a time, on a
+// dedicated stream, as the forward or backward pass reaches it.  Here each
+// layer is one contiguous record (NF4 codes of the seven projections, their
+// absmax scales, the two norm gains); two device slots alternate, so the copy
+// of layer i+1 runs on the copy stream while layer i computes.  Events order
+// the streams: the compute stream waits for copy_done[slot] before a layer,
+// and the copy into a slot waits for slot_free[slot] recorded after the
+// slot's previous layer finished.  A record already sitting in a slot when a
+// pass reaches it (the last two layers of a forward pass are the first two of
+// the backward pass) is reused instead of copied again.
+//
+// Resident mode keeps every record in device memory at the same intra-record
+// offsets, so the kernels run on byte-identical inputs: streamed and resident
+// results are bit-identical (the pages' own correctness bar, axbrief.com
+// article, "Beyond Memory: The Layer Streaming Breakthrough").
+#include <errno.h>
+#include <fcntl.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+#include <unistd.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/lsn.h"
+#include "gemm.h"
+#include "host_codec.h"
+#include "ops.h"
+
+using namespace lsn;
+
+namespace {
+
+constexpr int NPROJ = 7;
+constexpr uint64_t REC_ALIGN = 4096;
+constexpr int VCHUNK = 16384;  // vocabulary rows per LM-head GEMM
+
+inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+struct Carver {
+  uint64_t off = 0;
+  uint64_t take(uint64_t bytes) {
+    off = align_up(off, 256);
+    const uint64_t o = off;
+    off += bytes;
+    return o;
+  }
+};
+
+}  // namespace
+
+struct lsn_ctx {
+  lsn_config cfg{};
+  std::string store_path;
+  hipStream_t cs = nullptr;    // compute stream (caller's)
+  hipStream_t copy = nullptr;  // the scheduler's copy stream
+  hipEvent_t copy_done[2] = {nullptr, nullptr};
+  hipEvent_t slot_free[2] = {nullptr, nullptr};
+  bool slot_used[2] = {false, false};   // slot_free[s] has been recorded
+  bool copy_issued[2] = {false, false}; // copy_done[s] has been recorded
+  int slot_layer[2] = {-1, -1};
+  int device = 0;
+
+  char* ws = nullptr;
+  uint64_t ws_bytes = 0, ws_needed = 0;
+
+  // record layout
+  int64_t N[NPROJ] = {}, K[NPROJ] = {};
+  uint64_t code_off[NPROJ] = {}, amax_off[NPROJ] = {}, norm_off[2] = {};
+  uint64_t rec_bytes = 0;
+  int QKV = 0, QD = 0, KVD = 0;
+
+  // host store
+  uint8_t* store = nullptr;  // pinned, n_layers records (host / resident modes)
+  uint8_t* bounce[2] = {nullptr, nullptr};  // pinned bounce buffers (file mode)
+  int fd = -1;
+  std::vector<char> loaded;
+
+  // device regions
+  uint8_t* records = nullptr;  // resident: L records; streamed: 2 slots
+  uint16_t *embed = nullptr, *lm_head = nullptr, *final_norm = nullptr;
+  float *lora_p = nullptr, *lora_g = nullptr;
+  uint64_t lora_n = 0;
+  std::vector<int64_t> lA, lB;  // float offsets of A and B per (layer, proj); -1 if none
+  bool head_loaded = false;
+
+  // activation scratch (one layer at max_tokens)
+  uint16_t *n1, *qkvb, *Pb, *O, *n2, *a, *dgu, *dO, *dqkvb, *aext, *bext, *nf, *dlog;
+  float *rstd1, *qkv, *scores, *Pf, *h2, *rstd2, *gu, *da, *dguf, *dn, *dh2, *dqkv, *lt, *lu,
+      *rstdf, *logits, *run_m, *run_s, *tlogit, *lse, *dnf;
+  int64_t ext_rows = 0;
+
+  // pass state
+  int pass_kind = -1, n_seq = 0, seq_len = 0, T = 0;
+  std::vector<int> order, slot_of;
+  size_t pos = 0;
+  bool adapters_on = true;
+  const float* lm_h = nullptr;
+  int lm_T = 0;
+
+  float levels[16];
+  uint64_t loads = 0, bytes_h2d = 0;
+  bool poisoned = false;
+  std::string err;
+
+  bool targeted(int p) const { return (cfg.lora_targets >> p) & 1u; }
+  float lora_scale() const { return cfg.lora_alpha / (float)cfg.lora_rank; }
+  float* A_of(int layer, int p) const {
+    const int64_t o = lA[layer * NPROJ + p];
+    return o < 0 ? nullptr : lora_p + o;
+  }
+  float* B_of(int layer, int p) const {
+    const int64_t o = lB[layer * NPROJ + p];
+    return o < 0 ? nullptr : lora_p + o;
+  }
+  float* dA_of(int layer, int p) const {
+    const int64_t o = lA[layer * NPROJ + p];
+    return o < 0 ? nullptr : lora_g + o;
+  }
+  float* dB_of(int layer, int p) const {
+    const int64_t o = lB[layer * NPROJ + p];
+    return o < 0 ? nullptr : lora_g + o;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// error plumbing
+// ---------------------------------------------------------------------------
+static lsn_status fail(lsn_ctx* c, lsn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (c) {
+    c->err = buf;
+    if (st == LSN_ERR_HIP || st == LSN_ERR_IO) c->poisoned = true;
+  }
+  return st;
+}
+
+#define HIPCHK(c, expr)                                                                     \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess)                                                                   \
+      return fail(c, LSN_ERR_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_), \
+                  __FILE__, __LINE__);                                                      \
+  } while (0)
+
+#define CHECK_CTX(c)                                                  \
+  do {                                                                \
+    if (!(c)) return LSN_ERR_INVALID;                                 \
+    if ((c)->poisoned) return LSN_ERR_STATE;                          \
+  } while (0)
+
+static lsn_status launch_check(lsn_ctx* c) {
+  HIPCHK(c, hipGetLastError());
+  return LSN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// configuration checks and layout
+// ---------------------------------------------------------------------------
+static bool cfg_valid(const lsn_config* g, std::string* why) {
+  auto bad = [&](const char* m) {
+    *why = m;
+    return false;
+  };
+  if (!g) return bad("null config");
+  if (g->n_layers <= 0 || g->hidden <= 0 || g->n_heads <= 0 || g->n_kv_heads <= 0 ||
+      g->head_dim <= 0 || g->ffn <= 0 || g->vocab <= 0)
+    return bad("non-positive shape");
+  if (g->n_heads % g->n_kv_heads) return bad("n_heads must be a multiple of n_kv_heads");
+  if (g->head_dim % 16) return bad("head_dim must be a multiple of 16");
+  if (g->hidden % 16 || g->ffn % 16) return bad("hidden and ffn must be multiples of 16");
+  if (g->vocab % 8) return bad("vocab must be a multiple of 8");
+  if (g->lora_rank < 1 || g->lora_rank > 16) return bad("lora_rank must be 1..16");
+  if (g->lora_targets >= (1u << NPROJ)) return bad("lora_targets has unknown bits");
+  if (g->max_tokens <= 0 || g->max_seq_len <= 0 || g->max_seq_len > g->max_tokens)
+    return bad("bad max_tokens / max_seq_len");
+  if (g->mode < LSN_RESIDENT || g->mode > LSN_STREAM_FILE) return bad("bad mode");
+  if (g->mode == LSN_STREAM_FILE && (!g->store_path || !g->store_path[0]))
+    return bad("file mode needs store_path");
+  if (!(g->rms_eps > 0.f) || !(g->rope_theta > 0.f)) return bad("bad eps / theta");
+  return true;
+}
+
+static void record_layout(lsn_ctx* c) {
+  const lsn_config& g = c->cfg;
+  const int64_t H = g.hidden, F = g.ffn;
+  c->QD = g.n_heads * g.head_dim;
+  c->KVD = g.n_kv_heads * g.head_dim;
+  c->QKV = c->QD + 2 * c->KVD;
+  const int64_t n[NPROJ] = {c->QD, c->KVD, c->KVD, H, F, F, H};
+  const int64_t k[NPROJ] = {H, H, H, c->QD, H, H, F};
+  uint64_t off = 0;
+  for (int p = 0; p < NPROJ; ++p) {  // codes back to back (q|k|v and gate|up fuse)
+    c->N[p] = n[p];
+    c->K[p] = k[p];
+    c->code_off[p] = off;
+    off += (uint64_t)n[p] * k[p] / 2;
+  }
+  off = align_up(off, 256);
+  for (int p = 0; p < NPROJ; ++p) {  // absmax back to back, same order
+    c->amax_off[p] = off;
+    off += (uint64_t)n[p] * k[p] / 64 * 4;
+  }
+  off = align_up(off, 256);
+  c->norm_off[0] = off;
+  off += H * 2;
+  c->norm_off[1] = off;
+  off += H * 2;
+  c->rec_bytes = align_up(off, REC_ALIGN);
+}
+
+// Carves the workspace; with base == nullptr only measures.
+static uint64_t carve(lsn_ctx* c, char* base) {
+  const lsn_config& g = c->cfg;
+  const int64_t T = g.max_tokens, S = g.max_seq_len, H = g.hidden, F = g.ffn, V = g.vocab;
+  const int64_t r = g.lora_rank;
+  Carver cv;
+  auto P = [&](uint64_t bytes) -> char* { const uint64_t o = cv.take(bytes); return base ? base + o : nullptr; };
+  const int nrec = (g.mode == LSN_RESIDENT) ? g.n_layers : 2;
+  c->records = (uint8_t*)P((uint64_t)nrec * c->rec_bytes);
+  c->embed = (uint16_t*)P(V * H * 2);
+  c->lm_head = g.tied_embeddings ? c->embed : (uint16_t*)P(V * H * 2);
+  c->final_norm = (uint16_t*)P(H * 2);
+  // adapters
+  c->lA.assign((size_t)g.n_layers * NPROJ, -1);
+  c->lB.assign((size_t)g.n_layers * NPROJ, -1);
+  uint64_t nfl = 0;
+  for (int l = 0; l < g.n_layers; ++l)
+    for (int p = 0; p < NPROJ; ++p)
+      if (c->targeted(p)) {
+        c->lA[l * NPROJ + p] = (int64_t)nfl;
+        nfl += align_up((uint64_t)c->K[p] * r, 64);
+        c->lB[l * NPROJ + p] = (int64_t)nfl;
+        nfl += align_up((uint64_t)r * c->N[p], 64);
+      }
+  c->lora_n = nfl;
+  c->lora_p = (float*)P(std::max<uint64_t>(nfl, 1) * 4);
+  c->lora_g = (float*)P(std::max<uint64_t>(nfl, 1) * 4);
+  // one layer of activations
+  const int64_t Z = (int64_t)g.n_heads * T * S;  // sum over sequences of heads * S * S
+  const int64_t QKV = c->QKV, QD = c->QD;
+  c->n1 = (uint16_t*)P(T * H * 2);
+  c->rstd1 = (float*)P(T * 4);
+  c->qkv = (float*)P(T * QKV * 4);
+  c->qkvb = (uint16_t*)P(T * QKV * 2);
+  c->scores = (float*)P(Z * 4);
+  c->Pf = (float*)P(Z * 4);
+  c->Pb = (uint16_t*)P(Z * 2);
+  c->O = (uint16_t*)P(T * QD * 2);
+  c->h2 = (float*)P(T * H * 4);
+  c->n2 = (uint16_t*)P(T * H * 2);
+  c->rstd2 = (float*)P(T * 4);
+  c->gu = (float*)P(T * 2 * F * 4);
+  c->a = (uint16_t*)P(T * F * 2);
+  c->da = (float*)P(T * F * 4);
+  c->dgu = (uint16_t*)P(T * 2 * F * 2);
+  c->dguf = (float*)P(T * 2 * F * 4);
+  c->dn = (float*)P(T * H * 4);
+  c->dh2 = (float*)P(T * H * 4);
+  c->dO = (uint16_t*)P(T * QD * 2);
+  c->dqkv = (float*)P(T * QKV * 4);
+  c->dqkvb = (uint16_t*)P(T * QKV * 2);
+  c->lt = (float*)P(NPROJ * T * 16 * 4);
+  c->lu = (float*)P(T * 16 * 4);
+  c->ext_rows = std::max<int64_t>({QKV, 2 * F, H, QD, F});
+  c->aext = (uint16_t*)P(T * 48 * 2);
+  c->bext = (uint16_t*)P(c->ext_rows * 48 * 2);
+  // LM head
+  const int64_t Vc = std::min<int64_t>(V, VCHUNK);
+  c->nf = (uint16_t*)P(T * H * 2);
+  c->rstdf = (float*)P(T * 4);
+  c->logits = (float*)P(T * Vc * 4);
+  c->dlog = (uint16_t*)P(T * Vc * 2);
+  c->run_m = (float*)P(T * 4);
+  c->run_s = (float*)P(T * 4);
+  c->tlogit = (float*)P(T * 4);
+  c->lse = (float*)P(T * 4);
+  c->dnf = (float*)P(T * H * 4);
+  return align_up(cv.off, 256);
+}
+
+// ---------------------------------------------------------------------------
+// scheduler
+// ---------------------------------------------------------------------------
+static const uint8_t* rec_ptr(lsn_ctx* c, size_t idx) {
+  if (c->cfg.mode == LSN_RESIDENT) return c->records + (uint64_t)c->order[idx] * c->rec_bytes;
+  return c->records + (uint64_t)c->slot_of[idx] * c->rec_bytes;
+}
+
+static lsn_status copy_into_slot(lsn_ctx* c, int layer, int s) {
+  uint8_t* dst = c->records + (uint64_t)s * c->rec_bytes;
+  if (c->slot_used[s]) HIPCHK(c, hipStreamWaitEvent(c->copy, c->slot_free[s], 0));
+  const uint8_t* src;
+  if (c->cfg.mode == LSN_STREAM_FILE) {
+    // the bounce buffer of this slot is free once its previous copy finished
+    if (c->copy_issued[s]) HIPCHK(c, hipEventSynchronize(c->copy_done[s]));
+    uint64_t done = 0;
+    const uint64_t off = (uint64_t)layer * c->rec_bytes;
+    while (done < c->rec_bytes) {
+      const ssize_t got = pread(c->fd, c->bounce[s] + done, c->rec_bytes - done, off + done);
+      if (got <= 0)
+        return fail(c, LSN_ERR_IO, "read of layer %d record failed: %s", layer,
+                    got == 0 ? "unexpected end of file" : strerror(errno));
+      done += (uint64_t)got;
+    }
+    src = c->bounce[s];
+  } else {
+    src = c->store + (uint64_t)layer * c->rec_bytes;
+  }
+  HIPCHK(c, hipMemcpyAsync(dst, src, c->rec_bytes, hipMemcpyHostToDevice, c->copy));
+  HIPCHK(c, hipEventRecord(c->copy_done[s], c->copy));
+  c->copy_issued[s] = true;
+  c->slot_layer[s] = layer;
+  c->loads += 1;
+  c->bytes_h2d += c->rec_bytes;
+  return LSN_OK;
+}
+
+// Makes sure the records for pass positions pos and pos+1 are in a slot or
+// on their way.
+static lsn_status ensure_loads(lsn_ctx* c) {
+  if (c->cfg.mode == LSN_RESIDENT) return LSN_OK;
+  const size_t end = std::min(c->order.size(), c->pos + 2);
+  for (size_t i = c->pos; i < end; ++i) {
+    if (c->slot_of[i] >= 0) continue;
+    const int layer = c->order[i];
+    int s = -1;
+    for (int q = 0; q < 2; ++q)
+      if (c->slot_layer[q] == layer) s = q;
+    if (s < 0) {
+      // a slot not holding the record of any other position in the window
+      for (int q = 0; q < 2 && s < 0; ++q) {
+        bool needed = false;
+        for (size_t j = c->pos; j < end; ++j)
+          if (j != i && (c->slot_of[j] == q || (c->slot_of[j] < 0 && c->slot_layer[q] == c->order[j])))
+            needed = true;
+        if (!needed) s = q;
+      }
+      if (s < 0) return fail(c, LSN_ERR_STATE, "scheduler found no free slot");
+      lsn_status st = copy_into_slot(c, layer, s);
+      if (st != LSN_OK) return st;
+    }
+    c->slot_of[i] = s;
+  }
+  return LSN_OK;
+}
+
+static lsn_status layer_begin(lsn_ctx* c, int kind, int layer, const uint8_t** rec) {
+  if (c->pass_kind != kind) return fail(c, LSN_ERR_STATE, "layer call outside a matching pass");
+  if (c->pos >= c->order.size() || c->order[c->pos] != layer)
+    return fail(c, LSN_ERR_STATE, "layer %d out of order (expected %d)", layer,
+                c->pos < c->order.size() ? c->order[c->pos] : -1);
+  if (!c->loaded[layer]) return fail(c, LSN_ERR_STATE, "layer %d was never loaded", layer);
+  lsn_status st = ensure_loads(c);
+  if (st != LSN_OK) return st;
+  if (c->cfg.mode != LSN_RESIDENT)
+    HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_done[c->slot_of[c->pos]], 0));
+  *rec = rec_ptr(c, c->pos);
+  return LSN_OK;
+}
+
+static lsn_status layer_end(lsn_ctx* c) {
+  if (c->cfg.mode != LSN_RESIDENT) {
+    const int s = c->slot_of[c->pos];
+    HIPCHK(c, hipEventRecord(c->slot_free[s], c->cs));
+    c->slot_used[s] = true;
+  }
+  c->pos += 1;
+  lsn_status st = ensure_loads(c);
+  if (st != LSN_OK) return st;
+  return launch_check(c);
+}
+
+// ---------------------------------------------------------------------------
+// GEMM helpers
+// ---------------------------------------------------------------------------
+static GemmParams base_params(const lsn_ctx* c) {
+  GemmParams p;
+  memcpy(p.levels, c->levels, sizeof p.levels);
+  return p;
+}
+
+// projections sharing one GEMM: q|k|v, o, gate|up, down
+struct Group {
+  int first, count;
+};
+static const Group G_QKV{LSN_Q, 3}, G_O{LSN_O, 1}, G_GU{LSN_GATE, 2}, G_D{LSN_DOWN, 1};
+
+static int64_t group_rows(const lsn_ctx* c, Group g) {
+  int64_t n = 0;
+  for (int p = g.first; p < g.first + g.count; ++p) n += c->N[p];
+  return n;
+}
+
+// Forward low-rank extension of a group: t_p = x A_p (kept in lt[p]),
+// aext = bf16(s t_p) per adapted slot, bext = block layout of B_p^T.
+// Returns kext (0 when no adapter applies).
+static int lora_fwd_ext(lsn_ctx* c, int layer, Group g, const uint16_t* x, int64_t ldx, int T) {
+  if (!c->adapters_on) return 0;
+  int nad = 0;
+  for (int p = g.first; p < g.first + g.count; ++p) nad += c->targeted(p);
+  if (!nad) return 0;
+  const int r = c->cfg.lora_rank, kext = 16 * nad;
+  const float s = c->lora_scale();
+  const int64_t rows = group_rows(c, g);
+  // rows of one projection are zero in the other projections' slots
+  if (g.count > 1) fill_u32(c->bext, 0, rows * kext / 2, c->cs);
+  int slot = 0;
+  int64_t row0 = 0;
+  for (int p = g.first; p < g.first + g.count; ++p) {
+    if (c->targeted(p)) {
+      const int64_t K = c->K[p], N = c->N[p];
+      skinny_bf16(x, ldx, c->A_of(layer, p), r, 1, T, (int)K, r, c->lt + (int64_t)p * T * 16,
+                  c->aext + 16 * slot, kext, s, c->cs);
+      lora_ext(c->B_of(layer, p), 1, N, (int)N, r, c->bext + row0 * kext, kext, 16 * slot, c->cs);
+      ++slot;
+    }
+    row0 += c->N[p];
+  }
+  return kext;
+}
+
+// Backward of the low-rank branches of a group.  dyf: fp32 gradient of the
+// group's fused output [T, rows] (row stride lddy); x: forward input [T, K].
+// Adds dA, dB; prepares aext = bf16(s u_p), bext = A_p (bf16) for dX.
+static int lora_bwd_ext(lsn_ctx* c, int layer, Group g, const float* dyf, int64_t lddy,
+                        const uint16_t* x, int64_t ldx, int T) {
+  int nad = 0;
+  for (int p = g.first; p < g.first + g.count; ++p) nad += c->targeted(p);
+  if (!nad) return 0;
+  const int r = c->cfg.lora_rank, kext = 16 * nad;
+  const float s = c->lora_scale();
+  int slot = 0;
+  int64_t col0 = 0;
+  for (int p = g.first; p < g.first + g.count; ++p) {
+    if (c->targeted(p)) {
+      const int64_t K = c->K[p], N = c->N[p];
+      const float* dy = dyf + col0;
+      // u = dy B^T : W(k = n, j) = B[j*N + n]
+      skinny_f32(dy, lddy, c->B_of(layer, p), 1, N, T, (int)N, r, c->lu, c->aext + 16 * slot,
+                 kext, s, c->cs);
+      lora_dA_bf16(x, ldx, c->lu, T, (int)K, r, s, c->dA_of(layer, p), c->cs);
+      lora_dB_f32(c->lt + (int64_t)p * T * 16, dy, lddy, T, (int)N, r, s, c->dB_of(layer, p),
+                  c->cs);
+      lora_ext(c->A_of(layer, p), r, 1, (int)K, r, c->bext, kext, 16 * slot, c->cs);
+      ++slot;
+    }
+    col0 += c->N[p];
+  }
+  return kext;
+}
+
+static hipError_t nf4_fwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const uint16_t* x, int T,
+                               int kext, void* out, int cmode, const float* res) {
+  GemmParams p = base_params(c);
+  const int pf = g.first;
+  p.M = T;
+  p.N = (int)group_rows(c, g);
+  p.K = (int)c->K[pf];
+  p.A = x;
+  p.lda = c->K[pf];
+  p.B = rec + c->code_off[pf];
+  p.absmax = reinterpret_cast<const float*>(rec + c->amax_off[pf]);
+  p.rowlen = c->K[pf];
+  p.C = out;
+  p.ldc = p.N;
+  p.cmode = cmode;
+  p.R = res;
+  p.ldr = p.N;
+  if (kext) {
+    p.Aext = c->aext;
+    p.ldae = kext;
+    p.Bext = c->bext;
+    p.ldbe = kext;
+    p.kext = kext;
+  }
+  return gemm(p, A_BF16_K, B_NF4_K, 1, c->cs);
+}
+
+// dX = dY W_group (+ low-rank extension); dY is fp32 (opa A_F32_K) or bf16.
+static hipError_t nf4_bwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const void* dy, int opa,
+                               int T, int kext, void* out, int cmode) {
+  GemmParams p = base_params(c);
+  const int pf = g.first;
+  p.M = T;
+  p.N = (int)c->K[pf];
+  p.K = (int)group_rows(c, g);
+  p.A = dy;
+  p.lda = p.K;
+  p.B = rec + c->code_off[pf];
+  p.absmax = reinterpret_cast<const float*>(rec + c->amax_off[pf]);
+  p.rowlen = c->K[pf];
+  p.C = out;
+  p.ldc = p.N;
+  p.cmode = cmode;
+  if (kext) {
+    p.Aext = c->aext;
+    p.ldae = kext;
+    p.Bext = c->bext;
+    p.ldbe = kext;
+    p.kext = kext;
+  }
+  return gemm(p, opa, B_NF4_R, 1, c->cs);
+}
+
+// ---------------------------------------------------------------------------
+// one decoder layer
+// ---------------------------------------------------------------------------
+static lsn_status layer_forward(lsn_ctx* c, int layer, const uint8_t* rec, const float* h,
+                                float* out, bool final_residual) {
+  const lsn_config& g = c->cfg;
+  const int T = c->T, S = c->seq_len, H = g.hidden, F = g.ffn, d = g.head_dim;
+  const int nq = g.n_heads, nkv = g.n_kv_heads, grp = nq / nkv;
+  const int QKV = c->QKV, QD = c->QD, KVD = c->KVD;
+  const uint16_t* g1 = reinterpret_cast<const uint16_t*>(rec + c->norm_off[0]);
+  const uint16_t* g2 = reinterpret_cast<const uint16_t*>(rec + c->norm_off[1]);
+  hipStream_t s = c->cs;
+
+  rmsnorm_fwd(h, g1, T, H, g.rms_eps, c->n1, c->rstd1, s);
+  int kext = lora_fwd_ext(c, layer, G_QKV, c->n1, H, T);
+  HIPCHK(c, nf4_fwd_gemm(c, rec, G_QKV, c->n1, T, kext, c->qkv, C_F32, nullptr));
+  rope_fwd(c->qkv, c->qkvb, T, S, nq, nkv, d, g.rope_theta, s);
+
+  // attention: scores = q k^T / sqrt(d) per (sequence, head)
+  {
+    GemmParams p = base_params(c);
+    p.M = S; p.N = S; p.K = d;
+    p.A = c->qkvb; p.lda = QKV;
+    p.B = c->qkvb + QD; p.ldb = QKV;
+    p.zdiv = nq; p.grpB = grp;
+    p.sA_o = (int64_t)S * QKV; p.sA_i = d;
+    p.sB_o = (int64_t)S * QKV; p.sB_i = d;
+    p.C = c->scores; p.ldc = S;
+    p.sC_o = (int64_t)nq * S * S; p.sC_i = (int64_t)S * S;
+    p.alpha = 1.0f / sqrtf((float)d);
+    HIPCHK(c, gemm(p, A_BF16_K, B_BF16_K, c->n_seq * nq, s));
+  }
+  softmax_causal(c->scores, c->Pf, c->Pb, S, (int64_t)c->n_seq * nq * S, s);
+  {  // O = P V
+    GemmParams p = base_params(c);
+    p.M = S; p.N = d; p.K = S;
+    p.A = c->Pb; p.lda = S;
+    p.B = c->qkvb + QD + KVD; p.ldb = QKV;
+    p.zdiv = nq; p.grpB = grp;
+    p.sA_o = (int64_t)nq * S * S; p.sA_i = (int64_t)S * S;
+    p.sB_o = (int64_t)S * QKV; p.sB_i = d;
+    p.C = c->O; p.ldc = QD; p.cmode = C_BF16;
+    p.sC_o = (int64_t)S * QD; p.sC_i = d;
+    HIPCHK(c, gemm(p, A_BF16_K, B_BF16_R, c->n_seq * nq, s));
+  }
+  kext = lora_fwd_ext(c, layer, G_O, c->O, QD, T);
+  HIPCHK(c, nf4_fwd_gemm(c, rec, G_O, c->O, T, kext, c->h2, C_F32_RES, h));
+  rmsnorm_fwd(c->h2, g2, T, H, g.rms_eps, c->n2, c->rstd2, s);
+  kext = lora_fwd_ext(c, layer, G_GU, c->n2, H, T);
+  HIPCHK(c, nf4_fwd_gemm(c, rec, G_GU, c->n2, T, kext, c->gu, C_F32, nullptr));
+  swiglu_fwd(c->gu, c->a, T, F, s);
+  kext = lora_fwd_ext(c, layer, G_D, c->a, F, T);  // also keeps t of down for backward
+  if (final_residual)
+    HIPCHK(c, nf4_fwd_gemm(c, rec, G_D, c->a, T, kext, out, C_F32_RES, c->h2));
+  return launch_check(c);
+}
+
+static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, const float* h,
+                                 const float* dout, float* dh) {
+  const lsn_config& g = c->cfg;
+  const int T = c->T, S = c->seq_len, H = g.hidden, F = g.ffn, d = g.head_dim;
+  const int nq = g.n_heads, nkv = g.n_kv_heads, grp = nq / nkv;
+  const int QKV = c->QKV, QD = c->QD, KVD = c->KVD;
+  const uint16_t* g1 = reinterpret_cast<const uint16_t*>(rec + c->norm_off[0]);
+  const uint16_t* g2 = reinterpret_cast<const uint16_t*>(rec + c->norm_off[1]);
+  hipStream_t s = c->cs;
+
+  // recompute the forward activations of this layer (adapters on)
+  lsn_status st = layer_forward(c, layer, rec, h, nullptr, false);
+  if (st != LSN_OK) return st;
+
+  // MLP: out = h2 + down(silu(gate) * up)
+  int kext = lora_bwd_ext(c, layer, G_D, dout, H, c->a, F, T);
+  HIPCHK(c, nf4_bwd_gemm(c, rec, G_D, dout, A_F32_K, T, kext, c->da, C_F32));
+  const bool gu_ad = c->targeted(LSN_GATE) || c->targeted(LSN_UP);
+  swiglu_bwd(c->gu, c->da, c->dgu, gu_ad ? c->dguf : nullptr, T, F, s);
+  kext = lora_bwd_ext(c, layer, G_GU, c->dguf, 2 * F, c->n2, H, T);
+  HIPCHK(c, nf4_bwd_gemm(c, rec, G_GU, c->dgu, A_BF16_K, T, kext, c->dn, C_F32));
+  rmsnorm_bwd(c->h2, g2, c->rstd2, c->dn, dout, T, H, c->dh2, s);
+
+  // attention block: h2 = h + o(attn(rope(q), rope(k), v))
+  kext = lora_bwd_ext(c, layer, G_O, c->dh2, H, c->O, QD, T);
+  HIPCHK(c, nf4_bwd_gemm(c, rec, G_O, c->dh2, A_F32_K, T, kext, c->dO, C_BF16));
+  const int Z = c->n_seq * nq;
+  {  // dP = dO V^T
+    GemmParams p = base_params(c);
+    p.M = S; p.N = S; p.K = d;
+    p.A = c->dO; p.lda = QD;
+    p.B = c->qkvb + QD + KVD; p.ldb = QKV;
+    p.zdiv = nq; p.grpB = grp;
+    p.sA_o = (int64_t)S * QD; p.sA_i = d;
+    p.sB_o = (int64_t)S * QKV; p.sB_i = d;
+    p.C = c->scores; p.ldc = S;
+    p.sC_o = (int64_t)nq * S * S; p.sC_i = (int64_t)S * S;
+    HIPCHK(c, gemm(p, A_BF16_K, B_BF16_K, Z, s));
+  }
+  {  // dV[kv] = sum over its q heads of P^T dO
+    GemmParams p = base_params(c);
+    p.M = S; p.N = d; p.K = S;
+    p.A = c->Pb; p.lda = S;
+    p.B = c->dO; p.ldb = QD;
+    p.zdiv = nkv; p.grpB = 1;
+    p.sA_o = (int64_t)nq * S * S; p.sA_i = (int64_t)grp * S * S; p.sA_seg = (int64_t)S * S;
+    p.sB_o = (int64_t)S * QD; p.sB_i = (int64_t)grp * d; p.sB_seg = d;
+    p.nseg = grp;
+    p.C = c->dqkv + QD + KVD; p.ldc = QKV;
+    p.sC_o = (int64_t)S * QKV; p.sC_i = d;
+    HIPCHK(c, gemm(p, A_BF16_R, B_BF16_R, c->n_seq * nkv, s));
+  }
+  softmax_bwd(c->Pf, c->scores, c->Pb, S, (int64_t)Z * S, s);  // dS (bf16) over Pb
+  const float scale = 1.0f / sqrtf((float)d);
+  {  // dQ = scale dS K
+    GemmParams p = base_params(c);
+    p.M = S; p.N = d; p.K = S;
+    p.A = c->Pb; p.lda = S;
+    p.B = c->qkvb + QD; p.ldb = QKV;
+    p.zdiv = nq; p.grpB = grp;
+    p.sA_o = (int64_t)nq * S * S; p.sA_i = (int64_t)S * S;
+    p.sB_o = (int64_t)S * QKV; p.sB_i = d;
+    p.C = c->dqkv; p.ldc = QKV;
+    p.sC_o = (int64_t)S * QKV; p.sC_i = d;
+    p.alpha = scale;
+    HIPCHK(c, gemm(p, A_BF16_K, B_BF16_R, Z, s));
+  }
+  {  // dK[kv] = scale sum over its q heads of dS^T Q
+    GemmParams p = base_params(c);
+    p.M = S; p.N = d; p.K = S;
+    p.A = c->Pb; p.lda = S;
+    p.B = c->qkvb; p.ldb = QKV;
+    p.zdiv = nkv; p.grpB = 1;
+    p.sA_o = (int64_t)nq * S * S; p.sA_i = (int64_t)grp * S * S; p.sA_seg = (int64_t)S * S;
+    p.sB_o = (int64_t)S * QKV; p.sB_i = (int64_t)grp * d; p.sB_seg = d;
+    p.nseg = grp;
+    p.C = c->dqkv + QD; p.ldc = QKV;
+    p.sC_o = (int64_t)S * QKV; p.sC_i = d;
+    p.alpha = scale;
+    HIPCHK(c, gemm(p, A_BF16_R, B_BF16_R, c->n_seq * nkv, s));
+  }
+  rope_bwd(c->dqkv, c->dqkvb, T, S, nq, nkv, d, g.rope_theta, s);
+  kext = lora_bwd_ext(c, layer, G_QKV, c->dqkv, QKV, c->n1, H, T);
+  HIPCHK(c, nf4_bwd_gemm(c, rec, G_QKV, c->dqkvb, A_BF16_K, T, kext, c->dn, C_F32));
+  rmsnorm_bwd(h, g1, c->rstd1, c->dn, c->dh2, T, H, dh, s);
+  return launch_check(c);
+}
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+lsn_status lsn_nf4_codebook(float* out16) {
+  if (!out16) return LSN_ERR_INVALID;
+  nf4_levels(out16);
+  return LSN_OK;
+}
+
+lsn_status lsn_nf4_quantize(const float* w, uint64_t n, uint8_t* codes, float* absmax) {
+  if (!w || !codes || !absmax) return n == 0 ? LSN_OK : LSN_ERR_INVALID;
+  return nf4_quantize(w, n, codes, absmax) ? LSN_OK : LSN_ERR_INVALID;
+}
+
+lsn_status lsn_nf4_dequantize_host(const uint8_t* codes, const float* absmax, uint64_t n,
+                                   float* w) {
+  if (!codes || !absmax || !w) return n == 0 ? LSN_OK : LSN_ERR_INVALID;
+  nf4_dequantize_host(codes, absmax, n, w);
+  return LSN_OK;
+}
+
+lsn_status lsn_nf4_dequant(const uint8_t* codes, const float* absmax, uint64_t n, void* out,
+                           int32_t out_bf16, void* hip_stream) {
+  if (n == 0) return LSN_OK;
+  if (!codes || !absmax || !out || n % 8) return LSN_ERR_INVALID;
+  float lv[16];
+  nf4_levels(lv);
+  nf4_dequant(codes, absmax, (int64_t)n, lv, out_bf16 ? nullptr : (float*)out,
+              out_bf16 ? (uint16_t*)out : nullptr, (hipStream_t)hip_stream);
+  return hipGetLastError() == hipSuccess ? LSN_OK : LSN_ERR_HIP;
+}
+
+// scratch of the stateless projection: t/u fp32 [M,16], aext bf16 [M,16],
+// bext bf16 [max(N,K),16]
+lsn_status lsn_nf4_linear_scratch_bytes(int32_t M, int32_t K, int32_t N, int32_t r,
+                                        uint64_t* bytes) {
+  if (!bytes || M < 0 || K <= 0 || N <= 0 || r < 0 || r > 16) return LSN_ERR_INVALID;
+  *bytes = align_up((uint64_t)M * 16 * 4, 256) * 2 + align_up((uint64_t)M * 16 * 2, 256) +
+           align_up((uint64_t)std::max(N, K) * 16 * 2, 256);
+  return LSN_OK;
+}
+
+static lsn_status linear_args_ok(const uint8_t* codes, const float* absmax, int32_t M, int32_t K,
+                                 int32_t N, const void* X, const float* A, const float* B,
+                                 int32_t r, void* scratch, uint64_t sb) {
+  if (!codes || !absmax || !X || M < 0 || K <= 0 || N <= 0) return LSN_ERR_INVALID;
+  if (K % 16 || N % 8) return LSN_ERR_INVALID;
+  if (r < 0 || r > 16) return LSN_ERR_INVALID;
+  if (r > 0 && (!A || !B)) return LSN_ERR_INVALID;
+  uint64_t need = 0;
+  lsn_nf4_linear_scratch_bytes(M, K, N, r, &need);
+  if (r > 0 && (!scratch || sb < need)) return LSN_ERR_INVALID;
+  return LSN_OK;
+}
+
+lsn_status lsn_nf4_linear_fwd(const uint8_t* codes, const float* absmax, int32_t M, int32_t K,
+                              int32_t N, const uint16_t* X, const float* A, const float* B,
+                              int32_t r, float s, float* Y, void* scratch, uint64_t sb,
+                              void* hip_stream) {
+  lsn_status st = linear_args_ok(codes, absmax, M, K, N, X, A, B, r, scratch, sb);
+  if (st != LSN_OK || !Y) return st != LSN_OK ? st : LSN_ERR_INVALID;
+  if (M == 0) return LSN_OK;
+  hipStream_t hs = (hipStream_t)hip_stream;
+  char* sc = (char*)scratch;
+  float* t = (float*)sc;
+  uint16_t* aext = (uint16_t*)(sc + align_up((uint64_t)M * 16 * 4, 256) * 2);
+  uint16_t* bext = (uint16_t*)((char*)aext + align_up((uint64_t)M * 16 * 2, 256));
+  GemmParams p;
+  nf4_levels(p.levels);
+  p.M = M; p.N = N; p.K = K;
+  p.A = X; p.lda = K;
+  p.B = codes; p.absmax = absmax; p.rowlen = K;
+  p.C = Y; p.ldc = N;
+  if (r > 0) {
+    skinny_bf16(X, K, A, r, 1, M, K, r, t, aext, 16, s, hs);
+    lora_ext(B, 1, N, N, r, bext, 16, 0, hs);
+    p.Aext = aext; p.ldae = 16; p.Bext = bext; p.ldbe = 16; p.kext = 16;
+  }
+  return gemm(p, A_BF16_K, B_NF4_K, 1, hs) == hipSuccess && hipGetLastError() == hipSuccess
+             ? LSN_OK
+             : LSN_ERR_HIP;
+}
+
+lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t M, int32_t K,
+                              int32_t N, const uint16_t* X, const float* A, const float* B,
+                              int32_t r, float s, const uint16_t* dY, float* dX, float* dA,
+                              float* dB, void* scratch, uint64_t sb, void* hip_stream) {
+  lsn_status st = linear_args_ok(codes, absmax, M, K, N, X, A, B, r, scratch, sb);
+  if (st != LSN_OK) return st;
+  if (!dY || !dX || (r > 0 && (!dA || !dB))) return LSN_ERR_INVALID;
+  hipStream_t hs = (hipStream_t)hip_stream;
+  if (r > 0) {
+    fill_u32(dA, 0, (int64_t)K * r, hs);
+    fill_u32(dB, 0, (int64_t)r * N, hs);
+  }
+  if (M == 0) {
+    return hipGetLastError() == hipSuccess ? LSN_OK : LSN_ERR_HIP;
+  }
+  char* sc = (char*)scratch;
+  float* t = (float*)sc;
+  float* u = (float*)(sc + align_up((uint64_t)M * 16 * 4, 256));
+  uint16_t* aext = (uint16_t*)(sc + align_up((uint64_t)M * 16 * 4, 256) * 2);
+  uint16_t* bext = (uint16_t*)((char*)aext + align_up((uint64_t)M * 16 * 2, 256));
+  GemmParams p;
+  nf4_levels(p.levels);
+  p.M = M; p.N = K; p.K = N;
+  p.A = dY; p.lda = N;
+  p.B = codes; p.absmax = absmax; p.rowlen = K;
+  p.C = dX; p.ldc = K;
+  if (r > 0) {
+    skinny_bf16(X, K, A, r, 1, M, K, r, t, nullptr, 0, s, hs);          // t = X A
+    skinny_bf16(dY, N, B, 1, N, M, N, r, u, aext, 16, s, hs);           // u = dY B^T
+    lora_dA_bf16(X, K, u, M, K, r, s, dA, hs);                          // dA = s X^T u
+    lora_dB_bf16(t, dY, N, M, N, r, s, dB, hs);                         // dB = s t^T dY
+    lora_ext(A, r, 1, K, r, bext, 16, 0, hs);                           // bext = A
+    p.Aext = aext; p.ldae = 16; p.Bext = bext; p.ldbe = 16; p.kext = 16;
+  }
+  return gemm(p, A_BF16_K, B_NF4_R, 1, hs) == hipSuccess && hipGetLastError() == hipSuccess
+             ? LSN_OK
+             : LSN_ERR_HIP;
+}
+
+lsn_status lsn_workspace_bytes(const lsn_config* cfg, uint64_t* bytes) {
+  std::string why;
+  if (!bytes || !cfg_valid(cfg, &why)) return LSN_ERR_INVALID;
+  lsn_ctx tmp;
+  tmp.cfg = *cfg;
+  record_layout(&tmp);
+  *bytes = carve(&tmp, nullptr);
+  return LSN_OK;
+}
+
+lsn_status lsn_create(const lsn_config* cfg, void* dev_ws, uint64_t ws_bytes, void* hip_stream,
+                      lsn_ctx** out) {
+  std::string why;
+  if (!out) return LSN_ERR_INVALID;
+  *out = nullptr;
+  if (!cfg_valid(cfg, &why)) return LSN_ERR_INVALID;
+  lsn_ctx* c = new lsn_ctx();
+  c->cfg = *cfg;
+  if (cfg->store_path) c->store_path = cfg->store_path;
+  c->cfg.store_path = c->store_path.c_str();
+  record_layout(c);
+  c->ws_needed = carve(c, nullptr);
+  if (!dev_ws || ws_bytes < c->ws_needed || (cfg->vram_budget && c->ws_needed > cfg->vram_budget)) {
+    delete c;
+    return LSN_ERR_NOFIT;
+  }
+  c->ws = (char*)dev_ws;
+  c->ws_bytes = ws_bytes;
+  carve(c, c->ws);
+  c->cs = (hipStream_t)hip_stream;
+  nf4_levels(c->levels);
+  c->loaded.assign(cfg->n_layers, 0);
+  auto cleanup = [&](lsn_status st) {
+    lsn_destroy(c);
+    return st;
+  };
+  if (hipGetDevice(&c->device) != hipSuccess) return cleanup(LSN_ERR_HIP);
+  if (hipStreamCreateWithFlags(&c->copy, hipStreamNonBlocking) != hipSuccess)
+    return cleanup(LSN_ERR_HIP);
+  for (int i = 0; i < 2; ++i)
+    if (hipEventCreateWithFlags(&c->copy_done[i], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c->slot_free[i], hipEventDisableTiming) != hipSuccess)
+      return cleanup(LSN_ERR_HIP);
+  if (cfg->mode == LSN_STREAM_FILE) {
+    c->fd = open(c->store_path.c_str(), O_RDWR | O_CREAT, 0644);
+    if (c->fd < 0) return cleanup(LSN_ERR_IO);
+    for (int i = 0; i < 2; ++i)
+      if (hipHostMalloc((void**)&c->bounce[i], c->rec_bytes, hipHostMallocDefault) != hipSuccess)
+        return cleanup(LSN_ERR_HIP);
+  } else {
+    if (hipHostMalloc((void**)&c->store, (uint64_t)cfg->n_layers * c->rec_bytes,
+                      hipHostMallocDefault) != hipSuccess)
+      return cleanup(LSN_ERR_HIP);
+  }
+  // adapters start at zero (A and B); gradients at zero
+  fill_u32(c->lora_p, 0, (int64_t)c->lora_n, c->cs);
+  fill_u32(c->lora_g, 0, (int64_t)c->lora_n, c->cs);
+  if (hipGetLastError() != hipSuccess || hipStreamSynchronize(c->cs) != hipSuccess)
+    return cleanup(LSN_ERR_HIP);
+  *out = c;
+  return LSN_OK;
+}
+
+void lsn_destroy(lsn_ctx* c) {
+  if (!c) return;
+  // teardown: errors here have nowhere to go
+  if (c->copy) (void)hipStreamSynchronize(c->copy);
+  (void)hipStreamSynchronize(c->cs);
+  for (int i = 0; i < 2; ++i) {
+    if (c->copy_done[i]) (void)hipEventDestroy(c->copy_done[i]);
+    if (c->slot_free[i]) (void)hipEventDestroy(c->slot_free[i]);
+    if (c->bounce[i]) (void)hipHostFree(c->bounce[i]);
+  }
+  if (c->copy) (void)hipStreamDestroy(c->copy);
+  if (c->store) (void)hipHostFree(c->store);
+  if (c->fd >= 0) close(c->fd);
+  delete c;
+}
+
+const char* lsn_last_error(const lsn_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+lsn_status lsn_sync(lsn_ctx* c) {
+  if (!c) return LSN_ERR_INVALID;
+  if (c->poisoned) return LSN_ERR_STATE;
+  HIPCHK(c, hipStreamSynchronize(c->copy));
+  HIPCHK(c, hipStreamSynchronize(c->cs));
+  HIPCHK(c, hipGetLastError());
+  return LSN_OK;
+}
+
+lsn_status lsn_record_bytes(const lsn_ctx* c, uint64_t* bytes) {
+  if (!c || !bytes) return LSN_ERR_INVALID;
+  *bytes = c->rec_bytes;
+  return LSN_OK;
+}
+
+lsn_status lsn_load_layer_nf4(lsn_ctx* c, int32_t layer, const uint8_t* const* codes,
+                              const float* const* absmax, const uint16_t* attn_norm,
+                              const uint16_t* mlp_norm) {
+  CHECK_CTX(c);
+  if (layer < 0 || layer >= c->cfg.n_layers || !codes || !absmax || !attn_norm || !mlp_norm)
+    return fail(c, LSN_ERR_INVALID, "bad lsn_load_layer_nf4 arguments");
+  for (int p = 0; p < NPROJ; ++p)
+    if (!codes[p] || !absmax[p]) return fail(c, LSN_ERR_INVALID, "null projection %d", p);
+  std::vector<uint8_t> tmp;
+  uint8_t* rec;
+  if (c->cfg.mode == LSN_STREAM_FILE) {
+    tmp.assign(c->rec_bytes, 0);
+    rec = tmp.data();
+  } else {
+    rec = c->store + (uint64_t)layer * c->rec_bytes;
+    memset(rec, 0, c->rec_bytes);
+  }
+  for (int p = 0; p < NPROJ; ++p) {
+    const uint64_t n = (uint64_t)c->N[p] * c->K[p];
+    memcpy(rec + c->code_off[p], codes[p], n / 2);
+    memcpy(rec + c->amax_off[p], absmax[p], n / 64 * 4);
+  }
+  const int H = c->cfg.hidden;
+  memcpy(rec + c->norm_off[0], attn_norm, H * 2);
+  memcpy(rec + c->norm_off[1], mlp_norm, H * 2);
+  if (c->cfg.mode == LSN_STREAM_FILE) {
+    uint64_t done = 0;
+    const uint64_t off = (uint64_t)layer * c->rec_bytes;
+    while (done < c->rec_bytes) {
+      const ssize_t w = pwrite(c->fd, rec + done, c->rec_bytes - done, off + done);
+      if (w <= 0) return fail(c, LSN_ERR_IO, "write of layer %d record failed", layer);
+      done += (uint64_t)w;
+    }
+  } else if (c->cfg.mode == LSN_RESIDENT) {
+    HIPCHK(c, hipMemcpyAsync(c->records + (uint64_t)layer * c->rec_bytes, rec, c->rec_bytes,
+                             hipMemcpyHostToDevice, c->cs));
+    HIPCHK(c, hipStreamSynchronize(c->cs));
+  }
+  // a slot holding an older copy of this layer is stale now
+  for (int s = 0; s < 2; ++s)
+    if (c->slot_layer[s] == layer) c->slot_layer[s] = -1;
+  c->loaded[layer] = 1;
+  return LSN_OK;
+}
+
+lsn_status lsn_load_head(lsn_ctx* c, const uint16_t* embed, const uint16_t* lm_head,
+                         const uint16_t* final_norm) {
+  CHECK_CTX(c);
+  if (!embed || !final_norm || (!c->cfg.tied_embeddings && !lm_head))
+    return fail(c, LSN_ERR_INVALID, "bad lsn_load_head arguments");
+  const uint64_t vb = (uint64_t)c->cfg.vocab * c->cfg.hidden * 2;
+  HIPCHK(c, hipMemcpy(c->embed, embed, vb, hipMemcpyHostToDevice));
+  if (!c->cfg.tied_embeddings) HIPCHK(c, hipMemcpy(c->lm_head, lm_head, vb, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->final_norm, final_norm, (uint64_t)c->cfg.hidden * 2,
+                      hipMemcpyHostToDevice));
+  c->head_loaded = true;
+  return LSN_OK;
+}
+
+lsn_status lsn_set_lora(lsn_ctx* c, int32_t layer, int32_t proj, const float* A, const float* B) {
+  CHECK_CTX(c);
+  if (layer < 0 || layer >= c->cfg.n_layers || proj < 0 || proj >= NPROJ || !c->targeted(proj))
+    return fail(c, LSN_ERR_INVALID, "no adapter at layer %d projection %d", layer, proj);
+  const int r = c->cfg.lora_rank;
+  HIPCHK(c, hipStreamSynchronize(c->cs));
+  if (A) HIPCHK(c, hipMemcpy(c->A_of(layer, proj), A, (uint64_t)c->K[proj] * r * 4, hipMemcpyHostToDevice));
+  if (B) HIPCHK(c, hipMemcpy(c->B_of(layer, proj), B, (uint64_t)r * c->N[proj] * 4, hipMemcpyHostToDevice));
+  return LSN_OK;
+}
+
+lsn_status lsn_get_lora(lsn_ctx* c, int32_t layer, int32_t proj, float* A, float* B, float* dA,
+                        float* dB) {
+  CHECK_CTX(c);
+  if (layer < 0 || layer >= c->cfg.n_layers || proj < 0 || proj >= NPROJ || !c->targeted(proj))
+    return fail(c, LSN_ERR_INVALID, "no adapter at layer %d projection %d", layer, proj);
+  const int r = c->cfg.lora_rank;
+  const uint64_t na = (uint64_t)c->K[proj] * r * 4, nbb = (uint64_t)r * c->N[proj] * 4;
+  HIPCHK(c, hipStreamSynchronize(c->cs));
+  if (A) HIPCHK(c, hipMemcpy(A, c->A_of(layer, proj), na, hipMemcpyDeviceToHost));
+  if (B) HIPCHK(c, hipMemcpy(B, c->B_of(layer, proj), nbb, hipMemcpyDeviceToHost));
+  if (dA) HIPCHK(c, hipMemcpy(dA, c->dA_of(layer, proj), na, hipMemcpyDeviceToHost));
+  if (dB) HIPCHK(c, hipMemcpy(dB, c->dB_of(layer, proj), nbb, hipMemcpyDeviceToHost));
+  return LSN_OK;
+}
+
+lsn_status lsn_set_adapter_enabled(lsn_ctx* c, int32_t enabled) {
+  CHECK_CTX(c);
+  c->adapters_on = enabled != 0;
+  return LSN_OK;
+}
+
+lsn_status lsn_zero_grads(lsn_ctx* c) {
+  CHECK_CTX(c);
+  fill_u32(c->lora_g, 0, (int64_t)c->lora_n, c->cs);
+  return launch_check(c);
+}
+
+lsn_status lsn_sgd_step(lsn_ctx* c, float lr) {
+  CHECK_CTX(c);
+  if (!std::isfinite(lr)) return fail(c, LSN_ERR_INVALID, "non-finite learning rate");
+  if (c->lora_n) sgd(c->lora_p, c->lora_g, lr, (int64_t)c->lora_n, c->cs);
+  return launch_check(c);
+}
+
+lsn_status lsn_begin_pass(lsn_ctx* c, int32_t kind, int32_t n_seq, int32_t seq_len) {
+  CHECK_CTX(c);
+  if ((kind != LSN_PASS_FWD && kind != LSN_PASS_BWD) || n_seq <= 0 || seq_len <= 0 ||
+      seq_len % 8 || seq_len > c->cfg.max_seq_len ||
+      (int64_t)n_seq * seq_len > c->cfg.max_tokens)
+    return fail(c, LSN_ERR_INVALID, "bad pass (kind %d, %d x %d)", kind, n_seq, seq_len);
+  if (kind == LSN_PASS_BWD && !c->adapters_on)
+    return fail(c, LSN_ERR_STATE, "backward needs the adapters enabled");
+  const int L = c->cfg.n_layers;
+  c->pass_kind = kind;
+  c->n_seq = n_seq;
+  c->seq_len = seq_len;
+  c->T = n_seq * seq_len;
+  c->order.resize(L);
+  for (int i = 0; i < L; ++i) c->order[i] = (kind == LSN_PASS_FWD) ? i : L - 1 - i;
+  c->slot_of.assign(L, -1);
+  c->pos = 0;
+  return ensure_loads(c);
+}
+
+lsn_status lsn_embed(lsn_ctx* c, const int32_t* tokens, float* h0) {
+  CHECK_CTX(c);
+  if (!tokens || !h0 || c->T <= 0) return fail(c, LSN_ERR_INVALID, "bad lsn_embed arguments");
+  if (!c->head_loaded) return fail(c, LSN_ERR_STATE, "head tables not loaded");
+  embed(tokens, c->embed, c->T, c->cfg.hidden, h0, c->cs);
+  return launch_check(c);
+}
+
+lsn_status lsn_forward_layer(lsn_ctx* c, int32_t layer, const float* h_in, float* h_out) {
+  CHECK_CTX(c);
+  if (!h_in || !h_out) return fail(c, LSN_ERR_INVALID, "null activation");
+  const uint8_t* rec;
+  lsn_status st = layer_begin(c, LSN_PASS_FWD, layer, &rec);
+  if (st != LSN_OK) return st;
+  st = layer_forward(c, layer, rec, h_in, h_out, true);
+  if (st != LSN_OK) return st;
+  return layer_end(c);
+}
+
+lsn_status lsn_backward_layer(lsn_ctx* c, int32_t layer, const float* h_in, const float* dh_out,
+                              float* dh_in) {
+  CHECK_CTX(c);
+  if (!h_in || !dh_out || !dh_in) return fail(c, LSN_ERR_INVALID, "null activation");
+  const uint8_t* rec;
+  lsn_status st = layer_begin(c, LSN_PASS_BWD, layer, &rec);
+  if (st != LSN_OK) return st;
+  st = layer_backward(c, layer, rec, h_in, dh_out, dh_in);
+  if (st != LSN_OK) return st;
+  return layer_end(c);
+}
+
+static lsn_status lm_logits_chunk(lsn_ctx* c, int v0, int Vc) {
+  GemmParams p = base_params(c);
+  p.M = c->T; p.N = Vc; p.K = c->cfg.hidden;
+  p.A = c->nf; p.lda = c->cfg.hidden;
+  p.B = c->lm_head + (int64_t)v0 * c->cfg.hidden; p.ldb = c->cfg.hidden;
+  p.C = c->logits; p.ldc = Vc;
+  HIPCHK(c, gemm(p, A_BF16_K, B_BF16_K, 1, c->cs));
+  return LSN_OK;
+}
+
+lsn_status lsn_lm_head_logprobs(lsn_ctx* c, const float* h, const int32_t* targets, float* logp) {
+  CHECK_CTX(c);
+  if (!h || !targets || !logp || c->T <= 0) return fail(c, LSN_ERR_INVALID, "bad lm_head arguments");
+  if (!c->head_loaded) return fail(c, LSN_ERR_STATE, "head tables not loaded");
+  const int T = c->T, V = c->cfg.vocab, H = c->cfg.hidden;
+  rmsnorm_fwd(h, c->final_norm, T, H, c->cfg.rms_eps, c->nf, c->rstdf, c->cs);
+  for (int v0 = 0; v0 < V; v0 += VCHUNK) {
+    const int Vc = std::min(VCHUNK, V - v0);
+    lsn_status st = lm_logits_chunk(c, v0, Vc);
+    if (st != LSN_OK) return st;
+    lse_chunk(c->logits, T, Vc, v0, targets, c->run_m, c->run_s, c->tlogit, v0 == 0, c->cs);
+  }
+  lse_final(c->run_m, c->run_s, c->tlogit, targets, T, logp, c->lse, c->cs);
+  c->lm_h = h;
+  c->lm_T = T;
+  return launch_check(c);
+}
+
+lsn_status lsn_lm_head_backward(lsn_ctx* c, const float* h, const int32_t* targets,
+                                const float* dlogp, float* dh) {
+  CHECK_CTX(c);
+  if (!h || !targets || !dlogp || !dh) return fail(c, LSN_ERR_INVALID, "bad lm_head arguments");
+  if (h != c->lm_h || c->lm_T != c->T)
+    return fail(c, LSN_ERR_STATE, "lm_head_backward must follow lm_head_logprobs on the same h");
+  const int T = c->T, V = c->cfg.vocab, H = c->cfg.hidden;
+  for (int v0 = 0; v0 < V; v0 += VCHUNK) {
+    const int Vc = std::min(VCHUNK, V - v0);
+    lsn_status st = lm_logits_chunk(c, v0, Vc);
+    if (st != LSN_OK) return st;
+    dlogits(c->logits, T, Vc, v0, c->lse, targets, dlogp, c->dlog, c->cs);
+    GemmParams p = base_params(c);  // dn += dlogits W_chunk
+    p.M = T; p.N = H; p.K = Vc;
+    p.A = c->dlog; p.lda = Vc;
+    p.B = c->lm_head + (int64_t)v0 * H; p.ldb = H;
+    p.C = c->dnf; p.ldc = H;
+    p.cmode = (v0 == 0) ? C_F32 : C_F32_ACC;
+    HIPCHK(c, gemm(p, A_BF16_K, B_BF16_R, 1, c->cs));
+  }
+  rmsnorm_bwd(h, c->final_norm, c->rstdf, c->dnf, nullptr, T, H, dh, c->cs);
+  return launch_check(c);
+}
+
+lsn_status lsn_sft_loss(lsn_ctx* c, const float* logp, const int32_t* targets, int32_t n,
+                        float* loss, float* dlogp) {
+  CHECK_CTX(c);
+  if (!logp || !targets || !loss || !dlogp || n <= 0)
+    return fail(c, LSN_ERR_INVALID, "bad sft_loss arguments");
+  sft_loss(logp, targets, n, loss, dlogp, c->cs);
+  return launch_check(c);
+}
+
+lsn_status lsn_dpo_loss(lsn_ctx* c, const float* lp, const float* lr, int32_t seq_len,
+                        int32_t prompt_len, float beta, float* out6, float* dlogp) {
+  CHECK_CTX(c);
+  if (!lp || !lr || !out6 || !dlogp || seq_len < 2 || prompt_len < 1 || prompt_len >= seq_len)
+    return fail(c, LSN_ERR_INVALID, "bad dpo_loss arguments");
+  dpo_loss(lp, lr, seq_len, prompt_len, beta, out6, dlogp, c->cs);
+  return launch_check(c);
+}
+
+lsn_status lsn_stats(const lsn_ctx* c, uint64_t* layer_loads, uint64_t* bytes_h2d,
+                     uint64_t* ws_bytes) {
+  if (!c) return LSN_ERR_INVALID;
+  if (layer_loads) *layer_loads = c->loads;
+  if (bytes_h2d) *bytes_h2d = c->bytes_h2d;
+  if (ws_bytes) *ws_bytes = c->ws_needed;
+  return LSN_OK;
+}
+
+lsn_status lsn_copy_stream(const lsn_ctx* c, void** s) {
+  if (!c || !s) return LSN_ERR_INVALID;
+  *s = (void*)c->copy;
+  return LSN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every symbol the header declares, and its host NF4 codec agrees bit for bit
+with the oracle's."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import nf4 as onf4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from layer_streamed_nf4_double_amd import _lib as L
+    return L
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "lsn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    raw = ctypes.CDLL(L.LIB_PATH)
+    names = _declared()
+    assert len(names) >= 25
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in lsn.h but not exported"
+    assert set(names) == set(L.EXPORTED), "binding and header disagree"
+
+
+def test_codebook_bit_equal_to_oracle():
+    L = _lib()
+    cb = L.lsn_nf4_codebook()
+    assert np.array_equal(cb.view(np.uint32), onf4.codebook().view(np.uint32))
+
+
+def _adversarial():
+    c = onf4.codebook()
+    m = onf4.midpoints()
+    rng = np.random.default_rng(5)
+    blocks = []
+    b = np.zeros(64, np.float32); b[0] = 1.0; b[1:16] = m; b[16:31] = c[:15]
+    blocks.append(b)                                               # exact ties / levels
+    blocks.append(np.zeros(64, np.float32))                         # all-zero block
+    b = np.full(64, -0.0, np.float32); b[5] = -3.0; blocks.append(b)
+    b = (rng.standard_normal(64) * 1e-30).astype(np.float32); blocks.append(b)  # tiny values
+    b = np.nextafter(m, np.float32(2)).astype(np.float32)
+    blocks.append(np.concatenate([[1.0], b, np.nextafter(m, np.float32(-2)), np.zeros(64 - 31)]).astype(np.float32))
+    return np.concatenate(blocks)
+
+
+@pytest.mark.parametrize("case", ["normal", "adversarial", "rows688", "odd"])
+def test_quantize_bit_equal_to_oracle(case):
+    L = _lib()
+    rng = np.random.default_rng(1)
+    if case == "normal":
+        w = rng.standard_normal(64 * 3000, dtype=np.float32) * np.float32(0.02)
+    elif case == "adversarial":
+        w = _adversarial()
+    elif case == "rows688":   # a [256, 688] down projection: blocks straddle rows
+        w = (rng.standard_normal((256, 688), dtype=np.float32) * np.float32(0.02)).reshape(-1)
+    else:
+        w = rng.standard_normal(64 * 5 + 37, dtype=np.float32)
+    codes, absmax = L.lsn_nf4_quantize(w)
+    oc, oa = onf4.quantize(w)
+    assert np.array_equal(codes, oc)
+    assert np.array_equal(absmax.view(np.uint32), oa.view(np.uint32))
+    d = L.lsn_nf4_dequantize_host(codes, absmax, w.size)
+    od = onf4.dequantize(oc, oa, w.size)
+    assert np.array_equal(d.view(np.uint32), od.view(np.uint32))
+
+
+def test_quantize_large_multithreaded_matches_oracle():
+    L = _lib()
+    w = np.random.default_rng(2).standard_normal(64 * 40000, dtype=np.float32)
+    codes, absmax = L.lsn_nf4_quantize(w)
+    oc, oa = onf4.quantize(w)
+    assert np.array_equal(codes, oc) and np.array_equal(absmax, oa)
+
+
+def test_quantize_rejects_non_finite():
+    L = _lib()
+    w = np.zeros(128, np.float32)
+    w[77] = np.inf
+    with pytest.raises(L.LsnError) as e:
+        L.lsn_nf4_quantize(w)
+    assert e.value.status == L.LSN_ERR_INVALID
+
+
+def test_workspace_and_preflight_refusal():
+    import synth
+    from layer_streamed_nf4_double_amd import trainer
+    L = _lib()
+    shape = dict(synth.WORKLOADS["tiny"], n_layers=6)
+    cfg = trainer.make_config(shape, "stream_host")
+    need = L.lsn_workspace_bytes(cfg)
+    cfg_res = trainer.make_config(shape, "resident")
+    need_res = L.lsn_workspace_bytes(cfg_res)
+    assert need_res > need        # resident keeps every record, streaming two slots
+    # a workspace that is too small is refused before any device work
+    with pytest.raises(L.LsnError) as e:
+        L.lsn_create(cfg, 0x1000, need - 1, 0)
+    assert e.value.status == L.LSN_ERR_NOFIT
+    cfg.vram_budget = need - 1
+    with pytest.raises(L.LsnError) as e:
+        L.lsn_create(cfg, 0x1000, need, 0)
+    assert e.value.status == L.LSN_ERR_NOFIT
+
+
+def test_invalid_configs_rejected():
+    import synth
+    from layer_streamed_nf4_double_amd import trainer
+    L = _lib()
+    for field, val in [("lora_rank", 17), ("n_kv_heads", 3), ("head_dim", 60), ("vocab", 1001),
+                       ("max_seq_len", 10 ** 6)]:
+        cfg = trainer.make_config(synth.WORKLOADS["tiny"], "stream_host")
+        setattr(cfg, field, val)
+        with pytest.raises(L.LsnError) as e:
+            L.lsn_workspace_bytes(cfg)
+        assert e.value.status == L.LSN_ERR_INVALID, field
+
+
+def test_record_sizes_match_layout():
+    """Per-layer record = NF4 codes (P/2) + absmax (P/16) + norms, 4 KiB aligned."""
+    import synth
+    from layer_streamed_nf4_double_amd import trainer
+    L = _lib()
+    for name, want in [("tiny", 444672), ("llama3.1-8b-shaped", 122683392),
+                       ("qwen2.5-3b-shaped", 43352064)]:
+        w = dict(synth.WORKLOADS[name], n_layers=4)
+        P = sum(np.prod(synth.proj_shape(w, p)) for p in synth.PROJ)
+        assert P // 2 + P // 16 == want
+        cfg = trainer.make_config(w, "stream_host")
+        ws_stream = L.lsn_workspace_bytes(cfg)
+        cfg.mode = L.LSN_RESIDENT
+        ws_res = L.lsn_workspace_bytes(cfg)
+        rec = (ws_res - ws_stream) // (w["n_layers"] - 2)
+        assert want <= rec <= want + 4096 + 256 * 4 + 4 * w["hidden"]
