@@ -18,7 +18,8 @@ void softmax_bwd(const float* Pf, const float* dP, uint16_t* dS, int S, int64_t 
 void swiglu_fwd(const float* gu, uint16_t* a, int T, int F, hipStream_t s);
 void swiglu_bwd(const float* gu, const float* da, uint16_t* dgu, float* dguf, int T, int F,
                 hipStream_t s);
-void embed(const int32_t* tok, const uint16_t* table, int T, int H, float* h, hipStream_t s);
+void embed(const int32_t* tok, const uint16_t* table, int T, int H, int V, float* h,
+           hipStream_t s);
 void skinny_bf16(const uint16_t* X, int64_t ldx, const float* W, int64_t sk, int64_t sj, int M,
                  int K, int r, float* out, uint16_t* ext, int64_t ldext, float scale,
                  hipStream_t s);

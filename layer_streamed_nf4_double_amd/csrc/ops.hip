@@ -182,11 +182,14 @@ __global__ void swiglu_bwd_k(const float* __restrict__ gu, const float* __restri
 // ---------------------------------------------------------------------------
 // embedding rows (bf16 table) -> fp32
 // ---------------------------------------------------------------------------
+// a token id outside [0, V) yields a NaN row instead of an out-of-bounds read
 __global__ void embed_k(const int32_t* __restrict__ tok, const uint16_t* __restrict__ table,
-                        int H, float* __restrict__ h) {
+                        int H, int V, float* __restrict__ h) {
   const int64_t t = blockIdx.x;
   const int64_t v = tok[t];
-  for (int i = threadIdx.x; i < H; i += blockDim.x) h[t * H + i] = bf16_to_f32(table[v * H + i]);
+  const bool ok = v >= 0 && v < V;
+  for (int i = threadIdx.x; i < H; i += blockDim.x)
+    h[t * H + i] = ok ? bf16_to_f32(table[v * H + i]) : __builtin_nanf("");
 }
 
 // ---------------------------------------------------------------------------
@@ -503,8 +506,9 @@ void swiglu_bwd(const float* gu, const float* da, uint16_t* dgu, float* dguf, in
   const int64_t n = (int64_t)T * F;
   hipLaunchKernelGGL(swiglu_bwd_k, dim3(nb(n, 256)), dim3(256), 0, s, gu, da, dgu, dguf, F, n);
 }
-void embed(const int32_t* tok, const uint16_t* table, int T, int H, float* h, hipStream_t s) {
-  hipLaunchKernelGGL(embed_k, dim3(T), dim3(256), 0, s, tok, table, H, h);
+void embed(const int32_t* tok, const uint16_t* table, int T, int H, int V, float* h,
+           hipStream_t s) {
+  hipLaunchKernelGGL(embed_k, dim3(T), dim3(256), 0, s, tok, table, H, V, h);
 }
 void skinny_bf16(const uint16_t* X, int64_t ldx, const float* W, int64_t sk, int64_t sj, int M,
                  int K, int r, float* out, uint16_t* ext, int64_t ldext, float scale,

@@ -1008,7 +1008,7 @@ lsn_status lsn_embed(lsn_ctx* c, const int32_t* tokens, float* h0) {
   CHECK_CTX(c);
   if (!tokens || !h0 || c->T <= 0) return fail(c, LSN_ERR_INVALID, "bad lsn_embed arguments");
   if (!c->head_loaded) return fail(c, LSN_ERR_STATE, "head tables not loaded");
-  embed(tokens, c->embed, c->T, c->cfg.hidden, h0, c->cs);
+  embed(tokens, c->embed, c->T, c->cfg.hidden, c->cfg.vocab, h0, c->cs);
   return launch_check(c);
 }
 

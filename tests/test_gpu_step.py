@@ -1,0 +1,220 @@
+"""GPU parity of whole training steps through the C ABI.
+
+* SFT on the tiny decoder (2 layers, hidden 256, 4 heads, FFN 688, vocab
+  1024, seq 64; LoRA r=8, alpha=16 on q, v; B = 0 then one SGD step, lr 0.1):
+  step 1 compares loss, log-probs and dB (dA is exactly 0 on both sides) and
+  the updated adapters; the oracle's updated adapters are then loaded into
+  the GPU and step 2 compares again with dA != 0.
+* DPO on the tiny decoder: policy == reference (B = 0) gives ln 2 and equal
+  log-probs bit for bit; with B != 0 loss, z and gradients match the oracle.
+* streamed (host RAM or file) and resident runs are bit-identical, and the
+  scheduler copies exactly the expected number of layer records.
+"""
+import math
+import os
+import sys
+import tempfile
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import model as om
+from tests.modelbuild import assert_close, gpu_model, oracle_model, rel
+
+pytestmark = pytest.mark.gpu
+TINY = synth.WORKLOADS["tiny"]
+LR = 0.1
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available()
+    return t
+
+
+def _dev_tokens(torch, tokens):
+    from layer_streamed_nf4_double_amd.trainer import sft_targets
+    tok = torch.from_numpy(np.ascontiguousarray(tokens.reshape(-1).astype(np.int32))).cuda()
+    tgt = torch.from_numpy(sft_targets(tokens)).cuda()
+    return tok, tgt
+
+
+def _grads(m, w, targets=("q", "v")):
+    out = []
+    for layer in range(w["n_layers"]):
+        d = {}
+        for p in targets:
+            A, B, dA, dB = m.get_lora(layer, p)
+            d[p] = (A, B, dA, dB)
+        out.append(d)
+    return out
+
+
+def _run_sft(torch, m, tokens, lr=LR):
+    tok, tgt = _dev_tokens(torch, tokens)
+    n_seq, S = tokens.shape
+    loss = m.sft_step(tok, tgt, n_seq, S, lr)
+    m.sync()
+    return float(loss[0].item()), m.logp[: n_seq * S].cpu().numpy().copy()
+
+
+def test_sft_tiny_two_steps_vs_oracle(torch):
+    w = TINY
+    tokens = synth.sft_tokens(w)
+    say("[sft-tiny] oracle")
+    cfg, layers, lora, head = oracle_model(w, b_zero=True)
+    o1 = om.sft_step(cfg, layers, lora, head, tokens, LR)
+    say("[sft-tiny] gpu stream_host step 1")
+    m = gpu_model(w, "stream_host", b_zero=True)
+    loss1, logp1 = _run_sft(torch, m, tokens)
+    g1 = _grads(m, w)
+    assert abs(loss1 - o1["loss"]) <= 2e-2 * abs(o1["loss"])
+    assert_close(logp1, o1["logp"], 2e-2, "logp step 1")
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            A, B, dA, dB = g1[layer][p]
+            odA, odB = o1["grads"][layer][p]
+            assert np.all(dA == 0) and np.all(odA == 0), "dA must vanish at B = 0"
+            assert_close(dB, odB, 5e-2, f"dB L{layer} {p} step 1")
+            oA, oB = o1["lora_new"][layer][p]
+            assert np.array_equal(A, oA.astype(np.float32)), "A unchanged by SGD at dA = 0"
+            assert_close(B, oB, 5e-2, f"B' L{layer} {p}")
+    # step 2 from identical parameters: the oracle's updated adapters
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            A, B = o1["lora_new"][layer][p]
+            m.set_lora(layer, p, A.astype(np.float32), B.astype(np.float32))
+    say("[sft-tiny] gpu step 2")
+    o2 = om.sft_step(cfg, layers, o1["lora_new"], head, tokens, LR)
+    loss2, logp2 = _run_sft(torch, m, tokens)
+    g2 = _grads(m, w)
+    assert abs(loss2 - o2["loss"]) <= 2e-2 * abs(o2["loss"])
+    assert_close(logp2, o2["logp"], 2e-2, "logp step 2")
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            _, _, dA, dB = g2[layer][p]
+            odA, odB = o2["grads"][layer][p]
+            assert np.abs(odA).max() > 0
+            assert_close(dA, odA, 5e-2, f"dA L{layer} {p} step 2")
+            assert_close(dB, odB, 5e-2, f"dB L{layer} {p} step 2")
+    m.close()
+
+
+def _bits(x):
+    return np.asarray(x, np.float32).view(np.uint32)
+
+
+def _two_step_record(torch, m, w, tokens):
+    rec = []
+    for _ in range(2):
+        loss, logp = _run_sft(torch, m, tokens)
+        rec.append((np.float32(loss), logp, _grads(m, w)))
+    return rec
+
+
+def _assert_bit_identical(a, b):
+    for (la, pa, ga), (lb, pb, gb) in zip(a, b):
+        assert _bits(la) == _bits(lb)
+        assert np.array_equal(_bits(pa), _bits(pb))
+        for da, db in zip(ga, gb):
+            for p in da:
+                for x, y in zip(da[p], db[p]):
+                    assert np.array_equal(_bits(x), _bits(y))
+
+
+@pytest.mark.parametrize("n_layers", [2, 5])
+def test_streamed_equals_resident_bitwise(torch, n_layers):
+    w = dict(TINY, n_layers=n_layers)
+    tokens = synth.tokens((2, 64), w["vocab"], 77)
+    say(f"[stream==resident] L={n_layers}")
+    res = gpu_model(w, "resident", b_zero=False, max_tokens=128)
+    a = _two_step_record(torch, res, w, tokens)
+    res.close()
+    st = gpu_model(w, "stream_host", b_zero=False, max_tokens=128)
+    b = _two_step_record(torch, st, w, tokens)
+    loads, nbytes, _ = st.stats()
+    st.close()
+    _assert_bit_identical(a, b)
+    # forward copies all L records, backward reuses the last two; the next
+    # step's forward reuses the two the backward ended on
+    L_ = n_layers
+    want = (L_ + max(L_ - 2, 0)) + (max(L_ - 2, 0) + max(L_ - 2, 0))
+    assert loads == want, (loads, want)
+    with tempfile.TemporaryDirectory() as d:
+        fm = gpu_model(w, "stream_file", b_zero=False, max_tokens=128,
+                       store_path=os.path.join(d, "store.bin"))
+        c = _two_step_record(torch, fm, w, tokens)
+        fm.close()
+    _assert_bit_identical(a, c)
+
+
+def test_dpo_tiny(torch):
+    w = dict(TINY)
+    S, P, beta = 64, 16, 0.1
+    rng_tok = synth.tokens((P,), w["vocab"], 88, synth.TID_PROMPT)
+    ch = np.concatenate([rng_tok, synth.tokens((S - P,), w["vocab"], 88, synth.TID_CHOSEN)])
+    rj = np.concatenate([rng_tok, synth.tokens((S - P,), w["vocab"], 88, synth.TID_REJECTED)])
+    tokens = np.stack([ch, rj])
+    tok, tgt = _dev_tokens(torch, tokens)
+    # policy == reference: B = 0
+    say("[dpo-tiny] B=0 -> ln 2")
+    m = gpu_model(w, "stream_host", b_zero=True, max_tokens=2 * S)
+    out = m.dpo_step(tok, tgt, S, P, beta, None)
+    m.sync()
+    o = out.cpu().numpy()
+    assert o[1] == 0.0, "z must be exactly 0 when the adapter contributes nothing"
+    assert abs(float(o[0]) - math.log(2.0)) <= 1e-7
+    assert np.array_equal(_bits(m.logp[:2 * S].cpu().numpy()),
+                          _bits(m.logp_ref[:2 * S].cpu().numpy()))
+    m.close()
+    # B != 0: parity with the oracle
+    say("[dpo-tiny] B!=0 vs oracle")
+    cfg, layers, lora, head = oracle_model(w, b_zero=False)
+    od = om.dpo_step(cfg, layers, lora, head, ch, rj, P, beta, LR)
+    m = gpu_model(w, "stream_host", b_zero=False, max_tokens=2 * S)
+    out = m.dpo_step(tok, tgt, S, P, beta, LR)
+    m.sync()
+    o = out.cpu().numpy()
+    assert abs(o[0] - od["loss"]) <= 2e-2 * abs(od["loss"])
+    # z = beta * (difference of ~2.6e3-nat log-prob sums) cancels; its bar is
+    # 2e-2 relative with a floor of beta (one nat of log-prob difference)
+    assert abs(o[1] - od["z"]) <= 2e-2 * max(abs(od["z"]), beta)
+    assert_close(m.logp[:2 * S].cpu().numpy(), od["logp_policy"], 2e-2, "policy logp")
+    assert_close(m.logp_ref[:2 * S].cpu().numpy(), od["logp_ref"], 2e-2, "reference logp")
+    g = _grads(m, w)
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            _, _, dA, dB = g[layer][p]
+            odA, odB = od["grads"][layer][p]
+            assert_close(dA, odA, 5e-2, f"DPO dA L{layer} {p}")
+            assert_close(dB, odB, 5e-2, f"DPO dB L{layer} {p}")
+    m.close()
+
+
+def test_all_projections_adapted_gqa(torch):
+    """Every projection adapted, grouped kv heads, two sequences."""
+    w = dict(TINY, n_heads=4, n_kv_heads=2, n_layers=2)
+    targets = synth.PROJ
+    tokens = synth.tokens((2, 32), w["vocab"], 91)
+    say("[all-targets gqa]")
+    cfg, layers, lora, head = oracle_model(w, b_zero=False, lora_targets=targets)
+    o = om.sft_step(cfg, layers, lora, head, tokens, LR)
+    m = gpu_model(w, "stream_host", b_zero=False, lora_targets=targets, max_tokens=64,
+                  max_seq_len=32)
+    loss, logp = _run_sft(torch, m, tokens)
+    assert abs(loss - o["loss"]) <= 2e-2 * abs(o["loss"])
+    assert_close(logp, o["logp"], 2e-2, "logp")
+    g = _grads(m, w, targets)
+    for layer in range(w["n_layers"]):
+        for p in targets:
+            _, _, dA, dB = g[layer][p]
+            odA, odB = o["grads"][layer][p]
+            assert_close(dA, odA, 5e-2, f"dA L{layer} {p}")
+            assert_close(dB, odB, 5e-2, f"dB L{layer} {p}")
+    m.close()
