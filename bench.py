@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of layer-streamed NF4-LoRA training on one MI355X.
+
+Default workload: a Llama-3.1-8B-shaped decoder (32 layers, hidden 4096,
+32 q / 8 kv heads of 128, SwiGLU 14336, vocab 128256, RoPE theta 5e5), random
+N(0, 0.02) base quantized to NF4 (block-64 absmax) and held in pinned host
+RAM, LoRA r=16 (alpha 32) on q and v, one sequence of 512 uniform random
+tokens.  A step is one streamed SFT step: forward over the stack (each layer
+record copied host->device into one of two slots on a side stream while the
+previous layer computes), LM-head log-probs, loss, LM-head backward, backward
+over the stack (records streamed again, layer recomputed from its saved
+input), SGD on the adapter.  The same model then runs streamed DPO steps on
+one preference pair (2 x 512 tokens, 128 shared prompt tokens, beta 0.1).
+
+Prints ONE JSON line (rank 0, N = 1).  Timing: W warm-up steps, then K steps
+between two device synchronizations.  Inputs are resident before the clock
+starts (the base in pinned host memory, tokens on the device).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/sec (streamed NF4-LoRA SFT & DPO, 1 GPU); peak VRAM; % roofline"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama3.1-8b-shaped")
+    ap.add_argument("--mode", default="stream_host", choices=["stream_host", "resident"])
+    ap.add_argument("--dpo-steps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--link-mb", type=int, default=256)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# model construction (off the clock)
+# ---------------------------------------------------------------------------
+def quantized_layers(w):
+    """Seeded fp32 weights -> NF4 records with the library's host codec."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import synth
+    from layer_streamed_nf4_double_amd import _lib as L
+
+    def one(layer):
+        codes, absmax = [], []
+        for p in synth.PROJ:
+            c, a = L.lsn_nf4_quantize(synth.layer_weights_f32(w, layer, p))
+            codes.append(c)
+            absmax.append(a)
+        return codes, absmax
+
+    ones = np.full(w["hidden"], 0x3F80, np.uint16)
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        for layer, (codes, absmax) in enumerate(ex.map(one, range(w["n_layers"]))):
+            if layer % 8 == 0:
+                log(f"[bench] quantized layer {layer}/{w['n_layers']}")
+            yield layer, codes, absmax, ones, ones
+
+
+def build_model(w, mode, max_tokens, max_seq_len, layers, head):
+    import numpy as np
+
+    import synth
+    from layer_streamed_nf4_double_amd.trainer import LayerStreamedLoRA
+    m = LayerStreamedLoRA(w, mode, max_tokens=max_tokens, max_seq_len=max_seq_len)
+    for layer, codes, absmax, g1, g2 in layers:
+        m.load_layer(layer, codes, absmax, g1, g2)
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            A, B = synth.lora_init(w, layer, p, b_zero=True)
+            m.set_lora(layer, p, A, B)
+    emb, lm, ones = head
+    m.load_head(emb, lm, ones)
+    return m
+
+
+def link_bandwidth(torch, mb, reps=20):
+    """Pinned host -> device copies of mb MiB on one stream (GB/s, best and median)."""
+    n = mb << 20
+    src = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    times = []
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            dst.copy_(src, non_blocking=True)
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            dst.copy_(src, non_blocking=True)
+            e1.record(s)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) / 1e3)
+    times.sort()
+    return n / times[0] / 1e9, n / times[len(times) // 2] / 1e9
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, tokens):
+    """Times the float32 oracle on one decoder layer (dequantize + forward, and
+    dequantize + recomputed forward + backward) and on the LM head (forward +
+    backward) at the real shape and 512 tokens, then scales to a full step:
+    L x layer + head."""
+    import numpy as np
+
+    import synth
+    from oracle import model as om
+    from oracle import nf4 as onf4
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cfg = om.Config(n_layers=w["n_layers"], hidden=w["hidden"], n_heads=w["n_heads"],
+                    n_kv_heads=w["n_kv_heads"], head_dim=w["head_dim"], ffn=w["ffn"],
+                    vocab=w["vocab"], rms_eps=w["rms_eps"], rope_theta=w["rope_theta"],
+                    lora_rank=w["lora_rank"], lora_alpha=w["lora_alpha"], tied=w["tied"])
+    # off the clock: NF4 quantization of one layer (oracle codec), head tables
+    rec = {}
+    for p in synth.PROJ:
+        W = synth.layer_weights_f32(w, 0, p)
+        rec[p] = onf4.quantize(W) + (W.shape,)
+    lora = {p: synth.lora_init(w, 0, p, b_zero=True) for p in ("q", "v")}
+    emb, lm, _ = synth.head_tables(w)
+    head = dict(embed=synth.bf16_to_f32(emb), lm_head=synth.bf16_to_f32(lm),
+                final_norm=np.ones(w["hidden"], np.float32))
+    h = head["embed"][tokens.reshape(-1)]
+    targets = om.sft_targets(tokens)
+
+    def deq():
+        lw = {p: onf4.dequantize(c, a, int(np.prod(s))).reshape(s) for p, (c, a, s) in rec.items()}
+        lw["attn_norm"] = np.ones(w["hidden"], np.float32)
+        lw["mlp_norm"] = np.ones(w["hidden"], np.float32)
+        return lw
+
+    t0 = time.perf_counter()
+    lw = deq()
+    out, _ = om.layer_forward(cfg, lw, lora, h, 1)
+    t1 = time.perf_counter()
+    lw = deq()
+    _, cache = om.layer_forward(cfg, lw, lora, h, 1)
+    om.layer_backward(cfg, lw, lora, cache, out)
+    t2 = time.perf_counter()
+    logp, hc = om.head_logprobs(cfg, head, out, targets)
+    _, dlogp = om.sft_loss(logp, targets)
+    om.head_backward(cfg, head, hc, dlogp)
+    t3 = time.perf_counter()
+    step = w["n_layers"] * ((t1 - t0) + (t2 - t1)) + (t3 - t2)
+    T = tokens.size
+    return {"value": T / step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"float32 numpy oracle, one {w['hidden']}-wide decoder layer "
+                       f"(dequantize+forward {t1 - t0:.2f} s; dequantize+recompute+backward "
+                       f"{t2 - t1:.2f} s) and the LM head fwd+bwd ({t3 - t2:.2f} s) at "
+                       f"{T} tokens, scaled to {w['n_layers']} layers: {step:.1f} s/step")}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU (no collectives, no sharding); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    from layer_streamed_nf4_double_amd import _lib as L
+    from layer_streamed_nf4_double_amd.trainer import sft_targets
+
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    S = w["seq_len"]
+    log(f"[bench] workload {args.workload} mode {args.mode}")
+
+    # ---- off the clock: weights, head tables, tokens ----
+    t_setup = time.perf_counter()
+    layers = list(quantized_layers(w))
+    head = synth.head_tables(w)
+    tokens = synth.sft_tokens(w)
+    tok = torch.from_numpy(tokens.reshape(-1).astype(np.int32)).cuda()
+    tgt = torch.from_numpy(sft_targets(tokens)).cuda()
+    log(f"[bench] setup {time.perf_counter() - t_setup:.1f} s")
+
+    link_best, link_med = link_bandwidth(torch, args.link_mb)
+    log(f"[bench] host->device link: best {link_best:.1f} GB/s, median {link_med:.1f} GB/s")
+
+    # ---- SFT ----
+    torch.cuda.reset_peak_memory_stats()
+    m = build_model(w, args.mode, S, S, layers, head)
+    rec_bytes = L.lsn_record_bytes(m.ctx)
+    for _ in range(args.warmup):
+        m.sft_step(tok, tgt, 1, S, 1e-4)
+    m.sync()
+    loads0, bytes0, ws = m.stats()
+    L.lsn_set_profiling(m.ctx, 1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        m.sft_step(tok, tgt, 1, S, 1e-4)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dt = (t1 - t0) / args.steps
+    loads1, bytes1, _ = m.stats()
+    peak = torch.cuda.max_memory_allocated()
+    loss = float(m.loss[0].item())
+    n_gemm, flops, ms = L.lsn_profile_query(m.ctx, 0, 0, 2, 0)   # NF4 fwd GEMM, 256x128 tile
+    n_cp, cp_bytes, cp_ms = L.lsn_profile_query(m.ctx, 1)
+    L.lsn_set_profiling(m.ctx, 0)
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    h2d_per_step = (bytes1 - bytes0) / args.steps
+    loads_per_step = (loads1 - loads0) / args.steps
+    sft_tok_s = S / dt
+    log(f"[bench] SFT {dt * 1e3:.1f} ms/step, {sft_tok_s:.1f} tok/s, loss {loss:.4f}, "
+        f"{loads_per_step:.1f} loads/step, peak {peak / 1e9:.2f} GB")
+
+    achieved = flops / (ms / 1e3) / 1e12 if ms > 0 else 0.0
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None,
+                "kernel": "gemm_kernel<256,128,A_BF16_K,B_NF4_K> (fused NF4-dequant GEMM)",
+                "launches": int(n_gemm), "avg_us": round(ms / max(n_gemm, 1) * 1e3, 2),
+                "flop_per_launch": flops / max(n_gemm, 1)}
+    copy_gbps = cp_bytes / (cp_ms / 1e3) / 1e9 if cp_ms > 0 else 0.0
+    link = {"bound": "host-link", "measured_peak_GBps": round(link_best, 2),
+            "measured_median_GBps": round(link_med, 2),
+            "h2d_bytes_per_step": int(h2d_per_step), "record_bytes": int(rec_bytes),
+            "layer_loads_per_step": loads_per_step,
+            "achieved_GBps": round(h2d_per_step / dt / 1e9, 2),
+            "frac": round(h2d_per_step / dt / 1e9 / link_best, 4),
+            "copy_engine_GBps_while_copying": round(copy_gbps, 2)}
+
+    # ---- DPO on the same streamed base ----
+    dpo = None
+    if args.dpo_steps > 0:
+        ch, rj = synth.dpo_pair(w)
+        dtok = np.stack([ch, rj])
+        dt_tok = torch.from_numpy(dtok.reshape(-1).astype(np.int32)).cuda()
+        dt_tgt = torch.from_numpy(sft_targets(dtok)).cuda()
+        torch.cuda.reset_peak_memory_stats()
+        md = build_model(w, args.mode, 2 * S, S, layers, head)
+        P, beta = synth.dpo_prompt_len(w), synth.DPO_PAIR["beta"]
+        for _ in range(max(1, args.warmup)):
+            md.dpo_step(dt_tok, dt_tgt, S, P, beta, 1e-4)
+        md.sync()
+        l0, b0, _ = md.stats()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.dpo_steps):
+            md.dpo_step(dt_tok, dt_tgt, S, P, beta, 1e-4)
+        torch.cuda.synchronize()
+        ddt = (time.perf_counter() - t0) / args.dpo_steps
+        l1, b1, _ = md.stats()
+        dpeak = torch.cuda.max_memory_allocated()
+        out = md.loss[:2].cpu().numpy()
+        md.close()
+        del md
+        torch.cuda.empty_cache()
+        dpo = {"tokens_per_s": round(2 * S / ddt, 2), "ms_per_step": round(ddt * 1e3, 2),
+               "tokens_per_step": 2 * S, "loss": float(out[0]),
+               "layer_loads_per_step": (l1 - l0) / args.dpo_steps,
+               "layer_loads_ratio_vs_sft": round((l1 - l0) / args.dpo_steps / max(loads_per_step, 1e-9), 3),
+               "h2d_GBps": round((b1 - b0) / args.dpo_steps / ddt / 1e9, 2),
+               "link_frac": round((b1 - b0) / args.dpo_steps / ddt / 1e9 / link_best, 4),
+               "peak_vram_bytes": int(dpeak),
+               "peak_vram_ratio_vs_sft": round(dpeak / peak, 3)}
+        log(f"[bench] DPO {ddt * 1e3:.1f} ms/step, {2 * S / ddt:.1f} tok/s, loss {out[0]:.4f}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle sample)")
+        cpu = cpu_baseline(w, tokens)
+        log(f"[bench] oracle {cpu['value']:.3f} tok/s on {cpu['cores']} threads")
+
+    line = {"metric": METRIC, "value": round(sft_tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 3),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,0.02) NF4 base, uniform random tokens)",
+            "config": {"workload": f"{args.workload} streamed LoRA-SFT step",
+                       "n_layers": w["n_layers"], "hidden": w["hidden"], "ffn": w["ffn"],
+                       "vocab": w["vocab"], "heads": f"{w['n_heads']}q/{w['n_kv_heads']}kv",
+                       "global_batch": 1, "seq_len": S, "lora": "r16 a32 q,v",
+                       "base": "NF4 block-64, pinned host RAM" if args.mode == "stream_host"
+                       else "NF4 block-64, device resident",
+                       "parallelism": "none (1 GPU)"},
+            "peak_vram_bytes": int(peak), "loss": loss,
+            "roofline": roofline, "link": link, "dpo": dpo, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

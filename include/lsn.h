@@ -240,6 +240,23 @@ lsn_status lsn_stats(const lsn_ctx* ctx, uint64_t* layer_loads, uint64_t* bytes_
 /* The copy stream (hipStream_t) the scheduler uses, for timing its copies. */
 lsn_status lsn_copy_stream(const lsn_ctx* ctx, void** hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * Live timing (measurement only; results are unchanged).  With on != 0 the
+ * context records a timing event pair around every NF4 GEMM launch (compute
+ * stream) and every layer-record copy (copy stream) from now on; any call
+ * clears earlier records.  Synchronizes both streams.
+ * ------------------------------------------------------------------------- */
+lsn_status lsn_set_profiling(lsn_ctx* ctx, int32_t on);
+/* Totals over the recorded events.  what = 0: NF4 GEMM launches whose operand
+ * forms are (a, b) -- A: 0 bf16 row-major, 1 bf16 transposed, 2 fp32
+ * row-major; B: 0 bf16 [N,K], 1 bf16 [K,N], 2 NF4 W^T used as y = x W,
+ * 3 NF4 W^T used as dx = dy W^T -- and whose tile id is tile (0: 256x128,
+ * 1: 128x128, 2: 64x64; -1: any); work = algorithmic flops 2*M*N*K per
+ * problem (the low-rank extension not counted).  what = 1: record copies;
+ * work = bytes.  count = launches, ms = summed event time.  Synchronizes. */
+lsn_status lsn_profile_query(lsn_ctx* ctx, int32_t what, int32_t a, int32_t b, int32_t tile,
+                             uint64_t* count, double* work, double* ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -79,6 +79,9 @@ _SIGS = {
     "lsn_dpo_loss": [_P, _P, _P, _I32, _I32, _F, _P, _P],
     "lsn_stats": [_P, ctypes.POINTER(_U64), ctypes.POINTER(_U64), ctypes.POINTER(_U64)],
     "lsn_copy_stream": [_P, ctypes.POINTER(_P)],
+    "lsn_set_profiling": [_P, _I32],
+    "lsn_profile_query": [_P, _I32, _I32, _I32, _I32, ctypes.POINTER(_U64),
+                          ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -295,3 +298,15 @@ def lsn_copy_stream(ctx):
     s = _P(None)
     _check(_lib.lsn_copy_stream(ctx, ctypes.byref(s)), ctx, "lsn_copy_stream")
     return s.value or 0
+
+
+def lsn_set_profiling(ctx, on):
+    _check(_lib.lsn_set_profiling(ctx, int(on)), ctx, "lsn_set_profiling")
+
+
+def lsn_profile_query(ctx, what, a=0, b=0, tile=-1):
+    """(launches, work, ms) over the recorded events (see lsn.h)."""
+    n, w, t = _U64(0), ctypes.c_double(0), ctypes.c_double(0)
+    _check(_lib.lsn_profile_query(ctx, what, a, b, tile, ctypes.byref(n), ctypes.byref(w),
+                                  ctypes.byref(t)), ctx, "lsn_profile_query")
+    return n.value, w.value, t.value

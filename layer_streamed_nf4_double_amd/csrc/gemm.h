@@ -40,6 +40,10 @@ struct GemmParams {
   float levels[16] = {};  // NF4 code levels
 };
 
+enum { TILE_256x128 = 0, TILE_128x128 = 1, TILE_64x64 = 2 };
+
 hipError_t gemm(const GemmParams& p, int opa, int opb, int batch, hipStream_t s);
+// the tile configuration gemm() launches for this problem
+int gemm_tile(int M, int N, int batch);
 
 }  // namespace lsn

@@ -406,15 +406,23 @@ static hipError_t launch_t(const GemmParams& p, int batch, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Large problems take the 256 x 128 tile (each dequantized weight feeds 256
+// rows); small ones trade reuse for enough workgroups to fill 256 CUs.
+int gemm_tile(int M, int N, int batch) {
+  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 127) / 128) * batch;
+  const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128) * batch;
+  if (M >= 256 && t256 >= 192) return TILE_256x128;
+  if (M >= 128 && t128 >= 128) return TILE_128x128;
+  return TILE_64x64;
+}
+
 template <int OPA, int OPB>
 static hipError_t launch_tiles(const GemmParams& p, int batch, hipStream_t s) {
-  // Large problems take the 256 x 128 tile (each dequantized weight feeds 256
-  // rows); small ones trade reuse for enough workgroups to fill 256 CUs.
-  const int64_t t256 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128) * batch;
-  const int64_t t128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) * batch;
-  if (p.M >= 256 && t256 >= 192) return launch_t<256, 128, OPA, OPB>(p, batch, s);
-  if (p.M >= 128 && t128 >= 128) return launch_t<128, 128, OPA, OPB>(p, batch, s);
-  return launch_t<64, 64, OPA, OPB>(p, batch, s);
+  switch (gemm_tile(p.M, p.N, batch)) {
+    case TILE_256x128: return launch_t<256, 128, OPA, OPB>(p, batch, s);
+    case TILE_128x128: return launch_t<128, 128, OPA, OPB>(p, batch, s);
+    default: return launch_t<64, 64, OPA, OPB>(p, batch, s);
+  }
 }
 
 hipError_t gemm(const GemmParams& p, int opa, int opb, int batch, hipStream_t s) {

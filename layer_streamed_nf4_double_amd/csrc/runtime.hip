@@ -108,6 +108,17 @@ struct lsn_ctx {
 
   float levels[16];
   uint64_t loads = 0, bytes_h2d = 0;
+
+  // optional timing of GEMM launches and record copies (event pairs)
+  struct ProfRec {
+    int what, a, b, tile;
+    double work;
+    hipEvent_t e0, e1;
+  };
+  bool profiling = false;
+  std::vector<ProfRec> prof;
+  std::vector<hipEvent_t> evpool;
+  size_t evnext = 0;
   bool poisoned = false;
   std::string err;
 
@@ -164,6 +175,40 @@ static lsn_status fail(lsn_ctx* c, lsn_status st, const char* fmt, ...) {
 static lsn_status launch_check(lsn_ctx* c) {
   HIPCHK(c, hipGetLastError());
   return LSN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// profiling
+// ---------------------------------------------------------------------------
+static hipEvent_t take_event(lsn_ctx* c) {
+  if (c->evnext == c->evpool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    c->evpool.push_back(e);
+  }
+  return c->evpool[c->evnext++];
+}
+
+static bool prof_begin(lsn_ctx* c, lsn_ctx::ProfRec* r, hipStream_t s) {
+  if (!c->profiling) return false;
+  r->e0 = take_event(c);
+  r->e1 = take_event(c);
+  if (!r->e0 || !r->e1) return false;
+  return hipEventRecord(r->e0, s) == hipSuccess;
+}
+
+static void prof_end(lsn_ctx* c, lsn_ctx::ProfRec& r, hipStream_t s) {
+  if (hipEventRecord(r.e1, s) == hipSuccess) c->prof.push_back(r);
+}
+
+// every GEMM of a context goes through here; the NF4 ones can be timed
+static hipError_t cgemm(lsn_ctx* c, const GemmParams& p, int opa, int opb, int batch) {
+  lsn_ctx::ProfRec r{0, opa, opb, gemm_tile(p.M, p.N, batch),
+                     2.0 * p.M * p.N * (double)p.K * p.nseg * batch, nullptr, nullptr};
+  const bool on = (opb == B_NF4_K || opb == B_NF4_R) && prof_begin(c, &r, c->cs);
+  const hipError_t e = gemm(p, opa, opb, batch, c->cs);
+  if (on) prof_end(c, r, c->cs);
+  return e;
 }
 
 // ---------------------------------------------------------------------------
@@ -319,7 +364,10 @@ static lsn_status copy_into_slot(lsn_ctx* c, int layer, int s) {
   } else {
     src = c->store + (uint64_t)layer * c->rec_bytes;
   }
+  lsn_ctx::ProfRec r{1, 0, 0, 0, (double)c->rec_bytes, nullptr, nullptr};
+  const bool on = prof_begin(c, &r, c->copy);
   HIPCHK(c, hipMemcpyAsync(dst, src, c->rec_bytes, hipMemcpyHostToDevice, c->copy));
+  if (on) prof_end(c, r, c->copy);
   HIPCHK(c, hipEventRecord(c->copy_done[s], c->copy));
   c->copy_issued[s] = true;
   c->slot_layer[s] = layer;
@@ -486,7 +534,7 @@ static hipError_t nf4_fwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const ui
     p.ldbe = kext;
     p.kext = kext;
   }
-  return gemm(p, A_BF16_K, B_NF4_K, 1, c->cs);
+  return cgemm(c, p, A_BF16_K, B_NF4_K, 1);
 }
 
 // dX = dY W_group (+ low-rank extension); dY is fp32 (opa A_F32_K) or bf16.
@@ -512,7 +560,7 @@ static hipError_t nf4_bwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const vo
     p.ldbe = kext;
     p.kext = kext;
   }
-  return gemm(p, opa, B_NF4_R, 1, c->cs);
+  return cgemm(c, p, opa, B_NF4_R, 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -545,7 +593,7 @@ static lsn_status layer_forward(lsn_ctx* c, int layer, const uint8_t* rec, const
     p.C = c->scores; p.ldc = S;
     p.sC_o = (int64_t)nq * S * S; p.sC_i = (int64_t)S * S;
     p.alpha = 1.0f / sqrtf((float)d);
-    HIPCHK(c, gemm(p, A_BF16_K, B_BF16_K, c->n_seq * nq, s));
+    HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_K, c->n_seq * nq));
   }
   softmax_causal(c->scores, c->Pf, c->Pb, S, (int64_t)c->n_seq * nq * S, s);
   {  // O = P V
@@ -558,7 +606,7 @@ static lsn_status layer_forward(lsn_ctx* c, int layer, const uint8_t* rec, const
     p.sB_o = (int64_t)S * QKV; p.sB_i = d;
     p.C = c->O; p.ldc = QD; p.cmode = C_BF16;
     p.sC_o = (int64_t)S * QD; p.sC_i = d;
-    HIPCHK(c, gemm(p, A_BF16_K, B_BF16_R, c->n_seq * nq, s));
+    HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, c->n_seq * nq));
   }
   kext = lora_fwd_ext(c, layer, G_O, c->O, QD, T);
   HIPCHK(c, nf4_fwd_gemm(c, rec, G_O, c->O, T, kext, c->h2, C_F32_RES, h));
@@ -609,7 +657,7 @@ static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, cons
     p.sB_o = (int64_t)S * QKV; p.sB_i = d;
     p.C = c->scores; p.ldc = S;
     p.sC_o = (int64_t)nq * S * S; p.sC_i = (int64_t)S * S;
-    HIPCHK(c, gemm(p, A_BF16_K, B_BF16_K, Z, s));
+    HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_K, Z));
   }
   {  // dV[kv] = sum over its q heads of P^T dO
     GemmParams p = base_params(c);
@@ -622,7 +670,7 @@ static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, cons
     p.nseg = grp;
     p.C = c->dqkv + QD + KVD; p.ldc = QKV;
     p.sC_o = (int64_t)S * QKV; p.sC_i = d;
-    HIPCHK(c, gemm(p, A_BF16_R, B_BF16_R, c->n_seq * nkv, s));
+    HIPCHK(c, cgemm(c, p, A_BF16_R, B_BF16_R, c->n_seq * nkv));
   }
   softmax_bwd(c->Pf, c->scores, c->Pb, S, (int64_t)Z * S, s);  // dS (bf16) over Pb
   const float scale = 1.0f / sqrtf((float)d);
@@ -637,7 +685,7 @@ static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, cons
     p.C = c->dqkv; p.ldc = QKV;
     p.sC_o = (int64_t)S * QKV; p.sC_i = d;
     p.alpha = scale;
-    HIPCHK(c, gemm(p, A_BF16_K, B_BF16_R, Z, s));
+    HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, Z));
   }
   {  // dK[kv] = scale sum over its q heads of dS^T Q
     GemmParams p = base_params(c);
@@ -651,7 +699,7 @@ static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, cons
     p.C = c->dqkv + QD; p.ldc = QKV;
     p.sC_o = (int64_t)S * QKV; p.sC_i = d;
     p.alpha = scale;
-    HIPCHK(c, gemm(p, A_BF16_R, B_BF16_R, c->n_seq * nkv, s));
+    HIPCHK(c, cgemm(c, p, A_BF16_R, B_BF16_R, c->n_seq * nkv));
   }
   rope_bwd(c->dqkv, c->dqkvb, T, S, nq, nkv, d, g.rope_theta, s);
   kext = lora_bwd_ext(c, layer, G_QKV, c->dqkv, QKV, c->n1, H, T);
@@ -857,6 +905,7 @@ void lsn_destroy(lsn_ctx* c) {
     if (c->slot_free[i]) (void)hipEventDestroy(c->slot_free[i]);
     if (c->bounce[i]) (void)hipHostFree(c->bounce[i]);
   }
+  for (hipEvent_t e : c->evpool) (void)hipEventDestroy(e);
   if (c->copy) (void)hipStreamDestroy(c->copy);
   if (c->store) (void)hipHostFree(c->store);
   if (c->fd >= 0) close(c->fd);
@@ -1041,7 +1090,7 @@ static lsn_status lm_logits_chunk(lsn_ctx* c, int v0, int Vc) {
   p.A = c->nf; p.lda = c->cfg.hidden;
   p.B = c->lm_head + (int64_t)v0 * c->cfg.hidden; p.ldb = c->cfg.hidden;
   p.C = c->logits; p.ldc = Vc;
-  HIPCHK(c, gemm(p, A_BF16_K, B_BF16_K, 1, c->cs));
+  HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_K, 1));
   return LSN_OK;
 }
 
@@ -1081,7 +1130,7 @@ lsn_status lsn_lm_head_backward(lsn_ctx* c, const float* h, const int32_t* targe
     p.B = c->lm_head + (int64_t)v0 * H; p.ldb = H;
     p.C = c->dnf; p.ldc = H;
     p.cmode = (v0 == 0) ? C_F32 : C_F32_ACC;
-    HIPCHK(c, gemm(p, A_BF16_K, B_BF16_R, 1, c->cs));
+    HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, 1));
   }
   rmsnorm_bwd(h, c->final_norm, c->rstdf, c->dnf, nullptr, T, H, dh, c->cs);
   return launch_check(c);
@@ -1111,6 +1160,44 @@ lsn_status lsn_stats(const lsn_ctx* c, uint64_t* layer_loads, uint64_t* bytes_h2
   if (layer_loads) *layer_loads = c->loads;
   if (bytes_h2d) *bytes_h2d = c->bytes_h2d;
   if (ws_bytes) *ws_bytes = c->ws_needed;
+  return LSN_OK;
+}
+
+lsn_status lsn_set_profiling(lsn_ctx* c, int32_t on) {
+  CHECK_CTX(c);
+  HIPCHK(c, hipStreamSynchronize(c->copy));
+  HIPCHK(c, hipStreamSynchronize(c->cs));
+  c->prof.clear();
+  c->evnext = 0;
+  c->profiling = on != 0;
+  while (c->profiling && c->evpool.size() < 16384) {
+    hipEvent_t e;
+    HIPCHK(c, hipEventCreate(&e));
+    c->evpool.push_back(e);
+  }
+  return LSN_OK;
+}
+
+lsn_status lsn_profile_query(lsn_ctx* c, int32_t what, int32_t a, int32_t b, int32_t tile,
+                             uint64_t* count, double* work, double* ms) {
+  CHECK_CTX(c);
+  if (what != 0 && what != 1) return fail(c, LSN_ERR_INVALID, "bad profile kind");
+  HIPCHK(c, hipStreamSynchronize(c->copy));
+  HIPCHK(c, hipStreamSynchronize(c->cs));
+  uint64_t n = 0;
+  double w = 0, t = 0;
+  for (const auto& r : c->prof) {
+    if (r.what != what) continue;
+    if (what == 0 && (r.a != a || r.b != b || (tile >= 0 && r.tile != tile))) continue;
+    float e = 0.f;
+    HIPCHK(c, hipEventElapsedTime(&e, r.e0, r.e1));
+    n += 1;
+    w += r.work;
+    t += e;
+  }
+  if (count) *count = n;
+  if (work) *work = w;
+  if (ms) *ms = t;
   return LSN_OK;
 }
 

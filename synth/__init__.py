@@ -119,10 +119,15 @@ def sft_tokens(w):
     return tokens((w["n_seq"], w["seq_len"]), w["vocab"], w["wid"])
 
 
+def dpo_prompt_len(w, pair=DPO_PAIR):
+    """128 shared prompt tokens at seq 512; a quarter of shorter sequences."""
+    return min(pair["prompt_len"], w["seq_len"] // 4)
+
+
 def dpo_pair(w, pair=DPO_PAIR):
-    """(chosen [S], rejected [S]): a shared random prompt, then independent
-    random responses."""
-    S, P, V = pair["seq_len"], pair["prompt_len"], w["vocab"]
+    """(chosen [S], rejected [S]) at the workload's sequence length: a shared
+    random prompt, then independent random responses."""
+    S, P, V = w["seq_len"], dpo_prompt_len(w, pair), w["vocab"]
     prompt = tokens((P,), V, pair["wid"], TID_PROMPT)
     ch = tokens((S - P,), V, pair["wid"], TID_CHOSEN)
     rj = tokens((S - P,), V, pair["wid"], TID_REJECTED)
