@@ -37,13 +37,24 @@ struct GemmParams {
   int64_t ldr = 0;
   float alpha = 1.f;
   int cmode = C_F32;
+  // split-k scratch (fp32, split * M * N); without it the k range is not split
+  float* part = nullptr;
+  int64_t part_floats = 0;
+  int ksplit = 1;  // set by gemm()
   float levels[16] = {};  // NF4 code levels
 };
 
 enum { TILE_256x128 = 0, TILE_128x128 = 1, TILE_64x64 = 2 };
 
+struct GemmPlan {
+  int tile = TILE_64x64;
+  int split = 1;
+};
+
 hipError_t gemm(const GemmParams& p, int opa, int opb, int batch, hipStream_t s);
-// the tile configuration gemm() launches for this problem
-int gemm_tile(int M, int N, int batch);
+// the tile and split-k gemm() chooses for a problem
+GemmPlan gemm_plan(int M, int N, int K, int nseg, int batch);
+// fp32 scratch a split-k launch of this problem needs (0 when not split)
+int64_t gemm_partial_floats(int M, int N, int K, int nseg, int batch);
 
 }  // namespace lsn

@@ -190,6 +190,8 @@ struct LoadNf4K {  // B(n,k) from W^T[n, k] (forward); one code word = 8 k
 
 template <int ROWS>
 struct LoadNf4R {  // B(n,k) from W^T[k, n] (input gradient); task = 4 k x 8 n
+  // Lanes take consecutive k-groups: each wave's 8-byte LDS writes then hit
+  // every bank exactly twice (the minimum for 64 x 8 bytes).
   static constexpr int TASKS = ROWS * 2;  // 16 k-groups x ROWS/8 n-groups
   static_assert(TASKS <= NTHREADS, "one task per thread at most");
   uint32_t code[4];
@@ -200,7 +202,7 @@ struct LoadNf4R {  // B(n,k) from W^T[k, n] (input gradient); task = 4 k x 8 n
     const int t = threadIdx.x;
     active = t < TASKS;
     if (!active) return;
-    const int ng = t % (ROWS / 8), kg = t / (ROWS / 8);
+    const int kg = t & 15, ng = t >> 4;
     const int n = row0 + ng * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -218,17 +220,14 @@ struct LoadNf4R {  // B(n,k) from W^T[k, n] (input gradient); task = 4 k x 8 n
   LSN_DEV void store(uint16_t* lds, const float* lv) const {
     if (!active) return;
     const int t = threadIdx.x;
-    const int ng = t % (ROWS / 8), kg = t / (ROWS / 8);
-    float w[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) w[i][j] = lv[(code[i] >> (4 * j)) & 15u] * amax[i];
+    const int kg = t & 15, ng = t >> 4;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {  // LDS row n = ng*8 + j, k = kg*4 .. +3
       u32x2 o;
-      o[0] = pack_bf16x2(w[0][j], w[1][j]);
-      o[1] = pack_bf16x2(w[2][j], w[3][j]);
+      o[0] = pack_bf16x2(lv[(code[0] >> (4 * j)) & 15u] * amax[0],
+                         lv[(code[1] >> (4 * j)) & 15u] * amax[1]);
+      o[1] = pack_bf16x2(lv[(code[2] >> (4 * j)) & 15u] * amax[2],
+                         lv[(code[3] >> (4 * j)) & 15u] * amax[3]);
       *reinterpret_cast<u32x2*>(lds + (ng * 8 + j) * PITCH + kg * 4) = o;
     }
   }
@@ -287,7 +286,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
   LB lb;
 
   const int nkt = (p.K + BK - 1) / BK;
-  const int total = nkt * p.nseg;
+  // split-k: blockIdx.y takes k-tiles [it0, it1) of the nseg * nkt
+  const int ntile = nkt * p.nseg;
+  const int kper = (ntile + p.ksplit - 1) / p.ksplit;
+  const int it0 = min(ntile, (int)blockIdx.y * kper), it1 = min(ntile, it0 + kper);
 
   auto prefetch = [&](int it) {
     const int seg = it / nkt, k0 = (it % nkt) * BK;
@@ -312,14 +314,14 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
   };
 
   const int lr = lane & 31, lk = (lane >> 5) * 8;
-  if (total > 0) {
-    prefetch(0);
+  if (it1 > it0) {
+    prefetch(it0);
     __syncthreads();  // sLv visible
     store(0);
     __syncthreads();
-    for (int it = 0; it < total; ++it) {
-      const int cur = it & 1;
-      if (it + 1 < total) prefetch(it + 1);
+    for (int it = it0; it < it1; ++it) {
+      const int cur = (it - it0) & 1;
+      if (it + 1 < it1) prefetch(it + 1);
       const uint16_t* a_base = sA[cur] + (wm * WTM + lr) * PITCH + lk;
       const uint16_t* b_base = sB[cur] + (wn * WTN + lr) * PITCH + lk;
 #pragma unroll
@@ -337,13 +339,13 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
           for (int j = 0; j < TN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-      if (it + 1 < total) store(cur ^ 1);
+      if (it + 1 < it1) store(cur ^ 1);
       __syncthreads();
     }
   }
 
   // ---- LoRA extension: extra k columns read directly as fragments ----
-  if (p.kext > 0) {
+  if (p.kext > 0 && blockIdx.y == 0) {
     for (int e0 = 0; e0 < p.kext; e0 += 16) {
       bf16x8 af[TM], bfr[TN];
 #pragma unroll
@@ -381,6 +383,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
       for (int e = 0; e < 16; ++e) {
         const int m = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
         if (m >= p.M) continue;
+        if (p.ksplit > 1) {  // raw partial sum of this k range
+          p.part[((int64_t)blockIdx.y * p.M + m) * p.N + n] = acc[i][j][e];
+          continue;
+        }
         const float v = p.alpha * acc[i][j][e];
         const int64_t o = offC + (int64_t)m * p.ldc + n;
         switch (p.cmode) {
@@ -396,29 +402,78 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// split-k reduction: partial sums added in split order, then the epilogue
+// ---------------------------------------------------------------------------
+__global__ void gemm_reduce_k(const GemmParams p) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)p.M * p.N) return;
+  const int m = (int)(i / p.N), n = (int)(i % p.N);
+  float acc = 0.f;
+  for (int y = 0; y < p.ksplit; ++y) acc += p.part[((int64_t)y * p.M + m) * p.N + n];
+  const float v = p.alpha * acc;
+  const int64_t o = (int64_t)m * p.ldc + n;
+  switch (p.cmode) {
+    case C_F32: reinterpret_cast<float*>(p.C)[o] = v; break;
+    case C_F32_ACC: reinterpret_cast<float*>(p.C)[o] += v; break;
+    case C_F32_RES: reinterpret_cast<float*>(p.C)[o] = p.R[(int64_t)m * p.ldr + n] + v; break;
+    default: reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16_bits(v); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------
+// Tile and split-k choice.  M >= 256 takes the 256 x 128 tile (each
+// dequantized weight feeds 256 rows).  A single problem with fewer than 200
+// tiles splits its k range so that about 256 workgroups run (one per CU);
+// batched problems choose smaller tiles instead.
+GemmPlan gemm_plan(int M, int N, int K, int nseg, int batch) {
+  GemmPlan g;
+  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 127) / 128) * batch;
+  const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128) * batch;
+  const int64_t t64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64) * batch;
+  int64_t tiles;
+  if (batch == 1) {
+    if (M >= 256) { g.tile = TILE_256x128; tiles = t256; }
+    else if (M >= 128) { g.tile = TILE_128x128; tiles = t128; }
+    else { g.tile = TILE_64x64; tiles = t64; }
+    const int nkt = (K + 63) / 64 * nseg;
+    if (tiles < 200) {
+      int sp = (int)std::min<int64_t>(8, (256 + tiles - 1) / tiles);
+      sp = std::min(sp, std::max(1, nkt / 4));
+      g.split = std::max(sp, 1);
+    }
+  } else {
+    if (M >= 256 && t256 >= 192) g.tile = TILE_256x128;
+    else if (M >= 128 && t128 >= 128) g.tile = TILE_128x128;
+    else g.tile = TILE_64x64;
+  }
+  return g;
+}
+
+int64_t gemm_partial_floats(int M, int N, int K, int nseg, int batch) {
+  const GemmPlan g = gemm_plan(M, N, K, nseg, batch);
+  return g.split > 1 ? (int64_t)g.split * M * N : 0;
+}
+
 template <int BM, int BN, int OPA, int OPB>
 static hipError_t launch_t(const GemmParams& p, int batch, hipStream_t s) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, OPA, OPB>), dim3(tiles, 1, batch), dim3(NTHREADS), 0,
-                     s, p);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, OPA, OPB>), dim3(tiles, p.ksplit, batch),
+                     dim3(NTHREADS), 0, s, p);
+  if (p.ksplit > 1) {
+    const int64_t n = (int64_t)p.M * p.N;
+    hipLaunchKernelGGL(gemm_reduce_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
-// Large problems take the 256 x 128 tile (each dequantized weight feeds 256
-// rows); small ones trade reuse for enough workgroups to fill 256 CUs.
-int gemm_tile(int M, int N, int batch) {
-  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 127) / 128) * batch;
-  const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128) * batch;
-  if (M >= 256 && t256 >= 192) return TILE_256x128;
-  if (M >= 128 && t128 >= 128) return TILE_128x128;
-  return TILE_64x64;
-}
-
 template <int OPA, int OPB>
-static hipError_t launch_tiles(const GemmParams& p, int batch, hipStream_t s) {
-  switch (gemm_tile(p.M, p.N, batch)) {
+static hipError_t launch_tiles(GemmParams p, int batch, hipStream_t s) {
+  const GemmPlan g = gemm_plan(p.M, p.N, p.K, p.nseg, batch);
+  p.ksplit = g.split;
+  if (p.ksplit > 1 && (!p.part || p.part_floats < (int64_t)p.ksplit * p.M * p.N)) p.ksplit = 1;
+  switch (g.tile) {
     case TILE_256x128: return launch_t<256, 128, OPA, OPB>(p, batch, s);
     case TILE_128x128: return launch_t<128, 128, OPA, OPB>(p, batch, s);
     default: return launch_t<64, 64, OPA, OPB>(p, batch, s);

@@ -1,0 +1,35 @@
+// Low-rank products of the LoRA branch (lora.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace lsn {
+
+// out(row, j) (+)= scale * sum_k X(row, k) W(k, j) for j < r (r <= 16);
+// ext(row, j) = bf16(ext_scale * sum) for j < r and 0 for r <= j < 16.
+struct LoraMM {
+  const void* X = nullptr;
+  int x_f32 = 0;   // X element type: 0 bf16, 1 fp32
+  int trans = 0;   // 0: X[row*ldx + k]; 1: X[k*ldx + row]
+  int64_t ldx = 0;
+  int R = 0, K = 0;
+  const float* W = nullptr;  // W(k, j) = W[k*sk + j*sj]
+  int64_t sk = 0, sj = 0;
+  int r = 0;
+  float* out = nullptr;      // out(row, j) at out[row*so_r + j*so_j]; may be null
+  int64_t so_r = 0, so_j = 0;
+  int accumulate = 0;
+  float scale = 1.f;
+  uint16_t* ext = nullptr;   // optional bf16 copy
+  int64_t ld_ext = 0;
+  float ext_scale = 1.f;
+};
+
+// floats of split-k scratch lora_mm wants for these sizes (0: no split)
+int64_t lora_mm_partial_floats(int R, int K);
+// partial may be null (then one pass over k)
+hipError_t lora_mm(const LoraMM& a, float* partial, int64_t partial_floats, hipStream_t s);
+
+}  // namespace lsn

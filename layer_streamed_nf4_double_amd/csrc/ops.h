@@ -20,17 +20,6 @@ void swiglu_bwd(const float* gu, const float* da, uint16_t* dgu, float* dguf, in
                 hipStream_t s);
 void embed(const int32_t* tok, const uint16_t* table, int T, int H, int V, float* h,
            hipStream_t s);
-void skinny_bf16(const uint16_t* X, int64_t ldx, const float* W, int64_t sk, int64_t sj, int M,
-                 int K, int r, float* out, uint16_t* ext, int64_t ldext, float scale,
-                 hipStream_t s);
-void skinny_f32(const float* X, int64_t ldx, const float* W, int64_t sk, int64_t sj, int M, int K,
-                int r, float* out, uint16_t* ext, int64_t ldext, float scale, hipStream_t s);
-void lora_dA_bf16(const uint16_t* X, int64_t ldx, const float* U, int M, int K, int r, float sc,
-                  float* dA, hipStream_t s);
-void lora_dB_f32(const float* T, const float* DY, int64_t ldy, int M, int N, int r, float sc,
-                 float* dB, hipStream_t s);
-void lora_dB_bf16(const float* T, const uint16_t* DY, int64_t ldy, int M, int N, int r, float sc,
-                  float* dB, hipStream_t s);
 void lora_ext(const float* W, int64_t srow, int64_t sj, int R, int r, uint16_t* out, int64_t ld,
               int c0, hipStream_t s);
 void lse_chunk(const float* logits, int T, int Vc, int v0, const int32_t* tgt, float* run_m,

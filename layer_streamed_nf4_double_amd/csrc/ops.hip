@@ -1,6 +1,6 @@
 // Per-layer kernels around the GEMMs: RMSNorm, RoPE, causal softmax, SwiGLU,
-// embedding gather, LoRA skinny products and gradients, the vocabulary-chunk
-// log-softmax, losses, SGD, NF4 dequantization and small converters.
+// embedding gather, LoRA operand packing, the vocabulary-chunk log-softmax,
+// losses, SGD, NF4 dequantization and small converters.
 //
 // Every reduction runs in a fixed order (one owner thread, or a fixed
 // butterfly + fixed cross-wave order), with no atomics, so a run is
@@ -190,119 +190,6 @@ __global__ void embed_k(const int32_t* __restrict__ tok, const uint16_t* __restr
   const bool ok = v >= 0 && v < V;
   for (int i = threadIdx.x; i < H; i += blockDim.x)
     h[t * H + i] = ok ? bf16_to_f32(table[v * H + i]) : __builtin_nanf("");
-}
-
-// ---------------------------------------------------------------------------
-// LoRA skinny products (r <= 16)
-//   out[m, j] = sum_k X(m, k) * W(k, j),  W(k, j) = Wp[k*sk + j*sj]
-// 16 rows per block, 256 threads = 16 rows x 16 ranks; K in chunks of 64
-// staged through LDS; each output summed by one thread in k order.
-// Optional bf16(scale * out) copy into ext[m*ldext + j].
-// ---------------------------------------------------------------------------
-template <typename TX>
-__global__ void skinny_k(const TX* __restrict__ X, int64_t ldx, const float* __restrict__ Wp,
-                         int64_t sk, int64_t sj, int M, int K, int r, float* __restrict__ out,
-                         uint16_t* __restrict__ ext, int64_t ldext, float scale) {
-  __shared__ float sx[16][65];
-  __shared__ float sw[64][17];
-  const int m0 = blockIdx.x * 16;
-  const int tr = threadIdx.x >> 4, tj = threadIdx.x & 15;
-  float acc = 0.f;
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    for (int i = threadIdx.x; i < 16 * 64; i += 256) {
-      const int rr = i >> 6, kk = i & 63;
-      const int m = m0 + rr, k = k0 + kk;
-      float v = 0.f;
-      if (m < M && k < K) {
-        if constexpr (sizeof(TX) == 2)
-          v = bf16_to_f32(X[(int64_t)m * ldx + k]);
-        else
-          v = X[(int64_t)m * ldx + k];
-      }
-      sx[rr][kk] = v;
-    }
-    for (int i = threadIdx.x; i < 64 * 16; i += 256) {
-      const int kk = i >> 4, j = i & 15;
-      const int k = k0 + kk;
-      sw[kk][j] = (k < K && j < r) ? Wp[(int64_t)k * sk + (int64_t)j * sj] : 0.f;
-    }
-    __syncthreads();
-    const int kn = min(64, K - k0);
-    for (int kk = 0; kk < kn; ++kk) acc += sx[tr][kk] * sw[kk][tj];
-    __syncthreads();
-  }
-  const int m = m0 + tr;
-  if (m < M && tj < r) {
-    out[(int64_t)m * r + tj] = acc;
-    if (ext) ext[(int64_t)m * ldext + tj] = f32_to_bf16_bits(scale * acc);
-  }
-  if (m < M && ext && tj >= r) ext[(int64_t)m * ldext + tj] = 0;  // pad ranks to 16
-}
-
-// dA[k, j] += s * sum_m X[m, k] * U[m, j]   (one thread per k, all r ranks)
-template <typename TX>
-__global__ void lora_dA_k(const TX* __restrict__ X, int64_t ldx, const float* __restrict__ U,
-                          int M, int K, int r, float s, float* __restrict__ dA) {
-  __shared__ float su[256][16];
-  const int k = blockIdx.x * blockDim.x + threadIdx.x;
-  float acc[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-  for (int m0 = 0; m0 < M; m0 += 256) {
-    const int mn = min(256, M - m0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < 256 * 16; i += blockDim.x) {
-      const int mm = i >> 4, j = i & 15;
-      su[mm][j] = (mm < mn && j < r) ? U[(int64_t)(m0 + mm) * r + j] : 0.f;
-    }
-    __syncthreads();
-    if (k < K) {
-      for (int mm = 0; mm < mn; ++mm) {
-        float x;
-        if constexpr (sizeof(TX) == 2)
-          x = bf16_to_f32(X[(int64_t)(m0 + mm) * ldx + k]);
-        else
-          x = X[(int64_t)(m0 + mm) * ldx + k];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[j] += x * su[mm][j];
-      }
-    }
-  }
-  if (k < K)
-    for (int j = 0; j < r; ++j) dA[(int64_t)k * r + j] += s * acc[j];
-}
-
-// dB[j, n] += s * sum_m T[m, j] * DY[m, n]   (one thread per n, all r ranks)
-template <typename TY>
-__global__ void lora_dB_k(const float* __restrict__ T, const TY* __restrict__ DY, int64_t ldy,
-                          int M, int N, int r, float s, float* __restrict__ dB) {
-  __shared__ float st[256][16];
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  float acc[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-  for (int m0 = 0; m0 < M; m0 += 256) {
-    const int mn = min(256, M - m0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < 256 * 16; i += blockDim.x) {
-      const int mm = i >> 4, j = i & 15;
-      st[mm][j] = (mm < mn && j < r) ? T[(int64_t)(m0 + mm) * r + j] : 0.f;
-    }
-    __syncthreads();
-    if (n < N) {
-      for (int mm = 0; mm < mn; ++mm) {
-        float y;
-        if constexpr (sizeof(TY) == 2)
-          y = bf16_to_f32(DY[(int64_t)(m0 + mm) * ldy + n]);
-        else
-          y = DY[(int64_t)(m0 + mm) * ldy + n];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[j] += st[mm][j] * y;
-      }
-    }
-  }
-  if (n < N)
-    for (int j = 0; j < r; ++j) dB[(int64_t)j * N + n] += s * acc[j];
 }
 
 // out[row*ld + c0 + j] = bf16(W(row, j)), W(row, j) = Wp[row*srow + j*sj], j < 16
@@ -509,32 +396,6 @@ void swiglu_bwd(const float* gu, const float* da, uint16_t* dgu, float* dguf, in
 void embed(const int32_t* tok, const uint16_t* table, int T, int H, int V, float* h,
            hipStream_t s) {
   hipLaunchKernelGGL(embed_k, dim3(T), dim3(256), 0, s, tok, table, H, V, h);
-}
-void skinny_bf16(const uint16_t* X, int64_t ldx, const float* W, int64_t sk, int64_t sj, int M,
-                 int K, int r, float* out, uint16_t* ext, int64_t ldext, float scale,
-                 hipStream_t s) {
-  hipLaunchKernelGGL(skinny_k<uint16_t>, dim3(nb(M, 16)), dim3(256), 0, s, X, ldx, W, sk, sj, M,
-                     K, r, out, ext, ldext, scale);
-}
-void skinny_f32(const float* X, int64_t ldx, const float* W, int64_t sk, int64_t sj, int M, int K,
-                int r, float* out, uint16_t* ext, int64_t ldext, float scale, hipStream_t s) {
-  hipLaunchKernelGGL(skinny_k<float>, dim3(nb(M, 16)), dim3(256), 0, s, X, ldx, W, sk, sj, M, K,
-                     r, out, ext, ldext, scale);
-}
-void lora_dA_bf16(const uint16_t* X, int64_t ldx, const float* U, int M, int K, int r, float sc,
-                  float* dA, hipStream_t s) {
-  hipLaunchKernelGGL(lora_dA_k<uint16_t>, dim3(nb(K, 256)), dim3(256), 0, s, X, ldx, U, M, K, r,
-                     sc, dA);
-}
-void lora_dB_f32(const float* T, const float* DY, int64_t ldy, int M, int N, int r, float sc,
-                 float* dB, hipStream_t s) {
-  hipLaunchKernelGGL(lora_dB_k<float>, dim3(nb(N, 256)), dim3(256), 0, s, T, DY, ldy, M, N, r, sc,
-                     dB);
-}
-void lora_dB_bf16(const float* T, const uint16_t* DY, int64_t ldy, int M, int N, int r, float sc,
-                  float* dB, hipStream_t s) {
-  hipLaunchKernelGGL(lora_dB_k<uint16_t>, dim3(nb(N, 256)), dim3(256), 0, s, T, DY, ldy, M, N, r,
-                     sc, dB);
 }
 void lora_ext(const float* W, int64_t srow, int64_t sj, int R, int r, uint16_t* out, int64_t ld,
               int c0, hipStream_t s) {

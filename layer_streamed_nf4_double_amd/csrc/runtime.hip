@@ -33,6 +33,7 @@
 #include "../../include/lsn.h"
 #include "gemm.h"
 #include "host_codec.h"
+#include "lora.h"
 #include "ops.h"
 
 using namespace lsn;
@@ -95,8 +96,8 @@ struct lsn_ctx {
   // activation scratch (one layer at max_tokens)
   uint16_t *n1, *qkvb, *Pb, *O, *n2, *a, *dgu, *dO, *dqkvb, *aext, *bext, *nf, *dlog;
   float *rstd1, *qkv, *scores, *Pf, *h2, *rstd2, *gu, *da, *dguf, *dn, *dh2, *dqkv, *lt, *lu,
-      *rstdf, *logits, *run_m, *run_s, *tlogit, *lse, *dnf;
-  int64_t ext_rows = 0;
+      *rstdf, *logits, *run_m, *run_s, *tlogit, *lse, *dnf, *lpart, *gpart;
+  int64_t ext_rows = 0, lpart_floats = 0, gpart_floats = 0;
 
   // pass state
   int pass_kind = -1, n_seq = 0, seq_len = 0, T = 0;
@@ -202,8 +203,10 @@ static void prof_end(lsn_ctx* c, lsn_ctx::ProfRec& r, hipStream_t s) {
 }
 
 // every GEMM of a context goes through here; the NF4 ones can be timed
-static hipError_t cgemm(lsn_ctx* c, const GemmParams& p, int opa, int opb, int batch) {
-  lsn_ctx::ProfRec r{0, opa, opb, gemm_tile(p.M, p.N, batch),
+static hipError_t cgemm(lsn_ctx* c, GemmParams p, int opa, int opb, int batch) {
+  p.part = c->gpart;
+  p.part_floats = c->gpart_floats;
+  lsn_ctx::ProfRec r{0, opa, opb, gemm_plan(p.M, p.N, p.K, p.nseg, batch).tile,
                      2.0 * p.M * p.N * (double)p.K * p.nseg * batch, nullptr, nullptr};
   const bool on = (opb == B_NF4_K || opb == B_NF4_R) && prof_begin(c, &r, c->cs);
   const hipError_t e = gemm(p, opa, opb, batch, c->cs);
@@ -318,6 +321,24 @@ static uint64_t carve(lsn_ctx* c, char* base) {
   c->dqkv = (float*)P(T * QKV * 4);
   c->dqkvb = (uint16_t*)P(T * QKV * 2);
   c->lt = (float*)P(NPROJ * T * 16 * 4);
+  c->lpart_floats = 0;
+  for (int p = 0; p < NPROJ; ++p)
+    if (c->targeted(p))
+      c->lpart_floats = std::max<int64_t>(
+          {c->lpart_floats, lora_mm_partial_floats((int)T, (int)c->K[p]),
+           lora_mm_partial_floats((int)T, (int)c->N[p]), lora_mm_partial_floats((int)c->K[p], (int)T),
+           lora_mm_partial_floats((int)c->N[p], (int)T)});
+  c->lpart = (float*)P(std::max<int64_t>(c->lpart_floats, 1) * 4);
+  {  // split-k scratch of the largest single-problem GEMM at max_tokens
+    const int64_t Vc0 = std::min<int64_t>(V, VCHUNK);
+    const int64_t shapes[][3] = {{QKV, H}, {H, QD}, {2 * F, H}, {H, F}, {F, H},
+                                 {H, 2 * F}, {QD, H}, {H, QKV}, {Vc0, H}, {H, Vc0}};
+    c->gpart_floats = 0;
+    for (const auto& sh : shapes)
+      c->gpart_floats = std::max<int64_t>(
+          c->gpart_floats, gemm_partial_floats((int)T, (int)sh[0], (int)sh[1], 1, 1));
+    c->gpart = (float*)P(std::max<int64_t>(c->gpart_floats, 1) * 4);
+  }
   c->lu = (float*)P(T * 16 * 4);
   c->ext_rows = std::max<int64_t>({QKV, 2 * F, H, QD, F});
   c->aext = (uint16_t*)P(T * 48 * 2);
@@ -470,8 +491,12 @@ static int lora_fwd_ext(lsn_ctx* c, int layer, Group g, const uint16_t* x, int64
   for (int p = g.first; p < g.first + g.count; ++p) {
     if (c->targeted(p)) {
       const int64_t K = c->K[p], N = c->N[p];
-      skinny_bf16(x, ldx, c->A_of(layer, p), r, 1, T, (int)K, r, c->lt + (int64_t)p * T * 16,
-                  c->aext + 16 * slot, kext, s, c->cs);
+      LoraMM m;  // t = x A, aext = bf16(s t)
+      m.X = x; m.ldx = ldx; m.R = T; m.K = (int)K;
+      m.W = c->A_of(layer, p); m.sk = r; m.sj = 1; m.r = r;
+      m.out = c->lt + (int64_t)p * T * 16; m.so_r = r; m.so_j = 1;
+      m.ext = c->aext + 16 * slot; m.ld_ext = kext; m.ext_scale = s;
+      (void)lora_mm(m, c->lpart, c->lpart_floats, c->cs);
       lora_ext(c->B_of(layer, p), 1, N, (int)N, r, c->bext + row0 * kext, kext, 16 * slot, c->cs);
       ++slot;
     }
@@ -497,11 +522,22 @@ static int lora_bwd_ext(lsn_ctx* c, int layer, Group g, const float* dyf, int64_
       const int64_t K = c->K[p], N = c->N[p];
       const float* dy = dyf + col0;
       // u = dy B^T : W(k = n, j) = B[j*N + n]
-      skinny_f32(dy, lddy, c->B_of(layer, p), 1, N, T, (int)N, r, c->lu, c->aext + 16 * slot,
-                 kext, s, c->cs);
-      lora_dA_bf16(x, ldx, c->lu, T, (int)K, r, s, c->dA_of(layer, p), c->cs);
-      lora_dB_f32(c->lt + (int64_t)p * T * 16, dy, lddy, T, (int)N, r, s, c->dB_of(layer, p),
-                  c->cs);
+      LoraMM u;  // u = dy B^T, aext = bf16(s u)
+      u.X = dy; u.x_f32 = 1; u.ldx = lddy; u.R = T; u.K = (int)N;
+      u.W = c->B_of(layer, p); u.sk = 1; u.sj = N; u.r = r;
+      u.out = c->lu; u.so_r = r; u.so_j = 1;
+      u.ext = c->aext + 16 * slot; u.ld_ext = kext; u.ext_scale = s;
+      (void)lora_mm(u, c->lpart, c->lpart_floats, c->cs);
+      LoraMM ga;  // dA += s x^T u
+      ga.X = x; ga.trans = 1; ga.ldx = ldx; ga.R = (int)K; ga.K = T;
+      ga.W = c->lu; ga.sk = r; ga.sj = 1; ga.r = r;
+      ga.out = c->dA_of(layer, p); ga.so_r = r; ga.so_j = 1; ga.accumulate = 1; ga.scale = s;
+      (void)lora_mm(ga, c->lpart, c->lpart_floats, c->cs);
+      LoraMM gb;  // dB += s t^T dy, stored dB[j*N + n]
+      gb.X = dy; gb.x_f32 = 1; gb.trans = 1; gb.ldx = lddy; gb.R = (int)N; gb.K = T;
+      gb.W = c->lt + (int64_t)p * T * 16; gb.sk = r; gb.sj = 1; gb.r = r;
+      gb.out = c->dB_of(layer, p); gb.so_r = 1; gb.so_j = N; gb.accumulate = 1; gb.scale = s;
+      (void)lora_mm(gb, c->lpart, c->lpart_floats, c->cs);
       lora_ext(c->A_of(layer, p), r, 1, (int)K, r, c->bext, kext, 16 * slot, c->cs);
       ++slot;
     }
@@ -742,13 +778,37 @@ lsn_status lsn_nf4_dequant(const uint8_t* codes, const float* absmax, uint64_t n
   return hipGetLastError() == hipSuccess ? LSN_OK : LSN_ERR_HIP;
 }
 
-// scratch of the stateless projection: t/u fp32 [M,16], aext bf16 [M,16],
-// bext bf16 [max(N,K),16]
+// Scratch of the stateless projection: t, u fp32 [M,16]; aext bf16 [M,16];
+// bext bf16 [max(N,K),16]; split-k partial sums of the low-rank products and
+// of the GEMM.
+struct LinScratch {
+  float *t = nullptr, *u = nullptr, *lpart = nullptr, *gpart = nullptr;
+  uint16_t *aext = nullptr, *bext = nullptr;
+  int64_t lpf = 0, gpf = 0;
+  uint64_t bytes = 0;
+};
+
+static LinScratch lin_scratch(char* base, int M, int K, int N) {
+  LinScratch L;
+  Carver cv;
+  auto P = [&](uint64_t b) -> char* { const uint64_t o = cv.take(b); return base ? base + o : nullptr; };
+  L.lpf = std::max<int64_t>({lora_mm_partial_floats(M, K), lora_mm_partial_floats(M, N),
+                             lora_mm_partial_floats(K, M), lora_mm_partial_floats(N, M)});
+  L.gpf = std::max(gemm_partial_floats(M, N, K, 1, 1), gemm_partial_floats(M, K, N, 1, 1));
+  L.t = (float*)P((uint64_t)M * 16 * 4);
+  L.u = (float*)P((uint64_t)M * 16 * 4);
+  L.aext = (uint16_t*)P((uint64_t)M * 16 * 2);
+  L.bext = (uint16_t*)P((uint64_t)std::max(N, K) * 16 * 2);
+  L.lpart = (float*)P((uint64_t)L.lpf * 4);
+  L.gpart = (float*)P((uint64_t)L.gpf * 4);
+  L.bytes = align_up(cv.off, 256);
+  return L;
+}
+
 lsn_status lsn_nf4_linear_scratch_bytes(int32_t M, int32_t K, int32_t N, int32_t r,
                                         uint64_t* bytes) {
   if (!bytes || M < 0 || K <= 0 || N <= 0 || r < 0 || r > 16) return LSN_ERR_INVALID;
-  *bytes = align_up((uint64_t)M * 16 * 4, 256) * 2 + align_up((uint64_t)M * 16 * 2, 256) +
-           align_up((uint64_t)std::max(N, K) * 16 * 2, 256);
+  *bytes = lin_scratch(nullptr, M, K, N).bytes;
   return LSN_OK;
 }
 
@@ -759,10 +819,15 @@ static lsn_status linear_args_ok(const uint8_t* codes, const float* absmax, int3
   if (K % 16 || N % 8) return LSN_ERR_INVALID;
   if (r < 0 || r > 16) return LSN_ERR_INVALID;
   if (r > 0 && (!A || !B)) return LSN_ERR_INVALID;
-  uint64_t need = 0;
-  lsn_nf4_linear_scratch_bytes(M, K, N, r, &need);
-  if (r > 0 && (!scratch || sb < need)) return LSN_ERR_INVALID;
+  if (r > 0 && (!scratch || sb < lin_scratch(nullptr, M, K, N).bytes)) return LSN_ERR_INVALID;
   return LSN_OK;
+}
+
+// Without enough scratch (allowed when r = 0) the GEMM runs without split-k.
+static LinScratch lin_scratch_or_none(void* scratch, uint64_t sb, int M, int K, int N) {
+  LinScratch L = lin_scratch(nullptr, M, K, N);
+  if (!scratch || sb < L.bytes) return LinScratch();
+  return lin_scratch((char*)scratch, M, K, N);
 }
 
 lsn_status lsn_nf4_linear_fwd(const uint8_t* codes, const float* absmax, int32_t M, int32_t K,
@@ -773,20 +838,23 @@ lsn_status lsn_nf4_linear_fwd(const uint8_t* codes, const float* absmax, int32_t
   if (st != LSN_OK || !Y) return st != LSN_OK ? st : LSN_ERR_INVALID;
   if (M == 0) return LSN_OK;
   hipStream_t hs = (hipStream_t)hip_stream;
-  char* sc = (char*)scratch;
-  float* t = (float*)sc;
-  uint16_t* aext = (uint16_t*)(sc + align_up((uint64_t)M * 16 * 4, 256) * 2);
-  uint16_t* bext = (uint16_t*)((char*)aext + align_up((uint64_t)M * 16 * 2, 256));
+  const LinScratch L = lin_scratch_or_none(scratch, sb, M, K, N);
   GemmParams p;
   nf4_levels(p.levels);
   p.M = M; p.N = N; p.K = K;
   p.A = X; p.lda = K;
   p.B = codes; p.absmax = absmax; p.rowlen = K;
   p.C = Y; p.ldc = N;
+  p.part = L.gpart; p.part_floats = L.gpf;
   if (r > 0) {
-    skinny_bf16(X, K, A, r, 1, M, K, r, t, aext, 16, s, hs);
-    lora_ext(B, 1, N, N, r, bext, 16, 0, hs);
-    p.Aext = aext; p.ldae = 16; p.Bext = bext; p.ldbe = 16; p.kext = 16;
+    LoraMM m;  // t = X A, aext = bf16(s t)
+    m.X = X; m.ldx = K; m.R = M; m.K = K;
+    m.W = A; m.sk = r; m.sj = 1; m.r = r;
+    m.out = L.t; m.so_r = r; m.so_j = 1;
+    m.ext = L.aext; m.ld_ext = 16; m.ext_scale = s;
+    (void)lora_mm(m, L.lpart, L.lpf, hs);
+    lora_ext(B, 1, N, N, r, L.bext, 16, 0, hs);
+    p.Aext = L.aext; p.ldae = 16; p.Bext = L.bext; p.ldbe = 16; p.kext = 16;
   }
   return gemm(p, A_BF16_K, B_NF4_K, 1, hs) == hipSuccess && hipGetLastError() == hipSuccess
              ? LSN_OK
@@ -805,27 +873,39 @@ lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t
     fill_u32(dA, 0, (int64_t)K * r, hs);
     fill_u32(dB, 0, (int64_t)r * N, hs);
   }
-  if (M == 0) {
-    return hipGetLastError() == hipSuccess ? LSN_OK : LSN_ERR_HIP;
-  }
-  char* sc = (char*)scratch;
-  float* t = (float*)sc;
-  float* u = (float*)(sc + align_up((uint64_t)M * 16 * 4, 256));
-  uint16_t* aext = (uint16_t*)(sc + align_up((uint64_t)M * 16 * 4, 256) * 2);
-  uint16_t* bext = (uint16_t*)((char*)aext + align_up((uint64_t)M * 16 * 2, 256));
+  if (M == 0) return hipGetLastError() == hipSuccess ? LSN_OK : LSN_ERR_HIP;
+  const LinScratch L = lin_scratch_or_none(scratch, sb, M, K, N);
   GemmParams p;
   nf4_levels(p.levels);
   p.M = M; p.N = K; p.K = N;
   p.A = dY; p.lda = N;
   p.B = codes; p.absmax = absmax; p.rowlen = K;
   p.C = dX; p.ldc = K;
+  p.part = L.gpart; p.part_floats = L.gpf;
   if (r > 0) {
-    skinny_bf16(X, K, A, r, 1, M, K, r, t, nullptr, 0, s, hs);          // t = X A
-    skinny_bf16(dY, N, B, 1, N, M, N, r, u, aext, 16, s, hs);           // u = dY B^T
-    lora_dA_bf16(X, K, u, M, K, r, s, dA, hs);                          // dA = s X^T u
-    lora_dB_bf16(t, dY, N, M, N, r, s, dB, hs);                         // dB = s t^T dY
-    lora_ext(A, r, 1, K, r, bext, 16, 0, hs);                           // bext = A
-    p.Aext = aext; p.ldae = 16; p.Bext = bext; p.ldbe = 16; p.kext = 16;
+    LoraMM m;  // t = X A
+    m.X = X; m.ldx = K; m.R = M; m.K = K;
+    m.W = A; m.sk = r; m.sj = 1; m.r = r;
+    m.out = L.t; m.so_r = r; m.so_j = 1;
+    (void)lora_mm(m, L.lpart, L.lpf, hs);
+    LoraMM uu;  // u = dY B^T, aext = bf16(s u)
+    uu.X = dY; uu.ldx = N; uu.R = M; uu.K = N;
+    uu.W = B; uu.sk = 1; uu.sj = N; uu.r = r;
+    uu.out = L.u; uu.so_r = r; uu.so_j = 1;
+    uu.ext = L.aext; uu.ld_ext = 16; uu.ext_scale = s;
+    (void)lora_mm(uu, L.lpart, L.lpf, hs);
+    LoraMM ga;  // dA += s X^T u
+    ga.X = X; ga.trans = 1; ga.ldx = K; ga.R = K; ga.K = M;
+    ga.W = L.u; ga.sk = r; ga.sj = 1; ga.r = r;
+    ga.out = dA; ga.so_r = r; ga.so_j = 1; ga.accumulate = 1; ga.scale = s;
+    (void)lora_mm(ga, L.lpart, L.lpf, hs);
+    LoraMM gb;  // dB += s t^T dY
+    gb.X = dY; gb.trans = 1; gb.ldx = N; gb.R = N; gb.K = M;
+    gb.W = L.t; gb.sk = r; gb.sj = 1; gb.r = r;
+    gb.out = dB; gb.so_r = 1; gb.so_j = N; gb.accumulate = 1; gb.scale = s;
+    (void)lora_mm(gb, L.lpart, L.lpf, hs);
+    lora_ext(A, r, 1, K, r, L.bext, 16, 0, hs);  // bext = A
+    p.Aext = L.aext; p.ldae = 16; p.Bext = L.bext; p.ldbe = 16; p.kext = 16;
   }
   return gemm(p, A_BF16_K, B_NF4_R, 1, hs) == hipSuccess && hipGetLastError() == hipSuccess
              ? LSN_OK

@@ -84,15 +84,20 @@ def rel(g, o):
 
 
 def assert_close(g, o, tol, what):
-    """Norm-relative error <= tol and every element within tol of the
-    oracle, measured against |o| + rms(o)."""
+    """Norm-relative error <= tol (the bar), and every element within
+    tol * (|o| + rms(o) * sqrt(2 ln n)): the absolute floor is the largest
+    of n Gaussian errors whose norm sits at the bar, so an element fails only
+    if it is an outlier the norm alone would hide.  Prints the errors."""
     g = np.asarray(g, np.float64).reshape(-1)
     o = np.asarray(o, np.float64).reshape(-1)
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU values"
     r = rel(g, o)
-    assert r <= tol, f"{what}: relative L2 error {r:.3e} > {tol}"
     rms = np.sqrt(np.mean(o * o)) if o.size else 0.0
-    bad = np.abs(g - o) > tol * (np.abs(o) + rms)
+    worst = float(np.max(np.abs(g - o))) if o.size else 0.0
+    print(f"  [{what}] rel L2 {r:.2e}, worst |diff| {worst:.2e} (rms {rms:.2e})", flush=True)
+    assert r <= tol, f"{what}: relative L2 error {r:.3e} > {tol}"
+    floor = rms * np.sqrt(2.0 * np.log(max(o.size, 2)))
+    bad = np.abs(g - o) > tol * (np.abs(o) + floor)
     assert not bad.any(), (f"{what}: {int(bad.sum())} of {o.size} elements off, worst "
                            f"{np.max(np.abs(g - o)):.3e} (rms {rms:.3e})")
     return r
