@@ -40,7 +40,23 @@ def parse():
     ap.add_argument("--dpo-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--link-mb", type=int, default=256)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only run device-to-device copies of this size (counter calibration)")
     return ap.parse_args()
+
+
+def copy_probe(mb, reps=5):
+    """Plain device copies of known size: FETCH_SIZE / WRITE_SIZE of these
+    dispatches calibrate the HBM traffic counters."""
+    import torch
+    n = mb << 20
+    src = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n, "reps": reps}), flush=True)
 
 
 def log(*a):
@@ -181,6 +197,9 @@ def main():
         print("bench.py: this build runs on exactly one GPU (no collectives, no sharding); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe_mb:
+        copy_probe(args.copy_probe_mb)
+        return
     import numpy as np
     import torch
 

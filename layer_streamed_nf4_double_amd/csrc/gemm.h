@@ -41,6 +41,8 @@ struct GemmParams {
   float* part = nullptr;
   int64_t part_floats = 0;
   int ksplit = 1;  // set by gemm()
+  // optional timing events recorded right before / after the main kernel
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
   float levels[16] = {};  // NF4 code levels
 };
 

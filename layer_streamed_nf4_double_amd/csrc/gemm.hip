@@ -56,28 +56,39 @@ LSN_DEV u32x4 nf4_dequant8(uint32_t w, float a, const float* lv) {
 }
 
 // ---------------------------------------------------------------------------
-// operand loaders: prefetch(kt) issues global loads into registers,
-// store(lds) converts and writes the 64-deep slice to LDS as [row][k].
+// operand loaders.  prefetch() issues the global loads of one 64-deep K slice
+// into registers (no bounds checks when the slice is fully inside the
+// matrix); store<Q>() converts / dequantizes the Q-th quarter of it and writes
+// it to LDS as [row][k], so the four quarters can be interleaved with the four
+// MFMA steps of the previous slice.
 // ---------------------------------------------------------------------------
+template <int CH, int Q>
+struct Quarter {  // chunk indices i with 4*i/CH == Q
+  static constexpr int lo = (Q * CH + 3) / 4, hi = ((Q + 1) * CH + 3) / 4;
+};
+
 template <int ROWS>
 struct LoadBf16K {  // rows k-contiguous bf16
   static constexpr int CH = ROWS * 8 / NTHREADS;  // 16-byte chunks per thread
   u32x4 v[CH];
-  LSN_DEV void prefetch(const uint16_t* base, int64_t ld, int row0, int nrows, int k0, int K) {
+  LSN_DEV void prefetch(const uint16_t* base, int64_t ld, int row0, int nrows, int k0, int K,
+                        bool full) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
       const int r = c >> 3, kc = (c & 7) * 8;
       const int row = row0 + r, k = k0 + kc;
-      if (row < nrows && k < K)
-        v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)row * ld + k);
-      else
-        v[i] = u32x4{0, 0, 0, 0};
+      // out-of-range chunks load a valid address and are zeroed (no branch)
+      const bool ok = full || (row < nrows && k < K);
+      const int rc = ok ? row : 0, kcl = ok ? k : 0;
+      const u32x4 t = *reinterpret_cast<const u32x4*>(base + (int64_t)rc * ld + kcl);
+      v[i] = ok ? t : u32x4{0, 0, 0, 0};
     }
   }
+  template <int Q>
   LSN_DEV void store(uint16_t* lds) const {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
+    for (int i = Quarter<CH, Q>::lo; i < Quarter<CH, Q>::hi; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
       *reinterpret_cast<u32x4*>(lds + (c >> 3) * PITCH + (c & 7) * 8) = v[i];
     }
@@ -88,25 +99,25 @@ template <int ROWS>
 struct LoadF32K {  // fp32 rows, rounded to bf16 on the way to LDS
   static constexpr int CH = ROWS * 8 / NTHREADS;
   f32x4 v[CH][2];
-  LSN_DEV void prefetch(const float* base, int64_t ld, int row0, int nrows, int k0, int K) {
+  LSN_DEV void prefetch(const float* base, int64_t ld, int row0, int nrows, int k0, int K,
+                        bool full) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
       const int r = c >> 3, kc = (c & 7) * 8;
       const int row = row0 + r, k = k0 + kc;
-      if (row < nrows && k < K) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(base + (int64_t)row * ld + k);
-        v[i][0] = p[0];
-        v[i][1] = p[1];
-      } else {
-        v[i][0] = f32x4{0, 0, 0, 0};
-        v[i][1] = f32x4{0, 0, 0, 0};
-      }
+      const bool ok = full || (row < nrows && k < K);
+      const int rc = ok ? row : 0, kcl = ok ? k : 0;
+      const f32x4* p = reinterpret_cast<const f32x4*>(base + (int64_t)rc * ld + kcl);
+      const f32x4 a0 = p[0], a1 = p[1];
+      v[i][0] = ok ? a0 : f32x4{0, 0, 0, 0};
+      v[i][1] = ok ? a1 : f32x4{0, 0, 0, 0};
     }
   }
+  template <int Q>
   LSN_DEV void store(uint16_t* lds) const {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
+    for (int i = Quarter<CH, Q>::lo; i < Quarter<CH, Q>::hi; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
       u32x4 o;
       o[0] = pack_bf16x2(v[i][0][0], v[i][0][1]);
@@ -122,28 +133,28 @@ template <int ROWS>
 struct LoadBf16R {  // element (row, k) at base[k*ld + row]; 8x8 register transpose
   static_assert(ROWS <= NTHREADS, "one 8x8 task per thread at most");
   u32x4 v[8];
-  bool active;
-  LSN_DEV void prefetch(const uint16_t* base, int64_t ld, int row0, int nrows, int k0, int K) {
+  LSN_DEV void prefetch(const uint16_t* base, int64_t ld, int row0, int nrows, int k0, int K,
+                        bool full) {
     const int t = threadIdx.x;
-    active = t < ROWS;  // ROWS/8 row groups x 8 k groups
-    if (!active) return;
+    if (t >= ROWS) return;  // ROWS/8 row groups x 8 k groups
     const int rg = t >> 3, kg = t & 7;
     const int row = row0 + rg * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int k = k0 + kg * 8 + i;
-      if (row < nrows && k < K)
-        v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)k * ld + row);
-      else
-        v[i] = u32x4{0, 0, 0, 0};
+      const bool ok = full || (row < nrows && k < K);
+      const int rc = ok ? row : 0, kcl = ok ? k : 0;
+      const u32x4 t = *reinterpret_cast<const u32x4*>(base + (int64_t)kcl * ld + rc);
+      v[i] = ok ? t : u32x4{0, 0, 0, 0};
     }
   }
+  template <int Q>
   LSN_DEV void store(uint16_t* lds) const {
-    if (!active) return;
     const int t = threadIdx.x;
+    if (t >= ROWS) return;
     const int rg = t >> 3, kg = t & 7;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {  // output row rg*8 + j holds k = kg*8 .. +7
+    for (int j = 2 * Q; j < 2 * Q + 2; ++j) {  // output row rg*8 + j holds k = kg*8 .. +7
       u32x4 o;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -162,25 +173,24 @@ struct LoadNf4K {  // B(n,k) from W^T[n, k] (forward); one code word = 8 k
   uint32_t code[CH];
   float amax[CH];
   LSN_DEV void prefetch(const uint8_t* codes, const float* absmax, int64_t rowlen, int row0,
-                        int nrows, int k0, int K) {
+                        int nrows, int k0, int K, bool full) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
       const int r = c >> 3, kc = (c & 7) * 8;
       const int row = row0 + r, k = k0 + kc;
-      if (row < nrows && k < K) {
-        const int64_t e = (int64_t)row * rowlen + k;
-        code[i] = *reinterpret_cast<const uint32_t*>(codes + (e >> 1));
-        amax[i] = absmax[e >> 6];
-      } else {
-        code[i] = 0x77777777u;  // level 7 is exactly 0
-        amax[i] = 0.f;
-      }
+      const bool ok = full || (row < nrows && k < K);
+      const int64_t e = ok ? (int64_t)row * rowlen + k : 0;
+      const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + (e >> 1));
+      const float am = absmax[e >> 6];
+      code[i] = ok ? cw : 0x77777777u;  // level 7 is exactly 0
+      amax[i] = ok ? am : 0.f;
     }
   }
+  template <int Q>
   LSN_DEV void store(uint16_t* lds, const float* lv) const {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
+    for (int i = Quarter<CH, Q>::lo; i < Quarter<CH, Q>::hi; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
       *reinterpret_cast<u32x4*>(lds + (c >> 3) * PITCH + (c & 7) * 8) =
           nf4_dequant8(code[i], amax[i], lv);
@@ -196,33 +206,30 @@ struct LoadNf4R {  // B(n,k) from W^T[k, n] (input gradient); task = 4 k x 8 n
   static_assert(TASKS <= NTHREADS, "one task per thread at most");
   uint32_t code[4];
   float amax[4];
-  bool active;
   LSN_DEV void prefetch(const uint8_t* codes, const float* absmax, int64_t rowlen, int row0,
-                        int nrows, int k0, int K) {
+                        int nrows, int k0, int K, bool full) {
     const int t = threadIdx.x;
-    active = t < TASKS;
-    if (!active) return;
+    if (t >= TASKS) return;
     const int kg = t & 15, ng = t >> 4;
     const int n = row0 + ng * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = k0 + kg * 4 + i;
-      if (n < nrows && k < K) {
-        const int64_t e = (int64_t)k * rowlen + n;
-        code[i] = *reinterpret_cast<const uint32_t*>(codes + (e >> 1));
-        amax[i] = absmax[e >> 6];
-      } else {
-        code[i] = 0x77777777u;
-        amax[i] = 0.f;
-      }
+      const bool ok = full || (n < nrows && k < K);
+      const int64_t e = ok ? (int64_t)k * rowlen + n : 0;
+      const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + (e >> 1));
+      const float am = absmax[e >> 6];
+      code[i] = ok ? cw : 0x77777777u;
+      amax[i] = ok ? am : 0.f;
     }
   }
+  template <int Q>
   LSN_DEV void store(uint16_t* lds, const float* lv) const {
-    if (!active) return;
     const int t = threadIdx.x;
+    if (t >= TASKS) return;
     const int kg = t & 15, ng = t >> 4;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {  // LDS row n = ng*8 + j, k = kg*4 .. +3
+    for (int j = 2 * Q; j < 2 * Q + 2; ++j) {  // LDS row n = ng*8 + j, k = kg*4 .. +3
       u32x2 o;
       o[0] = pack_bf16x2(lv[(code[0] >> (4 * j)) & 15u] * amax[0],
                          lv[(code[1] >> (4 * j)) & 15u] * amax[1]);
@@ -241,6 +248,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
   constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM >= 1 && TN >= 1, "tile too small");
+  constexpr bool NF4B = (OPB == B_NF4_K || OPB == B_NF4_R);
 
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * PITCH];
@@ -272,7 +280,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // loaders
+  // loaders: two register stages (slices it+1 and it+2 while it computes)
   using LA = typename std::conditional<
       OPA == A_BF16_K, LoadBf16K<BM>,
       typename std::conditional<OPA == A_F32_K, LoadF32K<BM>, LoadBf16R<BM>>::type>::type;
@@ -282,65 +290,93 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
           OPB == B_BF16_R, LoadBf16R<BN>,
           typename std::conditional<OPB == B_NF4_K, LoadNf4K<BN>, LoadNf4R<BN>>::type>::type>::
       type;
-  LA la;
-  LB lb;
+  LA la[2];
+  LB lb[2];
 
   const int nkt = (p.K + BK - 1) / BK;
   // split-k: blockIdx.y takes k-tiles [it0, it1) of the nseg * nkt
   const int ntile = nkt * p.nseg;
   const int kper = (ntile + p.ksplit - 1) / p.ksplit;
   const int it0 = min(ntile, (int)blockIdx.y * kper), it1 = min(ntile, it0 + kper);
+  const bool rows_a_full = m0 + BM <= p.M, rows_b_full = n0 + BN <= p.N;
 
-  auto prefetch = [&](int it) {
+  auto prefetch = [&](LA& a, LB& bb, int it) {
     const int seg = it / nkt, k0 = (it % nkt) * BK;
+    const bool kfull = k0 + BK <= p.K;
     if constexpr (OPA == A_F32_K)
-      la.prefetch(reinterpret_cast<const float*>(p.A) + offA + seg * p.sA_seg, p.lda, m0, p.M,
-                  k0, p.K);
+      a.prefetch(reinterpret_cast<const float*>(p.A) + offA + seg * p.sA_seg, p.lda, m0, p.M, k0,
+                 p.K, rows_a_full && kfull);
     else
-      la.prefetch(reinterpret_cast<const uint16_t*>(p.A) + offA + seg * p.sA_seg, p.lda, m0,
-                  p.M, k0, p.K);
-    if constexpr (OPB == B_NF4_K || OPB == B_NF4_R)
-      lb.prefetch(reinterpret_cast<const uint8_t*>(p.B), p.absmax, p.rowlen, n0, p.N, k0, p.K);
+      a.prefetch(reinterpret_cast<const uint16_t*>(p.A) + offA + seg * p.sA_seg, p.lda, m0, p.M,
+                 k0, p.K, rows_a_full && kfull);
+    if constexpr (NF4B)
+      bb.prefetch(reinterpret_cast<const uint8_t*>(p.B), p.absmax, p.rowlen, n0, p.N, k0, p.K,
+                  rows_b_full && kfull);
     else
-      lb.prefetch(reinterpret_cast<const uint16_t*>(p.B) + offB + seg * p.sB_seg, p.ldb, n0,
-                  p.N, k0, p.K);
+      bb.prefetch(reinterpret_cast<const uint16_t*>(p.B) + offB + seg * p.sB_seg, p.ldb, n0, p.N,
+                  k0, p.K, rows_b_full && kfull);
   };
-  auto store = [&](int buf) {
-    la.store(sA[buf]);
-    if constexpr (OPB == B_NF4_K || OPB == B_NF4_R)
-      lb.store(sB[buf], sLv);
+  auto store_q = [&](auto q_, const LA& a, const LB& bb, int buf) {
+    constexpr int Q = decltype(q_)::value;
+    a.template store<Q>(sA[buf]);
+    if constexpr (NF4B)
+      bb.template store<Q>(sB[buf], sLv);
     else
-      lb.store(sB[buf]);
+      bb.template store<Q>(sB[buf]);
   };
 
   const int lr = lane & 31, lk = (lane >> 5) * 8;
-  if (it1 > it0) {
-    prefetch(it0);
-    __syncthreads();  // sLv visible
-    store(0);
-    __syncthreads();
-    for (int it = it0; it < it1; ++it) {
-      const int cur = (it - it0) & 1;
-      if (it + 1 < it1) prefetch(it + 1);
-      const uint16_t* a_base = sA[cur] + (wm * WTM + lr) * PITCH + lk;
-      const uint16_t* b_base = sB[cur] + (wn * WTN + lr) * PITCH + lk;
+  // one K slice from LDS buffer S, interleaving the store of the next slice
+  // (register stage S^1) into the other buffer.  Fragments are double
+  // buffered: step KK+1's LDS reads are issued before step KK's MFMAs.
+  auto body = [&](auto s_, int it) {
+    constexpr int S = decltype(s_)::value;
+    // Unconditional (branch-free body): past the end the prefetch re-reads the
+    // last slice and the store fills a buffer no one reads any more.
+    prefetch(la[S], lb[S], min(it + 2, it1 - 1));
+    const uint16_t* a_base = sA[S] + (wm * WTM + lr) * PITCH + lk;
+    const uint16_t* b_base = sB[S] + (wn * WTN + lr) * PITCH + lk;
+    bf16x8 af[2][TM], bfr[2][TN];
+    auto read = [&](int f, int kk) {
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8 af[TM], bfr[TN];
+      for (int i = 0; i < TM; ++i)
+        af[f][i] = *reinterpret_cast<const bf16x8*>(a_base + i * 32 * PITCH + kk * 16);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(a_base + i * 32 * PITCH + kk * 16);
+      for (int j = 0; j < TN; ++j)
+        bfr[f][j] = *reinterpret_cast<const bf16x8*>(b_base + j * 32 * PITCH + kk * 16);
+    };
+    auto kstep = [&](auto kk_) {
+      constexpr int KK = decltype(kk_)::value;
+      if constexpr (KK < BK / 16 - 1) read((KK + 1) & 1, KK + 1);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8*>(b_base + j * 32 * PITCH + kk * 16);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-      if (it + 1 < it1) store(cur ^ 1);
-      __syncthreads();
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[KK & 1][i], bfr[KK & 1][j],
+                                                               acc[i][j], 0, 0, 0);
+      store_q(std::integral_constant<int, KK>{}, la[S ^ 1], lb[S ^ 1], S ^ 1);
+    };
+    read(0, 0);
+    kstep(std::integral_constant<int, 0>{});
+    kstep(std::integral_constant<int, 1>{});
+    kstep(std::integral_constant<int, 2>{});
+    kstep(std::integral_constant<int, 3>{});
+    __syncthreads();
+  };
+
+  if (it1 > it0) {
+    prefetch(la[0], lb[0], it0);
+    prefetch(la[1], lb[1], min(it0 + 1, it1 - 1));
+    __syncthreads();  // sLv visible
+    store_q(std::integral_constant<int, 0>{}, la[0], lb[0], 0);
+    store_q(std::integral_constant<int, 1>{}, la[0], lb[0], 0);
+    store_q(std::integral_constant<int, 2>{}, la[0], lb[0], 0);
+    store_q(std::integral_constant<int, 3>{}, la[0], lb[0], 0);
+    __syncthreads();
+    // slice it lives in LDS buffer (it - it0) & 1, which is the stage parity
+    for (int it = it0; it < it1; it += 2) {
+      body(std::integral_constant<int, 0>{}, it);
+      if (it + 1 < it1) body(std::integral_constant<int, 1>{}, it + 1);
     }
   }
 
@@ -459,8 +495,10 @@ int64_t gemm_partial_floats(int M, int N, int K, int nseg, int batch) {
 template <int BM, int BN, int OPA, int OPB>
 static hipError_t launch_t(const GemmParams& p, int batch, hipStream_t s) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  if (p.ev0) (void)hipEventRecord(p.ev0, s);
   hipLaunchKernelGGL((gemm_kernel<BM, BN, OPA, OPB>), dim3(tiles, p.ksplit, batch),
                      dim3(NTHREADS), 0, s, p);
+  if (p.ev1) (void)hipEventRecord(p.ev1, s);
   if (p.ksplit > 1) {
     const int64_t n = (int64_t)p.M * p.N;
     hipLaunchKernelGGL(gemm_reduce_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);

@@ -208,9 +208,16 @@ static hipError_t cgemm(lsn_ctx* c, GemmParams p, int opa, int opb, int batch) {
   p.part_floats = c->gpart_floats;
   lsn_ctx::ProfRec r{0, opa, opb, gemm_plan(p.M, p.N, p.K, p.nseg, batch).tile,
                      2.0 * p.M * p.N * (double)p.K * p.nseg * batch, nullptr, nullptr};
-  const bool on = (opb == B_NF4_K || opb == B_NF4_R) && prof_begin(c, &r, c->cs);
+  // events bracket the GEMM kernel only (not a split-k reduction)
+  const bool on = c->profiling && (opb == B_NF4_K || opb == B_NF4_R);
+  if (on) {
+    r.e0 = take_event(c);
+    r.e1 = take_event(c);
+    p.ev0 = r.e0;
+    p.ev1 = r.e1;
+  }
   const hipError_t e = gemm(p, opa, opb, batch, c->cs);
-  if (on) prof_end(c, r, c->cs);
+  if (on && r.e0 && r.e1) c->prof.push_back(r);
   return e;
 }
 
