@@ -39,7 +39,6 @@ namespace lsn {
 
 constexpr int BK = 64;        // K depth staged per iteration
 constexpr int PITCH = 72;     // LDS row pitch in bf16 (64 + 8 pad: conflict-free b128 reads)
-constexpr int NTHREADS = 256; // 4 waves, arranged 2 x 2 over the tile
 
 // ---------------------------------------------------------------------------
 // NF4 dequantization of one 32-bit code word (8 elements) to 4 packed bf16x2
@@ -67,21 +66,33 @@ struct Quarter {  // chunk indices i with 4*i/CH == Q
   static constexpr int lo = (Q * CH + 3) / 4, hi = ((Q + 1) * CH + 3) / 4;
 };
 
-template <int ROWS>
-struct LoadBf16K {  // rows k-contiguous bf16
+// Addressing: init() computes each lane's 32-bit element offsets once; per
+// slice only a uniform (scalar) base pointer moves, so a load is one
+// scalar-base + vector-offset instruction.  Rows outside the matrix read
+// row 0 and are zeroed; k beyond K (last slice only) likewise.
+template <int ROWS, int NTHREADS>
+struct LoadBf16K {  // rows k-contiguous bf16; base = &A(0, k0)
   static constexpr int CH = ROWS * 8 / NTHREADS;  // 16-byte chunks per thread
   u32x4 v[CH];
-  LSN_DEV void prefetch(const uint16_t* base, int64_t ld, int row0, int nrows, int k0, int K,
-                        bool full) {
+  uint32_t off[CH];
+  uint32_t rowok;  // bit i: chunk i's row exists
+  LSN_DEV void init(int64_t ld, int row0, int nrows) {
+    rowok = 0;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      const int r = c >> 3, kc = (c & 7) * 8;
-      const int row = row0 + r, k = k0 + kc;
-      // out-of-range chunks load a valid address and are zeroed (no branch)
-      const bool ok = full || (row < nrows && k < K);
-      const int rc = ok ? row : 0, kcl = ok ? k : 0;
-      const u32x4 t = *reinterpret_cast<const u32x4*>(base + (int64_t)rc * ld + kcl);
+      const int row = row0 + (c >> 3), kc = (c & 7) * 8;
+      const bool ok = row < nrows;
+      rowok |= (ok ? 1u : 0u) << i;
+      off[i] = (uint32_t)((ok ? (int64_t)row * ld : 0) + kc);
+    }
+  }
+  LSN_DEV void prefetch(const uint16_t* base, int k0, int K, bool full) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int kc = ((threadIdx.x + i * NTHREADS) & 7) * 8;
+      const bool ok = full || (((rowok >> i) & 1u) && k0 + kc < K);
+      const u32x4 t = *reinterpret_cast<const u32x4*>(base + (ok ? off[i] : 0u));
       v[i] = ok ? t : u32x4{0, 0, 0, 0};
     }
   }
@@ -95,20 +106,29 @@ struct LoadBf16K {  // rows k-contiguous bf16
   }
 };
 
-template <int ROWS>
-struct LoadF32K {  // fp32 rows, rounded to bf16 on the way to LDS
+template <int ROWS, int NTHREADS>
+struct LoadF32K {  // fp32 rows, rounded to bf16 on the way to LDS; base = &A(0, k0)
   static constexpr int CH = ROWS * 8 / NTHREADS;
   f32x4 v[CH][2];
-  LSN_DEV void prefetch(const float* base, int64_t ld, int row0, int nrows, int k0, int K,
-                        bool full) {
+  uint32_t off[CH];
+  uint32_t rowok;
+  LSN_DEV void init(int64_t ld, int row0, int nrows) {
+    rowok = 0;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      const int r = c >> 3, kc = (c & 7) * 8;
-      const int row = row0 + r, k = k0 + kc;
-      const bool ok = full || (row < nrows && k < K);
-      const int rc = ok ? row : 0, kcl = ok ? k : 0;
-      const f32x4* p = reinterpret_cast<const f32x4*>(base + (int64_t)rc * ld + kcl);
+      const int row = row0 + (c >> 3), kc = (c & 7) * 8;
+      const bool ok = row < nrows;
+      rowok |= (ok ? 1u : 0u) << i;
+      off[i] = (uint32_t)((ok ? (int64_t)row * ld : 0) + kc);
+    }
+  }
+  LSN_DEV void prefetch(const float* base, int k0, int K, bool full) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int kc = ((threadIdx.x + i * NTHREADS) & 7) * 8;
+      const bool ok = full || (((rowok >> i) & 1u) && k0 + kc < K);
+      const f32x4* p = reinterpret_cast<const f32x4*>(base + (ok ? off[i] : 0u));
       const f32x4 a0 = p[0], a1 = p[1];
       v[i][0] = ok ? a0 : f32x4{0, 0, 0, 0};
       v[i][1] = ok ? a1 : f32x4{0, 0, 0, 0};
@@ -129,22 +149,28 @@ struct LoadF32K {  // fp32 rows, rounded to bf16 on the way to LDS
   }
 };
 
-template <int ROWS>
-struct LoadBf16R {  // element (row, k) at base[k*ld + row]; 8x8 register transpose
+template <int ROWS, int NTHREADS>
+struct LoadBf16R {  // element (row, k) at A[k*ld + row]; base = &A(k0 row of storage); 8x8 transpose
   static_assert(ROWS <= NTHREADS, "one 8x8 task per thread at most");
   u32x4 v[8];
-  LSN_DEV void prefetch(const uint16_t* base, int64_t ld, int row0, int nrows, int k0, int K,
-                        bool full) {
+  uint32_t off0;  // offset of (row group, k = kg*8)
+  uint32_t ldu;
+  bool rowok;
+  LSN_DEV void init(int64_t ld, int row0, int nrows) {
     const int t = threadIdx.x;
-    if (t >= ROWS) return;  // ROWS/8 row groups x 8 k groups
-    const int rg = t >> 3, kg = t & 7;
+    const int rg = (t >> 3), kg = t & 7;
     const int row = row0 + rg * 8;
+    rowok = t < ROWS && row < nrows;
+    off0 = (uint32_t)((int64_t)kg * 8 * ld + (rowok ? row : 0));
+    ldu = (uint32_t)ld;
+  }
+  LSN_DEV void prefetch(const uint16_t* base, int k0, int K, bool full) {
+    if (threadIdx.x >= ROWS) return;  // ROWS/8 row groups x 8 k groups
+    const int kg = threadIdx.x & 7;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int k = k0 + kg * 8 + i;
-      const bool ok = full || (row < nrows && k < K);
-      const int rc = ok ? row : 0, kcl = ok ? k : 0;
-      const u32x4 t = *reinterpret_cast<const u32x4*>(base + (int64_t)kcl * ld + rc);
+      const bool ok = full || (rowok && k0 + kg * 8 + i < K);
+      const u32x4 t = *reinterpret_cast<const u32x4*>(base + (ok ? off0 + (uint32_t)i * ldu : 0u));
       v[i] = ok ? t : u32x4{0, 0, 0, 0};
     }
   }
@@ -167,22 +193,33 @@ struct LoadBf16R {  // element (row, k) at base[k*ld + row]; 8x8 register transp
   }
 };
 
-template <int ROWS>
+template <int ROWS, int NTHREADS>
 struct LoadNf4K {  // B(n,k) from W^T[n, k] (forward); one code word = 8 k
   static constexpr int CH = ROWS * 8 / NTHREADS;
   uint32_t code[CH];
   float amax[CH];
-  LSN_DEV void prefetch(const uint8_t* codes, const float* absmax, int64_t rowlen, int row0,
-                        int nrows, int k0, int K, bool full) {
+  uint32_t e[CH];  // element index of (row, kc) at k0 = 0
+  uint32_t rowok;
+  LSN_DEV void init(int64_t rowlen, int row0, int nrows) {
+    rowok = 0;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      const int r = c >> 3, kc = (c & 7) * 8;
-      const int row = row0 + r, k = k0 + kc;
-      const bool ok = full || (row < nrows && k < K);
-      const int64_t e = ok ? (int64_t)row * rowlen + k : 0;
-      const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + (e >> 1));
-      const float am = absmax[e >> 6];
+      const int row = row0 + (c >> 3), kc = (c & 7) * 8;
+      const bool ok = row < nrows;
+      rowok |= (ok ? 1u : 0u) << i;
+      e[i] = (uint32_t)((ok ? (int64_t)row * rowlen : 0) + kc);
+    }
+  }
+  // codes: byte base of the matrix; k0 even
+  LSN_DEV void prefetch(const uint8_t* codes, const float* absmax, int k0, int K, bool full) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int kc = ((threadIdx.x + i * NTHREADS) & 7) * 8;
+      const bool ok = full || (((rowok >> i) & 1u) && k0 + kc < K);
+      const uint32_t ei = ok ? e[i] + (uint32_t)k0 : 0u;
+      const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + (ei >> 1));
+      const float am = absmax[ei >> 6];
       code[i] = ok ? cw : 0x77777777u;  // level 7 is exactly 0
       amax[i] = ok ? am : 0.f;
     }
@@ -198,27 +235,36 @@ struct LoadNf4K {  // B(n,k) from W^T[n, k] (forward); one code word = 8 k
   }
 };
 
-template <int ROWS>
-struct LoadNf4R {  // B(n,k) from W^T[k, n] (input gradient); task = 4 k x 8 n
-  // Lanes take consecutive k-groups: each wave's 8-byte LDS writes then hit
-  // every bank exactly twice (the minimum for 64 x 8 bytes).
-  static constexpr int TASKS = ROWS * 2;  // 16 k-groups x ROWS/8 n-groups
-  static_assert(TASKS <= NTHREADS, "one task per thread at most");
-  uint32_t code[4];
-  float amax[4];
-  LSN_DEV void prefetch(const uint8_t* codes, const float* absmax, int64_t rowlen, int row0,
-                        int nrows, int k0, int K, bool full) {
+template <int ROWS, int NTHREADS>
+struct LoadNf4R {  // B(n,k) from W^T[k, n] (input gradient); task = KG k x 8 n
+  // KG consecutive rows of W^T (k) by one code word (8 n) per thread, every
+  // thread busy.  Lanes take consecutive k-groups, so a wave's KG*2-byte LDS
+  // writes cover the banks evenly (conflict-free for KG = 2, two-way for 4).
+  static constexpr int KG = 64 * ROWS / (8 * NTHREADS);
+  static constexpr int NKG = 64 / KG;  // k-groups per slice
+  static_assert(KG == 2 || KG == 4, "unsupported NF4 transpose tiling");
+  uint32_t code[KG];
+  float amax[KG];
+  uint32_t e0;  // element index of (k = kg*KG, n) at k0 = 0
+  uint32_t rl;
+  bool rowok;
+  LSN_DEV void init(int64_t rowlen, int row0, int nrows) {
     const int t = threadIdx.x;
-    if (t >= TASKS) return;
-    const int kg = t & 15, ng = t >> 4;
+    const int kg = t % NKG, ng = t / NKG;
     const int n = row0 + ng * 8;
+    rowok = n < nrows;
+    e0 = (uint32_t)((int64_t)kg * KG * rowlen + (rowok ? n : 0));
+    rl = (uint32_t)rowlen;
+  }
+  LSN_DEV void prefetch(const uint8_t* codes, const float* absmax, int k0, int K, bool full) {
+    const int kg = threadIdx.x % NKG;
+    const uint32_t eb = e0 + (uint32_t)k0 * rl;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = k0 + kg * 4 + i;
-      const bool ok = full || (n < nrows && k < K);
-      const int64_t e = ok ? (int64_t)k * rowlen + n : 0;
-      const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + (e >> 1));
-      const float am = absmax[e >> 6];
+    for (int i = 0; i < KG; ++i) {
+      const bool ok = full || (rowok && k0 + kg * KG + i < K);
+      const uint32_t ei = ok ? eb + (uint32_t)i * rl : 0u;
+      const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + (ei >> 1));
+      const float am = absmax[ei >> 6];
       code[i] = ok ? cw : 0x77777777u;
       amax[i] = ok ? am : 0.f;
     }
@@ -226,16 +272,21 @@ struct LoadNf4R {  // B(n,k) from W^T[k, n] (input gradient); task = 4 k x 8 n
   template <int Q>
   LSN_DEV void store(uint16_t* lds, const float* lv) const {
     const int t = threadIdx.x;
-    if (t >= TASKS) return;
-    const int kg = t & 15, ng = t >> 4;
+    const int kg = t % NKG, ng = t / NKG;
 #pragma unroll
-    for (int j = 2 * Q; j < 2 * Q + 2; ++j) {  // LDS row n = ng*8 + j, k = kg*4 .. +3
-      u32x2 o;
-      o[0] = pack_bf16x2(lv[(code[0] >> (4 * j)) & 15u] * amax[0],
-                         lv[(code[1] >> (4 * j)) & 15u] * amax[1]);
-      o[1] = pack_bf16x2(lv[(code[2] >> (4 * j)) & 15u] * amax[2],
-                         lv[(code[3] >> (4 * j)) & 15u] * amax[3]);
-      *reinterpret_cast<u32x2*>(lds + (ng * 8 + j) * PITCH + kg * 4) = o;
+    for (int j = 2 * Q; j < 2 * Q + 2; ++j) {  // LDS row n = ng*8 + j, k = kg*KG ..
+      if constexpr (KG == 4) {
+        u32x2 o;
+        o[0] = pack_bf16x2(lv[(code[0] >> (4 * j)) & 15u] * amax[0],
+                           lv[(code[1] >> (4 * j)) & 15u] * amax[1]);
+        o[1] = pack_bf16x2(lv[(code[2] >> (4 * j)) & 15u] * amax[2],
+                           lv[(code[3] >> (4 * j)) & 15u] * amax[3]);
+        *reinterpret_cast<u32x2*>(lds + (ng * 8 + j) * PITCH + kg * 4) = o;
+      } else {
+        *reinterpret_cast<uint32_t*>(lds + (ng * 8 + j) * PITCH + kg * 2) =
+            pack_bf16x2(lv[(code[0] >> (4 * j)) & 15u] * amax[0],
+                        lv[(code[1] >> (4 * j)) & 15u] * amax[1]);
+      }
     }
   }
 };
@@ -243,9 +294,11 @@ struct LoadNf4R {  // B(n,k) from W^T[k, n] (input gradient); task = 4 k x 8 n
 // ---------------------------------------------------------------------------
 // kernel
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int OPA, int OPB>
-__global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
-  constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile
+template <int BM, int BN, int WGM, int WGN, int NS, int OPA, int OPB>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(const GemmParams p) {
+  static_assert(NS % 2 == 0, "register stages come in pairs (two LDS buffers)");
+  constexpr int NTHREADS = WGM * WGN * 64;   // waves arranged WGM x WGN
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM >= 1 && TN >= 1, "tile too small");
   constexpr bool NF4B = (OPB == B_NF4_K || OPB == B_NF4_R);
@@ -270,7 +323,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
   if (threadIdx.x < 16) sLv[threadIdx.x] = p.levels[threadIdx.x];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -280,18 +333,27 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // loaders: two register stages (slices it+1 and it+2 while it computes)
+  // loaders: NS register stages (slices it+1 .. it+NS while slice it computes)
   using LA = typename std::conditional<
-      OPA == A_BF16_K, LoadBf16K<BM>,
-      typename std::conditional<OPA == A_F32_K, LoadF32K<BM>, LoadBf16R<BM>>::type>::type;
+      OPA == A_BF16_K, LoadBf16K<BM, NTHREADS>,
+      typename std::conditional<OPA == A_F32_K, LoadF32K<BM, NTHREADS>,
+                                LoadBf16R<BM, NTHREADS>>::type>::type;
   using LB = typename std::conditional<
-      OPB == B_BF16_K, LoadBf16K<BN>,
+      OPB == B_BF16_K, LoadBf16K<BN, NTHREADS>,
       typename std::conditional<
-          OPB == B_BF16_R, LoadBf16R<BN>,
-          typename std::conditional<OPB == B_NF4_K, LoadNf4K<BN>, LoadNf4R<BN>>::type>::type>::
-      type;
-  LA la[2];
-  LB lb[2];
+          OPB == B_BF16_R, LoadBf16R<BN, NTHREADS>,
+          typename std::conditional<OPB == B_NF4_K, LoadNf4K<BN, NTHREADS>,
+                                    LoadNf4R<BN, NTHREADS>>::type>::type>::type;
+  LA la[NS];
+  LB lb[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    la[q].init(p.lda, m0, p.M);
+    if constexpr (NF4B)
+      lb[q].init(p.rowlen, n0, p.N);
+    else
+      lb[q].init(p.ldb, n0, p.N);
+  }
 
   const int nkt = (p.K + BK - 1) / BK;
   // split-k: blockIdx.y takes k-tiles [it0, it1) of the nseg * nkt
@@ -300,21 +362,24 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
   const int it0 = min(ntile, (int)blockIdx.y * kper), it1 = min(ntile, it0 + kper);
   const bool rows_a_full = m0 + BM <= p.M, rows_b_full = n0 + BN <= p.N;
 
+  // uniform per-slice base pointers; per-lane offsets were fixed by init()
   auto prefetch = [&](LA& a, LB& bb, int it) {
     const int seg = it / nkt, k0 = (it % nkt) * BK;
     const bool kfull = k0 + BK <= p.K;
+    const int64_t ka = (OPA == A_BF16_R) ? (int64_t)k0 * p.lda : k0;
     if constexpr (OPA == A_F32_K)
-      a.prefetch(reinterpret_cast<const float*>(p.A) + offA + seg * p.sA_seg, p.lda, m0, p.M, k0,
-                 p.K, rows_a_full && kfull);
+      a.prefetch(reinterpret_cast<const float*>(p.A) + offA + seg * p.sA_seg + ka, k0, p.K,
+                 rows_a_full && kfull);
     else
-      a.prefetch(reinterpret_cast<const uint16_t*>(p.A) + offA + seg * p.sA_seg, p.lda, m0, p.M,
-                 k0, p.K, rows_a_full && kfull);
-    if constexpr (NF4B)
-      bb.prefetch(reinterpret_cast<const uint8_t*>(p.B), p.absmax, p.rowlen, n0, p.N, k0, p.K,
+      a.prefetch(reinterpret_cast<const uint16_t*>(p.A) + offA + seg * p.sA_seg + ka, k0, p.K,
+                 rows_a_full && kfull);
+    if constexpr (NF4B) {
+      bb.prefetch(reinterpret_cast<const uint8_t*>(p.B), p.absmax, k0, p.K, rows_b_full && kfull);
+    } else {
+      const int64_t kb = (OPB == B_BF16_R) ? (int64_t)k0 * p.ldb : k0;
+      bb.prefetch(reinterpret_cast<const uint16_t*>(p.B) + offB + seg * p.sB_seg + kb, k0, p.K,
                   rows_b_full && kfull);
-    else
-      bb.prefetch(reinterpret_cast<const uint16_t*>(p.B) + offB + seg * p.sB_seg, p.ldb, n0, p.N,
-                  k0, p.K, rows_b_full && kfull);
+    }
   };
   auto store_q = [&](auto q_, const LA& a, const LB& bb, int buf) {
     constexpr int Q = decltype(q_)::value;
@@ -326,16 +391,19 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
   };
 
   const int lr = lane & 31, lk = (lane >> 5) * 8;
-  // one K slice from LDS buffer S, interleaving the store of the next slice
-  // (register stage S^1) into the other buffer.  Fragments are double
-  // buffered: step KK+1's LDS reads are issued before step KK's MFMAs.
+  // One K slice: slice it sits in LDS buffer S & 1 (stage S held it); the
+  // next slice (stage S+1) is stored, in quarters between the MFMA steps,
+  // into the other buffer, and stage S is refilled with slice it+NS.
+  // Fragments are double buffered: step KK+1's LDS reads are issued before
+  // step KK's MFMAs.
   auto body = [&](auto s_, int it) {
     constexpr int S = decltype(s_)::value;
+    constexpr int B = S & 1, SN = (S + 1) % NS;
     // Unconditional (branch-free body): past the end the prefetch re-reads the
     // last slice and the store fills a buffer no one reads any more.
-    prefetch(la[S], lb[S], min(it + 2, it1 - 1));
-    const uint16_t* a_base = sA[S] + (wm * WTM + lr) * PITCH + lk;
-    const uint16_t* b_base = sB[S] + (wn * WTN + lr) * PITCH + lk;
+    prefetch(la[S], lb[S], min(it + NS, it1 - 1));
+    const uint16_t* a_base = sA[B] + (wm * WTM + lr) * PITCH + lk;
+    const uint16_t* b_base = sB[B] + (wn * WTN + lr) * PITCH + lk;
     bf16x8 af[2][TM], bfr[2][TN];
     auto read = [&](int f, int kk) {
 #pragma unroll
@@ -354,7 +422,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[KK & 1][i], bfr[KK & 1][j],
                                                                acc[i][j], 0, 0, 0);
-      store_q(std::integral_constant<int, KK>{}, la[S ^ 1], lb[S ^ 1], S ^ 1);
+      store_q(std::integral_constant<int, KK>{}, la[SN], lb[SN], B ^ 1);
     };
     read(0, 0);
     kstep(std::integral_constant<int, 0>{});
@@ -365,18 +433,22 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmParams p) {
   };
 
   if (it1 > it0) {
-    prefetch(la[0], lb[0], it0);
-    prefetch(la[1], lb[1], min(it0 + 1, it1 - 1));
+#pragma unroll
+    for (int q = 0; q < NS; ++q) prefetch(la[q], lb[q], min(it0 + q, it1 - 1));
     __syncthreads();  // sLv visible
     store_q(std::integral_constant<int, 0>{}, la[0], lb[0], 0);
     store_q(std::integral_constant<int, 1>{}, la[0], lb[0], 0);
     store_q(std::integral_constant<int, 2>{}, la[0], lb[0], 0);
     store_q(std::integral_constant<int, 3>{}, la[0], lb[0], 0);
     __syncthreads();
-    // slice it lives in LDS buffer (it - it0) & 1, which is the stage parity
-    for (int it = it0; it < it1; it += 2) {
+    // stage (it - it0) % NS holds slice it; its LDS buffer is that parity
+    for (int it = it0; it < it1; it += NS) {
       body(std::integral_constant<int, 0>{}, it);
       if (it + 1 < it1) body(std::integral_constant<int, 1>{}, it + 1);
+      if constexpr (NS > 2) {
+        if (it + 2 < it1) body(std::integral_constant<int, 2 % NS>{}, it + 2);
+        if (it + 3 < it1) body(std::integral_constant<int, 3 % NS>{}, it + 3);
+      }
     }
   }
 
@@ -492,12 +564,12 @@ int64_t gemm_partial_floats(int M, int N, int K, int nseg, int batch) {
   return g.split > 1 ? (int64_t)g.split * M * N : 0;
 }
 
-template <int BM, int BN, int OPA, int OPB>
+template <int BM, int BN, int WGM, int WGN, int NS, int OPA, int OPB>
 static hipError_t launch_t(const GemmParams& p, int batch, hipStream_t s) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (p.ev0) (void)hipEventRecord(p.ev0, s);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, OPA, OPB>), dim3(tiles, p.ksplit, batch),
-                     dim3(NTHREADS), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, NS, OPA, OPB>), dim3(tiles, p.ksplit, batch),
+                     dim3(WGM * WGN * 64), 0, s, p);
   if (p.ev1) (void)hipEventRecord(p.ev1, s);
   if (p.ksplit > 1) {
     const int64_t n = (int64_t)p.M * p.N;
@@ -512,14 +584,29 @@ static hipError_t launch_tiles(GemmParams p, int batch, hipStream_t s) {
   p.ksplit = g.split;
   if (p.ksplit > 1 && (!p.part || p.part_floats < (int64_t)p.ksplit * p.M * p.N)) p.ksplit = 1;
   switch (g.tile) {
-    case TILE_256x128: return launch_t<256, 128, OPA, OPB>(p, batch, s);
-    case TILE_128x128: return launch_t<128, 128, OPA, OPB>(p, batch, s);
-    default: return launch_t<64, 64, OPA, OPB>(p, batch, s);
+    // 256 x 128: 8 waves (two per SIMD) of 64 x 64; smaller tiles: 4 waves
+    case TILE_256x128: return launch_t<256, 128, 4, 2, 2, OPA, OPB>(p, batch, s);
+    case TILE_128x128: return launch_t<128, 128, 2, 2, 2, OPA, OPB>(p, batch, s);
+    default: return launch_t<64, 64, 2, 2, 2, OPA, OPB>(p, batch, s);
   }
+}
+
+// The loaders address within one matrix (one batch entry and segment) with
+// 32-bit element offsets; larger matrices are rejected.
+static bool offsets_fit(const GemmParams& p, int opa, int opb) {
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t a_ext = (opa == A_BF16_R) ? (int64_t)p.K * p.lda + p.M : (int64_t)p.M * p.lda + p.K;
+  int64_t b_ext;
+  if (opb == B_NF4_K) b_ext = (int64_t)p.N * p.rowlen + p.K;
+  else if (opb == B_NF4_R) b_ext = (int64_t)p.K * p.rowlen + p.N;
+  else if (opb == B_BF16_R) b_ext = (int64_t)p.K * p.ldb + p.N;
+  else b_ext = (int64_t)p.N * p.ldb + p.K;
+  return a_ext < lim && b_ext < lim;
 }
 
 hipError_t gemm(const GemmParams& p, int opa, int opb, int batch, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0 || batch <= 0) return hipSuccess;
+  if (!offsets_fit(p, opa, opb)) return hipErrorInvalidValue;
 #define LSN_CASE(A_, B_) \
   if (opa == A_ && opb == B_) return launch_tiles<A_, B_>(p, batch, s);
   LSN_CASE(A_BF16_K, B_NF4_K)
