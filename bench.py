@@ -63,6 +63,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic():
+    """HBM bytes per launch of the fused NF4 GEMM from the committed
+    rocprofv3 FETCH_SIZE + WRITE_SIZE runs, if the GEMM source is unchanged
+    since they were taken (else None)."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "nf4_gemm_llama8b_sft_traffic.md")
+    src = os.path.join(ROOT, "layer_streamed_nf4_double_amd", "csrc", "gemm.hip")
+    try:
+        kv = dict(l.split(": ", 1) for l in open(prof).read().splitlines() if ": " in l and
+                  l.split(": ", 1)[0] in ("traffic_bytes_per_launch", "gemm_source_sha256"))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if kv.get("gemm_source_sha256", "").strip() != digest:
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
 # ---------------------------------------------------------------------------
 # model construction (off the clock)
 # ---------------------------------------------------------------------------
@@ -258,7 +276,7 @@ def main():
     achieved = flops / (ms / 1e3) / 1e12 if ms > 0 else 0.0
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": None,
+                "traffic": measured_traffic(),
                 "kernel": "gemm_kernel<256,128,A_BF16_K,B_NF4_K> (fused NF4-dequant GEMM)",
                 "launches": int(n_gemm), "avg_us": round(ms / max(n_gemm, 1) * 1e3, 2),
                 "flop_per_launch": flops / max(n_gemm, 1)}
@@ -298,6 +316,7 @@ def main():
         del md
         torch.cuda.empty_cache()
         dpo = {"tokens_per_s": round(2 * S / ddt, 2), "ms_per_step": round(ddt * 1e3, 2),
+               "reference_pass": "fused with the policy forward (one record copy per layer)",
                "tokens_per_step": 2 * S, "loss": float(out[0]),
                "layer_loads_per_step": (l1 - l0) / args.dpo_steps,
                "layer_loads_ratio_vs_sft": round((l1 - l0) / args.dpo_steps / max(loads_per_step, 1e-9), 3),

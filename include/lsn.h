@@ -195,6 +195,18 @@ lsn_status lsn_embed(lsn_ctx* ctx, const int32_t* tokens, float* h0);
  * RMSNorm, q/k/v (+LoRA), RoPE, causal GQA attention, o (+LoRA) + residual,
  * RMSNorm, SwiGLU MLP (+LoRA) + residual. */
 lsn_status lsn_forward_layer(lsn_ctx* ctx, int32_t layer, const float* h_in, float* h_out);
+/* Reference and policy forward of one layer on ONE copy of its record: the
+ * layer runs first with every low-rank branch skipped on h_ref_in ->
+ * h_ref_out (the DPO reference model: the same base with the adapter off,
+ * page "Show HN: Fine-tune an 8B model on a 4 GB laptop GPU", first
+ * paragraph), then with the adapter state set by lsn_set_adapter_enabled on
+ * h_in -> h_out.  Results are bit-identical to two separate passes; the
+ * streamed base is read once instead of twice (that page's second paragraph
+ * gives the cost of separate passes: 1.52x the layer reads of SFT).
+ * Device fp32 [T, hidden] each; the outputs must not alias the other
+ * stream's buffers. */
+lsn_status lsn_forward_layer_pair(lsn_ctx* ctx, int32_t layer, const float* h_ref_in,
+                                  float* h_ref_out, const float* h_in, float* h_out);
 /* Recomputes the layer from its saved input, then back-propagates:
  * dh_in = d loss / d h_in (may alias dh_out), and adds the adapter
  * gradients of this layer into the context's gradient buffers.  The base
@@ -232,6 +244,24 @@ lsn_status lsn_sft_loss(lsn_ctx* ctx, const float* logp, const int32_t* targets,
 lsn_status lsn_dpo_loss(lsn_ctx* ctx, const float* logp_pol, const float* logp_ref,
                         int32_t seq_len, int32_t prompt_len, float beta, float* out6,
                         float* dlogp_pol);
+
+/* Other preference losses over the same streamed base (page "axbrief.com",
+ * "The Architecture of Low-VRAM Alignment", and the evermx page: DPO, ORPO,
+ * SimPO and KTO run over layer streaming; the pages give no formulas).
+ * Same pair layout and response positions as lsn_dpo_loss; n = seq_len -
+ * prompt_len response tokens per sequence; mc, mr = pc/n, pr/n.
+ *   LSN_LOSS_DPO   as lsn_dpo_loss (param unused)
+ *   LSN_LOSS_SIMPO u = beta(mc - mr) - param (param = gamma), loss = -log sig(u)
+ *   LSN_LOSS_ORPO  v = lo(mc) - lo(mr), lo(m) = m - log(1 - e^m),
+ *                  loss = -mc - param * log sig(v) (param = lambda; beta unused)
+ *   LSN_LOSS_KTO   loss = (1 - sig(beta(pc-rc))) + (1 - sig(-beta(pr-rr)))
+ *                  (chosen desirable, rejected undesirable, reference point 0)
+ * logp_ref (device) is required for DPO and KTO and ignored otherwise.
+ * out6 = {loss, z|u|v|pc-rc, pc, pr, rc, rr}; dlogp_pol as for DPO. */
+enum { LSN_LOSS_DPO = 0, LSN_LOSS_SIMPO = 1, LSN_LOSS_ORPO = 2, LSN_LOSS_KTO = 3 };
+lsn_status lsn_pref_loss(lsn_ctx* ctx, int32_t kind, const float* logp_pol, const float* logp_ref,
+                         int32_t seq_len, int32_t prompt_len, float beta, float param,
+                         float* out6, float* dlogp_pol);
 
 /* Counters since lsn_create: layer records copied host->device, bytes copied
  * host->device by the scheduler, and workspace bytes carved.  Any may be NULL. */

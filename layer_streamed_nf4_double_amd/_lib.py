@@ -72,11 +72,13 @@ _SIGS = {
     "lsn_begin_pass": [_P, _I32, _I32, _I32],
     "lsn_embed": [_P, _P, _P],
     "lsn_forward_layer": [_P, _I32, _P, _P],
+    "lsn_forward_layer_pair": [_P, _I32, _P, _P, _P, _P],
     "lsn_backward_layer": [_P, _I32, _P, _P, _P],
     "lsn_lm_head_logprobs": [_P, _P, _P, _P],
     "lsn_lm_head_backward": [_P, _P, _P, _P, _P],
     "lsn_sft_loss": [_P, _P, _P, _I32, _P, _P],
     "lsn_dpo_loss": [_P, _P, _P, _I32, _I32, _F, _P, _P],
+    "lsn_pref_loss": [_P, _I32, _P, _P, _I32, _I32, _F, _F, _P, _P],
     "lsn_stats": [_P, ctypes.POINTER(_U64), ctypes.POINTER(_U64), ctypes.POINTER(_U64)],
     "lsn_copy_stream": [_P, ctypes.POINTER(_P)],
     "lsn_set_profiling": [_P, _I32],
@@ -262,6 +264,11 @@ def lsn_forward_layer(ctx, layer, h_in, h_out):
     _check(_lib.lsn_forward_layer(ctx, layer, _ptr(h_in), _ptr(h_out)), ctx, "lsn_forward_layer")
 
 
+def lsn_forward_layer_pair(ctx, layer, h_ref_in, h_ref_out, h_in, h_out):
+    _check(_lib.lsn_forward_layer_pair(ctx, layer, _ptr(h_ref_in), _ptr(h_ref_out), _ptr(h_in),
+                                       _ptr(h_out)), ctx, "lsn_forward_layer_pair")
+
+
 def lsn_backward_layer(ctx, layer, h_in, dh_out, dh_in):
     _check(_lib.lsn_backward_layer(ctx, layer, _ptr(h_in), _ptr(dh_out), _ptr(dh_in)), ctx,
            "lsn_backward_layer")
@@ -285,6 +292,15 @@ def lsn_sft_loss(ctx, logp, targets, n, loss, dlogp):
 def lsn_dpo_loss(ctx, logp_pol, logp_ref, seq_len, prompt_len, beta, out6, dlogp_pol):
     _check(_lib.lsn_dpo_loss(ctx, _ptr(logp_pol), _ptr(logp_ref), seq_len, prompt_len, beta,
                              _ptr(out6), _ptr(dlogp_pol)), ctx, "lsn_dpo_loss")
+
+
+LSN_LOSS_DPO, LSN_LOSS_SIMPO, LSN_LOSS_ORPO, LSN_LOSS_KTO = 0, 1, 2, 3
+
+
+def lsn_pref_loss(ctx, kind, logp_pol, logp_ref, seq_len, prompt_len, beta, param, out6,
+                  dlogp_pol):
+    _check(_lib.lsn_pref_loss(ctx, kind, _ptr(logp_pol), _ptr(logp_ref), seq_len, prompt_len,
+                              beta, param, _ptr(out6), _ptr(dlogp_pol)), ctx, "lsn_pref_loss")
 
 
 def lsn_stats(ctx):

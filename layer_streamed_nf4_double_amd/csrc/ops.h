@@ -30,8 +30,9 @@ void dlogits(const float* logits, int T, int Vc, int v0, const float* lse, const
              const float* dlogp, uint16_t* out, hipStream_t s);
 void sft_loss(const float* logp, const int32_t* tgt, int n, float* loss, float* dlogp,
               hipStream_t s);
-void dpo_loss(const float* lp, const float* lr, int S, int P, float beta, float* out,
-              float* dlogp, hipStream_t s);
+// kind: 0 DPO, 1 SimPO, 2 ORPO, 3 KTO (lr may be null for 1 and 2)
+void pref_loss(int kind, const float* lp, const float* lr, int S, int P, float beta, float p2,
+               float* out, float* dlogp, hipStream_t s);
 void sgd(float* p, const float* g, float lr, int64_t n, hipStream_t s);
 void fill_u32(void* p, uint32_t v, int64_t n, hipStream_t s);
 void f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);

@@ -279,34 +279,71 @@ __global__ void sft_loss_k(const float* __restrict__ logp, const int32_t* __rest
   for (int i = threadIdx.x; i < n; i += blockDim.x) dlogp[i] = (tgt[i] >= 0) ? g : 0.f;
 }
 
-__global__ void dpo_loss_k(const float* __restrict__ lp, const float* __restrict__ lr, int S,
-                           int P, float beta, float* __restrict__ out,
-                           float* __restrict__ dlogp) {
+// Preference losses on one pair laid out as two sequences (chosen, rejected)
+// of S tokens; response targets at positions P-1 .. S-2 (n = S-P each).
+// kind 0 DPO:   z = beta((pc-rc)-(pr-rr)),  loss = softplus(-z)
+// kind 1 SimPO: u = beta(pc/n - pr/n) - p2, loss = softplus(-u)
+// kind 2 ORPO:  v = lo(pc/n) - lo(pr/n), lo(m) = m - log(1-e^m),
+//               loss = -pc/n + p2 softplus(-v)
+// kind 3 KTO:   loss = (1 - sig(beta(pc-rc))) + (1 - sig(-beta(pr-rr)))
+// out = {loss, z|u|v|pc-rc, pc, pr, rc, rr}; dlogp on response positions.
+LSN_DEV float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+LSN_DEV float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+__global__ void pref_loss_k(int kind, const float* __restrict__ lp, const float* __restrict__ lr,
+                            int S, int P, float beta, float p2, float* __restrict__ out,
+                            float* __restrict__ dlogp) {
   __shared__ float red[16];
   float v[4] = {0.f, 0.f, 0.f, 0.f};  // pc, pr, rc, rr
   for (int i = threadIdx.x; i < 2 * S; i += blockDim.x) {
     const int seq = i / S, pos = i % S;
     if (pos >= P - 1 && pos <= S - 2) {
       v[seq] += lp[i];
-      v[2 + seq] += lr[i];
+      if (lr) v[2 + seq] += lr[i];
     }
   }
   for (int q = 0; q < 4; ++q) v[q] = block_sum(v[q], red);
-  const float z = beta * ((v[0] - v[2]) - (v[1] - v[3]));
-  // -log sigmoid(z) = softplus(-z), stable form
-  const float loss = fmaxf(-z, 0.f) + log1pf(expf(-fabsf(z)));
-  const float g = beta / (1.0f + expf(z));  // beta * sigmoid(-z)
+  const float pc = v[0], pr = v[1], rc = v[2], rr = v[3];
+  const float n = (float)(S - P);
+  float loss = 0.f, aux = 0.f, gc = 0.f, gr = 0.f;
+  if (kind == 0) {
+    aux = beta * ((pc - rc) - (pr - rr));
+    loss = softplus_f(-aux);
+    const float g = beta * sigmoid_f(-aux);
+    gc = -g;
+    gr = g;
+  } else if (kind == 1) {
+    aux = beta * (pc / n - pr / n) - p2;
+    loss = softplus_f(-aux);
+    const float g = sigmoid_f(-aux) * beta / n;
+    gc = -g;
+    gr = g;
+  } else if (kind == 2) {
+    const float mc = pc / n, mr = pr / n;
+    const float oc = -expm1f(mc), orr = -expm1f(mr);  // 1 - e^m
+    aux = (mc - logf(oc)) - (mr - logf(orr));
+    loss = -mc + p2 * softplus_f(-aux);
+    const float g = p2 * sigmoid_f(-aux);
+    gc = (-1.0f - g / oc) / n;
+    gr = (g / orr) / n;
+  } else {
+    aux = pc - rc;
+    const float sc = sigmoid_f(beta * aux), sr = sigmoid_f(-beta * (pr - rr));
+    loss = (1.0f - sc) + (1.0f - sr);
+    gc = -beta * sc * (1.0f - sc);
+    gr = beta * sr * (1.0f - sr);
+  }
   if (threadIdx.x == 0) {
     out[0] = loss;
-    out[1] = z;
-    out[2] = v[0];
-    out[3] = v[1];
-    out[4] = v[2];
-    out[5] = v[3];
+    out[1] = aux;
+    out[2] = pc;
+    out[3] = pr;
+    out[4] = rc;
+    out[5] = rr;
   }
   for (int i = threadIdx.x; i < 2 * S; i += blockDim.x) {
     const int seq = i / S, pos = i % S;
-    dlogp[i] = (pos >= P - 1 && pos <= S - 2) ? (seq == 0 ? -g : g) : 0.f;
+    dlogp[i] = (pos >= P - 1 && pos <= S - 2) ? (seq == 0 ? gc : gr) : 0.f;
   }
 }
 
@@ -421,9 +458,10 @@ void sft_loss(const float* logp, const int32_t* tgt, int n, float* loss, float* 
               hipStream_t s) {
   hipLaunchKernelGGL(sft_loss_k, dim3(1), dim3(1024), 0, s, logp, tgt, n, loss, dlogp);
 }
-void dpo_loss(const float* lp, const float* lr, int S, int P, float beta, float* out,
-              float* dlogp, hipStream_t s) {
-  hipLaunchKernelGGL(dpo_loss_k, dim3(1), dim3(1024), 0, s, lp, lr, S, P, beta, out, dlogp);
+void pref_loss(int kind, const float* lp, const float* lr, int S, int P, float beta, float p2,
+               float* out, float* dlogp, hipStream_t s) {
+  hipLaunchKernelGGL(pref_loss_k, dim3(1), dim3(1024), 0, s, kind, lp, lr, S, P, beta, p2, out,
+                     dlogp);
 }
 void sgd(float* p, const float* g, float lr, int64_t n, hipStream_t s) {
   hipLaunchKernelGGL(sgd_k, dim3(nb(n, 256)), dim3(256), 0, s, p, g, lr, n);

@@ -1159,6 +1159,28 @@ lsn_status lsn_forward_layer(lsn_ctx* c, int32_t layer, const float* h_in, float
   return layer_end(c);
 }
 
+lsn_status lsn_forward_layer_pair(lsn_ctx* c, int32_t layer, const float* h_ref_in,
+                                  float* h_ref_out, const float* h_in, float* h_out) {
+  CHECK_CTX(c);
+  if (!h_ref_in || !h_ref_out || !h_in || !h_out)
+    return fail(c, LSN_ERR_INVALID, "null activation");
+  if (h_ref_out == h_in || h_ref_out == h_out || h_out == h_ref_in)
+    return fail(c, LSN_ERR_INVALID, "reference and policy activations must not overlap");
+  const uint8_t* rec;
+  lsn_status st = layer_begin(c, LSN_PASS_FWD, layer, &rec);
+  if (st != LSN_OK) return st;
+  // the same record, first without the low-rank branches (reference model),
+  // then with them (policy); the kernels are the ones of lsn_forward_layer
+  const bool on = c->adapters_on;
+  c->adapters_on = false;
+  st = layer_forward(c, layer, rec, h_ref_in, h_ref_out, true);
+  c->adapters_on = on;
+  if (st != LSN_OK) return st;
+  st = layer_forward(c, layer, rec, h_in, h_out, true);
+  if (st != LSN_OK) return st;
+  return layer_end(c);
+}
+
 lsn_status lsn_backward_layer(lsn_ctx* c, int32_t layer, const float* h_in, const float* dh_out,
                               float* dh_in) {
   CHECK_CTX(c);
@@ -1237,7 +1259,20 @@ lsn_status lsn_dpo_loss(lsn_ctx* c, const float* lp, const float* lr, int32_t se
   CHECK_CTX(c);
   if (!lp || !lr || !out6 || !dlogp || seq_len < 2 || prompt_len < 1 || prompt_len >= seq_len)
     return fail(c, LSN_ERR_INVALID, "bad dpo_loss arguments");
-  dpo_loss(lp, lr, seq_len, prompt_len, beta, out6, dlogp, c->cs);
+  pref_loss(0, lp, lr, seq_len, prompt_len, beta, 0.f, out6, dlogp, c->cs);
+  return launch_check(c);
+}
+
+lsn_status lsn_pref_loss(lsn_ctx* c, int32_t kind, const float* lp, const float* lr,
+                         int32_t seq_len, int32_t prompt_len, float beta, float param,
+                         float* out6, float* dlogp) {
+  CHECK_CTX(c);
+  if (kind < LSN_LOSS_DPO || kind > LSN_LOSS_KTO || !lp || !out6 || !dlogp || seq_len < 2 ||
+      prompt_len < 1 || prompt_len >= seq_len)
+    return fail(c, LSN_ERR_INVALID, "bad pref_loss arguments");
+  if ((kind == LSN_LOSS_DPO || kind == LSN_LOSS_KTO) && !lr)
+    return fail(c, LSN_ERR_INVALID, "this loss needs reference log-probs");
+  pref_loss(kind, lp, lr, seq_len, prompt_len, beta, param, out6, dlogp, c->cs);
   return launch_check(c);
 }
 

@@ -8,7 +8,9 @@ LM-head log-probs, loss, LM-head backward, backward over the stack in reverse
 adapter.  One DPO step (page "Show HN: Fine-tune an 8B model on a 4 GB laptop
 GPU", first paragraph): a reference forward with the adapter switched off,
 then the policy forward with it on, both over the same streamed base, then
-the DPO loss and the backward of the policy pass.
+the DPO loss and the backward of the policy pass.  By default both forwards
+run on one copy of each layer record (lsn_forward_layer_pair), so a DPO step
+streams the stack twice, like SFT, instead of three times.
 """
 import numpy as np
 
@@ -17,6 +19,8 @@ from ._lib import (LSN_PASS_BWD, LSN_PASS_FWD, LSN_RESIDENT, LSN_STREAM_FILE,
                    LSN_STREAM_HOST, PROJ, PROJ_ID)
 
 MODES = {"resident": LSN_RESIDENT, "stream_host": LSN_STREAM_HOST, "stream_file": LSN_STREAM_FILE}
+PREF_LOSSES = {"dpo": L.LSN_LOSS_DPO, "simpo": L.LSN_LOSS_SIMPO, "orpo": L.LSN_LOSS_ORPO,
+               "kto": L.LSN_LOSS_KTO}
 
 
 def make_config(shape, mode="stream_host", max_tokens=None, max_seq_len=None,
@@ -63,6 +67,7 @@ class LayerStreamedLoRA:
         T, H, nl = self.cfg.max_tokens, self.cfg.hidden, self.cfg.n_layers
         f32 = dict(dtype=torch.float32, device=self.device)
         self.hs = [torch.empty(T, H, **f32) for _ in range(nl + 1)]
+        self.href = [torch.empty(T, H, **f32) for _ in range(2)]  # fused DPO reference
         self.dh = torch.empty(T, H, **f32)
         self.logp = torch.empty(T, **f32)
         self.logp_ref = torch.empty(T, **f32)
@@ -143,18 +148,63 @@ class LayerStreamedLoRA:
             L.lsn_sgd_step(self.ctx, lr)
         return self.loss
 
-    def dpo_step(self, tokens, targets, seq_len, prompt_len, beta, lr):
+    def _forward_pair(self, tokens, n_seq, seq_len):
+        """Reference (adapter off) and policy forward sharing every layer
+        record; the policy inputs are kept.  Returns (h_ref_L, h_L)."""
+        T = n_seq * seq_len
+        L.lsn_begin_pass(self.ctx, LSN_PASS_FWD, n_seq, seq_len)
+        hs = [h[:T] for h in self.hs]
+        hr = [h[:T] for h in self.href]
+        L.lsn_embed(self.ctx, tokens, hs[0])
+        L.lsn_embed(self.ctx, tokens, hr[0])
+        for i in range(self.cfg.n_layers):
+            L.lsn_forward_layer_pair(self.ctx, i, hr[i % 2], hr[(i + 1) % 2], hs[i], hs[i + 1])
+        return hr[self.cfg.n_layers % 2], hs[self.cfg.n_layers]
+
+    def dpo_step(self, tokens, targets, seq_len, prompt_len, beta, lr, fused=True):
         """tokens, targets: device int32 [2*seq_len] (chosen then rejected).
-        loss[0..5] = loss, z, pc, pr, rc, rr."""
+        loss[0..5] = loss, z, pc, pr, rc, rr.  fused: the reference forward
+        runs on the same record copy as the policy forward (2L record loads
+        per step instead of 3L); the results are the same bits."""
         T = 2 * seq_len
-        L.lsn_set_adapter_enabled(self.ctx, 0)
-        h_ref = self._forward(tokens, 2, seq_len, save=False)
-        L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T])
-        L.lsn_set_adapter_enabled(self.ctx, 1)
-        hL = self._forward(tokens, 2, seq_len, save=True)
+        if fused:
+            L.lsn_set_adapter_enabled(self.ctx, 1)
+            h_ref, hL = self._forward_pair(tokens, 2, seq_len)
+            L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T])
+        else:
+            L.lsn_set_adapter_enabled(self.ctx, 0)
+            h_ref = self._forward(tokens, 2, seq_len, save=False)
+            L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T])
+            L.lsn_set_adapter_enabled(self.ctx, 1)
+            hL = self._forward(tokens, 2, seq_len, save=True)
         L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T])
         L.lsn_dpo_loss(self.ctx, self.logp[:T], self.logp_ref[:T], seq_len, prompt_len, beta,
                        self.loss, self.dlogp[:T])
+        L.lsn_lm_head_backward(self.ctx, hL, targets, self.dlogp[:T], self.dh[:T])
+        self._backward(2, seq_len)
+        if lr is not None:
+            L.lsn_sgd_step(self.ctx, lr)
+        return self.loss
+
+
+    def pref_step(self, kind, tokens, targets, seq_len, prompt_len, beta, param, lr):
+        """One preference step on a pair with the loss ``kind`` (dpo, simpo, orpo,
+        kto).  Losses with a reference (dpo, kto) run the adapter-off forward on
+        the same record copies as the policy forward; reference-free ones
+        (simpo, orpo) stream the stack once forward, like SFT."""
+        T = 2 * seq_len
+        k = PREF_LOSSES[kind]
+        L.lsn_set_adapter_enabled(self.ctx, 1)
+        ref = None
+        if k in (L.LSN_LOSS_DPO, L.LSN_LOSS_KTO):
+            h_ref, hL = self._forward_pair(tokens, 2, seq_len)
+            L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T])
+            ref = self.logp_ref[:T]
+        else:
+            hL = self._forward(tokens, 2, seq_len, save=True)
+        L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T])
+        L.lsn_pref_loss(self.ctx, k, self.logp[:T], ref, seq_len, prompt_len, beta, param,
+                        self.loss, self.dlogp[:T])
         L.lsn_lm_head_backward(self.ctx, hL, targets, self.dlogp[:T], self.dh[:T])
         self._backward(2, seq_len)
         if lr is not None:

@@ -465,3 +465,108 @@ def dpo_step(cfg, layers, lora, head, chosen, rejected, prompt_len, beta, lr,
     _, grads = backward_stack(cfg, layers, lora, head, inputs, dh, 2, dequantize_layer)
     return dict(loss=loss, z=z, logp_policy=logp_pol, logp_ref=logp_ref,
                 grads=grads, lora_new=sgd(lora, grads, lr))
+
+
+# --------------------------------------------------------------------------
+# other preference losses over the same streamed base
+# --------------------------------------------------------------------------
+# The pages list ORPO, SimPO and KTO as running over layer streaming (axbrief
+# article, "The Architecture of Low-VRAM Alignment"; the evermx page); they
+# give no formulas.  The plainest readings, on one pair laid out as two
+# sequences (chosen, rejected) with response targets at positions
+# prompt_len-1 .. S-2:
+#   SimPO  u = beta (mean_c - mean_r) - gamma,  loss = -log sigmoid(u)
+#          (mean_* = average response log-prob; reference-free)
+#   ORPO   loss = -mean_c - lam * log sigmoid(odds_c - odds_r),
+#          odds(m) = m - log(1 - exp(m))  (log-odds of the average token
+#          probability exp(m); reference-free)
+#   KTO    r_* = sum_* (policy) - sum_* (reference); chosen desirable,
+#          rejected undesirable, reference point 0:
+#          loss = (1 - sigmoid(beta r_c)) + (1 - sigmoid(-beta r_r))
+# Each returns (loss, dloss/dlogp_policy [2S], aux dict).
+
+def _pair_stats(logp, seq_len, prompt_len):
+    mask = response_mask(seq_len, prompt_len, 2)
+    S = seq_len
+    n_c = int(mask[:S].sum())
+    n_r = int(mask[S:].sum())
+    s_c = np.sum(logp[:S][mask[:S]])
+    s_r = np.sum(logp[S:][mask[S:]])
+    return mask, n_c, n_r, s_c, s_r
+
+
+def simpo_loss(logp, seq_len, prompt_len, beta, gamma):
+    mask, n_c, n_r, s_c, s_r = _pair_stats(logp, seq_len, prompt_len)
+    S = seq_len
+    u = beta * (s_c / n_c - s_r / n_r) - gamma
+    loss = -log_sigmoid(u)
+    g = sigmoid(-u)                       # -dloss/du
+    d = np.zeros_like(logp)
+    d[:S][mask[:S]] = -g * beta / n_c
+    d[S:][mask[S:]] = g * beta / n_r
+    return loss, d, dict(u=u)
+
+
+def log_odds(m):
+    """log(p / (1 - p)) for p = exp(m), m < 0."""
+    return m - np.log(-np.expm1(m))
+
+
+def orpo_loss(logp, seq_len, prompt_len, lam):
+    mask, n_c, n_r, s_c, s_r = _pair_stats(logp, seq_len, prompt_len)
+    S = seq_len
+    m_c, m_r = s_c / n_c, s_r / n_r
+    v = log_odds(m_c) - log_odds(m_r)
+    loss = -m_c - lam * log_sigmoid(v)
+    # d log_odds / dm = 1 / (1 - exp(m))
+    dv_c = 1.0 / (-np.expm1(m_c))
+    dv_r = 1.0 / (-np.expm1(m_r))
+    g = lam * sigmoid(-v)                 # -dloss/dv from the odds term
+    d = np.zeros_like(logp)
+    d[:S][mask[:S]] = (-1.0 - g * dv_c) / n_c
+    d[S:][mask[S:]] = (g * dv_r) / n_r
+    return loss, d, dict(v=v)
+
+
+def kto_loss(logp_policy, logp_ref, seq_len, prompt_len, beta):
+    mask, n_c, n_r, pc, pr = _pair_stats(logp_policy, seq_len, prompt_len)
+    _, _, _, rc, rr = _pair_stats(logp_ref, seq_len, prompt_len)
+    S = seq_len
+    r_c, r_r = pc - rc, pr - rr
+    loss = (1.0 - sigmoid(beta * r_c)) + (1.0 - sigmoid(-beta * r_r))
+    sc = sigmoid(beta * r_c)
+    sr = sigmoid(-beta * r_r)
+    d = np.zeros_like(logp_policy)
+    d[:S][mask[:S]] = -beta * sc * (1.0 - sc)
+    d[S:][mask[S:]] = beta * sr * (1.0 - sr)
+    return loss, d, dict(r_c=r_c, r_r=r_r)
+
+
+def pref_step(cfg, layers, lora, head, chosen, rejected, prompt_len, kind, beta, param, lr):
+    """One LoRA step with a preference loss ``kind`` (dpo, simpo, orpo, kto);
+    param is gamma (simpo) or lambda (orpo).  Reference log-probs, when the
+    loss uses them, come from the same base with the adapter off."""
+    tokens = np.stack([np.asarray(chosen), np.asarray(rejected)])
+    S = tokens.shape[1]
+    targets = sft_targets(tokens)
+    ref = None
+    if kind in ("dpo", "kto"):
+        h_ref, _ = forward_stack(cfg, layers, lora, head, tokens, False)
+        ref, _ = head_logprobs(cfg, head, h_ref, targets)
+    hL, inputs = forward_stack(cfg, layers, lora, head, tokens, True)
+    logp, hc = head_logprobs(cfg, head, hL, targets)
+    if kind == "dpo":
+        loss, dlogp, aux = dpo_loss(logp, ref, S, prompt_len, beta)
+    elif kind == "simpo":
+        loss, dlogp, a = simpo_loss(logp, S, prompt_len, beta, param)
+        aux = a["u"]
+    elif kind == "orpo":
+        loss, dlogp, a = orpo_loss(logp, S, prompt_len, param)
+        aux = a["v"]
+    else:
+        loss, dlogp, a = kto_loss(logp, ref, S, prompt_len, beta)
+        aux = a["r_c"]
+    dh = head_backward(cfg, head, hc, dlogp)
+    _, grads = backward_stack(cfg, layers, lora, head, inputs, dh, 2)
+    return dict(loss=loss, aux=aux, logp_policy=logp, logp_ref=ref, grads=grads,
+                lora_new=sgd(lora, grads, lr))

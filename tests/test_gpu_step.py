@@ -218,3 +218,72 @@ def test_all_projections_adapted_gqa(torch):
             assert_close(dA, odA, 5e-2, f"dA L{layer} {p}")
             assert_close(dB, odB, 5e-2, f"dB L{layer} {p}")
     m.close()
+
+
+def _dpo_record(torch, m, w, tok, tgt, S, P, beta, fused):
+    rec = []
+    for _ in range(2):
+        out = m.dpo_step(tok, tgt, S, P, beta, LR, fused=fused)
+        m.sync()
+        rec.append((out[:6].cpu().numpy().copy(), m.logp[:2 * S].cpu().numpy().copy(),
+                    m.logp_ref[:2 * S].cpu().numpy().copy(), _grads(m, w)))
+    return rec
+
+
+def test_dpo_fused_reference_pass_bitwise(torch):
+    """The reference forward run on the same layer copy as the policy forward
+    gives the same bits as a separate adapter-off pass, with 2L instead of 3L
+    record copies per step (minus the 2 reused at each pass boundary)."""
+    w = dict(TINY, n_layers=5)
+    S, P, beta = 64, 16, 0.1
+    pr = synth.tokens((P,), w["vocab"], 89, synth.TID_PROMPT)
+    ch = np.concatenate([pr, synth.tokens((S - P,), w["vocab"], 89, synth.TID_CHOSEN)])
+    rj = np.concatenate([pr, synth.tokens((S - P,), w["vocab"], 89, synth.TID_REJECTED)])
+    tok, tgt = _dev_tokens(torch, np.stack([ch, rj]))
+    say("[dpo fused vs separate]")
+    sep = gpu_model(w, "stream_host", b_zero=False, max_tokens=2 * S)
+    a = _dpo_record(torch, sep, w, tok, tgt, S, P, beta, fused=False)
+    loads_sep = sep.stats()[0]
+    sep.close()
+    fus = gpu_model(w, "stream_host", b_zero=False, max_tokens=2 * S)
+    b = _dpo_record(torch, fus, w, tok, tgt, S, P, beta, fused=True)
+    loads_fus = fus.stats()[0]
+    fus.close()
+    for (oa, la, ra, ga), (ob, lb, rb, gb) in zip(a, b):
+        assert np.array_equal(_bits(oa), _bits(ob))
+        assert np.array_equal(_bits(la), _bits(lb)) and np.array_equal(_bits(ra), _bits(rb))
+        for da, db in zip(ga, gb):
+            for p in da:
+                for x, y in zip(da[p], db[p]):
+                    assert np.array_equal(_bits(x), _bits(y))
+    L_ = w["n_layers"]
+    assert loads_sep == (3 * L_ - 2) + (3 * L_ - 4), loads_sep
+    assert loads_fus == (2 * L_ - 2) + (2 * L_ - 4), loads_fus
+
+
+@pytest.mark.parametrize("kind,beta,param", [("simpo", 2.0, 0.5), ("orpo", 0.0, 0.1),
+                                             ("kto", 0.1, 0.0), ("dpo", 0.1, 0.0)])
+def test_preference_losses_tiny(torch, kind, beta, param):
+    w = dict(TINY)
+    S, P = 64, 16
+    pr = synth.tokens((P,), w["vocab"], 90, synth.TID_PROMPT)
+    ch = np.concatenate([pr, synth.tokens((S - P,), w["vocab"], 90, synth.TID_CHOSEN)])
+    rj = np.concatenate([pr, synth.tokens((S - P,), w["vocab"], 90, synth.TID_REJECTED)])
+    tok, tgt = _dev_tokens(torch, np.stack([ch, rj]))
+    say(f"[pref {kind}]")
+    cfg, layers, lora, head = oracle_model(w, b_zero=False)
+    od = om.pref_step(cfg, layers, lora, head, ch, rj, P, kind, beta, param, LR)
+    m = gpu_model(w, "stream_host", b_zero=False, max_tokens=2 * S)
+    out = m.pref_step(kind, tok, tgt, S, P, beta, param, LR)
+    m.sync()
+    o = out.cpu().numpy()
+    assert abs(o[0] - od["loss"]) <= 2e-2 * abs(od["loss"]), (o[0], od["loss"])
+    assert_close(m.logp[:2 * S].cpu().numpy(), od["logp_policy"], 2e-2, "policy logp")
+    g = _grads(m, w)
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            _, _, dA, dB = g[layer][p]
+            odA, odB = od["grads"][layer][p]
+            assert_close(dA, odA, 5e-2, f"{kind} dA L{layer} {p}")
+            assert_close(dB, odB, 5e-2, f"{kind} dB L{layer} {p}")
+    m.close()
