@@ -134,6 +134,12 @@ lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t
 /* Device bytes the context needs for cfg (records or slots, head tables,
  * adapters and gradients, one layer's activations at max_tokens). */
 lsn_status lsn_workspace_bytes(const lsn_config* cfg, uint64_t* bytes);
+/* Bytes of one layer record for cfg (codes + absmax + norm gains, 4 KiB
+ * aligned): the host store holds n_layers of them, a streamed step copies
+ * each one twice.  Used to choose RAM or file storage before lsn_create
+ * ("RAM when it fits, NVMe when it does not": page "Soup: Fine-Tune an 8B
+ * Model on a 4 GB GPU", "The Core Idea: Layer Streaming"). */
+lsn_status lsn_config_record_bytes(const lsn_config* cfg, uint64_t* bytes);
 /* dev_ws: device, ws_bytes >= lsn_workspace_bytes (else LSN_ERR_NOFIT, the
  * pre-flight refusal of a run that will not fit: page "Soup: Fine-Tune an 8B
  * Model on a 4 GB GPU", "A Practical Quick Start").  hip_stream: the compute

@@ -57,6 +57,7 @@ _SIGS = {
     "lsn_nf4_linear_bwd": [_P, _P, _I32, _I32, _I32, _P, _P, _P, _I32, _F, _P, _P, _P, _P, _P,
                            _U64, _P],
     "lsn_workspace_bytes": [_CFG, ctypes.POINTER(_U64)],
+    "lsn_config_record_bytes": [_CFG, ctypes.POINTER(_U64)],
     "lsn_create": [_CFG, _P, _U64, _P, ctypes.POINTER(_P)],
     "lsn_destroy": [_P],
     "lsn_last_error": [_P],
@@ -176,6 +177,13 @@ def lsn_nf4_linear_bwd(codes, absmax, M, K, N, X, A, B, r, s, dY, dX, dA, dB, sc
 def lsn_workspace_bytes(cfg):
     b = _U64(0)
     _check(_lib.lsn_workspace_bytes(ctypes.byref(cfg), ctypes.byref(b)), what="lsn_workspace_bytes")
+    return b.value
+
+
+def lsn_config_record_bytes(cfg):
+    b = _U64(0)
+    _check(_lib.lsn_config_record_bytes(ctypes.byref(cfg), ctypes.byref(b)),
+           what="lsn_config_record_bytes")
     return b.value
 
 

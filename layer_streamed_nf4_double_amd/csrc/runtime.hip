@@ -929,6 +929,16 @@ lsn_status lsn_workspace_bytes(const lsn_config* cfg, uint64_t* bytes) {
   return LSN_OK;
 }
 
+lsn_status lsn_config_record_bytes(const lsn_config* cfg, uint64_t* bytes) {
+  std::string why;
+  if (!bytes || !cfg_valid(cfg, &why)) return LSN_ERR_INVALID;
+  lsn_ctx tmp;
+  tmp.cfg = *cfg;
+  record_layout(&tmp);
+  *bytes = tmp.rec_bytes;
+  return LSN_OK;
+}
+
 lsn_status lsn_create(const lsn_config* cfg, void* dev_ws, uint64_t ws_bytes, void* hip_stream,
                       lsn_ctx** out) {
   std::string why;

@@ -12,6 +12,8 @@ the DPO loss and the backward of the policy pass.  By default both forwards
 run on one copy of each layer record (lsn_forward_layer_pair), so a DPO step
 streams the stack twice, like SFT, instead of three times.
 """
+import os
+
 import numpy as np
 
 from . import _lib as L
@@ -54,10 +56,28 @@ class LayerStreamedLoRA:
 
     def __init__(self, shape, mode="stream_host", max_tokens=None, max_seq_len=None,
                  lora_targets=("q", "v"), store_path=None, device="cuda:0", stream=None):
+        """mode: resident | stream_host | stream_file | auto.  'auto' keeps the
+        base in pinned RAM when it fits and in a file (store_path, or a file
+        in $TMPDIR) when it does not; every mode is pre-flighted against the
+        free device memory (adapter.NoFit)."""
+        import tempfile
+
         import torch
+
+        from . import adapter
         self.torch = torch
         self.shape = dict(shape)
         self.device = torch.device(device)
+        probe = make_config(shape, "stream_host" if mode == "auto" else mode, max_tokens,
+                            max_seq_len, lora_targets, store_path)
+        free, _ = torch.cuda.mem_get_info(self.device)
+        mode = adapter.plan_run(shape["n_layers"], L.lsn_config_record_bytes(probe),
+                                L.lsn_workspace_bytes(probe), free,
+                                adapter.host_bytes_available(),
+                                source="auto" if mode == "auto" else mode)
+        if mode == "stream_file" and not store_path:
+            store_path = os.path.join(tempfile.gettempdir(), f"lsn_store_{os.getpid()}.bin")
+        self.mode = mode
         self.cfg = make_config(shape, mode, max_tokens, max_seq_len, lora_targets, store_path)
         self.lora_targets = tuple(lora_targets)
         self.ws_bytes = L.lsn_workspace_bytes(self.cfg)

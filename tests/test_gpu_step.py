@@ -287,3 +287,42 @@ def test_preference_losses_tiny(torch, kind, beta, param):
             assert_close(dA, odA, 5e-2, f"{kind} dA L{layer} {p}")
             assert_close(dB, odB, 5e-2, f"{kind} dB L{layer} {p}")
     m.close()
+
+
+def test_adapter_export_import_round_trip(torch, tmp_path):
+    """Saved adapters load back bit for bit into a fresh context and change
+    the model's output (they are not inert)."""
+    from layer_streamed_nf4_double_amd import adapter as ad
+    w = dict(TINY)
+    tokens = synth.sft_tokens(w)
+    say("[adapter export/import]")
+    m = gpu_model(w, "stream_host", b_zero=False)
+    _run_sft(torch, m, tokens)                       # one step: adapters move
+    ad.save_adapter(m, str(tmp_path / "adapter"))
+    want = _grads(m, w)
+    loss_m, _ = _run_sft(torch, m, tokens, lr=None)  # forward with trained adapters
+    m.close()
+    fresh = gpu_model(w, "stream_host", b_zero=True)
+    loss_base, _ = _run_sft(torch, fresh, tokens, lr=None)
+    ad.load_adapter(fresh, str(tmp_path / "adapter"))
+    got = _grads(fresh, w)
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            assert np.array_equal(_bits(got[layer][p][0]), _bits(want[layer][p][0]))
+            assert np.array_equal(_bits(got[layer][p][1]), _bits(want[layer][p][1]))
+    loss_loaded, _ = _run_sft(torch, fresh, tokens, lr=None)
+    fresh.close()
+    assert _bits(np.float32(loss_loaded)) == _bits(np.float32(loss_m))
+    assert loss_loaded != loss_base
+
+
+def test_auto_source_and_preflight(torch):
+    from layer_streamed_nf4_double_amd import adapter as ad
+    from layer_streamed_nf4_double_amd.trainer import LayerStreamedLoRA
+    w = dict(TINY)
+    m = LayerStreamedLoRA(w, "auto")
+    assert m.mode == "stream_host"          # a 2-layer tiny stack fits in RAM
+    m.close()
+    free, _ = torch.cuda.mem_get_info()
+    with pytest.raises(ad.NoFit):           # a workspace larger than the card
+        ad.plan_run(1, 1, free + (1 << 30), free, 1 << 40)
