@@ -68,8 +68,8 @@ def measured_traffic():
     rocprofv3 FETCH_SIZE + WRITE_SIZE runs, if the GEMM source is unchanged
     since they were taken (else None)."""
     import hashlib
-    prof = os.path.join(ROOT, "profiles", "nf4_gemm_llama8b_sft_traffic.md")
-    src = os.path.join(ROOT, "layer_streamed_nf4_double_amd", "csrc", "gemm.hip")
+    prof = os.path.join(ROOT, "profiles", "nf4f_gemm_llama8b_sft_traffic.md")
+    src = os.path.join(ROOT, "layer_streamed_nf4_double_amd", "csrc", "gemm_nf4f.hip")
     try:
         kv = dict(l.split(": ", 1) for l in open(prof).read().splitlines() if ": " in l and
                   l.split(": ", 1)[0] in ("traffic_bytes_per_launch", "gemm_source_sha256"))
@@ -261,7 +261,7 @@ def main():
     loads1, bytes1, _ = m.stats()
     peak = torch.cuda.max_memory_allocated()
     loss = float(m.loss[0].item())
-    n_gemm, flops, ms = L.lsn_profile_query(m.ctx, 0, 0, 2, 0)   # NF4 fwd GEMM, 256x128 tile
+    n_gemm, flops, ms = L.lsn_profile_query(m.ctx, 0, 0, 2, 3)   # NF4 fwd GEMM, 256x256 kernel
     n_cp, cp_bytes, cp_ms = L.lsn_profile_query(m.ctx, 1)
     L.lsn_set_profiling(m.ctx, 0)
     m.close()
@@ -277,7 +277,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(),
-                "kernel": "gemm_kernel<256,128,A_BF16_K,B_NF4_K> (fused NF4-dequant GEMM)",
+                "kernel": "nf4f_kernel (fused NF4-dequant MFMA GEMM, 256x256 tile)",
                 "launches": int(n_gemm), "avg_us": round(ms / max(n_gemm, 1) * 1e3, 2),
                 "flop_per_launch": flops / max(n_gemm, 1)}
     copy_gbps = cp_bytes / (cp_ms / 1e3) / 1e9 if cp_ms > 0 else 0.0

@@ -46,7 +46,8 @@ struct GemmParams {
   float levels[16] = {};  // NF4 code levels
 };
 
-enum { TILE_256x128 = 0, TILE_128x128 = 1, TILE_64x64 = 2 };
+// TILE_NF4F: the 256 x 256 forward NF4 kernel of gemm_nf4f.hip
+enum { TILE_256x128 = 0, TILE_128x128 = 1, TILE_64x64 = 2, TILE_NF4F = 3 };
 
 struct GemmPlan {
   int tile = TILE_64x64;
@@ -54,9 +55,21 @@ struct GemmPlan {
 };
 
 hipError_t gemm(const GemmParams& p, int opa, int opb, int batch, hipStream_t s);
+// the tile id gemm() launches for these operand forms
+int gemm_tile(const GemmParams& p, int opa, int opb, int batch);
 // the tile and split-k gemm() chooses for a problem
 GemmPlan gemm_plan(int M, int N, int K, int nseg, int batch);
-// fp32 scratch a split-k launch of this problem needs (0 when not split)
+// fp32 scratch a split-k launch of this problem needs (0 when not split),
+// for any operand forms
 int64_t gemm_partial_floats(int M, int N, int K, int nseg, int batch);
+
+// split-k reduction kernel (partial sums added in split order, then the epilogue)
+__global__ void gemm_reduce_k(const GemmParams p);
+
+// forward NF4 kernel (gemm_nf4f.hip): y = x W with x bf16 [M, K] row-major and
+// W^T NF4 [N, K]; used by gemm() whenever nf4f_eligible() holds
+bool nf4f_eligible(const GemmParams& p, int batch);
+int nf4f_split(int M, int N, int K);
+hipError_t nf4f_launch(GemmParams p, hipStream_t s);
 
 }  // namespace lsn

@@ -1,0 +1,415 @@
+// Forward NF4 projection y = x W for full 64-deep K slices, built around the
+// matrix cores of one CDNA4 compute unit.
+//
+//   C[m, n] (op)= alpha * sum_k x[m, k] * bf16(level[code(n, k)] * absmax(n, k))
+//                 (+ the low-rank extension of gemm.hip)
+//
+// The weight is the NF4 record's W^T [N, K] (codes two per byte, even element
+// in the low nibble, one fp32 absmax per 64 consecutive elements of a row),
+// so every 64-deep K slice of a row is exactly one absmax block.
+//
+// Work split.  A workgroup of four waves (one per SIMD) owns a 256 x 256
+// output tile; wave w owns all 256 rows and the 64 columns n0 + 64w .. +63,
+// i.e. 8 x 2 tiles of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per
+// lane).  Because the waves split only the N dimension, each weight element
+// of the tile is dequantized exactly once per workgroup, directly into the
+// B-fragment registers of the wave that uses it; the dequantized weight never
+// passes through LDS.  Only the activation slice [256 x 64] is shared through
+// LDS, so LDS read traffic per MFMA is half that of a 64 x 64 wave tile that
+// reads both operands from LDS.
+//
+// K order inside a slice.  An MFMA sums over 16 k; which 16 of the slice's 64
+// it takes is free as long as both operands agree.  Lane half h (lane / 32)
+// takes k = 32h + 8kk .. +7 in k-step kk, so each lane's weight codes for a
+// whole slice are 16 contiguous bytes (one load) and its activation chunks
+// are the 16-byte chunks 4h + kk of its rows.
+//
+// Memory pipeline (one iteration = one slice).  Activations, codes and
+// absmax go global -> LDS with direct loads (global_load_lds_dwordx4 /
+// _dword), three slices ahead, into three LDS stages; a slice's activation
+// chunks are XOR-swizzled by row so the fragment reads (ds_read_b128) are
+// free of bank conflicts.  The direct loads are issued from inline asm: the
+// compiler does not see them, so it cannot order every later LDS read behind
+// them; the kernel itself waits for its own loads (vmcnt) and then meets the
+// other waves at one barrier per slice, placed before the last k-step so the
+// next slice's first fragments load while the last MFMAs run.  Weight codes
+// are dequantized just in time, one k-step ahead of their MFMAs; the 16 code
+// levels are read from a 16-word LDS table (broadcast reads).
+//
+// Determinism: every output element is reduced by one lane in a fixed order
+// (split-k partial sums are added in split order by gemm_reduce_k).
+#include "common.h"
+#include "gemm.h"
+#include <algorithm>
+#include <type_traits>
+
+namespace lsn {
+
+namespace {
+
+constexpr int FM = 256, FN = 256, FK = 64;
+constexpr int NST = 3;                 // LDS stages
+constexpr int A_STAGE = FM * FK * 2;   // 32 KiB of activations (bf16)
+constexpr int C_STAGE = FN * FK / 2;   // 8 KiB of codes
+constexpr int GROUP = 8 + 2 + 1;       // direct loads per wave per slice
+
+// One direct global -> LDS load of 16 (or 4) bytes per lane: lane l writes
+// LDS bytes [lds + 16 l, +16) from gbase + voff (gbase and lds uniform).  M0
+// carries the LDS address; one wait state separates its write from the load.
+// No register is written.  The compiler uses M0 nowhere else in this kernel
+// (a test checks the generated code), so the asm overwrites it freely.
+LSN_DEV void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(gbase), "s"(lds)
+      : "memory");
+}
+LSN_DEV void dma4(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(voff), "s"(gbase), "s"(lds)
+      : "memory");
+}
+
+template <typename T>
+LSN_DEV uint32_t lds_addr(T* q) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)q;
+}
+
+// swizzle of the 16-byte chunk index of activation row r: rows r and r + 8
+// differ in the low bit so that 16 consecutive rows reading one logical chunk
+// hit 16 distinct 4-bank groups (and 8 consecutive rows 8 distinct ones)
+LSN_DEV int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Eight NF4 codes (one 32-bit word; element 2p in the low nibble of byte p)
+// to eight bf16 products level * absmax, each rounded once.  Byte p of t0 /
+// t1 is 4 * code of element 2p / 2p+1 (the byte offset of its level).
+template <typename Level>
+LSN_DEV bf16x8 dequant8(uint32_t q, float a, Level level) {
+  const uint32_t t0 = (q << 2) & 0x3C3C3C3Cu, t1 = (q >> 2) & 0x3C3C3C3Cu;
+  u32x4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    r[p] = pack_bf16x2(level((t0 >> (8 * p)) & 0xFFu) * a, level((t1 >> (8 * p)) & 0xFFu) * a);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+}  // namespace
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding)
+#define LSN_WAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+__global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
+  // the code levels first: their LDS address fits the 16-bit offset of a ds_read
+  __shared__ __attribute__((aligned(64))) float sLv[16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[NST][A_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sC[NST][C_STAGE];
+  __shared__ __attribute__((aligned(1024))) float sM[NST][FN];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+  const int lr = lane & 31, hh = lane >> 5;
+
+  // ---- tile coordinates (XCD-aware: consecutive ids land on one XCD) ----
+  const int mt = (p.M + FM - 1) / FM;
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int per = nblk / 8, rem = nblk % 8, x = b % 8;
+  const int id = x * per + min(x, rem) + b / 8;
+  const int m0 = (id % mt) * FM, n0 = (id / mt) * FN;
+
+  if (threadIdx.x < 16) sLv[threadIdx.x] = p.levels[threadIdx.x];
+  // level of code c: byte offset 4c into sLv (all lanes read among 16 words:
+  // broadcast reads, free of bank conflicts)
+  auto level = [&](uint32_t c4) {
+    return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(sLv) + c4);
+  };
+
+  // ---- direct-load byte offsets of this lane (slice 0) ----
+  // activations: load i of wave w fills stage rows (8w + i) * 8 .. +7;
+  // lane -> row + lane / 8, physical chunk lane % 8
+  uint32_t offA[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = (w * 8 + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    const int row = min(m0 + r, p.M - 1);
+    offA[i] = (uint32_t)(((int64_t)row * p.lda + c * 8) * 2);
+  }
+  // codes: load i of wave w fills weight rows (2w + i) * 32 .. +31 (32 B
+  // each); lane -> row + lane / 2, physical half lane % 2
+  uint32_t offC[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (w * 2 + i) * 32 + (lane >> 1);
+    const int h = (lane & 1) ^ ((r >> 3) & 1);
+    const int row = min(n0 + r, p.N - 1);
+    offC[i] = (uint32_t)((int64_t)row * (p.K / 2) + h * 16);
+  }
+  // absmax: wave w fills rows 64w .. +63, lane -> row 64w + lane
+  const uint32_t offM =
+      (uint32_t)((int64_t)min(n0 + w * 64 + lane, p.N - 1) * (p.K / FK) * 4);
+
+  const uint8_t* gA = reinterpret_cast<const uint8_t*>(p.A);
+  const uint8_t* gC = reinterpret_cast<const uint8_t*>(p.B);
+  const uint8_t* gM = reinterpret_cast<const uint8_t*>(p.absmax);
+
+  // split-k: blockIdx.y takes slices [it0, it1)
+  const int nkt = p.K / FK;
+  const int kper = (nkt + p.ksplit - 1) / p.ksplit;
+  const int it0 = min(nkt, (int)blockIdx.y * kper), it1 = min(nkt, it0 + kper);
+
+  // the GROUP direct loads of slice it into LDS stage st
+  auto issue = [&](int it, int st) {
+    const uint8_t* a = gA + it * (FK * 2);
+    const uint32_t la = lds_addr(sA[st]) + w * 8 * 1024;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(a, offA[i], la + i * 1024);
+    const uint8_t* c = gC + it * (FK / 2);
+    const uint32_t lc = lds_addr(sC[st]) + w * 2 * 1024;
+    dma16(c, offC[0], lc);
+    dma16(c, offC[1], lc + 1024);
+    dma4(gM + it * 4, offM, lds_addr(&sM[st][w * 64]));
+  };
+
+  // ---- per-lane LDS read offsets ----
+  // activation fragment of row tile i, k-step kk: row i*32 + lr, logical chunk
+  // 4*hh + kk -> physical (4*hh ^ swz(lr)) ^ kk (kk only flips the low bits)
+  const int sa0 = lr * 128 + (((4 * hh) ^ swz(lr)) * 16);
+  // codes of column tile j: row 64w + 32j + lr, logical half hh
+  const int sc0 = (w * 64 + lr) * 32 + ((hh ^ ((lr >> 3) & 1)) * 16);
+  const int sm0 = w * 64 + lr;
+
+  f32x16 acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  bf16x8 af[2][8];  // activation fragments, double buffered over k-steps
+  bf16x8 bq[2][2];  // weight fragments [kk & 1][j]
+  u32x4 cq[2], cqn[2];  // codes of this slice and of the next one (per column tile)
+  float ca[2], can[2];
+
+  auto read_codes = [&](u32x4 (&q)[2], float (&a)[2], int st) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      q[j] = *reinterpret_cast<const u32x4*>(sC[st] + sc0 + j * 1024);
+      a[j] = sM[st][sm0 + j * 32];
+    }
+  };
+
+  // One k-step as 16 MFMA slots (row tile s/2, column tile s%2).  Between
+  // them, in a fixed order (sched_barrier after every slot): the next
+  // k-step's eight activation fragments (slots 0-7), the nibble addresses
+  // and level lookups of its two weight tiles (slots 0-7), and the products
+  // and bf16 packing (slots 8-15, when the lookups have long returned).
+  // extra(s) adds per-slot work (the direct loads of the last k-step).
+  auto kstep = [&](auto kk_, const uint8_t* an, const u32x4 (&q)[2], const float (&a)[2],
+                   int kn, auto extra) {
+    constexpr int F = decltype(kk_)::value & 1;
+    uint32_t ad[2][8];
+    float lvv[2][8];
+    u32x4 r[2];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      acc[s >> 1][s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          af[F][s >> 1], bq[F][s & 1], acc[s >> 1][s & 1], 0, 0, 0);
+      if (s < 8) af[F ^ 1][s] = *reinterpret_cast<const bf16x8*>(an + s * 4096);
+      if (s < 8) {
+        const int jt = s >> 2, ph = s & 3;
+        if (ph == 0) {
+          const uint32_t w0 = q[jt][kn];
+          ad[jt][0] = (w0 << 2) & 0x3C3C3C3Cu;
+          ad[jt][1] = (w0 >> 2) & 0x3C3C3C3Cu;
+        } else if (ph == 1) {
+          ad[jt][2] = ad[jt][0] >> 8;
+          ad[jt][3] = ad[jt][1] >> 8;
+          ad[jt][4] = ad[jt][0] >> 16;
+          lvv[jt][0] = level(ad[jt][0] & 0xFFu);
+          lvv[jt][1] = level(ad[jt][1] & 0xFFu);
+        } else if (ph == 2) {
+          ad[jt][5] = ad[jt][1] >> 16;
+          ad[jt][6] = ad[jt][0] >> 24;
+          ad[jt][7] = ad[jt][1] >> 24;
+          lvv[jt][2] = level(ad[jt][2] & 0xFFu);
+          lvv[jt][3] = level(ad[jt][3] & 0xFFu);
+        } else {
+#pragma unroll
+          for (int e = 4; e < 8; ++e)
+            lvv[jt][e] = level(ad[jt][e] & 0xFFu);
+        }
+      } else {
+        const int jt = (s - 8) >> 2, pp = (s - 8) & 3;
+        r[jt][pp] = pack_bf16x2(lvv[jt][2 * pp] * a[jt], lvv[jt][2 * pp + 1] * a[jt]);
+        if (pp == 3) bq[F ^ 1][jt] = __builtin_bit_cast(bf16x8, r[jt]);
+      }
+      extra(s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto none = [](int) {};
+
+  if (it1 > it0) {
+    // prologue: slices it0 .. it0+2 (clamped) into stages 0 .. 2
+    issue(it0, 0);
+    issue(min(it0 + 1, it1 - 1), 1);
+    issue(min(it0 + 2, it1 - 1), 2);
+    LSN_WAIT_VM(2 * GROUP);
+    __syncthreads();
+    read_codes(cq, ca, 0);
+    {
+      const uint8_t* sa = sA[0] + sa0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) af[0][i] = *reinterpret_cast<const bf16x8*>(sa + i * 4096);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bq[0][j] = dequant8(cq[j][0], ca[j], level);
+    }
+    // Slice t (u = t - it0) sits in stage u % 3.  Each wave's codes and
+    // absmax are the rows it loaded itself, so after waiting for its own
+    // loads of slice t + 1 (k-step 2; only slice t + 2's may be in flight)
+    // it reads slice t + 1's codes without a barrier.  Before k-step 3 all
+    // of slice t's activations have been read by this wave (lgkmcnt(0)); the
+    // barrier then makes slice t + 1's activations visible and stage u % 3
+    // free, and k-step 3 refills it with slice t + 3.
+    int st = 0;
+    for (int t = it0; t < it1; ++t) {
+      const int st1 = st == NST - 1 ? 0 : st + 1;
+      kstep(std::integral_constant<int, 0>{}, sA[st] + (sa0 ^ 16), cq, ca, 1, none);
+      kstep(std::integral_constant<int, 1>{}, sA[st] + (sa0 ^ 32), cq, ca, 2, none);
+      LSN_WAIT_VM(GROUP);
+      kstep(std::integral_constant<int, 2>{}, sA[st] + (sa0 ^ 48), cq, ca, 3,
+            [&](int s) { if (s == 8) read_codes(cqn, can, st1); });
+      __syncthreads();  // (its fence waits lgkmcnt(0): this wave's reads of stage st are done)
+      const uint8_t* a_next = gA + min(t + 3, it1 - 1) * (FK * 2);
+      const uint8_t* c_next = gC + min(t + 3, it1 - 1) * (FK / 2);
+      const uint32_t la = lds_addr(sA[st]) + w * 8 * 1024;
+      const uint32_t lc = lds_addr(sC[st]) + w * 2 * 1024;
+      const uint32_t lm = lds_addr(&sM[st][w * 64]);
+      const uint8_t* m_next = gM + min(t + 3, it1 - 1) * 4;
+      kstep(std::integral_constant<int, 3>{}, sA[st1] + sa0, cqn, can, 0, [&](int s) {
+        if (s < 8) dma16(a_next, offA[s], la + s * 1024);
+        if (s == 8) dma16(c_next, offC[0], lc);
+        if (s == 9) dma16(c_next, offC[1], lc + 1024);
+        if (s == 10) dma4(m_next, offM, lm);
+      });
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        cq[j] = cqn[j];
+        ca[j] = can[j];
+      }
+      st = st1;
+    }
+    LSN_WAIT_VM(0);  // no direct load may still be writing LDS when the waves exit
+  }
+
+  // ---- low-rank extension: extra k columns read directly as fragments ----
+  const int lk = hh * 8;
+  if (p.kext > 0 && blockIdx.y == 0) {
+    for (int e0 = 0; e0 < p.kext; e0 += 16) {
+      bf16x8 af[8], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = min(m0 + i * 32 + lr, p.M - 1);
+        af[i] = *reinterpret_cast<const bf16x8*>(p.Aext + (int64_t)m * p.ldae + e0 + lk);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = min(n0 + w * 64 + j * 32 + lr, p.N - 1);
+        bfr[j] = *reinterpret_cast<const bf16x8*>(p.Bext + (int64_t)n * p.ldbe + e0 + lk);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: lane holds column lr, rows (e/4)*8 + (lane/32)*4 + e%4 ----
+  // one fully unrolled copy per output mode (MODE -1: raw split-k partial sum)
+  auto epilogue = [&](auto mode_) {
+    constexpr int MODE = decltype(mode_)::value;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + w * 64 + j * 32 + lr;
+        const bool nok = n < p.N;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + i * 32 + (e >> 2) * 8 + hh * 4 + (e & 3);
+          if (!nok || m >= p.M) continue;
+          const float a = acc[i][j][e];
+          if constexpr (MODE < 0) {
+            p.part[((int64_t)blockIdx.y * p.M + m) * p.N + n] = a;
+          } else {
+            const float v = p.alpha * a;
+            const int64_t o = (int64_t)m * p.ldc + n;
+            if constexpr (MODE == C_F32) reinterpret_cast<float*>(p.C)[o] = v;
+            if constexpr (MODE == C_F32_ACC) reinterpret_cast<float*>(p.C)[o] += v;
+            if constexpr (MODE == C_F32_RES)
+              reinterpret_cast<float*>(p.C)[o] = p.R[(int64_t)m * p.ldr + n] + v;
+            if constexpr (MODE == C_BF16) reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16_bits(v);
+          }
+        }
+      }
+  };
+  if (p.ksplit > 1) epilogue(std::integral_constant<int, -1>{});
+  else if (p.cmode == C_F32) epilogue(std::integral_constant<int, C_F32>{});
+  else if (p.cmode == C_F32_ACC) epilogue(std::integral_constant<int, C_F32_ACC>{});
+  else if (p.cmode == C_F32_RES) epilogue(std::integral_constant<int, C_F32_RES>{});
+  else epilogue(std::integral_constant<int, C_BF16>{});
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+static bool aligned(const void* q, uintptr_t a) { return ((uintptr_t)q & (a - 1)) == 0; }
+
+bool nf4f_eligible(const GemmParams& p, int batch) {
+  if (batch != 1 || p.nseg != 1 || p.zdiv != 1) return false;
+  if (p.M < FM || p.K % FK != 0 || p.rowlen != p.K) return false;
+  if (p.lda % 8 != 0 || !aligned(p.A, 16) || !aligned(p.B, 16) || !aligned(p.absmax, 4))
+    return false;
+  if (p.kext > 0 && (p.kext % 16 != 0 || p.ldae % 8 != 0 || p.ldbe % 8 != 0 ||
+                     !aligned(p.Aext, 16) || !aligned(p.Bext, 16)))
+    return false;
+  // 32-bit per-lane offsets
+  const int64_t lim = (int64_t)1 << 31;
+  return (int64_t)p.M * p.lda < lim && (int64_t)p.N * (p.K / 2) < lim;
+}
+
+// One workgroup per CU (512 registers per lane): the k range is split
+// so that at most 256 workgroups run, each with at least four slices.
+int nf4f_split(int M, int N, int K) {
+  const int64_t tiles = (int64_t)((M + FM - 1) / FM) * ((N + FN - 1) / FN);
+  if (tiles >= 128) return 1;
+  int sp = (int)std::min<int64_t>(8, 256 / tiles);
+  sp = std::min(sp, std::max(1, K / FK / 4));
+  return std::max(sp, 1);
+}
+
+hipError_t nf4f_launch(GemmParams p, hipStream_t s) {
+  p.ksplit = nf4f_split(p.M, p.N, p.K);
+  if (p.ksplit > 1 && (!p.part || p.part_floats < (int64_t)p.ksplit * p.M * p.N)) p.ksplit = 1;
+  const int tiles = ((p.M + FM - 1) / FM) * ((p.N + FN - 1) / FN);
+  if (p.ev0) (void)hipEventRecord(p.ev0, s);
+  hipLaunchKernelGGL(nf4f_kernel, dim3(tiles, p.ksplit, 1), dim3(256), 0, s, p);
+  if (p.ev1) (void)hipEventRecord(p.ev1, s);
+  if (p.ksplit > 1) {
+    const int64_t n = (int64_t)p.M * p.N;
+    hipLaunchKernelGGL(gemm_reduce_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lsn

@@ -206,7 +206,7 @@ static void prof_end(lsn_ctx* c, lsn_ctx::ProfRec& r, hipStream_t s) {
 static hipError_t cgemm(lsn_ctx* c, GemmParams p, int opa, int opb, int batch) {
   p.part = c->gpart;
   p.part_floats = c->gpart_floats;
-  lsn_ctx::ProfRec r{0, opa, opb, gemm_plan(p.M, p.N, p.K, p.nseg, batch).tile,
+  lsn_ctx::ProfRec r{0, opa, opb, gemm_tile(p, opa, opb, batch),
                      2.0 * p.M * p.N * (double)p.K * p.nseg * batch, nullptr, nullptr};
   // events bracket the GEMM kernel only (not a split-k reduction)
   const bool on = c->profiling && (opb == B_NF4_K || opb == B_NF4_R);

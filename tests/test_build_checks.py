@@ -1,0 +1,58 @@
+"""Checks on the generated gfx950 code of the forward NF4 kernel (CPU only).
+
+The kernel's direct global -> LDS loads are inline asm that set M0 without
+saving it; that is only correct while the compiler itself uses M0 nowhere in
+the kernel.  The kernel must also keep its accumulators in registers (no
+scratch memory)."""
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+SRC = os.path.join(os.path.dirname(__file__), "..", "layer_streamed_nf4_double_amd", "csrc",
+                   "gemm_nf4f.hip")
+
+
+@pytest.fixture(scope="module")
+def asm():
+    if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
+        pytest.skip("hipcc not available")
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.s")
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", SRC, "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        return open(out).read()
+
+
+def _kernel_body(asm, name):
+    start = asm.index(f"{name}:")
+    end = asm.index(".Lfunc_end", start)
+    return asm[start:end]
+
+
+def test_m0_only_in_direct_loads(asm):
+    body = _kernel_body(asm, "_ZN3lsn11nf4f_kernelENS_10GemmParamsE")
+    inside = False
+    for line in body.splitlines():
+        if "ASMSTART" in line:
+            inside = True
+            continue
+        if "ASMEND" in line:
+            inside = False
+            continue
+        code = line.split(";")[0]
+        if not inside:
+            assert not re.search(r"\bm0\b", code), f"compiler uses M0: {line.strip()}"
+    assert body.count("global_load_lds_dwordx4") >= 10
+
+
+def test_no_scratch(asm):
+    i = asm.index(".name:           _ZN3lsn11nf4f_kernelENS_10GemmParamsE")
+    meta = asm[asm.rindex("- .agpr_count", 0, i):i + 2000]
+    assert re.search(r"\.private_segment_fixed_size:\s+0\b", meta), "kernel uses scratch"

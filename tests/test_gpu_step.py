@@ -25,6 +25,13 @@ from tests.modelbuild import assert_close, gpu_model, oracle_model, rel
 pytestmark = pytest.mark.gpu
 TINY = synth.WORKLOADS["tiny"]
 LR = 0.1
+# Two sequences of 128 tokens (256 per step), GQA, every projection adapted:
+# all forward projections (K = 256 or 704, multiples of 64) run the 256 x 256
+# forward NF4 kernel, with C_F32 and residual (C_F32_RES) outputs.
+SMALL256 = dict(wid=5, n_layers=2, hidden=256, n_heads=4, n_kv_heads=2, head_dim=64,
+                ffn=704, vocab=1024, rms_eps=1e-5, rope_theta=1e4, lora_rank=8,
+                lora_alpha=16.0, tied=False, n_seq=2, seq_len=128)
+ALL7 = ("q", "k", "v", "o", "gate", "up", "down")
 
 
 def say(*a):
@@ -326,3 +333,36 @@ def test_auto_source_and_preflight(torch):
     free, _ = torch.cuda.mem_get_info()
     with pytest.raises(ad.NoFit):           # a workspace larger than the card
         ad.plan_run(1, 1, free + (1 << 30), free, 1 << 40)
+
+
+def test_sft_256_tokens_all_projections_vs_oracle(torch):
+    """One SFT step at 256 tokens with B != 0 on all seven projections (the
+    forward NF4 GEMMs run the 256 x 256 kernel), then streamed == resident
+    bitwise."""
+    w = SMALL256
+    tokens = synth.sft_tokens(w)
+    say("[sft-256] oracle")
+    cfg, layers, lora, head = oracle_model(w, b_zero=False, lora_targets=ALL7)
+    o = om.sft_step(cfg, layers, lora, head, tokens, LR)
+    say("[sft-256] gpu stream_host")
+    m = gpu_model(w, "stream_host", b_zero=False, lora_targets=ALL7)
+    loss, logp = _run_sft(torch, m, tokens)
+    g = _grads(m, w, ALL7)
+    assert abs(loss - o["loss"]) <= 2e-2 * abs(o["loss"])
+    assert_close(logp, o["logp"], 2e-2, "logp")
+    for layer in range(w["n_layers"]):
+        for p in ALL7:
+            _, _, dA, dB = g[layer][p]
+            oA, oB = o["grads"][layer][p]
+            assert_close(dA, oA, 5e-2, f"dA L{layer} {p}")
+            assert_close(dB, oB, 5e-2, f"dB L{layer} {p}")
+    say("[sft-256] gpu resident")
+    r = gpu_model(w, "resident", b_zero=False, lora_targets=ALL7)
+    loss_r, logp_r = _run_sft(torch, r, tokens)
+    assert np.array_equal(np.float32(loss_r).view(np.uint32), np.float32(loss).view(np.uint32))
+    assert np.array_equal(logp_r.view(np.uint32), logp.view(np.uint32))
+    gr = _grads(r, w, ALL7)
+    for layer in range(w["n_layers"]):
+        for p in ALL7:
+            for u, v in zip(g[layer][p], gr[layer][p]):
+                assert np.array_equal(np.asarray(u).view(np.uint32), np.asarray(v).view(np.uint32))
