@@ -33,8 +33,8 @@
 // them; the kernel itself waits for its own loads (vmcnt) and then meets the
 // other waves at one barrier per slice, placed before the last k-step so the
 // next slice's first fragments load while the last MFMAs run.  Weight codes
-// are dequantized just in time, one k-step ahead of their MFMAs; the 16 code
-// levels are read from a 16-word LDS table (broadcast reads).
+// are dequantized just in time, one k-step ahead of their MFMAs: each code
+// byte indexes a 256-entry LDS table holding the levels of its two nibbles.
 //
 // Determinism: every output element is reduced by one lane in a fixed order
 // (split-k partial sums are added in split order by gemm_reduce_k).
@@ -87,16 +87,21 @@ LSN_DEV uint32_t lds_addr(T* q) {
 // hit 16 distinct 4-bank groups (and 8 consecutive rows 8 distinct ones)
 LSN_DEV int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// byte offset 8 * (byte p of code word q) into the level-pair table
+LSN_DEV uint32_t pair_off(uint32_t q, int p) {
+  return p == 0 ? (q << 3) & 0x7F8u : (q >> (8 * p - 3)) & 0x7F8u;
+}
+
 // Eight NF4 codes (one 32-bit word; element 2p in the low nibble of byte p)
-// to eight bf16 products level * absmax, each rounded once.  Byte p of t0 /
-// t1 is 4 * code of element 2p / 2p+1 (the byte offset of its level).
-template <typename Level>
-LSN_DEV bf16x8 dequant8(uint32_t q, float a, Level level) {
-  const uint32_t t0 = (q << 2) & 0x3C3C3C3Cu, t1 = (q >> 2) & 0x3C3C3C3Cu;
+// to eight bf16 products level * absmax, each rounded once.
+template <typename Pair>
+LSN_DEV bf16x8 dequant8(uint32_t q, float a, Pair pair) {
   u32x4 r;
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
-    r[p] = pack_bf16x2(level((t0 >> (8 * p)) & 0xFFu) * a, level((t1 >> (8 * p)) & 0xFFu) * a);
+  for (int p = 0; p < 4; ++p) {
+    const float2 l = pair(pair_off(q, p));
+    r[p] = pack_bf16x2(l.x * a, l.y * a);
+  }
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -107,8 +112,8 @@ LSN_DEV bf16x8 dequant8(uint32_t q, float a, Level level) {
   __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
-  // the code levels first: their LDS address fits the 16-bit offset of a ds_read
-  __shared__ __attribute__((aligned(64))) float sLv[16];
+  // the level-pair table first: its LDS address fits the 16-bit ds_read offset
+  __shared__ __attribute__((aligned(64))) float2 sPair[256];
   __shared__ __attribute__((aligned(1024))) uint8_t sA[NST][A_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sC[NST][C_STAGE];
   __shared__ __attribute__((aligned(1024))) float sM[NST][FN];
@@ -124,11 +129,11 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   const int id = x * per + min(x, rem) + b / 8;
   const int m0 = (id % mt) * FM, n0 = (id / mt) * FN;
 
-  if (threadIdx.x < 16) sLv[threadIdx.x] = p.levels[threadIdx.x];
-  // level of code c: byte offset 4c into sLv (all lanes read among 16 words:
-  // broadcast reads, free of bank conflicts)
-  auto level = [&](uint32_t c4) {
-    return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(sLv) + c4);
+  // entry b: the levels of code byte b (low nibble: even element, high
+  // nibble: odd element); one 8-byte read dequantizes two elements
+  sPair[threadIdx.x] = make_float2(p.levels[threadIdx.x & 15], p.levels[threadIdx.x >> 4]);
+  auto pair = [&](uint32_t b8) {  // b8 = 8 * code byte
+    return *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(sPair) + b8);
   };
 
   // ---- direct-load byte offsets of this lane (slice 0) ----
@@ -209,14 +214,13 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
 
   // One k-step as 16 MFMA slots (row tile s/2, column tile s%2).  Between
   // them, in a fixed order (sched_barrier after every slot): the next
-  // k-step's eight activation fragments (slots 0-7), the nibble addresses
-  // and level lookups of its two weight tiles (slots 0-7), and the products
-  // and bf16 packing (slots 8-15, when the lookups have long returned).
+  // k-step's eight activation fragments and the eight level-pair reads of
+  // its two weight tiles (slots 0-7), then the products and bf16 packing
+  // (slots 8-15, when the reads have long returned).
   // extra(s) adds per-slot work (the direct loads of the last k-step).
   auto kstep = [&](auto kk_, const uint8_t* an, const u32x4 (&q)[2], const float (&a)[2],
                    int kn, auto extra) {
     constexpr int F = decltype(kk_)::value & 1;
-    uint32_t ad[2][8];
     float lvv[2][8];
     u32x4 r[2];
 #pragma unroll
@@ -224,29 +228,11 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
       acc[s >> 1][s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           af[F][s >> 1], bq[F][s & 1], acc[s >> 1][s & 1], 0, 0, 0);
       if (s < 8) af[F ^ 1][s] = *reinterpret_cast<const bf16x8*>(an + s * 4096);
-      if (s < 8) {
+      if (s < 8) {  // level pair ph of tile jt (byte ph of the code word)
         const int jt = s >> 2, ph = s & 3;
-        if (ph == 0) {
-          const uint32_t w0 = q[jt][kn];
-          ad[jt][0] = (w0 << 2) & 0x3C3C3C3Cu;
-          ad[jt][1] = (w0 >> 2) & 0x3C3C3C3Cu;
-        } else if (ph == 1) {
-          ad[jt][2] = ad[jt][0] >> 8;
-          ad[jt][3] = ad[jt][1] >> 8;
-          ad[jt][4] = ad[jt][0] >> 16;
-          lvv[jt][0] = level(ad[jt][0] & 0xFFu);
-          lvv[jt][1] = level(ad[jt][1] & 0xFFu);
-        } else if (ph == 2) {
-          ad[jt][5] = ad[jt][1] >> 16;
-          ad[jt][6] = ad[jt][0] >> 24;
-          ad[jt][7] = ad[jt][1] >> 24;
-          lvv[jt][2] = level(ad[jt][2] & 0xFFu);
-          lvv[jt][3] = level(ad[jt][3] & 0xFFu);
-        } else {
-#pragma unroll
-          for (int e = 4; e < 8; ++e)
-            lvv[jt][e] = level(ad[jt][e] & 0xFFu);
-        }
+        const float2 l = pair(pair_off(q[jt][kn], ph));
+        lvv[jt][2 * ph] = l.x;
+        lvv[jt][2 * ph + 1] = l.y;
       } else {
         const int jt = (s - 8) >> 2, pp = (s - 8) & 3;
         r[jt][pp] = pack_bf16x2(lvv[jt][2 * pp] * a[jt], lvv[jt][2 * pp + 1] * a[jt]);
@@ -271,7 +257,7 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) af[0][i] = *reinterpret_cast<const bf16x8*>(sa + i * 4096);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bq[0][j] = dequant8(cq[j][0], ca[j], level);
+      for (int j = 0; j < 2; ++j) bq[0][j] = dequant8(cq[j][0], ca[j], pair);
     }
     // Slice t (u = t - it0) sits in stage u % 3.  Each wave's codes and
     // absmax are the rows it loaded itself, so after waiting for its own
