@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--mode", default="stream_host", choices=["stream_host", "resident"])
     ap.add_argument("--dpo-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the projection, dequant and resident measurements")
     ap.add_argument("--link-mb", type=int, default=256)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run device-to-device copies of this size (counter calibration)")
@@ -144,6 +146,96 @@ def link_bandwidth(torch, mb, reps=20):
             times.append(e0.elapsed_time(e1) / 1e3)
     times.sort()
     return n / times[0] / 1e9, n / times[len(times) // 2] / 1e9
+
+
+# ---------------------------------------------------------------------------
+# the single projection (512 x 4096 -> 14336, rank-16 adapter) and the
+# standalone dequantization, timed with events on the stream they run on
+def projection_kernels(torch, reps=20):
+    import numpy as np
+
+    import synth
+    from layer_streamed_nf4_double_amd import _lib as L
+    p = synth.PROJECTION
+    M, K, N, r, sc = p["M"], p["K"], p["N"], p["r"], p["scale"]
+    wid = p["wid"]
+    W = synth.normal((N, K), wid, 0, 0)
+    c, a = L.lsn_nf4_quantize(W)
+    cd, ad = torch.from_numpy(c).cuda(), torch.from_numpy(a).cuda()
+    X = torch.from_numpy(synth.bf16_bits(synth.normal((M, K), wid, 0, synth.TID_X, std=1.0))).cuda()
+    dY = torch.from_numpy(synth.bf16_bits(synth.normal((M, N), wid, 0, synth.TID_DY, std=1.0))).cuda()
+    A = torch.from_numpy(synth.normal((K, r), wid, 0, 10)).cuda()
+    B = torch.from_numpy(synth.normal((r, N), wid, 0, 11)).cuda()
+    Y = torch.empty(M, N, device="cuda")
+    dX = torch.empty(M, K, device="cuda")
+    dA = torch.empty(K, r, device="cuda")
+    dB = torch.empty(r, N, device="cuda")
+    Wb = torch.empty(N * K, dtype=torch.int16, device="cuda")
+    sb = L.lsn_nf4_linear_scratch_bytes(M, K, N, r)
+    scr = torch.empty(sb, dtype=torch.uint8, device="cuda")
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3  # us
+
+    fwd = timed(lambda: L.lsn_nf4_linear_fwd(cd, ad, M, K, N, X, A, B, r, sc, Y, scr, sb))
+    bwd = timed(lambda: L.lsn_nf4_linear_bwd(cd, ad, M, K, N, X, A, B, r, sc, dY, dX, dA, dB,
+                                             scr, sb))
+    deq = timed(lambda: L.lsn_nf4_dequant(cd, ad, N * K, Wb, 1))
+    gemm = 2.0 * M * N * K
+    lora_f = 2.0 * M * r * (K + N)          # x A and (s t) B
+    lora_b = 2.0 * M * r * (N + 2 * K + N)  # dY B^T, u A^T, x^T u, t^T dY
+    deq_bytes = N * K // 2 + N * K // 16 + 2 * N * K
+
+    def mf(flops, us):
+        t = flops / (us * 1e-6) / 1e12
+        return {"us": round(us, 2), "tflops": round(t, 1), "frac": round(t / MFMA_BF16_PEAK_TFLOPS, 4)}
+    gbps = deq_bytes / (deq * 1e-6) / 1e9
+    return {"shape": f"X [{M},{K}] bf16 . NF4 W [{K},{N}] + rank-{r} adapter",
+            "fwd": mf(gemm + lora_f, fwd), "bwd_dx_da_db": mf(gemm + lora_b, bwd),
+            "note": "end to end through lsn_nf4_linear_fwd / _bwd: adapter products, "
+                    "split-k reduction and NF4 GEMM; flops = 2MNK + adapter products",
+            "dequant_bf16": {"us": round(deq, 2), "bytes": deq_bytes, "GBps": round(gbps, 1),
+                             "frac": round(gbps / HBM_PEAK_GBPS, 4), "bound": "hbm"}}
+
+
+def step_flops(w, T, n_seq):
+    """Algorithmic flops of one SFT step: each projection 3 times (forward,
+    recompute, dX), the LM head twice (log-probs, dX), attention scores and
+    values in the forward, the recompute and twice in the backward."""
+    H, F, L = w["hidden"], w["ffn"], w["n_layers"]
+    d, nq, nkv = w["head_dim"], w["n_heads"], w["n_kv_heads"]
+    params = H * (nq * d) + 2 * H * (nkv * d) + (nq * d) * H + 3 * H * F
+    S = T // n_seq
+    attn = 2 * 2 * n_seq * S * S * d * nq
+    return 3 * 2 * T * params * L + 2 * 2 * T * w["vocab"] * H + 4 * attn * L
+
+
+def environment(torch, w, rec_bytes):
+    import platform
+    env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+           "gpu": torch.cuda.get_device_name(0), "seed": 0,
+           "pinned_store_bytes": int(rec_bytes) * w["n_layers"], "python": platform.python_version()}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            env["host_cpu"] = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+        with open("/proc/meminfo") as f:
+            env["host_ram_bytes"] = int(next(l.split()[1] for l in f if l.startswith("MemTotal"))) * 1024
+    except (OSError, StopIteration):
+        pass
+    return env
 
 
 # ---------------------------------------------------------------------------
@@ -326,6 +418,33 @@ def main():
                "peak_vram_ratio_vs_sft": round(dpeak / peak, 3)}
         log(f"[bench] DPO {ddt * 1e3:.1f} ms/step, {2 * S / ddt:.1f} tok/s, loss {out[0]:.4f}")
 
+    # ---- the same step with the base resident on the device (peak VRAM side by side) ----
+    resident = projection = None
+    if not args.no_extras:
+        if args.mode == "stream_host":
+            torch.cuda.reset_peak_memory_stats()
+            mr = build_model(w, "resident", S, S, layers, head)
+            for _ in range(args.warmup):
+                mr.sft_step(tok, tgt, 1, S, 1e-4)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                mr.sft_step(tok, tgt, 1, S, 1e-4)
+            torch.cuda.synchronize()
+            rdt = (time.perf_counter() - t0) / args.steps
+            resident = {"tokens_per_s": round(S / rdt, 2), "ms_per_step": round(rdt * 1e3, 2),
+                        "peak_vram_bytes": int(torch.cuda.max_memory_allocated()),
+                        "compute_frac": round(step_flops(w, S, 1) / rdt / 1e12
+                                              / MFMA_BF16_PEAK_TFLOPS, 4)}
+            mr.close()
+            del mr
+            torch.cuda.empty_cache()
+            log(f"[bench] resident SFT {rdt * 1e3:.1f} ms/step, peak "
+                f"{resident['peak_vram_bytes'] / 1e9:.2f} GB")
+        projection = projection_kernels(torch)
+        log(f"[bench] projection fwd {projection['fwd']['us']} us, bwd "
+            f"{projection['bwd_dx_da_db']['us']} us, dequant {projection['dequant_bf16']['us']} us")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle sample)")
@@ -344,7 +463,12 @@ def main():
                        else "NF4 block-64, device resident",
                        "parallelism": "none (1 GPU)"},
             "peak_vram_bytes": int(peak), "loss": loss,
-            "roofline": roofline, "link": link, "dpo": dpo, "cpu_baseline": cpu}
+            "roofline": roofline, "link": link,
+            "compute_utilization": {"flops_per_step": step_flops(w, S, 1),
+                                    "frac": round(step_flops(w, S, 1) / dt / 1e12
+                                                  / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "dpo": dpo, "resident": resident, "projection": projection,
+            "env": environment(torch, w, rec_bytes), "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 
 

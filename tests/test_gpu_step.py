@@ -117,6 +117,18 @@ def _bits(x):
     return np.asarray(x, np.float32).view(np.uint32)
 
 
+def _dpo_bars(od, beta):
+    """(loss bar, z bar).  z is a small difference of large log-prob sums:
+    2e-2 relative with a floor of beta.  The loss -log sigmoid(z) is a
+    function of z alone, so besides 2e-2 relative it may move by what z's bar
+    allows through d loss / dz = -sigmoid(-z) (for large z the loss is
+    exponentially small and its relative error equals z's absolute error)."""
+    z = float(od["z"])
+    zbar = 2e-2 * max(abs(z), beta)
+    sig = 1.0 / (1.0 + math.exp(z))
+    return max(2e-2 * abs(float(od["loss"])), sig * zbar), zbar
+
+
 def _two_step_record(torch, m, w, tokens):
     rec = []
     for _ in range(2):
@@ -188,10 +200,11 @@ def test_dpo_tiny(torch):
     out = m.dpo_step(tok, tgt, S, P, beta, LR)
     m.sync()
     o = out.cpu().numpy()
-    assert abs(o[0] - od["loss"]) <= 2e-2 * abs(od["loss"])
     # z = beta * (difference of ~2.6e3-nat log-prob sums) cancels; its bar is
     # 2e-2 relative with a floor of beta (one nat of log-prob difference)
-    assert abs(o[1] - od["z"]) <= 2e-2 * max(abs(od["z"]), beta)
+    lbar, zbar = _dpo_bars(od, beta)
+    assert abs(o[0] - od["loss"]) <= lbar
+    assert abs(o[1] - od["z"]) <= zbar
     assert_close(m.logp[:2 * S].cpu().numpy(), od["logp_policy"], 2e-2, "policy logp")
     assert_close(m.logp_ref[:2 * S].cpu().numpy(), od["logp_ref"], 2e-2, "reference logp")
     g = _grads(m, w)
@@ -366,3 +379,80 @@ def test_sft_256_tokens_all_projections_vs_oracle(torch):
         for p in ALL7:
             for u, v in zip(g[layer][p], gr[layer][p]):
                 assert np.array_equal(np.asarray(u).view(np.uint32), np.asarray(v).view(np.uint32))
+
+
+# The 8B layer shape at the bench's 512 tokens (hidden 4096, 32 q / 8 kv heads
+# of 128, FFN 14336, the same seeded layers as the 8B workload), two layers and
+# a 1024-entry vocabulary so that the float64 oracle stays within seconds.
+LLAMA8B_2L = dict(synth.WORKLOADS["llama3.1-8b-shaped"], n_layers=2, vocab=1024)
+
+
+@pytest.fixture(scope="module")
+def llama2l_oracle():
+    return oracle_model(LLAMA8B_2L, b_zero=False)
+
+
+def test_sft_llama8b_layer_shape_vs_oracle(torch, llama2l_oracle):
+    """One streamed SFT step at the full 8B layer shape (the kernels and launch
+    configuration the bench times) against the oracle; then streamed ==
+    resident bitwise at this shape."""
+    w = LLAMA8B_2L
+    tokens = synth.sft_tokens(w)
+    say("[sft-8b-shape] oracle")
+    cfg, layers, lora, head = llama2l_oracle
+    o = om.sft_step(cfg, layers, lora, head, tokens, LR)
+    say("[sft-8b-shape] gpu stream_host")
+    m = gpu_model(w, "stream_host", b_zero=False)
+    loss, logp = _run_sft(torch, m, tokens)
+    g = _grads(m, w)
+    assert abs(loss - o["loss"]) <= 2e-2 * abs(o["loss"])
+    assert_close(logp, o["logp"], 2e-2, "logp")
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            _, _, dA, dB = g[layer][p]
+            oA, oB = o["grads"][layer][p]
+            assert_close(dA, oA, 5e-2, f"dA L{layer} {p}")
+            assert_close(dB, oB, 5e-2, f"dB L{layer} {p}")
+    m.close()
+    say("[sft-8b-shape] gpu resident (bitwise)")
+    r = gpu_model(w, "resident", b_zero=False)
+    loss_r, logp_r = _run_sft(torch, r, tokens)
+    gr = _grads(r, w)
+    r.close()
+    assert np.array_equal(_bits(np.float32(loss_r)), _bits(np.float32(loss)))
+    assert np.array_equal(_bits(logp_r), _bits(logp))
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            for u, v in zip(g[layer][p], gr[layer][p]):
+                assert np.array_equal(_bits(np.asarray(u)), _bits(np.asarray(v)))
+
+
+def test_dpo_llama8b_layer_shape_vs_oracle(torch, llama2l_oracle):
+    """One streamed DPO step (fused reference pass) on one 2 x 512-token pair
+    at the full 8B layer shape against the oracle."""
+    w = LLAMA8B_2L
+    S, beta = w["seq_len"], synth.DPO_PAIR["beta"]
+    P = synth.dpo_prompt_len(w)
+    ch, rj = synth.dpo_pair(w)
+    tok, tgt = _dev_tokens(torch, np.stack([ch, rj]))
+    say("[dpo-8b-shape] oracle")
+    cfg, layers, lora, head = llama2l_oracle
+    od = om.dpo_step(cfg, layers, lora, head, ch, rj, P, beta, LR)
+    say("[dpo-8b-shape] gpu stream_host")
+    m = gpu_model(w, "stream_host", b_zero=False, max_tokens=2 * S)
+    out = m.dpo_step(tok, tgt, S, P, beta, LR)
+    m.sync()
+    o = out.cpu().numpy()
+    lbar, zbar = _dpo_bars(od, beta)
+    assert abs(o[0] - od["loss"]) <= lbar
+    assert abs(o[1] - od["z"]) <= zbar
+    assert_close(m.logp[:2 * S].cpu().numpy(), od["logp_policy"], 2e-2, "policy logp")
+    assert_close(m.logp_ref[:2 * S].cpu().numpy(), od["logp_ref"], 2e-2, "reference logp")
+    g = _grads(m, w)
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            _, _, dA, dB = g[layer][p]
+            odA, odB = od["grads"][layer][p]
+            assert_close(dA, odA, 5e-2, f"DPO dA L{layer} {p}")
+            assert_close(dB, odB, 5e-2, f"DPO dB L{layer} {p}")
+    m.close()
