@@ -1,7 +1,7 @@
 // Forward NF4 projection y = x W for full 64-deep K slices, built around the
 // matrix cores of one CDNA4 compute unit.
 //
-//   C[m, n] (op)= alpha * sum_k x[m, k] * bf16(level[code(n, k)] * absmax(n, k))
+//   C[m, n] (op)= sum_k x[m, k] * bf16(level[code(n, k)] * absmax(n, k))
 //                 (+ the low-rank extension of gemm.hip)
 //
 // The weight is the NF4 record's W^T [N, K] (codes two per byte, even element
@@ -111,6 +111,10 @@ LSN_DEV bf16x8 dequant8(uint32_t q, float a, Pair pair) {
 #define LSN_WAIT_VM(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
+// MODE: the output form (C_F32, C_F32_ACC, C_F32_RES, C_BF16), or -1 for the
+// raw split-k partial sums; one instantiation per form keeps the epilogue a
+// single straight-line path per tile kind.
+template <int MODE>
 __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   // the level-pair table first: its LDS address fits the 16-bit ds_read offset
   __shared__ __attribute__((aligned(64))) float2 sPair[256];
@@ -321,39 +325,77 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   }
 
   // ---- epilogue: lane holds column lr, rows (e/4)*8 + (lane/32)*4 + e%4 ----
-  // one fully unrolled copy per output mode (MODE -1: raw split-k partial sum)
-  auto epilogue = [&](auto mode_) {
-    constexpr int MODE = decltype(mode_)::value;
+  // Fully unrolled for the kernel's output mode (MODE -1: raw split-k
+  // partial sum).  A tile inside the matrix stores without per-element
+  // tests: a uniform row pointer plus a 32-bit lane offset.  The output and
+  // residual rows are restrict-qualified so that the loads need not wait for
+  // earlier stores; that holds even in place (C == R), since each lane's
+  // only same-address pair is one element's own load and store.
+  auto epilogue = [&](auto full_) {
+    constexpr bool FULL = decltype(full_)::value;
+    constexpr bool LOADS = MODE == C_F32_ACC || MODE == C_F32_RES;
+    float* const out = MODE < 0 ? p.part + (int64_t)blockIdx.y * p.M * p.N
+                                : reinterpret_cast<float*>(p.C);
+    const int64_t ld = MODE < 0 ? (int64_t)p.N : p.ldc;
+    const float* const src = MODE == C_F32_RES ? p.R : out;
+    const int64_t lds = MODE == C_F32_RES ? p.ldr : ld;
+    if constexpr (FULL) {
+      // byte offsets of this lane within a row pointer (uniform base +
+      // 32-bit offset: the scalar-base address form)
+      constexpr int ESZ = MODE == C_BF16 ? 2 : 4;
+      const uint32_t lo = (uint32_t)((hh * 4 * ld + w * 64 + lr) * ESZ);
+      const uint32_t ls = (uint32_t)((hh * 4 * lds + w * 64 + lr) * 4);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + w * 64 + j * 32 + lr;
-        const bool nok = n < p.N;
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int m = m0 + i * 32 + (e >> 2) * 8 + hh * 4 + (e & 3);
-          if (!nok || m >= p.M) continue;
-          const float a = acc[i][j][e];
-          if constexpr (MODE < 0) {
-            p.part[((int64_t)blockIdx.y * p.M + m) * p.N + n] = a;
-          } else {
-            const float v = p.alpha * a;
-            const int64_t o = (int64_t)m * p.ldc + n;
-            if constexpr (MODE == C_F32) reinterpret_cast<float*>(p.C)[o] = v;
-            if constexpr (MODE == C_F32_ACC) reinterpret_cast<float*>(p.C)[o] += v;
-            if constexpr (MODE == C_F32_RES)
-              reinterpret_cast<float*>(p.C)[o] = p.R[(int64_t)m * p.ldr + n] + v;
-            if constexpr (MODE == C_BF16) reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16_bits(v);
+          const int64_t r = m0 + i * 32 + (e >> 2) * 8 + (e & 3);
+          char* __restrict__ row =
+              MODE == C_BF16 ? reinterpret_cast<char*>(reinterpret_cast<uint16_t*>(p.C) + r * ld + n0)
+                             : reinterpret_cast<char*>(out + r * ld + n0);
+          const char* __restrict__ srow = reinterpret_cast<const char*>(src + r * lds + n0);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float a = acc[i][j][e];
+            if constexpr (MODE < 0) {
+              *reinterpret_cast<float*>(row + lo + j * 32 * ESZ) = a;
+            } else if constexpr (MODE == C_BF16) {
+              *reinterpret_cast<uint16_t*>(row + lo + j * 32 * ESZ) = f32_to_bf16_bits(a);
+            } else if constexpr (LOADS) {
+              *reinterpret_cast<float*>(row + lo + j * 128) =
+                  *reinterpret_cast<const float*>(srow + ls + j * 128) + a;
+            } else {
+              *reinterpret_cast<float*>(row + lo + j * 128) = a;
+            }
           }
         }
-      }
+    } else {
+      const int64_t lane = (int64_t)(m0 + hh * 4) * ld + (n0 + w * 64 + lr);
+      const int64_t rlane = (int64_t)(m0 + hh * 4) * lds + (n0 + w * 64 + lr);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = i * 32 + (e >> 2) * 8 + (e & 3);  // row within the tile, less hh*4
+          if (m0 + r + hh * 4 >= p.M) continue;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            if (n0 + w * 64 + j * 32 + lr >= p.N) continue;
+            const float a = acc[i][j][e];
+            const int64_t o = lane + (int64_t)r * ld + j * 32;
+            if constexpr (MODE < 0) {
+              out[o] = a;
+            } else if constexpr (MODE == C_BF16) {
+              reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16_bits(a);
+            } else {
+              out[o] = LOADS ? src[rlane + (int64_t)r * lds + j * 32] + a : a;
+            }
+          }
+        }
+    }
   };
-  if (p.ksplit > 1) epilogue(std::integral_constant<int, -1>{});
-  else if (p.cmode == C_F32) epilogue(std::integral_constant<int, C_F32>{});
-  else if (p.cmode == C_F32_ACC) epilogue(std::integral_constant<int, C_F32_ACC>{});
-  else if (p.cmode == C_F32_RES) epilogue(std::integral_constant<int, C_F32_RES>{});
-  else epilogue(std::integral_constant<int, C_BF16>{});
+  if (m0 + FM <= p.M && n0 + FN <= p.N) epilogue(std::true_type{});
+  else epilogue(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -362,7 +404,7 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
 static bool aligned(const void* q, uintptr_t a) { return ((uintptr_t)q & (a - 1)) == 0; }
 
 bool nf4f_eligible(const GemmParams& p, int batch) {
-  if (batch != 1 || p.nseg != 1 || p.zdiv != 1) return false;
+  if (batch != 1 || p.nseg != 1 || p.zdiv != 1 || p.alpha != 1.f) return false;
   if (p.M < FM || p.K % FK != 0 || p.rowlen != p.K) return false;
   if (p.lda % 8 != 0 || !aligned(p.A, 16) || !aligned(p.B, 16) || !aligned(p.absmax, 4))
     return false;
@@ -389,7 +431,12 @@ hipError_t nf4f_launch(GemmParams p, hipStream_t s) {
   if (p.ksplit > 1 && (!p.part || p.part_floats < (int64_t)p.ksplit * p.M * p.N)) p.ksplit = 1;
   const int tiles = ((p.M + FM - 1) / FM) * ((p.N + FN - 1) / FN);
   if (p.ev0) (void)hipEventRecord(p.ev0, s);
-  hipLaunchKernelGGL(nf4f_kernel, dim3(tiles, p.ksplit, 1), dim3(256), 0, s, p);
+  const dim3 grid(tiles, p.ksplit, 1);
+  if (p.ksplit > 1) hipLaunchKernelGGL(nf4f_kernel<-1>, grid, dim3(256), 0, s, p);
+  else if (p.cmode == C_F32) hipLaunchKernelGGL(nf4f_kernel<C_F32>, grid, dim3(256), 0, s, p);
+  else if (p.cmode == C_F32_ACC) hipLaunchKernelGGL(nf4f_kernel<C_F32_ACC>, grid, dim3(256), 0, s, p);
+  else if (p.cmode == C_F32_RES) hipLaunchKernelGGL(nf4f_kernel<C_F32_RES>, grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(nf4f_kernel<C_BF16>, grid, dim3(256), 0, s, p);
   if (p.ev1) (void)hipEventRecord(p.ev1, s);
   if (p.ksplit > 1) {
     const int64_t n = (int64_t)p.M * p.N;

@@ -30,29 +30,37 @@ def asm():
         return open(out).read()
 
 
-def _kernel_body(asm, name):
-    start = asm.index(f"{name}:")
-    end = asm.index(".Lfunc_end", start)
-    return asm[start:end]
+def _kernels(asm):
+    """(name, body, metadata) of every nf4f_kernel instantiation (one per
+    output form)."""
+    names = re.findall(r"^(_ZN3lsn11nf4f_kernelI\w+E):", asm, re.M)
+    assert len(names) >= 2, "nf4f_kernel instantiations not found"
+    out = []
+    for name in names:
+        start = asm.index(f"{name}:")
+        body = asm[start:asm.index(".Lfunc_end", start)]
+        i = asm.index(f".name:           {name}")
+        meta = asm[asm.rindex("- .agpr_count", 0, i):i + 2000]
+        out.append((name, body, meta))
+    return out
 
 
 def test_m0_only_in_direct_loads(asm):
-    body = _kernel_body(asm, "_ZN3lsn11nf4f_kernelENS_10GemmParamsE")
-    inside = False
-    for line in body.splitlines():
-        if "ASMSTART" in line:
-            inside = True
-            continue
-        if "ASMEND" in line:
-            inside = False
-            continue
-        code = line.split(";")[0]
-        if not inside:
-            assert not re.search(r"\bm0\b", code), f"compiler uses M0: {line.strip()}"
-    assert body.count("global_load_lds_dwordx4") >= 10
+    for name, body, _ in _kernels(asm):
+        inside = False
+        for line in body.splitlines():
+            if "ASMSTART" in line:
+                inside = True
+                continue
+            if "ASMEND" in line:
+                inside = False
+                continue
+            code = line.split(";")[0]
+            if not inside:
+                assert not re.search(r"\bm0\b", code), f"{name}: compiler uses M0: {line.strip()}"
+        assert body.count("global_load_lds_dwordx4") >= 10, name
 
 
 def test_no_scratch(asm):
-    i = asm.index(".name:           _ZN3lsn11nf4f_kernelENS_10GemmParamsE")
-    meta = asm[asm.rindex("- .agpr_count", 0, i):i + 2000]
-    assert re.search(r"\.private_segment_fixed_size:\s+0\b", meta), "kernel uses scratch"
+    for name, _, meta in _kernels(asm):
+        assert re.search(r"\.private_segment_fixed_size:\s+0\b", meta), f"{name} uses scratch"
