@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       acc[s >> 1][s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          af[F][s >> 1], bq[F][s & 1], acc[s >> 1][s & 1], 0, 0, 0);
+          bq[F][s & 1], af[F][s >> 1], acc[s >> 1][s & 1], 0, 0, 0);
       if (s < 8) af[F ^ 1][s] = *reinterpret_cast<const bf16x8*>(an + s * 4096);
       if (s < 8) {  // level pair ph of tile jt (byte ph of the code word)
         const int jt = s >> 2, ph = s & 3;
@@ -320,17 +320,18 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
   }
 
-  // ---- epilogue: lane holds column lr, rows (e/4)*8 + (lane/32)*4 + e%4 ----
-  // Fully unrolled for the kernel's output mode (MODE -1: raw split-k
-  // partial sum).  A tile inside the matrix stores without per-element
-  // tests: a uniform row pointer plus a 32-bit lane offset.  The output and
-  // residual rows are restrict-qualified so that the loads need not wait for
-  // earlier stores; that holds even in place (C == R), since each lane's
-  // only same-address pair is one element's own load and store.
+  // ---- epilogue ----
+  // The MFMAs take the weights as their first operand, so tile (i, j) holds
+  // y^T: lane (lr, hh) has output row m = m0 + 32i + lr and the columns
+  // n = n0 + 64w + 32j + 8g + 4hh + t in acc[i][j][4g + t], i.e. four
+  // consecutive columns per 16-byte store.  Fully unrolled for the kernel's
+  // output form (MODE -1: raw split-k partial sum).  The output and residual
+  // pointers are restrict-qualified: a lane's only same-address pair is one
+  // group's own load and store, so this also holds in place (C == R).
   auto epilogue = [&](auto full_) {
     constexpr bool FULL = decltype(full_)::value;
     constexpr bool LOADS = MODE == C_F32_ACC || MODE == C_F32_RES;
@@ -339,57 +340,28 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
     const int64_t ld = MODE < 0 ? (int64_t)p.N : p.ldc;
     const float* const src = MODE == C_F32_RES ? p.R : out;
     const int64_t lds = MODE == C_F32_RES ? p.ldr : ld;
-    if constexpr (FULL) {
-      // byte offsets of this lane within a row pointer (uniform base +
-      // 32-bit offset: the scalar-base address form)
-      constexpr int ESZ = MODE == C_BF16 ? 2 : 4;
-      const uint32_t lo = (uint32_t)((hh * 4 * ld + w * 64 + lr) * ESZ);
-      const uint32_t ls = (uint32_t)((hh * 4 * lds + w * 64 + lr) * 4);
+    const int nl = n0 + w * 64 + hh * 4;  // this lane's first column (t = 0, g = 0, j = 0)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + i * 32 + lr;
+      if (!FULL && m >= p.M) continue;
+      float* __restrict__ orow = out + (int64_t)m * ld + nl;
+      uint16_t* __restrict__ brow = reinterpret_cast<uint16_t*>(p.C) + (int64_t)m * ld + nl;
+      const float* __restrict__ srow = src + (int64_t)m * lds + nl;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t r = m0 + i * 32 + (e >> 2) * 8 + (e & 3);
-          char* __restrict__ row =
-              MODE == C_BF16 ? reinterpret_cast<char*>(reinterpret_cast<uint16_t*>(p.C) + r * ld + n0)
-                             : reinterpret_cast<char*>(out + r * ld + n0);
-          const char* __restrict__ srow = reinterpret_cast<const char*>(src + r * lds + n0);
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float a = acc[i][j][e];
-            if constexpr (MODE < 0) {
-              *reinterpret_cast<float*>(row + lo + j * 32 * ESZ) = a;
-            } else if constexpr (MODE == C_BF16) {
-              *reinterpret_cast<uint16_t*>(row + lo + j * 32 * ESZ) = f32_to_bf16_bits(a);
-            } else if constexpr (LOADS) {
-              *reinterpret_cast<float*>(row + lo + j * 128) =
-                  *reinterpret_cast<const float*>(srow + ls + j * 128) + a;
-            } else {
-              *reinterpret_cast<float*>(row + lo + j * 128) = a;
-            }
-          }
-        }
-    } else {
-      const int64_t lane = (int64_t)(m0 + hh * 4) * ld + (n0 + w * 64 + lr);
-      const int64_t rlane = (int64_t)(m0 + hh * 4) * lds + (n0 + w * 64 + lr);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = i * 32 + (e >> 2) * 8 + (e & 3);  // row within the tile, less hh*4
-          if (m0 + r + hh * 4 >= p.M) continue;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            if (n0 + w * 64 + j * 32 + lr >= p.N) continue;
-            const float a = acc[i][j][e];
-            const int64_t o = lane + (int64_t)r * ld + j * 32;
-            if constexpr (MODE < 0) {
-              out[o] = a;
-            } else if constexpr (MODE == C_BF16) {
-              reinterpret_cast<uint16_t*>(p.C)[o] = f32_to_bf16_bits(a);
-            } else {
-              out[o] = LOADS ? src[rlane + (int64_t)r * lds + j * 32] + a : a;
-            }
+        for (int g = 0; g < 4; ++g) {
+          const int c = j * 32 + g * 8;  // column offset of this group
+          if (!FULL && nl + c >= p.N) continue;
+          f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                     acc[i][j][4 * g + 3]};
+          if constexpr (LOADS) v += *reinterpret_cast<const f32x4*>(srow + c);
+          if constexpr (MODE == C_BF16) {
+            u32x2 b2 = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *reinterpret_cast<u32x2*>(brow + c) = b2;
+          } else {
+            *reinterpret_cast<f32x4*>(orow + c) = v;
           }
         }
     }
@@ -408,6 +380,9 @@ bool nf4f_eligible(const GemmParams& p, int batch) {
   if (p.M < FM || p.K % FK != 0 || p.rowlen != p.K) return false;
   if (p.lda % 8 != 0 || !aligned(p.A, 16) || !aligned(p.B, 16) || !aligned(p.absmax, 4))
     return false;
+  // 16-byte output groups (8-byte for bf16), also for the split-k partials
+  if (p.N % 4 != 0 || p.ldc % 4 != 0 || !aligned(p.C, 16) || !aligned(p.part, 16)) return false;
+  if (p.cmode == C_F32_RES && (p.ldr % 4 != 0 || !aligned(p.R, 16))) return false;
   if (p.kext > 0 && (p.kext % 16 != 0 || p.ldae % 8 != 0 || p.ldbe % 8 != 0 ||
                      !aligned(p.Aext, 16) || !aligned(p.Bext, 16)))
     return false;
