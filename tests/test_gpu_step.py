@@ -456,3 +456,27 @@ def test_dpo_llama8b_layer_shape_vs_oracle(torch, llama2l_oracle):
             assert_close(dA, odA, 5e-2, f"DPO dA L{layer} {p}")
             assert_close(dB, odB, 5e-2, f"DPO dB L{layer} {p}")
     m.close()
+
+
+def test_sft_qwen3b_layer_shape_vs_oracle(torch):
+    """One streamed SFT step at the 3B layer shape (hidden 2048, 16 q / 2 kv
+    heads of 128, FFN 11008, tied embedding, RoPE theta 1e6, eps 1e-6), two
+    layers, vocabulary 1024, 512 tokens, against the oracle."""
+    w = dict(synth.WORKLOADS["qwen2.5-3b-shaped"], n_layers=2, vocab=1024)
+    tokens = synth.sft_tokens(w)
+    say("[sft-3b-shape] oracle")
+    cfg, layers, lora, head = oracle_model(w, b_zero=False)
+    o = om.sft_step(cfg, layers, lora, head, tokens, LR)
+    say("[sft-3b-shape] gpu stream_host")
+    m = gpu_model(w, "stream_host", b_zero=False)
+    loss, logp = _run_sft(torch, m, tokens)
+    g = _grads(m, w)
+    m.close()
+    assert abs(loss - o["loss"]) <= 2e-2 * abs(o["loss"])
+    assert_close(logp, o["logp"], 2e-2, "logp")
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            _, _, dA, dB = g[layer][p]
+            oA, oB = o["grads"][layer][p]
+            assert_close(dA, oA, 5e-2, f"dA L{layer} {p}")
+            assert_close(dB, oB, 5e-2, f"dB L{layer} {p}")
