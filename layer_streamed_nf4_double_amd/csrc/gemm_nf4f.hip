@@ -77,6 +77,24 @@ LSN_DEV void dma4(const void* gbase, uint32_t voff, uint32_t lds) {
       : "memory");
 }
 
+// The same loads with M0 set once for a group: the instruction offset OFS
+// (13-bit signed) moves both the global address and the LDS address
+// (M0 + OFS + 16 lane), so the per-lane global offset passed in has OFS
+// already subtracted.  set_m0 includes the wait state before the first use.
+LSN_DEV void set_m0(uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" : : "s"(lds) : "memory");
+}
+template <int OFS>
+LSN_DEV void dma16_at(const void* gbase, uint32_t voff) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" : : "v"(voff), "s"(gbase), "i"(OFS)
+               : "memory");
+}
+template <int OFS>
+LSN_DEV void dma4_at(const void* gbase, uint32_t voff) {
+  asm volatile("global_load_lds_dword %0, %1 offset:%2" : : "v"(voff), "s"(gbase), "i"(OFS)
+               : "memory");
+}
+
 template <typename T>
 LSN_DEV uint32_t lds_addr(T* q) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)q;
@@ -161,6 +179,14 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
     const int row = min(n0 + r, p.N - 1);
     offC[i] = (uint32_t)((int64_t)row * (p.K / 2) + h * 16);
   }
+  // the same offsets for loads at instruction offset 1024 i - 4096 from one
+  // M0 (activation load i) and at 1024 i (code load i); never negative,
+  // since load i covers rows >= 8 i (activations) or >= 32 i (codes)
+  uint32_t offA_o[8], offC_o[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) offA_o[i] = offA[i] + 4096u - 1024u * i;
+  offC_o[0] = offC[0];
+  offC_o[1] = offC[1] - 1024u;
   // absmax: wave w fills rows 64w .. +63, lane -> row 64w + lane
   const uint32_t offM =
       (uint32_t)((int64_t)min(n0 + w * 64 + lane, p.N - 1) * (p.K / FK) * 4);
@@ -286,10 +312,27 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
       const uint32_t lm = lds_addr(&sM[st][w * 64]);
       const uint8_t* m_next = gM + min(t + 3, it1 - 1) * 4;
       kstep(std::integral_constant<int, 3>{}, sA[st1] + sa0, cqn, can, 0, [&](int s) {
-        if (s < 8) dma16(a_next, offA[s], la + s * 1024);
-        if (s == 8) dma16(c_next, offC[0], lc);
-        if (s == 9) dma16(c_next, offC[1], lc + 1024);
-        if (s == 10) dma4(m_next, offM, lm);
+        // one M0 per group; the loads address relative to it
+        if (s == 0) {
+          set_m0(la + 4096);
+          dma16_at<-4096>(a_next, offA_o[0]);
+        }
+        if (s == 1) dma16_at<-3072>(a_next, offA_o[1]);
+        if (s == 2) dma16_at<-2048>(a_next, offA_o[2]);
+        if (s == 3) dma16_at<-1024>(a_next, offA_o[3]);
+        if (s == 4) dma16_at<0>(a_next, offA_o[4]);
+        if (s == 5) dma16_at<1024>(a_next, offA_o[5]);
+        if (s == 6) dma16_at<2048>(a_next, offA_o[6]);
+        if (s == 7) dma16_at<3072>(a_next, offA_o[7]);
+        if (s == 8) {
+          set_m0(lc);
+          dma16_at<0>(c_next, offC_o[0]);
+        }
+        if (s == 9) dma16_at<1024>(c_next, offC_o[1]);
+        if (s == 10) {
+          set_m0(lm);
+          dma4_at<0>(m_next, offM);
+        }
       });
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
