@@ -46,8 +46,9 @@ struct GemmParams {
   float levels[16] = {};  // NF4 code levels
 };
 
-// TILE_NF4F: the 256 x 256 forward NF4 kernel of gemm_nf4f.hip
-enum { TILE_256x128 = 0, TILE_128x128 = 1, TILE_64x64 = 2, TILE_NF4F = 3 };
+// TILE_NF4F / TILE_NF4T: the 256 x 256 NF4 kernels of gemm_nf4f.hip (y = x W)
+// and gemm_nf4t.hip (dx = dy W)
+enum { TILE_256x128 = 0, TILE_128x128 = 1, TILE_64x64 = 2, TILE_NF4F = 3, TILE_NF4T = 4 };
 
 struct GemmPlan {
   int tile = TILE_64x64;
@@ -71,5 +72,11 @@ __global__ void gemm_reduce_k(const GemmParams p);
 bool nf4f_eligible(const GemmParams& p, int batch);
 int nf4f_split(int M, int N, int K);
 hipError_t nf4f_launch(GemmParams p, hipStream_t s);
+
+// input-gradient NF4 kernel (gemm_nf4t.hip): dx = dy W with dy bf16 [M, K]
+// row-major and the same W^T NF4 record [K, N] (operand form B_NF4_R); used by
+// gemm() whenever nf4t_eligible() holds; splits the k range like nf4f
+bool nf4t_eligible(const GemmParams& p, int batch);
+hipError_t nf4t_launch(GemmParams p, hipStream_t s);
 
 }  // namespace lsn

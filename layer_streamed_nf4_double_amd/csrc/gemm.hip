@@ -562,7 +562,7 @@ GemmPlan gemm_plan(int M, int N, int K, int nseg, int batch) {
 int64_t gemm_partial_floats(int M, int N, int K, int nseg, int batch) {
   const GemmPlan g = gemm_plan(M, N, K, nseg, batch);
   int64_t f = g.split > 1 ? (int64_t)g.split * M * N : 0;
-  if (batch == 1 && nseg == 1 && M >= 256 && K % 64 == 0) {  // forward NF4 kernel
+  if (batch == 1 && nseg == 1 && M >= 256 && K % 64 == 0) {  // the 256 x 256 NF4 kernels
     const int sp = nf4f_split(M, N, K);
     if (sp > 1) f = std::max<int64_t>(f, (int64_t)sp * M * N);
   }
@@ -571,6 +571,7 @@ int64_t gemm_partial_floats(int M, int N, int K, int nseg, int batch) {
 
 int gemm_tile(const GemmParams& p, int opa, int opb, int batch) {
   if (opa == A_BF16_K && opb == B_NF4_K && nf4f_eligible(p, batch)) return TILE_NF4F;
+  if (opa == A_BF16_K && opb == B_NF4_R && nf4t_eligible(p, batch)) return TILE_NF4T;
   return gemm_plan(p.M, p.N, p.K, p.nseg, batch).tile;
 }
 
@@ -618,6 +619,7 @@ hipError_t gemm(const GemmParams& p, int opa, int opb, int batch, hipStream_t s)
   if (p.M <= 0 || p.N <= 0 || batch <= 0) return hipSuccess;
   if (!offsets_fit(p, opa, opb)) return hipErrorInvalidValue;
   if (opa == A_BF16_K && opb == B_NF4_K && nf4f_eligible(p, batch)) return nf4f_launch(p, s);
+  if (opa == A_BF16_K && opb == B_NF4_R && nf4t_eligible(p, batch)) return nf4t_launch(p, s);
 #define LSN_CASE(A_, B_) \
   if (opa == A_ && opb == B_) return launch_tiles<A_, B_>(p, batch, s);
   LSN_CASE(A_BF16_K, B_NF4_K)

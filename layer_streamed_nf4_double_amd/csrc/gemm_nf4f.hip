@@ -40,6 +40,7 @@
 // (split-k partial sums are added in split order by gemm_reduce_k).
 #include "common.h"
 #include "gemm.h"
+#include "nf4_direct.h"
 #include <algorithm>
 #include <type_traits>
 
@@ -52,63 +53,6 @@ constexpr int NST = 3;                 // LDS stages
 constexpr int A_STAGE = FM * FK * 2;   // 32 KiB of activations (bf16)
 constexpr int C_STAGE = FN * FK / 2;   // 8 KiB of codes
 constexpr int GROUP = 8 + 2 + 1;       // direct loads per wave per slice
-
-// One direct global -> LDS load of 16 (or 4) bytes per lane: lane l writes
-// LDS bytes [lds + 16 l, +16) from gbase + voff (gbase and lds uniform).  M0
-// carries the LDS address; one wait state separates its write from the load.
-// No register is written.  The compiler uses M0 nowhere else in this kernel
-// (a test checks the generated code), so the asm overwrites it freely.
-LSN_DEV void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(gbase), "s"(lds)
-      : "memory");
-}
-LSN_DEV void dma4(const void* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %0, %1"
-      :
-      : "v"(voff), "s"(gbase), "s"(lds)
-      : "memory");
-}
-
-// The same loads with M0 set once for a group: the instruction offset OFS
-// (13-bit signed) moves both the global address and the LDS address
-// (M0 + OFS + 16 lane), so the per-lane global offset passed in has OFS
-// already subtracted.  set_m0 includes the wait state before the first use.
-LSN_DEV void set_m0(uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" : : "s"(lds) : "memory");
-}
-template <int OFS>
-LSN_DEV void dma16_at(const void* gbase, uint32_t voff) {
-  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" : : "v"(voff), "s"(gbase), "i"(OFS)
-               : "memory");
-}
-template <int OFS>
-LSN_DEV void dma4_at(const void* gbase, uint32_t voff) {
-  asm volatile("global_load_lds_dword %0, %1 offset:%2" : : "v"(voff), "s"(gbase), "i"(OFS)
-               : "memory");
-}
-
-template <typename T>
-LSN_DEV uint32_t lds_addr(T* q) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)q;
-}
-
-// swizzle of the 16-byte chunk index of activation row r: rows r and r + 8
-// differ in the low bit so that 16 consecutive rows reading one logical chunk
-// hit 16 distinct 4-bank groups (and 8 consecutive rows 8 distinct ones)
-LSN_DEV int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-// byte offset 8 * (byte p of code word q) into the level-pair table
-LSN_DEV uint32_t pair_off(uint32_t q, int p) {
-  return p == 0 ? (q << 3) & 0x7F8u : (q >> (8 * p - 3)) & 0x7F8u;
-}
 
 // Eight NF4 codes (one 32-bit word; element 2p in the low nibble of byte p)
 // to eight bf16 products level * absmax, each rounded once.
@@ -124,10 +68,6 @@ LSN_DEV bf16x8 dequant8(uint32_t q, float a, Pair pair) {
 }
 
 }  // namespace
-
-// s_waitcnt with only the vector-memory count constrained (gfx9 encoding)
-#define LSN_WAIT_VM(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // MODE: the output form (C_F32, C_F32_ACC, C_F32_RES, C_BF16), or -1 for the
 // raw split-k partial sums; one instantiation per form keeps the epilogue a

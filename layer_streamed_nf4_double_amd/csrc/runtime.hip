@@ -581,6 +581,9 @@ static hipError_t nf4_fwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const ui
 }
 
 // dX = dY W_group (+ low-rank extension); dY is fp32 (opa A_F32_K) or bf16.
+// fp32 dY is first rounded to bf16 (the value the MFMA takes anyway) into
+// dqkvb, which is free from the previous layer's q|k|v input gradient until
+// this layer's rope backward refills it.
 static hipError_t nf4_bwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const void* dy, int opa,
                                int T, int kext, void* out, int cmode) {
   GemmParams p = base_params(c);
@@ -588,6 +591,11 @@ static hipError_t nf4_bwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const vo
   p.M = T;
   p.N = (int)c->K[pf];
   p.K = (int)group_rows(c, g);
+  if (opa == A_F32_K) {
+    f32_to_bf16(static_cast<const float*>(dy), c->dqkvb, (int64_t)T * p.K, c->cs);
+    dy = c->dqkvb;
+    opa = A_BF16_K;
+  }
   p.A = dy;
   p.lda = p.K;
   p.B = rec + c->code_off[pf];

@@ -1,8 +1,9 @@
-"""Checks on the generated gfx950 code of the forward NF4 kernel (CPU only).
+"""Checks on the generated gfx950 code of the fused NF4 kernels (CPU only):
+nf4f_kernel (y = x W) and nf4t_kernel (dx = dy W).
 
-The kernel's direct global -> LDS loads are inline asm that set M0 without
+The kernels' direct global -> LDS loads are inline asm that set M0 without
 saving it; that is only correct while the compiler itself uses M0 nowhere in
-the kernel.  The kernel must also keep its accumulators in registers: no
+the kernel.  The kernels must also keep their accumulators in registers: no
 scratch access in the main loop."""
 import os
 import re
@@ -13,28 +14,30 @@ import tempfile
 import pytest
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SRC = os.path.join(os.path.dirname(__file__), "..", "layer_streamed_nf4_double_amd", "csrc",
-                   "gemm_nf4f.hip")
+CSRC = os.path.join(os.path.dirname(__file__), "..", "layer_streamed_nf4_double_amd", "csrc")
+KERNELS = {"nf4f_kernel": "gemm_nf4f.hip", "nf4t_kernel": "gemm_nf4t.hip"}
 
 
-@pytest.fixture(scope="module")
-def asm():
+@pytest.fixture(scope="module", params=sorted(KERNELS))
+def asm(request):
     if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
         pytest.skip("hipcc not available")
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
+        src = os.path.join(CSRC, KERNELS[request.param])
         cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", SRC, "-o", out]
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", src, "-o", out]
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
-        return open(out).read()
+        return request.param, open(out).read()
 
 
 def _kernels(asm):
-    """(name, body, metadata) of every nf4f_kernel instantiation (one per
+    """(name, body, metadata) of every instantiation of the kernel (one per
     output form)."""
-    names = re.findall(r"^(_ZN3lsn11nf4f_kernelI\w+E):", asm, re.M)
-    assert len(names) >= 2, "nf4f_kernel instantiations not found"
+    kernel, asm = asm
+    names = re.findall(r"^(_ZN3lsn%d%sI\w+E):" % (len(kernel), kernel), asm, re.M)
+    assert len(names) >= 2, f"{kernel} instantiations not found"
     out = []
     for name in names:
         start = asm.index(f"{name}:")

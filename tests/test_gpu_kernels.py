@@ -102,10 +102,16 @@ def _gpu_linear(torch, L, X, W, A, B, r, s, dY):
 # (256, 64, 256) one slice; (256, 832, 256) k range split 5/5/3; (512, 4096,
 # 256) split 8 x 8 slices; (257, 128, 296) one-row M tail and a ragged N
 # tile; (300, 1024, 2056) ragged M and N with the rank-16 extension.
+# M >= 256 with N a multiple of 64 and K a multiple of 64 (K >= 128) takes the
+# 256 x 256 input-gradient kernel: (256, 832, 256) a last column tile with one
+# of four waves inside; (512, 4096, 256) 32 tiles of 4 slices; (300, 384,
+# 1024) ragged M, half a column tile, split 4 and the rank-16 extension;
+# (512, 640, 2048) split 8 x 4 slices.
 @pytest.mark.parametrize("M,K,N,r", [(200, 688, 264, 8), (64, 256, 256, 16), (1, 16, 8, 4),
                                      (300, 1024, 2056, 16), (96, 512, 640, 0),
                                      (256, 64, 256, 0), (256, 832, 256, 16),
-                                     (512, 4096, 256, 0), (257, 128, 296, 8)])
+                                     (512, 4096, 256, 0), (257, 128, 296, 8),
+                                     (300, 384, 1024, 16), (512, 640, 2048, 0)])
 def test_linear_parity_small(torch, L, M, K, N, r):
     say(f"[linear] M={M} K={K} N={N} r={r}")
     s = 2.0
