@@ -66,6 +66,9 @@ int64_t gemm_partial_floats(int M, int N, int K, int nseg, int batch);
 
 // split-k reduction kernel (partial sums added in split order, then the epilogue)
 __global__ void gemm_reduce_k(const GemmParams p);
+// launches the reduction of p.ksplit partial sums (a vectorized form where the
+// shapes allow it; both add in split order)
+void gemm_reduce_launch(const GemmParams& p, hipStream_t s);
 
 // forward NF4 kernel (gemm_nf4f.hip): y = x W with x bf16 [M, K] row-major and
 // W^T NF4 [N, K]; used by gemm() whenever nf4f_eligible() holds

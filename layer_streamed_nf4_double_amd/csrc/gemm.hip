@@ -528,6 +528,61 @@ __global__ void gemm_reduce_k(const GemmParams p) {
   }
 }
 
+// The same reduction, four columns per thread and one block row per output
+// row (blockIdx.y = m): four splits are loaded at a time and then added in
+// split order, as above, so results are bitwise the same.  Needs N % 4 == 0
+// and 16-byte aligned rows.
+template <int CM>
+__global__ void gemm_reduce4_k(const GemmParams p) {
+  const int m = blockIdx.y;
+  const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (n >= p.N) return;
+  const f32x4* src = reinterpret_cast<const f32x4*>(p.part + (int64_t)m * p.N + n);
+  const int64_t stride = (int64_t)p.M * p.N / 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int y = 0;
+  for (; y + 4 <= p.ksplit; y += 4) {
+    const f32x4 a = src[y * stride], b = src[(y + 1) * stride];
+    const f32x4 c = src[(y + 2) * stride], d = src[(y + 3) * stride];
+    acc += a;
+    acc += b;
+    acc += c;
+    acc += d;
+  }
+  for (; y < p.ksplit; ++y) acc += src[y * stride];
+  const f32x4 r = p.alpha * acc;
+  const int64_t o = (int64_t)m * p.ldc + n;
+  if constexpr (CM == C_F32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + o) = r;
+  } else if constexpr (CM == C_F32_ACC) {
+    f32x4* c = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + o);
+    *c = *c + r;
+  } else if constexpr (CM == C_F32_RES) {
+    const f32x4 res = *reinterpret_cast<const f32x4*>(p.R + (int64_t)m * p.ldr + n);
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + o) = res + r;
+  } else {
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.C) + o) =
+        u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+  }
+}
+
+void gemm_reduce_launch(const GemmParams& p, hipStream_t s) {
+  const bool bf = p.cmode == C_BF16;
+  const bool vec = p.M <= 65535 && p.N % 4 == 0 && p.ldc % 4 == 0 &&
+                   ((uintptr_t)p.part & 15) == 0 && ((uintptr_t)p.C & (bf ? 7 : 15)) == 0 &&
+                   (p.cmode != C_F32_RES || (p.ldr % 4 == 0 && ((uintptr_t)p.R & 15) == 0));
+  if (!vec) {
+    const int64_t n = (int64_t)p.M * p.N;
+    hipLaunchKernelGGL(gemm_reduce_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+    return;
+  }
+  const dim3 grid((unsigned)((p.N / 4 + 255) / 256), (unsigned)p.M);
+  if (p.cmode == C_F32) hipLaunchKernelGGL(gemm_reduce4_k<C_F32>, grid, dim3(256), 0, s, p);
+  else if (p.cmode == C_F32_ACC) hipLaunchKernelGGL(gemm_reduce4_k<C_F32_ACC>, grid, dim3(256), 0, s, p);
+  else if (p.cmode == C_F32_RES) hipLaunchKernelGGL(gemm_reduce4_k<C_F32_RES>, grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(gemm_reduce4_k<C_BF16>, grid, dim3(256), 0, s, p);
+}
+
 // ---------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------
@@ -582,10 +637,7 @@ static hipError_t launch_t(const GemmParams& p, int batch, hipStream_t s) {
   hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, NS, OPA, OPB>), dim3(tiles, p.ksplit, batch),
                      dim3(WGM * WGN * 64), 0, s, p);
   if (p.ev1) (void)hipEventRecord(p.ev1, s);
-  if (p.ksplit > 1) {
-    const int64_t n = (int64_t)p.M * p.N;
-    hipLaunchKernelGGL(gemm_reduce_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
-  }
+  if (p.ksplit > 1) gemm_reduce_launch(p, s);
   return hipGetLastError();
 }
 

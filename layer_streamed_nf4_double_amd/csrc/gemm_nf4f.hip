@@ -37,7 +37,7 @@
 // byte indexes a 256-entry LDS table holding the levels of its two nibbles.
 //
 // Determinism: every output element is reduced by one lane in a fixed order
-// (split-k partial sums are added in split order by gemm_reduce_k).
+// (split-k partial sums are added in split order by gemm_reduce_launch).
 #include "common.h"
 #include "gemm.h"
 #include "nf4_direct.h"
@@ -396,10 +396,7 @@ hipError_t nf4f_launch(GemmParams p, hipStream_t s) {
   else if (p.cmode == C_F32_RES) hipLaunchKernelGGL(nf4f_kernel<C_F32_RES>, grid, dim3(256), 0, s, p);
   else hipLaunchKernelGGL(nf4f_kernel<C_BF16>, grid, dim3(256), 0, s, p);
   if (p.ev1) (void)hipEventRecord(p.ev1, s);
-  if (p.ksplit > 1) {
-    const int64_t n = (int64_t)p.M * p.N;
-    hipLaunchKernelGGL(gemm_reduce_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
-  }
+  if (p.ksplit > 1) gemm_reduce_launch(p, s);
   return hipGetLastError();
 }
 
