@@ -37,10 +37,12 @@ struct GemmParams {
   int64_t ldr = 0;
   float alpha = 1.f;
   int cmode = C_F32;
-  // split-k scratch (fp32, split * M * N); without it the k range is not split
+  // split-k scratch (fp32, split * split_stride(M, N)); without it the k range
+  // is not split
   float* part = nullptr;
   int64_t part_floats = 0;
-  int ksplit = 1;  // set by gemm()
+  int ksplit = 1;      // set by gemm()
+  int64_t pstride = 0;  // floats from one split's partial sums to the next (set by gemm())
   // optional timing events recorded right before / after the main kernel
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   float levels[16] = {};  // NF4 code levels
@@ -54,6 +56,13 @@ struct GemmPlan {
   int tile = TILE_64x64;
   int split = 1;
 };
+
+// Floats from one split's partial-sum buffer to the next: M * N plus 4 KiB.
+// The splits of a tile finish together and write their partial tiles at the
+// same offsets of their buffers; buffers a multiple of the memory-channel
+// interleave apart (M * N * 4 bytes often is) then send those writes to the
+// same channels, which halves their rate on MI355X.
+inline int64_t split_stride(int M, int N) { return (int64_t)M * N + 1024; }
 
 hipError_t gemm(const GemmParams& p, int opa, int opb, int batch, hipStream_t s);
 // the tile id gemm() launches for these operand forms

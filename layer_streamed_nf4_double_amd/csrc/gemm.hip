@@ -492,7 +492,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(const GemmParams p
         const int m = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
         if (m >= p.M) continue;
         if (p.ksplit > 1) {  // raw partial sum of this k range
-          p.part[((int64_t)blockIdx.y * p.M + m) * p.N + n] = acc[i][j][e];
+          p.part[blockIdx.y * p.pstride + (int64_t)m * p.N + n] = acc[i][j][e];
           continue;
         }
         const float v = p.alpha * acc[i][j][e];
@@ -517,7 +517,7 @@ __global__ void gemm_reduce_k(const GemmParams p) {
   if (i >= (int64_t)p.M * p.N) return;
   const int m = (int)(i / p.N), n = (int)(i % p.N);
   float acc = 0.f;
-  for (int y = 0; y < p.ksplit; ++y) acc += p.part[((int64_t)y * p.M + m) * p.N + n];
+  for (int y = 0; y < p.ksplit; ++y) acc += p.part[y * p.pstride + (int64_t)m * p.N + n];
   const float v = p.alpha * acc;
   const int64_t o = (int64_t)m * p.ldc + n;
   switch (p.cmode) {
@@ -538,7 +538,7 @@ __global__ void gemm_reduce4_k(const GemmParams p) {
   const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (n >= p.N) return;
   const f32x4* src = reinterpret_cast<const f32x4*>(p.part + (int64_t)m * p.N + n);
-  const int64_t stride = (int64_t)p.M * p.N / 4;
+  const int64_t stride = p.pstride / 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   int y = 0;
   for (; y + 4 <= p.ksplit; y += 4) {
@@ -568,7 +568,7 @@ __global__ void gemm_reduce4_k(const GemmParams p) {
 
 void gemm_reduce_launch(const GemmParams& p, hipStream_t s) {
   const bool bf = p.cmode == C_BF16;
-  const bool vec = p.M <= 65535 && p.N % 4 == 0 && p.ldc % 4 == 0 &&
+  const bool vec = p.M <= 65535 && p.N % 4 == 0 && p.pstride % 4 == 0 && p.ldc % 4 == 0 &&
                    ((uintptr_t)p.part & 15) == 0 && ((uintptr_t)p.C & (bf ? 7 : 15)) == 0 &&
                    (p.cmode != C_F32_RES || (p.ldr % 4 == 0 && ((uintptr_t)p.R & 15) == 0));
   if (!vec) {
@@ -616,10 +616,10 @@ GemmPlan gemm_plan(int M, int N, int K, int nseg, int batch) {
 
 int64_t gemm_partial_floats(int M, int N, int K, int nseg, int batch) {
   const GemmPlan g = gemm_plan(M, N, K, nseg, batch);
-  int64_t f = g.split > 1 ? (int64_t)g.split * M * N : 0;
+  int64_t f = g.split > 1 ? g.split * split_stride(M, N) : 0;
   if (batch == 1 && nseg == 1 && M >= 256 && K % 64 == 0) {  // the 256 x 256 NF4 kernels
     const int sp = nf4f_split(M, N, K);
-    if (sp > 1) f = std::max<int64_t>(f, (int64_t)sp * M * N);
+    if (sp > 1) f = std::max<int64_t>(f, sp * split_stride(M, N));
   }
   return f;
 }
@@ -645,7 +645,8 @@ template <int OPA, int OPB>
 static hipError_t launch_tiles(GemmParams p, int batch, hipStream_t s) {
   const GemmPlan g = gemm_plan(p.M, p.N, p.K, p.nseg, batch);
   p.ksplit = g.split;
-  if (p.ksplit > 1 && (!p.part || p.part_floats < (int64_t)p.ksplit * p.M * p.N)) p.ksplit = 1;
+  p.pstride = split_stride(p.M, p.N);
+  if (p.ksplit > 1 && (!p.part || p.part_floats < p.ksplit * p.pstride)) p.ksplit = 1;
   switch (g.tile) {
     // 256 x 128: 8 waves (two per SIMD) of 64 x 64; smaller tiles: 4 waves
     case TILE_256x128: return launch_t<256, 128, 4, 2, 2, OPA, OPB>(p, batch, s);

@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   auto epilogue = [&](auto full_) {
     constexpr bool FULL = decltype(full_)::value;
     constexpr bool LOADS = MODE == C_F32_ACC || MODE == C_F32_RES;
-    float* const out = MODE < 0 ? p.part + (int64_t)blockIdx.y * p.M * p.N
+    float* const out = MODE < 0 ? p.part + blockIdx.y * p.pstride
                                 : reinterpret_cast<float*>(p.C);
     const int64_t ld = MODE < 0 ? (int64_t)p.N : p.ldc;
     const float* const src = MODE == C_F32_RES ? p.R : out;
@@ -386,7 +386,8 @@ int nf4f_split(int M, int N, int K) {
 
 hipError_t nf4f_launch(GemmParams p, hipStream_t s) {
   p.ksplit = nf4f_split(p.M, p.N, p.K);
-  if (p.ksplit > 1 && (!p.part || p.part_floats < (int64_t)p.ksplit * p.M * p.N)) p.ksplit = 1;
+  p.pstride = split_stride(p.M, p.N);
+  if (p.ksplit > 1 && (!p.part || p.part_floats < p.ksplit * p.pstride)) p.ksplit = 1;
   const int tiles = ((p.M + FM - 1) / FM) * ((p.N + FN - 1) / FN);
   if (p.ev0) (void)hipEventRecord(p.ev0, s);
   const dim3 grid(tiles, p.ksplit, 1);

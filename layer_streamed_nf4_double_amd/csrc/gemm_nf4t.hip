@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) void nf4t_kernel(const GemmParams p) {
     constexpr bool FULL = decltype(full_)::value;
     constexpr bool LOADS = MODE == C_F32_ACC || MODE == C_F32_RES;
     if (!FULL && nw >= p.N) return;
-    float* const out = MODE < 0 ? p.part + (int64_t)blockIdx.y * p.M * p.N
+    float* const out = MODE < 0 ? p.part + blockIdx.y * p.pstride
                                 : reinterpret_cast<float*>(p.C);
     const int64_t ld = MODE < 0 ? (int64_t)p.N : p.ldc;
     const float* const src = MODE == C_F32_RES ? p.R : out;
@@ -383,7 +383,8 @@ bool nf4t_eligible(const GemmParams& p, int batch) {
 
 hipError_t nf4t_launch(GemmParams p, hipStream_t s) {
   p.ksplit = nf4f_split(p.M, p.N, p.K);
-  if (p.ksplit > 1 && (!p.part || p.part_floats < (int64_t)p.ksplit * p.M * p.N)) p.ksplit = 1;
+  p.pstride = split_stride(p.M, p.N);
+  if (p.ksplit > 1 && (!p.part || p.part_floats < p.ksplit * p.pstride)) p.ksplit = 1;
   const int tiles = ((p.M + TM - 1) / TM) * ((p.N + TN - 1) / TN);
   if (p.ev0) (void)hipEventRecord(p.ev0, s);
   const dim3 grid(tiles, p.ksplit, 1);
