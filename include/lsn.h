@@ -287,7 +287,8 @@ lsn_status lsn_set_profiling(lsn_ctx* ctx, int32_t on);
  * forms are (a, b) -- A: 0 bf16 row-major, 1 bf16 transposed, 2 fp32
  * row-major; B: 0 bf16 [N,K], 1 bf16 [K,N], 2 NF4 W^T used as y = x W,
  * 3 NF4 W^T used as dx = dy W^T -- and whose tile id is tile (0: 256x128,
- * 1: 128x128, 2: 64x64, 3: the 256x256 forward NF4 kernel; -1: any);
+ * 1: 128x128, 2: 64x64, 3: the 256x256 forward NF4 kernel, 4: the 256x256
+ * input-gradient NF4 kernel; -1: any);
  * work = algorithmic flops 2*M*N*K per
  * problem (the low-rank extension not counted).  what = 1: record copies;
  * work = bytes.  count = launches, ms = summed event time.  Synchronizes. */

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblsn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["gemm.hip", "gemm_nf4f.hip", "gemm_nf4t.hip", "ops.hip", "lora.hip", "runtime.hip", "nf4_host.cpp"]
+SOURCES = ["gemm.hip", "gemm_nf4f.hip", "gemm_nf4t.hip", "gemm_bf16.hip", "ops.hip", "lora.hip", "runtime.hip", "nf4_host.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are switched off for device code on purpose.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

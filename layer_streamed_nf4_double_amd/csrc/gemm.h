@@ -49,8 +49,11 @@ struct GemmParams {
 };
 
 // TILE_NF4F / TILE_NF4T: the 256 x 256 NF4 kernels of gemm_nf4f.hip (y = x W)
-// and gemm_nf4t.hip (dx = dy W)
-enum { TILE_256x128 = 0, TILE_128x128 = 1, TILE_64x64 = 2, TILE_NF4F = 3, TILE_NF4T = 4 };
+// and gemm_nf4t.hip (dx = dy W); TILE_BF16F: the 256 x 256 bf16 kernel of
+// gemm_bf16.hip (C = A B^T, LM-head logits); TILE_BF16T: its C = A B
+// counterpart (LM-head input gradient)
+enum { TILE_256x128 = 0, TILE_128x128 = 1, TILE_64x64 = 2, TILE_NF4F = 3, TILE_NF4T = 4,
+       TILE_BF16F = 5, TILE_BF16T = 6 };
 
 struct GemmPlan {
   int tile = TILE_64x64;
@@ -90,5 +93,14 @@ hipError_t nf4f_launch(GemmParams p, hipStream_t s);
 // gemm() whenever nf4t_eligible() holds; splits the k range like nf4f
 bool nf4t_eligible(const GemmParams& p, int batch);
 hipError_t nf4t_launch(GemmParams p, hipStream_t s);
+
+// bf16 kernel (gemm_bf16.hip): C = A B^T with A [M, K] and B [N, K] bf16,
+// both k-contiguous (operand forms A_BF16_K, B_BF16_K); used by gemm()
+// whenever bf16f_eligible() holds; splits the k range like nf4f
+bool bf16f_eligible(const GemmParams& p, int batch);
+hipError_t bf16f_launch(GemmParams p, hipStream_t s);
+// ... and C = A B with B [K, N] bf16, N contiguous (operand form B_BF16_R)
+bool bf16t_eligible(const GemmParams& p, int batch);
+hipError_t bf16t_launch(GemmParams p, hipStream_t s);
 
 }  // namespace lsn

@@ -627,6 +627,8 @@ int64_t gemm_partial_floats(int M, int N, int K, int nseg, int batch) {
 int gemm_tile(const GemmParams& p, int opa, int opb, int batch) {
   if (opa == A_BF16_K && opb == B_NF4_K && nf4f_eligible(p, batch)) return TILE_NF4F;
   if (opa == A_BF16_K && opb == B_NF4_R && nf4t_eligible(p, batch)) return TILE_NF4T;
+  if (opa == A_BF16_K && opb == B_BF16_K && bf16f_eligible(p, batch)) return TILE_BF16F;
+  if (opa == A_BF16_K && opb == B_BF16_R && bf16t_eligible(p, batch)) return TILE_BF16T;
   return gemm_plan(p.M, p.N, p.K, p.nseg, batch).tile;
 }
 
@@ -673,6 +675,8 @@ hipError_t gemm(const GemmParams& p, int opa, int opb, int batch, hipStream_t s)
   if (!offsets_fit(p, opa, opb)) return hipErrorInvalidValue;
   if (opa == A_BF16_K && opb == B_NF4_K && nf4f_eligible(p, batch)) return nf4f_launch(p, s);
   if (opa == A_BF16_K && opb == B_NF4_R && nf4t_eligible(p, batch)) return nf4t_launch(p, s);
+  if (opa == A_BF16_K && opb == B_BF16_K && bf16f_eligible(p, batch)) return bf16f_launch(p, s);
+  if (opa == A_BF16_K && opb == B_BF16_R && bf16t_eligible(p, batch)) return bf16t_launch(p, s);
 #define LSN_CASE(A_, B_) \
   if (opa == A_ && opb == B_) return launch_tiles<A_, B_>(p, batch, s);
   LSN_CASE(A_BF16_K, B_NF4_K)

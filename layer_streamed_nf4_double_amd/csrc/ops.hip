@@ -206,28 +206,44 @@ __global__ void lora_ext_k(const float* __restrict__ Wp, int64_t srow, int64_t s
 // ---------------------------------------------------------------------------
 // vocabulary-chunk log-softmax (online max / sum) and target gather
 // ---------------------------------------------------------------------------
+// One block of 256 threads per row.  Each thread keeps a running (max, sum
+// of exp(x - max)) over its four-column groups in a fixed order, rescaling the
+// sum when the max grows; the block then combines the threads' pairs in a
+// fixed order.  Rows of Vc % 4 == 0 floats take 16-byte loads.
 __global__ void lse_chunk_k(const float* __restrict__ logits, int Vc, int v0,
                             const int32_t* __restrict__ tgt, float* __restrict__ run_m,
                             float* __restrict__ run_s, float* __restrict__ tlogit, int first) {
   __shared__ float red[16];
   const int64_t t = blockIdx.x;
   const float* x = logits + t * Vc;
-  float m = -INFINITY;
-  for (int i = threadIdx.x; i < Vc; i += blockDim.x) m = fmaxf(m, x[i]);
-  m = block_max(m, red);
-  float s = 0.f;
-  for (int i = threadIdx.x; i < Vc; i += blockDim.x) s += expf(x[i] - m);
-  s = block_sum(s, red);
+  float m = -INFINITY, s = 0.f;
+  auto add4 = [&](float a, float b, float c, float d) {
+    const float mv = fmaxf(fmaxf(a, b), fmaxf(c, d));
+    if (mv > m) {
+      s *= expf(m - mv);
+      m = mv;
+    }
+    s += expf(a - m) + expf(b - m) + expf(c - m) + expf(d - m);
+  };
+  const int n4 = (Vc % 4 == 0) ? Vc / 4 : 0;
+  const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
+  for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+    const f32x4 v = x4[i];
+    add4(v[0], v[1], v[2], v[3]);
+  }
+  for (int i = 4 * n4 + threadIdx.x; i < Vc; i += blockDim.x) add4(x[i], -INFINITY, -INFINITY, -INFINITY);
+  const float M = block_max(m, red);
+  s = block_sum(m == -INFINITY ? 0.f : s * expf(m - M), red);
   if (threadIdx.x == 0) {
     const int y = tgt[t];
     if (first) {
-      run_m[t] = m;
+      run_m[t] = M;
       run_s[t] = s;
       tlogit[t] = 0.f;
     } else {
       const float om = run_m[t], os = run_s[t];
-      const float nm = fmaxf(om, m);
-      run_s[t] = os * expf(om - nm) + s * expf(m - nm);
+      const float nm = fmaxf(om, M);
+      run_s[t] = os * expf(om - nm) + s * expf(M - nm);
       run_m[t] = nm;
     }
     if (y >= v0 && y < v0 + Vc) tlogit[t] = x[y - v0];
@@ -258,6 +274,30 @@ __global__ void dlogits_k(const float* __restrict__ logits, int Vc, int v0,
     g = dlogp[t] * (((v0 + i) == y ? 1.f : 0.f) - p);
   }
   out[t * Vc + i] = f32_to_bf16_bits(g);
+}
+// the same, eight columns per thread (Vc % 8 == 0, 16-byte aligned rows)
+__global__ void dlogits8_k(const float* __restrict__ logits, int Vc, int v0,
+                           const float* __restrict__ lse, const int32_t* __restrict__ tgt,
+                           const float* __restrict__ dlogp, uint16_t* __restrict__ out) {
+  const int64_t t = blockIdx.y;
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (i >= Vc) return;
+  const int y = tgt[t];
+  u32x4 o = {0u, 0u, 0u, 0u};
+  if (y >= 0) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(logits + t * Vc + i);
+    const f32x4 a = src[0], b = src[1];
+    const float l = lse[t], d = dlogp[t];
+    float g[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = expf((e < 4 ? a[e] : b[e - 4]) - l);
+      g[e] = d * (((v0 + i + e) == y ? 1.f : 0.f) - p);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(g[2 * e], g[2 * e + 1]);
+  }
+  *reinterpret_cast<u32x4*>(out + t * Vc + i) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -459,8 +499,12 @@ void lse_final(const float* run_m, const float* run_s, const float* tlogit, cons
 }
 void dlogits(const float* logits, int T, int Vc, int v0, const float* lse, const int32_t* tgt,
              const float* dlogp, uint16_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(dlogits_k, dim3(nb(Vc, 256), T), dim3(256), 0, s, logits, Vc, v0, lse, tgt,
-                     dlogp, out);
+  if (Vc % 8 == 0 && ((uintptr_t)logits & 15) == 0 && ((uintptr_t)out & 15) == 0)
+    hipLaunchKernelGGL(dlogits8_k, dim3(nb(Vc / 8, 256), T), dim3(256), 0, s, logits, Vc, v0, lse,
+                       tgt, dlogp, out);
+  else
+    hipLaunchKernelGGL(dlogits_k, dim3(nb(Vc, 256), T), dim3(256), 0, s, logits, Vc, v0, lse, tgt,
+                       dlogp, out);
 }
 void sft_loss(const float* logp, const int32_t* tgt, int n, float* loss, float* dlogp,
               hipStream_t s) {

@@ -42,7 +42,13 @@ namespace {
 
 constexpr int NPROJ = 7;
 constexpr uint64_t REC_ALIGN = 4096;
-constexpr int VCHUNK = 16384;  // vocabulary rows per LM-head GEMM
+// Vocabulary rows per LM-head GEMM: about 256 output tiles of 256 x 256 at
+// max_tokens rows (one workgroup per CU, no split-k), at least 16384.  The
+// fp32 logits of one chunk then take at most 64 MiB up to 1024 tokens.
+inline int vchunk_for(int64_t max_tokens) {
+  const int64_t mt = (max_tokens + 255) / 256;
+  return (int)std::max<int64_t>(16384, std::min<int64_t>(65536, 256 / mt * 256));
+}
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -98,6 +104,7 @@ struct lsn_ctx {
   float *rstd1, *qkv, *scores, *Pf, *h2, *rstd2, *gu, *da, *dguf, *dn, *dh2, *dqkv, *lt, *lu,
       *rstdf, *logits, *run_m, *run_s, *tlogit, *lse, *dnf, *lpart, *gpart;
   int64_t ext_rows = 0, lpart_floats = 0, gpart_floats = 0;
+  int vchunk = 16384;  // vocabulary rows per LM-head GEMM (vchunk_for(max_tokens))
 
   // pass state
   int pass_kind = -1, n_seq = 0, seq_len = 0, T = 0;
@@ -281,6 +288,7 @@ static uint64_t carve(lsn_ctx* c, char* base) {
   const lsn_config& g = c->cfg;
   const int64_t T = g.max_tokens, S = g.max_seq_len, H = g.hidden, F = g.ffn, V = g.vocab;
   const int64_t r = g.lora_rank;
+  c->vchunk = vchunk_for(T);
   Carver cv;
   auto P = [&](uint64_t bytes) -> char* { const uint64_t o = cv.take(bytes); return base ? base + o : nullptr; };
   const int nrec = (g.mode == LSN_RESIDENT) ? g.n_layers : 2;
@@ -337,7 +345,7 @@ static uint64_t carve(lsn_ctx* c, char* base) {
            lora_mm_partial_floats((int)c->N[p], (int)T)});
   c->lpart = (float*)P(std::max<int64_t>(c->lpart_floats, 1) * 4);
   {  // split-k scratch of the largest single-problem GEMM at max_tokens
-    const int64_t Vc0 = std::min<int64_t>(V, VCHUNK);
+    const int64_t Vc0 = std::min<int64_t>(V, c->vchunk);
     const int64_t shapes[][3] = {{QKV, H}, {H, QD}, {2 * F, H}, {H, F}, {F, H},
                                  {H, 2 * F}, {QD, H}, {H, QKV}, {Vc0, H}, {H, Vc0}};
     c->gpart_floats = 0;
@@ -351,7 +359,7 @@ static uint64_t carve(lsn_ctx* c, char* base) {
   c->aext = (uint16_t*)P(T * 48 * 2);
   c->bext = (uint16_t*)P(c->ext_rows * 48 * 2);
   // LM head
-  const int64_t Vc = std::min<int64_t>(V, VCHUNK);
+  const int64_t Vc = std::min<int64_t>(V, c->vchunk);
   c->nf = (uint16_t*)P(T * H * 2);
   c->rstdf = (float*)P(T * 4);
   c->logits = (float*)P(T * Vc * 4);
@@ -1227,8 +1235,8 @@ lsn_status lsn_lm_head_logprobs(lsn_ctx* c, const float* h, const int32_t* targe
   if (!c->head_loaded) return fail(c, LSN_ERR_STATE, "head tables not loaded");
   const int T = c->T, V = c->cfg.vocab, H = c->cfg.hidden;
   rmsnorm_fwd(h, c->final_norm, T, H, c->cfg.rms_eps, c->nf, c->rstdf, c->cs);
-  for (int v0 = 0; v0 < V; v0 += VCHUNK) {
-    const int Vc = std::min(VCHUNK, V - v0);
+  for (int v0 = 0; v0 < V; v0 += c->vchunk) {
+    const int Vc = std::min(c->vchunk, V - v0);
     lsn_status st = lm_logits_chunk(c, v0, Vc);
     if (st != LSN_OK) return st;
     lse_chunk(c->logits, T, Vc, v0, targets, c->run_m, c->run_s, c->tlogit, v0 == 0, c->cs);
@@ -1246,8 +1254,8 @@ lsn_status lsn_lm_head_backward(lsn_ctx* c, const float* h, const int32_t* targe
   if (h != c->lm_h || c->lm_T != c->T)
     return fail(c, LSN_ERR_STATE, "lm_head_backward must follow lm_head_logprobs on the same h");
   const int T = c->T, V = c->cfg.vocab, H = c->cfg.hidden;
-  for (int v0 = 0; v0 < V; v0 += VCHUNK) {
-    const int Vc = std::min(VCHUNK, V - v0);
+  for (int v0 = 0; v0 < V; v0 += c->vchunk) {
+    const int Vc = std::min(c->vchunk, V - v0);
     lsn_status st = lm_logits_chunk(c, v0, Vc);
     if (st != LSN_OK) return st;
     dlogits(c->logits, T, Vc, v0, c->lse, targets, dlogp, c->dlog, c->cs);

@@ -1,5 +1,6 @@
-"""Checks on the generated gfx950 code of the fused NF4 kernels (CPU only):
-nf4f_kernel (y = x W) and nf4t_kernel (dx = dy W).
+"""Checks on the generated gfx950 code of the direct-load GEMM kernels (CPU
+only): nf4f_kernel (y = x W), nf4t_kernel (dx = dy W), bf16f_kernel
+(C = A B^T in bf16) and bf16t_kernel (C = A B in bf16).
 
 The kernels' direct global -> LDS loads are inline asm that set M0 without
 saving it; that is only correct while the compiler itself uses M0 nowhere in
@@ -15,7 +16,8 @@ import pytest
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CSRC = os.path.join(os.path.dirname(__file__), "..", "layer_streamed_nf4_double_amd", "csrc")
-KERNELS = {"nf4f_kernel": "gemm_nf4f.hip", "nf4t_kernel": "gemm_nf4t.hip"}
+KERNELS = {"nf4f_kernel": "gemm_nf4f.hip", "nf4t_kernel": "gemm_nf4t.hip",
+           "bf16f_kernel": "gemm_bf16.hip", "bf16t_kernel": "gemm_bf16.hip"}
 
 
 @pytest.fixture(scope="module", params=sorted(KERNELS))

@@ -348,6 +348,30 @@ def test_auto_source_and_preflight(torch):
         ad.plan_run(1, 1, free + (1 << 30), free, 1 << 40)
 
 
+def test_sft_large_vocab_multichunk_head_vs_oracle(torch):
+    """One SFT step with a 70000-entry vocabulary at 2 x 152 tokens: the LM
+    head runs three vocabulary chunks (32768, 32768, 4464 rows: online
+    log-sum-exp across chunks, dlogits per chunk, dh accumulated over chunks)
+    on the 256 x 256 bf16 logits kernel with a ragged row tile and a ragged
+    last column tile."""
+    w = dict(SMALL256, n_layers=1, vocab=70000, n_seq=2, seq_len=152)
+    tokens = synth.sft_tokens(w)
+    say("[sft-vocab70000] oracle")
+    cfg, layers, lora, head = oracle_model(w, b_zero=False, lora_targets=ALL7)
+    o = om.sft_step(cfg, layers, lora, head, tokens, LR)
+    say("[sft-vocab70000] gpu stream_host")
+    m = gpu_model(w, "stream_host", b_zero=False, lora_targets=ALL7)
+    loss, logp = _run_sft(torch, m, tokens)
+    g = _grads(m, w, ALL7)
+    assert abs(loss - o["loss"]) <= 2e-2 * abs(o["loss"])
+    assert_close(logp, o["logp"], 2e-2, "logp")
+    for p in ALL7:
+        _, _, dA, dB = g[0][p]
+        oA, oB = o["grads"][0][p]
+        assert_close(dA, oA, 5e-2, f"dA {p}")
+        assert_close(dB, oB, 5e-2, f"dB {p}")
+
+
 def test_sft_256_tokens_all_projections_vs_oracle(torch):
     """One SFT step at 256 tokens with B != 0 on all seven projections (the
     forward NF4 GEMMs run the 256 x 256 kernel), then streamed == resident
