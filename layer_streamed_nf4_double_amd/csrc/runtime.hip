@@ -188,10 +188,13 @@ static lsn_status launch_check(lsn_ctx* c) {
 // ---------------------------------------------------------------------------
 // profiling
 // ---------------------------------------------------------------------------
+// Timing events only bracket work for elapsed-time queries made after a full
+// synchronization, so they skip the system-scope fence of an event record
+// (an L2 writeback that would itself take time between the brackets).
 static hipEvent_t take_event(lsn_ctx* c) {
   if (c->evnext == c->evpool.size()) {
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     c->evpool.push_back(e);
   }
   return c->evpool[c->evnext++];
