@@ -225,10 +225,17 @@ lsn_status lsn_backward_layer(lsn_ctx* ctx, int32_t layer, const float* h_in_sav
  * LM head.  h: device fp32 [T, hidden]; targets: device int32 [T] (a negative
  * target gives logp 0); logp: device fp32 [T] = log softmax(RMSNorm(h) W_lm^T)
  * at the target, over the vocabulary in chunks (online max / sum).
- * lm_head_backward must follow the lm_head_logprobs call on the same h:
- * dh (device fp32 [T, hidden], overwritten) from dlogp (device fp32 [T]).
+ * want_grad_state != 0 also keeps, per position, the expected embedding row
+ * E[t] = sum_v softmax_v W_v, accumulated chunk by chunk (rescaled to the
+ * running max), for the backward.  lm_head_backward must follow an
+ * lm_head_logprobs call with want_grad_state on the same h (else
+ * LSN_ERR_STATE): dh (device fp32 [T, hidden], overwritten) from dlogp
+ * (device fp32 [T]) as dlogp_t (W[y_t] - E[t]) through the final RMSNorm,
+ * with no second pass over W_lm (page "Soup: ...", the LM-head logprobs and
+ * their gradient).
  * ------------------------------------------------------------------------- */
-lsn_status lsn_lm_head_logprobs(lsn_ctx* ctx, const float* h, const int32_t* targets, float* logp);
+lsn_status lsn_lm_head_logprobs(lsn_ctx* ctx, const float* h, const int32_t* targets, float* logp,
+                                int32_t want_grad_state);
 lsn_status lsn_lm_head_backward(lsn_ctx* ctx, const float* h, const int32_t* targets,
                                 const float* dlogp, float* dh);
 

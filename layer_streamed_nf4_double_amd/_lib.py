@@ -75,7 +75,7 @@ _SIGS = {
     "lsn_forward_layer": [_P, _I32, _P, _P],
     "lsn_forward_layer_pair": [_P, _I32, _P, _P, _P, _P],
     "lsn_backward_layer": [_P, _I32, _P, _P, _P],
-    "lsn_lm_head_logprobs": [_P, _P, _P, _P],
+    "lsn_lm_head_logprobs": [_P, _P, _P, _P, _I32],
     "lsn_lm_head_backward": [_P, _P, _P, _P, _P],
     "lsn_sft_loss": [_P, _P, _P, _I32, _P, _P],
     "lsn_dpo_loss": [_P, _P, _P, _I32, _I32, _F, _P, _P],
@@ -282,9 +282,9 @@ def lsn_backward_layer(ctx, layer, h_in, dh_out, dh_in):
            "lsn_backward_layer")
 
 
-def lsn_lm_head_logprobs(ctx, h, targets, logp):
-    _check(_lib.lsn_lm_head_logprobs(ctx, _ptr(h), _ptr(targets), _ptr(logp)), ctx,
-           "lsn_lm_head_logprobs")
+def lsn_lm_head_logprobs(ctx, h, targets, logp, want_grad_state):
+    _check(_lib.lsn_lm_head_logprobs(ctx, _ptr(h), _ptr(targets), _ptr(logp), int(want_grad_state)),
+           ctx, "lsn_lm_head_logprobs")
 
 
 def lsn_lm_head_backward(ctx, h, targets, dlogp, dh):

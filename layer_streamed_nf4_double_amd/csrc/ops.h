@@ -25,9 +25,16 @@ void lora_ext(const float* W, int64_t srow, int64_t sj, int R, int r, uint16_t* 
 void lse_chunk(const float* logits, int T, int Vc, int v0, const int32_t* tgt, float* run_m,
                float* run_s, float* tlogit, int first, hipStream_t s);
 void lse_final(const float* run_m, const float* run_s, const float* tlogit, const int32_t* tgt,
-               int T, float* logp, float* lse, hipStream_t s);
-void dlogits(const float* logits, int T, int Vc, int v0, const float* lse, const int32_t* tgt,
-             const float* dlogp, uint16_t* out, hipStream_t s);
+               int T, float* logp, float* lse, float* inv, hipStream_t s);
+// chunk pass that also writes p~ = bf16(exp(l - m')) and alpha = exp(m - m')
+void lse_chunk_acc(const float* logits, int T, int Vc, int v0, const int32_t* tgt, float* run_m,
+                   float* run_s, float* tlogit, float* alpha, uint16_t* pt, int first,
+                   hipStream_t s);
+// x[t, :] *= f[t] (n % 4 == 0, 16-byte aligned rows)
+void scale_rows(float* x, const float* f, int T, int n, hipStream_t s);
+// E[t, :] = dlogp[t] * (W[y_t, :] - E[t, :]) in place
+void head_grad(const float* dlogp, const int32_t* tgt, const uint16_t* W, int T, int H, float* E,
+               hipStream_t s);
 void sft_loss(const float* logp, const int32_t* tgt, int n, float* loss, float* dlogp,
               hipStream_t s);
 // kind: 0 DPO, 1 SimPO, 2 ORPO, 3 KTO (lr may be null for 1 and 2)

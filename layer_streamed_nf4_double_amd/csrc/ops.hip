@@ -206,98 +206,113 @@ __global__ void lora_ext_k(const float* __restrict__ Wp, int64_t srow, int64_t s
 // ---------------------------------------------------------------------------
 // vocabulary-chunk log-softmax (online max / sum) and target gather
 // ---------------------------------------------------------------------------
-// One block of 256 threads per row.  Each thread keeps a running (max, sum
-// of exp(x - max)) over its four-column groups in a fixed order, rescaling the
-// sum when the max grows; the block then combines the threads' pairs in a
-// fixed order.  Rows of Vc % 4 == 0 floats take 16-byte loads.
-__global__ void lse_chunk_k(const float* __restrict__ logits, int Vc, int v0,
-                            const int32_t* __restrict__ tgt, float* __restrict__ run_m,
-                            float* __restrict__ run_s, float* __restrict__ tlogit, int first) {
-  __shared__ float red[16];
-  const int64_t t = blockIdx.x;
-  const float* x = logits + t * Vc;
-  float m = -INFINITY, s = 0.f;
-  auto add4 = [&](float a, float b, float c, float d) {
-    const float mv = fmaxf(fmaxf(a, b), fmaxf(c, d));
-    if (mv > m) {
-      s *= expf(m - mv);
-      m = mv;
-    }
-    s += expf(a - m) + expf(b - m) + expf(c - m) + expf(d - m);
-  };
-  const int n4 = (Vc % 4 == 0) ? Vc / 4 : 0;
-  const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
-  for (int i = threadIdx.x; i < n4; i += blockDim.x) {
-    const f32x4 v = x4[i];
-    add4(v[0], v[1], v[2], v[3]);
-  }
-  for (int i = 4 * n4 + threadIdx.x; i < Vc; i += blockDim.x) add4(x[i], -INFINITY, -INFINITY, -INFINITY);
-  const float M = block_max(m, red);
-  s = block_sum(m == -INFINITY ? 0.f : s * expf(m - M), red);
-  if (threadIdx.x == 0) {
-    const int y = tgt[t];
-    if (first) {
-      run_m[t] = M;
-      run_s[t] = s;
-      tlogit[t] = 0.f;
-    } else {
-      const float om = run_m[t], os = run_s[t];
-      const float nm = fmaxf(om, M);
-      run_s[t] = os * expf(om - nm) + s * expf(M - nm);
-      run_m[t] = nm;
-    }
-    if (y >= v0 && y < v0 + Vc) tlogit[t] = x[y - v0];
-  }
-}
-
+// lse = m + log(sum); logp at the target; inv (when given) = 1 / sum
 __global__ void lse_final_k(const float* __restrict__ run_m, const float* __restrict__ run_s,
                             const float* __restrict__ tlogit, const int32_t* __restrict__ tgt,
-                            int T, float* __restrict__ logp, float* __restrict__ lse) {
+                            int T, float* __restrict__ logp, float* __restrict__ lse,
+                            float* __restrict__ inv) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   const float l = run_m[t] + logf(run_s[t]);
   lse[t] = l;
   logp[t] = (tgt[t] >= 0) ? tlogit[t] - l : 0.f;
+  if (inv) inv[t] = 1.0f / run_s[t];
 }
 
-// dlogits = dlogp * (onehot(y) - exp(l - lse)) -> bf16 [T, Vc]
-__global__ void dlogits_k(const float* __restrict__ logits, int Vc, int v0,
-                          const float* __restrict__ lse, const int32_t* __restrict__ tgt,
-                          const float* __restrict__ dlogp, uint16_t* __restrict__ out) {
-  const int64_t t = blockIdx.y;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= Vc) return;
-  const int y = tgt[t];
-  float g = 0.f;
-  if (y >= 0) {
-    const float p = expf(logits[t * Vc + i] - lse[t]);
-    g = dlogp[t] * (((v0 + i) == y ? 1.f : 0.f) - p);
-  }
-  out[t * Vc + i] = f32_to_bf16_bits(g);
-}
-// the same, eight columns per thread (Vc % 8 == 0, 16-byte aligned rows)
-__global__ void dlogits8_k(const float* __restrict__ logits, int Vc, int v0,
-                           const float* __restrict__ lse, const int32_t* __restrict__ tgt,
-                           const float* __restrict__ dlogp, uint16_t* __restrict__ out) {
-  const int64_t t = blockIdx.y;
-  const int i = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
-  if (i >= Vc) return;
-  const int y = tgt[t];
-  u32x4 o = {0u, 0u, 0u, 0u};
-  if (y >= 0) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(logits + t * Vc + i);
-    const f32x4 a = src[0], b = src[1];
-    const float l = lse[t], d = dlogp[t];
-    float g[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = expf((e < 4 ? a[e] : b[e - 4]) - l);
-      g[e] = d * (((v0 + i + e) == y ? 1.f : 0.f) - p);
+// Chunk pass of the LM head.  With m the running max before the chunk, M
+// the chunk max and m' = max(m, M): the chunk's sum of exp(l - m') is merged
+// into the running sum as sum * alpha + chunk sum with alpha = exp(m - m').
+// One block of 256 threads per row; the row is read twice (max, then the
+// exponentials), each thread in a fixed order, then fixed-order block sums.
+// ACC (the pass that keeps the backward's state) also writes alpha, which
+// rescales the expected-row accumulator, and p~ = bf16(exp(l - m')) [T, Vc]
+// for the accumulator GEMM; the sums are the same bits either way.
+template <bool ACC>
+__global__ void lse_chunk_k(const float* __restrict__ logits, int Vc, int v0,
+                            const int32_t* __restrict__ tgt, float* __restrict__ run_m,
+                            float* __restrict__ run_s, float* __restrict__ tlogit,
+                            float* __restrict__ alpha, uint16_t* __restrict__ pt, int first) {
+  __shared__ float red[16];
+  const int64_t t = blockIdx.x;
+  const float* x = logits + t * Vc;
+  uint16_t* o = ACC ? pt + t * Vc : nullptr;
+  const bool vec = Vc % 8 == 0;  // 16-byte rows of logits and of p~
+  float mx = -INFINITY;
+  if (vec) {
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
+    for (int i = threadIdx.x; i < Vc / 4; i += blockDim.x) {
+      const f32x4 v = x4[i];
+      mx = fmaxf(mx, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(g[2 * e], g[2 * e + 1]);
+  } else {
+    for (int i = threadIdx.x; i < Vc; i += blockDim.x) mx = fmaxf(mx, x[i]);
   }
-  *reinterpret_cast<u32x4*>(out + t * Vc + i) = o;
+  const float M = block_max(mx, red);
+  const float mo = first ? -INFINITY : run_m[t];
+  const float mn = fmaxf(mo, M);
+  float sum = 0.f;
+  if (vec) {
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
+    for (int i = threadIdx.x; i < Vc / 8; i += blockDim.x) {
+      const f32x4 a = x4[2 * i], b2 = x4[2 * i + 1];
+      float e[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        e[q] = expf((q < 4 ? a[q] : b2[q - 4]) - mn);
+        sum += e[q];
+      }
+      if constexpr (ACC) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(e[2 * q], e[2 * q + 1]);
+        reinterpret_cast<u32x4*>(o)[i] = w;
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < Vc; i += blockDim.x) {
+      const float e = expf(x[i] - mn);
+      sum += e;
+      if constexpr (ACC) o[i] = f32_to_bf16_bits(e);
+    }
+  }
+  const float S = block_sum(sum, red);
+  if (threadIdx.x == 0) {
+    const float al = first ? 0.f : expf(mo - mn);
+    run_s[t] = first ? S : run_s[t] * al + S;
+    run_m[t] = mn;
+    if constexpr (ACC) alpha[t] = al;
+    if (first) tlogit[t] = 0.f;
+    const int y = tgt[t];
+    if (y >= v0 && y < v0 + Vc) tlogit[t] = x[y - v0];
+  }
+}
+
+// x[t, :] *= f[t] over rows of n columns (n % 4 == 0, 16-byte aligned rows)
+__global__ void scale_rows_k(f32x4* __restrict__ x, const float* __restrict__ f, int n4,
+                             int64_t total4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total4) return;
+  x[i] = x[i] * f[i / n4];
+}
+
+__global__ void scale_rows1_k(float* __restrict__ x, const float* __restrict__ f, int n,
+                              int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < total) x[i] *= f[i / n];
+}
+
+// LM-head input gradient from the expected embedding row E (in place):
+// dn[t, :] = dlogp[t] * (W[y_t, :] - E[t, :]); a position without a target
+// has dlogp 0 and gets 0.
+__global__ void head_grad_k(const float* __restrict__ dlogp, const int32_t* __restrict__ tgt,
+                            const uint16_t* __restrict__ W, int H, int64_t n,
+                            float* __restrict__ E) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int64_t t = i / H;
+  const int y = tgt[t];
+  const float wy = y >= 0 ? bf16_to_f32(W[(int64_t)y * H + (i - t * H)]) : 0.f;
+  E[i] = dlogp[t] * (wy - E[i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -489,22 +504,34 @@ void lora_ext(const float* W, int64_t srow, int64_t sj, int R, int r, uint16_t* 
 }
 void lse_chunk(const float* logits, int T, int Vc, int v0, const int32_t* tgt, float* run_m,
                float* run_s, float* tlogit, int first, hipStream_t s) {
-  hipLaunchKernelGGL(lse_chunk_k, dim3(T), dim3(256), 0, s, logits, Vc, v0, tgt, run_m, run_s,
-                     tlogit, first);
+  hipLaunchKernelGGL(lse_chunk_k<false>, dim3(T), dim3(256), 0, s, logits, Vc, v0, tgt, run_m,
+                     run_s, tlogit, nullptr, nullptr, first);
 }
 void lse_final(const float* run_m, const float* run_s, const float* tlogit, const int32_t* tgt,
-               int T, float* logp, float* lse, hipStream_t s) {
+               int T, float* logp, float* lse, float* inv, hipStream_t s) {
   hipLaunchKernelGGL(lse_final_k, dim3(nb(T, 256)), dim3(256), 0, s, run_m, run_s, tlogit, tgt, T,
-                     logp, lse);
+                     logp, lse, inv);
 }
-void dlogits(const float* logits, int T, int Vc, int v0, const float* lse, const int32_t* tgt,
-             const float* dlogp, uint16_t* out, hipStream_t s) {
-  if (Vc % 8 == 0 && ((uintptr_t)logits & 15) == 0 && ((uintptr_t)out & 15) == 0)
-    hipLaunchKernelGGL(dlogits8_k, dim3(nb(Vc / 8, 256), T), dim3(256), 0, s, logits, Vc, v0, lse,
-                       tgt, dlogp, out);
-  else
-    hipLaunchKernelGGL(dlogits_k, dim3(nb(Vc, 256), T), dim3(256), 0, s, logits, Vc, v0, lse, tgt,
-                       dlogp, out);
+void lse_chunk_acc(const float* logits, int T, int Vc, int v0, const int32_t* tgt, float* run_m,
+                   float* run_s, float* tlogit, float* alpha, uint16_t* pt, int first,
+                   hipStream_t s) {
+  hipLaunchKernelGGL(lse_chunk_k<true>, dim3(T), dim3(256), 0, s, logits, Vc, v0, tgt, run_m,
+                     run_s, tlogit, alpha, pt, first);
+}
+void scale_rows(float* x, const float* f, int T, int n, hipStream_t s) {
+  if (n % 4 == 0 && ((uintptr_t)x & 15) == 0) {
+    const int64_t total4 = (int64_t)T * n / 4;
+    hipLaunchKernelGGL(scale_rows_k, dim3(nb(total4, 256)), dim3(256), 0, s,
+                       reinterpret_cast<f32x4*>(x), f, n / 4, total4);
+  } else {
+    const int64_t total = (int64_t)T * n;
+    hipLaunchKernelGGL(scale_rows1_k, dim3(nb(total, 256)), dim3(256), 0, s, x, f, n, total);
+  }
+}
+void head_grad(const float* dlogp, const int32_t* tgt, const uint16_t* W, int T, int H, float* E,
+               hipStream_t s) {
+  const int64_t n = (int64_t)T * H;
+  hipLaunchKernelGGL(head_grad_k, dim3(nb(n, 256)), dim3(256), 0, s, dlogp, tgt, W, H, n, E);
 }
 void sft_loss(const float* logp, const int32_t* tgt, int n, float* loss, float* dlogp,
               hipStream_t s) {

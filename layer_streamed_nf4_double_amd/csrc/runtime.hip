@@ -113,6 +113,8 @@ struct lsn_ctx {
   bool adapters_on = true;
   const float* lm_h = nullptr;
   int lm_T = 0;
+  bool lm_grad = false;  // the last lm_head_logprobs kept the expected-row accumulator
+  float* head_f = nullptr;  // per-row factors of the LM head [T]
 
   float levels[16];
   uint64_t loads = 0, bytes_h2d = 0;
@@ -371,6 +373,7 @@ static uint64_t carve(lsn_ctx* c, char* base) {
   c->run_s = (float*)P(T * 4);
   c->tlogit = (float*)P(T * 4);
   c->lse = (float*)P(T * 4);
+  c->head_f = (float*)P(T * 4);
   c->dnf = (float*)P(T * H * 4);
   return align_up(cv.off, 256);
 }
@@ -1232,37 +1235,32 @@ static lsn_status lm_logits_chunk(lsn_ctx* c, int v0, int Vc) {
   return LSN_OK;
 }
 
-lsn_status lsn_lm_head_logprobs(lsn_ctx* c, const float* h, const int32_t* targets, float* logp) {
+// Per vocabulary chunk: logits = n W_chunk^T, then the running max and sum
+// of exp over the vocabulary.  With want_grad_state the pass also keeps, in
+// dnf, the expected embedding row E[t] = sum_v softmax(l_t)_v W_v: each chunk
+// rescales the accumulator to the new running max (alpha) and adds
+// p~ W_chunk, and the end divides by the sum.  The backward then needs no
+// second pass over W_lm.
+lsn_status lsn_lm_head_logprobs(lsn_ctx* c, const float* h, const int32_t* targets, float* logp,
+                                int32_t want_grad_state) {
   CHECK_CTX(c);
   if (!h || !targets || !logp || c->T <= 0) return fail(c, LSN_ERR_INVALID, "bad lm_head arguments");
   if (!c->head_loaded) return fail(c, LSN_ERR_STATE, "head tables not loaded");
   const int T = c->T, V = c->cfg.vocab, H = c->cfg.hidden;
+  const bool acc = want_grad_state != 0;
   rmsnorm_fwd(h, c->final_norm, T, H, c->cfg.rms_eps, c->nf, c->rstdf, c->cs);
   for (int v0 = 0; v0 < V; v0 += c->vchunk) {
     const int Vc = std::min(c->vchunk, V - v0);
     lsn_status st = lm_logits_chunk(c, v0, Vc);
     if (st != LSN_OK) return st;
-    lse_chunk(c->logits, T, Vc, v0, targets, c->run_m, c->run_s, c->tlogit, v0 == 0, c->cs);
-  }
-  lse_final(c->run_m, c->run_s, c->tlogit, targets, T, logp, c->lse, c->cs);
-  c->lm_h = h;
-  c->lm_T = T;
-  return launch_check(c);
-}
-
-lsn_status lsn_lm_head_backward(lsn_ctx* c, const float* h, const int32_t* targets,
-                                const float* dlogp, float* dh) {
-  CHECK_CTX(c);
-  if (!h || !targets || !dlogp || !dh) return fail(c, LSN_ERR_INVALID, "bad lm_head arguments");
-  if (h != c->lm_h || c->lm_T != c->T)
-    return fail(c, LSN_ERR_STATE, "lm_head_backward must follow lm_head_logprobs on the same h");
-  const int T = c->T, V = c->cfg.vocab, H = c->cfg.hidden;
-  for (int v0 = 0; v0 < V; v0 += c->vchunk) {
-    const int Vc = std::min(c->vchunk, V - v0);
-    lsn_status st = lm_logits_chunk(c, v0, Vc);
-    if (st != LSN_OK) return st;
-    dlogits(c->logits, T, Vc, v0, c->lse, targets, dlogp, c->dlog, c->cs);
-    GemmParams p = base_params(c);  // dn += dlogits W_chunk
+    if (!acc) {
+      lse_chunk(c->logits, T, Vc, v0, targets, c->run_m, c->run_s, c->tlogit, v0 == 0, c->cs);
+      continue;
+    }
+    lse_chunk_acc(c->logits, T, Vc, v0, targets, c->run_m, c->run_s, c->tlogit, c->head_f,
+                  c->dlog, v0 == 0, c->cs);
+    if (v0 > 0) scale_rows(c->dnf, c->head_f, T, H, c->cs);
+    GemmParams p = base_params(c);  // E~ (+)= p~ W_chunk
     p.M = T; p.N = H; p.K = Vc;
     p.A = c->dlog; p.lda = Vc;
     p.B = c->lm_head + (int64_t)v0 * H; p.ldb = H;
@@ -1270,7 +1268,29 @@ lsn_status lsn_lm_head_backward(lsn_ctx* c, const float* h, const int32_t* targe
     p.cmode = (v0 == 0) ? C_F32 : C_F32_ACC;
     HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, 1));
   }
+  lse_final(c->run_m, c->run_s, c->tlogit, targets, T, logp, c->lse, acc ? c->head_f : nullptr,
+            c->cs);
+  if (acc) scale_rows(c->dnf, c->head_f, T, H, c->cs);
+  c->lm_h = h;
+  c->lm_T = T;
+  c->lm_grad = acc;
+  return launch_check(c);
+}
+
+// dn[t] = d loss / d n[t] = sum_v dlogits_v W_v with dlogits = dlogp_t
+// (onehot(y_t) - softmax) = dlogp_t (W[y_t] - E[t]); then the final RMSNorm
+// backward.
+lsn_status lsn_lm_head_backward(lsn_ctx* c, const float* h, const int32_t* targets,
+                                const float* dlogp, float* dh) {
+  CHECK_CTX(c);
+  if (!h || !targets || !dlogp || !dh) return fail(c, LSN_ERR_INVALID, "bad lm_head arguments");
+  if (h != c->lm_h || c->lm_T != c->T || !c->lm_grad)
+    return fail(c, LSN_ERR_STATE,
+                "lm_head_backward must follow lm_head_logprobs with want_grad_state on the same h");
+  const int T = c->T, H = c->cfg.hidden;
+  head_grad(dlogp, targets, c->lm_head, T, H, c->dnf, c->cs);
   rmsnorm_bwd(h, c->final_norm, c->rstdf, c->dnf, nullptr, T, H, dh, c->cs);
+  c->lm_grad = false;  // the accumulator is consumed
   return launch_check(c);
 }
 

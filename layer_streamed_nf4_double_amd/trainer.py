@@ -160,7 +160,7 @@ class LayerStreamedLoRA:
         loss tensor (loss[0]); logp of the step stays in self.logp."""
         T = n_seq * seq_len
         hL = self._forward(tokens, n_seq, seq_len, save=True)
-        L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T])
+        L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T], 1)
         L.lsn_sft_loss(self.ctx, self.logp[:T], targets, T, self.loss, self.dlogp[:T])
         L.lsn_lm_head_backward(self.ctx, hL, targets, self.dlogp[:T], self.dh[:T])
         self._backward(n_seq, seq_len)
@@ -190,14 +190,14 @@ class LayerStreamedLoRA:
         if fused:
             L.lsn_set_adapter_enabled(self.ctx, 1)
             h_ref, hL = self._forward_pair(tokens, 2, seq_len)
-            L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T])
+            L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T], 0)
         else:
             L.lsn_set_adapter_enabled(self.ctx, 0)
             h_ref = self._forward(tokens, 2, seq_len, save=False)
-            L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T])
+            L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T], 0)
             L.lsn_set_adapter_enabled(self.ctx, 1)
             hL = self._forward(tokens, 2, seq_len, save=True)
-        L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T])
+        L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T], 1)
         L.lsn_dpo_loss(self.ctx, self.logp[:T], self.logp_ref[:T], seq_len, prompt_len, beta,
                        self.loss, self.dlogp[:T])
         L.lsn_lm_head_backward(self.ctx, hL, targets, self.dlogp[:T], self.dh[:T])
@@ -218,11 +218,11 @@ class LayerStreamedLoRA:
         ref = None
         if k in (L.LSN_LOSS_DPO, L.LSN_LOSS_KTO):
             h_ref, hL = self._forward_pair(tokens, 2, seq_len)
-            L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T])
+            L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T], 0)
             ref = self.logp_ref[:T]
         else:
             hL = self._forward(tokens, 2, seq_len, save=True)
-        L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T])
+        L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T], 1)
         L.lsn_pref_loss(self.ctx, k, self.logp[:T], ref, seq_len, prompt_len, beta, param,
                         self.loss, self.dlogp[:T])
         L.lsn_lm_head_backward(self.ctx, hL, targets, self.dlogp[:T], self.dh[:T])

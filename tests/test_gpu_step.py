@@ -351,9 +351,10 @@ def test_auto_source_and_preflight(torch):
 def test_sft_large_vocab_multichunk_head_vs_oracle(torch):
     """One SFT step with a 70000-entry vocabulary at 2 x 152 tokens: the LM
     head runs three vocabulary chunks (32768, 32768, 4464 rows: online
-    log-sum-exp across chunks, dlogits per chunk, dh accumulated over chunks)
-    on the 256 x 256 bf16 logits kernel with a ragged row tile and a ragged
-    last column tile."""
+    log-sum-exp across chunks and the expected-row accumulator rescaled to
+    the running max chunk by chunk, then dh from it) on the 256 x 256 bf16
+    kernels with a ragged row tile and a ragged last column tile.  A head
+    backward after a logprobs pass that kept no accumulator is refused."""
     w = dict(SMALL256, n_layers=1, vocab=70000, n_seq=2, seq_len=152)
     tokens = synth.sft_tokens(w)
     say("[sft-vocab70000] oracle")
@@ -370,6 +371,13 @@ def test_sft_large_vocab_multichunk_head_vs_oracle(torch):
         oA, oB = o["grads"][0][p]
         assert_close(dA, oA, 5e-2, f"dA {p}")
         assert_close(dB, oB, 5e-2, f"dB {p}")
+    from layer_streamed_nf4_double_amd import _lib as L
+    T = w["n_seq"] * w["seq_len"]
+    _, tgt = _dev_tokens(torch, tokens)
+    hL = m.hs[w["n_layers"]][:T]
+    L.lsn_lm_head_logprobs(m.ctx, hL, tgt, m.logp[:T], 0)
+    with pytest.raises(L.LsnError):
+        L.lsn_lm_head_backward(m.ctx, hL, tgt, m.dlogp[:T], m.dh[:T])
 
 
 def test_sft_256_tokens_all_projections_vs_oracle(torch):
