@@ -27,6 +27,25 @@ struct LoraMM {
   float ext_scale = 1.f;
 };
 
+// The forward down-projections of all adapted projections of one group,
+// which share their input x: t_p = x A_p for p < n, in one launch.
+//   x bf16 [R, K] (row stride ldx); AT_p = bf16(A_p)^T [16, K] (rows j >= r
+//   zero; lora_at builds it); t_p fp32 [R, r] row-major;
+//   ext[row, 16 p + j] = bf16(ext_scale t_p(row, j)) for j < r, 0 for r <= j < 16.
+struct LoraDown {
+  const uint16_t* X = nullptr;
+  int64_t ldx = 0;
+  int R = 0, K = 0, r = 0, n = 0;
+  const uint16_t* AT[3] = {};
+  float* t[3] = {};
+  uint16_t* ext = nullptr;
+  int64_t ld_ext = 0;
+  float ext_scale = 1.f;
+};
+hipError_t lora_down(const LoraDown& a, hipStream_t s);
+// AT = bf16(A)^T [16, K] from A fp32 [K, r] row-major (rows j >= r zero)
+void lora_at(const float* A, int K, int r, uint16_t* AT, hipStream_t s);
+
 // floats of split-k scratch lora_mm wants for these sizes (0: no split)
 int64_t lora_mm_partial_floats(int R, int K);
 // partial may be null (then one pass over k)

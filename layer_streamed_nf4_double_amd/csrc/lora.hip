@@ -99,6 +99,92 @@ int64_t lora_mm_partial_floats(int R, int K) {
   return ns > 1 ? (int64_t)ns * R * 16 : 0;
 }
 
+// One workgroup of 16 waves owns 16 rows; wave w takes the 32-deep k steps
+// w, w + 16, ... for every adapter at once, so each x fragment (one 16-byte
+// load where rows are aligned) feeds n MFMAs; the waves' sums are added in
+// LDS in wave order.  No split-k: one launch per group.
+constexpr int DW = 16;  // waves per workgroup of lora_down_k
+
+template <bool VEC>
+__global__ __launch_bounds__(DW * 64) void lora_down_k(const LoraDown a) {
+  __shared__ float red[DW][3][16][17];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = blockIdx.x * 16;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const int row = row0 + lr;
+  const bool rin = row < a.R;
+  f32x4 acc[3] = {};
+  for (int k0 = wave * KSTEP; k0 < a.K; k0 += DW * KSTEP) {
+    bf16x8 xf;
+    if (VEC) {
+      // K % 8 == 0: a lane's eight columns are all inside the row or all past it
+      xf = (rin && k0 + lk < a.K)
+               ? *reinterpret_cast<const bf16x8*>(a.X + (int64_t)row * a.ldx + k0 + lk)
+               : bf16x8{};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = k0 + lk + i;
+        xf[i] = (bf16)((rin && k < a.K) ? bf16_to_f32(a.X[(int64_t)row * a.ldx + k]) : 0.f);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      if (q >= a.n) break;
+      bf16x8 wf;
+      if (VEC) {
+        wf = (k0 + lk < a.K) ? *reinterpret_cast<const bf16x8*>(a.AT[q] + (int64_t)lr * a.K + k0 + lk)
+                             : bf16x8{};
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int k = k0 + lk + i;
+          wf[i] = (bf16)(k < a.K ? bf16_to_f32(a.AT[q][(int64_t)lr * a.K + k]) : 0.f);
+        }
+      }
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, wf, acc[q], 0, 0, 0);
+    }
+  }
+  // lane holds column j = lane % 16, rows (lane / 16) * 4 + i
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][q][(lane >> 4) * 4 + i][lane & 15] = acc[q][i];
+  __syncthreads();
+  // thread -> (adapter q, row rr, column j)
+  const int q = threadIdx.x >> 8, rr = (threadIdx.x >> 4) & 15, j = threadIdx.x & 15;
+  const int orow = row0 + rr;
+  if (q >= a.n || orow >= a.R) return;
+  float v = 0.f;
+#pragma unroll
+  for (int w = 0; w < DW; ++w) v += red[w][q][rr][j];
+  if (j < a.r) a.t[q][(int64_t)orow * a.r + j] = v;
+  a.ext[(int64_t)orow * a.ld_ext + 16 * q + j] = (j < a.r) ? f32_to_bf16_bits(a.ext_scale * v) : 0;
+}
+
+__global__ void lora_at_k(const float* __restrict__ A, int K, int r, uint16_t* __restrict__ AT) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)16 * K) return;
+  const int j = (int)(i / K), k = (int)(i % K);
+  AT[i] = j < r ? f32_to_bf16_bits(A[(int64_t)k * r + j]) : 0;
+}
+
+void lora_at(const float* A, int K, int r, uint16_t* AT, hipStream_t s) {
+  const int64_t n = (int64_t)16 * K;
+  hipLaunchKernelGGL(lora_at_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, A, K, r, AT);
+}
+
+hipError_t lora_down(const LoraDown& a, hipStream_t s) {
+  if (a.R <= 0 || a.n <= 0) return hipSuccess;
+  if (a.n > 3 || a.r > 16) return hipErrorInvalidValue;
+  bool vec = a.K % 8 == 0 && a.ldx % 8 == 0 && ((uintptr_t)a.X & 15) == 0;
+  for (int q = 0; q < a.n; ++q) vec = vec && ((uintptr_t)a.AT[q] & 15) == 0;
+  const dim3 grid((a.R + 15) / 16);
+  if (vec) hipLaunchKernelGGL(lora_down_k<true>, grid, dim3(DW * 64), 0, s, a);
+  else hipLaunchKernelGGL(lora_down_k<false>, grid, dim3(DW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t lora_mm(const LoraMM& a, float* partial, int64_t partial_floats, hipStream_t s) {
   if (a.R <= 0) return hipSuccess;
   int ns, kc;

@@ -114,6 +114,16 @@ struct lsn_ctx {
   const float* lm_h = nullptr;
   int lm_T = 0;
   bool lm_grad = false;  // the last lm_head_logprobs kept the expected-row accumulator
+  // forward B extensions (bf16 block layout of B_p^T), one per layer and
+  // adapted group, valid while fext_ver matches lora_version (bumped by every
+  // adapter write)
+  uint16_t* fext = nullptr;
+  std::vector<int64_t> fext_off;
+  uint16_t* fat = nullptr;            // bf16(A_p)^T [16, K_p] per layer and adapter
+  std::vector<int64_t> fat_off;
+  std::vector<uint64_t> fext_ver;
+  uint64_t lora_version = 1;
+  const uint16_t* fwd_bext = nullptr;  // the extension of the group being launched
   float* head_f = nullptr;  // per-row factors of the LM head [T]
 
   float levels[16];
@@ -288,6 +298,17 @@ static void record_layout(lsn_ctx* c) {
   c->rec_bytes = align_up(off, REC_ALIGN);
 }
 
+struct Group {
+  int first, count;
+};
+static const Group G_QKV{LSN_Q, 3}, G_O{LSN_O, 1}, G_GU{LSN_GATE, 2}, G_D{LSN_DOWN, 1};
+
+static int64_t group_rows(const lsn_ctx* c, Group g) {
+  int64_t n = 0;
+  for (int p = g.first; p < g.first + g.count; ++p) n += c->N[p];
+  return n;
+}
+
 // Carves the workspace; with base == nullptr only measures.
 static uint64_t carve(lsn_ctx* c, char* base) {
   const lsn_config& g = c->cfg;
@@ -363,6 +384,31 @@ static uint64_t carve(lsn_ctx* c, char* base) {
   c->ext_rows = std::max<int64_t>({QKV, 2 * F, H, QD, F});
   c->aext = (uint16_t*)P(T * 48 * 2);
   c->bext = (uint16_t*)P(c->ext_rows * 48 * 2);
+  {
+    const Group groups[4] = {G_QKV, G_O, G_GU, G_D};
+    c->fext_off.assign((size_t)g.n_layers * 4, -1);
+    c->fext_ver.assign((size_t)g.n_layers * 4, 0);
+    uint64_t fe = 0;
+    for (int l = 0; l < g.n_layers; ++l)
+      for (int gi = 0; gi < 4; ++gi) {
+        int nad = 0;
+        for (int p = groups[gi].first; p < groups[gi].first + groups[gi].count; ++p)
+          nad += c->targeted(p);
+        if (!nad) continue;
+        c->fext_off[(size_t)l * 4 + gi] = (int64_t)fe;
+        fe += align_up((uint64_t)group_rows(c, groups[gi]) * 16 * nad, 128);
+      }
+    c->fext = (uint16_t*)P(std::max<uint64_t>(fe, 1) * 2);
+    c->fat_off.assign((size_t)g.n_layers * NPROJ, -1);
+    uint64_t fa = 0;
+    for (int l = 0; l < g.n_layers; ++l)
+      for (int p = 0; p < NPROJ; ++p)
+        if (c->targeted(p)) {
+          c->fat_off[(size_t)l * NPROJ + p] = (int64_t)fa;
+          fa += align_up((uint64_t)16 * c->K[p], 64);
+        }
+    c->fat = (uint16_t*)P(std::max<uint64_t>(fa, 1) * 2);
+  }
   // LM head
   const int64_t Vc = std::min<int64_t>(V, c->vchunk);
   c->nf = (uint16_t*)P(T * H * 2);
@@ -483,46 +529,51 @@ static GemmParams base_params(const lsn_ctx* c) {
 }
 
 // projections sharing one GEMM: q|k|v, o, gate|up, down
-struct Group {
-  int first, count;
-};
-static const Group G_QKV{LSN_Q, 3}, G_O{LSN_O, 1}, G_GU{LSN_GATE, 2}, G_D{LSN_DOWN, 1};
-
-static int64_t group_rows(const lsn_ctx* c, Group g) {
-  int64_t n = 0;
-  for (int p = g.first; p < g.first + g.count; ++p) n += c->N[p];
-  return n;
+static int group_index(Group g) {
+  return g.first == LSN_Q ? 0 : g.first == LSN_O ? 1 : g.first == LSN_GATE ? 2 : 3;
 }
 
-// Forward low-rank extension of a group: t_p = x A_p (kept in lt[p]),
-// aext = bf16(s t_p) per adapted slot, bext = block layout of B_p^T.
-// Returns kext (0 when no adapter applies).
+// Forward low-rank extension of a group: t_p = x A_p (kept in lt[p]) and
+// aext = bf16(s t_p) per adapted slot in one launch.  The bf16 copies it
+// reads (A_p^T, and the block layout of the B_p^T for the GEMM) are cached
+// per layer and rebuilt after adapter writes.
 static int lora_fwd_ext(lsn_ctx* c, int layer, Group g, const uint16_t* x, int64_t ldx, int T) {
+  c->fwd_bext = nullptr;
   if (!c->adapters_on) return 0;
   int nad = 0;
   for (int p = g.first; p < g.first + g.count; ++p) nad += c->targeted(p);
   if (!nad) return 0;
   const int r = c->cfg.lora_rank, kext = 16 * nad;
-  const float s = c->lora_scale();
-  const int64_t rows = group_rows(c, g);
-  // rows of one projection are zero in the other projections' slots
-  if (g.count > 1) fill_u32(c->bext, 0, rows * kext / 2, c->cs);
-  int slot = 0;
-  int64_t row0 = 0;
-  for (int p = g.first; p < g.first + g.count; ++p) {
-    if (c->targeted(p)) {
-      const int64_t K = c->K[p], N = c->N[p];
-      LoraMM m;  // t = x A, aext = bf16(s t)
-      m.X = x; m.ldx = ldx; m.R = T; m.K = (int)K;
-      m.W = c->A_of(layer, p); m.sk = r; m.sj = 1; m.r = r;
-      m.out = c->lt + (int64_t)p * T * 16; m.so_r = r; m.so_j = 1;
-      m.ext = c->aext + 16 * slot; m.ld_ext = kext; m.ext_scale = s;
-      (void)lora_mm(m, c->lpart, c->lpart_floats, c->cs);
-      lora_ext(c->B_of(layer, p), 1, N, (int)N, r, c->bext + row0 * kext, kext, 16 * slot, c->cs);
-      ++slot;
+  LoraDown d;
+  d.X = x; d.ldx = ldx; d.R = T; d.K = (int)c->K[g.first]; d.r = r;
+  d.ext = c->aext; d.ld_ext = kext; d.ext_scale = c->lora_scale();
+  const size_t ci = (size_t)layer * 4 + group_index(g);
+  uint16_t* be = c->fext + c->fext_off[ci];
+  if (c->fext_ver[ci] != c->lora_version) {  // rebuild the layer's bf16 copies
+    // rows of one projection are zero in the other projections' slots
+    if (g.count > 1) fill_u32(be, 0, group_rows(c, g) * kext / 2, c->cs);
+    int slot = 0;
+    int64_t row0 = 0;
+    for (int p = g.first; p < g.first + g.count; ++p) {
+      if (c->targeted(p)) {
+        lora_ext(c->B_of(layer, p), 1, c->N[p], (int)c->N[p], r, be + row0 * kext, kext,
+                 16 * slot, c->cs);
+        lora_at(c->A_of(layer, p), (int)c->K[p], r, c->fat + c->fat_off[(size_t)layer * NPROJ + p],
+                c->cs);
+        ++slot;
+      }
+      row0 += c->N[p];
     }
-    row0 += c->N[p];
+    c->fext_ver[ci] = c->lora_version;
   }
+  for (int p = g.first; p < g.first + g.count; ++p)
+    if (c->targeted(p)) {
+      d.AT[d.n] = c->fat + c->fat_off[(size_t)layer * NPROJ + p];
+      d.t[d.n] = c->lt + (int64_t)p * T * 16;
+      ++d.n;
+    }
+  (void)lora_down(d, c->cs);
+  c->fwd_bext = be;
   return kext;
 }
 
@@ -587,7 +638,7 @@ static hipError_t nf4_fwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const ui
   if (kext) {
     p.Aext = c->aext;
     p.ldae = kext;
-    p.Bext = c->bext;
+    p.Bext = c->fwd_bext;
     p.ldbe = kext;
     p.kext = kext;
   }
@@ -1113,6 +1164,7 @@ lsn_status lsn_set_lora(lsn_ctx* c, int32_t layer, int32_t proj, const float* A,
     return fail(c, LSN_ERR_INVALID, "no adapter at layer %d projection %d", layer, proj);
   const int r = c->cfg.lora_rank;
   HIPCHK(c, hipStreamSynchronize(c->cs));
+  ++c->lora_version;
   if (A) HIPCHK(c, hipMemcpy(c->A_of(layer, proj), A, (uint64_t)c->K[proj] * r * 4, hipMemcpyHostToDevice));
   if (B) HIPCHK(c, hipMemcpy(c->B_of(layer, proj), B, (uint64_t)r * c->N[proj] * 4, hipMemcpyHostToDevice));
   return LSN_OK;
@@ -1149,6 +1201,7 @@ lsn_status lsn_sgd_step(lsn_ctx* c, float lr) {
   CHECK_CTX(c);
   if (!std::isfinite(lr)) return fail(c, LSN_ERR_INVALID, "non-finite learning rate");
   if (c->lora_n) sgd(c->lora_p, c->lora_g, lr, (int64_t)c->lora_n, c->cs);
+  ++c->lora_version;
   return launch_check(c);
 }
 
