@@ -143,8 +143,9 @@ lsn_status lsn_config_record_bytes(const lsn_config* cfg, uint64_t* bytes);
 /* dev_ws: device, ws_bytes >= lsn_workspace_bytes (else LSN_ERR_NOFIT, the
  * pre-flight refusal of a run that will not fit: page "Soup: Fine-Tune an 8B
  * Model on a 4 GB GPU", "A Practical Quick Start").  hip_stream: the compute
- * stream (hipStream_t, may be 0).  The workspace stays owned by the caller and
- * must outlive the context. */
+ * stream (hipStream_t, may be 0).  The context's copy stream is created
+ * non-blocking, so it never synchronizes implicitly with the null stream.  The
+ * workspace stays owned by the caller and must outlive the context. */
 lsn_status lsn_create(const lsn_config* cfg, void* dev_ws, uint64_t ws_bytes, void* hip_stream,
                       lsn_ctx** out);
 void lsn_destroy(lsn_ctx* ctx);

@@ -435,10 +435,15 @@ static const uint8_t* rec_ptr(lsn_ctx* c, size_t idx) {
 static lsn_status copy_into_slot(lsn_ctx* c, int layer, int s) {
   uint8_t* dst = c->records + (uint64_t)s * c->rec_bytes;
   if (c->slot_used[s]) HIPCHK(c, hipStreamWaitEvent(c->copy, c->slot_free[s], 0));
+  // The host waits for the previous copy into this slot, so at most one
+  // copy per slot is queued.  With a whole step of copies queued the
+  // runtime's copy queue fills: hipMemcpyAsync then blocks the host for
+  // milliseconds and later copies reach the engine late.  Every dependency
+  // of the copy waited for is already enqueued.  (For the file source this
+  // also frees the slot's bounce buffer.)
+  if (c->copy_issued[s]) HIPCHK(c, hipEventSynchronize(c->copy_done[s]));
   const uint8_t* src;
   if (c->cfg.mode == LSN_STREAM_FILE) {
-    // the bounce buffer of this slot is free once its previous copy finished
-    if (c->copy_issued[s]) HIPCHK(c, hipEventSynchronize(c->copy_done[s]));
     uint64_t done = 0;
     const uint64_t off = (uint64_t)layer * c->rec_bytes;
     while (done < c->rec_bytes) {

@@ -12,6 +12,7 @@ the DPO loss and the backward of the policy pass.  By default both forwards
 run on one copy of each layer record (lsn_forward_layer_pair), so a DPO step
 streams the stack twice, like SFT, instead of three times.
 """
+import contextlib
 import os
 
 import numpy as np
@@ -82,6 +83,9 @@ class LayerStreamedLoRA:
         self.lora_targets = tuple(lora_targets)
         self.ws_bytes = L.lsn_workspace_bytes(self.cfg)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        # The caller's current stream by default.  When another stream is
+        # given, the step methods order it against the caller's current
+        # stream on entry and exit.
         self.stream = stream or torch.cuda.current_stream(self.device)
         self.ctx = L.lsn_create(self.cfg, self.ws, self.ws_bytes, self.stream.cuda_stream)
         T, H, nl = self.cfg.max_tokens, self.cfg.hidden, self.cfg.n_layers
@@ -96,8 +100,22 @@ class LayerStreamedLoRA:
 
     def close(self):
         if self.ctx:
+            self.stream.synchronize()
             L.lsn_destroy(self.ctx)
             self.ctx = None
+
+    @contextlib.contextmanager
+    def _ordered(self):
+        """Runs a step on the context's stream after the caller's pending
+        work, and makes the caller's stream wait for the step."""
+        cur = self.torch.cuda.current_stream(self.device)
+        if cur != self.stream:
+            self.stream.wait_stream(cur)
+        try:
+            yield
+        finally:
+            if cur != self.stream:
+                cur.wait_stream(self.stream)
 
     def __del__(self):
         try:
@@ -158,15 +176,16 @@ class LayerStreamedLoRA:
     def sft_step(self, tokens, targets, n_seq, seq_len, lr):
         """tokens, targets: device int32 [n_seq*seq_len].  Returns the device
         loss tensor (loss[0]); logp of the step stays in self.logp."""
-        T = n_seq * seq_len
-        hL = self._forward(tokens, n_seq, seq_len, save=True)
-        L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T], 1)
-        L.lsn_sft_loss(self.ctx, self.logp[:T], targets, T, self.loss, self.dlogp[:T])
-        L.lsn_lm_head_backward(self.ctx, hL, targets, self.dlogp[:T], self.dh[:T])
-        self._backward(n_seq, seq_len)
-        if lr is not None:
-            L.lsn_sgd_step(self.ctx, lr)
-        return self.loss
+        with self._ordered():
+            T = n_seq * seq_len
+            hL = self._forward(tokens, n_seq, seq_len, save=True)
+            L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T], 1)
+            L.lsn_sft_loss(self.ctx, self.logp[:T], targets, T, self.loss, self.dlogp[:T])
+            L.lsn_lm_head_backward(self.ctx, hL, targets, self.dlogp[:T], self.dh[:T])
+            self._backward(n_seq, seq_len)
+            if lr is not None:
+                L.lsn_sgd_step(self.ctx, lr)
+            return self.loss
 
     def _forward_pair(self, tokens, n_seq, seq_len):
         """Reference (adapter off) and policy forward sharing every layer
@@ -186,25 +205,26 @@ class LayerStreamedLoRA:
         loss[0..5] = loss, z, pc, pr, rc, rr.  fused: the reference forward
         runs on the same record copy as the policy forward (2L record loads
         per step instead of 3L); the results are the same bits."""
-        T = 2 * seq_len
-        if fused:
-            L.lsn_set_adapter_enabled(self.ctx, 1)
-            h_ref, hL = self._forward_pair(tokens, 2, seq_len)
-            L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T], 0)
-        else:
-            L.lsn_set_adapter_enabled(self.ctx, 0)
-            h_ref = self._forward(tokens, 2, seq_len, save=False)
-            L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T], 0)
-            L.lsn_set_adapter_enabled(self.ctx, 1)
-            hL = self._forward(tokens, 2, seq_len, save=True)
-        L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T], 1)
-        L.lsn_dpo_loss(self.ctx, self.logp[:T], self.logp_ref[:T], seq_len, prompt_len, beta,
-                       self.loss, self.dlogp[:T])
-        L.lsn_lm_head_backward(self.ctx, hL, targets, self.dlogp[:T], self.dh[:T])
-        self._backward(2, seq_len)
-        if lr is not None:
-            L.lsn_sgd_step(self.ctx, lr)
-        return self.loss
+        with self._ordered():
+            T = 2 * seq_len
+            if fused:
+                L.lsn_set_adapter_enabled(self.ctx, 1)
+                h_ref, hL = self._forward_pair(tokens, 2, seq_len)
+                L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T], 0)
+            else:
+                L.lsn_set_adapter_enabled(self.ctx, 0)
+                h_ref = self._forward(tokens, 2, seq_len, save=False)
+                L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T], 0)
+                L.lsn_set_adapter_enabled(self.ctx, 1)
+                hL = self._forward(tokens, 2, seq_len, save=True)
+            L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T], 1)
+            L.lsn_dpo_loss(self.ctx, self.logp[:T], self.logp_ref[:T], seq_len, prompt_len, beta,
+                           self.loss, self.dlogp[:T])
+            L.lsn_lm_head_backward(self.ctx, hL, targets, self.dlogp[:T], self.dh[:T])
+            self._backward(2, seq_len)
+            if lr is not None:
+                L.lsn_sgd_step(self.ctx, lr)
+            return self.loss
 
 
     def pref_step(self, kind, tokens, targets, seq_len, prompt_len, beta, param, lr):
@@ -212,24 +232,25 @@ class LayerStreamedLoRA:
         kto).  Losses with a reference (dpo, kto) run the adapter-off forward on
         the same record copies as the policy forward; reference-free ones
         (simpo, orpo) stream the stack once forward, like SFT."""
-        T = 2 * seq_len
-        k = PREF_LOSSES[kind]
-        L.lsn_set_adapter_enabled(self.ctx, 1)
-        ref = None
-        if k in (L.LSN_LOSS_DPO, L.LSN_LOSS_KTO):
-            h_ref, hL = self._forward_pair(tokens, 2, seq_len)
-            L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T], 0)
-            ref = self.logp_ref[:T]
-        else:
-            hL = self._forward(tokens, 2, seq_len, save=True)
-        L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T], 1)
-        L.lsn_pref_loss(self.ctx, k, self.logp[:T], ref, seq_len, prompt_len, beta, param,
-                        self.loss, self.dlogp[:T])
-        L.lsn_lm_head_backward(self.ctx, hL, targets, self.dlogp[:T], self.dh[:T])
-        self._backward(2, seq_len)
-        if lr is not None:
-            L.lsn_sgd_step(self.ctx, lr)
-        return self.loss
+        with self._ordered():
+            T = 2 * seq_len
+            k = PREF_LOSSES[kind]
+            L.lsn_set_adapter_enabled(self.ctx, 1)
+            ref = None
+            if k in (L.LSN_LOSS_DPO, L.LSN_LOSS_KTO):
+                h_ref, hL = self._forward_pair(tokens, 2, seq_len)
+                L.lsn_lm_head_logprobs(self.ctx, h_ref, targets, self.logp_ref[:T], 0)
+                ref = self.logp_ref[:T]
+            else:
+                hL = self._forward(tokens, 2, seq_len, save=True)
+            L.lsn_lm_head_logprobs(self.ctx, hL, targets, self.logp[:T], 1)
+            L.lsn_pref_loss(self.ctx, k, self.logp[:T], ref, seq_len, prompt_len, beta, param,
+                            self.loss, self.dlogp[:T])
+            L.lsn_lm_head_backward(self.ctx, hL, targets, self.dlogp[:T], self.dh[:T])
+            self._backward(2, seq_len)
+            if lr is not None:
+                L.lsn_sgd_step(self.ctx, lr)
+            return self.loss
 
 
 def sft_targets(tokens):
