@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--workload", default="llama3.1-8b-shaped")
     ap.add_argument("--mode", default="stream_host", choices=["stream_host", "resident"])
     ap.add_argument("--dpo-steps", type=int, default=5)
+    ap.add_argument("--file-steps", type=int, default=2,
+                    help="timed SFT steps with the base streamed from a store file (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the projection, dequant and resident measurements")
@@ -110,12 +112,13 @@ def quantized_layers(w):
             yield layer, codes, absmax, ones, ones
 
 
-def build_model(w, mode, max_tokens, max_seq_len, layers, head):
+def build_model(w, mode, max_tokens, max_seq_len, layers, head, store_path=None):
     import numpy as np
 
     import synth
     from layer_streamed_nf4_double_amd.trainer import LayerStreamedLoRA
-    m = LayerStreamedLoRA(w, mode, max_tokens=max_tokens, max_seq_len=max_seq_len)
+    m = LayerStreamedLoRA(w, mode, max_tokens=max_tokens, max_seq_len=max_seq_len,
+                          store_path=store_path)
     for layer, codes, absmax, g1, g2 in layers:
         m.load_layer(layer, codes, absmax, g1, g2)
     for layer in range(w["n_layers"]):
@@ -125,6 +128,98 @@ def build_model(w, mode, max_tokens, max_seq_len, layers, head):
     emb, lm, ones = head
     m.load_head(emb, lm, ones)
     return m
+
+
+def storage_read_bandwidth(path, request):
+    """Sequential O_DIRECT read of the whole file at path in requests of
+    `request` bytes (the record size, as the file source issues them) into a
+    page-aligned buffer: GB/s, or None when the file system refuses O_DIRECT."""
+    import mmap
+    try:
+        fd = os.open(path, os.O_RDONLY | os.O_DIRECT)
+    except OSError:
+        return None
+    buf = mmap.mmap(-1, request)
+    try:
+        done, t0 = 0, time.perf_counter()
+        while True:
+            n = os.preadv(fd, [buf], done)
+            if n <= 0:
+                break
+            done += n
+        dt = time.perf_counter() - t0
+    finally:
+        os.close(fd)
+        buf.close()
+    return done / dt / 1e9
+
+
+def mount_of(path):
+    """(device, file system type) of the mount holding path, from /proc/mounts."""
+    path = os.path.realpath(path)
+    best = ("?", "?", "")
+    try:
+        with open("/proc/mounts") as f:
+            for line in f:
+                dev, mnt, fstype = line.split()[:3]
+                if (path == mnt or path.startswith(mnt.rstrip("/") + "/")) and len(mnt) > len(best[2]):
+                    best = (dev, fstype, mnt)
+    except OSError:
+        pass
+    return best[0], best[1]
+
+
+def file_source_leg(torch, L, w, S, layers, head, tok, tgt, rec_bytes, steps):
+    """The SFT step with the base streamed from a store file on local storage
+    (records read with O_DIRECT into pinned bounce buffers, then copied to the
+    slots).  The roofline is the storage read rate, probed on the same file."""
+    import shutil
+    import tempfile
+    d = tempfile.mkdtemp(prefix="lsn_store_")
+    path = os.path.join(d, "store.bin")
+    try:
+        torch.cuda.reset_peak_memory_stats()
+        mf = build_model(w, "stream_file", S, S, layers, head, store_path=path)
+        direct = L.lsn_file_direct_io(mf.ctx)
+        fd = os.open(path, os.O_RDONLY)
+        os.fsync(fd)
+        os.close(fd)
+        # two passes: the virtual disk's backing store caches on its host side,
+        # so the second pass shows the rate the streamed steps see
+        probes = [storage_read_bandwidth(path, rec_bytes) for _ in range(2)]
+        disk = None if probes[0] is None else max(probes)
+        log(f"[bench] store file on {mount_of(path)}: O_DIRECT {direct}, "
+            f"probe reads {[p if p is None else round(p, 2) for p in probes]} GB/s")
+        mf.sft_step(tok, tgt, 1, S, 1e-4)
+        mf.sync()
+        l0, b0, _ = mf.stats()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            mf.sft_step(tok, tgt, 1, S, 1e-4)
+            torch.cuda.synchronize()
+            log(f"[bench] file source step {i + 1}/{steps}")
+        fdt = (time.perf_counter() - t0) / steps
+        l1, b1, _ = mf.stats()
+        fpeak = torch.cuda.max_memory_allocated()
+        floss = float(mf.loss[0].item())
+        mf.close()
+        del mf
+        torch.cuda.empty_cache()
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    gbps = (b1 - b0) / steps / fdt / 1e9
+    dev, fstype = mount_of(d)
+    out = {"tokens_per_s": round(S / fdt, 2), "ms_per_step": round(fdt * 1e3, 1),
+           "steps": steps, "loss": floss, "direct_io": bool(direct),
+           "storage": f"{dev} ({fstype})", "layer_loads_per_step": (l1 - l0) / steps,
+           "achieved_GBps": round(gbps, 2),
+           "bound": "storage read", "probe_read_GBps": None if disk is None else round(disk, 2),
+           "probe_passes_GBps": [p if p is None else round(p, 2) for p in probes],
+           "frac": None if not disk else round(gbps / disk, 4),
+           "pinned_host_bytes": 2 * int(rec_bytes), "peak_vram_bytes": int(fpeak)}
+    log(f"[bench] file source {fdt * 1e3:.0f} ms/step, {S / fdt:.1f} tok/s, {gbps:.2f} GB/s")
+    return out
 
 
 def link_bandwidth(torch, mb, reps=20):
@@ -419,7 +514,7 @@ def main():
         log(f"[bench] DPO {ddt * 1e3:.1f} ms/step, {2 * S / ddt:.1f} tok/s, loss {out[0]:.4f}")
 
     # ---- the same step with the base resident on the device (peak VRAM side by side) ----
-    resident = projection = None
+    resident = projection = file_src = None
     if not args.no_extras:
         if args.mode == "stream_host":
             torch.cuda.reset_peak_memory_stats()
@@ -441,6 +536,9 @@ def main():
             torch.cuda.empty_cache()
             log(f"[bench] resident SFT {rdt * 1e3:.1f} ms/step, peak "
                 f"{resident['peak_vram_bytes'] / 1e9:.2f} GB")
+        if args.mode == "stream_host" and args.file_steps > 0:
+            file_src = file_source_leg(torch, L, w, S, layers, head, tok, tgt, rec_bytes,
+                                       args.file_steps)
         projection = projection_kernels(torch)
         log(f"[bench] projection fwd {projection['fwd']['us']} us, bwd "
             f"{projection['bwd_dx_da_db']['us']} us, dequant {projection['dequant_bf16']['us']} us")
@@ -467,7 +565,7 @@ def main():
             "compute_utilization": {"flops_per_step": step_flops(w, S, 1),
                                     "frac": round(step_flops(w, S, 1) / dt / 1e12
                                                   / MFMA_BF16_PEAK_TFLOPS, 4)},
-            "dpo": dpo, "resident": resident, "projection": projection,
+            "dpo": dpo, "resident": resident, "file_source": file_src, "projection": projection,
             "env": environment(torch, w, rec_bytes), "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 

@@ -153,6 +153,12 @@ const char* lsn_last_error(const lsn_ctx* ctx);
 lsn_status lsn_sync(lsn_ctx* ctx);
 /* bytes of one layer record (NF4 codes + absmax + norm gains), 4 KiB aligned */
 lsn_status lsn_record_bytes(const lsn_ctx* ctx, uint64_t* bytes);
+/* *direct = 1 when the file source reads its records with O_DIRECT (around
+ * the page cache, so each streamed step reads the storage device), 0 when the
+ * file system refused O_DIRECT and reads are buffered, or when the context
+ * has no file source (page "Soup: Fine-Tune an 8B Model on a 4 GB GPU", "The
+ * Core Idea: Layer Streaming": the base may stream from NVMe). */
+lsn_status lsn_file_direct_io(const lsn_ctx* ctx, int32_t* direct);
 
 /* ---------------------------------------------------------------------------
  * Frozen base (page "Soup: Fine-Tune an 8B Model on a 4 GB GPU", "The Core

@@ -63,6 +63,7 @@ _SIGS = {
     "lsn_last_error": [_P],
     "lsn_sync": [_P],
     "lsn_record_bytes": [_P, ctypes.POINTER(_U64)],
+    "lsn_file_direct_io": [_P, ctypes.POINTER(_I32)],
     "lsn_load_layer_nf4": [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _P],
     "lsn_load_head": [_P, _P, _P, _P],
     "lsn_set_lora": [_P, _I32, _I32, _P, _P],
@@ -211,6 +212,12 @@ def lsn_record_bytes(ctx):
     b = _U64(0)
     _check(_lib.lsn_record_bytes(ctx, ctypes.byref(b)), ctx, "lsn_record_bytes")
     return b.value
+
+
+def lsn_file_direct_io(ctx):
+    d = _I32(0)
+    _check(_lib.lsn_file_direct_io(ctx, ctypes.byref(d)), ctx, "lsn_file_direct_io")
+    return bool(d.value)
 
 
 def lsn_load_layer_nf4(ctx, layer, codes, absmax, attn_norm_bf16, mlp_norm_bf16):

@@ -24,10 +24,14 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+#include <sys/mman.h>
 #include <unistd.h>
 
 #include <algorithm>
+#include <condition_variable>
+#include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "../../include/lsn.h"
@@ -88,7 +92,23 @@ struct lsn_ctx {
   // host store
   uint8_t* store = nullptr;  // pinned, n_layers records (host / resident modes)
   uint8_t* bounce[2] = {nullptr, nullptr};  // pinned bounce buffers (file mode)
-  int fd = -1;
+  int fd = -1;   // file mode: the store file, buffered (writes; reads without O_DIRECT)
+  int dfd = -1;  // file mode: the same file opened O_DIRECT for the record reads
+  // File mode: a reader thread fills two page-aligned staging buffers, each
+  // tagged with the layer it holds.  The host thread takes a staged record,
+  // asks for the next record of the pass in the other buffer, and copies the
+  // staged one into the slot's pinned bounce buffer meanwhile.
+  struct Reader {
+    std::thread th;
+    std::mutex mu;
+    std::condition_variable cv;
+    uint8_t* buf[2] = {nullptr, nullptr};
+    int layer[2] = {-1, -1};  // record held or being read (-1: none)
+    bool ready[2] = {false, false};
+    int err[2] = {0, 0};      // errno of a failed read (EIO for a short file)
+    int req = -1;             // buffer the thread fills next (-1: none)
+    bool quit = false;
+  } rd;
   std::vector<char> loaded;
 
   // device regions
@@ -432,7 +452,103 @@ static const uint8_t* rec_ptr(lsn_ctx* c, size_t idx) {
   return c->records + (uint64_t)c->slot_of[idx] * c->rec_bytes;
 }
 
-static lsn_status copy_into_slot(lsn_ctx* c, int layer, int s) {
+// dst = src for n bytes, split over a few threads (host memory to pinned
+// host memory; one thread moves ~10 GB/s, a record is ~120 MB at 8B).
+static void parallel_copy(uint8_t* dst, const uint8_t* src, uint64_t n) {
+  constexpr int NT = 8;
+  const uint64_t part = (n / NT + 4095) & ~(uint64_t)4095;
+  std::thread th[NT - 1];
+  int started = 0;
+  for (int i = 1; i < NT; ++i) {
+    const uint64_t b = (uint64_t)i * part;
+    if (b >= n) break;
+    const uint64_t len = std::min(part, n - b);
+    th[started++] = std::thread([=] { memcpy(dst + b, src + b, len); });
+  }
+  memcpy(dst, src, std::min(part, n));
+  for (int i = 0; i < started; ++i) th[i].join();
+}
+
+static int read_record(const lsn_ctx* c, uint8_t* dst, int layer) {
+  const int fd = c->dfd >= 0 ? c->dfd : c->fd;
+  const uint64_t off = (uint64_t)layer * c->rec_bytes;
+  uint64_t done = 0;
+  while (done < c->rec_bytes) {
+    const ssize_t got = pread(fd, dst + done, c->rec_bytes - done, off + done);
+    if (got < 0) return errno ? errno : EIO;
+    if (got == 0) return EIO;
+    done += (uint64_t)got;
+  }
+  return 0;
+}
+
+static void reader_main(lsn_ctx* c) {
+  lsn_ctx::Reader& r = c->rd;
+  std::unique_lock<std::mutex> lk(r.mu);
+  for (;;) {
+    r.cv.wait(lk, [&] { return r.quit || r.req >= 0; });
+    if (r.quit) return;
+    const int i = r.req, layer = r.layer[i];
+    r.req = -1;
+    lk.unlock();
+    const int e = read_record(c, r.buf[i], layer);
+    lk.lock();
+    r.err[i] = e;
+    r.ready[i] = true;
+    r.cv.notify_all();
+  }
+}
+
+// Waits until the reader has nothing queued or in flight.
+static void reader_idle(lsn_ctx::Reader& r, std::unique_lock<std::mutex>& lk) {
+  r.cv.wait(lk, [&] {
+    return r.req < 0 && (r.layer[0] < 0 || r.ready[0]) && (r.layer[1] < 0 || r.ready[1]);
+  });
+}
+
+// Staging buffer holding the record of `layer`, read now if it is neither
+// staged nor on its way; then the next record `next` (-1: none) is queued
+// into the other buffer.  Returns -1 after a failed read (errno in *err).
+static int reader_take(lsn_ctx* c, int layer, int next, int* err) {
+  lsn_ctx::Reader& r = c->rd;
+  std::unique_lock<std::mutex> lk(r.mu);
+  int i = r.layer[0] == layer ? 0 : r.layer[1] == layer ? 1 : -1;
+  if (i < 0 || (r.ready[i] && r.err[i])) {
+    reader_idle(r, lk);
+    i = r.layer[0] == next ? 1 : 0;  // keep a staged `next`
+    r.layer[i] = layer;
+    r.ready[i] = false;
+    r.req = i;
+    r.cv.notify_all();
+  }
+  r.cv.wait(lk, [&] { return r.ready[i]; });
+  if (r.err[i]) {
+    *err = r.err[i];
+    r.layer[i] = -1;
+    return -1;
+  }
+  const int j = 1 - i;
+  if (next >= 0 && next != layer && r.layer[j] != next) {
+    reader_idle(r, lk);
+    r.layer[j] = next;
+    r.ready[j] = false;
+    r.req = j;
+    r.cv.notify_all();
+  }
+  return i;
+}
+
+// A rewritten record must not be served from a staging buffer.
+static void reader_forget(lsn_ctx* c, int layer) {
+  lsn_ctx::Reader& r = c->rd;
+  if (!r.th.joinable()) return;
+  std::unique_lock<std::mutex> lk(r.mu);
+  reader_idle(r, lk);
+  for (int i = 0; i < 2; ++i)
+    if (r.layer[i] == layer) r.layer[i] = -1;
+}
+
+static lsn_status copy_into_slot(lsn_ctx* c, int layer, int s, int next) {
   uint8_t* dst = c->records + (uint64_t)s * c->rec_bytes;
   if (c->slot_used[s]) HIPCHK(c, hipStreamWaitEvent(c->copy, c->slot_free[s], 0));
   // The host waits for the previous copy into this slot, so at most one
@@ -444,15 +560,15 @@ static lsn_status copy_into_slot(lsn_ctx* c, int layer, int s) {
   if (c->copy_issued[s]) HIPCHK(c, hipEventSynchronize(c->copy_done[s]));
   const uint8_t* src;
   if (c->cfg.mode == LSN_STREAM_FILE) {
-    uint64_t done = 0;
-    const uint64_t off = (uint64_t)layer * c->rec_bytes;
-    while (done < c->rec_bytes) {
-      const ssize_t got = pread(c->fd, c->bounce[s] + done, c->rec_bytes - done, off + done);
-      if (got <= 0)
-        return fail(c, LSN_ERR_IO, "read of layer %d record failed: %s", layer,
-                    got == 0 ? "unexpected end of file" : strerror(errno));
-      done += (uint64_t)got;
-    }
+    // O_DIRECT cannot target the pinned bounce buffers (the kernel cannot
+    // pin driver-mapped pages for direct I/O), so reads land in ordinary
+    // page-aligned staging buffers and are copied over by several threads
+    // while the reader fetches the next record.
+    int err = 0;
+    const int i = reader_take(c, layer, next, &err);
+    if (i < 0)
+      return fail(c, LSN_ERR_IO, "read of layer %d record failed: %s", layer, strerror(err));
+    parallel_copy(c->bounce[s], c->rd.buf[i], c->rec_bytes);
     src = c->bounce[s];
   } else {
     src = c->store + (uint64_t)layer * c->rec_bytes;
@@ -490,7 +606,13 @@ static lsn_status ensure_loads(lsn_ctx* c) {
         if (!needed) s = q;
       }
       if (s < 0) return fail(c, LSN_ERR_STATE, "scheduler found no free slot");
-      lsn_status st = copy_into_slot(c, layer, s);
+      // the record after this one in the pass, for the file reader's read-ahead
+      int next = -1;
+      if (i + 1 < c->order.size()) {
+        next = c->order[i + 1];
+        if (c->slot_layer[0] == next || c->slot_layer[1] == next) next = -1;
+      }
+      lsn_status st = copy_into_slot(c, layer, s, next);
       if (st != LSN_OK) return st;
     }
     c->slot_of[i] = s;
@@ -1053,6 +1175,18 @@ lsn_status lsn_create(const lsn_config* cfg, void* dev_ws, uint64_t ws_bytes, vo
   if (cfg->mode == LSN_STREAM_FILE) {
     c->fd = open(c->store_path.c_str(), O_RDWR | O_CREAT, 0644);
     if (c->fd < 0) return cleanup(LSN_ERR_IO);
+    // Record reads bypass the page cache, so a step reads the device and a
+    // store larger than host memory streams without evicting everything
+    // else.  Records are 4 KiB multiples at 4 KiB offsets and the bounce
+    // buffers are page aligned, as O_DIRECT asks.  A file system without
+    // O_DIRECT (tmpfs) falls back to buffered reads.
+    c->dfd = open(c->store_path.c_str(), O_RDONLY | O_DIRECT);
+    for (int i = 0; i < 2; ++i) {
+      void* m = mmap(nullptr, c->rec_bytes, PROT_READ | PROT_WRITE, MAP_PRIVATE | MAP_ANONYMOUS, -1, 0);
+      if (m == MAP_FAILED) return cleanup(LSN_ERR_IO);
+      c->rd.buf[i] = (uint8_t*)m;
+    }
+    c->rd.th = std::thread(reader_main, c);
     for (int i = 0; i < 2; ++i)
       if (hipHostMalloc((void**)&c->bounce[i], c->rec_bytes, hipHostMallocDefault) != hipSuccess)
         return cleanup(LSN_ERR_HIP);
@@ -1083,6 +1217,17 @@ void lsn_destroy(lsn_ctx* c) {
   for (hipEvent_t e : c->evpool) (void)hipEventDestroy(e);
   if (c->copy) (void)hipStreamDestroy(c->copy);
   if (c->store) (void)hipHostFree(c->store);
+  if (c->rd.th.joinable()) {
+    {
+      std::lock_guard<std::mutex> g(c->rd.mu);
+      c->rd.quit = true;
+    }
+    c->rd.cv.notify_all();
+    c->rd.th.join();
+  }
+  for (uint8_t* b : c->rd.buf)
+    if (b) munmap(b, c->rec_bytes);
+  if (c->dfd >= 0) close(c->dfd);
   if (c->fd >= 0) close(c->fd);
   delete c;
 }
@@ -1101,6 +1246,12 @@ lsn_status lsn_sync(lsn_ctx* c) {
 lsn_status lsn_record_bytes(const lsn_ctx* c, uint64_t* bytes) {
   if (!c || !bytes) return LSN_ERR_INVALID;
   *bytes = c->rec_bytes;
+  return LSN_OK;
+}
+
+lsn_status lsn_file_direct_io(const lsn_ctx* c, int32_t* direct) {
+  if (!c || !direct) return LSN_ERR_INVALID;
+  *direct = c->dfd >= 0 ? 1 : 0;
   return LSN_OK;
 }
 
@@ -1142,9 +1293,10 @@ lsn_status lsn_load_layer_nf4(lsn_ctx* c, int32_t layer, const uint8_t* const* c
                              hipMemcpyHostToDevice, c->cs));
     HIPCHK(c, hipStreamSynchronize(c->cs));
   }
-  // a slot holding an older copy of this layer is stale now
+  // a slot or staging buffer holding an older copy of this layer is stale now
   for (int s = 0; s < 2; ++s)
     if (c->slot_layer[s] == layer) c->slot_layer[s] = -1;
+  reader_forget(c, layer);
   c->loaded[layer] = 1;
   return LSN_OK;
 }

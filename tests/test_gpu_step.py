@@ -158,6 +158,8 @@ def test_streamed_equals_resident_bitwise(torch, n_layers):
     st = gpu_model(w, "stream_host", b_zero=False, max_tokens=128)
     b = _two_step_record(torch, st, w, tokens)
     loads, nbytes, _ = st.stats()
+    from layer_streamed_nf4_double_amd import _lib as L
+    assert not L.lsn_file_direct_io(st.ctx)  # no file source
     st.close()
     _assert_bit_identical(a, b)
     # forward copies all L records, backward reuses the last two; the next
@@ -169,6 +171,7 @@ def test_streamed_equals_resident_bitwise(torch, n_layers):
         fm = gpu_model(w, "stream_file", b_zero=False, max_tokens=128,
                        store_path=os.path.join(d, "store.bin"))
         c = _two_step_record(torch, fm, w, tokens)
+        say(f"[stream==resident] file source reads with O_DIRECT: {L.lsn_file_direct_io(fm.ctx)}")
         fm.close()
     _assert_bit_identical(a, c)
 
