@@ -176,6 +176,45 @@ def test_streamed_equals_resident_bitwise(torch, n_layers):
     _assert_bit_identical(a, c)
 
 
+def _load_layer_from(m, w, layer, src_layer):
+    """Loads the record built from layer src_layer's seeded weights as layer."""
+    from layer_streamed_nf4_double_amd import _lib as L
+    ones = np.full(w["hidden"], 0x3F80, np.uint16)
+    codes, absmax = [], []
+    for p in synth.PROJ:
+        c, a = L.lsn_nf4_quantize(synth.layer_weights_f32(w, src_layer, p))
+        codes.append(c)
+        absmax.append(a)
+    m.load_layer(layer, codes, absmax, ones, ones)
+
+
+@pytest.mark.parametrize("mode", ["resident", "stream_host", "stream_file"])
+def test_reloaded_layer_record_takes_effect(torch, mode, tmp_path):
+    """A layer record rewritten between steps is what the next step uses.
+    After a streamed step, layer 0 still sits in a device slot (the next
+    forward would reuse it), and with the file source its record also sits
+    in the reader's staging buffers; neither old copy may be served.  The
+    step after the rewrite equals, bitwise, the step of a model built with
+    the new record from the start."""
+    w = dict(TINY, n_layers=4)
+    tokens = synth.tokens((2, 64), w["vocab"], 91)
+    store = (lambda n: str(tmp_path / f"{n}.bin")) if mode == "stream_file" else (lambda n: None)
+    say(f"[reload] {mode}")
+    m = gpu_model(w, mode, b_zero=False, max_tokens=128, store_path=store("a"))
+    _, logp0 = _run_sft(torch, m, tokens, lr=None)
+    _load_layer_from(m, w, 0, 3)
+    loss_a, logp_a = _run_sft(torch, m, tokens, lr=None)
+    ga = _grads(m, w)
+    m.close()
+    f = gpu_model(w, mode, b_zero=False, max_tokens=128, store_path=store("b"))
+    _load_layer_from(f, w, 0, 3)
+    loss_b, logp_b = _run_sft(torch, f, tokens, lr=None)
+    gb = _grads(f, w)
+    f.close()
+    assert not np.array_equal(_bits(logp0), _bits(logp_a)), "the new record changed nothing"
+    _assert_bit_identical([(np.float32(loss_a), logp_a, ga)], [(np.float32(loss_b), logp_b, gb)])
+
+
 def test_dpo_tiny(torch):
     w = dict(TINY)
     S, P, beta = 64, 16, 0.1
