@@ -46,6 +46,55 @@ hipError_t lora_down(const LoraDown& a, hipStream_t s);
 // AT = bf16(A)^T [16, K] from A fp32 [K, r] row-major (rows j >= r zero)
 void lora_at(const float* A, int K, int r, uint16_t* AT, hipStream_t s);
 
+// u_p = dy_p B_p^T for the n adapted projections of one group, in one launch
+// (the first step of the branch's backward):
+//   dy_p = dy + col0[p] (elements), fp32 or bf16 rows of stride lddy;
+//   B_p fp32 [r, N_p];
+//   u_p fp32 [R, r] row-major; ext[row, 16 p + j] = bf16(ext_scale u_p(row, j))
+//   for j < r and 0 for r <= j < 16.
+// Needs N_p % 32 == 0 and 16-byte aligned rows (lora_u_ok).  partial
+// (may be null): room for the column-split sums, n * S * R * 16 floats with
+// S <= 8 chosen to fit; they are added in a fixed order.
+struct LoraU {
+  const void* dy = nullptr;
+  int dy_f32 = 1;
+  int64_t lddy = 0;
+  int R = 0, r = 0, n = 0;
+  int64_t col0[3] = {};
+  int N[3] = {};
+  const float* B[3] = {};
+  float* u[3] = {};
+  uint16_t* ext = nullptr;
+  int64_t ld_ext = 0;
+  float ext_scale = 1.f;
+};
+bool lora_u_ok(const LoraU& a);
+hipError_t lora_u(const LoraU& a, float* partial, int64_t partial_floats, hipStream_t s);
+
+// Gradients of the adapters as reductions over the tokens m < R:
+//   out_z(c, j) (+)= scale * sum_m Y(m, c) Z_z(m, j)     c < C, j < r
+// for the nz pairs (Z_z, out_z) of each job, which share the job's Y (fp32 or
+// bf16, Y(m, c) = Y[m*ldy + c]).  dA_p += s x^T u_p is one job whose Y is the
+// group input x (one pass over x for every adapter of the group); dB_p +=
+// s t_p^T dy_p is one job per adapter.  Z_z(m, j) = Z_z[m*ldz + j] (fp32);
+// out_z(c, j) at out_z[c*so_c + j*so_j].  No scratch.
+struct LoraTGradJob {
+  const void* Y = nullptr;
+  int C = 0, nz = 0;
+  int64_t so_c = 0, so_j = 0;
+  const float* Z[3] = {};
+  int64_t ldz[3] = {};
+  float* out[3] = {};
+};
+struct LoraTGrad {
+  int R = 0, r = 0, y_f32 = 0, njobs = 0;
+  int64_t ldy = 0;
+  float scale = 1.f;
+  int accumulate = 1;
+  LoraTGradJob job[3];
+};
+hipError_t lora_tgrad(const LoraTGrad& a, hipStream_t s);
+
 // floats of split-k scratch lora_mm wants for these sizes (0: no split)
 int64_t lora_mm_partial_floats(int R, int K);
 // partial may be null (then one pass over k)

@@ -185,6 +185,267 @@ hipError_t lora_down(const LoraDown& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// u_p = dy_p B_p^T.  One workgroup of UW waves owns 16 rows of one adapter
+// and one of S column ranges; wave w takes the 32-wide column steps w,
+// w + UW, ... of its range, each as two 16-byte loads of dy (one for bf16)
+// and two of B per lane; the waves' sums are added in LDS in wave order.
+// With S > 1 the ranges' sums go to a buffer and lora_u_reduce_k adds them
+// in range order.
+constexpr int UW = 8;  // waves per workgroup of lora_u_k
+
+struct USplit {
+  int S = 1, cols = 0;   // column ranges per adapter and their width (multiple of 32)
+  float* part = nullptr;  // [n][S][R][16]
+};
+
+template <bool DF32>
+__global__ __launch_bounds__(UW * 64) void lora_u_k(const LoraU a, const USplit sp) {
+  __shared__ float red[UW][16][17];
+  const int q = blockIdx.y, rs = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = blockIdx.x * 16;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const bool rin = row0 + lr < a.R, jin = lr < a.r;
+  const int N = a.N[q];
+  const int nb = rs * sp.cols, ne = min(N, nb + sp.cols);
+  const int64_t yo = a.col0[q] + (int64_t)(rin ? row0 + lr : 0) * a.lddy + lk;
+  const float* B = a.B[q] + (int64_t)(jin ? lr : 0) * N + lk;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int n0 = nb + wave * 32; n0 < ne; n0 += UW * 32) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 af, bw;
+    if constexpr (DF32) {
+      const float* dy = reinterpret_cast<const float*>(a.dy) + yo + n0;
+      const f32x4 x0 = rin ? *reinterpret_cast<const f32x4*>(dy) : zero;
+      const f32x4 x1 = rin ? *reinterpret_cast<const f32x4*>(dy + 4) : zero;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        af[i] = (bf16)x0[i];
+        af[i + 4] = (bf16)x1[i];
+      }
+    } else {
+      const uint16_t* dy = reinterpret_cast<const uint16_t*>(a.dy) + yo + n0;
+      af = rin ? *reinterpret_cast<const bf16x8*>(dy) : bf16x8{};
+    }
+    const f32x4 b0 = jin ? *reinterpret_cast<const f32x4*>(B + n0) : zero;
+    const f32x4 b1 = jin ? *reinterpret_cast<const f32x4*>(B + n0 + 4) : zero;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bw[i] = (bf16)b0[i];
+      bw[i + 4] = (bf16)b1[i];
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bw, acc, 0, 0, 0);
+  }
+  // lane holds column j = lane % 16, rows (lane / 16) * 4 + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][(lane >> 4) * 4 + i][lane & 15] = acc[i];
+  __syncthreads();
+  if (threadIdx.x >= 256) return;
+  const int rr = threadIdx.x >> 4, j = threadIdx.x & 15, row = row0 + rr;
+  float v = 0.f;
+#pragma unroll
+  for (int w = 0; w < UW; ++w) v += red[w][rr][j];
+  if (row >= a.R) return;
+  if (sp.S > 1) {
+    sp.part[(((int64_t)q * sp.S + rs) * a.R + row) * 16 + j] = v;
+    return;
+  }
+  if (j < a.r) a.u[q][(int64_t)row * a.r + j] = v;
+  if (a.ext)
+    a.ext[(int64_t)row * a.ld_ext + 16 * q + j] = j < a.r ? f32_to_bf16_bits(a.ext_scale * v) : 0;
+}
+
+__global__ void lora_u_reduce_k(const LoraU a, const USplit sp) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)a.n * a.R * 16) return;
+  const int q = (int)(i / ((int64_t)a.R * 16));
+  const int row = (int)((i >> 4) % a.R), j = (int)(i & 15);
+  float v = 0.f;
+  for (int s = 0; s < sp.S; ++s) v += sp.part[(((int64_t)q * sp.S + s) * a.R + row) * 16 + j];
+  if (j < a.r) a.u[q][(int64_t)row * a.r + j] = v;
+  if (a.ext)
+    a.ext[(int64_t)row * a.ld_ext + 16 * q + j] = j < a.r ? f32_to_bf16_bits(a.ext_scale * v) : 0;
+}
+
+static bool al16(const void* q) { return ((uintptr_t)q & 15) == 0; }
+
+bool lora_u_ok(const LoraU& a) {
+  const int v = a.dy_f32 ? 4 : 8;  // elements per 16 bytes
+  if (a.n < 1 || a.n > 3 || a.r > 16 || a.lddy % v != 0 || !al16(a.dy)) return false;
+  for (int q = 0; q < a.n; ++q)
+    if (a.N[q] % 32 != 0 || a.col0[q] % v != 0 || !al16(a.B[q])) return false;
+  return true;
+}
+
+hipError_t lora_u(const LoraU& a, float* partial, int64_t partial_floats, hipStream_t s) {
+  if (a.R <= 0 || a.n <= 0) return hipSuccess;
+  if (!lora_u_ok(a)) return hipErrorInvalidValue;
+  // column ranges of >= 512 so that ~256 workgroups stream dy (one range
+  // when the buffer is missing or too small)
+  int nmax = 0;
+  for (int q = 0; q < a.n; ++q) nmax = std::max(nmax, a.N[q]);
+  const int rb = (a.R + 15) / 16;
+  USplit sp;
+  sp.S = std::max(1, std::min({8, nmax / 512, 256 / std::max(1, rb * a.n)}));
+  while (sp.S > 1 && (!partial || (int64_t)a.n * sp.S * a.R * 16 > partial_floats)) --sp.S;
+  sp.cols = ((nmax + sp.S - 1) / sp.S + 31) / 32 * 32;
+  sp.part = partial;
+  const dim3 grid(rb, a.n, sp.S);
+  if (a.dy_f32) hipLaunchKernelGGL(lora_u_k<true>, grid, dim3(UW * 64), 0, s, a, sp);
+  else hipLaunchKernelGGL(lora_u_k<false>, grid, dim3(UW * 64), 0, s, a, sp);
+  if (sp.S > 1) {
+    const int64_t n = (int64_t)a.n * a.R * 16;
+    hipLaunchKernelGGL(lora_u_reduce_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, sp);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Adapter gradients.  A workgroup of 4 waves owns 64 columns c of one job.
+// Per block of TB tokens it loads Y [TB x 64] and every Z_z [TB x 16] in one
+// burst (16-byte loads where the row allows), rounds them to bf16 and stores
+// them transposed in LDS (column-major in m), so that each MFMA fragment --
+// 8 consecutive tokens of one column -- is one 16-byte LDS read; wave w then
+// runs the block's MFMAs for its 16 columns.  Every output element is one
+// lane's sum in token order: deterministic.
+constexpr int TB = 256;      // tokens per LDS block
+constexpr int TBP = TB + 8;  // padded row (bf16) of the transposed tiles
+
+template <bool YF32>
+__global__ __launch_bounds__(256) void lora_tgrad_k(const LoraTGrad a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sY[64][TBP];
+  __shared__ __attribute__((aligned(16))) uint16_t sZ[3][16][TBP];
+  const LoraTGradJob& jb = a.job[blockIdx.y];
+  const int c0 = blockIdx.x * 64;
+  if (c0 >= jb.C) return;  // uniform over the workgroup
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int nz = jb.nz;
+  f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // staging map: thread t takes 8 consecutive columns cc of token rows
+  // t / 8 + 32 i of the block; Z entries: token t / 8 + 32 i, j pair 2 (t % 8)
+  const int cc = (t & 7) * 8, mr = t >> 3;
+  const bool cfull = c0 + cc + 8 <= jb.C;
+  const bool yvec = cfull && (a.ldy % (YF32 ? 4 : 8)) == 0 &&
+                    ((uintptr_t)jb.Y & 15) == 0 && ((c0 + cc) % (YF32 ? 4 : 8)) == 0;
+  for (int mb = 0; mb < a.R; mb += TB) {
+    // every load of the block first (one round trip), then bf16 + LDS
+    constexpr int NI = TB / 32;
+    float v[NI][8];
+    float zv[3][NI][2];
+    if (yvec) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int m = mb + mr + 32 * i;
+        const bool in = m < a.R;
+        if constexpr (YF32) {
+          const float* y = reinterpret_cast<const float*>(jb.Y) + (int64_t)(in ? m : 0) * a.ldy + c0 + cc;
+          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+          const f32x4 y0 = in ? *reinterpret_cast<const f32x4*>(y) : zero;
+          const f32x4 y1 = in ? *reinterpret_cast<const f32x4*>(y + 4) : zero;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[i][e] = y0[e];
+            v[i][e + 4] = y1[e];
+          }
+        } else {
+          const uint16_t* y =
+              reinterpret_cast<const uint16_t*>(jb.Y) + (int64_t)(in ? m : 0) * a.ldy + c0 + cc;
+          const u32x4 zero = {0u, 0u, 0u, 0u};
+          const u32x4 w4 = in ? *reinterpret_cast<const u32x4*>(y) : zero;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[i][2 * e] = bf16_to_f32((uint16_t)(w4[e] & 0xffff));
+            v[i][2 * e + 1] = bf16_to_f32((uint16_t)(w4[e] >> 16));
+          }
+        }
+      }
+    } else {  // ragged column block or unaligned rows
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int m = mb + mr + 32 * i;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = c0 + cc + e;
+          float y = 0.f;
+          if (m < a.R && c < jb.C) {
+            const int64_t o = (int64_t)m * a.ldy + c;
+            if constexpr (YF32) y = reinterpret_cast<const float*>(jb.Y)[o];
+            else y = bf16_to_f32(reinterpret_cast<const uint16_t*>(jb.Y)[o]);
+          }
+          v[i][e] = y;
+        }
+      }
+    }
+    const int jz = 2 * (t & 7);
+#pragma unroll
+    for (int z = 0; z < 3; ++z) {
+      if (z >= nz) break;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int m = mb + mr + 32 * i;
+        const float* zr = jb.Z[z] + (int64_t)(m < a.R ? m : 0) * jb.ldz[z];
+        zv[z][i][0] = (m < a.R && jz < a.r) ? zr[jz] : 0.f;
+        zv[z][i][1] = (m < a.R && jz + 1 < a.r) ? zr[jz + 1] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int ml = mr + 32 * i;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sY[cc + e][ml] = f32_to_bf16_bits(v[i][e]);
+#pragma unroll
+      for (int z = 0; z < 3; ++z) {
+        if (z >= nz) break;
+        sZ[z][jz][ml] = f32_to_bf16_bits(zv[z][i][0]);
+        sZ[z][jz + 1][ml] = f32_to_bf16_bits(zv[z][i][1]);
+      }
+    }
+    __syncthreads();
+    const int nk = min(TB, a.R - mb);
+    for (int k0 = 0; k0 < nk; k0 += 32) {
+      const int kk = k0 + (lane >> 4) * 8;
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&sY[16 * wave + (lane & 15)][kk]);
+#pragma unroll
+      for (int z = 0; z < 3; ++z) {
+        if (z >= nz) break;
+        const bf16x8 bz = *reinterpret_cast<const bf16x8*>(&sZ[z][lane & 15][kk]);
+        acc[z] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bz, acc[z], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // lane holds C[c = 16 wave + 4 (lane / 16) + i][j = lane % 16]
+  const int j = lane & 15;
+  if (j >= a.r) return;
+#pragma unroll
+  for (int z = 0; z < 3; ++z) {
+    if (z >= nz) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = c0 + 16 * wave + 4 * (lane >> 4) + i;
+      if (c >= jb.C) continue;
+      float* o = jb.out[z] + (int64_t)c * jb.so_c + (int64_t)j * jb.so_j;
+      const float v = a.scale * acc[z][i];
+      *o = a.accumulate ? *o + v : v;
+    }
+  }
+}
+
+hipError_t lora_tgrad(const LoraTGrad& a, hipStream_t s) {
+  if (a.R <= 0 || a.njobs <= 0) return hipSuccess;
+  if (a.njobs > 3 || a.r > 16) return hipErrorInvalidValue;
+  int cmax = 0;
+  for (int q = 0; q < a.njobs; ++q) {
+    if (a.job[q].nz < 1 || a.job[q].nz > 3) return hipErrorInvalidValue;
+    cmax = std::max(cmax, a.job[q].C);
+  }
+  const dim3 grid((cmax + 63) / 64, a.njobs);
+  if (a.y_f32) hipLaunchKernelGGL(lora_tgrad_k<true>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(lora_tgrad_k<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t lora_mm(const LoraMM& a, float* partial, int64_t partial_floats, hipStream_t s) {
   if (a.R <= 0) return hipSuccess;
   int ns, kc;

@@ -456,40 +456,314 @@ __global__ void nf4_dequant_k(const uint32_t* __restrict__ codes, const float* _
 }
 
 // ---------------------------------------------------------------------------
+// 16-byte forms of the kernels above, for rows whose length is a multiple of
+// 4 (8 for softmax) and 16-byte aligned; same per-element arithmetic, each
+// thread in a fixed order.  The launchers fall back to the scalar kernels
+// for other shapes.
+// ---------------------------------------------------------------------------
+LSN_DEV float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+LSN_DEV float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+LSN_DEV bool al16(const void* q) { return ((uintptr_t)q & 15) == 0; }
+
+__global__ __launch_bounds__(256) void rmsnorm_fwd4_k(const float* __restrict__ h,
+                                                      const uint16_t* __restrict__ g, int H,
+                                                      float eps, uint16_t* __restrict__ y,
+                                                      float* __restrict__ rstd) {
+  __shared__ float red[16];
+  const int64_t row = blockIdx.x;
+  const f32x4* x = reinterpret_cast<const f32x4*>(h + row * H);
+  const int n4 = H >> 2;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const f32x4 v = x[i];
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  if (threadIdx.x == 0) rstd[row] = r;
+  const u32x2* gw = reinterpret_cast<const u32x2*>(g);
+  u32x2* yo = reinterpret_cast<u32x2*>(y + row * H);
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const f32x4 v = x[i];
+    const u32x2 w = gw[i];
+    yo[i] = u32x2{pack_bf16x2(bf_lo(w[0]) * (v[0] * r), bf_hi(w[0]) * (v[1] * r)),
+                  pack_bf16x2(bf_lo(w[1]) * (v[2] * r), bf_hi(w[1]) * (v[3] * r))};
+  }
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_bwd4_k(const float* __restrict__ h,
+                                                      const uint16_t* __restrict__ g,
+                                                      const float* __restrict__ rstd,
+                                                      const float* __restrict__ dy,
+                                                      const float* dres, int H, float* out) {
+  __shared__ float red[16];
+  const int64_t row = blockIdx.x;
+  const f32x4* x = reinterpret_cast<const f32x4*>(h + row * H);
+  const f32x4* d = reinterpret_cast<const f32x4*>(dy + row * H);
+  const u32x2* gw = reinterpret_cast<const u32x2*>(g);
+  const int n4 = H >> 2;
+  float dot = 0.f;
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const f32x4 xv = x[i], dv = d[i];
+    const u32x2 w = gw[i];
+    dot += bf_lo(w[0]) * dv[0] * xv[0] + bf_hi(w[0]) * dv[1] * xv[1] +
+           bf_lo(w[1]) * dv[2] * xv[2] + bf_hi(w[1]) * dv[3] * xv[3];
+  }
+  dot = block_sum(dot, red);
+  const float r = rstd[row];
+  const float c = r * r * r * dot / (float)H;
+  f32x4* o = reinterpret_cast<f32x4*>(out + row * H);
+  const f32x4* dr = dres ? reinterpret_cast<const f32x4*>(dres + row * H) : nullptr;
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const f32x4 xv = x[i], dv = d[i];
+    const u32x2 w = gw[i];
+    f32x4 v = {r * bf_lo(w[0]) * dv[0] - c * xv[0], r * bf_hi(w[0]) * dv[1] - c * xv[1],
+               r * bf_lo(w[1]) * dv[2] - c * xv[2], r * bf_hi(w[1]) * dv[3] - c * xv[3]};
+    if (dr) v = dr[i] + v;
+    o[i] = v;
+  }
+}
+
+// RoPE with the token's d/2 angles computed once per block into LDS.
+template <bool FWD>
+__global__ __launch_bounds__(256) void rope4_k(float* __restrict__ xin, uint16_t* __restrict__ out,
+                                               int S, int nq, int nkv, int d, float theta) {
+  __shared__ float sc[128], ss[128];
+  const int64_t t = blockIdx.x;
+  const int pos = (int)(t % S);
+  const int W = (nq + 2 * nkv) * d, half = d / 2, h4 = half / 4;
+  for (int j = threadIdx.x; j < half; j += 256) rope_angle(pos, j, d, theta, &sc[j], &ss[j]);
+  __syncthreads();
+  float* x = xin + t * W;
+  uint16_t* y = out + t * W;
+  const int nrot = (nq + nkv) * h4;  // 4-wide groups of rotated pairs
+  for (int i = threadIdx.x; i < nrot; i += 256) {
+    const int head = i / h4, j = (i % h4) * 4;
+    f32x4* p1 = reinterpret_cast<f32x4*>(x + head * d + j);
+    f32x4* p2 = reinterpret_cast<f32x4*>(x + head * d + j + half);
+    const f32x4 a = *p1, b = *p2;
+    f32x4 r1, r2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float c = sc[j + e], s = ss[j + e];
+      if (FWD) {
+        r1[e] = a[e] * c - b[e] * s;
+        r2[e] = b[e] * c + a[e] * s;
+      } else {
+        r1[e] = a[e] * c + b[e] * s;
+        r2[e] = b[e] * c - a[e] * s;
+      }
+    }
+    if (!FWD) {
+      *p1 = r1;
+      *p2 = r2;
+    }
+    *reinterpret_cast<u32x2*>(y + head * d + j) =
+        u32x2{pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
+    *reinterpret_cast<u32x2*>(y + head * d + j + half) =
+        u32x2{pack_bf16x2(r2[0], r2[1]), pack_bf16x2(r2[2], r2[3])};
+  }
+  const int o0 = (nq + nkv) * d;
+  for (int i = threadIdx.x; i < nkv * d / 4; i += 256) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(x + o0)[i];
+    reinterpret_cast<u32x2*>(y + o0)[i] = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+}
+
+// Causal softmax, one wave per row, the row held in registers (NCH 16-byte
+// chunks per lane, S <= 256 NCH): one exp per element.
+template <int NCH>
+__global__ __launch_bounds__(256) void softmax_causal4_k(const float* __restrict__ sc,
+                                                         float* __restrict__ Pf,
+                                                         uint16_t* __restrict__ Pb, int S,
+                                                         int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int i = (int)(row % S), n4 = S >> 2;
+  const f32x4* x = reinterpret_cast<const f32x4*>(sc + row * S);
+  f32x4 v[NCH];
+  float m = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) {
+    const int c = lane + 64 * q;
+    v[q] = (c < n4 && 4 * c <= i) ? x[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (c < n4 && 4 * c + e <= i) m = fmaxf(m, v[q][e]);
+  }
+  m = wave_max(m);
+  float sum = 0.f;
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) {
+    const int c = lane + 64 * q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ex = (c < n4 && 4 * c + e <= i) ? expf(v[q][e] - m) : 0.f;
+      v[q][e] = ex;
+      sum += ex;
+    }
+  }
+  sum = wave_sum(sum);
+  const float inv = 1.0f / sum;
+  f32x4* pf = reinterpret_cast<f32x4*>(Pf + row * S);
+  u32x2* pb = reinterpret_cast<u32x2*>(Pb + row * S);
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) {
+    const int c = lane + 64 * q;
+    if (c >= n4) continue;
+    const f32x4 p = v[q] * inv;
+    pf[c] = p;
+    pb[c] = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+  }
+}
+
+// dS = P (dP - sum_j dP P), one wave per row, 16-byte chunks
+__global__ __launch_bounds__(256) void softmax_bwd4_k(const float* __restrict__ Pf,
+                                                      const float* __restrict__ dP,
+                                                      uint16_t* __restrict__ dS, int S,
+                                                      int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int i = (int)(row % S), n4 = S >> 2;
+  const f32x4* p = reinterpret_cast<const f32x4*>(Pf + row * S);
+  const f32x4* g = reinterpret_cast<const f32x4*>(dP + row * S);
+  float dot = 0.f;
+  for (int c = lane; c < n4 && 4 * c <= i; c += 64) {
+    const f32x4 pv = p[c], gv = g[c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * c + e <= i) dot += pv[e] * gv[e];
+  }
+  dot = wave_sum(dot);
+  u32x2* o = reinterpret_cast<u32x2*>(dS + row * S);
+  for (int c = lane; c < n4; c += 64) {
+    if (4 * c > i) {
+      o[c] = u32x2{0u, 0u};
+      continue;
+    }
+    const f32x4 pv = p[c], gv = g[c];
+    float r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = (4 * c + e <= i) ? pv[e] * (gv[e] - dot) : 0.f;
+    o[c] = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+  }
+}
+
+// SwiGLU, 4 features per thread; blockIdx.y = token
+__global__ __launch_bounds__(256) void swiglu_fwd4_k(const float* __restrict__ gu,
+                                                     uint16_t* __restrict__ a, int F) {
+  const int f = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (f >= F) return;
+  const int64_t t = blockIdx.y;
+  const f32x4 g = *reinterpret_cast<const f32x4*>(gu + t * 2 * F + f);
+  const f32x4 u = *reinterpret_cast<const f32x4*>(gu + t * 2 * F + F + f);
+  float r[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = g[e] * sigm(g[e]) * u[e];
+  *reinterpret_cast<u32x2*>(a + t * F + f) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+}
+
+__global__ __launch_bounds__(256) void swiglu_bwd4_k(const float* __restrict__ gu,
+                                                     const float* __restrict__ da,
+                                                     uint16_t* __restrict__ dgu,
+                                                     float* __restrict__ dguf, int F) {
+  const int f = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (f >= F) return;
+  const int64_t t = blockIdx.y;
+  const f32x4 g = *reinterpret_cast<const f32x4*>(gu + t * 2 * F + f);
+  const f32x4 u = *reinterpret_cast<const f32x4*>(gu + t * 2 * F + F + f);
+  const f32x4 d = *reinterpret_cast<const f32x4*>(da + t * F + f);
+  f32x4 dg, du;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float s = sigm(g[e]);
+    dg[e] = d[e] * u[e] * (s * (1.0f + g[e] * (1.0f - s)));
+    du[e] = d[e] * (g[e] * s);
+  }
+  *reinterpret_cast<u32x2*>(dgu + t * 2 * F + f) =
+      u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+  *reinterpret_cast<u32x2*>(dgu + t * 2 * F + F + f) =
+      u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+  if (dguf) {
+    *reinterpret_cast<f32x4*>(dguf + t * 2 * F + f) = dg;
+    *reinterpret_cast<f32x4*>(dguf + t * 2 * F + F + f) = du;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static inline unsigned nb(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
 
+static bool a16(const void* q) { return ((uintptr_t)q & 15) == 0; }
+
 void rmsnorm_fwd(const float* h, const uint16_t* g, int T, int H, float eps, uint16_t* y,
                  float* rstd, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_fwd_k, dim3(T), dim3(256), 0, s, h, g, H, eps, y, rstd);
+  if (H % 4 == 0 && a16(h) && ((uintptr_t)g & 7) == 0 && ((uintptr_t)y & 7) == 0)
+    hipLaunchKernelGGL(rmsnorm_fwd4_k, dim3(T), dim3(256), 0, s, h, g, H, eps, y, rstd);
+  else
+    hipLaunchKernelGGL(rmsnorm_fwd_k, dim3(T), dim3(256), 0, s, h, g, H, eps, y, rstd);
 }
 void rmsnorm_bwd(const float* h, const uint16_t* g, const float* rstd, const float* dy,
                  const float* dres, int T, int H, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_bwd_k, dim3(T), dim3(256), 0, s, h, g, rstd, dy, dres, H, out);
+  if (H % 4 == 0 && a16(h) && a16(dy) && a16(out) && (!dres || a16(dres)) &&
+      ((uintptr_t)g & 7) == 0)
+    hipLaunchKernelGGL(rmsnorm_bwd4_k, dim3(T), dim3(256), 0, s, h, g, rstd, dy, dres, H, out);
+  else
+    hipLaunchKernelGGL(rmsnorm_bwd_k, dim3(T), dim3(256), 0, s, h, g, rstd, dy, dres, H, out);
+}
+static bool rope_vec(const void* x, const void* y, int d) {
+  return d % 8 == 0 && d / 2 <= 128 && a16(x) && ((uintptr_t)y & 7) == 0;
 }
 void rope_fwd(const float* qkv, uint16_t* out, int T, int S, int nq, int nkv, int d, float theta,
               hipStream_t s) {
-  hipLaunchKernelGGL(rope_fwd_k, dim3(T), dim3(256), 0, s, qkv, out, S, nq, nkv, d, theta);
+  if (rope_vec(qkv, out, d))
+    hipLaunchKernelGGL(rope4_k<true>, dim3(T), dim3(256), 0, s, const_cast<float*>(qkv), out, S,
+                       nq, nkv, d, theta);
+  else
+    hipLaunchKernelGGL(rope_fwd_k, dim3(T), dim3(256), 0, s, qkv, out, S, nq, nkv, d, theta);
 }
 void rope_bwd(float* dqkv, uint16_t* outb, int T, int S, int nq, int nkv, int d, float theta,
               hipStream_t s) {
-  hipLaunchKernelGGL(rope_bwd_k, dim3(T), dim3(256), 0, s, dqkv, outb, S, nq, nkv, d, theta);
+  if (rope_vec(dqkv, outb, d))
+    hipLaunchKernelGGL(rope4_k<false>, dim3(T), dim3(256), 0, s, dqkv, outb, S, nq, nkv, d, theta);
+  else
+    hipLaunchKernelGGL(rope_bwd_k, dim3(T), dim3(256), 0, s, dqkv, outb, S, nq, nkv, d, theta);
 }
 void softmax_causal(const float* sc, float* Pf, uint16_t* Pb, int S, int64_t rows,
                     hipStream_t s) {
-  hipLaunchKernelGGL(softmax_causal_k, dim3(nb(rows, 4)), dim3(256), 0, s, sc, Pf, Pb, S, rows);
+  const bool vec = S % 8 == 0 && a16(sc) && a16(Pf) && ((uintptr_t)Pb & 7) == 0;
+  const dim3 grid(nb(rows, 4)), blk(256);
+  if (vec && S <= 256) hipLaunchKernelGGL(softmax_causal4_k<1>, grid, blk, 0, s, sc, Pf, Pb, S, rows);
+  else if (vec && S <= 512) hipLaunchKernelGGL(softmax_causal4_k<2>, grid, blk, 0, s, sc, Pf, Pb, S, rows);
+  else if (vec && S <= 1024) hipLaunchKernelGGL(softmax_causal4_k<4>, grid, blk, 0, s, sc, Pf, Pb, S, rows);
+  else if (vec && S <= 2048) hipLaunchKernelGGL(softmax_causal4_k<8>, grid, blk, 0, s, sc, Pf, Pb, S, rows);
+  else hipLaunchKernelGGL(softmax_causal_k, grid, blk, 0, s, sc, Pf, Pb, S, rows);
 }
 void softmax_bwd(const float* Pf, const float* dP, uint16_t* dS, int S, int64_t rows,
                  hipStream_t s) {
-  hipLaunchKernelGGL(softmax_bwd_k, dim3(nb(rows, 4)), dim3(256), 0, s, Pf, dP, dS, S, rows);
+  if (S % 8 == 0 && a16(Pf) && a16(dP) && ((uintptr_t)dS & 7) == 0)
+    hipLaunchKernelGGL(softmax_bwd4_k, dim3(nb(rows, 4)), dim3(256), 0, s, Pf, dP, dS, S, rows);
+  else
+    hipLaunchKernelGGL(softmax_bwd_k, dim3(nb(rows, 4)), dim3(256), 0, s, Pf, dP, dS, S, rows);
 }
 void swiglu_fwd(const float* gu, uint16_t* a, int T, int F, hipStream_t s) {
+  if (F % 4 == 0 && T <= 65535 && a16(gu) && ((uintptr_t)a & 7) == 0) {
+    hipLaunchKernelGGL(swiglu_fwd4_k, dim3(nb(F / 4, 256), T), dim3(256), 0, s, gu, a, F);
+    return;
+  }
   const int64_t n = (int64_t)T * F;
   hipLaunchKernelGGL(swiglu_fwd_k, dim3(nb(n, 256)), dim3(256), 0, s, gu, a, F, n);
 }
 void swiglu_bwd(const float* gu, const float* da, uint16_t* dgu, float* dguf, int T, int F,
                 hipStream_t s) {
+  if (F % 4 == 0 && T <= 65535 && a16(gu) && a16(da) && ((uintptr_t)dgu & 7) == 0 &&
+      (!dguf || a16(dguf))) {
+    hipLaunchKernelGGL(swiglu_bwd4_k, dim3(nb(F / 4, 256), T), dim3(256), 0, s, gu, da, dgu, dguf, F);
+    return;
+  }
   const int64_t n = (int64_t)T * F;
   hipLaunchKernelGGL(swiglu_bwd_k, dim3(nb(n, 256)), dim3(256), 0, s, gu, da, dgu, dguf, F, n);
 }

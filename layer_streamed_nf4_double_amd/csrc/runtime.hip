@@ -400,7 +400,7 @@ static uint64_t carve(lsn_ctx* c, char* base) {
           c->gpart_floats, gemm_partial_floats((int)T, (int)sh[0], (int)sh[1], 1, 1));
     c->gpart = (float*)P(std::max<int64_t>(c->gpart_floats, 1) * 4);
   }
-  c->lu = (float*)P(T * 16 * 4);
+  c->lu = (float*)P(3 * T * 16 * 4);  // u_p of up to three adapters of a group
   c->ext_rows = std::max<int64_t>({QKV, 2 * F, H, QD, F});
   c->aext = (uint16_t*)P(T * 48 * 2);
   c->bext = (uint16_t*)P(c->ext_rows * 48 * 2);
@@ -707,6 +707,8 @@ static int lora_fwd_ext(lsn_ctx* c, int layer, Group g, const uint16_t* x, int64
 // Backward of the low-rank branches of a group.  dyf: fp32 gradient of the
 // group's fused output [T, rows] (row stride lddy); x: forward input [T, K].
 // Adds dA, dB; prepares aext = bf16(s u_p), bext = A_p (bf16) for dX.
+// Three launches for all adapters of the group: u_p = dy_p B_p^T (with
+// aext), dA_p += s x^T u_p (one pass over x), dB_p += s t_p^T dy_p.
 static int lora_bwd_ext(lsn_ctx* c, int layer, Group g, const float* dyf, int64_t lddy,
                         const uint16_t* x, int64_t ldx, int T) {
   int nad = 0;
@@ -714,34 +716,68 @@ static int lora_bwd_ext(lsn_ctx* c, int layer, Group g, const float* dyf, int64_
   if (!nad) return 0;
   const int r = c->cfg.lora_rank, kext = 16 * nad;
   const float s = c->lora_scale();
-  int slot = 0;
+  LoraU u;
+  u.dy = dyf; u.dy_f32 = 1; u.lddy = lddy; u.R = T; u.r = r;
+  u.ext = c->aext; u.ld_ext = kext; u.ext_scale = s;
+  LoraTGrad ga;  // dA_p += s x^T u_p, dA stored [K, r]
+  ga.R = T; ga.r = r; ga.y_f32 = 0; ga.ldy = ldx; ga.scale = s; ga.njobs = 1;
+  ga.job[0].Y = x; ga.job[0].C = (int)c->K[g.first]; ga.job[0].so_c = r; ga.job[0].so_j = 1;
+  LoraTGrad gb;  // dB_p += s t_p^T dy_p, dB stored [r, N_p]
+  gb.R = T; gb.r = r; gb.y_f32 = 1; gb.ldy = lddy; gb.scale = s;
   int64_t col0 = 0;
   for (int p = g.first; p < g.first + g.count; ++p) {
     if (c->targeted(p)) {
-      const int64_t K = c->K[p], N = c->N[p];
-      const float* dy = dyf + col0;
-      // u = dy B^T : W(k = n, j) = B[j*N + n]
-      LoraMM u;  // u = dy B^T, aext = bf16(s u)
-      u.X = dy; u.x_f32 = 1; u.ldx = lddy; u.R = T; u.K = (int)N;
-      u.W = c->B_of(layer, p); u.sk = 1; u.sj = N; u.r = r;
-      u.out = c->lu; u.so_r = r; u.so_j = 1;
-      u.ext = c->aext + 16 * slot; u.ld_ext = kext; u.ext_scale = s;
-      (void)lora_mm(u, c->lpart, c->lpart_floats, c->cs);
-      LoraMM ga;  // dA += s x^T u
-      ga.X = x; ga.trans = 1; ga.ldx = ldx; ga.R = (int)K; ga.K = T;
-      ga.W = c->lu; ga.sk = r; ga.sj = 1; ga.r = r;
-      ga.out = c->dA_of(layer, p); ga.so_r = r; ga.so_j = 1; ga.accumulate = 1; ga.scale = s;
-      (void)lora_mm(ga, c->lpart, c->lpart_floats, c->cs);
-      LoraMM gb;  // dB += s t^T dy, stored dB[j*N + n]
-      gb.X = dy; gb.x_f32 = 1; gb.trans = 1; gb.ldx = lddy; gb.R = (int)N; gb.K = T;
-      gb.W = c->lt + (int64_t)p * T * 16; gb.sk = r; gb.sj = 1; gb.r = r;
-      gb.out = c->dB_of(layer, p); gb.so_r = 1; gb.so_j = N; gb.accumulate = 1; gb.scale = s;
-      (void)lora_mm(gb, c->lpart, c->lpart_floats, c->cs);
-      lora_ext(c->A_of(layer, p), r, 1, (int)K, r, c->bext, kext, 16 * slot, c->cs);
-      ++slot;
+      const int q = u.n++;
+      u.col0[q] = col0;
+      u.N[q] = (int)c->N[p];
+      u.B[q] = c->B_of(layer, p);
+      u.u[q] = c->lu + (int64_t)q * T * 16;
+      LoraTGradJob& ja = ga.job[0];
+      ja.Z[ja.nz] = u.u[q];
+      ja.ldz[ja.nz] = r;
+      ja.out[ja.nz] = c->dA_of(layer, p);
+      ++ja.nz;
+      LoraTGradJob& jb = gb.job[gb.njobs++];
+      jb.Y = dyf + col0;
+      jb.C = (int)c->N[p];
+      jb.nz = 1;
+      jb.so_c = 1;
+      jb.so_j = c->N[p];
+      jb.Z[0] = c->lt + (int64_t)p * T * 16;
+      jb.ldz[0] = r;
+      jb.out[0] = c->dB_of(layer, p);
     }
     col0 += c->N[p];
   }
+  if (lora_u_ok(u)) {
+    (void)lora_u(u, c->lpart, c->lpart_floats, c->cs);
+    (void)lora_tgrad(ga, c->cs);
+    (void)lora_tgrad(gb, c->cs);
+  } else {  // rows not 16-byte aligned: the general product, one adapter at a time
+    for (int q = 0; q < u.n; ++q) {
+      const float* dy = dyf + u.col0[q];
+      LoraMM mu;  // u = dy B^T, aext = bf16(s u)
+      mu.X = dy; mu.x_f32 = 1; mu.ldx = lddy; mu.R = T; mu.K = u.N[q];
+      mu.W = u.B[q]; mu.sk = 1; mu.sj = u.N[q]; mu.r = r;
+      mu.out = u.u[q]; mu.so_r = r; mu.so_j = 1;
+      mu.ext = c->aext + 16 * q; mu.ld_ext = kext; mu.ext_scale = s;
+      (void)lora_mm(mu, c->lpart, c->lpart_floats, c->cs);
+      LoraMM ma;  // dA += s x^T u
+      ma.X = x; ma.trans = 1; ma.ldx = ldx; ma.R = ga.job[0].C; ma.K = T;
+      ma.W = u.u[q]; ma.sk = r; ma.sj = 1; ma.r = r;
+      ma.out = ga.job[0].out[q]; ma.so_r = r; ma.so_j = 1; ma.accumulate = 1; ma.scale = s;
+      (void)lora_mm(ma, c->lpart, c->lpart_floats, c->cs);
+      LoraMM mb;  // dB += s t^T dy, stored dB[j*N + n]
+      mb.X = dy; mb.x_f32 = 1; mb.trans = 1; mb.ldx = lddy; mb.R = u.N[q]; mb.K = T;
+      mb.W = gb.job[q].Z[0]; mb.sk = r; mb.sj = 1; mb.r = r;
+      mb.out = gb.job[q].out[0]; mb.so_r = 1; mb.so_j = u.N[q]; mb.accumulate = 1; mb.scale = s;
+      (void)lora_mm(mb, c->lpart, c->lpart_floats, c->cs);
+    }
+  }
+  int slot = 0;
+  for (int p = g.first; p < g.first + g.count; ++p)
+    if (c->targeted(p))
+      lora_ext(c->A_of(layer, p), r, 1, (int)c->K[p], r, c->bext, kext, 16 * slot++, c->cs);
   return kext;
 }
 
@@ -1095,22 +1131,30 @@ lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t
     m.W = A; m.sk = r; m.sj = 1; m.r = r;
     m.out = L.t; m.so_r = r; m.so_j = 1;
     (void)lora_mm(m, L.lpart, L.lpf, hs);
-    LoraMM uu;  // u = dY B^T, aext = bf16(s u)
-    uu.X = dY; uu.ldx = N; uu.R = M; uu.K = N;
-    uu.W = B; uu.sk = 1; uu.sj = N; uu.r = r;
-    uu.out = L.u; uu.so_r = r; uu.so_j = 1;
+    LoraU uu;  // u = dY B^T, aext = bf16(s u)
+    uu.dy = dY; uu.dy_f32 = 0; uu.lddy = N; uu.R = M; uu.r = r; uu.n = 1;
+    uu.N[0] = N; uu.B[0] = B; uu.u[0] = L.u;
     uu.ext = L.aext; uu.ld_ext = 16; uu.ext_scale = s;
-    (void)lora_mm(uu, L.lpart, L.lpf, hs);
-    LoraMM ga;  // dA += s X^T u
-    ga.X = X; ga.trans = 1; ga.ldx = K; ga.R = K; ga.K = M;
-    ga.W = L.u; ga.sk = r; ga.sj = 1; ga.r = r;
-    ga.out = dA; ga.so_r = r; ga.so_j = 1; ga.accumulate = 1; ga.scale = s;
-    (void)lora_mm(ga, L.lpart, L.lpf, hs);
-    LoraMM gb;  // dB += s t^T dY
-    gb.X = dY; gb.trans = 1; gb.ldx = N; gb.R = N; gb.K = M;
-    gb.W = L.t; gb.sk = r; gb.sj = 1; gb.r = r;
-    gb.out = dB; gb.so_r = 1; gb.so_j = N; gb.accumulate = 1; gb.scale = s;
-    (void)lora_mm(gb, L.lpart, L.lpf, hs);
+    if (lora_u_ok(uu)) {
+      (void)lora_u(uu, L.lpart, L.lpf, hs);
+    } else {
+      LoraMM mu;
+      mu.X = dY; mu.ldx = N; mu.R = M; mu.K = N;
+      mu.W = B; mu.sk = 1; mu.sj = N; mu.r = r;
+      mu.out = L.u; mu.so_r = r; mu.so_j = 1;
+      mu.ext = L.aext; mu.ld_ext = 16; mu.ext_scale = s;
+      (void)lora_mm(mu, L.lpart, L.lpf, hs);
+    }
+    LoraTGrad ga;  // dA += s X^T u
+    ga.R = M; ga.r = r; ga.y_f32 = 0; ga.ldy = K; ga.scale = s; ga.njobs = 1;
+    ga.job[0].Y = X; ga.job[0].C = K; ga.job[0].nz = 1; ga.job[0].so_c = r; ga.job[0].so_j = 1;
+    ga.job[0].Z[0] = L.u; ga.job[0].ldz[0] = r; ga.job[0].out[0] = dA;
+    (void)lora_tgrad(ga, hs);
+    LoraTGrad gb;  // dB += s t^T dY, stored dB[j*N + n]
+    gb.R = M; gb.r = r; gb.y_f32 = 0; gb.ldy = N; gb.scale = s; gb.njobs = 1;
+    gb.job[0].Y = dY; gb.job[0].C = N; gb.job[0].nz = 1; gb.job[0].so_c = 1; gb.job[0].so_j = N;
+    gb.job[0].Z[0] = L.t; gb.job[0].ldz[0] = r; gb.job[0].out[0] = dB;
+    (void)lora_tgrad(gb, hs);
     lora_ext(A, r, 1, K, r, L.bext, 16, 0, hs);  // bext = A
     p.Aext = L.aext; p.ldae = 16; p.Bext = L.bext; p.ldbe = 16; p.kext = 16;
   }
