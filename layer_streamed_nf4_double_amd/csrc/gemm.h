@@ -23,6 +23,12 @@ struct GemmParams {
   int64_t sA_o = 0, sA_i = 0, sB_o = 0, sB_i = 0, sC_o = 0, sC_i = 0;
   // the reduction runs over nseg segments of K each; segment s shifts A and B
   int nseg = 1;
+  // causal attention products (M and K or M and N index the same sequence):
+  // CAUSAL_SKIP_UPPER skips output tiles wholly above the diagonal (n > m),
+  // which no consumer reads; CAUSAL_K_TO_ROW ends the reduction at the tile's
+  // last row (A is zero for k > m); CAUSAL_K_FROM_ROW starts it at the tile's
+  // first row, in every segment (A is zero for k < m)
+  int causal = 0;
   int64_t sA_seg = 0, sB_seg = 0;
   // low-rank extension (bf16, k-contiguous, kext a multiple of 16)
   const uint16_t* Aext = nullptr;
@@ -52,6 +58,8 @@ struct GemmParams {
 // and gemm_nf4t.hip (dx = dy W); TILE_BF16F: the 256 x 256 bf16 kernel of
 // gemm_bf16.hip (C = A B^T, LM-head logits); TILE_BF16T: its C = A B
 // counterpart (LM-head input gradient)
+enum { CAUSAL_NONE = 0, CAUSAL_SKIP_UPPER = 1, CAUSAL_K_TO_ROW = 2, CAUSAL_K_FROM_ROW = 3 };
+
 enum { TILE_256x128 = 0, TILE_128x128 = 1, TILE_64x64 = 2, TILE_NF4F = 3, TILE_NF4T = 4,
        TILE_BF16F = 5, TILE_BF16T = 6 };
 

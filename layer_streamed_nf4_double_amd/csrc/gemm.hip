@@ -313,6 +313,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(const GemmParams p
   const int per = nblk / 8, rem = nblk % 8, x = b % 8;
   const int id = x * per + min(x, rem) + b / 8;
   const int m0 = (id % mt) * BM, n0 = (id / mt) * BN;
+  if (p.causal == CAUSAL_SKIP_UPPER && n0 >= m0 + BM) return;  // uniform per workgroup
 
   const int z = blockIdx.z;
   const int zo = z / p.zdiv, zi = z % p.zdiv;
@@ -356,15 +357,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(const GemmParams p
   }
 
   const int nkt = (p.K + BK - 1) / BK;
-  // split-k: blockIdx.y takes k-tiles [it0, it1) of the nseg * nkt
-  const int ntile = nkt * p.nseg;
+  // k-tiles [kt_lo, kt_lo + nk) of every segment (all of them unless causal)
+  int kt_lo = 0, nk = nkt;
+  if (p.causal == CAUSAL_K_TO_ROW) nk = min(nkt, (m0 + BM + BK - 1) / BK);
+  if (p.causal == CAUSAL_K_FROM_ROW) {
+    kt_lo = min(nkt, m0 / BK);
+    nk = nkt - kt_lo;
+  }
+  // split-k: blockIdx.y takes tiles [it0, it1) of the nseg * nk
+  const int ntile = nk * p.nseg;
   const int kper = (ntile + p.ksplit - 1) / p.ksplit;
   const int it0 = min(ntile, (int)blockIdx.y * kper), it1 = min(ntile, it0 + kper);
   const bool rows_a_full = m0 + BM <= p.M, rows_b_full = n0 + BN <= p.N;
 
   // uniform per-slice base pointers; per-lane offsets were fixed by init()
   auto prefetch = [&](LA& a, LB& bb, int it) {
-    const int seg = it / nkt, k0 = (it % nkt) * BK;
+    const int seg = it / max(nk, 1), k0 = (kt_lo + it % max(nk, 1)) * BK;
     const bool kfull = k0 + BK <= p.K;
     const int64_t ka = (OPA == A_BF16_R) ? (int64_t)k0 * p.lda : k0;
     if constexpr (OPA == A_F32_K)

@@ -464,7 +464,8 @@ __global__ __launch_bounds__(256) void bf16t_kernel(const GemmParams p) {
 static bool aligned_to(const void* q, uintptr_t a) { return ((uintptr_t)q & (a - 1)) == 0; }
 
 bool bf16f_eligible(const GemmParams& p, int batch) {
-  if (batch != 1 || p.nseg != 1 || p.zdiv != 1 || p.alpha != 1.f || p.kext != 0) return false;
+  if (batch != 1 || p.nseg != 1 || p.zdiv != 1 || p.alpha != 1.f || p.kext != 0 || p.causal)
+    return false;
   if (p.M < BM || p.N < 64 || p.K % BK != 0) return false;
   if (p.lda % 8 != 0 || p.ldb % 8 != 0 || p.lda < 64 || p.ldb < 64 || !aligned_to(p.A, 16) ||
       !aligned_to(p.B, 16))
@@ -476,7 +477,8 @@ bool bf16f_eligible(const GemmParams& p, int batch) {
 }
 
 bool bf16t_eligible(const GemmParams& p, int batch) {
-  if (batch != 1 || p.nseg != 1 || p.zdiv != 1 || p.alpha != 1.f || p.kext != 0) return false;
+  if (batch != 1 || p.nseg != 1 || p.zdiv != 1 || p.alpha != 1.f || p.kext != 0 || p.causal)
+    return false;
   if (p.M < BM || p.N < 64 || p.N % 64 != 0 || p.K % BK != 0) return false;
   if (p.lda % 8 != 0 || p.lda < 64 || p.ldb % 8 != 0 || p.ldb < p.N || !aligned_to(p.A, 16) ||
       !aligned_to(p.B, 16))

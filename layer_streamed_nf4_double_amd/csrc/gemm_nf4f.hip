@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
 static bool aligned(const void* q, uintptr_t a) { return ((uintptr_t)q & (a - 1)) == 0; }
 
 bool nf4f_eligible(const GemmParams& p, int batch) {
-  if (batch != 1 || p.nseg != 1 || p.zdiv != 1 || p.alpha != 1.f) return false;
+  if (batch != 1 || p.nseg != 1 || p.zdiv != 1 || p.alpha != 1.f || p.causal) return false;
   if (p.M < FM || p.K % FK != 0 || p.rowlen != p.K) return false;
   if (p.lda % 8 != 0 || !aligned(p.A, 16) || !aligned(p.B, 16) || !aligned(p.absmax, 4))
     return false;

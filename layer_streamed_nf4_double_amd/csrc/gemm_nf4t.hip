@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256) void nf4t_kernel(const GemmParams p) {
 static bool aligned16(const void* q) { return ((uintptr_t)q & 15) == 0; }
 
 bool nf4t_eligible(const GemmParams& p, int batch) {
-  if (batch != 1 || p.nseg != 1 || p.zdiv != 1 || p.alpha != 1.f) return false;
+  if (batch != 1 || p.nseg != 1 || p.zdiv != 1 || p.alpha != 1.f || p.causal) return false;
   if (p.M < TM || p.K % TK != 0 || p.rowlen != p.N || p.N % 64 != 0 || p.N < 128) return false;
   if (p.lda % 8 != 0 || !aligned16(p.A) || !aligned16(p.B) || ((uintptr_t)p.absmax & 3) != 0)
     return false;

@@ -872,6 +872,7 @@ static lsn_status layer_forward(lsn_ctx* c, int layer, const uint8_t* rec, const
     p.C = c->scores; p.ldc = S;
     p.sC_o = (int64_t)nq * S * S; p.sC_i = (int64_t)S * S;
     p.alpha = 1.0f / sqrtf((float)d);
+    p.causal = CAUSAL_SKIP_UPPER;  // the softmax reads keys <= query only
     HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_K, c->n_seq * nq));
   }
   softmax_causal(c->scores, c->Pf, c->Pb, S, (int64_t)c->n_seq * nq * S, s);
@@ -885,6 +886,7 @@ static lsn_status layer_forward(lsn_ctx* c, int layer, const uint8_t* rec, const
     p.sB_o = (int64_t)S * QKV; p.sB_i = d;
     p.C = c->O; p.ldc = QD; p.cmode = C_BF16;
     p.sC_o = (int64_t)S * QD; p.sC_i = d;
+    p.causal = CAUSAL_K_TO_ROW;  // P is zero for keys > query
     HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, c->n_seq * nq));
   }
   kext = lora_fwd_ext(c, layer, G_O, c->O, QD, T);
@@ -936,6 +938,7 @@ static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, cons
     p.sB_o = (int64_t)S * QKV; p.sB_i = d;
     p.C = c->scores; p.ldc = S;
     p.sC_o = (int64_t)nq * S * S; p.sC_i = (int64_t)S * S;
+    p.causal = CAUSAL_SKIP_UPPER;  // the softmax backward reads keys <= query only
     HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_K, Z));
   }
   {  // dV[kv] = sum over its q heads of P^T dO
@@ -949,6 +952,7 @@ static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, cons
     p.nseg = grp;
     p.C = c->dqkv + QD + KVD; p.ldc = QKV;
     p.sC_o = (int64_t)S * QKV; p.sC_i = d;
+    p.causal = CAUSAL_K_FROM_ROW;  // P^T is zero for queries < key
     HIPCHK(c, cgemm(c, p, A_BF16_R, B_BF16_R, c->n_seq * nkv));
   }
   softmax_bwd(c->Pf, c->scores, c->Pb, S, (int64_t)Z * S, s);  // dS (bf16) over Pb
@@ -964,6 +968,7 @@ static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, cons
     p.C = c->dqkv; p.ldc = QKV;
     p.sC_o = (int64_t)S * QKV; p.sC_i = d;
     p.alpha = scale;
+    p.causal = CAUSAL_K_TO_ROW;  // dS is zero for keys > query
     HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, Z));
   }
   {  // dK[kv] = scale sum over its q heads of dS^T Q
@@ -978,6 +983,7 @@ static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, cons
     p.C = c->dqkv + QD; p.ldc = QKV;
     p.sC_o = (int64_t)S * QKV; p.sC_i = d;
     p.alpha = scale;
+    p.causal = CAUSAL_K_FROM_ROW;  // dS^T is zero for queries < key
     HIPCHK(c, cgemm(c, p, A_BF16_R, B_BF16_R, c->n_seq * nkv));
   }
   rope_bwd(c->dqkv, c->dqkvb, T, S, nq, nkv, d, g.rope_theta, s);

@@ -176,6 +176,29 @@ def test_streamed_equals_resident_bitwise(torch, n_layers):
     _assert_bit_identical(a, c)
 
 
+def test_wide_heads_long_sequence_vs_oracle(torch):
+    """head_dim 272 (> 256) and a 2304-token sequence (> 2048): the shapes
+    for which RoPE and the causal softmax run their scalar kernels instead of
+    the 16-byte ones.  One SFT step with B != 0 against the oracle."""
+    w = dict(TINY, n_layers=1, n_heads=1, n_kv_heads=1, head_dim=272, seq_len=2304)
+    tokens = synth.sft_tokens(w)
+    say("[wide-heads] oracle")
+    cfg, layers, lora, head = oracle_model(w, b_zero=False)
+    o = om.sft_step(cfg, layers, lora, head, tokens, LR)
+    say("[wide-heads] gpu stream_host")
+    m = gpu_model(w, "stream_host", b_zero=False)
+    loss, logp = _run_sft(torch, m, tokens)
+    g = _grads(m, w)
+    m.close()
+    assert abs(loss - o["loss"]) <= 2e-2 * abs(o["loss"])
+    assert_close(logp, o["logp"], 2e-2, "logp")
+    for p in ("q", "v"):
+        _, _, dA, dB = g[0][p]
+        oA, oB = o["grads"][0][p]
+        assert_close(dA, oA, 5e-2, f"dA {p}")
+        assert_close(dB, oB, 5e-2, f"dB {p}")
+
+
 def _load_layer_from(m, w, layer, src_layer):
     """Loads the record built from layer src_layer's seeded weights as layer."""
     from layer_streamed_nf4_double_amd import _lib as L
