@@ -49,7 +49,8 @@ struct GemmParams {
   int64_t part_floats = 0;
   int ksplit = 1;      // set by gemm()
   int64_t pstride = 0;  // floats from one split's partial sums to the next (set by gemm())
-  // optional timing events recorded right before / after the main kernel
+  // optional timing events that record the main kernel's start and end (passed
+  // to hipExtLaunchKernelGGL, so they add no dispatch of their own)
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   float levels[16] = {};  // NF4 code levels
 };

@@ -32,6 +32,8 @@
 // weights live (a streamed slot or a resident record): the kernel only sees
 // byte offsets inside the record.
 #include "common.h"
+#include <hip/hip_ext.h>
+
 #include "gemm.h"
 #include <type_traits>
 
@@ -643,10 +645,10 @@ int gemm_tile(const GemmParams& p, int opa, int opb, int batch) {
 template <int BM, int BN, int WGM, int WGN, int NS, int OPA, int OPB>
 static hipError_t launch_t(const GemmParams& p, int batch, hipStream_t s) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  if (p.ev0) (void)hipEventRecord(p.ev0, s);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, NS, OPA, OPB>), dim3(tiles, p.ksplit, batch),
-                     dim3(WGM * WGN * 64), 0, s, p);
-  if (p.ev1) (void)hipEventRecord(p.ev1, s);
+  // the timing events, when given, ride on the kernel's own dispatch (no
+  // extra packets around it)
+  hipExtLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, NS, OPA, OPB>), dim3(tiles, p.ksplit, batch),
+                        dim3(WGM * WGN * 64), 0, s, p.ev0, p.ev1, 0, p);
   if (p.ksplit > 1) gemm_reduce_launch(p, s);
   return hipGetLastError();
 }

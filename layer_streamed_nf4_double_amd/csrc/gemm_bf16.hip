@@ -23,6 +23,8 @@
 //
 // Determinism: every output element is reduced by one lane in a fixed order.
 #include "common.h"
+#include <hip/hip_ext.h>
+
 #include "gemm.h"
 #include "nf4_direct.h"
 #include <algorithm>
@@ -494,14 +496,17 @@ hipError_t bf16t_launch(GemmParams p, hipStream_t s) {
   p.pstride = split_stride(p.M, p.N);
   if (p.ksplit > 1 && (!p.part || p.part_floats < p.ksplit * p.pstride)) p.ksplit = 1;
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  if (p.ev0) (void)hipEventRecord(p.ev0, s);
   const dim3 grid(tiles, p.ksplit, 1);
-  if (p.ksplit > 1) hipLaunchKernelGGL(bf16t_kernel<-1>, grid, dim3(256), 0, s, p);
-  else if (p.cmode == C_F32) hipLaunchKernelGGL(bf16t_kernel<C_F32>, grid, dim3(256), 0, s, p);
-  else if (p.cmode == C_F32_ACC) hipLaunchKernelGGL(bf16t_kernel<C_F32_ACC>, grid, dim3(256), 0, s, p);
-  else if (p.cmode == C_F32_RES) hipLaunchKernelGGL(bf16t_kernel<C_F32_RES>, grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(bf16t_kernel<C_BF16>, grid, dim3(256), 0, s, p);
-  if (p.ev1) (void)hipEventRecord(p.ev1, s);
+  if (p.ksplit > 1)
+    hipExtLaunchKernelGGL(bf16t_kernel<-1>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+  else if (p.cmode == C_F32)
+    hipExtLaunchKernelGGL(bf16t_kernel<C_F32>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+  else if (p.cmode == C_F32_ACC)
+    hipExtLaunchKernelGGL(bf16t_kernel<C_F32_ACC>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+  else if (p.cmode == C_F32_RES)
+    hipExtLaunchKernelGGL(bf16t_kernel<C_F32_RES>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+  else
+    hipExtLaunchKernelGGL(bf16t_kernel<C_BF16>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
   if (p.ksplit > 1) gemm_reduce_launch(p, s);
   return hipGetLastError();
 }
@@ -511,14 +516,17 @@ hipError_t bf16f_launch(GemmParams p, hipStream_t s) {
   p.pstride = split_stride(p.M, p.N);
   if (p.ksplit > 1 && (!p.part || p.part_floats < p.ksplit * p.pstride)) p.ksplit = 1;
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  if (p.ev0) (void)hipEventRecord(p.ev0, s);
   const dim3 grid(tiles, p.ksplit, 1);
-  if (p.ksplit > 1) hipLaunchKernelGGL(bf16f_kernel<-1>, grid, dim3(256), 0, s, p);
-  else if (p.cmode == C_F32) hipLaunchKernelGGL(bf16f_kernel<C_F32>, grid, dim3(256), 0, s, p);
-  else if (p.cmode == C_F32_ACC) hipLaunchKernelGGL(bf16f_kernel<C_F32_ACC>, grid, dim3(256), 0, s, p);
-  else if (p.cmode == C_F32_RES) hipLaunchKernelGGL(bf16f_kernel<C_F32_RES>, grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(bf16f_kernel<C_BF16>, grid, dim3(256), 0, s, p);
-  if (p.ev1) (void)hipEventRecord(p.ev1, s);
+  if (p.ksplit > 1)
+    hipExtLaunchKernelGGL(bf16f_kernel<-1>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+  else if (p.cmode == C_F32)
+    hipExtLaunchKernelGGL(bf16f_kernel<C_F32>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+  else if (p.cmode == C_F32_ACC)
+    hipExtLaunchKernelGGL(bf16f_kernel<C_F32_ACC>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+  else if (p.cmode == C_F32_RES)
+    hipExtLaunchKernelGGL(bf16f_kernel<C_F32_RES>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+  else
+    hipExtLaunchKernelGGL(bf16f_kernel<C_BF16>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
   if (p.ksplit > 1) gemm_reduce_launch(p, s);
   return hipGetLastError();
 }

@@ -38,6 +38,8 @@
 // Determinism: every output element is reduced by one lane in a fixed order
 // (split-k partial sums are added in split order by gemm_reduce_launch).
 #include "common.h"
+#include <hip/hip_ext.h>
+
 #include "gemm.h"
 #include "nf4_direct.h"
 #include <algorithm>
@@ -386,14 +388,17 @@ hipError_t nf4t_launch(GemmParams p, hipStream_t s) {
   p.pstride = split_stride(p.M, p.N);
   if (p.ksplit > 1 && (!p.part || p.part_floats < p.ksplit * p.pstride)) p.ksplit = 1;
   const int tiles = ((p.M + TM - 1) / TM) * ((p.N + TN - 1) / TN);
-  if (p.ev0) (void)hipEventRecord(p.ev0, s);
   const dim3 grid(tiles, p.ksplit, 1);
-  if (p.ksplit > 1) hipLaunchKernelGGL(nf4t_kernel<-1>, grid, dim3(256), 0, s, p);
-  else if (p.cmode == C_F32) hipLaunchKernelGGL(nf4t_kernel<C_F32>, grid, dim3(256), 0, s, p);
-  else if (p.cmode == C_F32_ACC) hipLaunchKernelGGL(nf4t_kernel<C_F32_ACC>, grid, dim3(256), 0, s, p);
-  else if (p.cmode == C_F32_RES) hipLaunchKernelGGL(nf4t_kernel<C_F32_RES>, grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(nf4t_kernel<C_BF16>, grid, dim3(256), 0, s, p);
-  if (p.ev1) (void)hipEventRecord(p.ev1, s);
+  if (p.ksplit > 1)
+    hipExtLaunchKernelGGL(nf4t_kernel<-1>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+  else if (p.cmode == C_F32)
+    hipExtLaunchKernelGGL(nf4t_kernel<C_F32>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+  else if (p.cmode == C_F32_ACC)
+    hipExtLaunchKernelGGL(nf4t_kernel<C_F32_ACC>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+  else if (p.cmode == C_F32_RES)
+    hipExtLaunchKernelGGL(nf4t_kernel<C_F32_RES>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+  else
+    hipExtLaunchKernelGGL(nf4t_kernel<C_BF16>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
   if (p.ksplit > 1) gemm_reduce_launch(p, s);
   return hipGetLastError();
 }
