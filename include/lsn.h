@@ -77,6 +77,19 @@ typedef struct {
   int32_t mode;            /* LSN_RESIDENT | LSN_STREAM_HOST | LSN_STREAM_FILE */
   const char* store_path;  /* LSN_STREAM_FILE: file that holds the layer records */
   uint64_t vram_budget;    /* 0 = none; else lsn_create refuses a larger workspace */
+  /* 1 (streamed modes only): the embedding and LM-head tables stay in the
+   * library's pinned host memory instead of the workspace; the embedding
+   * gather and the head backward's target rows read them over the host link,
+   * and each LM-head pass streams W_lm in slot-sized row chunks through the
+   * two layer slots (page "Soup: Fine-Tune an 8B Model on a 4 GB GPU", "The
+   * Core Idea: Layer Streaming": only the current layer and the adapter
+   * need to sit in VRAM).  0: both tables live in the workspace. */
+  int32_t head_on_host;
+  /* vocabulary rows per LM-head chunk: 0 picks them (about 256 output tiles
+   * at max_tokens, at least 16384, and with head_on_host at most one slot of
+   * W_lm rows); else a multiple of 8, at most one slot of rows with
+   * head_on_host.  The logits buffer holds max_tokens x rows fp32. */
+  int32_t head_chunk_rows;
 } lsn_config;
 
 /* ---------------------------------------------------------------------------

@@ -41,7 +41,8 @@ class lsn_config(ctypes.Structure):
                 ("lora_rank", ctypes.c_int32), ("lora_alpha", ctypes.c_float),
                 ("lora_targets", ctypes.c_uint32), ("max_tokens", ctypes.c_int32),
                 ("max_seq_len", ctypes.c_int32), ("mode", ctypes.c_int32),
-                ("store_path", ctypes.c_char_p), ("vram_budget", ctypes.c_uint64)]
+                ("store_path", ctypes.c_char_p), ("vram_budget", ctypes.c_uint64),
+                ("head_on_host", ctypes.c_int32), ("head_chunk_rows", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p

@@ -113,7 +113,10 @@ struct lsn_ctx {
 
   // device regions
   uint8_t* records = nullptr;  // resident: L records; streamed: 2 slots
+  // embed / lm_head: device tables, or with head_on_host device-visible
+  // pointers to the pinned host copies embed_h / lm_head_h
   uint16_t *embed = nullptr, *lm_head = nullptr, *final_norm = nullptr;
+  uint16_t *embed_h = nullptr, *lm_head_h = nullptr;
   float *lora_p = nullptr, *lora_g = nullptr;
   uint64_t lora_n = 0;
   std::vector<int64_t> lA, lB;  // float offsets of A and B per (layer, proj); -1 if none
@@ -287,6 +290,20 @@ static bool cfg_valid(const lsn_config* g, std::string* why) {
   if (g->mode == LSN_STREAM_FILE && (!g->store_path || !g->store_path[0]))
     return bad("file mode needs store_path");
   if (!(g->rms_eps > 0.f) || !(g->rope_theta > 0.f)) return bad("bad eps / theta");
+  if (g->head_on_host && g->mode == LSN_RESIDENT)
+    return bad("head_on_host needs a streamed base (the head streams through its slots)");
+  if (g->head_chunk_rows < 0 || g->head_chunk_rows % 8) return bad("head_chunk_rows must be a multiple of 8");
+  return true;
+}
+
+// Checks that need the record layout: a head chunk must fit a slot.
+static bool layout_valid(const lsn_ctx* c, std::string* why) {
+  const lsn_config& g = c->cfg;
+  if (g.head_on_host && g.head_chunk_rows > 0 &&
+      (uint64_t)g.head_chunk_rows * g.hidden * 2 > c->rec_bytes) {
+    *why = "head_chunk_rows exceed one slot of W_lm rows";
+    return false;
+  }
   return true;
 }
 
@@ -335,12 +352,18 @@ static uint64_t carve(lsn_ctx* c, char* base) {
   const int64_t T = g.max_tokens, S = g.max_seq_len, H = g.hidden, F = g.ffn, V = g.vocab;
   const int64_t r = g.lora_rank;
   c->vchunk = vchunk_for(T);
+  if (g.head_on_host)  // a chunk of W_lm rows fits one slot
+    c->vchunk = (int)std::max<int64_t>(
+        256, std::min<int64_t>(c->vchunk, (int64_t)(c->rec_bytes / (uint64_t)(H * 2)) / 256 * 256));
+  if (g.head_chunk_rows > 0) c->vchunk = g.head_chunk_rows;
   Carver cv;
   auto P = [&](uint64_t bytes) -> char* { const uint64_t o = cv.take(bytes); return base ? base + o : nullptr; };
   const int nrec = (g.mode == LSN_RESIDENT) ? g.n_layers : 2;
   c->records = (uint8_t*)P((uint64_t)nrec * c->rec_bytes);
-  c->embed = (uint16_t*)P(V * H * 2);
-  c->lm_head = g.tied_embeddings ? c->embed : (uint16_t*)P(V * H * 2);
+  if (!g.head_on_host) {
+    c->embed = (uint16_t*)P(V * H * 2);
+    c->lm_head = g.tied_embeddings ? c->embed : (uint16_t*)P(V * H * 2);
+  }
   c->final_norm = (uint16_t*)P(H * 2);
   // adapters
   c->lA.assign((size_t)g.n_layers * NPROJ, -1);
@@ -1175,6 +1198,7 @@ lsn_status lsn_workspace_bytes(const lsn_config* cfg, uint64_t* bytes) {
   lsn_ctx tmp;
   tmp.cfg = *cfg;
   record_layout(&tmp);
+  if (!layout_valid(&tmp, &why)) return LSN_ERR_INVALID;
   *bytes = carve(&tmp, nullptr);
   return LSN_OK;
 }
@@ -1200,6 +1224,10 @@ lsn_status lsn_create(const lsn_config* cfg, void* dev_ws, uint64_t ws_bytes, vo
   if (cfg->store_path) c->store_path = cfg->store_path;
   c->cfg.store_path = c->store_path.c_str();
   record_layout(c);
+  if (!layout_valid(c, &why)) {
+    delete c;
+    return LSN_ERR_INVALID;
+  }
   c->ws_needed = carve(c, nullptr);
   if (!dev_ws || ws_bytes < c->ws_needed || (cfg->vram_budget && c->ws_needed > cfg->vram_budget)) {
     delete c;
@@ -1265,6 +1293,8 @@ void lsn_destroy(lsn_ctx* c) {
     if (c->bounce[i]) (void)hipHostFree(c->bounce[i]);
   }
   for (hipEvent_t e : c->evpool) (void)hipEventDestroy(e);
+  if (c->lm_head_h && c->lm_head_h != c->embed_h) (void)hipHostFree(c->lm_head_h);
+  if (c->embed_h) (void)hipHostFree(c->embed_h);
   if (c->copy) (void)hipStreamDestroy(c->copy);
   if (c->store) (void)hipHostFree(c->store);
   if (c->rd.th.joinable()) {
@@ -1357,8 +1387,27 @@ lsn_status lsn_load_head(lsn_ctx* c, const uint16_t* embed, const uint16_t* lm_h
   if (!embed || !final_norm || (!c->cfg.tied_embeddings && !lm_head))
     return fail(c, LSN_ERR_INVALID, "bad lsn_load_head arguments");
   const uint64_t vb = (uint64_t)c->cfg.vocab * c->cfg.hidden * 2;
-  HIPCHK(c, hipMemcpy(c->embed, embed, vb, hipMemcpyHostToDevice));
-  if (!c->cfg.tied_embeddings) HIPCHK(c, hipMemcpy(c->lm_head, lm_head, vb, hipMemcpyHostToDevice));
+  if (c->cfg.head_on_host) {
+    // pinned host copies, read by the kernels through device-visible pointers
+    if (!c->embed_h) {
+      if (hipHostMalloc((void**)&c->embed_h, vb, hipHostMallocDefault) != hipSuccess)
+        return fail(c, LSN_ERR_HIP, "pinned host embedding table");
+      if (!c->cfg.tied_embeddings &&
+          hipHostMalloc((void**)&c->lm_head_h, vb, hipHostMallocDefault) != hipSuccess)
+        return fail(c, LSN_ERR_HIP, "pinned host LM-head table");
+      if (c->cfg.tied_embeddings) c->lm_head_h = c->embed_h;
+      HIPCHK(c, hipHostGetDevicePointer((void**)&c->embed, c->embed_h, 0));
+      HIPCHK(c, hipHostGetDevicePointer((void**)&c->lm_head, c->lm_head_h, 0));
+    }
+    HIPCHK(c, hipStreamSynchronize(c->cs));  // no kernel or copy still reads the old tables
+    HIPCHK(c, hipStreamSynchronize(c->copy));
+    memcpy(c->embed_h, embed, vb);
+    if (!c->cfg.tied_embeddings) memcpy(c->lm_head_h, lm_head, vb);
+  } else {
+    HIPCHK(c, hipMemcpy(c->embed, embed, vb, hipMemcpyHostToDevice));
+    if (!c->cfg.tied_embeddings)
+      HIPCHK(c, hipMemcpy(c->lm_head, lm_head, vb, hipMemcpyHostToDevice));
+  }
   HIPCHK(c, hipMemcpy(c->final_norm, final_norm, (uint64_t)c->cfg.hidden * 2,
                       hipMemcpyHostToDevice));
   c->head_loaded = true;
@@ -1485,13 +1534,29 @@ lsn_status lsn_backward_layer(lsn_ctx* c, int32_t layer, const float* h_in, cons
   return layer_end(c);
 }
 
-static lsn_status lm_logits_chunk(lsn_ctx* c, int v0, int Vc) {
+static lsn_status lm_logits_chunk(lsn_ctx* c, const uint16_t* W, int Vc) {
   GemmParams p = base_params(c);
   p.M = c->T; p.N = Vc; p.K = c->cfg.hidden;
   p.A = c->nf; p.lda = c->cfg.hidden;
-  p.B = c->lm_head + (int64_t)v0 * c->cfg.hidden; p.ldb = c->cfg.hidden;
+  p.B = W; p.ldb = c->cfg.hidden;
   p.C = c->logits; p.ldc = Vc;
   HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_K, 1));
+  return LSN_OK;
+}
+
+// head_on_host: W_lm rows [v0, v0 + Vc) into slot s on the copy stream, after
+// the slot's previous user is done (as copy_into_slot does for records).
+static lsn_status copy_head_chunk(lsn_ctx* c, int v0, int Vc, int s) {
+  uint8_t* dst = c->records + (uint64_t)s * c->rec_bytes;
+  if (c->slot_used[s]) HIPCHK(c, hipStreamWaitEvent(c->copy, c->slot_free[s], 0));
+  if (c->copy_issued[s]) HIPCHK(c, hipEventSynchronize(c->copy_done[s]));
+  const uint64_t bytes = (uint64_t)Vc * c->cfg.hidden * 2;
+  HIPCHK(c, hipMemcpyAsync(dst, c->lm_head_h + (int64_t)v0 * c->cfg.hidden, bytes,
+                           hipMemcpyHostToDevice, c->copy));
+  HIPCHK(c, hipEventRecord(c->copy_done[s], c->copy));
+  c->copy_issued[s] = true;
+  c->slot_layer[s] = -1;  // the slot holds no layer record any more
+  c->bytes_h2d += bytes;
   return LSN_OK;
 }
 
@@ -1508,25 +1573,51 @@ lsn_status lsn_lm_head_logprobs(lsn_ctx* c, const float* h, const int32_t* targe
   if (!c->head_loaded) return fail(c, LSN_ERR_STATE, "head tables not loaded");
   const int T = c->T, V = c->cfg.vocab, H = c->cfg.hidden;
   const bool acc = want_grad_state != 0;
+  // head_on_host: W_lm streams through the two slots chunk by chunk, the
+  // next chunk copying while this one computes; the slots' layer records
+  // are overwritten, so no layer pass may be under way
+  const bool host = c->cfg.head_on_host != 0;
+  if (host && c->pos < c->order.size())
+    return fail(c, LSN_ERR_STATE, "lm_head with head_on_host inside a layer pass");
+  const int nch = (V + c->vchunk - 1) / c->vchunk;
+  if (host)
+    for (int i = 0; i < std::min(nch, 2); ++i) {
+      lsn_status st = copy_head_chunk(c, i * c->vchunk, std::min(c->vchunk, V - i * c->vchunk), i);
+      if (st != LSN_OK) return st;
+    }
   rmsnorm_fwd(h, c->final_norm, T, H, c->cfg.rms_eps, c->nf, c->rstdf, c->cs);
-  for (int v0 = 0; v0 < V; v0 += c->vchunk) {
-    const int Vc = std::min(c->vchunk, V - v0);
-    lsn_status st = lm_logits_chunk(c, v0, Vc);
+  for (int i = 0, v0 = 0; v0 < V; ++i, v0 += c->vchunk) {
+    const int Vc = std::min(c->vchunk, V - v0), sl = i & 1;
+    const uint16_t* W = c->lm_head + (int64_t)v0 * H;
+    if (host) {
+      HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_done[sl], 0));
+      W = reinterpret_cast<const uint16_t*>(c->records + (uint64_t)sl * c->rec_bytes);
+    }
+    lsn_status st = lm_logits_chunk(c, W, Vc);
     if (st != LSN_OK) return st;
     if (!acc) {
       lse_chunk(c->logits, T, Vc, v0, targets, c->run_m, c->run_s, c->tlogit, v0 == 0, c->cs);
-      continue;
+    } else {
+      lse_chunk_acc(c->logits, T, Vc, v0, targets, c->run_m, c->run_s, c->tlogit, c->head_f,
+                    c->dlog, v0 == 0, c->cs);
+      if (v0 > 0) scale_rows(c->dnf, c->head_f, T, H, c->cs);
+      GemmParams p = base_params(c);  // E~ (+)= p~ W_chunk
+      p.M = T; p.N = H; p.K = Vc;
+      p.A = c->dlog; p.lda = Vc;
+      p.B = W; p.ldb = H;
+      p.C = c->dnf; p.ldc = H;
+      p.cmode = (v0 == 0) ? C_F32 : C_F32_ACC;
+      HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, 1));
     }
-    lse_chunk_acc(c->logits, T, Vc, v0, targets, c->run_m, c->run_s, c->tlogit, c->head_f,
-                  c->dlog, v0 == 0, c->cs);
-    if (v0 > 0) scale_rows(c->dnf, c->head_f, T, H, c->cs);
-    GemmParams p = base_params(c);  // E~ (+)= p~ W_chunk
-    p.M = T; p.N = H; p.K = Vc;
-    p.A = c->dlog; p.lda = Vc;
-    p.B = c->lm_head + (int64_t)v0 * H; p.ldb = H;
-    p.C = c->dnf; p.ldc = H;
-    p.cmode = (v0 == 0) ? C_F32 : C_F32_ACC;
-    HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, 1));
+    if (host) {
+      HIPCHK(c, hipEventRecord(c->slot_free[sl], c->cs));
+      c->slot_used[sl] = true;
+      if (i + 2 < nch) {
+        const int v2 = (i + 2) * c->vchunk;
+        st = copy_head_chunk(c, v2, std::min(c->vchunk, V - v2), sl);
+        if (st != LSN_OK) return st;
+      }
+    }
   }
   lse_final(c->run_m, c->run_s, c->tlogit, targets, T, logp, c->lse, acc ? c->head_f : nullptr,
             c->cs);

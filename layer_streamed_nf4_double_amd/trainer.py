@@ -27,7 +27,8 @@ PREF_LOSSES = {"dpo": L.LSN_LOSS_DPO, "simpo": L.LSN_LOSS_SIMPO, "orpo": L.LSN_L
 
 
 def make_config(shape, mode="stream_host", max_tokens=None, max_seq_len=None,
-                lora_targets=("q", "v"), store_path=None, vram_budget=0):
+                lora_targets=("q", "v"), store_path=None, vram_budget=0, head_on_host=False,
+                head_chunk_rows=0):
     """lsn_config from a shape dict (n_layers, hidden, n_heads, n_kv_heads,
     head_dim, ffn, vocab, rms_eps, rope_theta, lora_rank, lora_alpha, tied)."""
     cfg = L.lsn_config()
@@ -49,6 +50,8 @@ def make_config(shape, mode="stream_host", max_tokens=None, max_seq_len=None,
     cfg.mode = MODES[mode]
     cfg.store_path = store_path.encode() if store_path else None
     cfg.vram_budget = vram_budget
+    cfg.head_on_host = int(bool(head_on_host))
+    cfg.head_chunk_rows = head_chunk_rows
     return cfg
 
 
@@ -56,11 +59,14 @@ class LayerStreamedLoRA:
     """A context plus the activation tensors of one step."""
 
     def __init__(self, shape, mode="stream_host", max_tokens=None, max_seq_len=None,
-                 lora_targets=("q", "v"), store_path=None, device="cuda:0", stream=None):
+                 lora_targets=("q", "v"), store_path=None, device="cuda:0", stream=None,
+                 head_on_host=False, head_chunk_rows=0):
         """mode: resident | stream_host | stream_file | auto.  'auto' keeps the
         base in pinned RAM when it fits and in a file (store_path, or a file
         in $TMPDIR) when it does not; every mode is pre-flighted against the
-        free device memory (adapter.NoFit)."""
+        free device memory (adapter.NoFit).  head_on_host (streamed modes):
+        the embedding and LM-head tables stay in pinned host memory and W_lm
+        streams through the layer slots."""
         import tempfile
 
         import torch
@@ -70,7 +76,8 @@ class LayerStreamedLoRA:
         self.shape = dict(shape)
         self.device = torch.device(device)
         probe = make_config(shape, "stream_host" if mode == "auto" else mode, max_tokens,
-                            max_seq_len, lora_targets, store_path)
+                            max_seq_len, lora_targets, store_path, head_on_host=head_on_host,
+                            head_chunk_rows=head_chunk_rows)
         free, _ = torch.cuda.mem_get_info(self.device)
         mode = adapter.plan_run(shape["n_layers"], L.lsn_config_record_bytes(probe),
                                 L.lsn_workspace_bytes(probe), free,
@@ -79,7 +86,8 @@ class LayerStreamedLoRA:
         if mode == "stream_file" and not store_path:
             store_path = os.path.join(tempfile.gettempdir(), f"lsn_store_{os.getpid()}.bin")
         self.mode = mode
-        self.cfg = make_config(shape, mode, max_tokens, max_seq_len, lora_targets, store_path)
+        self.cfg = make_config(shape, mode, max_tokens, max_seq_len, lora_targets, store_path,
+                               head_on_host=head_on_host, head_chunk_rows=head_chunk_rows)
         self.lora_targets = tuple(lora_targets)
         self.ws_bytes = L.lsn_workspace_bytes(self.cfg)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)

@@ -55,10 +55,11 @@ def oracle_model(w, b_zero, lora_targets=("q", "v"), dtype=np.float64):
 
 
 def gpu_model(w, mode, b_zero, lora_targets=("q", "v"), store_path=None, max_tokens=None,
-              max_seq_len=None):
+              max_seq_len=None, head_on_host=False, head_chunk_rows=0):
     from layer_streamed_nf4_double_amd import _lib as L
     from layer_streamed_nf4_double_amd.trainer import LayerStreamedLoRA
     m = LayerStreamedLoRA(w, mode, max_tokens=max_tokens, max_seq_len=max_seq_len,
+                          head_on_host=head_on_host, head_chunk_rows=head_chunk_rows,
                           lora_targets=lora_targets, store_path=store_path)
     ones = np.full(w["hidden"], BF16_ONE, np.uint16)
     for layer in range(w["n_layers"]):

@@ -126,6 +126,26 @@ def test_invalid_configs_rejected():
         assert e.value.status == L.LSN_ERR_INVALID, field
 
 
+def test_head_on_host_workspace():
+    """With head_on_host the embedding and LM-head tables leave the workspace
+    (2 V H bf16 for an untied head, V H for a tied one); the option needs a
+    streamed base."""
+    import synth
+    from layer_streamed_nf4_double_amd import trainer
+    L = _lib()
+    for name in ("llama3.1-8b-shaped", "qwen2.5-3b-shaped", "tiny"):
+        w = dict(synth.WORKLOADS[name], n_layers=4)
+        dev = L.lsn_workspace_bytes(trainer.make_config(w, "stream_host"))
+        host = L.lsn_workspace_bytes(trainer.make_config(w, "stream_host", head_on_host=True))
+        tables = (1 if w["tied"] else 2) * w["vocab"] * w["hidden"] * 2
+        # the smaller LM-head chunk (one slot of W_lm rows) also shrinks its buffers
+        assert tables <= dev - host <= tables + 6 * w["seq_len"] * w["n_seq"] * 65536, name
+        cfg = trainer.make_config(w, "resident", head_on_host=True)
+        with pytest.raises(L.LsnError) as e:
+            L.lsn_workspace_bytes(cfg)
+        assert e.value.status == L.LSN_ERR_INVALID
+
+
 def test_record_sizes_match_layout():
     """Per-layer record = NF4 codes (P/2) + absmax (P/16) + norms, 4 KiB aligned."""
     import synth

@@ -176,6 +176,68 @@ def test_streamed_equals_resident_bitwise(torch, n_layers):
     _assert_bit_identical(a, c)
 
 
+@pytest.mark.parametrize("mode,tied", [("stream_host", False), ("stream_file", False),
+                                       ("stream_host", True)])
+def test_head_on_host_matches_device_head(torch, mode, tied, tmp_path):
+    """Embedding and LM-head tables in pinned host memory, W_lm streamed
+    through the layer slots in two chunks (768 + 256 rows here).  Two SFT
+    steps equal, bitwise, the run with the tables on the device and the same
+    768-row chunks, and match the oracle within the parity bar.  The head
+    displaces the two records the backward would have reused, so each step
+    loads two more."""
+    w = dict(TINY, n_layers=3, tied=tied)
+    tokens = synth.sft_tokens(w)
+    say(f"[head-on-host] {mode} tied={tied} oracle")
+    cfg, layers, lora, head = oracle_model(w, b_zero=False)
+    o = om.sft_step(cfg, layers, lora, head, tokens, LR)
+    dev = gpu_model(w, "stream_host", b_zero=False, head_chunk_rows=768)
+    a = _two_step_record(torch, dev, w, tokens)
+    la, _, _ = dev.stats()
+    dev.close()
+    store = str(tmp_path / "store.bin") if mode == "stream_file" else None
+    host = gpu_model(w, mode, b_zero=False, head_on_host=True, store_path=store)
+    b = _two_step_record(torch, host, w, tokens)
+    lb, _, _ = host.stats()
+    host.close()
+    assert lb - la == 4, (la, lb)
+    lb0, pb0, _ = b[0]
+    assert abs(float(lb0) - o["loss"]) <= 2e-2 * abs(o["loss"])
+    assert_close(pb0, o["logp"], 2e-2, "logp vs oracle")
+    _assert_bit_identical(a, b)
+
+
+def test_head_on_host_dpo(torch):
+    """The fused DPO step with the head tables on the host: both head passes
+    (reference and policy) stream W_lm; policy == reference at B = 0 gives
+    ln 2, and B != 0 equals, bitwise, the device-table run with the same
+    chunks."""
+    w = dict(TINY, n_layers=2)
+    S, P, beta = 64, 16, 0.1
+    rng_tok = synth.tokens((P,), w["vocab"], 88, synth.TID_PROMPT)
+    ch = np.concatenate([rng_tok, synth.tokens((S - P,), w["vocab"], 88, synth.TID_CHOSEN)])
+    rj = np.concatenate([rng_tok, synth.tokens((S - P,), w["vocab"], 88, synth.TID_REJECTED)])
+    tok, tgt = _dev_tokens(torch, np.stack([ch, rj]))
+    m = gpu_model(w, "stream_host", b_zero=True, max_tokens=2 * S, head_on_host=True)
+    out = m.dpo_step(tok, tgt, S, P, beta, None)
+    m.sync()
+    assert abs(float(out.cpu().numpy()[0]) - math.log(2.0)) <= 1e-7
+    m.close()
+    res = []
+    for hoh in (False, True):
+        m = gpu_model(w, "stream_host", b_zero=False, max_tokens=2 * S, head_on_host=hoh,
+                      head_chunk_rows=768)
+        out = m.dpo_step(tok, tgt, S, P, beta, LR)
+        m.sync()
+        res.append((out.cpu().numpy()[:6].copy(), _grads(m, w)))
+        m.close()
+    (o0, g0), (o1, g1) = res
+    assert np.array_equal(_bits(o0), _bits(o1))
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            for x, y in zip(g0[layer][p], g1[layer][p]):
+                assert np.array_equal(_bits(x), _bits(y))
+
+
 def test_wide_heads_long_sequence_vs_oracle(torch):
     """head_dim 272 (> 256) and a 2304-token sequence (> 2048): the shapes
     for which RoPE and the causal softmax run their scalar kernels instead of
