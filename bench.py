@@ -112,13 +112,14 @@ def quantized_layers(w):
             yield layer, codes, absmax, ones, ones
 
 
-def build_model(w, mode, max_tokens, max_seq_len, layers, head, store_path=None):
+def build_model(w, mode, max_tokens, max_seq_len, layers, head, store_path=None,
+                head_on_host=False):
     import numpy as np
 
     import synth
     from layer_streamed_nf4_double_amd.trainer import LayerStreamedLoRA
     m = LayerStreamedLoRA(w, mode, max_tokens=max_tokens, max_seq_len=max_seq_len,
-                          store_path=store_path)
+                          store_path=store_path, head_on_host=head_on_host)
     for layer, codes, absmax, g1, g2 in layers:
         m.load_layer(layer, codes, absmax, g1, g2)
     for layer in range(w["n_layers"]):
@@ -219,6 +220,41 @@ def file_source_leg(torch, L, w, S, layers, head, tok, tgt, rec_bytes, steps):
            "frac": None if not disk else round(gbps / disk, 4),
            "pinned_host_bytes": 2 * int(rec_bytes), "peak_vram_bytes": int(fpeak)}
     log(f"[bench] file source {fdt * 1e3:.0f} ms/step, {S / fdt:.1f} tok/s, {gbps:.2f} GB/s")
+    return out
+
+
+def head_on_host_leg(torch, L, w, S, layers, head, tok, tgt, steps, link_best):
+    """The streamed SFT step with the embedding and LM-head tables in pinned
+    host memory: W_lm streams through the layer slots each step, and the
+    device holds the slots, the adapters and one layer's activations."""
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    m = build_model(w, "stream_host", S, S, layers, head, head_on_host=True)
+    m.sft_step(tok, tgt, 1, S, 1e-4)
+    m.sync()
+    l0, b0, _ = m.stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        m.sft_step(tok, tgt, 1, S, 1e-4)
+    torch.cuda.synchronize()
+    hdt = (time.perf_counter() - t0) / steps
+    l1, b1, _ = m.stats()
+    peak = torch.cuda.max_memory_allocated()
+    loss = float(m.loss[0].item())
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    gbps = (b1 - b0) / steps / hdt / 1e9
+    out = {"tokens_per_s": round(S / hdt, 2), "ms_per_step": round(hdt * 1e3, 2), "steps": steps,
+           "loss": loss, "peak_vram_bytes": int(peak),
+           "layer_loads_per_step": (l1 - l0) / steps,
+           "h2d_bytes_per_step": int((b1 - b0) / steps), "achieved_GBps": round(gbps, 2),
+           "link_frac": round(gbps / link_best, 4),
+           "note": "embedding and LM head in pinned host memory; W_lm streamed through the "
+                   "layer slots each step"}
+    log(f"[bench] head on host: {hdt * 1e3:.1f} ms/step, {S / hdt:.1f} tok/s, "
+        f"peak {peak / 1e9:.2f} GB, {gbps:.1f} GB/s")
     return out
 
 
@@ -514,7 +550,7 @@ def main():
         log(f"[bench] DPO {ddt * 1e3:.1f} ms/step, {2 * S / ddt:.1f} tok/s, loss {out[0]:.4f}")
 
     # ---- the same step with the base resident on the device (peak VRAM side by side) ----
-    resident = projection = file_src = None
+    resident = projection = file_src = head_host = None
     if not args.no_extras:
         if args.mode == "stream_host":
             torch.cuda.reset_peak_memory_stats()
@@ -536,6 +572,9 @@ def main():
             torch.cuda.empty_cache()
             log(f"[bench] resident SFT {rdt * 1e3:.1f} ms/step, peak "
                 f"{resident['peak_vram_bytes'] / 1e9:.2f} GB")
+        if args.mode == "stream_host":
+            head_host = head_on_host_leg(torch, L, w, S, layers, head, tok, tgt,
+                                         max(1, args.steps // 2), link_best)
         if args.mode == "stream_host" and args.file_steps > 0:
             file_src = file_source_leg(torch, L, w, S, layers, head, tok, tgt, rec_bytes,
                                        args.file_steps)
@@ -565,7 +604,8 @@ def main():
             "compute_utilization": {"flops_per_step": step_flops(w, S, 1),
                                     "frac": round(step_flops(w, S, 1) / dt / 1e12
                                                   / MFMA_BF16_PEAK_TFLOPS, 4)},
-            "dpo": dpo, "resident": resident, "file_source": file_src, "projection": projection,
+            "dpo": dpo, "resident": resident, "head_on_host": head_host, "file_source": file_src,
+            "projection": projection,
             "env": environment(torch, w, rec_bytes), "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 
