@@ -1,0 +1,135 @@
+"""Checks at the full size and launch configuration the bench times: the
+Llama-3.1-8B-shaped workload (hidden 4096, FFN 14336, vocabulary 128256,
+32 layers, one sequence of 512 tokens).
+
+The oracle cannot run 32 layers of this model inside a test, so the full
+depth is checked through properties that hold at any size (streamed ==
+resident, bitwise), and the full-size LM head -- the one part of the step
+the layer-shape tests run at a reduced vocabulary -- on sampled rows the
+oracle computes one by one."""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import model as om
+from tests.modelbuild import BF16_ONE, assert_close, gpu_model, oracle_config
+
+pytestmark = pytest.mark.gpu
+
+W8 = synth.WORKLOADS["llama3.1-8b-shaped"]
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available()
+    return t
+
+
+def test_full_size_lm_head_vs_oracle(torch):
+    """The LM head at 512 tokens x 128256 vocabulary rows (the chunked logits,
+    log-sum-exp and expected-row kernels the bench runs) on seeded hidden
+    states: logp and dh of 16 sampled rows against the oracle's head, every
+    row finite, and no prediction at the last position."""
+    from layer_streamed_nf4_double_amd import _lib as L
+    w = dict(W8, n_layers=1)
+    T, H = w["n_seq"] * w["seq_len"], w["hidden"]
+    h = synth.normal((T, H), w["wid"], 0, synth.TID_X, std=1.0)
+    targets = om.sft_targets(synth.sft_tokens(w)).reshape(-1).astype(np.int32)
+    valid = targets >= 0
+    dlogp = np.where(valid, -1.0 / valid.sum(), 0.0).astype(np.float32)
+    say("[head-8b] gpu")
+    m = gpu_model(w, "stream_host", b_zero=True)
+    hd = torch.from_numpy(h).cuda()
+    tg = torch.from_numpy(targets).cuda()
+    dl = torch.from_numpy(dlogp).cuda()
+    logp = torch.empty(T, dtype=torch.float32, device="cuda")
+    dh = torch.empty_like(hd)
+    L.lsn_begin_pass(m.ctx, L.LSN_PASS_FWD, w["n_seq"], w["seq_len"])
+    L.lsn_lm_head_logprobs(m.ctx, hd, tg, logp, 1)
+    L.lsn_lm_head_backward(m.ctx, hd, tg, dl, dh)
+    m.sync()
+    g_logp, g_dh = logp.cpu().numpy(), dh.cpu().numpy()
+    m.close()
+    assert np.all(np.isfinite(g_logp)) and np.all(np.isfinite(g_dh))
+    assert g_logp[-1] == 0.0 and np.all(g_logp[valid] < 0)
+    say("[head-8b] oracle rows")
+    _, lm, _ = synth.head_tables(w)
+    head = dict(lm_head=synth.bf16_to_f32(lm).astype(np.float64), final_norm=np.ones(H))
+    rows = np.sort(np.random.default_rng(7).choice(T - 1, 16, replace=False))
+    o_logp, cache = om.head_logprobs(oracle_config(w), head, h[rows].astype(np.float64),
+                                     targets[rows])
+    o_dh = om.head_backward(oracle_config(w), head, cache, dlogp[rows].astype(np.float64))
+    assert_close(g_logp[rows], o_logp, 2e-2, "logp rows")
+    assert_close(g_dh[rows], o_dh, 2e-2, "dh rows")
+
+
+def _layer_records(w):
+    """NF4 codes and absmax of every layer, quantized once with the
+    library's host codec."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from layer_streamed_nf4_double_amd import _lib as L
+
+    def one(layer):
+        out = [L.lsn_nf4_quantize(synth.layer_weights_f32(w, layer, p)) for p in synth.PROJ]
+        return [c for c, _ in out], [a for _, a in out]
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        return list(ex.map(one, range(w["n_layers"])))
+
+
+def _model(w, mode, records, head):
+    from layer_streamed_nf4_double_amd.trainer import LayerStreamedLoRA
+    m = LayerStreamedLoRA(w, mode)
+    ones = np.full(w["hidden"], BF16_ONE, np.uint16)
+    for layer, (codes, absmax) in enumerate(records):
+        m.load_layer(layer, codes, absmax, ones, ones)
+        for p in ("q", "v"):
+            A, B = synth.lora_init(w, layer, p, b_zero=False)
+            m.set_lora(layer, p, A, B)
+    emb, lm, _ = head
+    m.load_head(emb, lm, ones)
+    return m
+
+
+def test_full_depth_streamed_equals_resident(torch):
+    """One SFT step of the full 8B workload, streamed from pinned host memory
+    and with the base resident on the device: the loss, all 512 logp and
+    the adapter gradients of the first and last layers are the same bits;
+    the streamed step copies each record once in the forward and all but
+    the two last layers again in the backward."""
+    from layer_streamed_nf4_double_amd.trainer import sft_targets
+    w = W8
+    say("[full-8b] quantize 32 layers")
+    records = _layer_records(w)
+    head = synth.head_tables(w)
+    tokens = synth.sft_tokens(w)
+    tok = torch.from_numpy(tokens.reshape(-1).astype(np.int32)).cuda()
+    tgt = torch.from_numpy(sft_targets(tokens)).cuda()
+    S = w["seq_len"]
+    out = {}
+    for mode in ("resident", "stream_host"):
+        say(f"[full-8b] {mode}")
+        m = _model(w, mode, records, head)
+        m.sft_step(tok, tgt, 1, S, None)
+        m.sync()
+        grads = {(l, p): m.get_lora(l, p)[2:] for l in (0, w["n_layers"] - 1) for p in ("q", "v")}
+        out[mode] = (m.loss[0].item(), m.logp[:S].cpu().numpy().copy(), grads, m.stats()[0])
+        m.close()
+        del m
+        torch.cuda.empty_cache()
+    (lr_, pr, gr, _), (ls, ps, gs, loads) = out["resident"], out["stream_host"]
+    assert np.float32(lr_).view(np.uint32) == np.float32(ls).view(np.uint32)
+    assert np.array_equal(pr.view(np.uint32), ps.view(np.uint32))
+    for k in gr:
+        for x, y in zip(gr[k], gs[k]):
+            assert np.any(x != 0), k
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), k
+    assert loads == 2 * w["n_layers"] - 2, loads
