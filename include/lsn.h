@@ -108,7 +108,7 @@ lsn_status lsn_nf4_codebook(float* out16);
  * absmax: host [(n+63)/64].  Multithreaded; deterministic. */
 lsn_status lsn_nf4_quantize(const float* w, uint64_t n, uint8_t* codes, float* absmax);
 /* host inverse: w[e] = fl32(level[code_e] * absmax[e/64]). */
-lsn_status lsn_nf4_dequantize_host(const uint8_t* codes, const float* absmax, uint64_t n, float* w);
+lsn_status lsn_nf4_dequantize(const uint8_t* codes, const float* absmax, uint64_t n, float* w);
 
 /* ---------------------------------------------------------------------------
  * Device NF4 dequantization (all pointers device).  out_bf16 = 0: fp32

@@ -51,7 +51,7 @@ _CFG = ctypes.POINTER(lsn_config)
 _SIGS = {
     "lsn_nf4_codebook": [_P],
     "lsn_nf4_quantize": [_P, _U64, _P, _P],
-    "lsn_nf4_dequantize_host": [_P, _P, _U64, _P],
+    "lsn_nf4_dequantize": [_P, _P, _U64, _P],
     "lsn_nf4_dequant": [_P, _P, _U64, _P, _I32, _P],
     "lsn_nf4_linear_scratch_bytes": [_I32, _I32, _I32, _I32, ctypes.POINTER(_U64)],
     "lsn_nf4_linear_fwd": [_P, _P, _I32, _I32, _I32, _P, _P, _P, _I32, _F, _P, _P, _U64, _P],
@@ -139,11 +139,11 @@ def lsn_nf4_quantize(w):
     return codes, absmax
 
 
-def lsn_nf4_dequantize_host(codes, absmax, n):
+def lsn_nf4_dequantize(codes, absmax, n):
     out = np.zeros(n, np.float32)
-    _check(_lib.lsn_nf4_dequantize_host(_ptr(np.ascontiguousarray(codes)),
+    _check(_lib.lsn_nf4_dequantize(_ptr(np.ascontiguousarray(codes)),
                                         _ptr(np.ascontiguousarray(absmax)), n, _ptr(out)),
-           what="lsn_nf4_dequantize_host")
+           what="lsn_nf4_dequantize")
     return out
 
 

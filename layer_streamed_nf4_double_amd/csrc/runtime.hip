@@ -1032,7 +1032,7 @@ lsn_status lsn_nf4_quantize(const float* w, uint64_t n, uint8_t* codes, float* a
   return nf4_quantize(w, n, codes, absmax) ? LSN_OK : LSN_ERR_INVALID;
 }
 
-lsn_status lsn_nf4_dequantize_host(const uint8_t* codes, const float* absmax, uint64_t n,
+lsn_status lsn_nf4_dequantize(const uint8_t* codes, const float* absmax, uint64_t n,
                                    float* w) {
   if (!codes || !absmax || !w) return n == 0 ? LSN_OK : LSN_ERR_INVALID;
   nf4_dequantize_host(codes, absmax, n, w);

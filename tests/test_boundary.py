@@ -71,7 +71,7 @@ def test_quantize_bit_equal_to_oracle(case):
     oc, oa = onf4.quantize(w)
     assert np.array_equal(codes, oc)
     assert np.array_equal(absmax.view(np.uint32), oa.view(np.uint32))
-    d = L.lsn_nf4_dequantize_host(codes, absmax, w.size)
+    d = L.lsn_nf4_dequantize(codes, absmax, w.size)
     od = onf4.dequantize(oc, oa, w.size)
     assert np.array_equal(d.view(np.uint32), od.view(np.uint32))
 
