@@ -162,6 +162,9 @@ lsn_status lsn_config_record_bytes(const lsn_config* cfg, uint64_t* bytes);
 lsn_status lsn_create(const lsn_config* cfg, void* dev_ws, uint64_t ws_bytes, void* hip_stream,
                       lsn_ctx** out);
 void lsn_destroy(lsn_ctx* ctx);
+/* The message of the context's last error.  With ctx == NULL: the message of
+ * the calling thread's last failed call that takes no context (lsn_create,
+ * the stateless projection and dequantization calls). */
 const char* lsn_last_error(const lsn_ctx* ctx);
 lsn_status lsn_sync(lsn_ctx* ctx);
 /* bytes of one layer record (NF4 codes + absmax + norm gains), 4 KiB aligned */

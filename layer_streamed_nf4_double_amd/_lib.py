@@ -8,6 +8,11 @@ import ctypes
 import os
 
 import numpy as np
+# PyTorch ships its own HIP runtime (libamdhip64.so, soname libamdhip64.so.7)
+# and the library links the system one under that soname.  With torch loaded
+# first the library binds to torch's runtime; loaded first itself, it would
+# bring in a second runtime that does not see the GPU once torch has taken it.
+import torch  # noqa: F401  (load order only)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblsn.so")
@@ -114,10 +119,9 @@ def _ptr(x):
 
 def _check(st, ctx=None, what=""):
     if st != LSN_OK:
-        msg = what
-        if ctx:
-            m = _lib.lsn_last_error(ctx)
-            msg = f"{what}: {m.decode() if m else ''}"
+        # without a context the library keeps the thread's last message
+        m = _lib.lsn_last_error(ctx if ctx else None)
+        msg = f"{what}: {m.decode() if m else ''}"
         raise LsnError(st, msg)
 
 

@@ -611,7 +611,7 @@ GemmPlan gemm_plan(int M, int N, int K, int nseg, int batch) {
     else if (M >= 128) { g.tile = TILE_128x128; tiles = t128; }
     else { g.tile = TILE_64x64; tiles = t64; }
     const int nkt = (K + 63) / 64 * nseg;
-    if (tiles < 200) {
+    if (tiles > 0 && tiles < 200) {  // (no tiles at M = 0: nothing to split)
       int sp = (int)std::min<int64_t>(8, (256 + tiles - 1) / tiles);
       sp = std::min(sp, std::max(1, nkt / 4));
       g.split = std::max(sp, 1);

@@ -209,11 +209,37 @@ static lsn_status fail(lsn_ctx* c, lsn_status st, const char* fmt, ...) {
                   __FILE__, __LINE__);                                                      \
   } while (0)
 
+// hipGetLastError reports the last failed HIP call of the thread, whoever
+// made it; a status left by the caller's own HIP calls (a not-ready event or
+// stream query, say) is theirs, so every entry point clears it first and the
+// launch checks see only this call's errors.
 #define CHECK_CTX(c)                                                  \
   do {                                                                \
     if (!(c)) return LSN_ERR_INVALID;                                 \
     if ((c)->poisoned) return LSN_ERR_STATE;                          \
+    (void)hipGetLastError();                                          \
   } while (0)
+
+// Calls without a context keep their last error message per thread
+// (lsn_last_error(NULL)).
+static thread_local std::string g_err;
+
+static lsn_status fail0(lsn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+// the status of the launches of a call without a context
+static lsn_status launch_status0(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return LSN_OK;
+  return fail0(LSN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
 
 static lsn_status launch_check(lsn_ctx* c) {
   HIPCHK(c, hipGetLastError());
@@ -1043,11 +1069,12 @@ lsn_status lsn_nf4_dequant(const uint8_t* codes, const float* absmax, uint64_t n
                            int32_t out_bf16, void* hip_stream) {
   if (n == 0) return LSN_OK;
   if (!codes || !absmax || !out || n % 8) return LSN_ERR_INVALID;
+  (void)hipGetLastError();  // a status left by the caller's HIP calls is not ours
   float lv[16];
   nf4_levels(lv);
   nf4_dequant(codes, absmax, (int64_t)n, lv, out_bf16 ? nullptr : (float*)out,
               out_bf16 ? (uint16_t*)out : nullptr, (hipStream_t)hip_stream);
-  return hipGetLastError() == hipSuccess ? LSN_OK : LSN_ERR_HIP;
+  return launch_status0("lsn_nf4_dequant");
 }
 
 // Scratch of the stateless projection: t, u fp32 [M,16]; aext bf16 [M,16];
@@ -1109,6 +1136,7 @@ lsn_status lsn_nf4_linear_fwd(const uint8_t* codes, const float* absmax, int32_t
   lsn_status st = linear_args_ok(codes, absmax, M, K, N, X, A, B, r, scratch, sb);
   if (st != LSN_OK || !Y) return st != LSN_OK ? st : LSN_ERR_INVALID;
   if (M == 0) return LSN_OK;
+  (void)hipGetLastError();  // a status left by the caller's HIP calls is not ours
   hipStream_t hs = (hipStream_t)hip_stream;
   const LinScratch L = lin_scratch_or_none(scratch, sb, M, K, N);
   GemmParams p;
@@ -1128,9 +1156,9 @@ lsn_status lsn_nf4_linear_fwd(const uint8_t* codes, const float* absmax, int32_t
     lora_ext(B, 1, N, N, r, L.bext, 16, 0, hs);
     p.Aext = L.aext; p.ldae = 16; p.Bext = L.bext; p.ldbe = 16; p.kext = 16;
   }
-  return gemm(p, A_BF16_K, B_NF4_K, 1, hs) == hipSuccess && hipGetLastError() == hipSuccess
-             ? LSN_OK
-             : LSN_ERR_HIP;
+  const hipError_t e = gemm(p, A_BF16_K, B_NF4_K, 1, hs);
+  if (e != hipSuccess) return fail0(LSN_ERR_HIP, "lsn_nf4_linear_fwd: %s", hipGetErrorString(e));
+  return launch_status0("lsn_nf4_linear_fwd");
 }
 
 lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t M, int32_t K,
@@ -1140,12 +1168,15 @@ lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t
   lsn_status st = linear_args_ok(codes, absmax, M, K, N, X, A, B, r, scratch, sb);
   if (st != LSN_OK) return st;
   if (!dY || !dX || (r > 0 && (!dA || !dB))) return LSN_ERR_INVALID;
+  (void)hipGetLastError();  // a status left by the caller's HIP calls is not ours
   hipStream_t hs = (hipStream_t)hip_stream;
-  if (r > 0) {
-    fill_u32(dA, 0, (int64_t)K * r, hs);
-    fill_u32(dB, 0, (int64_t)r * N, hs);
+  if (M == 0) {  // no tokens: zero adapter gradients
+    if (r > 0) {
+      fill_u32(dA, 0, (int64_t)K * r, hs);
+      fill_u32(dB, 0, (int64_t)r * N, hs);
+    }
+    return launch_status0("lsn_nf4_linear_bwd");
   }
-  if (M == 0) return hipGetLastError() == hipSuccess ? LSN_OK : LSN_ERR_HIP;
   const LinScratch L = lin_scratch_or_none(scratch, sb, M, K, N);
   GemmParams p;
   nf4_levels(p.levels);
@@ -1174,38 +1205,41 @@ lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t
       mu.ext = L.aext; mu.ld_ext = 16; mu.ext_scale = s;
       (void)lora_mm(mu, L.lpart, L.lpf, hs);
     }
-    LoraTGrad ga;  // dA += s X^T u
-    ga.R = M; ga.r = r; ga.y_f32 = 0; ga.ldy = K; ga.scale = s; ga.njobs = 1;
+    LoraTGrad ga;  // dA = s X^T u (every element written: no accumulation)
+    ga.R = M; ga.r = r; ga.y_f32 = 0; ga.ldy = K; ga.scale = s; ga.njobs = 1; ga.accumulate = 0;
     ga.job[0].Y = X; ga.job[0].C = K; ga.job[0].nz = 1; ga.job[0].so_c = r; ga.job[0].so_j = 1;
     ga.job[0].Z[0] = L.u; ga.job[0].ldz[0] = r; ga.job[0].out[0] = dA;
     (void)lora_tgrad(ga, hs);
-    LoraTGrad gb;  // dB += s t^T dY, stored dB[j*N + n]
-    gb.R = M; gb.r = r; gb.y_f32 = 0; gb.ldy = N; gb.scale = s; gb.njobs = 1;
+    LoraTGrad gb;  // dB = s t^T dY, stored dB[j*N + n]
+    gb.R = M; gb.r = r; gb.y_f32 = 0; gb.ldy = N; gb.scale = s; gb.njobs = 1; gb.accumulate = 0;
     gb.job[0].Y = dY; gb.job[0].C = N; gb.job[0].nz = 1; gb.job[0].so_c = 1; gb.job[0].so_j = N;
     gb.job[0].Z[0] = L.t; gb.job[0].ldz[0] = r; gb.job[0].out[0] = dB;
     (void)lora_tgrad(gb, hs);
     lora_ext(A, r, 1, K, r, L.bext, 16, 0, hs);  // bext = A
     p.Aext = L.aext; p.ldae = 16; p.Bext = L.bext; p.ldbe = 16; p.kext = 16;
   }
-  return gemm(p, A_BF16_K, B_NF4_R, 1, hs) == hipSuccess && hipGetLastError() == hipSuccess
-             ? LSN_OK
-             : LSN_ERR_HIP;
+  const hipError_t e = gemm(p, A_BF16_K, B_NF4_R, 1, hs);
+  if (e != hipSuccess) return fail0(LSN_ERR_HIP, "lsn_nf4_linear_bwd: %s", hipGetErrorString(e));
+  return launch_status0("lsn_nf4_linear_bwd");
 }
 
 lsn_status lsn_workspace_bytes(const lsn_config* cfg, uint64_t* bytes) {
   std::string why;
-  if (!bytes || !cfg_valid(cfg, &why)) return LSN_ERR_INVALID;
+  if (!bytes) return LSN_ERR_INVALID;
+  if (!cfg_valid(cfg, &why)) return fail0(LSN_ERR_INVALID, "lsn_workspace_bytes: %s", why.c_str());
   lsn_ctx tmp;
   tmp.cfg = *cfg;
   record_layout(&tmp);
-  if (!layout_valid(&tmp, &why)) return LSN_ERR_INVALID;
+  if (!layout_valid(&tmp, &why))
+    return fail0(LSN_ERR_INVALID, "lsn_workspace_bytes: %s", why.c_str());
   *bytes = carve(&tmp, nullptr);
   return LSN_OK;
 }
 
 lsn_status lsn_config_record_bytes(const lsn_config* cfg, uint64_t* bytes) {
   std::string why;
-  if (!bytes || !cfg_valid(cfg, &why)) return LSN_ERR_INVALID;
+  if (!bytes) return LSN_ERR_INVALID;
+  if (!cfg_valid(cfg, &why)) return fail0(LSN_ERR_INVALID, "lsn_config_record_bytes: %s", why.c_str());
   lsn_ctx tmp;
   tmp.cfg = *cfg;
   record_layout(&tmp);
@@ -1218,7 +1252,8 @@ lsn_status lsn_create(const lsn_config* cfg, void* dev_ws, uint64_t ws_bytes, vo
   std::string why;
   if (!out) return LSN_ERR_INVALID;
   *out = nullptr;
-  if (!cfg_valid(cfg, &why)) return LSN_ERR_INVALID;
+  if (!cfg_valid(cfg, &why)) return fail0(LSN_ERR_INVALID, "lsn_create: %s", why.c_str());
+  (void)hipGetLastError();  // a status left by the caller's HIP calls is not ours
   lsn_ctx* c = new lsn_ctx();
   c->cfg = *cfg;
   if (cfg->store_path) c->store_path = cfg->store_path;
@@ -1226,12 +1261,13 @@ lsn_status lsn_create(const lsn_config* cfg, void* dev_ws, uint64_t ws_bytes, vo
   record_layout(c);
   if (!layout_valid(c, &why)) {
     delete c;
-    return LSN_ERR_INVALID;
+    return fail0(LSN_ERR_INVALID, "lsn_create: %s", why.c_str());
   }
   c->ws_needed = carve(c, nullptr);
   if (!dev_ws || ws_bytes < c->ws_needed || (cfg->vram_budget && c->ws_needed > cfg->vram_budget)) {
+    const unsigned long long need = c->ws_needed;
     delete c;
-    return LSN_ERR_NOFIT;
+    return fail0(LSN_ERR_NOFIT, "lsn_create: the workspace needs %llu bytes", need);
   }
   c->ws = (char*)dev_ws;
   c->ws_bytes = ws_bytes;
@@ -1240,6 +1276,9 @@ lsn_status lsn_create(const lsn_config* cfg, void* dev_ws, uint64_t ws_bytes, vo
   nf4_levels(c->levels);
   c->loaded.assign(cfg->n_layers, 0);
   auto cleanup = [&](lsn_status st) {
+    const int en = errno;
+    const hipError_t e = hipGetLastError();
+    fail0(st, "lsn_create: %s", st == LSN_ERR_IO ? strerror(en) : hipGetErrorString(e));
     lsn_destroy(c);
     return st;
   };
@@ -1312,11 +1351,13 @@ void lsn_destroy(lsn_ctx* c) {
   delete c;
 }
 
-const char* lsn_last_error(const lsn_ctx* c) { return c ? c->err.c_str() : "null context"; }
+const char* lsn_last_error(const lsn_ctx* c) {
+  if (c) return c->err.c_str();
+  return g_err.empty() ? "no error recorded by a call without a context" : g_err.c_str();
+}
 
 lsn_status lsn_sync(lsn_ctx* c) {
-  if (!c) return LSN_ERR_INVALID;
-  if (c->poisoned) return LSN_ERR_STATE;
+  CHECK_CTX(c);
   HIPCHK(c, hipStreamSynchronize(c->copy));
   HIPCHK(c, hipStreamSynchronize(c->cs));
   HIPCHK(c, hipGetLastError());

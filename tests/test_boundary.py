@@ -107,6 +107,7 @@ def test_workspace_and_preflight_refusal():
     with pytest.raises(L.LsnError) as e:
         L.lsn_create(cfg, 0x1000, need - 1, 0)
     assert e.value.status == L.LSN_ERR_NOFIT
+    assert f"needs {need} bytes" in str(e.value), str(e.value)
     cfg.vram_budget = need - 1
     with pytest.raises(L.LsnError) as e:
         L.lsn_create(cfg, 0x1000, need, 0)
@@ -124,6 +125,8 @@ def test_invalid_configs_rejected():
         with pytest.raises(L.LsnError) as e:
             L.lsn_workspace_bytes(cfg)
         assert e.value.status == L.LSN_ERR_INVALID, field
+    # the reason travels with the error (calls without a context keep it per thread)
+    assert "max_seq_len" in str(e.value), str(e.value)
 
 
 def test_head_on_host_workspace():
@@ -162,3 +165,13 @@ def test_record_sizes_match_layout():
         ws_res = L.lsn_workspace_bytes(cfg)
         rec = (ws_res - ws_stream) // (w["n_layers"] - 2)
         assert want <= rec <= want + 4096 + 256 * 4 + 4 * w["hidden"]
+
+
+def test_one_hip_runtime_in_the_process():
+    """The library binds to PyTorch's HIP runtime: loading the binding maps a
+    single libamdhip64 into the process (a second runtime would not see the
+    GPU once torch holds it)."""
+    _lib()
+    with open("/proc/self/maps") as f:
+        paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    assert len(paths) == 1, paths

@@ -86,10 +86,12 @@ def _gpu_linear(torch, L, X, W, A, B, r, s, dY):
     Bd = _dev(torch, B) if r else None
     sb = L.lsn_nf4_linear_scratch_bytes(M, K, N, r)
     scr = torch.empty(max(sb, 1), dtype=torch.uint8, device="cuda")
-    Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
-    dX = torch.empty(M, K, dtype=torch.float32, device="cuda")
-    dA = torch.empty(K, max(r, 1), dtype=torch.float32, device="cuda")
-    dB = torch.empty(max(r, 1), N, dtype=torch.float32, device="cuda")
+    # outputs start as NaN: every element must be written, none accumulated into
+    nan = float("nan")
+    Y = torch.full((M, N), nan, dtype=torch.float32, device="cuda")
+    dX = torch.full((M, K), nan, dtype=torch.float32, device="cuda")
+    dA = torch.full((K, max(r, 1)), nan, dtype=torch.float32, device="cuda")
+    dB = torch.full((max(r, 1), N), nan, dtype=torch.float32, device="cuda")
     L.lsn_nf4_linear_fwd(cd, ad, M, K, N, Xd, Ad, Bd, r, s, Y, scr, sb)
     L.lsn_nf4_linear_bwd(cd, ad, M, K, N, Xd, Ad, Bd, r, s, dYd, dX, dA if r else None,
                          dB if r else None, scr, sb)
@@ -174,3 +176,21 @@ def test_linear_invalid_shapes_rejected(torch, L):
     assert e.value.status == L.LSN_ERR_INVALID
     # an empty batch is a no-op
     L.lsn_nf4_linear_fwd(z, z, 0, 16, 8, z, None, None, 0, 1.0, z, None, 0)
+
+
+def test_linear_empty_batch_zero_grads(torch, L):
+    """M = 0: the backward writes zero adapter gradients and nothing else."""
+    say("[linear] M=0 backward")
+    K, N, r = 64, 32, 4
+    codes, absmax = L.lsn_nf4_quantize(synth.normal((N, K), 5, 0, 0))
+    cd, ad = _dev(torch, codes), _dev(torch, absmax)
+    x = torch.zeros(8, dtype=torch.int16, device="cuda")  # never read or written at M = 0
+    A = torch.zeros(K, r, device="cuda")
+    B = torch.zeros(r, N, device="cuda")
+    dA = torch.full((K, r), float("nan"), device="cuda")
+    dB = torch.full((r, N), float("nan"), device="cuda")
+    sb = L.lsn_nf4_linear_scratch_bytes(0, K, N, r)
+    scr = torch.empty(max(sb, 1), dtype=torch.uint8, device="cuda")
+    L.lsn_nf4_linear_bwd(cd, ad, 0, K, N, x, A, B, r, 2.0, x, x, dA, dB, scr, sb)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dA).item() == 0 and torch.count_nonzero(dB).item() == 0
