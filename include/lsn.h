@@ -183,6 +183,8 @@ lsn_status lsn_file_direct_io(const lsn_ctx* ctx, int32_t* direct);
  * LSN_RESIDENT mode, into the device record).  codes[p]/absmax[p] as
  * lsn_nf4_quantize writes them for W_p^T; norms bf16 [hidden].
  * LSN_STREAM_FILE: the record is written to store_path at its offset.
+ * Between passes a layer may be loaded again: the call waits for any copy
+ * still reading the old record, and the next pass copies the new one.
  * ------------------------------------------------------------------------- */
 lsn_status lsn_load_layer_nf4(lsn_ctx* ctx, int32_t layer, const uint8_t* const* codes,
                               const float* const* absmax, const uint16_t* attn_norm_bf16,
@@ -202,7 +204,8 @@ lsn_status lsn_get_lora(lsn_ctx* ctx, int32_t layer, int32_t proj, float* A, flo
                         float* dB);
 /* 0: forward skips every low-rank branch (the DPO reference model, page
  * "Show HN: Fine-tune an 8B model on a 4 GB laptop GPU", first paragraph);
- * 1: branches on.  Backward requires 1. */
+ * 1: branches on.  Backward requires 1 (else LSN_ERR_STATE from lsn_begin_pass
+ * and from every lsn_backward_layer). */
 lsn_status lsn_set_adapter_enabled(lsn_ctx* ctx, int32_t enabled);
 lsn_status lsn_zero_grads(lsn_ctx* ctx);
 /* theta -= lr * grad for every adapter matrix (plain SGD). */

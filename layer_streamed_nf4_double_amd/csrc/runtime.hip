@@ -1390,6 +1390,8 @@ lsn_status lsn_load_layer_nf4(lsn_ctx* c, int32_t layer, const uint8_t* const* c
     tmp.assign(c->rec_bytes, 0);
     rec = tmp.data();
   } else {
+    // a copy queued by the last pass may still be reading the old record
+    HIPCHK(c, hipStreamSynchronize(c->copy));
     rec = c->store + (uint64_t)layer * c->rec_bytes;
     memset(rec, 0, c->rec_bytes);
   }
@@ -1445,6 +1447,7 @@ lsn_status lsn_load_head(lsn_ctx* c, const uint16_t* embed, const uint16_t* lm_h
     memcpy(c->embed_h, embed, vb);
     if (!c->cfg.tied_embeddings) memcpy(c->lm_head_h, lm_head, vb);
   } else {
+    HIPCHK(c, hipStreamSynchronize(c->cs));  // no queued kernel still reads the old tables
     HIPCHK(c, hipMemcpy(c->embed, embed, vb, hipMemcpyHostToDevice));
     if (!c->cfg.tied_embeddings)
       HIPCHK(c, hipMemcpy(c->lm_head, lm_head, vb, hipMemcpyHostToDevice));
@@ -1567,6 +1570,9 @@ lsn_status lsn_backward_layer(lsn_ctx* c, int32_t layer, const float* h_in, cons
                               float* dh_in) {
   CHECK_CTX(c);
   if (!h_in || !dh_out || !dh_in) return fail(c, LSN_ERR_INVALID, "null activation");
+  // the recompute and the adapter gradients both need the adapters on (they
+  // may have been switched off after lsn_begin_pass)
+  if (!c->adapters_on) return fail(c, LSN_ERR_STATE, "backward needs the adapters enabled");
   const uint8_t* rec;
   lsn_status st = layer_begin(c, LSN_PASS_BWD, layer, &rec);
   if (st != LSN_OK) return st;

@@ -147,6 +147,50 @@ def _assert_bit_identical(a, b):
                     assert np.array_equal(_bits(x), _bits(y))
 
 
+def _status(fn, *args):
+    from layer_streamed_nf4_double_amd import _lib as L
+    try:
+        fn(*args)
+    except L.LsnError as e:
+        return e.status
+    return L.LSN_OK
+
+
+def test_calls_out_of_order_fail_and_change_nothing(torch):
+    """Calls that break the pass contract return LSN_ERR_STATE (bad pass
+    arguments LSN_ERR_INVALID) before enqueueing anything: the context is not
+    poisoned, and the two SFT steps that follow give the same bits as on a
+    fresh model."""
+    from layer_streamed_nf4_double_amd import _lib as L
+    w = dict(TINY, n_layers=3)
+    tokens = synth.tokens((1, 64), w["vocab"], 5)
+    say("[order] fresh model")
+    ref = gpu_model(w, "stream_host", b_zero=False, max_tokens=64)
+    a = _two_step_record(torch, ref, w, tokens)
+    ref.close()
+    say("[order] misuse, then the same steps")
+    m = gpu_model(w, "stream_host", b_zero=False, max_tokens=64)
+    h = torch.zeros(64, w["hidden"], device="cuda")
+    ST, INV = L.LSN_ERR_STATE, L.LSN_ERR_INVALID
+    assert _status(L.lsn_forward_layer, m.ctx, 0, h, h) == ST          # outside a pass
+    L.lsn_begin_pass(m.ctx, L.LSN_PASS_FWD, 1, 64)
+    assert _status(L.lsn_forward_layer, m.ctx, 1, h, h) == ST          # layer 0 comes first
+    assert _status(L.lsn_backward_layer, m.ctx, 0, h, h, h) == ST      # not a backward pass
+    assert _status(L.lsn_begin_pass, m.ctx, L.LSN_PASS_FWD, 1, 60) == INV   # seq_len % 8
+    assert _status(L.lsn_begin_pass, m.ctx, L.LSN_PASS_FWD, 2, 64) == INV   # > max_tokens
+    L.lsn_set_adapter_enabled(m.ctx, 0)
+    assert _status(L.lsn_begin_pass, m.ctx, L.LSN_PASS_BWD, 1, 64) == ST
+    L.lsn_set_adapter_enabled(m.ctx, 1)
+    L.lsn_begin_pass(m.ctx, L.LSN_PASS_BWD, 1, 64)
+    L.lsn_set_adapter_enabled(m.ctx, 0)
+    assert _status(L.lsn_backward_layer, m.ctx, 2, h, h, h) == ST      # adapters switched off
+    assert b"adapters" in L._lib.lsn_last_error(m.ctx)
+    L.lsn_set_adapter_enabled(m.ctx, 1)
+    b = _two_step_record(torch, m, w, tokens)
+    m.close()
+    _assert_bit_identical(a, b)
+
+
 @pytest.mark.parametrize("n_layers", [2, 5])
 def test_streamed_equals_resident_bitwise(torch, n_layers):
     w = dict(TINY, n_layers=n_layers)
