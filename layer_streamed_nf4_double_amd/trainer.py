@@ -83,8 +83,10 @@ class LayerStreamedLoRA:
                                 L.lsn_workspace_bytes(probe), free,
                                 adapter.host_bytes_available(),
                                 source="auto" if mode == "auto" else mode)
+        self._own_store = None  # a store file this object created, removed by close()
         if mode == "stream_file" and not store_path:
-            store_path = os.path.join(tempfile.gettempdir(), f"lsn_store_{os.getpid()}.bin")
+            store_path = os.path.join(tempfile.gettempdir(), f"lsn_store_{os.getpid()}_{id(self)}.bin")
+            self._own_store = store_path
         self.mode = mode
         self.cfg = make_config(shape, mode, max_tokens, max_seq_len, lora_targets, store_path,
                                head_on_host=head_on_host, head_chunk_rows=head_chunk_rows)
@@ -111,6 +113,12 @@ class LayerStreamedLoRA:
             self.stream.synchronize()
             L.lsn_destroy(self.ctx)
             self.ctx = None
+        if getattr(self, "_own_store", None):
+            try:
+                os.remove(self._own_store)
+            except OSError:
+                pass
+            self._own_store = None
 
     @contextlib.contextmanager
     def _ordered(self):

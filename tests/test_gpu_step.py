@@ -514,6 +514,11 @@ def test_auto_source_and_preflight(torch):
     m = LayerStreamedLoRA(w, "auto")
     assert m.mode == "stream_host"          # a 2-layer tiny stack fits in RAM
     m.close()
+    f = LayerStreamedLoRA(w, "stream_file")  # no store_path: a temporary store file
+    path = f.cfg.store_path.decode()
+    assert os.path.exists(path)
+    f.close()
+    assert not os.path.exists(path)         # removed with the model that made it
     free, _ = torch.cuda.mem_get_info()
     with pytest.raises(ad.NoFit):           # a workspace larger than the card
         ad.plan_run(1, 1, free + (1 << 30), free, 1 << 40)
