@@ -75,9 +75,10 @@ class LayerStreamedLoRA:
         self.torch = torch
         self.shape = dict(shape)
         self.device = torch.device(device)
-        probe = make_config(shape, "stream_host" if mode == "auto" else mode, max_tokens,
-                            max_seq_len, lora_targets, store_path, head_on_host=head_on_host,
-                            head_chunk_rows=head_chunk_rows)
+        # sizes only (a streamed file store needs no path for them)
+        probe = make_config(shape, "stream_host" if mode in ("auto", "stream_file") else mode,
+                            max_tokens, max_seq_len, lora_targets, store_path,
+                            head_on_host=head_on_host, head_chunk_rows=head_chunk_rows)
         free, _ = torch.cuda.mem_get_info(self.device)
         mode = adapter.plan_run(shape["n_layers"], L.lsn_config_record_bytes(probe),
                                 L.lsn_workspace_bytes(probe), free,
