@@ -67,11 +67,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic():
+def measured_traffic(workload, mode):
     """HBM bytes per launch of the fused NF4 GEMM from the committed
-    rocprofv3 FETCH_SIZE + WRITE_SIZE runs, if the GEMM source is unchanged
-    since they were taken (else None)."""
+    rocprofv3 FETCH_SIZE + WRITE_SIZE runs of the default workload (the
+    8B-shaped streamed step), if the GEMM source is unchanged since they were
+    taken; None for any other workload or a changed kernel."""
     import hashlib
+    if workload != "llama3.1-8b-shaped" or mode != "stream_host":
+        return None
     prof = os.path.join(ROOT, "profiles", "nf4f_gemm_llama8b_sft_traffic.md")
     src = os.path.join(ROOT, "layer_streamed_nf4_double_amd", "csrc", "gemm_nf4f.hip")
     try:
@@ -499,7 +502,7 @@ def main():
     achieved = flops / (ms / 1e3) / 1e12 if ms > 0 else 0.0
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(),
+                "traffic": measured_traffic(args.workload, args.mode),
                 "kernel": "nf4f_kernel (fused NF4-dequant MFMA GEMM, 256x256 tile)",
                 "launches": int(n_gemm), "avg_us": round(ms / max(n_gemm, 1) * 1e3, 2),
                 "flop_per_launch": flops / max(n_gemm, 1)}
