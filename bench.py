@@ -25,6 +25,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+_T_START = time.perf_counter()
 METRIC = "train tokens/sec (streamed NF4-LoRA SFT & DPO, 1 GPU); peak VRAM; % roofline"
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBPS = 8000.0
@@ -354,9 +355,20 @@ def step_flops(w, T, n_seq):
 
 def environment(torch, w, rec_bytes):
     import platform
+    import subprocess
+    props = torch.cuda.get_device_properties(0)
     env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
-           "gpu": torch.cuda.get_device_name(0), "seed": 0,
-           "pinned_store_bytes": int(rec_bytes) * w["n_layers"], "python": platform.python_version()}
+           "gpu": torch.cuda.get_device_name(0), "gpu_arch": getattr(props, "gcnArchName", None),
+           "compute_units": props.multi_processor_count, "gpu_memory_bytes": props.total_memory,
+           "seed": 0, "pinned_store_bytes": int(rec_bytes) * w["n_layers"],
+           "python": platform.python_version(), "host_threads": os.cpu_count(),
+           "elapsed_s": round(time.perf_counter() - _T_START, 1)}
+    try:
+        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
+                             timeout=30).stdout
+        env["hipcc"] = next((l.strip() for l in out.splitlines() if "HIP version" in l), None)
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/opt/rocm/.info/version") as f:
             env["rocm"] = f.read().strip()
