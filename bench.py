@@ -500,6 +500,11 @@ def main():
     peak = torch.cuda.max_memory_allocated()
     loss = float(m.loss[0].item())
     n_gemm, flops, ms = L.lsn_profile_query(m.ctx, 0, 0, 2, 3)   # NF4 fwd GEMM, 256x256 kernel
+    # the copies' own rate, from event pairs around each record copy in one
+    # more (untimed) step: those events add packets between the copies, so
+    # the timed steps record GEMM launches only
+    L.lsn_set_profiling(m.ctx, 2)
+    m.sft_step(tok, tgt, 1, S, 1e-4)
     n_cp, cp_bytes, cp_ms = L.lsn_profile_query(m.ctx, 1)
     L.lsn_set_profiling(m.ctx, 0)
     m.close()

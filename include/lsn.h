@@ -310,10 +310,12 @@ lsn_status lsn_stats(const lsn_ctx* ctx, uint64_t* layer_loads, uint64_t* bytes_
 lsn_status lsn_copy_stream(const lsn_ctx* ctx, void** hip_stream);
 
 /* ---------------------------------------------------------------------------
- * Live timing (measurement only; results are unchanged).  With on != 0 the
- * context records a timing event pair around every NF4 GEMM launch (compute
- * stream) and every layer-record copy (copy stream) from now on; any call
- * clears earlier records.  Synchronizes both streams.
+ * Live timing (measurement only; results are unchanged).  on is a mask: bit
+ * 0 records a timing event pair on every NF4 GEMM launch (carried by the
+ * kernel's own dispatch on the compute stream, so it adds no packet), bit 1
+ * an event pair around every layer-record copy (two event packets on the
+ * copy stream per copy); 0 stops, other values give LSN_ERR_INVALID.  Any
+ * call clears earlier records.  Synchronizes both streams.
  * ------------------------------------------------------------------------- */
 lsn_status lsn_set_profiling(lsn_ctx* ctx, int32_t on);
 /* Totals over the recorded events.  what = 0: NF4 GEMM launches whose operand

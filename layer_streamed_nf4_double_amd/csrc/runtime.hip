@@ -158,7 +158,7 @@ struct lsn_ctx {
     double work;
     hipEvent_t e0, e1;
   };
-  bool profiling = false;
+  int profiling = 0;  // bit 0: NF4 GEMM launches, bit 1: record copies
   std::vector<ProfRec> prof;
   std::vector<hipEvent_t> evpool;
   size_t evnext = 0;
@@ -262,7 +262,7 @@ static hipEvent_t take_event(lsn_ctx* c) {
 }
 
 static bool prof_begin(lsn_ctx* c, lsn_ctx::ProfRec* r, hipStream_t s) {
-  if (!c->profiling) return false;
+  if (!(c->profiling & 2)) return false;
   r->e0 = take_event(c);
   r->e1 = take_event(c);
   if (!r->e0 || !r->e1) return false;
@@ -280,7 +280,7 @@ static hipError_t cgemm(lsn_ctx* c, GemmParams p, int opa, int opb, int batch) {
   lsn_ctx::ProfRec r{0, opa, opb, gemm_tile(p, opa, opb, batch),
                      2.0 * p.M * p.N * (double)p.K * p.nseg * batch, nullptr, nullptr};
   // events bracket the GEMM kernel only (not a split-k reduction)
-  const bool on = c->profiling && (opb == B_NF4_K || opb == B_NF4_R);
+  const bool on = (c->profiling & 1) && (opb == B_NF4_K || opb == B_NF4_R);
   if (on) {
     r.e0 = take_event(c);
     r.e1 = take_event(c);
@@ -1734,14 +1734,15 @@ lsn_status lsn_stats(const lsn_ctx* c, uint64_t* layer_loads, uint64_t* bytes_h2
 
 lsn_status lsn_set_profiling(lsn_ctx* c, int32_t on) {
   CHECK_CTX(c);
+  if (on < 0 || on > 3) return fail(c, LSN_ERR_INVALID, "profiling mask %d", on);
   HIPCHK(c, hipStreamSynchronize(c->copy));
   HIPCHK(c, hipStreamSynchronize(c->cs));
   c->prof.clear();
   c->evnext = 0;
-  c->profiling = on != 0;
+  c->profiling = on;
   while (c->profiling && c->evpool.size() < 16384) {
     hipEvent_t e;
-    HIPCHK(c, hipEventCreate(&e));
+    HIPCHK(c, hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
     c->evpool.push_back(e);
   }
   return LSN_OK;
