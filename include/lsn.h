@@ -5,11 +5,12 @@
  *
  * The method (web pages on the "Soup" fine-tuning CLI):
  *   - "Soup: Fine-Tune an 8B Model on a 4 GB GPU" (lucaberton.com), section
- *     "The Core Idea: Layer Streaming": the frozen base stays in CPU RAM or on
- *     NVMe; on a dedicated stream one decoder layer at a time is copied into
- *     VRAM as forward or backward needs it; peak VRAM is one layer plus the
- *     adapter; the streamed base may be NF4; only the LoRA adapter trains; for
- *     DPO the reference model is the same base with adapters disabled.
+ *     "The Core Idea: Layer Streaming": the frozen weights are held off the
+ *     GPU (host memory or a disk) and each decoder layer reaches device
+ *     memory, through a copy stream of its own, only when a pass needs it, so
+ *     device memory holds about one layer plus the adapter; the held weights
+ *     may be NF4; the LoRA adapter is the only trained state; DPO's reference
+ *     model is the same base run without the adapter.
  *   - "Show HN: Fine-tune an 8B model on a 4 GB laptop GPU" (elseif.net),
  *     first paragraph: policy log-probs with the adapter on, reference
  *     log-probs with it off, from the same streamed base; results bit-exact
@@ -90,6 +91,13 @@ typedef struct {
    * W_lm rows); else a multiple of 8, at most one slot of rows with
    * head_on_host.  The logits buffer holds max_tokens x rows fp32. */
   int32_t head_chunk_rows;
+  /* device slots the streamed modes copy layer records into: 0 or 2 = a
+   * double buffer (the copy of the next layer overlaps the current one); 3
+   * or 4 keep more records resident, so the first layers of a pass that
+   * another pass has just left in the slots are reused instead of copied
+   * again (2 * (n_slots - 2) fewer record copies per SFT step), at one
+   * record of device memory per slot.  Ignored when resident. */
+  int32_t n_slots;
 } lsn_config;
 
 /* ---------------------------------------------------------------------------
@@ -212,20 +220,33 @@ lsn_status lsn_zero_grads(lsn_ctx* ctx);
 lsn_status lsn_sgd_step(lsn_ctx* ctx, float lr);
 
 /* ---------------------------------------------------------------------------
- * A pass over the stack.  begin_pass fixes the layer order (FWD 0..L-1, BWD
- * L-1..0) and, when streaming, starts copying the first two layer records
- * into the two device slots on the copy stream.  Each forward_layer /
- * backward_layer must name the next layer of the pass (else LSN_ERR_STATE);
- * it waits for its record, runs, frees the slot and queues the copy of the
- * layer two ahead.  A record already in a slot is reused, not copied again.
- * n_seq sequences of seq_len tokens each, back to back (T = n_seq*seq_len).
+ * A pass over the stack (page "Soup: Fine-Tune an 8B Model on a 4 GB GPU",
+ * section "The Core Idea: Layer Streaming", second bullet: on a dedicated
+ * stream the base is copied into VRAM one decoder layer at a time, as the
+ * forward or the backward pass reaches it).  begin_pass fixes the layer
+ * order (FWD 0..L-1, BWD L-1..0) and the pass geometry: n_seq sequences of
+ * seq_len tokens each, back to back (T = n_seq*seq_len; seq_len % 8 == 0,
+ * seq_len <= max_seq_len, T <= max_tokens, else LSN_ERR_INVALID).  When
+ * streaming it starts copying the first layer records into the device slots
+ * on the copy stream.  Each forward_layer / backward_layer must name the next
+ * layer of the pass (else LSN_ERR_STATE, nothing enqueued); it waits for its
+ * record, runs, frees the slot and queues the copy of the next layer that is
+ * not in a slot.  A record already in a slot is reused, not copied again.
  * ------------------------------------------------------------------------- */
 lsn_status lsn_begin_pass(lsn_ctx* ctx, int32_t kind, int32_t n_seq, int32_t seq_len);
-/* tokens: device int32 [T]; h0: device fp32 [T, hidden] = embedding rows. */
+/* The input of the first decoder layer: the embedding row of each token (the
+ * pages stream only the decoder layers, same section, first and second
+ * bullets; the embedding table stays with the head tables).  tokens: device
+ * int32 [T] of the current pass; h0: device fp32 [T, hidden], overwritten.
+ * A token outside [0, vocab) gives a NaN row and reads no table row.
+ * LSN_ERR_STATE before lsn_load_head or outside a pass. */
 lsn_status lsn_embed(lsn_ctx* ctx, const int32_t* tokens, float* h0);
-/* h_in, h_out: device fp32 [T, hidden] (may alias).  One decoder layer:
- * RMSNorm, q/k/v (+LoRA), RoPE, causal GQA attention, o (+LoRA) + residual,
- * RMSNorm, SwiGLU MLP (+LoRA) + residual. */
+/* One decoder layer of the forward pass on the layer's streamed record (same
+ * section: the layer is in VRAM only while the pass needs it).  h_in, h_out:
+ * device fp32 [T, hidden] (may alias), caller-owned.  Computes RMSNorm,
+ * q/k/v (+LoRA), RoPE, causal GQA attention, o (+LoRA) + residual, RMSNorm,
+ * SwiGLU MLP (+LoRA) + residual; low-rank branches follow
+ * lsn_set_adapter_enabled.  The caller keeps h_in for the backward pass. */
 lsn_status lsn_forward_layer(lsn_ctx* ctx, int32_t layer, const float* h_in, float* h_out);
 /* Reference and policy forward of one layer on ONE copy of its record: the
  * layer runs first with every low-rank branch skipped on h_ref_in ->
@@ -239,26 +260,33 @@ lsn_status lsn_forward_layer(lsn_ctx* ctx, int32_t layer, const float* h_in, flo
  * stream's buffers. */
 lsn_status lsn_forward_layer_pair(lsn_ctx* ctx, int32_t layer, const float* h_ref_in,
                                   float* h_ref_out, const float* h_in, float* h_out);
-/* Recomputes the layer from its saved input, then back-propagates:
+/* One decoder layer of the backward pass (page "Soup: Fine-Tune an 8B Model
+ * on a 4 GB GPU", section "The Core Idea: Layer Streaming": the backward pass
+ * streams each layer again, and only the adapter trains).  Recomputes the
+ * layer from its saved input h_in_saved, then back-propagates:
  * dh_in = d loss / d h_in (may alias dh_out), and adds the adapter
  * gradients of this layer into the context's gradient buffers.  The base
- * gets no gradient (page "Soup: ...", "The Core Idea: Layer Streaming": the
- * backward re-reads each layer). */
+ * gets no gradient.  All device fp32 [T, hidden].  Needs the adapters on
+ * (else LSN_ERR_STATE). */
 lsn_status lsn_backward_layer(lsn_ctx* ctx, int32_t layer, const float* h_in_saved,
                               const float* dh_out, float* dh_in);
 
 /* ---------------------------------------------------------------------------
- * LM head.  h: device fp32 [T, hidden]; targets: device int32 [T] (a negative
- * target gives logp 0); logp: device fp32 [T] = log softmax(RMSNorm(h) W_lm^T)
- * at the target, over the vocabulary in chunks (online max / sum).
- * want_grad_state != 0 also keeps, per position, the expected embedding row
- * E[t] = sum_v softmax_v W_v, accumulated chunk by chunk (rescaled to the
- * running max), for the backward.  lm_head_backward must follow an
- * lm_head_logprobs call with want_grad_state on the same h (else
- * LSN_ERR_STATE): dh (device fp32 [T, hidden], overwritten) from dlogp
- * (device fp32 [T]) as dlogp_t (W[y_t] - E[t]) through the final RMSNorm,
- * with no second pass over W_lm (page "Soup: ...", the LM-head logprobs and
- * their gradient).
+ * LM head: the per-token log-probabilities of the training targets (page
+ * "Show HN: Fine-tune an 8B model on a 4 GB laptop GPU", first paragraph:
+ * the policy log-probs come from a pass with the adapter active, the
+ * reference log-probs from a pass of the same base with it switched off).
+ * h: device fp32 [T, hidden]; targets: device int32 [T] (a negative target
+ * gives logp 0; a target >= vocab gives NaN and reads no table row); logp:
+ * device fp32 [T] = log softmax(RMSNorm(h) W_lm^T) at the target, over the
+ * vocabulary in chunks (online max / sum).  want_grad_state != 0 also keeps,
+ * per position, the expected embedding row E[t] = sum_v softmax_v W_v,
+ * accumulated chunk by chunk (rescaled to the running max), for the
+ * backward.  lm_head_backward is the derivative of that definition: it must
+ * follow an lm_head_logprobs call with want_grad_state on the same h (else
+ * LSN_ERR_STATE) and writes dh (device fp32 [T, hidden], overwritten) from
+ * dlogp (device fp32 [T]) as dlogp_t (W[y_t] - E[t]) through the final
+ * RMSNorm, with no second pass over W_lm.
  * ------------------------------------------------------------------------- */
 lsn_status lsn_lm_head_logprobs(lsn_ctx* ctx, const float* h, const int32_t* targets, float* logp,
                                 int32_t want_grad_state);
@@ -306,6 +334,18 @@ lsn_status lsn_pref_loss(lsn_ctx* ctx, int32_t kind, const float* logp_pol, cons
  * host->device by the scheduler, and workspace bytes carved.  Any may be NULL. */
 lsn_status lsn_stats(const lsn_ctx* ctx, uint64_t* layer_loads, uint64_t* bytes_h2d,
                      uint64_t* ws_bytes);
+/* Fault injection, for tests of the stream ordering (results must not
+ * change: streamed runs are bit-exact against resident ones, page "Show HN:
+ * Fine-tune an 8B model on a 4 GB laptop GPU", first paragraph).
+ * copy_delay_us: a kernel on the copy stream waits this long before every
+ * copy into a slot (a compute that did not wait for its copy would read the
+ * slot early); compute_delay_us: a kernel on the compute stream waits this
+ * long before every layer's kernels (a copy that did not wait for the slot's
+ * last reader would overwrite it early); poison_slots != 0: every slot is
+ * filled with 0xFF bytes (NaN fp32, NaN absmax) on the copy stream just
+ * before a copy into it.  Delays 0..100000, else LSN_ERR_INVALID. */
+lsn_status lsn_set_fault_injection(lsn_ctx* ctx, int32_t copy_delay_us, int32_t compute_delay_us,
+                                   int32_t poison_slots);
 /* The copy stream (hipStream_t) the scheduler uses, for timing its copies. */
 lsn_status lsn_copy_stream(const lsn_ctx* ctx, void** hip_stream);
 

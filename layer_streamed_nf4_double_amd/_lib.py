@@ -47,7 +47,8 @@ class lsn_config(ctypes.Structure):
                 ("lora_targets", ctypes.c_uint32), ("max_tokens", ctypes.c_int32),
                 ("max_seq_len", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("store_path", ctypes.c_char_p), ("vram_budget", ctypes.c_uint64),
-                ("head_on_host", ctypes.c_int32), ("head_chunk_rows", ctypes.c_int32)]
+                ("head_on_host", ctypes.c_int32), ("head_chunk_rows", ctypes.c_int32),
+                ("n_slots", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -89,6 +90,7 @@ _SIGS = {
     "lsn_pref_loss": [_P, _I32, _P, _P, _I32, _I32, _F, _F, _P, _P],
     "lsn_stats": [_P, ctypes.POINTER(_U64), ctypes.POINTER(_U64), ctypes.POINTER(_U64)],
     "lsn_copy_stream": [_P, ctypes.POINTER(_P)],
+    "lsn_set_fault_injection": [_P, _I32, _I32, _I32],
     "lsn_set_profiling": [_P, _I32],
     "lsn_profile_query": [_P, _I32, _I32, _I32, _I32, ctypes.POINTER(_U64),
                           ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
@@ -334,6 +336,11 @@ def lsn_copy_stream(ctx):
     s = _P(None)
     _check(_lib.lsn_copy_stream(ctx, ctypes.byref(s)), ctx, "lsn_copy_stream")
     return s.value or 0
+
+
+def lsn_set_fault_injection(ctx, copy_delay_us=0, compute_delay_us=0, poison_slots=False):
+    _check(_lib.lsn_set_fault_injection(ctx, int(copy_delay_us), int(compute_delay_us),
+                                        int(bool(poison_slots))), ctx, "lsn_set_fault_injection")
 
 
 def lsn_set_profiling(ctx, on):

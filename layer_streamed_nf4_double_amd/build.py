@@ -31,6 +31,11 @@ def _compile(src):
 
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
+    # objects of sources no longer in SOURCES (an experiment's leftovers) go
+    want = {os.path.basename(src) + ".o" for src in SOURCES}
+    for name in os.listdir(BUILD):
+        if name.endswith(".o") and name not in want:
+            os.remove(os.path.join(BUILD, name))
     with ThreadPoolExecutor(max_workers=4) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"

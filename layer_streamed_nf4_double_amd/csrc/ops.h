@@ -24,23 +24,28 @@ void lora_ext(const float* W, int64_t srow, int64_t sj, int R, int r, uint16_t* 
               int c0, hipStream_t s);
 void lse_chunk(const float* logits, int T, int Vc, int v0, const int32_t* tgt, float* run_m,
                float* run_s, float* tlogit, int first, hipStream_t s);
+// targets >= V give NaN log-probs (no vocabulary entry), negative ones 0
 void lse_final(const float* run_m, const float* run_s, const float* tlogit, const int32_t* tgt,
-               int T, float* logp, float* lse, float* inv, hipStream_t s);
+               int T, int V, float* logp, float* lse, float* inv, hipStream_t s);
 // chunk pass that also writes p~ = bf16(exp(l - m')) and alpha = exp(m - m')
 void lse_chunk_acc(const float* logits, int T, int Vc, int v0, const int32_t* tgt, float* run_m,
                    float* run_s, float* tlogit, float* alpha, uint16_t* pt, int first,
                    hipStream_t s);
 // x[t, :] *= f[t] (n % 4 == 0, 16-byte aligned rows)
 void scale_rows(float* x, const float* f, int T, int n, hipStream_t s);
-// E[t, :] = dlogp[t] * (W[y_t, :] - E[t, :]) in place
-void head_grad(const float* dlogp, const int32_t* tgt, const uint16_t* W, int T, int H, float* E,
-               hipStream_t s);
+// E[t, :] = dlogp[t] * (W[y_t, :] - E[t, :]) in place (W[y_t] taken as 0
+// for y_t outside [0, V))
+void head_grad(const float* dlogp, const int32_t* tgt, const uint16_t* W, int T, int H, int V,
+               float* E, hipStream_t s);
 void sft_loss(const float* logp, const int32_t* tgt, int n, float* loss, float* dlogp,
               hipStream_t s);
 // kind: 0 DPO, 1 SimPO, 2 ORPO, 3 KTO (lr may be null for 1 and 2)
 void pref_loss(int kind, const float* lp, const float* lr, int S, int P, float beta, float p2,
                float* out, float* dlogp, hipStream_t s);
 void sgd(float* p, const float* g, float lr, int64_t n, hipStream_t s);
+// a kernel that waits `us` microseconds of the device wall clock (rate
+// wall_khz) on stream s, then exits
+void spin_us(uint32_t us, int wall_khz, hipStream_t s);
 void fill_u32(void* p, uint32_t v, int64_t n, hipStream_t s);
 void f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
 void nf4_dequant(const uint8_t* codes, const float* absmax, int64_t n, const float* levels,

@@ -206,16 +206,19 @@ __global__ void lora_ext_k(const float* __restrict__ Wp, int64_t srow, int64_t s
 // ---------------------------------------------------------------------------
 // vocabulary-chunk log-softmax (online max / sum) and target gather
 // ---------------------------------------------------------------------------
-// lse = m + log(sum); logp at the target; inv (when given) = 1 / sum
+// lse = m + log(sum); logp at the target; inv (when given) = 1 / sum.  A
+// negative target means "no target" (logp 0); a target >= V is not a
+// vocabulary entry and yields NaN, which the losses propagate.
 __global__ void lse_final_k(const float* __restrict__ run_m, const float* __restrict__ run_s,
                             const float* __restrict__ tlogit, const int32_t* __restrict__ tgt,
-                            int T, float* __restrict__ logp, float* __restrict__ lse,
+                            int T, int V, float* __restrict__ logp, float* __restrict__ lse,
                             float* __restrict__ inv) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   const float l = run_m[t] + logf(run_s[t]);
   lse[t] = l;
-  logp[t] = (tgt[t] >= 0) ? tlogit[t] - l : 0.f;
+  const int y = tgt[t];
+  logp[t] = y < 0 ? 0.f : y < V ? tlogit[t] - l : __builtin_nanf("");
   if (inv) inv[t] = 1.0f / run_s[t];
 }
 
@@ -303,15 +306,16 @@ __global__ void scale_rows1_k(float* __restrict__ x, const float* __restrict__ f
 
 // LM-head input gradient from the expected embedding row E (in place):
 // dn[t, :] = dlogp[t] * (W[y_t, :] - E[t, :]); a position without a target
-// has dlogp 0 and gets 0.
+// has dlogp 0 and gets 0.  A target outside [0, V) reads no row of W (its
+// log-prob is already NaN).
 __global__ void head_grad_k(const float* __restrict__ dlogp, const int32_t* __restrict__ tgt,
-                            const uint16_t* __restrict__ W, int H, int64_t n,
+                            const uint16_t* __restrict__ W, int H, int V, int64_t n,
                             float* __restrict__ E) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int64_t t = i / H;
   const int y = tgt[t];
-  const float wy = y >= 0 ? bf16_to_f32(W[(int64_t)y * H + (i - t * H)]) : 0.f;
+  const float wy = (y >= 0 && y < V) ? bf16_to_f32(W[(int64_t)y * H + (i - t * H)]) : 0.f;
   E[i] = dlogp[t] * (wy - E[i]);
 }
 
@@ -408,6 +412,14 @@ __global__ void pref_loss_k(int kind, const float* __restrict__ lp, const float*
 __global__ void sgd_k(float* __restrict__ p, const float* __restrict__ g, float lr, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] -= lr * g[i];
+}
+
+// One lane waits `ticks` periods of the device's constant-rate wall clock,
+// then exits (a delay of bounded length on the stream it runs on).
+__global__ void spin_k(uint64_t ticks) {
+  if (threadIdx.x != 0) return;
+  const uint64_t t0 = wall_clock64();
+  while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
 }
 
 __global__ void fill_k(uint32_t* __restrict__ p, uint32_t v, int64_t n) {
@@ -782,9 +794,9 @@ void lse_chunk(const float* logits, int T, int Vc, int v0, const int32_t* tgt, f
                      run_s, tlogit, nullptr, nullptr, first);
 }
 void lse_final(const float* run_m, const float* run_s, const float* tlogit, const int32_t* tgt,
-               int T, float* logp, float* lse, float* inv, hipStream_t s) {
+               int T, int V, float* logp, float* lse, float* inv, hipStream_t s) {
   hipLaunchKernelGGL(lse_final_k, dim3(nb(T, 256)), dim3(256), 0, s, run_m, run_s, tlogit, tgt, T,
-                     logp, lse, inv);
+                     V, logp, lse, inv);
 }
 void lse_chunk_acc(const float* logits, int T, int Vc, int v0, const int32_t* tgt, float* run_m,
                    float* run_s, float* tlogit, float* alpha, uint16_t* pt, int first,
@@ -802,10 +814,10 @@ void scale_rows(float* x, const float* f, int T, int n, hipStream_t s) {
     hipLaunchKernelGGL(scale_rows1_k, dim3(nb(total, 256)), dim3(256), 0, s, x, f, n, total);
   }
 }
-void head_grad(const float* dlogp, const int32_t* tgt, const uint16_t* W, int T, int H, float* E,
-               hipStream_t s) {
+void head_grad(const float* dlogp, const int32_t* tgt, const uint16_t* W, int T, int H, int V,
+               float* E, hipStream_t s) {
   const int64_t n = (int64_t)T * H;
-  hipLaunchKernelGGL(head_grad_k, dim3(nb(n, 256)), dim3(256), 0, s, dlogp, tgt, W, H, n, E);
+  hipLaunchKernelGGL(head_grad_k, dim3(nb(n, 256)), dim3(256), 0, s, dlogp, tgt, W, H, V, n, E);
 }
 void sft_loss(const float* logp, const int32_t* tgt, int n, float* loss, float* dlogp,
               hipStream_t s) {
@@ -818,6 +830,10 @@ void pref_loss(int kind, const float* lp, const float* lr, int S, int P, float b
 }
 void sgd(float* p, const float* g, float lr, int64_t n, hipStream_t s) {
   hipLaunchKernelGGL(sgd_k, dim3(nb(n, 256)), dim3(256), 0, s, p, g, lr, n);
+}
+void spin_us(uint32_t us, int wall_khz, hipStream_t s) {
+  const uint64_t ticks = (uint64_t)us * (uint64_t)wall_khz / 1000u;
+  hipLaunchKernelGGL(spin_k, dim3(1), dim3(64), 0, s, ticks);
 }
 void fill_u32(void* p, uint32_t v, int64_t n, hipStream_t s) {
   if (n <= 0) return;

@@ -14,6 +14,10 @@
 // pass reaches it (the last two layers of a forward pass are the first two of
 // the backward pass) is reused instead of copied again.
 //
+// The slot bookkeeping (which record goes into which slot, which event each
+// stream waits for) is the SlotScheduler of sched.h; this file supplies its
+// executor (HIP stream operations) and the record sources.
+//
 // Resident mode keeps every record in device memory at the same intra-record
 // offsets, so the kernels run on byte-identical inputs: streamed and resident
 // results are bit-identical (the pages' own correctness bar, axbrief.com
@@ -39,6 +43,7 @@
 #include "host_codec.h"
 #include "lora.h"
 #include "ops.h"
+#include "sched.h"
 
 using namespace lsn;
 
@@ -68,16 +73,26 @@ struct Carver {
 
 }  // namespace
 
+// The scheduler's executor: HIP stream operations on the context's streams
+// (defined after lsn_ctx).
+struct HipExec {
+  lsn_ctx* c;
+  int copy_wait_free(int s);
+  int host_wait_copy(int s);
+  int copy_record(int layer, int s, int next);
+  int compute_wait_copy(int s);
+  int compute_free(int s);
+};
+
 struct lsn_ctx {
   lsn_config cfg{};
   std::string store_path;
   hipStream_t cs = nullptr;    // compute stream (caller's)
   hipStream_t copy = nullptr;  // the scheduler's copy stream
-  hipEvent_t copy_done[2] = {nullptr, nullptr};
-  hipEvent_t slot_free[2] = {nullptr, nullptr};
-  bool slot_used[2] = {false, false};   // slot_free[s] has been recorded
-  bool copy_issued[2] = {false, false}; // copy_done[s] has been recorded
-  int slot_layer[2] = {-1, -1};
+  hipEvent_t copy_done[MAX_SLOTS] = {};
+  hipEvent_t slot_free[MAX_SLOTS] = {};
+  SlotScheduler<HipExec> sched;  // slots, pass order and position (streamed modes)
+  int nslots = 2;
   int device = 0;
 
   char* ws = nullptr;
@@ -91,7 +106,7 @@ struct lsn_ctx {
 
   // host store
   uint8_t* store = nullptr;  // pinned, n_layers records (host / resident modes)
-  uint8_t* bounce[2] = {nullptr, nullptr};  // pinned bounce buffers (file mode)
+  uint8_t* bounce[MAX_SLOTS] = {};  // pinned bounce buffers, one per slot (file mode)
   int fd = -1;   // file mode: the store file, buffered (writes; reads without O_DIRECT)
   int dfd = -1;  // file mode: the same file opened O_DIRECT for the record reads
   // File mode: a reader thread fills two page-aligned staging buffers, each
@@ -129,10 +144,8 @@ struct lsn_ctx {
   int64_t ext_rows = 0, lpart_floats = 0, gpart_floats = 0;
   int vchunk = 16384;  // vocabulary rows per LM-head GEMM (vchunk_for(max_tokens))
 
-  // pass state
+  // pass state (the layer order and position live in sched)
   int pass_kind = -1, n_seq = 0, seq_len = 0, T = 0;
-  std::vector<int> order, slot_of;
-  size_t pos = 0;
   bool adapters_on = true;
   const float* lm_h = nullptr;
   int lm_T = 0;
@@ -150,7 +163,13 @@ struct lsn_ctx {
   float* head_f = nullptr;  // per-row factors of the LM head [T]
 
   float levels[16];
-  uint64_t loads = 0, bytes_h2d = 0;
+  uint64_t bytes_h2d = 0;
+  // fault injection (tests): spin on the copy stream before each slot copy,
+  // spin on the compute stream before each layer's kernels, fill a slot with
+  // NaN bytes before each copy into it
+  uint32_t copy_delay_us = 0, compute_delay_us = 0;
+  bool poison_slots = false;
+  int wall_khz = 100000;  // device wall-clock rate for the spins
 
   // optional timing of GEMM launches and record copies (event pairs)
   struct ProfRec {
@@ -319,15 +338,35 @@ static bool cfg_valid(const lsn_config* g, std::string* why) {
   if (g->head_on_host && g->mode == LSN_RESIDENT)
     return bad("head_on_host needs a streamed base (the head streams through its slots)");
   if (g->head_chunk_rows < 0 || g->head_chunk_rows % 8) return bad("head_chunk_rows must be a multiple of 8");
+  if (g->n_slots != 0 && (g->n_slots < 2 || g->n_slots > MAX_SLOTS))
+    return bad("n_slots must be 0 (two) or 2..4");
   return true;
+}
+
+// device slots of a streamed configuration (0 in the config: a double buffer)
+static int slot_count(const lsn_config* g) { return g->n_slots ? g->n_slots : 2; }
+
+// Vocabulary rows per LM-head chunk: the configured count, else
+// vchunk_for(max_tokens), and with head_on_host (W_lm streams through the
+// layer slots) no more rows than one slot holds, rounded down to a multiple
+// of 256 (of 8 for a slot of fewer than 256 rows).
+static int head_chunk_rows(const lsn_ctx* c) {
+  const lsn_config& g = c->cfg;
+  if (g.head_chunk_rows > 0) return g.head_chunk_rows;
+  int64_t v = vchunk_for(g.max_tokens);
+  if (g.head_on_host) {
+    const int64_t slot_rows = (int64_t)(c->rec_bytes / ((uint64_t)g.hidden * 2));
+    v = std::min<int64_t>(v, slot_rows >= 256 ? slot_rows / 256 * 256 : slot_rows / 8 * 8);
+  }
+  return (int)v;
 }
 
 // Checks that need the record layout: a head chunk must fit a slot.
 static bool layout_valid(const lsn_ctx* c, std::string* why) {
   const lsn_config& g = c->cfg;
-  if (g.head_on_host && g.head_chunk_rows > 0 &&
-      (uint64_t)g.head_chunk_rows * g.hidden * 2 > c->rec_bytes) {
-    *why = "head_chunk_rows exceed one slot of W_lm rows";
+  const int64_t rows = head_chunk_rows(c);
+  if (g.head_on_host && (rows < 8 || (uint64_t)rows * g.hidden * 2 > c->rec_bytes)) {
+    *why = "an LM-head chunk of W_lm rows must fit one layer slot";
     return false;
   }
   return true;
@@ -377,14 +416,10 @@ static uint64_t carve(lsn_ctx* c, char* base) {
   const lsn_config& g = c->cfg;
   const int64_t T = g.max_tokens, S = g.max_seq_len, H = g.hidden, F = g.ffn, V = g.vocab;
   const int64_t r = g.lora_rank;
-  c->vchunk = vchunk_for(T);
-  if (g.head_on_host)  // a chunk of W_lm rows fits one slot
-    c->vchunk = (int)std::max<int64_t>(
-        256, std::min<int64_t>(c->vchunk, (int64_t)(c->rec_bytes / (uint64_t)(H * 2)) / 256 * 256));
-  if (g.head_chunk_rows > 0) c->vchunk = g.head_chunk_rows;
+  c->vchunk = head_chunk_rows(c);
   Carver cv;
   auto P = [&](uint64_t bytes) -> char* { const uint64_t o = cv.take(bytes); return base ? base + o : nullptr; };
-  const int nrec = (g.mode == LSN_RESIDENT) ? g.n_layers : 2;
+  const int nrec = (g.mode == LSN_RESIDENT) ? g.n_layers : slot_count(&g);
   c->records = (uint8_t*)P((uint64_t)nrec * c->rec_bytes);
   if (!g.head_on_host) {
     c->embed = (uint16_t*)P(V * H * 2);
@@ -429,7 +464,9 @@ static uint64_t carve(lsn_ctx* c, char* base) {
   c->dh2 = (float*)P(T * H * 4);
   c->dO = (uint16_t*)P(T * QD * 2);
   c->dqkv = (float*)P(T * QKV * 4);
-  c->dqkvb = (uint16_t*)P(T * QKV * 2);
+  // bf16 q|k|v input gradient, and the bf16 copy of the fp32 output gradient
+  // [T, hidden] that the dX GEMMs of down and o take: the larger of the two
+  c->dqkvb = (uint16_t*)P(T * std::max<int64_t>(QKV, H) * 2);
   c->lt = (float*)P(NPROJ * T * 16 * 4);
   c->lpart_floats = 0;
   for (int p = 0; p < NPROJ; ++p)
@@ -496,11 +533,6 @@ static uint64_t carve(lsn_ctx* c, char* base) {
 // ---------------------------------------------------------------------------
 // scheduler
 // ---------------------------------------------------------------------------
-static const uint8_t* rec_ptr(lsn_ctx* c, size_t idx) {
-  if (c->cfg.mode == LSN_RESIDENT) return c->records + (uint64_t)c->order[idx] * c->rec_bytes;
-  return c->records + (uint64_t)c->slot_of[idx] * c->rec_bytes;
-}
-
 // dst = src for n bytes, split over a few threads (host memory to pinned
 // host memory; one thread moves ~10 GB/s, a record is ~120 MB at 8B).
 static void parallel_copy(uint8_t* dst, const uint8_t* src, uint64_t n) {
@@ -597,16 +629,31 @@ static void reader_forget(lsn_ctx* c, int layer) {
     if (r.layer[i] == layer) r.layer[i] = -1;
 }
 
-static lsn_status copy_into_slot(lsn_ctx* c, int layer, int s, int next) {
+// Fault injection: the spin and the NaN fill are ordinary kernels on the
+// stream they delay, so results must not change (tests).
+static void inject_copy_faults(lsn_ctx* c, uint8_t* dst, uint64_t bytes) {
+  if (c->poison_slots) fill_u32(dst, 0xFFFFFFFFu, (int64_t)(bytes / 4), c->copy);
+  if (c->copy_delay_us) spin_us(c->copy_delay_us, c->wall_khz, c->copy);
+}
+
+int HipExec::copy_wait_free(int s) {
+  HIPCHK(c, hipStreamWaitEvent(c->copy, c->slot_free[s], 0));
+  return LSN_OK;
+}
+
+// The host waits for the previous copy into a slot before queueing the next,
+// so at most one copy per slot is queued.  With a whole step of copies queued
+// the runtime's copy queue fills: hipMemcpyAsync then blocks the host for
+// milliseconds and later copies reach the engine late.  Every dependency of
+// the waited copy is already enqueued.  (For the file source this also frees
+// the slot's bounce buffer.)
+int HipExec::host_wait_copy(int s) {
+  HIPCHK(c, hipEventSynchronize(c->copy_done[s]));
+  return LSN_OK;
+}
+
+int HipExec::copy_record(int layer, int s, int next) {
   uint8_t* dst = c->records + (uint64_t)s * c->rec_bytes;
-  if (c->slot_used[s]) HIPCHK(c, hipStreamWaitEvent(c->copy, c->slot_free[s], 0));
-  // The host waits for the previous copy into this slot, so at most one
-  // copy per slot is queued.  With a whole step of copies queued the
-  // runtime's copy queue fills: hipMemcpyAsync then blocks the host for
-  // milliseconds and later copies reach the engine late.  Every dependency
-  // of the copy waited for is already enqueued.  (For the file source this
-  // also frees the slot's bounce buffer.)
-  if (c->copy_issued[s]) HIPCHK(c, hipEventSynchronize(c->copy_done[s]));
   const uint8_t* src;
   if (c->cfg.mode == LSN_STREAM_FILE) {
     // O_DIRECT cannot target the pinned bounce buffers (the kernel cannot
@@ -622,76 +669,62 @@ static lsn_status copy_into_slot(lsn_ctx* c, int layer, int s, int next) {
   } else {
     src = c->store + (uint64_t)layer * c->rec_bytes;
   }
+  inject_copy_faults(c, dst, c->rec_bytes);
   lsn_ctx::ProfRec r{1, 0, 0, 0, (double)c->rec_bytes, nullptr, nullptr};
   const bool on = prof_begin(c, &r, c->copy);
   HIPCHK(c, hipMemcpyAsync(dst, src, c->rec_bytes, hipMemcpyHostToDevice, c->copy));
   if (on) prof_end(c, r, c->copy);
   HIPCHK(c, hipEventRecord(c->copy_done[s], c->copy));
-  c->copy_issued[s] = true;
-  c->slot_layer[s] = layer;
-  c->loads += 1;
   c->bytes_h2d += c->rec_bytes;
   return LSN_OK;
 }
 
-// Makes sure the records for pass positions pos and pos+1 are in a slot or
-// on their way.
-static lsn_status ensure_loads(lsn_ctx* c) {
-  if (c->cfg.mode == LSN_RESIDENT) return LSN_OK;
-  const size_t end = std::min(c->order.size(), c->pos + 2);
-  for (size_t i = c->pos; i < end; ++i) {
-    if (c->slot_of[i] >= 0) continue;
-    const int layer = c->order[i];
-    int s = -1;
-    for (int q = 0; q < 2; ++q)
-      if (c->slot_layer[q] == layer) s = q;
-    if (s < 0) {
-      // a slot not holding the record of any other position in the window
-      for (int q = 0; q < 2 && s < 0; ++q) {
-        bool needed = false;
-        for (size_t j = c->pos; j < end; ++j)
-          if (j != i && (c->slot_of[j] == q || (c->slot_of[j] < 0 && c->slot_layer[q] == c->order[j])))
-            needed = true;
-        if (!needed) s = q;
-      }
-      if (s < 0) return fail(c, LSN_ERR_STATE, "scheduler found no free slot");
-      // the record after this one in the pass, for the file reader's read-ahead
-      int next = -1;
-      if (i + 1 < c->order.size()) {
-        next = c->order[i + 1];
-        if (c->slot_layer[0] == next || c->slot_layer[1] == next) next = -1;
-      }
-      lsn_status st = copy_into_slot(c, layer, s, next);
-      if (st != LSN_OK) return st;
-    }
-    c->slot_of[i] = s;
-  }
+int HipExec::compute_wait_copy(int s) {
+  HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_done[s], 0));
   return LSN_OK;
 }
 
+int HipExec::compute_free(int s) {
+  HIPCHK(c, hipEventRecord(c->slot_free[s], c->cs));
+  return LSN_OK;
+}
+
+// Maps a scheduler status to the context's error (the executor's own
+// failures have set the message already).
+static lsn_status sched_status(lsn_ctx* c, int st) {
+  if (st == 0) return LSN_OK;
+  if (st == SCHED_NO_SLOT) return fail(c, LSN_ERR_STATE, "scheduler found no free slot");
+  return (lsn_status)st;
+}
+
 static lsn_status layer_begin(lsn_ctx* c, int kind, int layer, const uint8_t** rec) {
+  SlotScheduler<HipExec>& q = c->sched;
   if (c->pass_kind != kind) return fail(c, LSN_ERR_STATE, "layer call outside a matching pass");
-  if (c->pos >= c->order.size() || c->order[c->pos] != layer)
+  if (q.pos >= q.order.size() || q.order[q.pos] != layer)
     return fail(c, LSN_ERR_STATE, "layer %d out of order (expected %d)", layer,
-                c->pos < c->order.size() ? c->order[c->pos] : -1);
+                q.pos < q.order.size() ? q.order[q.pos] : -1);
   if (!c->loaded[layer]) return fail(c, LSN_ERR_STATE, "layer %d was never loaded", layer);
-  lsn_status st = ensure_loads(c);
-  if (st != LSN_OK) return st;
-  if (c->cfg.mode != LSN_RESIDENT)
-    HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_done[c->slot_of[c->pos]], 0));
-  *rec = rec_ptr(c, c->pos);
+  if (c->cfg.mode == LSN_RESIDENT) {
+    *rec = c->records + (uint64_t)layer * c->rec_bytes;
+  } else {
+    HipExec x{c};
+    int s = -1;
+    lsn_status st = sched_status(c, q.layer_begin(x, &s));
+    if (st != LSN_OK) return st;
+    *rec = c->records + (uint64_t)s * c->rec_bytes;
+  }
+  if (c->compute_delay_us) spin_us(c->compute_delay_us, c->wall_khz, c->cs);
   return LSN_OK;
 }
 
 static lsn_status layer_end(lsn_ctx* c) {
-  if (c->cfg.mode != LSN_RESIDENT) {
-    const int s = c->slot_of[c->pos];
-    HIPCHK(c, hipEventRecord(c->slot_free[s], c->cs));
-    c->slot_used[s] = true;
+  if (c->cfg.mode == LSN_RESIDENT) {
+    c->sched.pos += 1;
+  } else {
+    HipExec x{c};
+    lsn_status st = sched_status(c, c->sched.layer_end(x));
+    if (st != LSN_OK) return st;
   }
-  c->pos += 1;
-  lsn_status st = ensure_loads(c);
-  if (st != LSN_OK) return st;
   return launch_check(c);
 }
 
@@ -1129,16 +1162,12 @@ static LinScratch lin_scratch_or_none(void* scratch, uint64_t sb, int M, int K, 
   return lin_scratch((char*)scratch, M, K, N);
 }
 
-lsn_status lsn_nf4_linear_fwd(const uint8_t* codes, const float* absmax, int32_t M, int32_t K,
-                              int32_t N, const uint16_t* X, const float* A, const float* B,
-                              int32_t r, float s, float* Y, void* scratch, uint64_t sb,
-                              void* hip_stream) {
-  lsn_status st = linear_args_ok(codes, absmax, M, K, N, X, A, B, r, scratch, sb);
-  if (st != LSN_OK || !Y) return st != LSN_OK ? st : LSN_ERR_INVALID;
-  if (M == 0) return LSN_OK;
-  (void)hipGetLastError();  // a status left by the caller's HIP calls is not ours
-  hipStream_t hs = (hipStream_t)hip_stream;
-  const LinScratch L = lin_scratch_or_none(scratch, sb, M, K, N);
+// The forward projection on carved scratch L (adapter products, then the
+// NF4 GEMM with the low-rank extension; split-k partial sums in L.gpart).
+static lsn_status linear_fwd_core(const uint8_t* codes, const float* absmax, int32_t M, int32_t K,
+                                  int32_t N, const uint16_t* X, const float* A, const float* B,
+                                  int32_t r, float s, float* Y, const LinScratch& L,
+                                  hipStream_t hs, const char* what) {
   GemmParams p;
   nf4_levels(p.levels);
   p.M = M; p.N = N; p.K = K;
@@ -1157,8 +1186,21 @@ lsn_status lsn_nf4_linear_fwd(const uint8_t* codes, const float* absmax, int32_t
     p.Aext = L.aext; p.ldae = 16; p.Bext = L.bext; p.ldbe = 16; p.kext = 16;
   }
   const hipError_t e = gemm(p, A_BF16_K, B_NF4_K, 1, hs);
-  if (e != hipSuccess) return fail0(LSN_ERR_HIP, "lsn_nf4_linear_fwd: %s", hipGetErrorString(e));
-  return launch_status0("lsn_nf4_linear_fwd");
+  if (e != hipSuccess) return fail0(LSN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return launch_status0(what);
+}
+
+lsn_status lsn_nf4_linear_fwd(const uint8_t* codes, const float* absmax, int32_t M, int32_t K,
+                              int32_t N, const uint16_t* X, const float* A, const float* B,
+                              int32_t r, float s, float* Y, void* scratch, uint64_t sb,
+                              void* hip_stream) {
+  lsn_status st = linear_args_ok(codes, absmax, M, K, N, X, A, B, r, scratch, sb);
+  if (st != LSN_OK || !Y) return st != LSN_OK ? st : LSN_ERR_INVALID;
+  if (M == 0) return LSN_OK;
+  (void)hipGetLastError();  // a status left by the caller's HIP calls is not ours
+  const LinScratch L = lin_scratch_or_none(scratch, sb, M, K, N);
+  return linear_fwd_core(codes, absmax, M, K, N, X, A, B, r, s, Y, L, (hipStream_t)hip_stream,
+                         "lsn_nf4_linear_fwd");
 }
 
 lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t M, int32_t K,
@@ -1256,6 +1298,8 @@ lsn_status lsn_create(const lsn_config* cfg, void* dev_ws, uint64_t ws_bytes, vo
   (void)hipGetLastError();  // a status left by the caller's HIP calls is not ours
   lsn_ctx* c = new lsn_ctx();
   c->cfg = *cfg;
+  c->nslots = slot_count(cfg);
+  c->sched.init(c->nslots);
   if (cfg->store_path) c->store_path = cfg->store_path;
   c->cfg.store_path = c->store_path.c_str();
   record_layout(c);
@@ -1285,10 +1329,13 @@ lsn_status lsn_create(const lsn_config* cfg, void* dev_ws, uint64_t ws_bytes, vo
   if (hipGetDevice(&c->device) != hipSuccess) return cleanup(LSN_ERR_HIP);
   if (hipStreamCreateWithFlags(&c->copy, hipStreamNonBlocking) != hipSuccess)
     return cleanup(LSN_ERR_HIP);
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < c->nslots; ++i)
     if (hipEventCreateWithFlags(&c->copy_done[i], hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&c->slot_free[i], hipEventDisableTiming) != hipSuccess)
       return cleanup(LSN_ERR_HIP);
+  if (hipDeviceGetAttribute(&c->wall_khz, hipDeviceAttributeWallClockRate, c->device) != hipSuccess ||
+      c->wall_khz <= 0)
+    return cleanup(LSN_ERR_HIP);
   if (cfg->mode == LSN_STREAM_FILE) {
     c->fd = open(c->store_path.c_str(), O_RDWR | O_CREAT, 0644);
     if (c->fd < 0) return cleanup(LSN_ERR_IO);
@@ -1304,7 +1351,7 @@ lsn_status lsn_create(const lsn_config* cfg, void* dev_ws, uint64_t ws_bytes, vo
       c->rd.buf[i] = (uint8_t*)m;
     }
     c->rd.th = std::thread(reader_main, c);
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < c->nslots; ++i)
       if (hipHostMalloc((void**)&c->bounce[i], c->rec_bytes, hipHostMallocDefault) != hipSuccess)
         return cleanup(LSN_ERR_HIP);
   } else {
@@ -1326,7 +1373,7 @@ void lsn_destroy(lsn_ctx* c) {
   // teardown: errors here have nowhere to go
   if (c->copy) (void)hipStreamSynchronize(c->copy);
   (void)hipStreamSynchronize(c->cs);
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < MAX_SLOTS; ++i) {
     if (c->copy_done[i]) (void)hipEventDestroy(c->copy_done[i]);
     if (c->slot_free[i]) (void)hipEventDestroy(c->slot_free[i]);
     if (c->bounce[i]) (void)hipHostFree(c->bounce[i]);
@@ -1417,8 +1464,7 @@ lsn_status lsn_load_layer_nf4(lsn_ctx* c, int32_t layer, const uint8_t* const* c
     HIPCHK(c, hipStreamSynchronize(c->cs));
   }
   // a slot or staging buffer holding an older copy of this layer is stale now
-  for (int s = 0; s < 2; ++s)
-    if (c->slot_layer[s] == layer) c->slot_layer[s] = -1;
+  c->sched.forget(layer);
   reader_forget(c, layer);
   c->loaded[layer] = 1;
   return LSN_OK;
@@ -1518,11 +1564,16 @@ lsn_status lsn_begin_pass(lsn_ctx* c, int32_t kind, int32_t n_seq, int32_t seq_l
   c->n_seq = n_seq;
   c->seq_len = seq_len;
   c->T = n_seq * seq_len;
-  c->order.resize(L);
-  for (int i = 0; i < L; ++i) c->order[i] = (kind == LSN_PASS_FWD) ? i : L - 1 - i;
-  c->slot_of.assign(L, -1);
-  c->pos = 0;
-  return ensure_loads(c);
+  std::vector<int> order(L);
+  for (int i = 0; i < L; ++i) order[i] = (kind == LSN_PASS_FWD) ? i : L - 1 - i;
+  if (c->cfg.mode == LSN_RESIDENT) {  // no copies: the order only
+    c->sched.order = order;
+    c->sched.slot_of.assign(L, -1);
+    c->sched.pos = 0;
+    return LSN_OK;
+  }
+  HipExec x{c};
+  return sched_status(c, c->sched.begin(x, order));
 }
 
 lsn_status lsn_embed(lsn_ctx* c, const int32_t* tokens, float* h0) {
@@ -1592,17 +1643,18 @@ static lsn_status lm_logits_chunk(lsn_ctx* c, const uint16_t* W, int Vc) {
 }
 
 // head_on_host: W_lm rows [v0, v0 + Vc) into slot s on the copy stream, after
-// the slot's previous user is done (as copy_into_slot does for records).
+// the slot's previous reader is done (the scheduler's foreign-data protocol).
 static lsn_status copy_head_chunk(lsn_ctx* c, int v0, int Vc, int s) {
   uint8_t* dst = c->records + (uint64_t)s * c->rec_bytes;
-  if (c->slot_used[s]) HIPCHK(c, hipStreamWaitEvent(c->copy, c->slot_free[s], 0));
-  if (c->copy_issued[s]) HIPCHK(c, hipEventSynchronize(c->copy_done[s]));
+  HipExec x{c};
+  lsn_status st = sched_status(c, c->sched.foreign_prepare(x, s));
+  if (st != LSN_OK) return st;
   const uint64_t bytes = (uint64_t)Vc * c->cfg.hidden * 2;
+  inject_copy_faults(c, dst, bytes);
   HIPCHK(c, hipMemcpyAsync(dst, c->lm_head_h + (int64_t)v0 * c->cfg.hidden, bytes,
                            hipMemcpyHostToDevice, c->copy));
   HIPCHK(c, hipEventRecord(c->copy_done[s], c->copy));
-  c->copy_issued[s] = true;
-  c->slot_layer[s] = -1;  // the slot holds no layer record any more
+  c->sched.foreign_copied(s);
   c->bytes_h2d += bytes;
   return LSN_OK;
 }
@@ -1620,24 +1672,31 @@ lsn_status lsn_lm_head_logprobs(lsn_ctx* c, const float* h, const int32_t* targe
   if (!c->head_loaded) return fail(c, LSN_ERR_STATE, "head tables not loaded");
   const int T = c->T, V = c->cfg.vocab, H = c->cfg.hidden;
   const bool acc = want_grad_state != 0;
-  // head_on_host: W_lm streams through the two slots chunk by chunk, the
-  // next chunk copying while this one computes; the slots' layer records
-  // are overwritten, so no layer pass may be under way
+  // head_on_host: W_lm streams through two slots chunk by chunk, the next
+  // chunk copying while this one computes; those slots' layer records are
+  // overwritten (the two released earliest, whose records the next pass
+  // needs last), so no layer pass may be under way
   const bool host = c->cfg.head_on_host != 0;
-  if (host && c->pos < c->order.size())
+  if (host && c->sched.in_pass())
     return fail(c, LSN_ERR_STATE, "lm_head with head_on_host inside a layer pass");
   const int nch = (V + c->vchunk - 1) / c->vchunk;
-  if (host)
+  int hs[2] = {0, 1};
+  if (host) {
+    lsn_status st = sched_status(c, c->sched.foreign_slots(2, hs));
+    if (st != LSN_OK) return st;
     for (int i = 0; i < std::min(nch, 2); ++i) {
-      lsn_status st = copy_head_chunk(c, i * c->vchunk, std::min(c->vchunk, V - i * c->vchunk), i);
+      st = copy_head_chunk(c, i * c->vchunk, std::min(c->vchunk, V - i * c->vchunk), hs[i]);
       if (st != LSN_OK) return st;
     }
+  }
   rmsnorm_fwd(h, c->final_norm, T, H, c->cfg.rms_eps, c->nf, c->rstdf, c->cs);
   for (int i = 0, v0 = 0; v0 < V; ++i, v0 += c->vchunk) {
-    const int Vc = std::min(c->vchunk, V - v0), sl = i & 1;
+    const int Vc = std::min(c->vchunk, V - v0), sl = hs[i & 1];
     const uint16_t* W = c->lm_head + (int64_t)v0 * H;
     if (host) {
-      HIPCHK(c, hipStreamWaitEvent(c->cs, c->copy_done[sl], 0));
+      HipExec x{c};
+      lsn_status st = sched_status(c, c->sched.foreign_acquire(x, sl));
+      if (st != LSN_OK) return st;
       W = reinterpret_cast<const uint16_t*>(c->records + (uint64_t)sl * c->rec_bytes);
     }
     lsn_status st = lm_logits_chunk(c, W, Vc);
@@ -1657,8 +1716,9 @@ lsn_status lsn_lm_head_logprobs(lsn_ctx* c, const float* h, const int32_t* targe
       HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, 1));
     }
     if (host) {
-      HIPCHK(c, hipEventRecord(c->slot_free[sl], c->cs));
-      c->slot_used[sl] = true;
+      HipExec x{c};
+      st = sched_status(c, c->sched.foreign_release(x, sl));
+      if (st != LSN_OK) return st;
       if (i + 2 < nch) {
         const int v2 = (i + 2) * c->vchunk;
         st = copy_head_chunk(c, v2, std::min(c->vchunk, V - v2), sl);
@@ -1666,7 +1726,7 @@ lsn_status lsn_lm_head_logprobs(lsn_ctx* c, const float* h, const int32_t* targe
       }
     }
   }
-  lse_final(c->run_m, c->run_s, c->tlogit, targets, T, logp, c->lse, acc ? c->head_f : nullptr,
+  lse_final(c->run_m, c->run_s, c->tlogit, targets, T, V, logp, c->lse, acc ? c->head_f : nullptr,
             c->cs);
   if (acc) scale_rows(c->dnf, c->head_f, T, H, c->cs);
   c->lm_h = h;
@@ -1686,7 +1746,7 @@ lsn_status lsn_lm_head_backward(lsn_ctx* c, const float* h, const int32_t* targe
     return fail(c, LSN_ERR_STATE,
                 "lm_head_backward must follow lm_head_logprobs with want_grad_state on the same h");
   const int T = c->T, H = c->cfg.hidden;
-  head_grad(dlogp, targets, c->lm_head, T, H, c->dnf, c->cs);
+  head_grad(dlogp, targets, c->lm_head, T, H, c->cfg.vocab, c->dnf, c->cs);
   rmsnorm_bwd(h, c->final_norm, c->rstdf, c->dnf, nullptr, T, H, dh, c->cs);
   c->lm_grad = false;  // the accumulator is consumed
   return launch_check(c);
@@ -1726,7 +1786,7 @@ lsn_status lsn_pref_loss(lsn_ctx* c, int32_t kind, const float* lp, const float*
 lsn_status lsn_stats(const lsn_ctx* c, uint64_t* layer_loads, uint64_t* bytes_h2d,
                      uint64_t* ws_bytes) {
   if (!c) return LSN_ERR_INVALID;
-  if (layer_loads) *layer_loads = c->loads;
+  if (layer_loads) *layer_loads = c->sched.loads;
   if (bytes_h2d) *bytes_h2d = c->bytes_h2d;
   if (ws_bytes) *ws_bytes = c->ws_needed;
   return LSN_OK;
@@ -1768,6 +1828,18 @@ lsn_status lsn_profile_query(lsn_ctx* c, int32_t what, int32_t a, int32_t b, int
   if (count) *count = n;
   if (work) *work = w;
   if (ms) *ms = t;
+  return LSN_OK;
+}
+
+lsn_status lsn_set_fault_injection(lsn_ctx* c, int32_t copy_delay_us, int32_t compute_delay_us,
+                                   int32_t poison_slots) {
+  CHECK_CTX(c);
+  if (copy_delay_us < 0 || copy_delay_us > 100000 || compute_delay_us < 0 ||
+      compute_delay_us > 100000)
+    return fail(c, LSN_ERR_INVALID, "fault-injection delays must be 0..100000 us");
+  c->copy_delay_us = (uint32_t)copy_delay_us;
+  c->compute_delay_us = (uint32_t)compute_delay_us;
+  c->poison_slots = poison_slots != 0;
   return LSN_OK;
 }
 

@@ -28,7 +28,7 @@ PREF_LOSSES = {"dpo": L.LSN_LOSS_DPO, "simpo": L.LSN_LOSS_SIMPO, "orpo": L.LSN_L
 
 def make_config(shape, mode="stream_host", max_tokens=None, max_seq_len=None,
                 lora_targets=("q", "v"), store_path=None, vram_budget=0, head_on_host=False,
-                head_chunk_rows=0):
+                head_chunk_rows=0, n_slots=0):
     """lsn_config from a shape dict (n_layers, hidden, n_heads, n_kv_heads,
     head_dim, ffn, vocab, rms_eps, rope_theta, lora_rank, lora_alpha, tied)."""
     cfg = L.lsn_config()
@@ -52,6 +52,7 @@ def make_config(shape, mode="stream_host", max_tokens=None, max_seq_len=None,
     cfg.vram_budget = vram_budget
     cfg.head_on_host = int(bool(head_on_host))
     cfg.head_chunk_rows = head_chunk_rows
+    cfg.n_slots = n_slots
     return cfg
 
 
@@ -60,13 +61,15 @@ class LayerStreamedLoRA:
 
     def __init__(self, shape, mode="stream_host", max_tokens=None, max_seq_len=None,
                  lora_targets=("q", "v"), store_path=None, device="cuda:0", stream=None,
-                 head_on_host=False, head_chunk_rows=0):
+                 head_on_host=False, head_chunk_rows=0, n_slots=0, vram_budget=0):
         """mode: resident | stream_host | stream_file | auto.  'auto' keeps the
         base in pinned RAM when it fits and in a file (store_path, or a file
         in $TMPDIR) when it does not; every mode is pre-flighted against the
         free device memory (adapter.NoFit).  head_on_host (streamed modes):
         the embedding and LM-head tables stay in pinned host memory and W_lm
-        streams through the layer slots."""
+        streams through the layer slots.  n_slots: device slots of the layer
+        stream (0: two).  vram_budget: lsn_create refuses a workspace larger
+        than this many bytes (0: no limit)."""
         import tempfile
 
         import torch
@@ -78,7 +81,8 @@ class LayerStreamedLoRA:
         # sizes only (a streamed file store needs no path for them)
         probe = make_config(shape, "stream_host" if mode in ("auto", "stream_file") else mode,
                             max_tokens, max_seq_len, lora_targets, store_path,
-                            head_on_host=head_on_host, head_chunk_rows=head_chunk_rows)
+                            head_on_host=head_on_host, head_chunk_rows=head_chunk_rows,
+                            n_slots=n_slots)
         free, _ = torch.cuda.mem_get_info(self.device)
         mode = adapter.plan_run(shape["n_layers"], L.lsn_config_record_bytes(probe),
                                 L.lsn_workspace_bytes(probe), free,
@@ -90,7 +94,8 @@ class LayerStreamedLoRA:
             self._own_store = store_path
         self.mode = mode
         self.cfg = make_config(shape, mode, max_tokens, max_seq_len, lora_targets, store_path,
-                               head_on_host=head_on_host, head_chunk_rows=head_chunk_rows)
+                               vram_budget=vram_budget, head_on_host=head_on_host,
+                               head_chunk_rows=head_chunk_rows, n_slots=n_slots)
         self.lora_targets = tuple(lora_targets)
         self.ws_bytes = L.lsn_workspace_bytes(self.cfg)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
@@ -268,6 +273,29 @@ class LayerStreamedLoRA:
             if lr is not None:
                 L.lsn_sgd_step(self.ctx, lr)
             return self.loss
+
+
+def check_ids(tokens, targets, vocab):
+    """Host-side range check of a batch before it goes to the device: every
+    token id in [0, vocab), every target in [0, vocab) or -1 (no target).
+    The kernels stay in bounds for any id (an out-of-range token embeds as a
+    NaN row, an out-of-range target gives a NaN log-prob), so this turns a
+    bad batch into an error instead of a NaN loss."""
+    tokens = np.asarray(tokens)
+    targets = np.asarray(targets)
+    if tokens.size and (tokens.min() < 0 or tokens.max() >= vocab):
+        raise ValueError(f"token ids must lie in [0, {vocab})")
+    if targets.size and (targets.min() < -1 or targets.max() >= vocab):
+        raise ValueError(f"targets must lie in [0, {vocab}) or be -1")
+
+
+def device_batch(tokens, targets, vocab, device="cuda"):
+    """Checked int32 device copies of host tokens and targets (flattened)."""
+    import torch
+    tokens = np.ascontiguousarray(np.asarray(tokens).reshape(-1), dtype=np.int32)
+    targets = np.ascontiguousarray(np.asarray(targets).reshape(-1), dtype=np.int32)
+    check_ids(tokens, targets, vocab)
+    return (torch.from_numpy(tokens).to(device), torch.from_numpy(targets).to(device))
 
 
 def sft_targets(tokens):

@@ -16,10 +16,11 @@ Modules
 
 Sources.  The method is described on five web pages about the "Soup" CLI:
   * "Soup: Fine-Tune an 8B Model on a 4 GB GPU" (lucaberton.com), section
-    "The Core Idea: Layer Streaming": frozen base in host RAM or NVMe, copied
-    into VRAM one decoder layer at a time on a dedicated stream, optionally NF4;
-    only the LoRA adapter trains; for DPO the reference model is the same base
-    with adapters disabled.
+    "The Core Idea: Layer Streaming": the frozen weights live off the GPU (host
+    memory or a disk) and reach it layer by layer, through a copy stream of
+    their own, when a pass needs them; they may be stored as NF4; the LoRA
+    adapter is the only trained state; DPO's reference model is that same
+    base run without the adapter.
   * "Show HN: Fine-tune an 8B model on a 4 GB laptop GPU" (elseif.net),
     first and second paragraphs: policy and reference log-probabilities from
     two runs of the same base, bit-exact against a non-streamed run.

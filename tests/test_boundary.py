@@ -175,3 +175,45 @@ def test_one_hip_runtime_in_the_process():
     with open("/proc/self/maps") as f:
         paths = {line.split()[-1] for line in f if "libamdhip64" in line}
     assert len(paths) == 1, paths
+
+
+def test_host_id_check():
+    """trainer.check_ids: token ids in [0, vocab), targets in [0, vocab) or
+    -1; anything else is refused on the host before a batch reaches the
+    device."""
+    from layer_streamed_nf4_double_amd.trainer import check_ids
+    tok = np.array([[0, 5, 1023]], np.int32)
+    check_ids(tok, np.array([5, 1023, -1], np.int32), 1024)
+    for bad_tok, bad_tgt in [([[0, 1024, 3]], [1, 2, -1]), ([[-1, 2, 3]], [1, 2, -1]),
+                             ([[0, 1, 2]], [1, 1024, -1]), ([[0, 1, 2]], [1, -2, -1])]:
+        with pytest.raises(ValueError):
+            check_ids(np.array(bad_tok, np.int32), np.array(bad_tgt, np.int32), 1024)
+
+
+def test_config_checks_without_a_gpu():
+    """Configuration errors come back as LSN_ERR_INVALID from the sizing
+    calls (no device needed): the slot count, and an LM-head chunk that
+    cannot fit a layer slot when the head streams through the slots."""
+    L = _lib()
+    import synth
+    from layer_streamed_nf4_double_amd.trainer import make_config
+    w = synth.WORKLOADS["tiny"]
+    base = L.lsn_workspace_bytes(make_config(w, "stream_host"))
+    assert L.lsn_workspace_bytes(make_config(w, "stream_host", n_slots=2)) == base
+    rec = L.lsn_config_record_bytes(make_config(w, "stream_host"))
+    assert L.lsn_workspace_bytes(make_config(w, "stream_host", n_slots=4)) == base + 2 * rec
+    assert L.lsn_workspace_bytes(make_config(w, "resident", n_slots=4)) == \
+        L.lsn_workspace_bytes(make_config(w, "resident"))
+    for n in (1, 5, -1):
+        with pytest.raises(L.LsnError) as e:
+            L.lsn_workspace_bytes(make_config(w, "stream_host", n_slots=n))
+        assert e.value.status == L.LSN_ERR_INVALID
+    # an explicit head chunk larger than a slot of W_lm rows
+    rows = rec // (2 * w["hidden"]) // 8 * 8 + 8
+    with pytest.raises(L.LsnError):
+        L.lsn_workspace_bytes(make_config(w, "stream_host", head_on_host=True,
+                                          head_chunk_rows=rows))
+    # the automatic head chunk of a tiny slot stays inside it: a 1-layer,
+    # 64-wide stack whose slot holds fewer than 256 W_lm rows
+    small = dict(w, hidden=64, n_heads=1, n_kv_heads=1, head_dim=64, ffn=64, vocab=4096)
+    L.lsn_workspace_bytes(make_config(small, "stream_host", head_on_host=True))

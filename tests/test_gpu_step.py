@@ -669,7 +669,8 @@ def test_dpo_llama8b_layer_shape_vs_oracle(torch, llama2l_oracle):
 def test_sft_qwen3b_layer_shape_vs_oracle(torch):
     """One streamed SFT step at the 3B layer shape (hidden 2048, 16 q / 2 kv
     heads of 128, FFN 11008, tied embedding, RoPE theta 1e6, eps 1e-6), two
-    layers, vocabulary 1024, 512 tokens, against the oracle."""
+    layers, vocabulary 1024, 512 tokens, against the oracle; then the same
+    step with the base resident gives the same bits."""
     w = dict(synth.WORKLOADS["qwen2.5-3b-shaped"], n_layers=2, vocab=1024)
     tokens = synth.sft_tokens(w)
     say("[sft-3b-shape] oracle")
@@ -688,3 +689,14 @@ def test_sft_qwen3b_layer_shape_vs_oracle(torch):
             oA, oB = o["grads"][layer][p]
             assert_close(dA, oA, 5e-2, f"dA L{layer} {p}")
             assert_close(dB, oB, 5e-2, f"dB L{layer} {p}")
+    say("[sft-3b-shape] gpu resident (bitwise)")
+    r = gpu_model(w, "resident", b_zero=False)
+    loss_r, logp_r = _run_sft(torch, r, tokens)
+    gr = _grads(r, w)
+    r.close()
+    assert np.array_equal(_bits(np.float32(loss_r)), _bits(np.float32(loss)))
+    assert np.array_equal(_bits(logp_r), _bits(logp))
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            for u, v in zip(g[layer][p], gr[layer][p]):
+                assert np.array_equal(_bits(np.asarray(u)), _bits(np.asarray(v)))

@@ -100,11 +100,20 @@ def _model(w, mode, records, head):
 
 
 def test_full_depth_streamed_equals_resident(torch):
-    """One SFT step of the full 8B workload, streamed from pinned host memory
-    and with the base resident on the device: the loss, all 512 logp and
-    the adapter gradients of the first and last layers are the same bits;
-    the streamed step copies each record once in the forward and all but
-    the two last layers again in the backward."""
+    """One SFT step of the full 8B workload with the base resident on the
+    device, then streamed from pinned host memory with the process's
+    allocator capped at 4 GiB (the evermx page's notebook caps a card to
+    4 GB and asserts the streamed model equals a normal one): the loss, all
+    512 logp and the adapter gradients of the first and last layers are the
+    same bits; the resident model does not fit under the cap; the streamed
+    step copies each record once in the forward and all but the two last
+    layers again in the backward; and the resident peak exceeds the streamed
+    peak by exactly the L - 2 records the slots replace (one copy of the
+    weights minus two records, to the allocator's 1 MiB granularity: "Show
+    HN: Fine-tune an 8B model on a 4 GB laptop GPU", second paragraph,
+    prices a second resident copy of the weights at one copy of the
+    weights)."""
+    from layer_streamed_nf4_double_amd import _lib as L
     from layer_streamed_nf4_double_amd.trainer import sft_targets
     w = W8
     say("[full-8b] quantize 32 layers")
@@ -114,18 +123,44 @@ def test_full_depth_streamed_equals_resident(torch):
     tok = torch.from_numpy(tokens.reshape(-1).astype(np.int32)).cuda()
     tgt = torch.from_numpy(sft_targets(tokens)).cuda()
     S = w["seq_len"]
+    cap = 4 << 30
     out = {}
+    import gc
     for mode in ("resident", "stream_host"):
-        say(f"[full-8b] {mode}")
-        m = _model(w, mode, records, head)
-        m.sft_step(tok, tgt, 1, S, None)
-        m.sync()
-        grads = {(l, p): m.get_lora(l, p)[2:] for l in (0, w["n_layers"] - 1) for p in ("q", "v")}
-        out[mode] = (m.loss[0].item(), m.logp[:S].cpu().numpy().copy(), grads, m.stats()[0])
-        m.close()
-        del m
+        gc.collect()
+        torch.cuda.synchronize()
         torch.cuda.empty_cache()
-    (lr_, pr, gr, _), (ls, ps, gs, loads) = out["resident"], out["stream_host"]
+        base = torch.cuda.memory_allocated()
+        capped = mode == "stream_host"
+        if capped:
+            total = torch.cuda.get_device_properties(0).total_memory
+            torch.cuda.set_per_process_memory_fraction((cap + base) / total)
+            with pytest.raises((torch.cuda.OutOfMemoryError, RuntimeError)):
+                _model(w, "resident", records, head)
+            gc.collect()
+            torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        try:
+            say(f"[full-8b] {mode}" + (" under a 4 GiB cap" if capped else ""))
+            m = _model(w, mode, records, head)
+            m.sft_step(tok, tgt, 1, S, None)
+            m.sync()
+            peak = torch.cuda.max_memory_allocated() - base
+            rec_bytes = L.lsn_record_bytes(m.ctx)
+            grads = {(l, p): m.get_lora(l, p)[2:] for l in (0, w["n_layers"] - 1)
+                     for p in ("q", "v")}
+            out[mode] = (m.loss[0].item(), m.logp[:S].cpu().numpy().copy(), grads, m.stats()[0],
+                         peak, rec_bytes)
+            m.close()
+            del m
+        finally:
+            gc.collect()
+            torch.cuda.empty_cache()
+            if capped:
+                torch.cuda.set_per_process_memory_fraction(1.0)
+    (lr_, pr, gr, _, peak_r, rb), (ls, ps, gs, loads, peak_s, _) = (out["resident"],
+                                                                     out["stream_host"])
+    say(f"[full-8b] peak resident {peak_r / 1e9:.3f} GB, streamed {peak_s / 1e9:.3f} GB")
     assert np.float32(lr_).view(np.uint32) == np.float32(ls).view(np.uint32)
     assert np.array_equal(pr.view(np.uint32), ps.view(np.uint32))
     for k in gr:
@@ -133,3 +168,7 @@ def test_full_depth_streamed_equals_resident(torch):
             assert np.any(x != 0), k
             assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), k
     assert loads == 2 * w["n_layers"] - 2, loads
+    assert peak_s <= cap
+    # to the caching allocator's granularity (a large allocation's segment is
+    # rounded up to 2 MiB; an unsplit tail under 1 MiB counts as allocated)
+    assert abs((peak_r - peak_s) - (w["n_layers"] - 2) * rb) < (1 << 20), (peak_r - peak_s, rb)
