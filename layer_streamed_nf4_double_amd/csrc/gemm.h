@@ -94,7 +94,14 @@ void gemm_reduce_launch(const GemmParams& p, hipStream_t s);
 // forward NF4 kernel (gemm_nf4f.hip): y = x W with x bf16 [M, K] row-major and
 // W^T NF4 [N, K]; used by gemm() whenever nf4f_eligible() holds
 bool nf4f_eligible(const GemmParams& p, int batch);
+// the k split of the 256 x 256 NF4 tile (both NF4 kernels)
 int nf4f_split(int M, int N, int K);
+// the forward kernel's column tiles per wave (nt = 2: 256 x 256 tile, 1:
+// 256 x 128) and k split for a problem (gemm_partial_floats covers it)
+struct Nf4fPlan {
+  int nt, split;
+};
+Nf4fPlan nf4f_plan(int M, int N, int K);
 hipError_t nf4f_launch(GemmParams p, hipStream_t s);
 
 // input-gradient NF4 kernel (gemm_nf4t.hip): dx = dy W with dy bf16 [M, K]

@@ -627,8 +627,8 @@ GemmPlan gemm_plan(int M, int N, int K, int nseg, int batch) {
 int64_t gemm_partial_floats(int M, int N, int K, int nseg, int batch) {
   const GemmPlan g = gemm_plan(M, N, K, nseg, batch);
   int64_t f = g.split > 1 ? g.split * split_stride(M, N) : 0;
-  if (batch == 1 && nseg == 1 && M >= 256 && K % 64 == 0) {  // the 256 x 256 NF4 kernels
-    const int sp = nf4f_split(M, N, K);
+  if (batch == 1 && nseg == 1 && M >= 256 && K % 64 == 0) {  // the fused NF4 kernels
+    const int sp = std::max(nf4f_split(M, N, K), nf4f_plan(M, N, K).split);
     if (sp > 1) f = std::max<int64_t>(f, sp * split_stride(M, N));
   }
   return f;

@@ -8,15 +8,22 @@
 // in the low nibble, one fp32 absmax per 64 consecutive elements of a row),
 // so every 64-deep K slice of a row is exactly one absmax block.
 //
-// Work split.  A workgroup of four waves (one per SIMD) owns a 256 x 256
-// output tile; wave w owns all 256 rows and the 64 columns n0 + 64w .. +63,
-// i.e. 8 x 2 tiles of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per
-// lane).  Because the waves split only the N dimension, each weight element
-// of the tile is dequantized exactly once per workgroup, directly into the
+// Work split.  A workgroup of four waves (one per SIMD) owns a 256 x 128 NT
+// output tile (NT = 2: 256 x 256; NT = 1: 256 x 128, for narrow projections);
+// wave w owns all 256 rows and the 32 NT columns n0 + 32 NT w .. , i.e. 8 x NT
+// tiles of v_mfma_f32_32x32x16_bf16 (128 NT fp32 accumulators per lane).
+// Because the waves split only the N dimension, each weight element of the
+// tile is dequantized exactly once per workgroup, directly into the
 // B-fragment registers of the wave that uses it; the dequantized weight never
 // passes through LDS.  Only the activation slice [256 x 64] is shared through
-// LDS, so LDS read traffic per MFMA is half that of a 64 x 64 wave tile that
-// reads both operands from LDS.
+// LDS: 0.5 (NT = 2) or 1 (NT = 1) KiB of LDS reads per MFMA.
+//
+// Tile choice (nf4f_plan).  A narrow projection at a few hundred tokens has
+// few 256 x 256 tiles (32 at 512 x 4096 -> 4096), so filling 256 compute
+// units takes an 8-way k split whose fp32 partial sums (8 copies of the
+// output) cost more than the MFMAs.  The 256 x 128 tile doubles the tile
+// count and halves the split and its partial-sum traffic, at twice the LDS
+// reads per MFMA (about half the measured LDS bandwidth).
 //
 // K order inside a slice.  An MFMA sums over 16 k; which 16 of the slice's 64
 // it takes is free as long as both operands agree.  Lane half h (lane / 32)
@@ -50,11 +57,16 @@ namespace lsn {
 
 namespace {
 
-constexpr int FM = 256, FN = 256, FK = 64;
+constexpr int FM = 256, FK = 64;
 constexpr int NST = 3;                 // LDS stages
 constexpr int A_STAGE = FM * FK * 2;   // 32 KiB of activations (bf16)
-constexpr int C_STAGE = FN * FK / 2;   // 8 KiB of codes
-constexpr int GROUP = 8 + 2 + 1;       // direct loads per wave per slice
+// per column-tile count NT: tile width, codes per stage, direct loads per
+// wave per slice (8 activation, NT code, 1 absmax)
+template <int NT> struct Shape {
+  static constexpr int FN = 128 * NT;
+  static constexpr int C_STAGE = FN * FK / 2;
+  static constexpr int GROUP = 8 + NT + 1;
+};
 
 // Eight NF4 codes (one 32-bit word; element 2p in the low nibble of byte p)
 // to eight bf16 products level * absmax, each rounded once.
@@ -74,13 +86,16 @@ LSN_DEV bf16x8 dequant8(uint32_t q, float a, Pair pair) {
 // MODE: the output form (C_F32, C_F32_ACC, C_F32_RES, C_BF16), or -1 for the
 // raw split-k partial sums; one instantiation per form keeps the epilogue a
 // single straight-line path per tile kind.
-template <int MODE>
+template <int MODE, int NT>
 __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
+  constexpr int FN = Shape<NT>::FN, C_STAGE = Shape<NT>::C_STAGE, GROUP = Shape<NT>::GROUP;
+  constexpr int NS = 8 * NT;  // MFMA slots per k-step
   // the level-pair table first: its LDS address fits the 16-bit ds_read offset
   __shared__ __attribute__((aligned(64))) float2 sPair[256];
   __shared__ __attribute__((aligned(1024))) uint8_t sA[NST][A_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sC[NST][C_STAGE];
-  __shared__ __attribute__((aligned(1024))) float sM[NST][FN];
+  // absmax: 64 entries per wave (rows beyond its 32 NT columns are unused)
+  __shared__ __attribute__((aligned(1024))) float sM[NST][4 * 64];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -111,12 +126,12 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
     const int row = min(m0 + r, p.M - 1);
     offA[i] = (uint32_t)(((int64_t)row * p.lda + c * 8) * 2);
   }
-  // codes: load i of wave w fills weight rows (2w + i) * 32 .. +31 (32 B
+  // codes: load i of wave w fills weight rows (NT w + i) * 32 .. +31 (32 B
   // each); lane -> row + lane / 2, physical half lane % 2
-  uint32_t offC[2];
+  uint32_t offC[NT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (w * 2 + i) * 32 + (lane >> 1);
+  for (int i = 0; i < NT; ++i) {
+    const int r = (w * NT + i) * 32 + (lane >> 1);
     const int h = (lane & 1) ^ ((r >> 3) & 1);
     const int row = min(n0 + r, p.N - 1);
     offC[i] = (uint32_t)((int64_t)row * (p.K / 2) + h * 16);
@@ -124,14 +139,15 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   // the same offsets for loads at instruction offset 1024 i - 4096 from one
   // M0 (activation load i) and at 1024 i (code load i); never negative,
   // since load i covers rows >= 8 i (activations) or >= 32 i (codes)
-  uint32_t offA_o[8], offC_o[2];
+  uint32_t offA_o[8], offC_o[NT];
 #pragma unroll
   for (int i = 0; i < 8; ++i) offA_o[i] = offA[i] + 4096u - 1024u * i;
-  offC_o[0] = offC[0];
-  offC_o[1] = offC[1] - 1024u;
-  // absmax: wave w fills rows 64w .. +63, lane -> row 64w + lane
+#pragma unroll
+  for (int i = 0; i < NT; ++i) offC_o[i] = offC[i] - 1024u * i;
+  // absmax: wave w fills its 64-entry region with rows 32 NT w + lane
+  // (clamped; with NT = 1 the upper half is unused)
   const uint32_t offM =
-      (uint32_t)((int64_t)min(n0 + w * 64 + lane, p.N - 1) * (p.K / FK) * 4);
+      (uint32_t)((int64_t)min(n0 + w * 32 * NT + lane, p.N - 1) * (p.K / FK) * 4);
 
   const uint8_t* gA = reinterpret_cast<const uint8_t*>(p.A);
   const uint8_t* gC = reinterpret_cast<const uint8_t*>(p.B);
@@ -149,9 +165,9 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) dma16(a, offA[i], la + i * 1024);
     const uint8_t* c = gC + it * (FK / 2);
-    const uint32_t lc = lds_addr(sC[st]) + w * 2 * 1024;
-    dma16(c, offC[0], lc);
-    dma16(c, offC[1], lc + 1024);
+    const uint32_t lc = lds_addr(sC[st]) + w * NT * 1024;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) dma16(c, offC[i], lc + i * 1024);
     dma4(gM + it * 4, offM, lds_addr(&sM[st][w * 64]));
   };
 
@@ -159,54 +175,54 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   // activation fragment of row tile i, k-step kk: row i*32 + lr, logical chunk
   // 4*hh + kk -> physical (4*hh ^ swz(lr)) ^ kk (kk only flips the low bits)
   const int sa0 = lr * 128 + (((4 * hh) ^ swz(lr)) * 16);
-  // codes of column tile j: row 64w + 32j + lr, logical half hh
-  const int sc0 = (w * 64 + lr) * 32 + ((hh ^ ((lr >> 3) & 1)) * 16);
+  // codes of column tile j: row 32 NT w + 32j + lr, logical half hh
+  const int sc0 = (w * 32 * NT + lr) * 32 + ((hh ^ ((lr >> 3) & 1)) * 16);
   const int sm0 = w * 64 + lr;
 
-  f32x16 acc[8][2];
+  f32x16 acc[8][NT];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  bf16x8 af[2][8];  // activation fragments, double buffered over k-steps
-  bf16x8 bq[2][2];  // weight fragments [kk & 1][j]
-  u32x4 cq[2], cqn[2];  // codes of this slice and of the next one (per column tile)
-  float ca[2], can[2];
+  bf16x8 af[2][8];   // activation fragments, double buffered over k-steps
+  bf16x8 bq[2][NT];  // weight fragments [kk & 1][j]
+  u32x4 cq[NT], cqn[NT];  // codes of this slice and of the next one (per column tile)
+  float ca[NT], can[NT];
 
-  auto read_codes = [&](u32x4 (&q)[2], float (&a)[2], int st) {
+  auto read_codes = [&](u32x4 (&q)[NT], float (&a)[NT], int st) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NT; ++j) {
       q[j] = *reinterpret_cast<const u32x4*>(sC[st] + sc0 + j * 1024);
       a[j] = sM[st][sm0 + j * 32];
     }
   };
 
-  // One k-step as 16 MFMA slots (row tile s/2, column tile s%2).  Between
-  // them, in a fixed order (sched_barrier after every slot): the next
-  // k-step's eight activation fragments and the eight level-pair reads of
-  // its two weight tiles (slots 0-7), then the products and bf16 packing
-  // (slots 8-15, when the reads have long returned).
+  // One k-step as 8 NT MFMA slots (row tile s / NT, column tile s % NT).
+  // Between them, in a fixed order (sched_barrier after every slot): the next
+  // k-step's eight activation fragments (slots 0-7) and the 4 NT level-pair
+  // reads of its weight tiles (slots 0 .. 4 NT - 1), then the products and
+  // bf16 packing (slots 4 NT .. 8 NT - 1, when the reads have long returned).
   // extra(s) adds per-slot work (the direct loads of the last k-step).
-  auto kstep = [&](auto kk_, const uint8_t* an, const u32x4 (&q)[2], const float (&a)[2],
+  auto kstep = [&](auto kk_, const uint8_t* an, const u32x4 (&q)[NT], const float (&a)[NT],
                    int kn, auto extra) {
     constexpr int F = decltype(kk_)::value & 1;
-    float lvv[2][8];
-    u32x4 r[2];
+    float lvv[NT][8];
+    u32x4 r[NT];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      acc[s >> 1][s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          bq[F][s & 1], af[F][s >> 1], acc[s >> 1][s & 1], 0, 0, 0);
+    for (int s = 0; s < NS; ++s) {
+      acc[s / NT][s % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          bq[F][s % NT], af[F][s / NT], acc[s / NT][s % NT], 0, 0, 0);
       if (s < 8) af[F ^ 1][s] = *reinterpret_cast<const bf16x8*>(an + s * 4096);
-      if (s < 8) {  // level pair ph of tile jt (byte ph of the code word)
+      if (s < 4 * NT) {  // level pair ph of tile jt (byte ph of the code word)
         const int jt = s >> 2, ph = s & 3;
         const float2 l = pair(pair_off(q[jt][kn], ph));
         lvv[jt][2 * ph] = l.x;
         lvv[jt][2 * ph + 1] = l.y;
       } else {
-        const int jt = (s - 8) >> 2, pp = (s - 8) & 3;
+        const int jt = (s - 4 * NT) >> 2, pp = (s - 4 * NT) & 3;
         r[jt][pp] = pack_bf16x2(lvv[jt][2 * pp] * a[jt], lvv[jt][2 * pp + 1] * a[jt]);
         if (pp == 3) bq[F ^ 1][jt] = __builtin_bit_cast(bf16x8, r[jt]);
       }
@@ -229,7 +245,7 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) af[0][i] = *reinterpret_cast<const bf16x8*>(sa + i * 4096);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bq[0][j] = dequant8(cq[j][0], ca[j], pair);
+      for (int j = 0; j < NT; ++j) bq[0][j] = dequant8(cq[j][0], ca[j], pair);
     }
     // Slice t (u = t - it0) sits in stage u % 3.  Each wave's codes and
     // absmax are the rows it loaded itself, so after waiting for its own
@@ -245,12 +261,12 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
       kstep(std::integral_constant<int, 1>{}, sA[st] + (sa0 ^ 32), cq, ca, 2, none);
       LSN_WAIT_VM(GROUP);
       kstep(std::integral_constant<int, 2>{}, sA[st] + (sa0 ^ 48), cq, ca, 3,
-            [&](int s) { if (s == 8) read_codes(cqn, can, st1); });
+            [&](int s) { if (s == 4 * NT) read_codes(cqn, can, st1); });
       __syncthreads();  // (its fence waits lgkmcnt(0): this wave's reads of stage st are done)
       const uint8_t* a_next = gA + min(t + 3, it1 - 1) * (FK * 2);
       const uint8_t* c_next = gC + min(t + 3, it1 - 1) * (FK / 2);
       const uint32_t la = lds_addr(sA[st]) + w * 8 * 1024;
-      const uint32_t lc = lds_addr(sC[st]) + w * 2 * 1024;
+      const uint32_t lc = lds_addr(sC[st]) + w * NT * 1024;
       const uint32_t lm = lds_addr(&sM[st][w * 64]);
       const uint8_t* m_next = gM + min(t + 3, it1 - 1) * 4;
       kstep(std::integral_constant<int, 3>{}, sA[st1] + sa0, cqn, can, 0, [&](int s) {
@@ -266,18 +282,21 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
         if (s == 5) dma16_at<1024>(a_next, offA_o[5]);
         if (s == 6) dma16_at<2048>(a_next, offA_o[6]);
         if (s == 7) dma16_at<3072>(a_next, offA_o[7]);
-        if (s == 8) {
+        // codes and absmax: in slots 8-10 of a 16-slot k-step, after the
+        // last activation load in an 8-slot one
+        if (s == (NT == 2 ? 8 : 7)) {
           set_m0(lc);
           dma16_at<0>(c_next, offC_o[0]);
         }
-        if (s == 9) dma16_at<1024>(c_next, offC_o[1]);
-        if (s == 10) {
+        if constexpr (NT == 2)
+          if (s == 9) dma16_at<1024>(c_next, offC_o[NT - 1]);
+        if (s == (NT == 2 ? 10 : 7)) {
           set_m0(lm);
           dma4_at<0>(m_next, offM);
         }
       });
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NT; ++j) {
         cq[j] = cqn[j];
         ca[j] = can[j];
       }
@@ -290,21 +309,21 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   const int lk = hh * 8;
   if (p.kext > 0 && blockIdx.y == 0) {
     for (int e0 = 0; e0 < p.kext; e0 += 16) {
-      bf16x8 af[8], bfr[2];
+      bf16x8 af[8], bfr[NT];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int m = min(m0 + i * 32 + lr, p.M - 1);
         af[i] = *reinterpret_cast<const bf16x8*>(p.Aext + (int64_t)m * p.ldae + e0 + lk);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = min(n0 + w * 64 + j * 32 + lr, p.N - 1);
+      for (int j = 0; j < NT; ++j) {
+        const int n = min(n0 + w * 32 * NT + j * 32 + lr, p.N - 1);
         bfr[j] = *reinterpret_cast<const bf16x8*>(p.Bext + (int64_t)n * p.ldbe + e0 + lk);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
   }
@@ -313,7 +332,8 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   // The MFMAs take the weights as their first operand, so tile (i, j) holds
   // y^T: lane (lr, hh) has output row m = m0 + 32i + lr and the columns
   // n = n0 + 64w + 32j + 8g + 4hh + t in acc[i][j][4g + t], i.e. four
-  // consecutive columns per 16-byte store.  Fully unrolled for the kernel's
+  // consecutive columns per 16-byte store (n = n0 + 32 NT w + ... in
+  // general).  Fully unrolled for the kernel's
   // output form (MODE -1: raw split-k partial sum).  The output and residual
   // pointers are restrict-qualified: a lane's only same-address pair is one
   // group's own load and store, so this also holds in place (C == R).
@@ -325,7 +345,7 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
     const int64_t ld = MODE < 0 ? (int64_t)p.N : p.ldc;
     const float* const src = MODE == C_F32_RES ? p.R : out;
     const int64_t lds = MODE == C_F32_RES ? p.ldr : ld;
-    const int nl = n0 + w * 64 + hh * 4;  // this lane's first column (t = 0, g = 0, j = 0)
+    const int nl = n0 + w * 32 * NT + hh * 4;  // this lane's first column (t = 0, g = 0, j = 0)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int m = m0 + i * 32 + lr;
@@ -334,7 +354,7 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
       uint16_t* __restrict__ brow = reinterpret_cast<uint16_t*>(p.C) + (int64_t)m * ld + nl;
       const float* __restrict__ srow = src + (int64_t)m * lds + nl;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int c = j * 32 + g * 8;  // column offset of this group
@@ -377,31 +397,78 @@ bool nf4f_eligible(const GemmParams& p, int batch) {
 }
 
 // One workgroup per CU (512 registers per lane): the k range is split
-// so that at most 256 workgroups run, each with at least four slices.
+// so that at most 256 workgroups run, each with at least four slices.  This
+// is the split of the 256 x 256 tile (both NF4 kernels use it).
+static int split_for(int64_t tiles, int K);
 int nf4f_split(int M, int N, int K) {
-  const int64_t tiles = (int64_t)((M + FM - 1) / FM) * ((N + FN - 1) / FN);
+  return split_for((int64_t)((M + FM - 1) / FM) * ((N + 255) / 256), K);
+}
+
+// The forward kernel's tile and split: the tile width (256 or 128 columns)
+// and split (1..8, at least four slices per workgroup) with the lowest
+// modelled time
+//   rounds of 256 workgroups x slices per workgroup x time per slice
+//   + split-k partial sums: written once, read and added once, the sum
+//     written once ((2 split + 1) M N 4 bytes),
+// with times measured on MI355X at one workgroup per CU: 1.70 us per slice
+// of a 256 x 256 tile, 1.09 us of a 256 x 128 tile, 0.25 us per MB of
+// partial-sum traffic.  (512 tokens: 4096 -> 4096 ran 45 us on the wide tile
+// split 8, 36 us on the narrow one split 4; 4096 -> 14336 81 us split 2
+// against 71 us unsplit; 1024 tokens, 14336 -> 4096: 129 us wide, 135 us
+// narrow.)
+static int split_for(int64_t tiles, int K) {
   if (tiles >= 128) return 1;
-  int sp = (int)std::min<int64_t>(8, 256 / tiles);
+  int sp = (int)std::min<int64_t>(8, std::max<int64_t>(1, 256 / tiles));
   sp = std::min(sp, std::max(1, K / FK / 4));
   return std::max(sp, 1);
 }
 
-hipError_t nf4f_launch(GemmParams p, hipStream_t s) {
-  p.ksplit = nf4f_split(p.M, p.N, p.K);
-  p.pstride = split_stride(p.M, p.N);
-  if (p.ksplit > 1 && (!p.part || p.part_floats < p.ksplit * p.pstride)) p.ksplit = 1;
-  const int tiles = ((p.M + FM - 1) / FM) * ((p.N + FN - 1) / FN);
+static double plan_cost(int M, int N, int K, int nt, int split) {
+  const int64_t tiles = (int64_t)((M + FM - 1) / FM) * ((N + 128 * nt - 1) / (128 * nt));
+  const double rounds = (double)((tiles * split + 255) / 256);
+  const double slices = (double)((K / FK + split - 1) / split);
+  double us = rounds * slices * (nt == 2 ? 1.70 : 1.09);
+  if (split > 1) us += (2.0 * split + 1.0) * (double)M * N * 4.0 * 0.25e-6;
+  return us;
+}
+
+Nf4fPlan nf4f_plan(int M, int N, int K) {
+  Nf4fPlan best{2, 1};
+  double cost = plan_cost(M, N, K, 2, 1);
+  for (int nt = 2; nt >= 1; --nt)
+    for (int sp = 1; sp <= 8 && (sp == 1 || K / FK / sp >= 4); ++sp) {
+      const double c = plan_cost(M, N, K, nt, sp);
+      if (c < cost) {
+        cost = c;
+        best = {nt, sp};
+      }
+    }
+  return best;
+}
+
+template <int NT>
+static void nf4f_launch_t(const GemmParams& p, hipStream_t s) {
+  const int tiles = ((p.M + FM - 1) / FM) * ((p.N + Shape<NT>::FN - 1) / Shape<NT>::FN);
   const dim3 grid(tiles, p.ksplit, 1);
   if (p.ksplit > 1)
-    hipExtLaunchKernelGGL(nf4f_kernel<-1>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+    hipExtLaunchKernelGGL((nf4f_kernel<-1, NT>), grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
   else if (p.cmode == C_F32)
-    hipExtLaunchKernelGGL(nf4f_kernel<C_F32>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+    hipExtLaunchKernelGGL((nf4f_kernel<C_F32, NT>), grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
   else if (p.cmode == C_F32_ACC)
-    hipExtLaunchKernelGGL(nf4f_kernel<C_F32_ACC>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+    hipExtLaunchKernelGGL((nf4f_kernel<C_F32_ACC, NT>), grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
   else if (p.cmode == C_F32_RES)
-    hipExtLaunchKernelGGL(nf4f_kernel<C_F32_RES>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+    hipExtLaunchKernelGGL((nf4f_kernel<C_F32_RES, NT>), grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
   else
-    hipExtLaunchKernelGGL(nf4f_kernel<C_BF16>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+    hipExtLaunchKernelGGL((nf4f_kernel<C_BF16, NT>), grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+}
+
+hipError_t nf4f_launch(GemmParams p, hipStream_t s) {
+  const Nf4fPlan plan = nf4f_plan(p.M, p.N, p.K);
+  p.ksplit = plan.split;
+  p.pstride = split_stride(p.M, p.N);
+  if (p.ksplit > 1 && (!p.part || p.part_floats < p.ksplit * p.pstride)) p.ksplit = 1;
+  if (plan.nt == 2) nf4f_launch_t<2>(p, s);
+  else nf4f_launch_t<1>(p, s);
   if (p.ksplit > 1) gemm_reduce_launch(p, s);
   return hipGetLastError();
 }
