@@ -149,6 +149,24 @@ lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t
                               int32_t r, float s, const uint16_t* dY, float* dX, float* dA,
                               float* dB, void* scratch, uint64_t scratch_bytes, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward projection as lsn_nf4_linear_fwd, same arguments without the
+ * scratch, and the same bits (the same kernels and split-k).  Its scratch
+ * is a fixed 64 MiB device array inside the library (allocated by the HIP
+ * runtime with the library's code on each device it runs on, held until the
+ * process ends); the call allocates nothing.  A shape whose scratch (t and
+ * the bf16 adapter operands, the low-rank product's partial sums, and the
+ * NF4 GEMM's split-k partial sums: split x (M x N + 1024) fp32, split up to
+ * 8 when M x N is small) exceeds 64 MiB returns LSN_ERR_INVALID with the
+ * bytes it needs.  Every call on a device shares that device's array: calls
+ * that overlap on one device (two streams, two threads) race and corrupt
+ * each other's results; calls on one stream are ordered and safe. */
+lsn_status lsn_nf4_linear_fwd_noalloc(const uint8_t* codes, const float* absmax, int32_t M,
+                                      int32_t K, int32_t N, const uint16_t* X, const float* A,
+                                      const float* B, int32_t r, float s, float* Y,
+                                      void* hip_stream);
+
 /* ---------------------------------------------------------------------------
  * Context lifecycle.
  * ------------------------------------------------------------------------- */

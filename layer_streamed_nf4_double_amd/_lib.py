@@ -63,6 +63,7 @@ _SIGS = {
     "lsn_nf4_linear_fwd": [_P, _P, _I32, _I32, _I32, _P, _P, _P, _I32, _F, _P, _P, _U64, _P],
     "lsn_nf4_linear_bwd": [_P, _P, _I32, _I32, _I32, _P, _P, _P, _I32, _F, _P, _P, _P, _P, _P,
                            _U64, _P],
+    "lsn_nf4_linear_fwd_noalloc": [_P, _P, _I32, _I32, _I32, _P, _P, _P, _I32, _F, _P, _P],
     "lsn_workspace_bytes": [_CFG, ctypes.POINTER(_U64)],
     "lsn_config_record_bytes": [_CFG, ctypes.POINTER(_U64)],
     "lsn_create": [_CFG, _P, _U64, _P, ctypes.POINTER(_P)],
@@ -170,6 +171,12 @@ def lsn_nf4_linear_fwd(codes, absmax, M, K, N, X, A, B, r, s, Y, scratch, scratc
     _check(_lib.lsn_nf4_linear_fwd(_ptr(codes), _ptr(absmax), M, K, N, _ptr(X), _ptr(A), _ptr(B),
                                    r, s, _ptr(Y), _ptr(scratch), scratch_bytes, _ptr(stream)),
            what="lsn_nf4_linear_fwd")
+
+
+def lsn_nf4_linear_fwd_noalloc(codes, absmax, M, K, N, X, A, B, r, s, Y, stream=0):
+    _check(_lib.lsn_nf4_linear_fwd_noalloc(_ptr(codes), _ptr(absmax), M, K, N, _ptr(X), _ptr(A),
+                                           _ptr(B), r, s, _ptr(Y), _ptr(stream)),
+           what="lsn_nf4_linear_fwd_noalloc")
 
 
 def lsn_nf4_linear_bwd(codes, absmax, M, K, N, X, A, B, r, s, dY, dX, dA, dB, scratch,

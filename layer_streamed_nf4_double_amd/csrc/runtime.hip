@@ -1203,6 +1203,77 @@ lsn_status lsn_nf4_linear_fwd(const uint8_t* codes, const float* absmax, int32_t
                          "lsn_nf4_linear_fwd");
 }
 
+// ---------------------------------------------------------------------------
+// The same forward projection for callers that cannot allocate: its scratch
+// is this file-scope device array.  Host code never uses the array's name as
+// an address (on the host it names a stand-in, not device memory): each
+// device's address comes from hipGetSymbolAddress, taken once per device on
+// the first call there with that device current, and only that address is
+// passed to kernels.
+// ---------------------------------------------------------------------------
+constexpr uint64_t NOALLOC_SCRATCH_BYTES = 64ull << 20;
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+}  // namespace
+
+// The forward's share of the stateless scratch: t, aext [M, 16], bext
+// [N, 16], the low-rank product's split partials and the NF4 GEMM's split-k
+// partials of this shape only (the same split the scratch-taking call uses).
+static LinScratch lin_scratch_fwd(char* base, int M, int K, int N) {
+  LinScratch L;
+  Carver cv;
+  auto P = [&](uint64_t b) -> char* { const uint64_t o = cv.take(b); return base ? base + o : nullptr; };
+  L.lpf = lora_mm_partial_floats(M, K);
+  L.gpf = gemm_partial_floats(M, N, K, 1, 1);
+  L.t = (float*)P((uint64_t)M * 16 * 4);
+  L.aext = (uint16_t*)P((uint64_t)M * 16 * 2);
+  L.bext = (uint16_t*)P((uint64_t)N * 16 * 2);
+  L.lpart = (float*)P((uint64_t)std::max<int64_t>(L.lpf, 1) * 4);
+  L.gpart = (float*)P((uint64_t)std::max<int64_t>(L.gpf, 1) * 4);
+  L.bytes = align_up(cv.off, 256);
+  return L;
+}
+
+lsn_status lsn_nf4_linear_fwd_noalloc(const uint8_t* codes, const float* absmax, int32_t M,
+                                      int32_t K, int32_t N, const uint16_t* X, const float* A,
+                                      const float* B, int32_t r, float s, float* Y,
+                                      void* hip_stream) {
+  if (!codes || !absmax || !X || !Y || M < 0 || K <= 0 || N <= 0 || K % 16 || N % 8 || r < 0 ||
+      r > 16 || (r > 0 && (!A || !B)))
+    return fail0(LSN_ERR_INVALID, "lsn_nf4_linear_fwd_noalloc: bad arguments");
+  const uint64_t need = lin_scratch_fwd(nullptr, M, K, N).bytes;
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail0(LSN_ERR_INVALID,
+                 "lsn_nf4_linear_fwd_noalloc: %d x %d -> %d needs %llu bytes of scratch, more "
+                 "than the %llu of the fixed device array",
+                 M, K, N, (unsigned long long)need, (unsigned long long)NOALLOC_SCRATCH_BYTES);
+  if (M == 0) return LSN_OK;
+  (void)hipGetLastError();  // a status left by the caller's HIP calls is not ours
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+    return fail0(LSN_ERR_HIP, "lsn_nf4_linear_fwd_noalloc: no usable current device");
+  char* base;
+  {
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* ptr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !ptr)
+        return fail0(LSN_ERR_HIP, "lsn_nf4_linear_fwd_noalloc: scratch address: %s",
+                     hipGetErrorString(e));
+      g_scratch_ptr[dev] = (char*)ptr;
+    }
+    base = g_scratch_ptr[dev];
+  }
+  const LinScratch L = lin_scratch_fwd(base, M, K, N);
+  return linear_fwd_core(codes, absmax, M, K, N, X, A, B, r, s, Y, L, (hipStream_t)hip_stream,
+                         "lsn_nf4_linear_fwd_noalloc");
+}
+
 lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t M, int32_t K,
                               int32_t N, const uint16_t* X, const float* A, const float* B,
                               int32_t r, float s, const uint16_t* dY, float* dX, float* dA,
