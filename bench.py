@@ -41,10 +41,16 @@ def parse():
     ap.add_argument("--dpo-steps", type=int, default=5)
     ap.add_argument("--file-steps", type=int, default=2,
                     help="timed SFT steps with the base streamed from a store file (0: skip)")
+    ap.add_argument("--second-workload", default="qwen2.5-3b-shaped",
+                    help="a second streamed SFT + DPO leg ('' or 'none': skip)")
+    ap.add_argument("--second-steps", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the projection, dequant and resident measurements")
     ap.add_argument("--link-mb", type=int, default=256)
+    ap.add_argument("--projection-only", action="store_true",
+                    help="only time the single projection and the standalone dequantization "
+                         "(for counter profiles of those kernels)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run device-to-device copies of this size (counter calibration)")
     return ap.parse_args()
@@ -117,13 +123,13 @@ def quantized_layers(w):
 
 
 def build_model(w, mode, max_tokens, max_seq_len, layers, head, store_path=None,
-                head_on_host=False):
+                head_on_host=False, n_slots=0):
     import numpy as np
 
     import synth
     from layer_streamed_nf4_double_amd.trainer import LayerStreamedLoRA
     m = LayerStreamedLoRA(w, mode, max_tokens=max_tokens, max_seq_len=max_seq_len,
-                          store_path=store_path, head_on_host=head_on_host)
+                          store_path=store_path, head_on_host=head_on_host, n_slots=n_slots)
     for layer, codes, absmax, g1, g2 in layers:
         m.load_layer(layer, codes, absmax, g1, g2)
     for layer in range(w["n_layers"]):
@@ -260,6 +266,88 @@ def head_on_host_leg(torch, L, w, S, layers, head, tok, tgt, steps, link_best):
     log(f"[bench] head on host: {hdt * 1e3:.1f} ms/step, {S / hdt:.1f} tok/s, "
         f"peak {peak / 1e9:.2f} GB, {gbps:.1f} GB/s")
     return out
+
+
+def algorithmic_bytes(w, rec_bytes, dpo=False):
+    """Host-link bytes of one step as the method defines them (every decoder
+    record streamed per pass, the LM head table streamed once per head pass):
+    SFT 2 L records + 1 W_lm; DPO with a separate reference forward 3 L
+    records + 2 W_lm."""
+    wlm = w["vocab"] * w["hidden"] * 2
+    L = w["n_layers"]
+    return (3 * L * rec_bytes + 2 * wlm) if dpo else (2 * L * rec_bytes + wlm)
+
+
+def sft_leg(torch, w, layers, head, tok, tgt, steps, warmup, n_slots=0, mode="stream_host"):
+    """Streamed (or resident) SFT steps: ms/step, tokens/s, record loads and
+    host->device bytes per step, peak device memory, final loss."""
+    S = w["seq_len"]
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    m = build_model(w, mode, S, S, layers, head, n_slots=n_slots)
+    for _ in range(warmup):
+        m.sft_step(tok, tgt, 1, S, 1e-4)
+    m.sync()
+    l0, b0, _ = m.stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        m.sft_step(tok, tgt, 1, S, 1e-4)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    l1, b1, _ = m.stats()
+    out = {"tokens_per_s": round(S / dt, 2), "ms_per_step": round(dt * 1e3, 2), "steps": steps,
+           "peak_vram_bytes": int(torch.cuda.max_memory_allocated()),
+           "layer_loads_per_step": (l1 - l0) / steps, "h2d_bytes_per_step": int((b1 - b0) / steps),
+           "loss": float(m.loss[0].item())}
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    return out, dt
+
+
+def dpo_leg(torch, w, layers, head, steps, warmup, sft_peak, sft_loads, link_best, rec_bytes):
+    """Streamed DPO steps on one preference pair (fused reference pass)."""
+    import numpy as np
+
+    import synth
+    from layer_streamed_nf4_double_amd.trainer import device_batch, sft_targets
+    S = w["seq_len"]
+    ch, rj = synth.dpo_pair(w)
+    dtok = np.stack([ch, rj])
+    d_tok, d_tgt = device_batch(dtok, sft_targets(dtok), w["vocab"])
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    md = build_model(w, "stream_host", 2 * S, S, layers, head)
+    P, beta = synth.dpo_prompt_len(w), synth.DPO_PAIR["beta"]
+    for _ in range(max(1, warmup)):
+        md.dpo_step(d_tok, d_tgt, S, P, beta, 1e-4)
+    md.sync()
+    l0, b0, _ = md.stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        md.dpo_step(d_tok, d_tgt, S, P, beta, 1e-4)
+    torch.cuda.synchronize()
+    ddt = (time.perf_counter() - t0) / steps
+    l1, b1, _ = md.stats()
+    dpeak = torch.cuda.max_memory_allocated()
+    out = md.loss[:2].cpu().numpy()
+    md.close()
+    del md
+    torch.cuda.empty_cache()
+    alg = algorithmic_bytes(w, rec_bytes, dpo=True)
+    return {"tokens_per_s": round(2 * S / ddt, 2), "ms_per_step": round(ddt * 1e3, 2),
+            "reference_pass": "fused with the policy forward (one record copy per layer)",
+            "tokens_per_step": 2 * S, "loss": float(out[0]),
+            "layer_loads_per_step": (l1 - l0) / steps,
+            "layer_loads_ratio_vs_sft": round((l1 - l0) / steps / max(sft_loads, 1e-9), 3),
+            "h2d_GBps": round((b1 - b0) / steps / ddt / 1e9, 2),
+            "link_frac": round((b1 - b0) / steps / ddt / 1e9 / link_best, 4),
+            "algorithmic_bytes_per_step": int(alg),
+            "link_frac_algorithmic": round(alg / ddt / 1e9 / link_best, 4),
+            "peak_vram_bytes": int(dpeak),
+            "peak_vram_ratio_vs_sft": round(dpeak / sft_peak, 3)}
 
 
 def link_bandwidth(torch, mb, reps=20):
@@ -439,11 +527,58 @@ def cpu_baseline(w, tokens):
     t3 = time.perf_counter()
     step = w["n_layers"] * ((t1 - t0) + (t2 - t1)) + (t3 - t2)
     T = tokens.size
-    return {"value": T / step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"float32 numpy oracle, one {w['hidden']}-wide decoder layer "
-                       f"(dequantize+forward {t1 - t0:.2f} s; dequantize+recompute+backward "
-                       f"{t2 - t1:.2f} s) and the LM head fwd+bwd ({t3 - t2:.2f} s) at "
-                       f"{T} tokens, scaled to {w['n_layers']} layers: {step:.1f} s/step")}
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+    except Exception:
+        pass
+    out = {"value": T / step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "extrapolated": True, "blas": blas,
+           "sample": (f"float32 numpy oracle, one {w['hidden']}-wide decoder layer "
+                      f"(dequantize+forward {t1 - t0:.2f} s; dequantize+recompute+backward "
+                      f"{t2 - t1:.2f} s) and the LM head fwd+bwd ({t3 - t2:.2f} s) at "
+                      f"{T} tokens; the full step is extrapolated as {w['n_layers']} x the "
+                      f"layer + the head: {step:.1f} s/step")}
+    out["projection"] = cpu_projection(threads)
+    return out
+
+
+def cpu_projection(threads):
+    """The oracle's forward NF4 projection with a rank-16 adapter at
+    512 x 4096 -> 14336 (dequantize W, then x W + s (x A) B in float32), on
+    all BLAS threads and on one."""
+    import numpy as np
+
+    import synth
+    from oracle import model as om
+    from oracle import nf4 as onf4
+    p = synth.PROJECTION
+    M, K, N, r, sc, wid = p["M"], p["K"], p["N"], p["r"], p["scale"], p["wid"]
+    c, a = onf4.quantize(synth.normal((N, K), wid, 0, 0))
+    x = synth.bf16_to_f32(synth.bf16_bits(synth.normal((M, K), wid, 0, synth.TID_X, std=1.0)))
+    A = synth.normal((K, r), wid, 0, 10)
+    B = synth.normal((r, N), wid, 0, 11)
+
+    def run():
+        t0 = time.perf_counter()
+        Wt = onf4.dequantize(c, a, N * K).reshape(N, K)
+        om.lora_linear(x, Wt, A, B, sc)
+        return time.perf_counter() - t0
+
+    res = {"shape": f"[{M},{K}] x NF4 [{K},{N}] + rank-{r} adapter, float32",
+           "flops": 2.0 * M * N * K}
+    res["seconds_all_threads"] = round(min(run() for _ in range(2)), 3)
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            res["seconds_one_thread"] = round(run(), 3)
+    except Exception:
+        res["seconds_one_thread"] = None
+    res["threads"] = int(threads)
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -456,12 +591,16 @@ def main():
     if args.copy_probe_mb:
         copy_probe(args.copy_probe_mb)
         return
+    if args.projection_only:
+        import torch
+        print(json.dumps(projection_kernels(torch, reps=5)), flush=True)
+        return
     import numpy as np
     import torch
 
     import synth
     from layer_streamed_nf4_double_amd import _lib as L
-    from layer_streamed_nf4_double_amd.trainer import sft_targets
+    from layer_streamed_nf4_double_amd.trainer import device_batch, sft_targets
 
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[args.workload]
@@ -520,54 +659,43 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(args.workload, args.mode),
-                "kernel": "nf4f_kernel (fused NF4-dequant MFMA GEMM, 256x256 tile)",
+                "kernel": "nf4f_kernel (fused NF4-dequant MFMA GEMM, 256x256 or 256x128 tile)",
                 "launches": int(n_gemm), "avg_us": round(ms / max(n_gemm, 1) * 1e3, 2),
                 "flop_per_launch": flops / max(n_gemm, 1)}
     copy_gbps = cp_bytes / (cp_ms / 1e3) / 1e9 if cp_ms > 0 else 0.0
+    alg = algorithmic_bytes(w, rec_bytes)
     link = {"bound": "host-link", "measured_peak_GBps": round(link_best, 2),
             "measured_median_GBps": round(link_med, 2),
             "h2d_bytes_per_step": int(h2d_per_step), "record_bytes": int(rec_bytes),
             "layer_loads_per_step": loads_per_step,
             "achieved_GBps": round(h2d_per_step / dt / 1e9, 2),
             "frac": round(h2d_per_step / dt / 1e9 / link_best, 4),
+            "algorithmic_bytes_per_step": int(alg),
+            "frac_algorithmic": round(alg / dt / 1e9 / link_best, 4),
+            "note": "frac: bytes actually copied (2L - 4 records; the embedding and LM head stay "
+                    "in device memory). frac_algorithmic: the method's bytes (2L records + one "
+                    "W_lm pass) over the same step time; above 1 because the head stays "
+                    "resident and 4 records are reused",
             "copy_engine_GBps_while_copying": round(copy_gbps, 2)}
 
     # ---- DPO on the same streamed base ----
     dpo = None
     if args.dpo_steps > 0:
-        ch, rj = synth.dpo_pair(w)
-        dtok = np.stack([ch, rj])
-        dt_tok = torch.from_numpy(dtok.reshape(-1).astype(np.int32)).cuda()
-        dt_tgt = torch.from_numpy(sft_targets(dtok)).cuda()
-        torch.cuda.reset_peak_memory_stats()
-        md = build_model(w, args.mode, 2 * S, S, layers, head)
-        P, beta = synth.dpo_prompt_len(w), synth.DPO_PAIR["beta"]
-        for _ in range(max(1, args.warmup)):
-            md.dpo_step(dt_tok, dt_tgt, S, P, beta, 1e-4)
-        md.sync()
-        l0, b0, _ = md.stats()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.dpo_steps):
-            md.dpo_step(dt_tok, dt_tgt, S, P, beta, 1e-4)
-        torch.cuda.synchronize()
-        ddt = (time.perf_counter() - t0) / args.dpo_steps
-        l1, b1, _ = md.stats()
-        dpeak = torch.cuda.max_memory_allocated()
-        out = md.loss[:2].cpu().numpy()
-        md.close()
-        del md
-        torch.cuda.empty_cache()
-        dpo = {"tokens_per_s": round(2 * S / ddt, 2), "ms_per_step": round(ddt * 1e3, 2),
-               "reference_pass": "fused with the policy forward (one record copy per layer)",
-               "tokens_per_step": 2 * S, "loss": float(out[0]),
-               "layer_loads_per_step": (l1 - l0) / args.dpo_steps,
-               "layer_loads_ratio_vs_sft": round((l1 - l0) / args.dpo_steps / max(loads_per_step, 1e-9), 3),
-               "h2d_GBps": round((b1 - b0) / args.dpo_steps / ddt / 1e9, 2),
-               "link_frac": round((b1 - b0) / args.dpo_steps / ddt / 1e9 / link_best, 4),
-               "peak_vram_bytes": int(dpeak),
-               "peak_vram_ratio_vs_sft": round(dpeak / peak, 3)}
-        log(f"[bench] DPO {ddt * 1e3:.1f} ms/step, {2 * S / ddt:.1f} tok/s, loss {out[0]:.4f}")
+        dpo = dpo_leg(torch, w, layers, head, args.dpo_steps, args.warmup, peak, loads_per_step,
+                      link_best, rec_bytes)
+        log(f"[bench] DPO {dpo['ms_per_step']:.1f} ms/step, {dpo['tokens_per_s']:.1f} tok/s, "
+            f"loss {dpo['loss']:.4f}")
+
+    # ---- three device slots (one more record resident: two fewer copies per step) ----
+    slots3 = None
+    if args.mode == "stream_host" and not args.no_extras:
+        slots3, _ = sft_leg(torch, w, layers, head, tok, tgt, max(1, args.steps // 2),
+                            args.warmup, n_slots=3)
+        slots3["n_slots"] = 3
+        slots3["link_frac"] = round(slots3["h2d_bytes_per_step"] / (slots3["ms_per_step"] / 1e3)
+                                    / 1e9 / link_best, 4)
+        log(f"[bench] 3 slots: {slots3['ms_per_step']:.1f} ms/step, "
+            f"{slots3['layer_loads_per_step']} loads/step, peak {slots3['peak_vram_bytes'] / 1e9:.2f} GB")
 
     # ---- the same step with the base resident on the device (peak VRAM side by side) ----
     resident = projection = file_src = head_host = None
@@ -602,6 +730,34 @@ def main():
         log(f"[bench] projection fwd {projection['fwd']['us']} us, bwd "
             f"{projection['bwd_dx_da_db']['us']} us, dequant {projection['dequant_bf16']['us']} us")
 
+    # ---- a second workload: streamed SFT and DPO at its own shape ----
+    second = None
+    if args.second_workload not in ("", "none") and args.second_workload != args.workload:
+        w2 = synth.WORKLOADS[args.second_workload]
+        log(f"[bench] second workload {args.second_workload}")
+        layers2 = list(quantized_layers(w2))
+        head2 = synth.head_tables(w2)
+        tokens2 = synth.sft_tokens(w2)
+        tok2, tgt2 = device_batch(tokens2, sft_targets(tokens2), w2["vocab"])
+        sft2, dt2 = sft_leg(torch, w2, layers2, head2, tok2, tgt2, args.second_steps,
+                            args.warmup)
+        from layer_streamed_nf4_double_amd.trainer import make_config
+        rec2 = L.lsn_config_record_bytes(make_config(w2, "stream_host"))
+        alg2 = algorithmic_bytes(w2, rec2)
+        sft2.update({"record_bytes": int(rec2),
+                     "link_frac": round(sft2["h2d_bytes_per_step"] / dt2 / 1e9 / link_best, 4),
+                     "algorithmic_bytes_per_step": int(alg2),
+                     "link_frac_algorithmic": round(alg2 / dt2 / 1e9 / link_best, 4)})
+        dpo2 = dpo_leg(torch, w2, layers2, head2, max(1, args.second_steps // 2), args.warmup,
+                       sft2["peak_vram_bytes"], sft2["layer_loads_per_step"], link_best, rec2)
+        second = {"workload": f"{args.second_workload} streamed LoRA-SFT step (seq "
+                              f"{w2['seq_len']}) and DPO step (2 x {w2['seq_len']})",
+                  "n_layers": w2["n_layers"], "hidden": w2["hidden"], "vocab": w2["vocab"],
+                  "tied": bool(w2["tied"]), "sft": sft2, "dpo": dpo2}
+        log(f"[bench] {args.second_workload}: SFT {sft2['tokens_per_s']} tok/s, DPO "
+            f"{dpo2['tokens_per_s']} tok/s")
+        del layers2
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle sample)")
@@ -618,13 +774,17 @@ def main():
                        "global_batch": 1, "seq_len": S, "lora": "r16 a32 q,v",
                        "base": "NF4 block-64, pinned host RAM" if args.mode == "stream_host"
                        else "NF4 block-64, device resident",
+                       "head": "embedding and LM head (bf16) resident in device memory; the "
+                               "decoder layers stream (head_on_host: the head_on_host leg)",
+                       "slots": 2,
                        "parallelism": "none (1 GPU)"},
             "peak_vram_bytes": int(peak), "loss": loss,
             "roofline": roofline, "link": link,
             "compute_utilization": {"flops_per_step": step_flops(w, S, 1),
                                     "frac": round(step_flops(w, S, 1) / dt / 1e12
                                                   / MFMA_BF16_PEAK_TFLOPS, 4)},
-            "dpo": dpo, "resident": resident, "head_on_host": head_host, "file_source": file_src,
+            "dpo": dpo, "slots3": slots3, "resident": resident, "head_on_host": head_host,
+            "file_source": file_src, "second_workload": second,
             "projection": projection,
             "env": environment(torch, w, rec_bytes), "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
