@@ -43,6 +43,10 @@ void sft_loss(const float* logp, const int32_t* tgt, int n, float* loss, float* 
 void pref_loss(int kind, const float* lp, const float* lr, int S, int P, float beta, float p2,
                float* out, float* dlogp, hipStream_t s);
 void sgd(float* p, const float* g, float lr, int64_t n, hipStream_t s);
+// out[(q S + i) ldo + kv d + j] = sum over the grp q heads of kv (head
+// order) of part[((q nq + h) S + i) d + j]; d % 4 == 0, 16-byte aligned rows
+void group_sum(const float* part, int n_seq, int nq, int grp, int S, int d, float* out,
+               int64_t ldo, hipStream_t s);
 // a kernel that waits `us` microseconds of the device wall clock (rate
 // wall_khz) on stream s, then exits
 void spin_us(uint32_t us, int wall_khz, hipStream_t s);

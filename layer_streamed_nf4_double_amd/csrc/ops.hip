@@ -414,6 +414,26 @@ __global__ void sgd_k(float* __restrict__ p, const float* __restrict__ g, float 
   if (i < n) p[i] -= lr * g[i];
 }
 
+// Grouped-query sum: out[(q * S + i) * ldo + kv * d + j] = sum over the grp
+// q heads h of kv, in head order, of part[((q * nq + h) * S + i) * d + j]
+// (q: sequence, i: position, j: feature; four features per thread).
+__global__ void group_sum4_k(const f32x4* __restrict__ part, int nq, int grp, int S, int d4,
+                             float* __restrict__ out, int64_t ldo, int64_t total4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total4) return;
+  const int nkv = nq / grp;
+  const int j4 = (int)(i % d4);
+  int64_t r = i / d4;
+  const int pos = (int)(r % S);
+  r /= S;
+  const int kv = (int)(r % nkv);
+  const int64_t q = r / nkv;
+  const f32x4* src = part + ((q * nq + (int64_t)kv * grp) * S + pos) * d4 + j4;
+  f32x4 acc = src[0];
+  for (int g = 1; g < grp; ++g) acc += src[(int64_t)g * S * d4];
+  *reinterpret_cast<f32x4*>(out + (q * S + pos) * ldo + ((int64_t)kv * d4 + j4) * 4) = acc;
+}
+
 // One lane waits `ticks` periods of the device's constant-rate wall clock,
 // then exits (a delay of bounded length on the stream it runs on).
 __global__ void spin_k(uint64_t ticks) {
@@ -830,6 +850,12 @@ void pref_loss(int kind, const float* lp, const float* lr, int S, int P, float b
 }
 void sgd(float* p, const float* g, float lr, int64_t n, hipStream_t s) {
   hipLaunchKernelGGL(sgd_k, dim3(nb(n, 256)), dim3(256), 0, s, p, g, lr, n);
+}
+void group_sum(const float* part, int n_seq, int nq, int grp, int S, int d, float* out,
+               int64_t ldo, hipStream_t s) {
+  const int64_t total4 = (int64_t)n_seq * (nq / grp) * S * (d / 4);
+  hipLaunchKernelGGL(group_sum4_k, dim3(nb(total4, 256)), dim3(256), 0, s,
+                     reinterpret_cast<const f32x4*>(part), nq, grp, S, d / 4, out, ldo, total4);
 }
 void spin_us(uint32_t us, int wall_khz, hipStream_t s) {
   const uint64_t ticks = (uint64_t)us * (uint64_t)wall_khz / 1000u;

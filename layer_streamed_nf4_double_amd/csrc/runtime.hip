@@ -140,7 +140,7 @@ struct lsn_ctx {
   // activation scratch (one layer at max_tokens)
   uint16_t *n1, *qkvb, *Pb, *O, *n2, *a, *dgu, *dO, *dqkvb, *aext, *bext, *nf, *dlog;
   float *rstd1, *qkv, *scores, *Pf, *h2, *rstd2, *gu, *da, *dguf, *dn, *dh2, *dqkv, *lt, *lu,
-      *rstdf, *logits, *run_m, *run_s, *tlogit, *lse, *dnf, *lpart, *gpart;
+      *rstdf, *logits, *run_m, *run_s, *tlogit, *lse, *dnf, *lpart, *gpart, *hpart;
   int64_t ext_rows = 0, lpart_floats = 0, gpart_floats = 0;
   int vchunk = 16384;  // vocabulary rows per LM-head GEMM (vchunk_for(max_tokens))
 
@@ -467,6 +467,7 @@ static uint64_t carve(lsn_ctx* c, char* base) {
   // bf16 q|k|v input gradient, and the bf16 copy of the fp32 output gradient
   // [T, hidden] that the dX GEMMs of down and o take: the larger of the two
   c->dqkvb = (uint16_t*)P(T * std::max<int64_t>(QKV, H) * 2);
+  c->hpart = (float*)P(T * QD * 4);  // per-q-head dV / dK before the group sum
   c->lt = (float*)P(NPROJ * T * 16 * 4);
   c->lpart_floats = 0;
   for (int p = 0; p < NPROJ; ++p)
@@ -1023,19 +1024,22 @@ static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, cons
     p.causal = CAUSAL_SKIP_UPPER;  // the softmax backward reads keys <= query only
     HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_K, Z));
   }
-  {  // dV[kv] = sum over its q heads of P^T dO
+  // dV[kv] = sum over its q heads of P_h^T dO_h: one product per q head
+  // (batch n_seq x nq, 4x the workgroups of a product per kv head), then
+  // the group sums in head order
+  {
     GemmParams p = base_params(c);
     p.M = S; p.N = d; p.K = S;
     p.A = c->Pb; p.lda = S;
     p.B = c->dO; p.ldb = QD;
-    p.zdiv = nkv; p.grpB = 1;
-    p.sA_o = (int64_t)nq * S * S; p.sA_i = (int64_t)grp * S * S; p.sA_seg = (int64_t)S * S;
-    p.sB_o = (int64_t)S * QD; p.sB_i = (int64_t)grp * d; p.sB_seg = d;
-    p.nseg = grp;
-    p.C = c->dqkv + QD + KVD; p.ldc = QKV;
-    p.sC_o = (int64_t)S * QKV; p.sC_i = d;
+    p.zdiv = nq; p.grpB = 1;
+    p.sA_o = (int64_t)nq * S * S; p.sA_i = (int64_t)S * S;
+    p.sB_o = (int64_t)S * QD; p.sB_i = d;
+    p.C = c->hpart; p.ldc = d;
+    p.sC_o = (int64_t)nq * S * d; p.sC_i = (int64_t)S * d;
     p.causal = CAUSAL_K_FROM_ROW;  // P^T is zero for queries < key
-    HIPCHK(c, cgemm(c, p, A_BF16_R, B_BF16_R, c->n_seq * nkv));
+    HIPCHK(c, cgemm(c, p, A_BF16_R, B_BF16_R, Z));
+    group_sum(c->hpart, c->n_seq, nq, grp, S, d, c->dqkv + QD + KVD, QKV, s);
   }
   softmax_bwd(c->Pf, c->scores, c->Pb, S, (int64_t)Z * S, s);  // dS (bf16) over Pb
   const float scale = 1.0f / sqrtf((float)d);
@@ -1053,20 +1057,20 @@ static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, cons
     p.causal = CAUSAL_K_TO_ROW;  // dS is zero for keys > query
     HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, Z));
   }
-  {  // dK[kv] = scale sum over its q heads of dS^T Q
+  {  // dK[kv] = scale sum over its q heads of dS_h^T Q_h, as dV
     GemmParams p = base_params(c);
     p.M = S; p.N = d; p.K = S;
     p.A = c->Pb; p.lda = S;
     p.B = c->qkvb; p.ldb = QKV;
-    p.zdiv = nkv; p.grpB = 1;
-    p.sA_o = (int64_t)nq * S * S; p.sA_i = (int64_t)grp * S * S; p.sA_seg = (int64_t)S * S;
-    p.sB_o = (int64_t)S * QKV; p.sB_i = (int64_t)grp * d; p.sB_seg = d;
-    p.nseg = grp;
-    p.C = c->dqkv + QD; p.ldc = QKV;
-    p.sC_o = (int64_t)S * QKV; p.sC_i = d;
+    p.zdiv = nq; p.grpB = 1;
+    p.sA_o = (int64_t)nq * S * S; p.sA_i = (int64_t)S * S;
+    p.sB_o = (int64_t)S * QKV; p.sB_i = d;
+    p.C = c->hpart; p.ldc = d;
+    p.sC_o = (int64_t)nq * S * d; p.sC_i = (int64_t)S * d;
     p.alpha = scale;
     p.causal = CAUSAL_K_FROM_ROW;  // dS^T is zero for queries < key
-    HIPCHK(c, cgemm(c, p, A_BF16_R, B_BF16_R, c->n_seq * nkv));
+    HIPCHK(c, cgemm(c, p, A_BF16_R, B_BF16_R, Z));
+    group_sum(c->hpart, c->n_seq, nq, grp, S, d, c->dqkv + QD, QKV, s);
   }
   rope_bwd(c->dqkv, c->dqkvb, T, S, nq, nkv, d, g.rope_theta, s);
   kext = lora_bwd_ext(c, layer, G_QKV, c->dqkv, QKV, c->n1, H, T);
