@@ -39,6 +39,7 @@
 #include <vector>
 
 #include "../../include/lsn.h"
+#include "attn.h"
 #include "gemm.h"
 #include "host_codec.h"
 #include "lora.h"
@@ -928,6 +929,9 @@ static hipError_t nf4_bwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const vo
 // ---------------------------------------------------------------------------
 // one decoder layer
 // ---------------------------------------------------------------------------
+// final_residual: the forward of a pass (down projection and residual into
+// out); otherwise the backward's recompute, which stops before down and also
+// keeps the attention probabilities the backward reads
 static lsn_status layer_forward(lsn_ctx* c, int layer, const uint8_t* rec, const float* h,
                                 float* out, bool final_residual) {
   const lsn_config& g = c->cfg;
@@ -943,34 +947,48 @@ static lsn_status layer_forward(lsn_ctx* c, int layer, const uint8_t* rec, const
   HIPCHK(c, nf4_fwd_gemm(c, rec, G_QKV, c->n1, T, kext, c->qkv, C_F32, nullptr));
   rope_fwd(c->qkv, c->qkvb, T, S, nq, nkv, d, g.rope_theta, s);
 
-  // attention: scores = q k^T / sqrt(d) per (sequence, head)
-  {
-    GemmParams p = base_params(c);
-    p.M = S; p.N = S; p.K = d;
-    p.A = c->qkvb; p.lda = QKV;
-    p.B = c->qkvb + QD; p.ldb = QKV;
-    p.zdiv = nq; p.grpB = grp;
-    p.sA_o = (int64_t)S * QKV; p.sA_i = d;
-    p.sB_o = (int64_t)S * QKV; p.sB_i = d;
-    p.C = c->scores; p.ldc = S;
-    p.sC_o = (int64_t)nq * S * S; p.sC_i = (int64_t)S * S;
-    p.alpha = 1.0f / sqrtf((float)d);
-    p.causal = CAUSAL_SKIP_UPPER;  // the softmax reads keys <= query only
-    HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_K, c->n_seq * nq));
-  }
-  softmax_causal(c->scores, c->Pf, c->Pb, S, (int64_t)c->n_seq * nq * S, s);
-  {  // O = P V
-    GemmParams p = base_params(c);
-    p.M = S; p.N = d; p.K = S;
-    p.A = c->Pb; p.lda = S;
-    p.B = c->qkvb + QD + KVD; p.ldb = QKV;
-    p.zdiv = nq; p.grpB = grp;
-    p.sA_o = (int64_t)nq * S * S; p.sA_i = (int64_t)S * S;
-    p.sB_o = (int64_t)S * QKV; p.sB_i = d;
-    p.C = c->O; p.ldc = QD; p.cmode = C_BF16;
-    p.sC_o = (int64_t)S * QD; p.sC_i = d;
-    p.causal = CAUSAL_K_TO_ROW;  // P is zero for keys > query
-    HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, c->n_seq * nq));
+  // attention: one fused kernel where the shape allows (S <= 512, d 64 or
+  // 128), else scores, softmax and P v as three launches
+  uint16_t* vT = reinterpret_cast<uint16_t*>(c->scores);  // free until the backward's dP
+  if (attn_fwd_ok(S, d, QKV, QD, c->qkvb, c->O, vT)) {
+    AttnFwdParams ap;
+    ap.qkv = c->qkvb; ap.ld = QKV; ap.vT = vT;
+    ap.O = c->O; ap.ldo = QD;
+    ap.Pf = final_residual ? nullptr : c->Pf;
+    ap.Pb = final_residual ? nullptr : c->Pb;
+    ap.S = S; ap.nq = nq; ap.nkv = nkv;
+    ap.alpha = 1.0f / sqrtf((float)d);
+    HIPCHK(c, attn_fwd(ap, c->n_seq, d, s));
+  } else {
+    // attention: scores = q k^T / sqrt(d) per (sequence, head)
+    {
+      GemmParams p = base_params(c);
+      p.M = S; p.N = S; p.K = d;
+      p.A = c->qkvb; p.lda = QKV;
+      p.B = c->qkvb + QD; p.ldb = QKV;
+      p.zdiv = nq; p.grpB = grp;
+      p.sA_o = (int64_t)S * QKV; p.sA_i = d;
+      p.sB_o = (int64_t)S * QKV; p.sB_i = d;
+      p.C = c->scores; p.ldc = S;
+      p.sC_o = (int64_t)nq * S * S; p.sC_i = (int64_t)S * S;
+      p.alpha = 1.0f / sqrtf((float)d);
+      p.causal = CAUSAL_SKIP_UPPER;  // the softmax reads keys <= query only
+      HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_K, c->n_seq * nq));
+    }
+    softmax_causal(c->scores, c->Pf, c->Pb, S, (int64_t)c->n_seq * nq * S, s);
+    {  // O = P V
+      GemmParams p = base_params(c);
+      p.M = S; p.N = d; p.K = S;
+      p.A = c->Pb; p.lda = S;
+      p.B = c->qkvb + QD + KVD; p.ldb = QKV;
+      p.zdiv = nq; p.grpB = grp;
+      p.sA_o = (int64_t)nq * S * S; p.sA_i = (int64_t)S * S;
+      p.sB_o = (int64_t)S * QKV; p.sB_i = d;
+      p.C = c->O; p.ldc = QD; p.cmode = C_BF16;
+      p.sC_o = (int64_t)S * QD; p.sC_i = d;
+      p.causal = CAUSAL_K_TO_ROW;  // P is zero for keys > query
+      HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, c->n_seq * nq));
+    }
   }
   kext = lora_fwd_ext(c, layer, G_O, c->O, QD, T);
   HIPCHK(c, nf4_fwd_gemm(c, rec, G_O, c->O, T, kext, c->h2, C_F32_RES, h));
