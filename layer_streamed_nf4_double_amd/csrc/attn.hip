@@ -2,7 +2,7 @@
 //
 //   S = alpha q k^T (keys <= query), P = softmax(S) over the row, O = P v
 //
-// One workgroup (four waves) per (sequence, q head, 64-query tile).  The
+// One workgroup (eight waves) per (sequence, q head, 64-query tile).  The
 // tile's scores for its keys 0 .. q0 + 63 live in LDS (fp32, at most 64 x 512:
 // 129 KiB), so the scores never round-trip through HBM; only O (bf16) and,
 // in the backward's recompute, the probabilities the backward reads (P in
@@ -11,14 +11,20 @@
 // Phase 1 (scores): MFMA v_mfma_f32_32x32x16_bf16 with the keys as the first
 // operand and the queries as the second, so a lane's accumulators are four
 // consecutive keys of one query row: one 16-byte LDS store each.  Wave w
-// takes the 32-key tiles j = w, w + 4, ... of the tile's causal extent.
-// Phase 2 (softmax): wave w owns rows 16 w .. 16 w + 15; per row the same
-// arithmetic as the two-pass softmax kernel (max and sum over keys <= query,
+// takes the 32-key tiles j = w, w + 8, ... of the tile's causal extent.
+// Phase 2 (softmax): 16 lanes per row, a wave takes four rows at a time; per
+// row the arithmetic of a two-pass softmax (max and sum over keys <= query,
 // one exp per element); P (bf16) overwrites the front half of the row.
-// Phase 3 (O^T = v^T P^T): the first operand is v^T, read from a transposed
-// copy vT [seq][kv head][d][S] (an MFMA operand needs 8 consecutive keys per
-// lane), the second is P from LDS; a lane's accumulators are four
-// consecutive head dimensions of one query: one 8-byte bf16 store each.
+// Phase 3 (O^T = v^T P^T): the first operand is v^T (an MFMA operand needs 8
+// consecutive keys per lane), the second is P from LDS; a lane's
+// accumulators are four consecutive head dimensions of one query: one 8-byte
+// bf16 store each.
+//
+// Operand layout.  A fragment of q, k or v^T is 64 lanes x 16 bytes taken
+// from 32 rows; read from the row-major q|k|v rows, every load instruction
+// would touch 32 rows.  attn_prep_k first writes fragment-ordered copies
+// (each fragment 1 KiB contiguous, lane-major), so every operand load of the
+// fused kernel is one contiguous 1 KiB per wave.
 //
 // Every output is written by one lane after a fixed-order reduction:
 // results are deterministic and the same with or without the P outputs.
@@ -30,12 +36,25 @@ namespace lsn {
 
 namespace {
 constexpr int QT = 64;          // queries per workgroup
+constexpr int NW = 8;           // waves per workgroup (two per SIMD)
 constexpr int SMAX = 512;       // longest sequence the LDS score tile holds
 constexpr int RS = SMAX + 4;    // LDS row stride (floats): rows 4 banks apart
+
+// reductions over the 16 lanes of a row group, fixed butterfly order
+LSN_DEV float row16_max(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+LSN_DEV float row16_sum(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_k(const AttnFwdParams p) {
+__global__ __launch_bounds__(64 * NW) void attn_fwd_k(const AttnFwdParams p) {
   constexpr int KS = D / 16;  // MFMA k-steps over the head dimension
   __shared__ __attribute__((aligned(16))) float sS[QT * RS];
 
@@ -46,32 +65,27 @@ __global__ __launch_bounds__(256) void attn_fwd_k(const AttnFwdParams p) {
   const int qt = blockIdx.x, z = blockIdx.y;
   const int seq = z / nq, h = z % nq, kvh = h / (nq / p.nkv);
   const int q0 = qt * QT, nk = q0 + QT;  // keys 0 .. nk - 1
-  const int64_t ld = p.ld;
-  const uint16_t* Q = p.qkv + ((int64_t)seq * S + q0) * ld + h * D;
-  const uint16_t* Kp = p.qkv + (int64_t)seq * S * ld + (int64_t)nq * D + kvh * D;
-
+  // fragment-ordered operands (attn_prep_k): 512 elements per fragment
+  const int nt32 = S / 32;
+  const uint16_t* Qf = p.frag + ((int64_t)(seq * nq + h) * nt32 + q0 / 32) * KS * 512 + lane * 8;
+  const uint16_t* Kf = p.frag + (int64_t)p.n_seq * S * nq * D +
+                       (int64_t)(seq * p.nkv + kvh) * nt32 * KS * 512 + lane * 8;
   // ---- phase 1: scores of the tile's 64 queries against keys < nk ----
+  // key tiles j = w, w + NW, ...: K fragments double buffered (ka: j, kb: j + NW)
+  const int nkt = nk / 32;
   {
-    bf16x8 qf[2][KS];
+    bf16x8 qf[2][KS], ka[KS], kb[KS];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
-        qf[i][kk] = *reinterpret_cast<const bf16x8*>(Q + (int64_t)(32 * i + lr) * ld + 16 * kk + 8 * hh);
-    const int nkt = nk / 32;
-    bf16x8 kf[SMAX / 128][KS];
+        qf[i][kk] = *reinterpret_cast<const bf16x8*>(Qf + (i * KS + kk) * 512);
+    auto load_k = [&](bf16x8 (&f)[KS], int j) {
 #pragma unroll
-    for (int jj = 0; jj < SMAX / 128; ++jj) {
-      const int j = w + 4 * jj;
-      if (j < nkt)
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-          kf[jj][kk] = *reinterpret_cast<const bf16x8*>(Kp + (int64_t)(32 * j + lr) * ld + 16 * kk + 8 * hh);
-    }
-#pragma unroll
-    for (int jj = 0; jj < SMAX / 128; ++jj) {
-      const int j = w + 4 * jj;
-      if (j >= nkt) continue;
+      for (int kk = 0; kk < KS; ++kk)
+        f[kk] = *reinterpret_cast<const bf16x8*>(Kf + (j * KS + kk) * 512);
+    };
+    auto scores = [&](const bf16x8 (&f)[KS], int j) {
       f32x16 acc[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -81,7 +95,7 @@ __global__ __launch_bounds__(256) void attn_fwd_k(const AttnFwdParams p) {
       for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[jj][kk], qf[i][kk], acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[kk], qf[i][kk], acc[i], 0, 0, 0);
       // acc[i][4 g + t]: query 32 i + lr, key 32 j + 8 g + 4 hh + t
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -91,110 +105,152 @@ __global__ __launch_bounds__(256) void attn_fwd_k(const AttnFwdParams p) {
                            p.alpha * acc[i][4 * g + 2], p.alpha * acc[i][4 * g + 3]};
           *reinterpret_cast<f32x4*>(&sS[(32 * i + lr) * RS + 32 * j + 8 * g + 4 * hh]) = v;
         }
+    };
+    if (w < nkt) load_k(ka, w);
+    if (w + NW < nkt) load_k(kb, w + NW);
+    for (int j = w; j < nkt; j += 2 * NW) {
+      scores(ka, j);
+      if (j + 2 * NW < nkt) load_k(ka, j + 2 * NW);
+      if (j + NW < nkt) {
+        scores(kb, j + NW);
+        if (j + 3 * NW < nkt) load_k(kb, j + 3 * NW);
+      }
     }
+  }
+  // phase 3's first v^T fragments (wave w: head dimensions dt 32 .. +31;
+  // chunks of 64 keys, double buffered), loaded now so that they arrive
+  // during the softmax
+  constexpr int NDT = D / 32;  // 32-wide head-dimension tiles
+  // one (head-dimension tile, query tile) pair per wave; with d = 64 only
+  // four waves have one
+  const int dt = w % NDT, qi = w / NDT;
+  const bool pv_wave = qi < 2;
+  const int nch = nk / 64;               // 64-key chunks of the tile's extent
+  const uint16_t* Vf = p.frag + (int64_t)p.n_seq * S * (nq + p.nkv) * D +
+                       ((int64_t)(seq * p.nkv + kvh) * NDT + dt) * (S / 16) * 512 + lane * 8;
+  bf16x8 va[4], vb[4];
+  auto load_v = [&](bf16x8 (&f)[4], int ch) {  // k-steps 4 ch .. 4 ch + 3
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) f[kk] = *reinterpret_cast<const bf16x8*>(Vf + (4 * ch + kk) * 512);
+  };
+  if (pv_wave) {
+    load_v(va, 0);
+    if (nch > 1) load_v(vb, 1);
   }
   __syncthreads();
 
-  // ---- phase 2: causal softmax of the 64 rows ----
-  for (int rr = 0; rr < QT / 4; ++rr) {
-    const int r = w * (QT / 4) + rr, i = q0 + r;  // i: query position in the sequence
-    float* row = &sS[r * RS];
-    f32x4 v[SMAX / 256];
-    float m = -INFINITY;
+  // ---- phase 2: causal softmax, 16 lanes per row (four rows per wave at a
+  // time): lane s of a row takes its 16-byte chunks s, s + 16, ... ----
+  {
+    const int sub = lane & 15;
+#pragma unroll 1
+    for (int rnd = 0; rnd < QT / (4 * NW); ++rnd) {
+      const int r = rnd * 4 * NW + w * 4 + (lane >> 4), i = q0 + r;  // i: query position
+      float* row = &sS[r * RS];
+      f32x4 v[SMAX / 64];
+      float m = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < SMAX / 256; ++u) {
-      const int c = lane + 64 * u;
-      v[u] = 4 * c < nk ? *reinterpret_cast<const f32x4*>(row + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < SMAX / 64; ++u) {
+        const int c = sub + 16 * u;
+        v[u] = 4 * c < nk ? *reinterpret_cast<const f32x4*>(row + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * c + e <= i) m = fmaxf(m, v[u][e]);
-    }
-    m = wave_max(m);
-    float sum = 0.f;
-#pragma unroll
-    for (int u = 0; u < SMAX / 256; ++u) {
-      const int c = lane + 64 * u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ex = 4 * c + e <= i ? expf(v[u][e] - m) : 0.f;
-        v[u][e] = ex;
-        sum += ex;
+        for (int e = 0; e < 4; ++e)
+          if (4 * c + e <= i) m = fmaxf(m, v[u][e]);
       }
-    }
-    sum = wave_sum(sum);
-    const float inv = 1.0f / sum;
-    const int64_t prow = ((int64_t)z * S + i) * S;  // row i of head z in Pf / Pb
+      m = row16_max(m);
+      float sum = 0.f;
 #pragma unroll
-    for (int u = 0; u < SMAX / 256; ++u) {
-      const int c = lane + 64 * u;
-      if (4 * c >= nk) continue;
-      const f32x4 pv = v[u] * inv;
-      const u32x2 pb = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-      // bf16 P over the front half of the row: every lane's reads of this
-      // row precede (through m and sum) every write
-      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(row) + 4 * c) = pb;
-      if (p.Pf) *reinterpret_cast<f32x4*>(p.Pf + prow + 4 * c) = pv;
-      if (p.Pb) *reinterpret_cast<u32x2*>(p.Pb + prow + 4 * c) = pb;
+      for (int u = 0; u < SMAX / 64; ++u) {
+        const int c = sub + 16 * u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ex = 4 * c + e <= i ? expf(v[u][e] - m) : 0.f;
+          v[u][e] = ex;
+          sum += ex;
+        }
+      }
+      sum = row16_sum(sum);
+      const float inv = 1.0f / sum;
+      const int64_t prow = ((int64_t)z * S + i) * S;  // row i of head z in Pf / Pb
+#pragma unroll
+      for (int u = 0; u < SMAX / 64; ++u) {
+        const int c = sub + 16 * u;
+        if (4 * c >= nk) continue;
+        const f32x4 pv = v[u] * inv;
+        const u32x2 pb = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+        // bf16 P over the front half of the row: the row's 16 lanes are in
+        // one wave, and all their reads precede (through m and sum) any write
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(row) + 4 * c) = pb;
+        if (p.Pf) *reinterpret_cast<f32x4*>(p.Pf + prow + 4 * c) = pv;
+        if (p.Pb) *reinterpret_cast<u32x2*>(p.Pb + prow + 4 * c) = pb;
+      }
+      if (p.Pb)  // keys beyond the tile's extent: zero
+        for (int c = nk / 4 + sub; c < S / 4; c += 16)
+          *reinterpret_cast<u32x2*>(p.Pb + prow + 4 * c) = u32x2{0u, 0u};
     }
-    if (p.Pb)  // keys beyond the tile's extent: zero
-      for (int c = nk / 4 + lane; c < S / 4; c += 64)
-        *reinterpret_cast<u32x2*>(p.Pb + prow + 4 * c) = u32x2{0u, 0u};
   }
   __syncthreads();
 
   // ---- phase 3: O^T[d][q] = sum over keys of v^T[d][key] P^T[key][q] ----
   {
-    constexpr int NDT = D / 32;            // 32-wide head-dimension tiles
-    constexpr int QPW = NDT == 4 ? 2 : 1;  // query tiles per wave
-    const int dt = w % NDT, qi0 = NDT == 4 ? 0 : w / NDT;
-    const uint16_t* vT = p.vT + (((int64_t)seq * p.nkv + kvh) * D + dt * 32 + lr) * S + 8 * hh;
-    const int nks = nk / 16;
-    bf16x8 vf[SMAX / 16];
+    if (!pv_wave) return;
+    f32x16 acc;
 #pragma unroll
-    for (int ks = 0; ks < SMAX / 16; ++ks)
-      if (ks < nks) vf[ks] = *reinterpret_cast<const bf16x8*>(vT + 16 * ks);
-    f32x16 acc[QPW];
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    const char* sP = reinterpret_cast<const char*>(sS) + (32 * qi + lr) * RS * 4 + 16 * hh;
+    // every k-step of the tile's extent: P is zero for keys beyond a query
+    auto pv = [&](const bf16x8 (&f)[4], int ch) {
 #pragma unroll
-    for (int a = 0; a < QPW; ++a)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[a][e] = 0.f;
-    const char* sP = reinterpret_cast<const char*>(sS);
-#pragma unroll
-    for (int ks = 0; ks < SMAX / 16; ++ks) {
-#pragma unroll
-      for (int a = 0; a < QPW; ++a) {
-        const int qi = qi0 + a;
-        // query tile qi sees keys <= q0 + 32 qi + 31 only (P is zero beyond)
-        if (ks >= nks || 16 * ks >= q0 + 32 * qi + 32) continue;
-        const bf16x8 pf = *reinterpret_cast<const bf16x8*>(
-            sP + (size_t)(32 * qi + lr) * RS * 4 + (16 * ks + 8 * hh) * 2);
-        acc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks], pf, acc[a], 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 pf = *reinterpret_cast<const bf16x8*>(sP + (64 * ch + 16 * kk) * 2);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[kk], pf, acc, 0, 0, 0);
+      }
+    };
+    for (int ch = 0; ch < nch; ch += 2) {
+      pv(va, ch);
+      if (ch + 2 < nch) load_v(va, ch + 2);
+      if (ch + 1 < nch) {
+        pv(vb, ch + 1);
+        if (ch + 3 < nch) load_v(vb, ch + 3);
       }
     }
-    // acc[a][4 g + t]: head dimension dt 32 + 8 g + 4 hh + t, query 32 qi + lr
+    // acc[4 g + t]: head dimension dt 32 + 8 g + 4 hh + t, query 32 qi + lr
+    uint16_t* o = p.O + ((int64_t)seq * S + q0 + 32 * qi + lr) * p.ldo + h * D + dt * 32 + 4 * hh;
 #pragma unroll
-    for (int a = 0; a < QPW; ++a) {
-      uint16_t* o = p.O + ((int64_t)seq * S + q0 + 32 * (qi0 + a) + lr) * p.ldo + h * D + dt * 32 + 4 * hh;
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<u32x2*>(o + 8 * g) =
-            u32x2{pack_bf16x2(acc[a][4 * g], acc[a][4 * g + 1]),
-                  pack_bf16x2(acc[a][4 * g + 2], acc[a][4 * g + 3])};
-    }
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<u32x2*>(o + 8 * g) = u32x2{pack_bf16x2(acc[4 * g], acc[4 * g + 1]),
+                                                   pack_bf16x2(acc[4 * g + 2], acc[4 * g + 3])};
   }
 }
 
-// vT[seq][kv][j][s] = v[seq S + s][kv d + j]: one 64-token x d tile per block
-// through LDS (16-byte global loads and stores)
+// Fragment-ordered copies of q, k and v^T for attn_fwd_k, one 32-token x d
+// slab of one head per block (blockIdx.z: q heads, then k heads, then v
+// heads).  q and k: fragment (tile t, k-step kk), lane l = 32 hh + lr holds
+// row 32 t + lr, dimensions 16 kk + 8 hh .. +7.  v^T: fragment (dimension
+// tile dt, key step ks), lane l holds dimension 32 dt + lr, keys 16 ks + 8 hh
+// .. +7 (through an LDS transpose).  Writes are 16 bytes per lane, contiguous.
 template <int D>
-__global__ __launch_bounds__(256) void vtrans_k(const uint16_t* __restrict__ qkv, int64_t ld,
-                                                int64_t voff, int S, int nkv,
-                                                uint16_t* __restrict__ vT) {
-  __shared__ uint16_t t[D][64 + 8];
-  const int s0 = blockIdx.x * 64, sk = blockIdx.y;  // sk = seq nkv + kv
-  const int seq = sk / nkv, kv = sk % nkv;
-  const uint16_t* src = qkv + ((int64_t)seq * S + s0) * ld + voff + (int64_t)kv * D;
-  for (int c = threadIdx.x; c < 64 * D / 8; c += 256) {
+__global__ __launch_bounds__(256) void attn_prep_k(const uint16_t* __restrict__ qkv, int64_t ld,
+                                                   int S, int n_seq, int nq, int nkv,
+                                                   uint16_t* __restrict__ frag) {
+  constexpr int KS = D / 16;
+  __shared__ uint16_t t[D][32 + 8];
+  const int t32 = blockIdx.x, seq = blockIdx.y, hs = blockIdx.z;
+  const int nt32 = S / 32;
+  const uint16_t* src = qkv + ((int64_t)seq * S + 32 * t32) * ld + (int64_t)hs * D;
+  if (hs < nq + nkv) {  // q or k: a permutation of 16-byte chunks
+    const int64_t base = hs < nq ? ((int64_t)(seq * nq + hs) * nt32 + t32) * KS * 512
+                                 : (int64_t)n_seq * S * nq * D +
+                                       ((int64_t)(seq * nkv + hs - nq) * nt32 + t32) * KS * 512;
+    for (int c = threadIdx.x; c < KS * 64; c += 256) {
+      const int kk = c >> 6, l = c & 63;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src + (int64_t)(l & 31) * ld + 16 * kk + 8 * (l >> 5));
+      *reinterpret_cast<u32x4*>(frag + base + (int64_t)c * 8) = x;
+    }
+    return;
+  }
+  const int kv = hs - nq - nkv;
+  for (int c = threadIdx.x; c < 32 * D / 8; c += 256) {
     const int tok = c / (D / 8), j0 = (c % (D / 8)) * 8;
     const u32x4 x = *reinterpret_cast<const u32x4*>(src + (int64_t)tok * ld + j0);
 #pragma unroll
@@ -204,36 +260,37 @@ __global__ __launch_bounds__(256) void vtrans_k(const uint16_t* __restrict__ qkv
     }
   }
   __syncthreads();
-  uint16_t* dst = vT + ((int64_t)sk * D) * S + s0;
-  for (int c = threadIdx.x; c < D * 8; c += 256) {
-    const int j = c / 8, k0 = (c % 8) * 8;
+  // this slab holds key steps 2 t32 and 2 t32 + 1 of every dimension tile
+  const int64_t vbase = (int64_t)n_seq * S * (nq + nkv) * D + (int64_t)(seq * nkv + kv) * (D / 32) * (S / 16) * 512;
+  for (int c = threadIdx.x; c < (D / 32) * 2 * 64; c += 256) {
+    const int dt = c / 128, ksl = (c / 64) & 1, l = c & 63;
+    const int j = 32 * dt + (l & 31), k0 = 16 * ksl + 8 * (l >> 5);
     u32x4 x;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       x[e] = (uint32_t)t[j][k0 + 2 * e] | ((uint32_t)t[j][k0 + 2 * e + 1] << 16);
-    *reinterpret_cast<u32x4*>(dst + (int64_t)j * S + k0) = x;
+    *reinterpret_cast<u32x4*>(frag + vbase + ((int64_t)dt * (S / 16) + 2 * t32 + ksl) * 512 + l * 8) = x;
   }
 }
 
 static bool a16(const void* q) { return ((uintptr_t)q & 15) == 0; }
 
 bool attn_fwd_ok(int S, int d, int64_t ld, int64_t ldo, const void* qkv, const void* O,
-                 const void* vT) {
+                 const void* frag) {
   return (d == 64 || d == 128) && S % QT == 0 && S >= QT && S <= SMAX && ld % 8 == 0 &&
-         ldo % 4 == 0 && a16(qkv) && ((uintptr_t)O & 7) == 0 && a16(vT);
+         ldo % 4 == 0 && a16(qkv) && ((uintptr_t)O & 7) == 0 && a16(frag);
 }
 
-hipError_t attn_fwd(const AttnFwdParams& p, int n_seq, int d, hipStream_t s) {
-  const dim3 tgrid(p.S / 64, n_seq * p.nkv), grid(p.S / QT, n_seq * p.nq);
-  const int64_t voff = (int64_t)(p.nq + p.nkv) * d;
+hipError_t attn_fwd(const AttnFwdParams& p, int d, hipStream_t s) {
+  const dim3 pgrid(p.S / 32, p.n_seq, p.nq + 2 * p.nkv), grid(p.S / QT, p.n_seq * p.nq);
   if (d == 128) {
-    hipLaunchKernelGGL(vtrans_k<128>, tgrid, dim3(256), 0, s, p.qkv, p.ld, voff, p.S, p.nkv,
-                       const_cast<uint16_t*>(p.vT));
-    hipLaunchKernelGGL(attn_fwd_k<128>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_prep_k<128>, pgrid, dim3(256), 0, s, p.qkv, p.ld, p.S, p.n_seq, p.nq,
+                       p.nkv, p.frag);
+    hipLaunchKernelGGL(attn_fwd_k<128>, grid, dim3(64 * NW), 0, s, p);
   } else {
-    hipLaunchKernelGGL(vtrans_k<64>, tgrid, dim3(256), 0, s, p.qkv, p.ld, voff, p.S, p.nkv,
-                       const_cast<uint16_t*>(p.vT));
-    hipLaunchKernelGGL(attn_fwd_k<64>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_prep_k<64>, pgrid, dim3(256), 0, s, p.qkv, p.ld, p.S, p.n_seq, p.nq,
+                       p.nkv, p.frag);
+    hipLaunchKernelGGL(attn_fwd_k<64>, grid, dim3(64 * NW), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -949,16 +949,17 @@ static lsn_status layer_forward(lsn_ctx* c, int layer, const uint8_t* rec, const
 
   // attention: one fused kernel where the shape allows (S <= 512, d 64 or
   // 128), else scores, softmax and P v as three launches
-  uint16_t* vT = reinterpret_cast<uint16_t*>(c->scores);  // free until the backward's dP
-  if (attn_fwd_ok(S, d, QKV, QD, c->qkvb, c->O, vT)) {
+  // fragment-ordered operands in dqkv, free until the backward's attention
+  uint16_t* frag = reinterpret_cast<uint16_t*>(c->dqkv);
+  if (attn_fwd_ok(S, d, QKV, QD, c->qkvb, c->O, frag)) {
     AttnFwdParams ap;
-    ap.qkv = c->qkvb; ap.ld = QKV; ap.vT = vT;
+    ap.qkv = c->qkvb; ap.ld = QKV; ap.frag = frag;
     ap.O = c->O; ap.ldo = QD;
     ap.Pf = final_residual ? nullptr : c->Pf;
     ap.Pb = final_residual ? nullptr : c->Pb;
-    ap.S = S; ap.nq = nq; ap.nkv = nkv;
+    ap.n_seq = c->n_seq; ap.S = S; ap.nq = nq; ap.nkv = nkv;
     ap.alpha = 1.0f / sqrtf((float)d);
-    HIPCHK(c, attn_fwd(ap, c->n_seq, d, s));
+    HIPCHK(c, attn_fwd(ap, d, s));
   } else {
     // attention: scores = q k^T / sqrt(d) per (sequence, head)
     {
