@@ -92,8 +92,16 @@ struct LoraTGrad {
   float scale = 1.f;
   int accumulate = 1;
   LoraTGradJob job[3];
+  // set by lora_tgrad: tokens per split, splits, partial sums and their
+  // offsets per (job, z)
+  int tps = 0, nsplit = 1;
+  float* part = nullptr;
+  int64_t poff[3][3] = {};
 };
-hipError_t lora_tgrad(const LoraTGrad& a, hipStream_t s);
+// part (may be null): scratch for the token-split partial sums; the splits
+// (up to 8, about 256 workgroups in all) are limited to what fits, and added
+// in split order
+hipError_t lora_tgrad(const LoraTGrad& a, float* part, int64_t part_floats, hipStream_t s);
 
 // floats of split-k scratch lora_mm wants for these sizes (0: no split)
 int64_t lora_mm_partial_floats(int R, int K);

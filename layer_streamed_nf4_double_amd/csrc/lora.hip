@@ -307,8 +307,10 @@ hipError_t lora_u(const LoraU& a, float* partial, int64_t partial_floats, hipStr
 // burst (16-byte loads where the row allows), rounds them to bf16 and stores
 // them transposed in LDS (column-major in m), so that each MFMA fragment --
 // 8 consecutive tokens of one column -- is one 16-byte LDS read; wave w then
-// runs the block's MFMAs for its 16 columns.  Every output element is one
-// lane's sum in token order: deterministic.
+// runs the block's MFMAs for its 16 columns.  With few column blocks the
+// tokens are split over blockIdx.z (up to 8 ranges); each range's sum is one
+// lane's in token order and lora_tgrad_reduce_k adds the ranges in order:
+// deterministic.
 constexpr int TB = 256;      // tokens per LDS block
 constexpr int TBP = TB + 8;  // padded row (bf16) of the transposed tiles
 
@@ -319,6 +321,8 @@ __global__ __launch_bounds__(256) void lora_tgrad_k(const LoraTGrad a) {
   const LoraTGradJob& jb = a.job[blockIdx.y];
   const int c0 = blockIdx.x * 64;
   if (c0 >= jb.C) return;  // uniform over the workgroup
+  // token range of this split (blockIdx.z)
+  const int mlo = blockIdx.z * a.tps, mhi = min(a.R, mlo + a.tps);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int nz = jb.nz;
   f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(256) void lora_tgrad_k(const LoraTGrad a) {
   const bool cfull = c0 + cc + 8 <= jb.C;
   const bool yvec = cfull && (a.ldy % (YF32 ? 4 : 8)) == 0 &&
                     ((uintptr_t)jb.Y & 15) == 0 && ((c0 + cc) % (YF32 ? 4 : 8)) == 0;
-  for (int mb = 0; mb < a.R; mb += TB) {
+  for (int mb = mlo; mb < mhi; mb += TB) {
     // every load of the block first (one round trip), then bf16 + LDS
     constexpr int NI = TB / 32;
     float v[NI][8];
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(256) void lora_tgrad_k(const LoraTGrad a) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int m = mb + mr + 32 * i;
-        const bool in = m < a.R;
+        const bool in = m < mhi;
         if constexpr (YF32) {
           const float* y = reinterpret_cast<const float*>(jb.Y) + (int64_t)(in ? m : 0) * a.ldy + c0 + cc;
           const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -368,7 +372,7 @@ __global__ __launch_bounds__(256) void lora_tgrad_k(const LoraTGrad a) {
         for (int e = 0; e < 8; ++e) {
           const int c = c0 + cc + e;
           float y = 0.f;
-          if (m < a.R && c < jb.C) {
+          if (m < mhi && c < jb.C) {
             const int64_t o = (int64_t)m * a.ldy + c;
             if constexpr (YF32) y = reinterpret_cast<const float*>(jb.Y)[o];
             else y = bf16_to_f32(reinterpret_cast<const uint16_t*>(jb.Y)[o]);
@@ -384,9 +388,9 @@ __global__ __launch_bounds__(256) void lora_tgrad_k(const LoraTGrad a) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int m = mb + mr + 32 * i;
-        const float* zr = jb.Z[z] + (int64_t)(m < a.R ? m : 0) * jb.ldz[z];
-        zv[z][i][0] = (m < a.R && jz < a.r) ? zr[jz] : 0.f;
-        zv[z][i][1] = (m < a.R && jz + 1 < a.r) ? zr[jz + 1] : 0.f;
+        const float* zr = jb.Z[z] + (int64_t)(m < mhi ? m : 0) * jb.ldz[z];
+        zv[z][i][0] = (m < mhi && jz < a.r) ? zr[jz] : 0.f;
+        zv[z][i][1] = (m < mhi && jz + 1 < a.r) ? zr[jz + 1] : 0.f;
       }
     }
 #pragma unroll
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(256) void lora_tgrad_k(const LoraTGrad a) {
       }
     }
     __syncthreads();
-    const int nk = min(TB, a.R - mb);
+    const int nk = min(TB, mhi - mb);
     for (int k0 = 0; k0 < nk; k0 += 32) {
       const int kk = k0 + (lane >> 4) * 8;
       const bf16x8 af = *reinterpret_cast<const bf16x8*>(&sY[16 * wave + (lane & 15)][kk]);
@@ -425,6 +429,10 @@ __global__ __launch_bounds__(256) void lora_tgrad_k(const LoraTGrad a) {
     for (int i = 0; i < 4; ++i) {
       const int c = c0 + 16 * wave + 4 * (lane >> 4) + i;
       if (c >= jb.C) continue;
+      if (a.nsplit > 1) {  // raw sum of this token range, added by lora_tgrad_reduce_k
+        a.part[a.poff[blockIdx.y][z] + ((int64_t)blockIdx.z * jb.C + c) * 16 + j] = acc[z][i];
+        continue;
+      }
       float* o = jb.out[z] + (int64_t)c * jb.so_c + (int64_t)j * jb.so_j;
       const float v = a.scale * acc[z][i];
       *o = a.accumulate ? *o + v : v;
@@ -432,17 +440,58 @@ __global__ __launch_bounds__(256) void lora_tgrad_k(const LoraTGrad a) {
   }
 }
 
-hipError_t lora_tgrad(const LoraTGrad& a, hipStream_t s) {
+// out(c, j) (+)= scale * (sum over the token splits, in split order, of the
+// partial sums); blockIdx.y = job * 3 + z
+__global__ __launch_bounds__(256) void lora_tgrad_reduce_k(const LoraTGrad a) {
+  const int q = blockIdx.y / 3, z = blockIdx.y % 3;
+  const LoraTGradJob& jb = a.job[q];
+  if (z >= jb.nz) return;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // c * 16 + j
+  if (e >= (int64_t)jb.C * 16) return;
+  const int c = (int)(e >> 4), j = (int)(e & 15);
+  if (j >= a.r) return;
+  const float* pp = a.part + a.poff[q][z] + e;
+  float sum = 0.f;
+  for (int sp = 0; sp < a.nsplit; ++sp) sum += pp[(int64_t)sp * jb.C * 16];
+  float* o = jb.out[z] + (int64_t)c * jb.so_c + (int64_t)j * jb.so_j;
+  const float v = a.scale * sum;
+  *o = a.accumulate ? *o + v : v;
+}
+
+hipError_t lora_tgrad(const LoraTGrad& a0, float* part, int64_t part_floats, hipStream_t s) {
+  LoraTGrad a = a0;
   if (a.R <= 0 || a.njobs <= 0) return hipSuccess;
   if (a.njobs > 3 || a.r > 16) return hipErrorInvalidValue;
   int cmax = 0;
+  int64_t per_split = 0;  // partial-sum floats of one token split
   for (int q = 0; q < a.njobs; ++q) {
     if (a.job[q].nz < 1 || a.job[q].nz > 3) return hipErrorInvalidValue;
     cmax = std::max(cmax, a.job[q].C);
+    per_split += (int64_t)a.job[q].nz * a.job[q].C * 16;
   }
-  const dim3 grid((cmax + 63) / 64, a.njobs);
+  // token splits: about 256 workgroups, at least 64 tokens per split, and
+  // the partial sums within the scratch (else one pass over the tokens)
+  const int wgs = ((cmax + 63) / 64) * a.njobs;
+  int ns = std::max(1, std::min({8, 256 / std::max(wgs, 1), a.R / 64}));
+  if (!part) ns = 1;
+  while (ns > 1 && per_split * ns > part_floats) --ns;
+  a.tps = ((a.R + ns - 1) / ns + 31) / 32 * 32;
+  a.nsplit = (a.R + a.tps - 1) / a.tps;
+  a.part = part;
+  if (a.nsplit > 1) {
+    int64_t off = 0;
+    for (int q = 0; q < a.njobs; ++q)
+      for (int z = 0; z < a.job[q].nz; ++z) {
+        a.poff[q][z] = off;
+        off += (int64_t)a.nsplit * a.job[q].C * 16;
+      }
+  }
+  const dim3 grid((cmax + 63) / 64, a.njobs, a.nsplit);
   if (a.y_f32) hipLaunchKernelGGL(lora_tgrad_k<true>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(lora_tgrad_k<false>, grid, dim3(256), 0, s, a);
+  if (a.nsplit > 1)
+    hipLaunchKernelGGL(lora_tgrad_reduce_k, dim3((cmax * 16 + 255) / 256, a.njobs * 3), dim3(256), 0,
+                       s, a);
   return hipGetLastError();
 }
 

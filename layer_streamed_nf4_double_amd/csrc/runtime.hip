@@ -835,8 +835,10 @@ static int lora_bwd_ext(lsn_ctx* c, int layer, Group g, const float* dyf, int64_
   }
   if (lora_u_ok(u)) {
     (void)lora_u(u, c->lpart, c->lpart_floats, c->cs);
-    (void)lora_tgrad(ga, c->cs);
-    (void)lora_tgrad(gb, c->cs);
+    // token-split partial sums in hpart (free outside the attention backward)
+    const int64_t hpf = (int64_t)T * c->QD;
+    (void)lora_tgrad(ga, c->hpart, hpf, c->cs);
+    (void)lora_tgrad(gb, c->hpart, hpf, c->cs);
   } else {  // rows not 16-byte aligned: the general product, one adapter at a time
     for (int q = 0; q < u.n; ++q) {
       const float* dy = dyf + u.col0[q];
@@ -1345,12 +1347,12 @@ lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t
     ga.R = M; ga.r = r; ga.y_f32 = 0; ga.ldy = K; ga.scale = s; ga.njobs = 1; ga.accumulate = 0;
     ga.job[0].Y = X; ga.job[0].C = K; ga.job[0].nz = 1; ga.job[0].so_c = r; ga.job[0].so_j = 1;
     ga.job[0].Z[0] = L.u; ga.job[0].ldz[0] = r; ga.job[0].out[0] = dA;
-    (void)lora_tgrad(ga, hs);
+    (void)lora_tgrad(ga, L.lpart, L.lpf, hs);
     LoraTGrad gb;  // dB = s t^T dY, stored dB[j*N + n]
     gb.R = M; gb.r = r; gb.y_f32 = 0; gb.ldy = N; gb.scale = s; gb.njobs = 1; gb.accumulate = 0;
     gb.job[0].Y = dY; gb.job[0].C = N; gb.job[0].nz = 1; gb.job[0].so_c = 1; gb.job[0].so_j = N;
     gb.job[0].Z[0] = L.t; gb.job[0].ldz[0] = r; gb.job[0].out[0] = dB;
-    (void)lora_tgrad(gb, hs);
+    (void)lora_tgrad(gb, L.lpart, L.lpf, hs);
     lora_ext(A, r, 1, K, r, L.bext, 16, 0, hs);  // bext = A
     p.Aext = L.aext; p.ldae = 16; p.Bext = L.bext; p.ldbe = 16; p.kext = 16;
   }
