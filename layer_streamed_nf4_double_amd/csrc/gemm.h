@@ -49,6 +49,11 @@ struct GemmParams {
   int64_t part_floats = 0;
   int ksplit = 1;      // set by gemm()
   int64_t pstride = 0;  // floats from one split's partial sums to the next (set by gemm())
+  // defer_reduce: a split launch leaves its partial sums (dense [M, N] rows,
+  // buffer y at part + y pstride) for the consumer, which adds them in split
+  // order; split_used (host, may be null) receives the split launched
+  int defer_reduce = 0;
+  int* split_used = nullptr;
   // optional timing events that record the main kernel's start and end (passed
   // to hipExtLaunchKernelGGL, so they add no dispatch of their own)
   hipEvent_t ev0 = nullptr, ev1 = nullptr;

@@ -507,7 +507,8 @@ hipError_t bf16t_launch(GemmParams p, hipStream_t s) {
     hipExtLaunchKernelGGL(bf16t_kernel<C_F32_RES>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
   else
     hipExtLaunchKernelGGL(bf16t_kernel<C_BF16>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
-  if (p.ksplit > 1) gemm_reduce_launch(p, s);
+  if (p.split_used) *p.split_used = p.ksplit;
+  if (p.ksplit > 1 && !p.defer_reduce) gemm_reduce_launch(p, s);
   return hipGetLastError();
 }
 
@@ -527,7 +528,8 @@ hipError_t bf16f_launch(GemmParams p, hipStream_t s) {
     hipExtLaunchKernelGGL(bf16f_kernel<C_F32_RES>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
   else
     hipExtLaunchKernelGGL(bf16f_kernel<C_BF16>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
-  if (p.ksplit > 1) gemm_reduce_launch(p, s);
+  if (p.split_used) *p.split_used = p.ksplit;
+  if (p.ksplit > 1 && !p.defer_reduce) gemm_reduce_launch(p, s);
   return hipGetLastError();
 }
 

@@ -469,7 +469,8 @@ hipError_t nf4f_launch(GemmParams p, hipStream_t s) {
   if (p.ksplit > 1 && (!p.part || p.part_floats < p.ksplit * p.pstride)) p.ksplit = 1;
   if (plan.nt == 2) nf4f_launch_t<2>(p, s);
   else nf4f_launch_t<1>(p, s);
-  if (p.ksplit > 1) gemm_reduce_launch(p, s);
+  if (p.split_used) *p.split_used = p.ksplit;
+  if (p.ksplit > 1 && !p.defer_reduce) gemm_reduce_launch(p, s);
   return hipGetLastError();
 }
 

@@ -399,7 +399,8 @@ hipError_t nf4t_launch(GemmParams p, hipStream_t s) {
     hipExtLaunchKernelGGL(nf4t_kernel<C_F32_RES>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
   else
     hipExtLaunchKernelGGL(nf4t_kernel<C_BF16>, grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
-  if (p.ksplit > 1) gemm_reduce_launch(p, s);
+  if (p.split_used) *p.split_used = p.ksplit;
+  if (p.ksplit > 1 && !p.defer_reduce) gemm_reduce_launch(p, s);
   return hipGetLastError();
 }
 

@@ -4,6 +4,33 @@
 #include <stdint.h>
 
 namespace lsn {
+// An fp32 operand [rows, width] given as the sum of ns buffers p + y stride
+// (y < ns, rows of the operand's own width): the split-k partial sums of the
+// GEMM that produced it, which a consumer adds in split order exactly as the
+// split-k reduction would (ns = 1: the operand itself).  The *_fuses checks
+// say whether a consumer takes ns > 1 (16-byte aligned p and stride % 4 == 0
+// also required); otherwise it needs ns = 1.
+struct SplitSum {
+  const float* p = nullptr;
+  int ns = 1;
+  int64_t stride = 0;
+};
+bool rmsnorm_bwd_fuses(int H, const float* h, const float* out, const float* dres,
+                       const uint16_t* g);
+// outb (may be null): also bf16(out)
+void rmsnorm_bwd(const float* h, const uint16_t* g, const float* rstd, const SplitSum& dy,
+                 const float* dres, int T, int H, float* out, uint16_t* outb, hipStream_t s);
+// hout = res + src, then y = RMSNorm(hout) (needs rmsnorm_fwd_res_fuses)
+bool rmsnorm_fwd_res_fuses(int H, const float* res, const float* hout, const uint16_t* g,
+                           const uint16_t* y);
+void rmsnorm_fwd_res(const float* res, const SplitSum& src, const uint16_t* g, int T, int H,
+                     float eps, float* hout, uint16_t* y, float* rstd, hipStream_t s);
+bool rope_fwd_fuses(int d, const uint16_t* out);
+void rope_fwd(const SplitSum& qkv, uint16_t* out, int T, int S, int nq, int nkv, int d,
+              float theta, hipStream_t s);
+bool swiglu_bwd_fuses(int T, int F, const float* gu, const uint16_t* dgu, const float* dguf);
+void swiglu_bwd(const float* gu, const SplitSum& da, uint16_t* dgu, float* dguf, int T, int F,
+                hipStream_t s);
 void rmsnorm_fwd(const float* h, const uint16_t* g, int T, int H, float eps, uint16_t* y,
                  float* rstd, hipStream_t s);
 void rmsnorm_bwd(const float* h, const uint16_t* g, const float* rstd, const float* dy,

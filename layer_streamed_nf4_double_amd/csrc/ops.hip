@@ -497,6 +497,16 @@ LSN_DEV float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 LSN_DEV float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 LSN_DEV bool al16(const void* q) { return ((uintptr_t)q & 15) == 0; }
 
+// four consecutive elements of a SplitSum operand: the buffers added in
+// split order from zero, as the split-k reduction adds them (one buffer: the
+// value itself)
+LSN_DEV f32x4 sum4(const SplitSum& a, int64_t off) {
+  if (a.ns == 1) return *reinterpret_cast<const f32x4*>(a.p + off);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int y = 0; y < a.ns; ++y) acc += *reinterpret_cast<const f32x4*>(a.p + y * a.stride + off);
+  return acc;
+}
+
 __global__ __launch_bounds__(256) void rmsnorm_fwd4_k(const float* __restrict__ h,
                                                       const uint16_t* __restrict__ g, int H,
                                                       float eps, uint16_t* __restrict__ y,
@@ -523,20 +533,67 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd4_k(const float* __restrict__ 
   }
 }
 
+// h = res + src (the residual add of a projection whose split-k partial sums
+// src holds), written out, then RMSNorm of h as rmsnorm_fwd4_k
+__global__ __launch_bounds__(256) void rmsnorm_fwd_res4_k(const float* __restrict__ res,
+                                                          const SplitSum src,
+                                                          const uint16_t* __restrict__ g, int H,
+                                                          float eps, float* __restrict__ hout,
+                                                          uint16_t* __restrict__ y,
+                                                          float* __restrict__ rstd) {
+  __shared__ float red[16];
+  const int64_t row = blockIdx.x;
+  const f32x4* rr = reinterpret_cast<const f32x4*>(res + row * H);
+  f32x4* x = reinterpret_cast<f32x4*>(hout + row * H);
+  const int n4 = H >> 2;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const f32x4 v = rr[i] + sum4(src, row * H + 4 * i);
+    x[i] = v;
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  if (threadIdx.x == 0) rstd[row] = r;
+  const u32x2* gw = reinterpret_cast<const u32x2*>(g);
+  u32x2* yo = reinterpret_cast<u32x2*>(y + row * H);
+  for (int i = threadIdx.x; i < n4; i += 256) {  // this thread's own writes above
+    const f32x4 v = x[i];
+    const u32x2 w = gw[i];
+    yo[i] = u32x2{pack_bf16x2(bf_lo(w[0]) * (v[0] * r), bf_hi(w[0]) * (v[1] * r)),
+                  pack_bf16x2(bf_lo(w[1]) * (v[2] * r), bf_hi(w[1]) * (v[3] * r))};
+  }
+}
+
+// (dy: the output gradient, or the split-k partial sums of the GEMM that
+// produced it, summed once: up to 8 chunks per thread stay in registers
+// between the two passes; outb, if given, also receives bf16(out))
+constexpr int RB_CACHE = 8;
 __global__ __launch_bounds__(256) void rmsnorm_bwd4_k(const float* __restrict__ h,
                                                       const uint16_t* __restrict__ g,
                                                       const float* __restrict__ rstd,
-                                                      const float* __restrict__ dy,
-                                                      const float* dres, int H, float* out) {
+                                                      const SplitSum dy, const float* dres, int H,
+                                                      float* out, uint16_t* __restrict__ outb) {
   __shared__ float red[16];
   const int64_t row = blockIdx.x;
   const f32x4* x = reinterpret_cast<const f32x4*>(h + row * H);
-  const f32x4* d = reinterpret_cast<const f32x4*>(dy + row * H);
   const u32x2* gw = reinterpret_cast<const u32x2*>(g);
   const int n4 = H >> 2;
+  f32x4 dc[RB_CACHE];
   float dot = 0.f;
-  for (int i = threadIdx.x; i < n4; i += 256) {
-    const f32x4 xv = x[i], dv = d[i];
+#pragma unroll
+  for (int k = 0; k < RB_CACHE; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < n4) {
+      const f32x4 xv = x[i], dv = sum4(dy, row * H + 4 * i);
+      dc[k] = dv;
+      const u32x2 w = gw[i];
+      dot += bf_lo(w[0]) * dv[0] * xv[0] + bf_hi(w[0]) * dv[1] * xv[1] +
+             bf_lo(w[1]) * dv[2] * xv[2] + bf_hi(w[1]) * dv[3] * xv[3];
+    }
+  }
+  for (int i = threadIdx.x + 256 * RB_CACHE; i < n4; i += 256) {
+    const f32x4 xv = x[i], dv = sum4(dy, row * H + 4 * i);
     const u32x2 w = gw[i];
     dot += bf_lo(w[0]) * dv[0] * xv[0] + bf_hi(w[0]) * dv[1] * xv[1] +
            bf_lo(w[1]) * dv[2] * xv[2] + bf_hi(w[1]) * dv[3] * xv[3];
@@ -546,34 +603,44 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd4_k(const float* __restrict__ 
   const float c = r * r * r * dot / (float)H;
   f32x4* o = reinterpret_cast<f32x4*>(out + row * H);
   const f32x4* dr = dres ? reinterpret_cast<const f32x4*>(dres + row * H) : nullptr;
-  for (int i = threadIdx.x; i < n4; i += 256) {
-    const f32x4 xv = x[i], dv = d[i];
+  u32x2* ob = outb ? reinterpret_cast<u32x2*>(outb + row * H) : nullptr;
+  auto emit = [&](int i, const f32x4& dv) {
+    const f32x4 xv = x[i];
     const u32x2 w = gw[i];
     f32x4 v = {r * bf_lo(w[0]) * dv[0] - c * xv[0], r * bf_hi(w[0]) * dv[1] - c * xv[1],
                r * bf_lo(w[1]) * dv[2] - c * xv[2], r * bf_hi(w[1]) * dv[3] - c * xv[3]};
     if (dr) v = dr[i] + v;
     o[i] = v;
+    if (ob) ob[i] = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  };
+#pragma unroll
+  for (int k = 0; k < RB_CACHE; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < n4) emit(i, dc[k]);
   }
+  for (int i = threadIdx.x + 256 * RB_CACHE; i < n4; i += 256) emit(i, sum4(dy, row * H + 4 * i));
 }
 
 // RoPE with the token's d/2 angles computed once per block into LDS.
+// Forward: reads q|k|v from src (the projection's output or its split-k
+// partial sums); backward: rotates xin in place.
 template <bool FWD>
-__global__ __launch_bounds__(256) void rope4_k(float* __restrict__ xin, uint16_t* __restrict__ out,
-                                               int S, int nq, int nkv, int d, float theta) {
+__global__ __launch_bounds__(256) void rope4_k(const SplitSum src, float* __restrict__ xin,
+                                               uint16_t* __restrict__ out, int S, int nq,
+                                               int nkv, int d, float theta) {
   __shared__ float sc[128], ss[128];
   const int64_t t = blockIdx.x;
   const int pos = (int)(t % S);
   const int W = (nq + 2 * nkv) * d, half = d / 2, h4 = half / 4;
   for (int j = threadIdx.x; j < half; j += 256) rope_angle(pos, j, d, theta, &sc[j], &ss[j]);
   __syncthreads();
-  float* x = xin + t * W;
+  float* x = FWD ? nullptr : xin + t * W;
   uint16_t* y = out + t * W;
+  auto ld4 = [&](int o) { return FWD ? sum4(src, t * W + o) : *reinterpret_cast<const f32x4*>(x + o); };
   const int nrot = (nq + nkv) * h4;  // 4-wide groups of rotated pairs
   for (int i = threadIdx.x; i < nrot; i += 256) {
     const int head = i / h4, j = (i % h4) * 4;
-    f32x4* p1 = reinterpret_cast<f32x4*>(x + head * d + j);
-    f32x4* p2 = reinterpret_cast<f32x4*>(x + head * d + j + half);
-    const f32x4 a = *p1, b = *p2;
+    const f32x4 a = ld4(head * d + j), b = ld4(head * d + j + half);
     f32x4 r1, r2;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -587,8 +654,8 @@ __global__ __launch_bounds__(256) void rope4_k(float* __restrict__ xin, uint16_t
       }
     }
     if (!FWD) {
-      *p1 = r1;
-      *p2 = r2;
+      *reinterpret_cast<f32x4*>(x + head * d + j) = r1;
+      *reinterpret_cast<f32x4*>(x + head * d + j + half) = r2;
     }
     *reinterpret_cast<u32x2*>(y + head * d + j) =
         u32x2{pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
@@ -597,7 +664,7 @@ __global__ __launch_bounds__(256) void rope4_k(float* __restrict__ xin, uint16_t
   }
   const int o0 = (nq + nkv) * d;
   for (int i = threadIdx.x; i < nkv * d / 4; i += 256) {
-    const f32x4 v = reinterpret_cast<const f32x4*>(x + o0)[i];
+    const f32x4 v = ld4(o0 + 4 * i);
     reinterpret_cast<u32x2*>(y + o0)[i] = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   }
 }
@@ -697,8 +764,10 @@ __global__ __launch_bounds__(256) void swiglu_fwd4_k(const float* __restrict__ g
   *reinterpret_cast<u32x2*>(a + t * F + f) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
 }
 
+// (da: the gradient of a, or the split-k partial sums of the GEMM that
+// produced it)
 __global__ __launch_bounds__(256) void swiglu_bwd4_k(const float* __restrict__ gu,
-                                                     const float* __restrict__ da,
+                                                     const SplitSum da,
                                                      uint16_t* __restrict__ dgu,
                                                      float* __restrict__ dguf, int F) {
   const int f = (blockIdx.x * 256 + threadIdx.x) * 4;
@@ -706,7 +775,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd4_k(const float* __restrict__ g
   const int64_t t = blockIdx.y;
   const f32x4 g = *reinterpret_cast<const f32x4*>(gu + t * 2 * F + f);
   const f32x4 u = *reinterpret_cast<const f32x4*>(gu + t * 2 * F + F + f);
-  const f32x4 d = *reinterpret_cast<const f32x4*>(da + t * F + f);
+  const f32x4 d = sum4(da, t * F + f);
   f32x4 dg, du;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -740,27 +809,54 @@ void rmsnorm_fwd(const float* h, const uint16_t* g, int T, int H, float eps, uin
 }
 void rmsnorm_bwd(const float* h, const uint16_t* g, const float* rstd, const float* dy,
                  const float* dres, int T, int H, float* out, hipStream_t s) {
-  if (H % 4 == 0 && a16(h) && a16(dy) && a16(out) && (!dres || a16(dres)) &&
-      ((uintptr_t)g & 7) == 0)
-    hipLaunchKernelGGL(rmsnorm_bwd4_k, dim3(T), dim3(256), 0, s, h, g, rstd, dy, dres, H, out);
-  else
-    hipLaunchKernelGGL(rmsnorm_bwd_k, dim3(T), dim3(256), 0, s, h, g, rstd, dy, dres, H, out);
+  rmsnorm_bwd(h, g, rstd, SplitSum{dy, 1, 0}, dres, T, H, out, nullptr, s);
+}
+static bool split_vec(const SplitSum& a) { return a16(a.p) && a.stride % 4 == 0; }
+bool rmsnorm_bwd_fuses(int H, const float* h, const float* out, const float* dres,
+                       const uint16_t* g) {
+  return H % 4 == 0 && a16(h) && a16(out) && (!dres || a16(dres)) && ((uintptr_t)g & 7) == 0;
+}
+void rmsnorm_bwd(const float* h, const uint16_t* g, const float* rstd, const SplitSum& dy,
+                 const float* dres, int T, int H, float* out, uint16_t* outb, hipStream_t s) {
+  if (rmsnorm_bwd_fuses(H, h, out, dres, g) && split_vec(dy) && ((uintptr_t)outb & 7) == 0) {
+    hipLaunchKernelGGL(rmsnorm_bwd4_k, dim3(T), dim3(256), 0, s, h, g, rstd, dy, dres, H, out,
+                       outb);
+  } else if (dy.ns == 1) {
+    hipLaunchKernelGGL(rmsnorm_bwd_k, dim3(T), dim3(256), 0, s, h, g, rstd, dy.p, dres, H, out);
+    if (outb) f32_to_bf16(out, outb, (int64_t)T * H, s);
+  }
+}
+bool rmsnorm_fwd_res_fuses(int H, const float* res, const float* hout, const uint16_t* g,
+                           const uint16_t* y) {
+  return H % 4 == 0 && a16(res) && a16(hout) && ((uintptr_t)g & 7) == 0 &&
+         ((uintptr_t)y & 7) == 0;
+}
+void rmsnorm_fwd_res(const float* res, const SplitSum& src, const uint16_t* g, int T, int H,
+                     float eps, float* hout, uint16_t* y, float* rstd, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_fwd_res4_k, dim3(T), dim3(256), 0, s, res, src, g, H, eps, hout, y,
+                     rstd);
 }
 static bool rope_vec(const void* x, const void* y, int d) {
   return d % 8 == 0 && d / 2 <= 128 && a16(x) && ((uintptr_t)y & 7) == 0;
 }
+bool rope_fwd_fuses(int d, const uint16_t* out) { return rope_vec(out, out, d); }
 void rope_fwd(const float* qkv, uint16_t* out, int T, int S, int nq, int nkv, int d, float theta,
               hipStream_t s) {
-  if (rope_vec(qkv, out, d))
-    hipLaunchKernelGGL(rope4_k<true>, dim3(T), dim3(256), 0, s, const_cast<float*>(qkv), out, S,
-                       nq, nkv, d, theta);
-  else
-    hipLaunchKernelGGL(rope_fwd_k, dim3(T), dim3(256), 0, s, qkv, out, S, nq, nkv, d, theta);
+  rope_fwd(SplitSum{qkv, 1, 0}, out, T, S, nq, nkv, d, theta, s);
+}
+void rope_fwd(const SplitSum& qkv, uint16_t* out, int T, int S, int nq, int nkv, int d,
+              float theta, hipStream_t s) {
+  if (rope_vec(qkv.p, out, d) && split_vec(qkv))
+    hipLaunchKernelGGL(rope4_k<true>, dim3(T), dim3(256), 0, s, qkv, nullptr, out, S, nq, nkv, d,
+                       theta);
+  else if (qkv.ns == 1)
+    hipLaunchKernelGGL(rope_fwd_k, dim3(T), dim3(256), 0, s, qkv.p, out, S, nq, nkv, d, theta);
 }
 void rope_bwd(float* dqkv, uint16_t* outb, int T, int S, int nq, int nkv, int d, float theta,
               hipStream_t s) {
   if (rope_vec(dqkv, outb, d))
-    hipLaunchKernelGGL(rope4_k<false>, dim3(T), dim3(256), 0, s, dqkv, outb, S, nq, nkv, d, theta);
+    hipLaunchKernelGGL(rope4_k<false>, dim3(T), dim3(256), 0, s, SplitSum{}, dqkv, outb, S, nq,
+                       nkv, d, theta);
   else
     hipLaunchKernelGGL(rope_bwd_k, dim3(T), dim3(256), 0, s, dqkv, outb, S, nq, nkv, d, theta);
 }
@@ -789,15 +885,22 @@ void swiglu_fwd(const float* gu, uint16_t* a, int T, int F, hipStream_t s) {
   const int64_t n = (int64_t)T * F;
   hipLaunchKernelGGL(swiglu_fwd_k, dim3(nb(n, 256)), dim3(256), 0, s, gu, a, F, n);
 }
+bool swiglu_bwd_fuses(int T, int F, const float* gu, const uint16_t* dgu, const float* dguf) {
+  return F % 4 == 0 && T <= 65535 && a16(gu) && ((uintptr_t)dgu & 7) == 0 && (!dguf || a16(dguf));
+}
 void swiglu_bwd(const float* gu, const float* da, uint16_t* dgu, float* dguf, int T, int F,
                 hipStream_t s) {
-  if (F % 4 == 0 && T <= 65535 && a16(gu) && a16(da) && ((uintptr_t)dgu & 7) == 0 &&
-      (!dguf || a16(dguf))) {
+  swiglu_bwd(gu, SplitSum{da, 1, 0}, dgu, dguf, T, F, s);
+}
+void swiglu_bwd(const float* gu, const SplitSum& da, uint16_t* dgu, float* dguf, int T, int F,
+                hipStream_t s) {
+  if (swiglu_bwd_fuses(T, F, gu, dgu, dguf) && split_vec(da)) {
     hipLaunchKernelGGL(swiglu_bwd4_k, dim3(nb(F / 4, 256), T), dim3(256), 0, s, gu, da, dgu, dguf, F);
     return;
   }
+  if (da.ns != 1) return;
   const int64_t n = (int64_t)T * F;
-  hipLaunchKernelGGL(swiglu_bwd_k, dim3(nb(n, 256)), dim3(256), 0, s, gu, da, dgu, dguf, F, n);
+  hipLaunchKernelGGL(swiglu_bwd_k, dim3(nb(n, 256)), dim3(256), 0, s, gu, da.p, dgu, dguf, F, n);
 }
 void embed(const int32_t* tok, const uint16_t* table, int T, int H, int V, float* h,
            hipStream_t s) {

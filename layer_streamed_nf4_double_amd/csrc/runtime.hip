@@ -294,9 +294,18 @@ static void prof_end(lsn_ctx* c, lsn_ctx::ProfRec& r, hipStream_t s) {
 }
 
 // every GEMM of a context goes through here; the NF4 ones can be timed
-static hipError_t cgemm(lsn_ctx* c, GemmParams p, int opa, int opb, int batch) {
+// keep (may be null): when the launch splits k, its partial sums stay in
+// gpart for the next kernel, which adds them (*keep describes them; else
+// *keep is the output itself)
+static hipError_t cgemm(lsn_ctx* c, GemmParams p, int opa, int opb, int batch,
+                        SplitSum* keep = nullptr) {
   p.part = c->gpart;
   p.part_floats = c->gpart_floats;
+  int ns = 1;
+  if (keep) {
+    p.defer_reduce = 1;
+    p.split_used = &ns;
+  }
   lsn_ctx::ProfRec r{0, opa, opb, gemm_tile(p, opa, opb, batch),
                      2.0 * p.M * p.N * (double)p.K * p.nseg * batch, nullptr, nullptr};
   // events bracket the GEMM kernel only (not a split-k reduction)
@@ -309,6 +318,9 @@ static hipError_t cgemm(lsn_ctx* c, GemmParams p, int opa, int opb, int batch) {
   }
   const hipError_t e = gemm(p, opa, opb, batch, c->cs);
   if (on && r.e0 && r.e1) c->prof.push_back(r);
+  if (keep)
+    *keep = ns > 1 ? SplitSum{c->gpart, ns, split_stride(p.M, p.N)}
+                   : SplitSum{static_cast<const float*>(p.C), 1, 0};
   return e;
 }
 
@@ -868,7 +880,8 @@ static int lora_bwd_ext(lsn_ctx* c, int layer, Group g, const float* dyf, int64_
 }
 
 static hipError_t nf4_fwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const uint16_t* x, int T,
-                               int kext, void* out, int cmode, const float* res) {
+                               int kext, void* out, int cmode, const float* res,
+                               SplitSum* keep = nullptr) {
   GemmParams p = base_params(c);
   const int pf = g.first;
   p.M = T;
@@ -891,7 +904,7 @@ static hipError_t nf4_fwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const ui
     p.ldbe = kext;
     p.kext = kext;
   }
-  return cgemm(c, p, A_BF16_K, B_NF4_K, 1);
+  return cgemm(c, p, A_BF16_K, B_NF4_K, 1, keep);
 }
 
 // dX = dY W_group (+ low-rank extension); dY is fp32 (opa A_F32_K) or bf16.
@@ -899,7 +912,7 @@ static hipError_t nf4_fwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const ui
 // dqkvb, which is free from the previous layer's q|k|v input gradient until
 // this layer's rope backward refills it.
 static hipError_t nf4_bwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const void* dy, int opa,
-                               int T, int kext, void* out, int cmode) {
+                               int T, int kext, void* out, int cmode, SplitSum* keep = nullptr) {
   GemmParams p = base_params(c);
   const int pf = g.first;
   p.M = T;
@@ -925,7 +938,7 @@ static hipError_t nf4_bwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const vo
     p.ldbe = kext;
     p.kext = kext;
   }
-  return cgemm(c, p, opa, B_NF4_R, 1);
+  return cgemm(c, p, opa, B_NF4_R, 1, keep);
 }
 
 // ---------------------------------------------------------------------------
@@ -946,8 +959,15 @@ static lsn_status layer_forward(lsn_ctx* c, int layer, const uint8_t* rec, const
 
   rmsnorm_fwd(h, g1, T, H, g.rms_eps, c->n1, c->rstd1, s);
   int kext = lora_fwd_ext(c, layer, G_QKV, c->n1, H, T);
-  HIPCHK(c, nf4_fwd_gemm(c, rec, G_QKV, c->n1, T, kext, c->qkv, C_F32, nullptr));
-  rope_fwd(c->qkv, c->qkvb, T, S, nq, nkv, d, g.rope_theta, s);
+  // split-k partial sums of the projections go straight to their consumers
+  // (rope, the residual RMSNorm, the SwiGLU and RMSNorm backwards), which add
+  // them as the reduction would
+  SplitSum ss;
+  const bool rope_f = rope_fwd_fuses(d, c->qkvb);
+  HIPCHK(c, nf4_fwd_gemm(c, rec, G_QKV, c->n1, T, kext, c->qkv, C_F32, nullptr,
+                         rope_f ? &ss : nullptr));
+  if (rope_f) rope_fwd(ss, c->qkvb, T, S, nq, nkv, d, g.rope_theta, s);
+  else rope_fwd(c->qkv, c->qkvb, T, S, nq, nkv, d, g.rope_theta, s);
 
   // attention: one fused kernel where the shape allows (S <= 512, d 64 or
   // 128), else scores, softmax and P v as three launches
@@ -994,8 +1014,14 @@ static lsn_status layer_forward(lsn_ctx* c, int layer, const uint8_t* rec, const
     }
   }
   kext = lora_fwd_ext(c, layer, G_O, c->O, QD, T);
-  HIPCHK(c, nf4_fwd_gemm(c, rec, G_O, c->O, T, kext, c->h2, C_F32_RES, h));
-  rmsnorm_fwd(c->h2, g2, T, H, g.rms_eps, c->n2, c->rstd2, s);
+  if (rmsnorm_fwd_res_fuses(H, h, c->h2, g2, c->n2)) {  // h2 = h + o(...), then its norm
+    HIPCHK(c, nf4_fwd_gemm(c, rec, G_O, c->O, T, kext, c->h2, C_F32_RES, h, &ss));
+    if (ss.ns > 1) rmsnorm_fwd_res(h, ss, g2, T, H, g.rms_eps, c->h2, c->n2, c->rstd2, s);
+    else rmsnorm_fwd(c->h2, g2, T, H, g.rms_eps, c->n2, c->rstd2, s);
+  } else {
+    HIPCHK(c, nf4_fwd_gemm(c, rec, G_O, c->O, T, kext, c->h2, C_F32_RES, h));
+    rmsnorm_fwd(c->h2, g2, T, H, g.rms_eps, c->n2, c->rstd2, s);
+  }
   kext = lora_fwd_ext(c, layer, G_GU, c->n2, H, T);
   HIPCHK(c, nf4_fwd_gemm(c, rec, G_GU, c->n2, T, kext, c->gu, C_F32, nullptr));
   swiglu_fwd(c->gu, c->a, T, F, s);
@@ -1021,29 +1047,44 @@ static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, cons
 
   // MLP: out = h2 + down(silu(gate) * up)
   int kext = lora_bwd_ext(c, layer, G_D, dout, H, c->a, F, T);
-  HIPCHK(c, nf4_bwd_gemm(c, rec, G_D, dout, A_F32_K, T, kext, c->da, C_F32));
   const bool gu_ad = c->targeted(LSN_GATE) || c->targeted(LSN_UP);
-  swiglu_bwd(c->gu, c->da, c->dgu, gu_ad ? c->dguf : nullptr, T, F, s);
+  SplitSum ss;
+  const bool sw_f = swiglu_bwd_fuses(T, F, c->gu, c->dgu, gu_ad ? c->dguf : nullptr);
+  HIPCHK(c, nf4_bwd_gemm(c, rec, G_D, dout, A_F32_K, T, kext, c->da, C_F32, sw_f ? &ss : nullptr));
+  if (sw_f) swiglu_bwd(c->gu, ss, c->dgu, gu_ad ? c->dguf : nullptr, T, F, s);
+  else swiglu_bwd(c->gu, c->da, c->dgu, gu_ad ? c->dguf : nullptr, T, F, s);
   kext = lora_bwd_ext(c, layer, G_GU, c->dguf, 2 * F, c->n2, H, T);
-  HIPCHK(c, nf4_bwd_gemm(c, rec, G_GU, c->dgu, A_BF16_K, T, kext, c->dn, C_F32));
-  rmsnorm_bwd(c->h2, g2, c->rstd2, c->dn, dout, T, H, c->dh2, s);
+  const bool n2_f = rmsnorm_bwd_fuses(H, c->h2, c->dh2, dout, g2);
+  HIPCHK(c, nf4_bwd_gemm(c, rec, G_GU, c->dgu, A_BF16_K, T, kext, c->dn, C_F32, n2_f ? &ss : nullptr));
+  // dh2 also in bf16 (dqkvb, free until the rope backward), the o input
+  // gradient GEMM's operand
+  if (n2_f) rmsnorm_bwd(c->h2, g2, c->rstd2, ss, dout, T, H, c->dh2, c->dqkvb, s);
+  else rmsnorm_bwd(c->h2, g2, c->rstd2, SplitSum{c->dn, 1, 0}, dout, T, H, c->dh2, c->dqkvb, s);
 
   // attention block: h2 = h + o(attn(rope(q), rope(k), v))
   kext = lora_bwd_ext(c, layer, G_O, c->dh2, H, c->O, QD, T);
-  HIPCHK(c, nf4_bwd_gemm(c, rec, G_O, c->dh2, A_F32_K, T, kext, c->dO, C_BF16));
+  HIPCHK(c, nf4_bwd_gemm(c, rec, G_O, c->dqkvb, A_BF16_K, T, kext, c->dO, C_BF16));
   const int Z = c->n_seq * nq;
-  {  // dP = dO V^T
-    GemmParams p = base_params(c);
-    p.M = S; p.N = S; p.K = d;
-    p.A = c->dO; p.lda = QD;
-    p.B = c->qkvb + QD + KVD; p.ldb = QKV;
-    p.zdiv = nq; p.grpB = grp;
-    p.sA_o = (int64_t)S * QD; p.sA_i = d;
-    p.sB_o = (int64_t)S * QKV; p.sB_i = d;
-    p.C = c->scores; p.ldc = S;
-    p.sC_o = (int64_t)nq * S * S; p.sC_i = (int64_t)S * S;
-    p.causal = CAUSAL_SKIP_UPPER;  // the softmax backward reads keys <= query only
-    HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_K, Z));
+  const float scale = 1.0f / sqrtf((float)d);
+  // dP, dS and dQ in one fused kernel where the shape allows (its operand
+  // copies go to qkv, free after the recompute's rope); it overwrites Pb
+  // with dS, so dV (from P) runs first
+  uint16_t* bfrag = reinterpret_cast<uint16_t*>(c->qkv);
+  const bool fused = attn_bwd_ok(S, d, QKV, QD, QKV, c->qkvb, c->dO, c->dqkv, bfrag, c->Pf);
+  if (!fused) {
+    {  // dP = dO V^T
+      GemmParams p = base_params(c);
+      p.M = S; p.N = S; p.K = d;
+      p.A = c->dO; p.lda = QD;
+      p.B = c->qkvb + QD + KVD; p.ldb = QKV;
+      p.zdiv = nq; p.grpB = grp;
+      p.sA_o = (int64_t)S * QD; p.sA_i = d;
+      p.sB_o = (int64_t)S * QKV; p.sB_i = d;
+      p.C = c->scores; p.ldc = S;
+      p.sC_o = (int64_t)nq * S * S; p.sC_i = (int64_t)S * S;
+      p.causal = CAUSAL_SKIP_UPPER;  // the softmax backward reads keys <= query only
+      HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_K, Z));
+    }
   }
   // dV[kv] = sum over its q heads of P_h^T dO_h: one product per q head
   // (batch n_seq x nq, 4x the workgroups of a product per kv head), then
@@ -1062,21 +1103,28 @@ static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, cons
     HIPCHK(c, cgemm(c, p, A_BF16_R, B_BF16_R, Z));
     group_sum(c->hpart, c->n_seq, nq, grp, S, d, c->dqkv + QD + KVD, QKV, s);
   }
-  softmax_bwd(c->Pf, c->scores, c->Pb, S, (int64_t)Z * S, s);  // dS (bf16) over Pb
-  const float scale = 1.0f / sqrtf((float)d);
-  {  // dQ = scale dS K
-    GemmParams p = base_params(c);
-    p.M = S; p.N = d; p.K = S;
-    p.A = c->Pb; p.lda = S;
-    p.B = c->qkvb + QD; p.ldb = QKV;
-    p.zdiv = nq; p.grpB = grp;
-    p.sA_o = (int64_t)nq * S * S; p.sA_i = (int64_t)S * S;
-    p.sB_o = (int64_t)S * QKV; p.sB_i = d;
-    p.C = c->dqkv; p.ldc = QKV;
-    p.sC_o = (int64_t)S * QKV; p.sC_i = d;
-    p.alpha = scale;
-    p.causal = CAUSAL_K_TO_ROW;  // dS is zero for keys > query
-    HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, Z));
+  if (fused) {
+    AttnBwdParams ab;
+    ab.qkv = c->qkvb; ab.ld = QKV; ab.dO = c->dO; ab.lddo = QD; ab.frag = bfrag;
+    ab.Pin = c->Pf; ab.dS = c->Pb; ab.dQ = c->dqkv; ab.ldq = QKV;
+    ab.n_seq = c->n_seq; ab.S = S; ab.nq = nq; ab.nkv = nkv; ab.alpha = scale;
+    HIPCHK(c, attn_bwd(ab, d, s));
+  } else {
+    softmax_bwd(c->Pf, c->scores, c->Pb, S, (int64_t)Z * S, s);  // dS (bf16) over Pb
+    {  // dQ = scale dS K
+      GemmParams p = base_params(c);
+      p.M = S; p.N = d; p.K = S;
+      p.A = c->Pb; p.lda = S;
+      p.B = c->qkvb + QD; p.ldb = QKV;
+      p.zdiv = nq; p.grpB = grp;
+      p.sA_o = (int64_t)nq * S * S; p.sA_i = (int64_t)S * S;
+      p.sB_o = (int64_t)S * QKV; p.sB_i = d;
+      p.C = c->dqkv; p.ldc = QKV;
+      p.sC_o = (int64_t)S * QKV; p.sC_i = d;
+      p.alpha = scale;
+      p.causal = CAUSAL_K_TO_ROW;  // dS is zero for keys > query
+      HIPCHK(c, cgemm(c, p, A_BF16_K, B_BF16_R, Z));
+    }
   }
   {  // dK[kv] = scale sum over its q heads of dS_h^T Q_h, as dV
     GemmParams p = base_params(c);
@@ -1095,8 +1143,10 @@ static lsn_status layer_backward(lsn_ctx* c, int layer, const uint8_t* rec, cons
   }
   rope_bwd(c->dqkv, c->dqkvb, T, S, nq, nkv, d, g.rope_theta, s);
   kext = lora_bwd_ext(c, layer, G_QKV, c->dqkv, QKV, c->n1, H, T);
-  HIPCHK(c, nf4_bwd_gemm(c, rec, G_QKV, c->dqkvb, A_BF16_K, T, kext, c->dn, C_F32));
-  rmsnorm_bwd(h, g1, c->rstd1, c->dn, c->dh2, T, H, dh, s);
+  const bool n1_f = rmsnorm_bwd_fuses(H, h, dh, c->dh2, g1);
+  HIPCHK(c, nf4_bwd_gemm(c, rec, G_QKV, c->dqkvb, A_BF16_K, T, kext, c->dn, C_F32, n1_f ? &ss : nullptr));
+  if (n1_f) rmsnorm_bwd(h, g1, c->rstd1, ss, c->dh2, T, H, dh, nullptr, s);
+  else rmsnorm_bwd(h, g1, c->rstd1, c->dn, c->dh2, T, H, dh, s);
   return launch_check(c);
 }
 
