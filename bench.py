@@ -306,7 +306,8 @@ def sft_leg(torch, w, layers, head, tok, tgt, steps, warmup, n_slots=0, mode="st
     return out, dt
 
 
-def dpo_leg(torch, w, layers, head, steps, warmup, sft_peak, sft_loads, link_best, rec_bytes):
+def dpo_leg(torch, w, layers, head, steps, warmup, sft_peak, sft_loads, link_best, rec_bytes,
+            n_slots=0):
     """Streamed DPO steps on one preference pair (fused reference pass)."""
     import numpy as np
 
@@ -318,7 +319,7 @@ def dpo_leg(torch, w, layers, head, steps, warmup, sft_peak, sft_loads, link_bes
     d_tok, d_tgt = device_batch(dtok, sft_targets(dtok), w["vocab"])
     torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats()
-    md = build_model(w, "stream_host", 2 * S, S, layers, head)
+    md = build_model(w, "stream_host", 2 * S, S, layers, head, n_slots=n_slots)
     P, beta = synth.dpo_prompt_len(w), synth.DPO_PAIR["beta"]
     for _ in range(max(1, warmup)):
         md.dpo_step(d_tok, d_tgt, S, P, beta, 1e-4)
@@ -338,6 +339,7 @@ def dpo_leg(torch, w, layers, head, steps, warmup, sft_peak, sft_loads, link_bes
     torch.cuda.empty_cache()
     alg = algorithmic_bytes(w, rec_bytes, dpo=True)
     return {"tokens_per_s": round(2 * S / ddt, 2), "ms_per_step": round(ddt * 1e3, 2),
+            "n_slots": n_slots or 2,
             "reference_pass": "fused with the policy forward (one record copy per layer)",
             "tokens_per_step": 2 * S, "loss": float(out[0]),
             "layer_loads_per_step": (l1 - l0) / steps,
@@ -696,6 +698,11 @@ def main():
                                     / 1e9 / link_best, 4)
         log(f"[bench] 3 slots: {slots3['ms_per_step']:.1f} ms/step, "
             f"{slots3['layer_loads_per_step']} loads/step, peak {slots3['peak_vram_bytes'] / 1e9:.2f} GB")
+        if dpo is not None:
+            slots3["dpo"] = dpo_leg(torch, w, layers, head, max(1, args.dpo_steps // 2), args.warmup,
+                                    slots3["peak_vram_bytes"], slots3["layer_loads_per_step"],
+                                    link_best, rec_bytes, n_slots=3)
+            log(f"[bench] 3 slots: DPO {slots3['dpo']['ms_per_step']:.1f} ms/step")
 
     # ---- the same step with the base resident on the device (peak VRAM side by side) ----
     resident = projection = file_src = head_host = None
@@ -750,12 +757,18 @@ def main():
                      "link_frac_algorithmic": round(alg2 / dt2 / 1e9 / link_best, 4)})
         dpo2 = dpo_leg(torch, w2, layers2, head2, max(1, args.second_steps // 2), args.warmup,
                        sft2["peak_vram_bytes"], sft2["layer_loads_per_step"], link_best, rec2)
+        dpo2_3 = dpo_leg(torch, w2, layers2, head2, max(1, args.second_steps // 2), args.warmup,
+                         sft2["peak_vram_bytes"], sft2["layer_loads_per_step"], link_best, rec2,
+                         n_slots=3)
         second = {"workload": f"{args.second_workload} streamed LoRA-SFT step (seq "
                               f"{w2['seq_len']}) and DPO step (2 x {w2['seq_len']})",
                   "n_layers": w2["n_layers"], "hidden": w2["hidden"], "vocab": w2["vocab"],
-                  "tied": bool(w2["tied"]), "sft": sft2, "dpo": dpo2}
+                  "tied": bool(w2["tied"]), "sft": sft2, "dpo": dpo2, "dpo_slots3": dpo2_3,
+                  "link_note": "no record is copied while the LM head runs (both slots hold the "
+                               "backward's first records); the copies themselves start 20-60 us "
+                               "apart"}
         log(f"[bench] {args.second_workload}: SFT {sft2['tokens_per_s']} tok/s, DPO "
-            f"{dpo2['tokens_per_s']} tok/s")
+            f"{dpo2['tokens_per_s']} tok/s, DPO with 3 slots {dpo2_3['tokens_per_s']} tok/s")
         del layers2
 
     cpu = None

@@ -232,11 +232,38 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   };
   auto none = [](int) {};
 
+  // ---- low-rank extension: extra k columns read directly as fragments ----
+  // (split 0 only), added before the main loop: its loads are issued after
+  // the prologue's direct loads and land with them
+  auto extension = [&]() {
+    const int lk = hh * 8;
+    for (int e0 = 0; e0 < p.kext; e0 += 16) {
+      bf16x8 xf[8], bfr[NT];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = min(m0 + i * 32 + lr, p.M - 1);
+        xf[i] = *reinterpret_cast<const bf16x8*>(p.Aext + (int64_t)m * p.ldae + e0 + lk);
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int n = min(n0 + w * 32 * NT + j * 32 + lr, p.N - 1);
+        bfr[j] = *reinterpret_cast<const bf16x8*>(p.Bext + (int64_t)n * p.ldbe + e0 + lk);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], xf[i], acc[i][j], 0, 0, 0);
+    }
+  };
+  const bool ext = p.kext > 0 && blockIdx.y == 0;
+
   if (it1 > it0) {
     // prologue: slices it0 .. it0+2 (clamped) into stages 0 .. 2
     issue(it0, 0);
     issue(min(it0 + 1, it1 - 1), 1);
     issue(min(it0 + 2, it1 - 1), 2);
+    if (ext) extension();
     LSN_WAIT_VM(2 * GROUP);
     __syncthreads();
     read_codes(cq, ca, 0);
@@ -303,29 +330,8 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
       st = st1;
     }
     LSN_WAIT_VM(0);  // no direct load may still be writing LDS when the waves exit
-  }
-
-  // ---- low-rank extension: extra k columns read directly as fragments ----
-  const int lk = hh * 8;
-  if (p.kext > 0 && blockIdx.y == 0) {
-    for (int e0 = 0; e0 < p.kext; e0 += 16) {
-      bf16x8 af[8], bfr[NT];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int m = min(m0 + i * 32 + lr, p.M - 1);
-        af[i] = *reinterpret_cast<const bf16x8*>(p.Aext + (int64_t)m * p.ldae + e0 + lk);
-      }
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int n = min(n0 + w * 32 * NT + j * 32 + lr, p.N - 1);
-        bfr[j] = *reinterpret_cast<const bf16x8*>(p.Bext + (int64_t)n * p.ldbe + e0 + lk);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
+  } else if (ext) {
+    extension();
   }
 
   // ---- epilogue ----
