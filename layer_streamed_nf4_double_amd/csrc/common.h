@@ -28,6 +28,11 @@ LSN_DEV uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// SwiGLU activation silu(g) * u = g * sigmoid(g) * u in fp32.  One definition
+// for the stand-alone SwiGLU kernels and the gate|up GEMM epilogue, so both
+// give the same bits from the same gate and up values.
+LSN_DEV float swiglu_act(float g, float u) { return g * (1.0f / (1.0f + expf(-g))) * u; }
+
 // wave64 reductions in a fixed butterfly order (deterministic)
 LSN_DEV float wave_sum(float v) {
 #pragma unroll

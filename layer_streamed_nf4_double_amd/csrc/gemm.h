@@ -7,7 +7,10 @@ namespace lsn {
 
 enum { A_BF16_K = 0, A_BF16_R = 1, A_F32_K = 2 };
 enum { B_BF16_K = 0, B_BF16_R = 1, B_NF4_K = 2, B_NF4_R = 3 };
-enum { C_F32 = 0, C_F32_ACC = 1, C_F32_RES = 2, C_BF16 = 3 };
+// C_SWIGLU (forward NF4 kernel only): B holds the fused gate|up rows
+// [N = 2F, K]; the output is a = bf16(silu(gate) * up) [M, F] with row
+// stride ldc, computed in the epilogue from the two accumulators
+enum { C_F32 = 0, C_F32_ACC = 1, C_F32_RES = 2, C_BF16 = 3, C_SWIGLU = 4 };
 
 struct GemmParams {
   int M = 0, N = 0, K = 0;
@@ -108,6 +111,11 @@ struct Nf4fPlan {
 };
 Nf4fPlan nf4f_plan(int M, int N, int K);
 hipError_t nf4f_launch(GemmParams p, hipStream_t s);
+// whether the SwiGLU epilogue (cmode C_SWIGLU) takes this gate|up problem:
+// the forward kernel takes it and its plan is the unsplit 256 x 256 tile,
+// the one a plain fp32 launch of the same problem uses (so the gate and up
+// values the epilogue sees are those a C_F32 launch would store)
+bool nf4f_swiglu_ok(const GemmParams& p);
 
 // input-gradient NF4 kernel (gemm_nf4t.hip): dx = dy W with dy bf16 [M, K]
 // row-major and the same W^T NF4 record [K, N] (operand form B_NF4_R); used by

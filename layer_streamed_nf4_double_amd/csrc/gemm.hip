@@ -686,6 +686,8 @@ static bool offsets_fit(const GemmParams& p, int opa, int opb) {
 hipError_t gemm(const GemmParams& p, int opa, int opb, int batch, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0 || batch <= 0) return hipSuccess;
   if (!offsets_fit(p, opa, opb)) return hipErrorInvalidValue;
+  if (p.cmode == C_SWIGLU)  // the forward NF4 kernel's epilogue only
+    return opa == A_BF16_K && opb == B_NF4_K && batch == 1 ? nf4f_launch(p, s) : hipErrorInvalidValue;
   if (opa == A_BF16_K && opb == B_NF4_K && nf4f_eligible(p, batch)) return nf4f_launch(p, s);
   if (opa == A_BF16_K && opb == B_NF4_R && nf4t_eligible(p, batch)) return nf4t_launch(p, s);
   if (opa == A_BF16_K && opb == B_BF16_K && bf16f_eligible(p, batch)) return bf16f_launch(p, s);

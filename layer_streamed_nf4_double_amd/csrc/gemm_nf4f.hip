@@ -43,6 +43,14 @@
 // are dequantized just in time, one k-step ahead of their MFMAs: each code
 // byte indexes a 256-entry LDS table holding the levels of its two nibbles.
 //
+// SwiGLU epilogue (C_SWIGLU, 256 x 256 tile only).  The weight is the fused
+// gate|up record [2F, K]; a tile then covers gate columns n0 .. n0+127 and
+// the same up columns F+n0 .. F+n0+127: wave w's column tile 0 holds gate
+// columns n0+32w .., tile 1 the up columns of the same features, so each
+// lane has gate and up of the same (m, f) in matching accumulators and
+// writes a = bf16(silu(gate) * up) [M, F] directly (a quarter of the bytes of
+// the fp32 gate|up output, and no separate SwiGLU pass).
+//
 // Determinism: every output element is reduced by one lane in a fixed order
 // (split-k partial sums are added in split order by gemm_reduce_launch).
 #include "common.h"
@@ -90,6 +98,9 @@ template <int MODE, int NT>
 __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   constexpr int FN = Shape<NT>::FN, C_STAGE = Shape<NT>::C_STAGE, GROUP = Shape<NT>::GROUP;
   constexpr int NS = 8 * NT;  // MFMA slots per k-step
+  constexpr bool SW = MODE == C_SWIGLU;
+  static_assert(!SW || NT == 2, "the SwiGLU epilogue pairs two column tiles per wave");
+  constexpr int TN = SW ? FN / 2 : FN;  // output columns per tile
   // the level-pair table first: its LDS address fits the 16-bit ds_read offset
   __shared__ __attribute__((aligned(64))) float2 sPair[256];
   __shared__ __attribute__((aligned(1024))) uint8_t sA[NST][A_STAGE];
@@ -106,7 +117,14 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   const int nblk = gridDim.x, b = blockIdx.x;
   const int per = nblk / 8, rem = nblk % 8, x = b % 8;
   const int id = x * per + min(x, rem) + b / 8;
-  const int m0 = (id % mt) * FM, n0 = (id / mt) * FN;
+  const int m0 = (id % mt) * FM, n0 = (id / mt) * TN;
+  const int Fh = p.N / 2;  // SwiGLU: the feature count F
+  // weight row (W^T row, clamped into the matrix) of row rr of wave w's
+  // column tile j
+  auto wrow = [&](int j, int rr) {
+    if constexpr (SW) return j * Fh + min(n0 + 32 * w + rr, Fh - 1);
+    else return min(n0 + 32 * NT * w + 32 * j + rr, p.N - 1);
+  };
 
   // entry b: the levels of code byte b (low nibble: even element, high
   // nibble: odd element); one 8-byte read dequantizes two elements
@@ -133,8 +151,7 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   for (int i = 0; i < NT; ++i) {
     const int r = (w * NT + i) * 32 + (lane >> 1);
     const int h = (lane & 1) ^ ((r >> 3) & 1);
-    const int row = min(n0 + r, p.N - 1);
-    offC[i] = (uint32_t)((int64_t)row * (p.K / 2) + h * 16);
+    offC[i] = (uint32_t)((int64_t)wrow(i, lane >> 1) * (p.K / 2) + h * 16);
   }
   // the same offsets for loads at instruction offset 1024 i - 4096 from one
   // M0 (activation load i) and at 1024 i (code load i); never negative,
@@ -144,10 +161,10 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   for (int i = 0; i < 8; ++i) offA_o[i] = offA[i] + 4096u - 1024u * i;
 #pragma unroll
   for (int i = 0; i < NT; ++i) offC_o[i] = offC[i] - 1024u * i;
-  // absmax: wave w fills its 64-entry region with rows 32 NT w + lane
-  // (clamped; with NT = 1 the upper half is unused)
-  const uint32_t offM =
-      (uint32_t)((int64_t)min(n0 + w * 32 * NT + lane, p.N - 1) * (p.K / FK) * 4);
+  // absmax: wave w fills its 64-entry region with the rows of its column
+  // tiles (entry 32 j + rr: row rr of tile j; with NT = 1 the upper half is
+  // unused)
+  const uint32_t offM = (uint32_t)((int64_t)wrow(lane >> 5, lane & 31) * (p.K / FK) * 4);
 
   const uint8_t* gA = reinterpret_cast<const uint8_t*>(p.A);
   const uint8_t* gC = reinterpret_cast<const uint8_t*>(p.B);
@@ -245,10 +262,8 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
         xf[i] = *reinterpret_cast<const bf16x8*>(p.Aext + (int64_t)m * p.ldae + e0 + lk);
       }
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int n = min(n0 + w * 32 * NT + j * 32 + lr, p.N - 1);
-        bfr[j] = *reinterpret_cast<const bf16x8*>(p.Bext + (int64_t)n * p.ldbe + e0 + lk);
-      }
+      for (int j = 0; j < NT; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(p.Bext + (int64_t)wrow(j, lr) * p.ldbe + e0 + lk);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -345,39 +360,57 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   // group's own load and store, so this also holds in place (C == R).
   auto epilogue = [&](auto full_) {
     constexpr bool FULL = decltype(full_)::value;
-    constexpr bool LOADS = MODE == C_F32_ACC || MODE == C_F32_RES;
-    float* const out = MODE < 0 ? p.part + blockIdx.y * p.pstride
-                                : reinterpret_cast<float*>(p.C);
-    const int64_t ld = MODE < 0 ? (int64_t)p.N : p.ldc;
-    const float* const src = MODE == C_F32_RES ? p.R : out;
-    const int64_t lds = MODE == C_F32_RES ? p.ldr : ld;
-    const int nl = n0 + w * 32 * NT + hh * 4;  // this lane's first column (t = 0, g = 0, j = 0)
+    if constexpr (SW) {  // a[m][f] for f = n0 + 32w + 8g + 4hh + t
+      const int fl = n0 + 32 * w + hh * 4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = m0 + i * 32 + lr;
-      if (!FULL && m >= p.M) continue;
-      float* __restrict__ orow = out + (int64_t)m * ld + nl;
-      uint16_t* __restrict__ brow = reinterpret_cast<uint16_t*>(p.C) + (int64_t)m * ld + nl;
-      const float* __restrict__ srow = src + (int64_t)m * lds + nl;
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
+      for (int i = 0; i < 8; ++i) {
+        const int m = m0 + i * 32 + lr;
+        if (!FULL && m >= p.M) continue;
+        uint16_t* __restrict__ arow = reinterpret_cast<uint16_t*>(p.C) + (int64_t)m * p.ldc + fl;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int c = j * 32 + g * 8;  // column offset of this group
-          if (!FULL && nl + c >= p.N) continue;
-          f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                     acc[i][j][4 * g + 3]};
-          if constexpr (LOADS) v += *reinterpret_cast<const f32x4*>(srow + c);
-          if constexpr (MODE == C_BF16) {
-            u32x2 b2 = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-            *reinterpret_cast<u32x2*>(brow + c) = b2;
-          } else {
-            *reinterpret_cast<f32x4*>(orow + c) = v;
-          }
+          if (!FULL && fl + g * 8 >= Fh) continue;
+          float r[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) r[t] = swiglu_act(acc[i][0][4 * g + t], acc[i][1][4 * g + t]);
+          *reinterpret_cast<u32x2*>(arow + g * 8) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
         }
+      }
+    } else {
+      constexpr bool LOADS = MODE == C_F32_ACC || MODE == C_F32_RES;
+      float* const out = MODE < 0 ? p.part + blockIdx.y * p.pstride
+                                  : reinterpret_cast<float*>(p.C);
+      const int64_t ld = MODE < 0 ? (int64_t)p.N : p.ldc;
+      const float* const src = MODE == C_F32_RES ? p.R : out;
+      const int64_t lds = MODE == C_F32_RES ? p.ldr : ld;
+      const int nl = n0 + w * 32 * NT + hh * 4;  // this lane's first column (t = 0, g = 0, j = 0)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = m0 + i * 32 + lr;
+        if (!FULL && m >= p.M) continue;
+        float* __restrict__ orow = out + (int64_t)m * ld + nl;
+        uint16_t* __restrict__ brow = reinterpret_cast<uint16_t*>(p.C) + (int64_t)m * ld + nl;
+        const float* __restrict__ srow = src + (int64_t)m * lds + nl;
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = j * 32 + g * 8;  // column offset of this group
+            if (!FULL && nl + c >= p.N) continue;
+            f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                       acc[i][j][4 * g + 3]};
+            if constexpr (LOADS) v += *reinterpret_cast<const f32x4*>(srow + c);
+            if constexpr (MODE == C_BF16) {
+              u32x2 b2 = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+              *reinterpret_cast<u32x2*>(brow + c) = b2;
+            } else {
+              *reinterpret_cast<f32x4*>(orow + c) = v;
+            }
+          }
+      }
     }
   };
-  if (m0 + FM <= p.M && n0 + FN <= p.N) epilogue(std::true_type{});
+  if (m0 + FM <= p.M && (SW ? n0 + TN <= Fh : n0 + FN <= p.N)) epilogue(std::true_type{});
   else epilogue(std::false_type{});
 }
 
@@ -438,6 +471,12 @@ static double plan_cost(int M, int N, int K, int nt, int split) {
   return us;
 }
 
+bool nf4f_swiglu_ok(const GemmParams& p) {
+  if (p.cmode != C_SWIGLU || p.N % 8 != 0 || p.ldc % 4 != 0 || !nf4f_eligible(p, 1)) return false;
+  const Nf4fPlan plan = nf4f_plan(p.M, p.N, p.K);
+  return plan.nt == 2 && plan.split == 1;
+}
+
 Nf4fPlan nf4f_plan(int M, int N, int K) {
   Nf4fPlan best{2, 1};
   double cost = plan_cost(M, N, K, 2, 1);
@@ -469,6 +508,14 @@ static void nf4f_launch_t(const GemmParams& p, hipStream_t s) {
 }
 
 hipError_t nf4f_launch(GemmParams p, hipStream_t s) {
+  if (p.cmode == C_SWIGLU) {  // one unsplit launch, tiles of 128 features
+    if (!nf4f_swiglu_ok(p)) return hipErrorInvalidValue;
+    const int tiles = ((p.M + FM - 1) / FM) * ((p.N / 2 + 127) / 128);
+    hipExtLaunchKernelGGL((nf4f_kernel<C_SWIGLU, 2>), dim3(tiles, 1, 1), dim3(256), 0, s, p.ev0,
+                          p.ev1, 0, p);
+    if (p.split_used) *p.split_used = 1;
+    return hipGetLastError();
+  }
   const Nf4fPlan plan = nf4f_plan(p.M, p.N, p.K);
   p.ksplit = plan.split;
   p.pstride = split_stride(p.M, p.N);

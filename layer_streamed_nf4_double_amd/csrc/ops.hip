@@ -157,7 +157,7 @@ __global__ void swiglu_fwd_k(const float* __restrict__ gu, uint16_t* __restrict_
   if (i >= n) return;
   const int64_t t = i / F, f = i % F;
   const float g = gu[t * 2 * F + f], u = gu[t * 2 * F + F + f];
-  a[i] = f32_to_bf16_bits(g * sigm(g) * u);
+  a[i] = f32_to_bf16_bits(swiglu_act(g, u));
 }
 
 // dg = da * u * silu'(g), du = da * silu(g) -> bf16 [T, 2F] (+ fp32 copy)
@@ -760,7 +760,7 @@ __global__ __launch_bounds__(256) void swiglu_fwd4_k(const float* __restrict__ g
   const f32x4 u = *reinterpret_cast<const f32x4*>(gu + t * 2 * F + F + f);
   float r[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) r[e] = g[e] * sigm(g[e]) * u[e];
+  for (int e = 0; e < 4; ++e) r[e] = swiglu_act(g[e], u[e]);
   *reinterpret_cast<u32x2*>(a + t * F + f) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
 }
 

@@ -879,9 +879,10 @@ static int lora_bwd_ext(lsn_ctx* c, int layer, Group g, const float* dyf, int64_
   return kext;
 }
 
-static hipError_t nf4_fwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const uint16_t* x, int T,
-                               int kext, void* out, int cmode, const float* res,
-                               SplitSum* keep = nullptr) {
+// the forward GEMM of a group: out (op)= x W_group (+ low-rank extension);
+// with C_SWIGLU (gate|up only) out is a = bf16(silu(gate) * up) [T, F]
+static GemmParams fwd_params(lsn_ctx* c, const uint8_t* rec, Group g, const uint16_t* x, int T,
+                             int kext, void* out, int cmode, const float* res) {
   GemmParams p = base_params(c);
   const int pf = g.first;
   p.M = T;
@@ -893,7 +894,7 @@ static hipError_t nf4_fwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const ui
   p.absmax = reinterpret_cast<const float*>(rec + c->amax_off[pf]);
   p.rowlen = c->K[pf];
   p.C = out;
-  p.ldc = p.N;
+  p.ldc = cmode == C_SWIGLU ? p.N / 2 : p.N;
   p.cmode = cmode;
   p.R = res;
   p.ldr = p.N;
@@ -904,7 +905,13 @@ static hipError_t nf4_fwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const ui
     p.ldbe = kext;
     p.kext = kext;
   }
-  return cgemm(c, p, A_BF16_K, B_NF4_K, 1, keep);
+  return p;
+}
+
+static hipError_t nf4_fwd_gemm(lsn_ctx* c, const uint8_t* rec, Group g, const uint16_t* x, int T,
+                               int kext, void* out, int cmode, const float* res,
+                               SplitSum* keep = nullptr) {
+  return cgemm(c, fwd_params(c, rec, g, x, T, kext, out, cmode, res), A_BF16_K, B_NF4_K, 1, keep);
 }
 
 // dX = dY W_group (+ low-rank extension); dY is fp32 (opa A_F32_K) or bf16.
@@ -1023,8 +1030,18 @@ static lsn_status layer_forward(lsn_ctx* c, int layer, const uint8_t* rec, const
     rmsnorm_fwd(c->h2, g2, T, H, g.rms_eps, c->n2, c->rstd2, s);
   }
   kext = lora_fwd_ext(c, layer, G_GU, c->n2, H, T);
-  HIPCHK(c, nf4_fwd_gemm(c, rec, G_GU, c->n2, T, kext, c->gu, C_F32, nullptr));
-  swiglu_fwd(c->gu, c->a, T, F, s);
+  // The forward writes a = silu(gate) * up straight from the gate|up GEMM's
+  // accumulators where its kernel allows; the backward's recompute keeps
+  // gate and up (fp32) for the SwiGLU backward and rebuilds a from them only
+  // when the down adapter's gradients need it.  Both launches use the same
+  // tile plan, so a is the same either way.
+  const GemmParams pgu = fwd_params(c, rec, G_GU, c->n2, T, kext, c->a, C_SWIGLU, nullptr);
+  if (final_residual && nf4f_swiglu_ok(pgu)) {
+    HIPCHK(c, cgemm(c, pgu, A_BF16_K, B_NF4_K, 1));
+  } else {
+    HIPCHK(c, nf4_fwd_gemm(c, rec, G_GU, c->n2, T, kext, c->gu, C_F32, nullptr));
+    if (final_residual || (c->adapters_on && c->targeted(LSN_DOWN))) swiglu_fwd(c->gu, c->a, T, F, s);
+  }
   kext = lora_fwd_ext(c, layer, G_D, c->a, F, T);  // also keeps t of down for backward
   if (final_residual)
     HIPCHK(c, nf4_fwd_gemm(c, rec, G_D, c->a, T, kext, out, C_F32_RES, c->h2));

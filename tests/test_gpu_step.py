@@ -589,6 +589,50 @@ def test_sft_256_tokens_all_projections_vs_oracle(torch):
                 assert np.array_equal(np.asarray(u).view(np.uint32), np.asarray(v).view(np.uint32))
 
 
+# 512 tokens with an FFN of 8208 features (64 x 128 + 16): the gate|up GEMM
+# takes the SwiGLU epilogue (unsplit 256 x 256 tiles of 128 features), whose
+# last feature tile is ragged; every projection adapted, so the epilogue also
+# adds the gate and up low-rank columns and the backward rebuilds a for the
+# down adapter.
+RAGGED_FFN = dict(wid=6, n_layers=2, hidden=256, n_heads=4, n_kv_heads=2, head_dim=64,
+                  ffn=8208, vocab=1024, rms_eps=1e-5, rope_theta=1e4, lora_rank=8,
+                  lora_alpha=16.0, tied=False, n_seq=2, seq_len=256)
+
+
+def test_sft_swiglu_epilogue_ragged_ffn_vs_oracle(torch):
+    """SFT step with the fused SwiGLU epilogue on a ragged feature count
+    against the oracle, then streamed == resident bitwise."""
+    w = RAGGED_FFN
+    tokens = synth.sft_tokens(w)
+    say("[sft-ragged-ffn] oracle")
+    cfg, layers, lora, head = oracle_model(w, b_zero=False, lora_targets=ALL7)
+    o = om.sft_step(cfg, layers, lora, head, tokens, LR)
+    say("[sft-ragged-ffn] gpu stream_host")
+    m = gpu_model(w, "stream_host", b_zero=False, lora_targets=ALL7)
+    loss, logp = _run_sft(torch, m, tokens)
+    g = _grads(m, w, ALL7)
+    m.close()
+    assert abs(loss - o["loss"]) <= 2e-2 * abs(o["loss"])
+    assert_close(logp, o["logp"], 2e-2, "logp")
+    for layer in range(w["n_layers"]):
+        for p in ALL7:
+            _, _, dA, dB = g[layer][p]
+            oA, oB = o["grads"][layer][p]
+            assert_close(dA, oA, 5e-2, f"dA L{layer} {p}")
+            assert_close(dB, oB, 5e-2, f"dB L{layer} {p}")
+    say("[sft-ragged-ffn] gpu resident (bitwise)")
+    r = gpu_model(w, "resident", b_zero=False, lora_targets=ALL7)
+    loss_r, logp_r = _run_sft(torch, r, tokens)
+    gr = _grads(r, w, ALL7)
+    r.close()
+    assert np.array_equal(_bits(np.float32(loss_r)), _bits(np.float32(loss)))
+    assert np.array_equal(_bits(logp_r), _bits(logp))
+    for layer in range(w["n_layers"]):
+        for p in ALL7:
+            for u, v in zip(g[layer][p], gr[layer][p]):
+                assert np.array_equal(_bits(np.asarray(u)), _bits(np.asarray(v)))
+
+
 # The 8B layer shape at the bench's 512 tokens (hidden 4096, 32 q / 8 kv heads
 # of 128, FFN 14336, the same seeded layers as the 8B workload), two layers and
 # a 1024-entry vocabulary so that the float64 oracle stays within seconds.
