@@ -101,8 +101,10 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   constexpr bool SW = MODE == C_SWIGLU;
   static_assert(!SW || NT == 2, "the SwiGLU epilogue pairs two column tiles per wave");
   constexpr int TN = SW ? FN / 2 : FN;  // output columns per tile
-  // the level-pair table first: its LDS address fits the 16-bit ds_read offset
-  __shared__ __attribute__((aligned(64))) float2 sPair[256];
+  // the level-pair table at LDS address 0 (the largest alignment is placed
+  // first): a lookup's address is then just 8 x code byte, one shift of a
+  // byte-selected operand (v_lshlrev_b32_sdwa) per byte
+  __shared__ __attribute__((aligned(4096))) float2 sPair[256];
   __shared__ __attribute__((aligned(1024))) uint8_t sA[NST][A_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sC[NST][C_STAGE];
   // absmax: 64 entries per wave (rows beyond its 32 NT columns are unused)

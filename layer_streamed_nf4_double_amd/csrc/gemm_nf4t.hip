@@ -62,8 +62,10 @@ constexpr int TGROUP = 8 + 2 + 1;        // direct loads per wave per slice
 // raw split-k partial sums.
 template <int MODE>
 __global__ __launch_bounds__(256) void nf4t_kernel(const GemmParams p) {
-  // the level-pair table first: its LDS address fits the 16-bit ds_read offset
-  __shared__ __attribute__((aligned(64))) float2 sPair[256];
+  // the level-pair table at LDS address 0 (the largest alignment is placed
+  // first): a lookup's address is then just 8 x code byte, one shift of a
+  // byte-selected operand (v_lshlrev_b32_sdwa) per byte
+  __shared__ __attribute__((aligned(4096))) float2 sPair[256];
   __shared__ __attribute__((aligned(1024))) uint8_t sA[TST][TA_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sC[TST][4 * CW];
   __shared__ __attribute__((aligned(16))) float sM[TST][4][64];

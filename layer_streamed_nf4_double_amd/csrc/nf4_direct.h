@@ -63,7 +63,7 @@ LSN_DEV int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // byte offset 8 * (byte p of code word q) into the level-pair table
 LSN_DEV uint32_t pair_off(uint32_t q, int p) {
-  return p == 0 ? (q << 3) & 0x7F8u : (q >> (8 * p - 3)) & 0x7F8u;
+  return ((q >> (8 * p)) & 0xFFu) << 3;
 }
 
 }  // namespace
