@@ -51,11 +51,10 @@ __global__ __launch_bounds__(256) void bf16f_kernel(const GemmParams p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lr = lane & 31, hh = lane >> 5;
 
-  // ---- tile coordinates (XCD-aware: consecutive ids land on one XCD) ----
+  // ---- tile coordinates and k split (XCD-aware, split-major) ----
   const int mt = (p.M + BM - 1) / BM;
-  const int nblk = gridDim.x, b = blockIdx.x;
-  const int per = nblk / 8, rem = nblk % 8, x = b % 8;
-  const int id = x * per + min(x, rem) + b / 8;
+  const WorkUnit wu = xcd_unit();
+  const int id = wu.tile, ks = wu.split;
   const int m0 = (id % mt) * BM, n0 = (id / mt) * BN;
 
   // ---- direct-load byte offsets of this lane (slice 0) ----
@@ -85,10 +84,10 @@ __global__ __launch_bounds__(256) void bf16f_kernel(const GemmParams p) {
   const uint8_t* gA = reinterpret_cast<const uint8_t*>(p.A);
   const uint8_t* gB = reinterpret_cast<const uint8_t*>(p.B);
 
-  // split-k: blockIdx.y takes slices [it0, it1)
+  // split-k: split ks takes slices [it0, it1)
   const int nkt = p.K / BK;
   const int kper = (nkt + p.ksplit - 1) / p.ksplit;
-  const int it0 = min(nkt, (int)blockIdx.y * kper), it1 = min(nkt, it0 + kper);
+  const int it0 = min(nkt, ks * kper), it1 = min(nkt, it0 + kper);
 
   auto issue_a = [&](int it, int st) {
     const uint8_t* a = gA + it * (BK * 2);
@@ -206,7 +205,7 @@ __global__ __launch_bounds__(256) void bf16f_kernel(const GemmParams p) {
   auto epilogue = [&](auto full_) {
     constexpr bool FULL = decltype(full_)::value;
     constexpr bool LOADS = MODE == C_F32_ACC || MODE == C_F32_RES;
-    float* const out = MODE < 0 ? p.part + blockIdx.y * p.pstride : reinterpret_cast<float*>(p.C);
+    float* const out = MODE < 0 ? p.part + ks * p.pstride : reinterpret_cast<float*>(p.C);
     const int64_t ld = MODE < 0 ? (int64_t)p.N : p.ldc;
     const float* const src = MODE == C_F32_RES ? p.R : out;
     const int64_t lds = MODE == C_F32_RES ? p.ldr : ld;
@@ -259,9 +258,8 @@ __global__ __launch_bounds__(256) void bf16t_kernel(const GemmParams p) {
   const int lr = lane & 31, hh = lane >> 5;
 
   const int mt = (p.M + BM - 1) / BM;
-  const int nblk = gridDim.x, b = blockIdx.x;
-  const int per = nblk / 8, rem = nblk % 8, x = b % 8;
-  const int id = x * per + min(x, rem) + b / 8;
+  const WorkUnit wu = xcd_unit();
+  const int id = wu.tile, ks = wu.split;
   const int m0 = (id % mt) * BM, n0 = (id / mt) * BN;
   const int nw = n0 + 64 * w;              // this wave's first column
   const int nwl = min(nw, p.N - 64);       // the same, kept inside the matrix for loads
@@ -292,7 +290,7 @@ __global__ __launch_bounds__(256) void bf16t_kernel(const GemmParams p) {
 
   const int nkt = p.K / BK;
   const int kper = (nkt + p.ksplit - 1) / p.ksplit;
-  const int it0 = min(nkt, (int)blockIdx.y * kper), it1 = min(nkt, it0 + kper);
+  const int it0 = min(nkt, ks * kper), it1 = min(nkt, it0 + kper);
 
   auto issue_a = [&](int it, int st) {
     const uint8_t* a = gA + it * (BK * 2);
@@ -423,7 +421,7 @@ __global__ __launch_bounds__(256) void bf16t_kernel(const GemmParams p) {
     constexpr bool FULL = decltype(full_)::value;
     constexpr bool LOADS = MODE == C_F32_ACC || MODE == C_F32_RES;
     if (!FULL && nw >= p.N) return;
-    float* const out = MODE < 0 ? p.part + blockIdx.y * p.pstride : reinterpret_cast<float*>(p.C);
+    float* const out = MODE < 0 ? p.part + ks * p.pstride : reinterpret_cast<float*>(p.C);
     const int64_t ld = MODE < 0 ? (int64_t)p.N : p.ldc;
     const float* const src = MODE == C_F32_RES ? p.R : out;
     const int64_t lds = MODE == C_F32_RES ? p.ldr : ld;

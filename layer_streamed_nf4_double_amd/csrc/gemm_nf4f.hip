@@ -114,11 +114,10 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lr = lane & 31, hh = lane >> 5;
 
-  // ---- tile coordinates (XCD-aware: consecutive ids land on one XCD) ----
+  // ---- tile coordinates and k split (XCD-aware, split-major) ----
   const int mt = (p.M + FM - 1) / FM;
-  const int nblk = gridDim.x, b = blockIdx.x;
-  const int per = nblk / 8, rem = nblk % 8, x = b % 8;
-  const int id = x * per + min(x, rem) + b / 8;
+  const WorkUnit wu = xcd_unit();
+  const int id = wu.tile, ks = wu.split;
   const int m0 = (id % mt) * FM, n0 = (id / mt) * TN;
   const int Fh = p.N / 2;  // SwiGLU: the feature count F
   // weight row (W^T row, clamped into the matrix) of row rr of wave w's
@@ -172,10 +171,10 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
   const uint8_t* gC = reinterpret_cast<const uint8_t*>(p.B);
   const uint8_t* gM = reinterpret_cast<const uint8_t*>(p.absmax);
 
-  // split-k: blockIdx.y takes slices [it0, it1)
+  // split-k: split ks takes slices [it0, it1)
   const int nkt = p.K / FK;
   const int kper = (nkt + p.ksplit - 1) / p.ksplit;
-  const int it0 = min(nkt, (int)blockIdx.y * kper), it1 = min(nkt, it0 + kper);
+  const int it0 = min(nkt, ks * kper), it1 = min(nkt, it0 + kper);
 
   // the GROUP direct loads of slice it into LDS stage st
   auto issue = [&](int it, int st) {
@@ -273,7 +272,7 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], xf[i], acc[i][j], 0, 0, 0);
     }
   };
-  const bool ext = p.kext > 0 && blockIdx.y == 0;
+  const bool ext = p.kext > 0 && ks == 0;
 
   if (it1 > it0) {
     // prologue: slices it0 .. it0+2 (clamped) into stages 0 .. 2
@@ -380,7 +379,7 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
       }
     } else {
       constexpr bool LOADS = MODE == C_F32_ACC || MODE == C_F32_RES;
-      float* const out = MODE < 0 ? p.part + blockIdx.y * p.pstride
+      float* const out = MODE < 0 ? p.part + ks * p.pstride
                                   : reinterpret_cast<float*>(p.C);
       const int64_t ld = MODE < 0 ? (int64_t)p.N : p.ldc;
       const float* const src = MODE == C_F32_RES ? p.R : out;

@@ -74,11 +74,10 @@ __global__ __launch_bounds__(256) void nf4t_kernel(const GemmParams p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lr = lane & 31, hh = lane >> 5;
 
-  // ---- tile coordinates (XCD-aware: consecutive ids land on one XCD) ----
+  // ---- tile coordinates and k split (XCD-aware, split-major) ----
   const int mt = (p.M + TM - 1) / TM;
-  const int nblk = gridDim.x, b = blockIdx.x;
-  const int per = nblk / 8, rem = nblk % 8, x = b % 8;
-  const int id = x * per + min(x, rem) + b / 8;
+  const WorkUnit wu = xcd_unit();
+  const int id = wu.tile, ks = wu.split;
   const int m0 = (id % mt) * TM, n0 = (id / mt) * TN;
   const int nw = n0 + 64 * w;                // this wave's first column
   const int nwl = min(nw, p.N - 64);         // the same, kept inside the matrix for loads
@@ -123,10 +122,10 @@ __global__ __launch_bounds__(256) void nf4t_kernel(const GemmParams p) {
   const int64_t cstep = TK * crow;      // code bytes per slice
   const int64_t mstep = TK * mrow * 4;  // absmax bytes per slice
 
-  // split-k: blockIdx.y takes slices [it0, it1)
+  // split-k: split ks takes slices [it0, it1)
   const int nkt = p.K / TK;
   const int kper = (nkt + p.ksplit - 1) / p.ksplit;
-  const int it0 = min(nkt, (int)blockIdx.y * kper), it1 = min(nkt, it0 + kper);
+  const int it0 = min(nkt, ks * kper), it1 = min(nkt, it0 + kper);
 
   // the TGROUP direct loads of slice it into LDS stage st
   auto issue = [&](int it, int st) {
@@ -295,7 +294,7 @@ __global__ __launch_bounds__(256) void nf4t_kernel(const GemmParams p) {
 
   // ---- low-rank extension: extra k columns read directly as fragments ----
   const int lk = hh * 8;
-  if (p.kext > 0 && blockIdx.y == 0) {
+  if (p.kext > 0 && ks == 0) {
     for (int e0 = 0; e0 < p.kext; e0 += 16) {
       bf16x8 ax[8], bx[2];
 #pragma unroll
@@ -327,7 +326,7 @@ __global__ __launch_bounds__(256) void nf4t_kernel(const GemmParams p) {
     constexpr bool FULL = decltype(full_)::value;
     constexpr bool LOADS = MODE == C_F32_ACC || MODE == C_F32_RES;
     if (!FULL && nw >= p.N) return;
-    float* const out = MODE < 0 ? p.part + blockIdx.y * p.pstride
+    float* const out = MODE < 0 ? p.part + ks * p.pstride
                                 : reinterpret_cast<float*>(p.C);
     const int64_t ld = MODE < 0 ? (int64_t)p.N : p.ldc;
     const float* const src = MODE == C_F32_RES ? p.R : out;

@@ -61,6 +61,22 @@ LSN_DEV uint32_t lds_addr(T* q) {
 // hit 16 distinct 4-bank groups (and 8 consecutive rows 8 distinct ones)
 LSN_DEV int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// Work unit (tile id, k split) of this workgroup.  Workgroups go to the 8
+// XCDs round robin by linear id; each XCD takes a contiguous range of the
+// units ordered split-major, so the workgroups of one XCD share one split's
+// K range of the activations (a working set that fits its L2) besides
+// weight tiles.  Without a split this is the plain contiguous tile range.
+struct WorkUnit {
+  int tile, split;
+};
+LSN_DEV WorkUnit xcd_unit() {
+  const int X = gridDim.x, U = X * gridDim.y;
+  const int L = blockIdx.x + blockIdx.y * X;
+  const int x = L % 8, per = U / 8, rem = U % 8;
+  const int u = x * per + min(x, rem) + L / 8;
+  return {u % X, u / X};
+}
+
 // byte offset 8 * (byte p of code word q) into the level-pair table
 LSN_DEV uint32_t pair_off(uint32_t q, int p) {
   return ((q >> (8 * p)) & 0xFFu) << 3;
