@@ -437,3 +437,25 @@ def test_out_of_range_target_is_nan_not_a_read(torch):
     m.close()
     assert math.isnan(loss) and math.isnan(logp[5])
     assert np.all(np.isfinite(np.delete(logp, 5)))
+
+
+def test_serialized_run_equals_async_run(torch, tmp_path):
+    """The same SFT and DPO steps in a child process whose HIP runtime waits
+    before and after every kernel and every copy (AMD_SERIALIZE_KERNEL=3,
+    AMD_SERIALIZE_COPY=3: nothing overlaps, so no copy can race a kernel)
+    give the same bits as this process's asynchronous run, where record
+    copies overlap the layers' kernels."""
+    import subprocess
+    from tests import serial_run
+    ref = serial_run.run()
+    out = tmp_path / "serial.npz"
+    env = dict(os.environ, AMD_SERIALIZE_KERNEL="3", AMD_SERIALIZE_COPY="3")
+    say("[serialized] child process with serialized kernels and copies")
+    r = subprocess.run([sys.executable, "-u", os.path.join(os.path.dirname(__file__), "serial_run.py"),
+                        str(out)], env=env, capture_output=True, text=True, timeout=240)
+    say(r.stdout[-500:] + r.stderr[-1500:])
+    assert r.returncode == 0
+    got = np.load(out)
+    assert len(got.files) == len(ref)
+    for i, a in enumerate(ref):
+        assert np.array_equal(_bits(got[f"arr_{i}"]), _bits(a)), f"array {i} differs"
