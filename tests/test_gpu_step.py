@@ -744,3 +744,47 @@ def test_sft_qwen3b_layer_shape_vs_oracle(torch):
         for p in ("q", "v"):
             for u, v in zip(g[layer][p], gr[layer][p]):
                 assert np.array_equal(_bits(np.asarray(u)), _bits(np.asarray(v)))
+
+
+def test_dpo_qwen3b_layer_shape_vs_oracle_and_resident(torch):
+    """One streamed DPO step (fused reference pass) on a 2 x 512-token pair at
+    the 3B layer shape (tied embedding, GQA 16/2, FFN 11008), two layers and
+    a 1024-entry vocabulary, against the oracle; the same step with the base
+    resident gives the same bits (loss, z, the four sums, both log-prob
+    vectors, A, B, dA, dB)."""
+    w = dict(synth.WORKLOADS["qwen2.5-3b-shaped"], n_layers=2, vocab=1024)
+    S, beta = w["seq_len"], synth.DPO_PAIR["beta"]
+    P = synth.dpo_prompt_len(w)
+    ch, rj = synth.dpo_pair(w)
+    tok, tgt = _dev_tokens(torch, np.stack([ch, rj]))
+    say("[dpo-3b-shape] oracle")
+    cfg, layers, lora, head = oracle_model(w, b_zero=False)
+    od = om.dpo_step(cfg, layers, lora, head, ch, rj, P, beta, LR)
+    runs = {}
+    for mode in ("stream_host", "resident"):
+        say(f"[dpo-3b-shape] gpu {mode}")
+        m = gpu_model(w, mode, b_zero=False, max_tokens=2 * S)
+        out = m.dpo_step(tok, tgt, S, P, beta, LR)
+        m.sync()
+        runs[mode] = (out[:6].cpu().numpy().copy(), m.logp[:2 * S].cpu().numpy().copy(),
+                      m.logp_ref[:2 * S].cpu().numpy().copy(), _grads(m, w))
+        m.close()
+    o, logp, logp_ref, g = runs["stream_host"]
+    lbar, zbar = _dpo_bars(od, beta)
+    assert abs(o[0] - od["loss"]) <= lbar
+    assert abs(o[1] - od["z"]) <= zbar
+    assert_close(logp, od["logp_policy"], 2e-2, "policy logp")
+    assert_close(logp_ref, od["logp_ref"], 2e-2, "reference logp")
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            _, _, dA, dB = g[layer][p]
+            odA, odB = od["grads"][layer][p]
+            assert_close(dA, odA, 5e-2, f"DPO dA L{layer} {p}")
+            assert_close(dB, odB, 5e-2, f"DPO dB L{layer} {p}")
+    r = runs["resident"]
+    for a, b in zip((o, logp, logp_ref), r[:3]):
+        assert np.array_equal(_bits(a), _bits(b))
+    for layer in range(w["n_layers"]):
+        for p in ("q", "v"):
+            for u, v in zip(g[layer][p], r[3][layer][p]):
+                assert np.array_equal(_bits(np.asarray(u)), _bits(np.asarray(v)))
