@@ -85,9 +85,19 @@ def _layer_records(w):
         return list(ex.map(one, range(w["n_layers"])))
 
 
-def _model(w, mode, records, head):
+_RECORDS = {}
+
+
+def _records_8b(w):
+    """The 32 layer records, quantized once for the tests of this module."""
+    if "8b" not in _RECORDS:
+        _RECORDS["8b"] = _layer_records(w)
+    return _RECORDS["8b"]
+
+
+def _model(w, mode, records, head, max_tokens=None):
     from layer_streamed_nf4_double_amd.trainer import LayerStreamedLoRA
-    m = LayerStreamedLoRA(w, mode)
+    m = LayerStreamedLoRA(w, mode, max_tokens=max_tokens)
     ones = np.full(w["hidden"], BF16_ONE, np.uint16)
     for layer, (codes, absmax) in enumerate(records):
         m.load_layer(layer, codes, absmax, ones, ones)
@@ -117,7 +127,7 @@ def test_full_depth_streamed_equals_resident(torch):
     from layer_streamed_nf4_double_amd.trainer import sft_targets
     w = W8
     say("[full-8b] quantize 32 layers")
-    records = _layer_records(w)
+    records = _records_8b(w)
     head = synth.head_tables(w)
     tokens = synth.sft_tokens(w)
     tok = torch.from_numpy(tokens.reshape(-1).astype(np.int32)).cuda()
@@ -172,3 +182,48 @@ def test_full_depth_streamed_equals_resident(torch):
     # to the caching allocator's granularity (a large allocation's segment is
     # rounded up to 2 MiB; an unsplit tail under 1 MiB counts as allocated)
     assert abs((peak_r - peak_s) - (w["n_layers"] - 2) * rb) < (1 << 20), (peak_r - peak_s, rb)
+
+
+def test_full_depth_dpo_streamed_equals_resident(torch):
+    """One DPO step of the full 8B workload (one pair of 512-token sequences
+    sharing a 128-token prompt, beta 0.1, the reference forward fused with
+    the policy forward on each streamed record) with the base resident, then
+    streamed from pinned host memory: loss, z and the four log-prob sums,
+    all 1024 policy and reference log-probs, and the adapter gradients of
+    the first and last layers are the same bits -- the pages' bar stated for
+    the DPO reference pass itself ("Show HN: Fine-tune an 8B model on a 4 GB
+    laptop GPU", first paragraph); the streamed step copies 2L - 2 records,
+    as many as an SFT step."""
+    import gc
+    w = W8
+    records = _records_8b(w)
+    head = synth.head_tables(w)
+    S, beta = w["seq_len"], synth.DPO_PAIR["beta"]
+    P = synth.dpo_prompt_len(w)
+    ch, rj = synth.dpo_pair(w)
+    from layer_streamed_nf4_double_amd.trainer import device_batch, sft_targets
+    pair = np.stack([ch, rj])
+    tok, tgt = device_batch(pair, sft_targets(pair), w["vocab"])
+    out = {}
+    for mode in ("resident", "stream_host"):
+        gc.collect()
+        torch.cuda.empty_cache()
+        say(f"[full-8b dpo] {mode}")
+        m = _model(w, mode, records, head, max_tokens=2 * S)
+        o = m.dpo_step(tok, tgt, S, P, beta, None)
+        m.sync()
+        grads = {(l, p): m.get_lora(l, p)[2:] for l in (0, w["n_layers"] - 1) for p in ("q", "v")}
+        out[mode] = (o[:6].cpu().numpy().copy(), m.logp[:2 * S].cpu().numpy().copy(),
+                     m.logp_ref[:2 * S].cpu().numpy().copy(), grads, m.stats()[0])
+        m.close()
+        del m
+    r, s_ = out["resident"], out["stream_host"]
+    say(f"[full-8b dpo] loss {r[0][0]:.6f} z {r[0][1]:.6f}")
+    assert np.isfinite(r[0]).all() and r[0][1] != 0
+    for a, b in zip(r[:3], s_[:3]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    for k in r[3]:
+        for x, y in zip(r[3][k], s_[3][k]):
+            assert np.any(x != 0), k
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), k
+    assert s_[4] == 2 * w["n_layers"] - 2, s_[4]
