@@ -43,6 +43,17 @@
 // are dequantized just in time, one k-step ahead of their MFMAs: each code
 // byte indexes a 256-entry LDS table holding the levels of its two nibbles.
 //
+// Producer wave (256 x 128 tile).  With one wave per SIMD every instruction
+// a wave issues sits in line with its MFMAs, and a slice's eleven direct
+// loads per wave cost its last k-step about 200 cycles (clock stamps).  The
+// 256 x 128 form therefore runs a fifth wave that issues every direct load
+// of the workgroup (32 activation, 4 code, 4 absmax per slice), waits for
+// them and meets the four MFMA waves at the same one barrier per slice; the
+// MFMA waves issue no memory instruction in the main loop and read the next
+// slice's codes after that barrier, at the start of the last k-step.  (Its
+// 208 registers let a second wave share one SIMD; the 256 x 256 form, with
+// 256 accumulators per lane, keeps one wave per SIMD and its own loads.)
+//
 // SwiGLU epilogue (C_SWIGLU, 256 x 256 tile only).  The weight is the fused
 // gate|up record [2F, K]; a tile then covers gate columns n0 .. n0+127 and
 // the same up columns F+n0 .. F+n0+127: wave w's column tile 0 holds gate
@@ -95,7 +106,11 @@ LSN_DEV bf16x8 dequant8(uint32_t q, float a, Pair pair) {
 // raw split-k partial sums; one instantiation per form keeps the epilogue a
 // single straight-line path per tile kind.
 template <int MODE, int NT>
-__global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
+__global__ __launch_bounds__(NT == 1 ? 320 : 256) void nf4f_kernel(const GemmParams p) {
+  // NT = 1: a fifth wave issues every direct load of the workgroup (the
+  // producer); the four MFMA waves issue none in the main loop
+  constexpr bool PW = NT == 1;
+  constexpr int GP = 32 + 4 + 4;  // producer loads per slice
   constexpr int FN = Shape<NT>::FN, C_STAGE = Shape<NT>::C_STAGE, GROUP = Shape<NT>::GROUP;
   constexpr int NS = 8 * NT;  // MFMA slots per k-step
   constexpr bool SW = MODE == C_SWIGLU;
@@ -129,7 +144,8 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
 
   // entry b: the levels of code byte b (low nibble: even element, high
   // nibble: odd element); one 8-byte read dequantizes two elements
-  sPair[threadIdx.x] = make_float2(p.levels[threadIdx.x & 15], p.levels[threadIdx.x >> 4]);
+  if (threadIdx.x < 256)
+    sPair[threadIdx.x] = make_float2(p.levels[threadIdx.x & 15], p.levels[threadIdx.x >> 4]);
   auto pair = [&](uint32_t b8) {  // b8 = 8 * code byte
     return *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(sPair) + b8);
   };
@@ -188,6 +204,79 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
     for (int i = 0; i < NT; ++i) dma16(c, offC[i], lc + i * 1024);
     dma4(gM + it * 4, offM, lds_addr(&sM[st][w * 64]));
   };
+
+  if constexpr (PW) {
+    if (w == 4) {  // ---- the producer ----
+      // activation load i fills stage rows 8 i .. 8 i + 7 (lane -> row + lane
+      // / 8, physical chunk lane % 8); eight loads per M0 at offsets 1024 i -
+      // 4096, so the per-lane offsets have that subtracted
+      uint32_t oA[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int r = i * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        const int row = min(m0 + r, p.M - 1);
+        oA[i] = (uint32_t)(((int64_t)row * p.lda + c * 8) * 2) + 4096u - 1024u * (i & 7);
+      }
+      // code load i fills MFMA wave i's 32 rows (lane -> row + lane / 2,
+      // physical half lane % 2); absmax load i fills wave i's 64-entry region
+      uint32_t oC[4], oM[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = i * 32 + (lane >> 1);
+        const int h = (lane & 1) ^ ((r >> 3) & 1);
+        oC[i] = (uint32_t)((int64_t)min(n0 + 32 * i + (lane >> 1), p.N - 1) * (p.K / 2) + h * 16);
+        oM[i] = (uint32_t)((int64_t)min(n0 + 32 * i + lane, p.N - 1) * (p.K / FK) * 4);
+      }
+      const uint8_t* gA = reinterpret_cast<const uint8_t*>(p.A);
+      const uint8_t* gC = reinterpret_cast<const uint8_t*>(p.B);
+      const uint8_t* gM = reinterpret_cast<const uint8_t*>(p.absmax);
+      const int nkt = p.K / FK;
+      const int kper = (nkt + p.ksplit - 1) / p.ksplit;
+      const int it0 = min(nkt, ks * kper), it1 = min(nkt, it0 + kper);
+      if (it1 <= it0) return;  // (the MFMA waves then take no barrier either)
+      auto pissue = [&](int it, int st) {
+        const uint8_t* a = gA + it * (FK * 2);
+        const uint32_t la = lds_addr(sA[st]);
+        auto a8 = [&](auto g_) {
+          constexpr int g = decltype(g_)::value;
+          set_m0(la + g * 8192 + 4096);
+          dma16_at<-4096>(a, oA[8 * g + 0]);
+          dma16_at<-3072>(a, oA[8 * g + 1]);
+          dma16_at<-2048>(a, oA[8 * g + 2]);
+          dma16_at<-1024>(a, oA[8 * g + 3]);
+          dma16_at<0>(a, oA[8 * g + 4]);
+          dma16_at<1024>(a, oA[8 * g + 5]);
+          dma16_at<2048>(a, oA[8 * g + 6]);
+          dma16_at<3072>(a, oA[8 * g + 7]);
+        };
+        a8(std::integral_constant<int, 0>{});
+        a8(std::integral_constant<int, 1>{});
+        a8(std::integral_constant<int, 2>{});
+        a8(std::integral_constant<int, 3>{});
+        const uint8_t* c = gC + it * (FK / 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(c, oC[i], lds_addr(sC[st]) + i * 1024);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma4(gM + it * 4, oM[i], lds_addr(&sM[st][i * 64]));
+      };
+      // slices it0, it0 + 1 (clamped); slice it0 landed; then it0 + 2
+      pissue(it0, 0);
+      pissue(min(it0 + 1, it1 - 1), 1);
+      LSN_WAIT_VM(GP);
+      pissue(min(it0 + 2, it1 - 1), 2);
+      __syncthreads();
+      int st = 0;
+      for (int t = it0; t < it1; ++t) {
+        LSN_WAIT_VM(GP);  // slice t + 1 landed (only slice t + 2's loads in flight)
+        __syncthreads();  // the MFMA waves are done with stage st
+        pissue(min(t + 3, it1 - 1), st);
+        st = st == NST - 1 ? 0 : st + 1;
+      }
+      LSN_WAIT_VM(0);
+      return;
+    }
+  }
 
   // ---- per-lane LDS read offsets ----
   // activation fragment of row tile i, k-step kk: row i*32 + lr, logical chunk
@@ -249,6 +338,37 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
     }
   };
   auto none = [](int) {};
+  // PW, the last k-step of a slice (k-step 3, after the barrier): the next
+  // slice's codes are read here (slot 0), their level pairs in slots 2-3 and
+  // the products in slots 5-6, so the next k-step's weight fragment is ready
+  auto kstep3pw = [&](const uint8_t* an, int st1) {
+    float lvv[8];
+    u32x4 r;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      acc[s][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq[1][0], af[1][s], acc[s][0], 0, 0, 0);
+      af[0][s] = *reinterpret_cast<const bf16x8*>(an + s * 4096);
+      if (s == 0) read_codes(cqn, can, st1);
+      if (s == 2 || s == 3) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int ph = 2 * (s - 2) + u;
+          const float2 l = pair(pair_off(cqn[0][0], ph));
+          lvv[2 * ph] = l.x;
+          lvv[2 * ph + 1] = l.y;
+        }
+      }
+      if (s == 5 || s == 6) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int pp = 2 * (s - 5) + u;
+          r[pp] = pack_bf16x2(lvv[2 * pp] * can[0], lvv[2 * pp + 1] * can[0]);
+        }
+        if (s == 6) bq[0][0] = __builtin_bit_cast(bf16x8, r);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
   // ---- low-rank extension: extra k columns read directly as fragments ----
   // (split 0 only), added before the main loop: its loads are issued after
@@ -276,11 +396,13 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
 
   if (it1 > it0) {
     // prologue: slices it0 .. it0+2 (clamped) into stages 0 .. 2
-    issue(it0, 0);
-    issue(min(it0 + 1, it1 - 1), 1);
-    issue(min(it0 + 2, it1 - 1), 2);
+    if constexpr (!PW) {
+      issue(it0, 0);
+      issue(min(it0 + 1, it1 - 1), 1);
+      issue(min(it0 + 2, it1 - 1), 2);
+    }
     if (ext) extension();
-    LSN_WAIT_VM(2 * GROUP);
+    if constexpr (!PW) LSN_WAIT_VM(2 * GROUP);
     __syncthreads();
     read_codes(cq, ca, 0);
     {
@@ -302,6 +424,18 @@ __global__ __launch_bounds__(256) void nf4f_kernel(const GemmParams p) {
       const int st1 = st == NST - 1 ? 0 : st + 1;
       kstep(std::integral_constant<int, 0>{}, sA[st] + (sa0 ^ 16), cq, ca, 1, none);
       kstep(std::integral_constant<int, 1>{}, sA[st] + (sa0 ^ 32), cq, ca, 2, none);
+      if constexpr (PW) {
+        kstep(std::integral_constant<int, 2>{}, sA[st] + (sa0 ^ 48), cq, ca, 3, none);
+        __syncthreads();  // slice t + 1 landed (the producer waited); stage st is free
+        kstep3pw(sA[st1] + sa0, st1);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          cq[j] = cqn[j];
+          ca[j] = can[j];
+        }
+        st = st1;
+        continue;
+      }
       LSN_WAIT_VM(GROUP);
       kstep(std::integral_constant<int, 2>{}, sA[st] + (sa0 ^ 48), cq, ca, 3,
             [&](int s) { if (s == 4 * NT) read_codes(cqn, can, st1); });
@@ -496,16 +630,17 @@ template <int NT>
 static void nf4f_launch_t(const GemmParams& p, hipStream_t s) {
   const int tiles = ((p.M + FM - 1) / FM) * ((p.N + Shape<NT>::FN - 1) / Shape<NT>::FN);
   const dim3 grid(tiles, p.ksplit, 1);
+  const dim3 blk(NT == 1 ? 320 : 256);
   if (p.ksplit > 1)
-    hipExtLaunchKernelGGL((nf4f_kernel<-1, NT>), grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+    hipExtLaunchKernelGGL((nf4f_kernel<-1, NT>), grid, blk, 0, s, p.ev0, p.ev1, 0, p);
   else if (p.cmode == C_F32)
-    hipExtLaunchKernelGGL((nf4f_kernel<C_F32, NT>), grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+    hipExtLaunchKernelGGL((nf4f_kernel<C_F32, NT>), grid, blk, 0, s, p.ev0, p.ev1, 0, p);
   else if (p.cmode == C_F32_ACC)
-    hipExtLaunchKernelGGL((nf4f_kernel<C_F32_ACC, NT>), grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+    hipExtLaunchKernelGGL((nf4f_kernel<C_F32_ACC, NT>), grid, blk, 0, s, p.ev0, p.ev1, 0, p);
   else if (p.cmode == C_F32_RES)
-    hipExtLaunchKernelGGL((nf4f_kernel<C_F32_RES, NT>), grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+    hipExtLaunchKernelGGL((nf4f_kernel<C_F32_RES, NT>), grid, blk, 0, s, p.ev0, p.ev1, 0, p);
   else
-    hipExtLaunchKernelGGL((nf4f_kernel<C_BF16, NT>), grid, dim3(256), 0, s, p.ev0, p.ev1, 0, p);
+    hipExtLaunchKernelGGL((nf4f_kernel<C_BF16, NT>), grid, blk, 0, s, p.ev0, p.ev1, 0, p);
 }
 
 hipError_t nf4f_launch(GemmParams p, hipStream_t s) {
