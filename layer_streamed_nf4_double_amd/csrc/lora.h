@@ -31,20 +31,55 @@ struct LoraMM {
 // which share their input x: t_p = x A_p for p < n, in one launch.
 //   x bf16 [R, K] (row stride ldx); AT_p = bf16(A_p)^T [16, K] (rows j >= r
 //   zero; lora_at builds it); t_p fp32 [R, r] row-major;
-//   ext[row, 16 p + j] = bf16(ext_scale t_p(row, j)) for j < r, 0 for r <= j < 16.
+//   ext (may be null) [row, 16 p + j] = bf16(ext_scale t_p(row, j)) for j < r,
+//   0 for r <= j < 16.
+//   With AF[0] set (n == 1 only), A is read as fp32 [K, r] row-major from
+//   AF[0] (rounded to bf16 as it is loaded) and AT is not used.
+//   conv (optional): a bf16 row conversion, as lora_ext does, by extra
+//   workgroups of the same launch.
+struct ExtJob {
+  // out[row*ld + c0 + j*oj] = bf16(W[row*srow + j*sj]) for j < r, 0 for
+  // r <= j < 16, rows [0, rows); set by the launcher: vec (oj == 1 and every
+  // row's 16 outputs are 16-byte aligned) and wbytes (W's extent)
+  const float* W = nullptr;
+  int64_t srow = 0, sj = 0;
+  int rows = 0, r = 0;
+  uint16_t* out = nullptr;
+  int64_t ld = 0, oj = 1;
+  int c0 = 0;
+  int vec = 0;
+  uint32_t wbytes = 0;
+};
+// Up to 6 row conversions in one launch (one thread per row).
+struct ExtBatch {
+  ExtJob job[6];
+  int n = 0;
+};
+hipError_t lora_convert(const ExtBatch& b, hipStream_t s);
+// the job of lora_at (AT = bf16(A)^T [16, K] from A fp32 [K, r], rows j >= r
+// zero)
+ExtJob lora_at_job(const float* A, int K, int r, uint16_t* AT);
 struct LoraDown {
   const uint16_t* X = nullptr;
   int64_t ldx = 0;
   int R = 0, K = 0, r = 0, n = 0;
   const uint16_t* AT[3] = {};
+  const float* AF[3] = {};
   float* t[3] = {};
   uint16_t* ext = nullptr;
   int64_t ld_ext = 0;
   float ext_scale = 1.f;
+  ExtJob conv;
+  // optional split-k scratch (lora_down_partial_floats); without it, or too
+  // small, one workgroup per 16 rows takes the whole k range
+  float* part = nullptr;
+  int64_t part_floats = 0;
 };
 hipError_t lora_down(const LoraDown& a, hipStream_t s);
-// AT = bf16(A)^T [16, K] from A fp32 [K, r] row-major (rows j >= r zero)
-void lora_at(const float* A, int K, int r, uint16_t* AT, hipStream_t s);
+// floats of split-k scratch lora_down wants for these sizes (0: no split),
+// and a bound on it for every R' <= R and every K
+int64_t lora_down_partial_floats(int R, int K, int n);
+int64_t lora_down_partial_floats_max(int R, int n);
 
 // u_p = dy_p B_p^T for the n adapted projections of one group, in one launch
 // (the first step of the branch's backward):

@@ -77,8 +77,7 @@ __global__ void lora_reduce_k(const LoraMM a, int nsplit, const float* __restric
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)a.R * 16) return;
   const int row = (int)(i >> 4), j = (int)(i & 15);
-  float v = 0.f;
-  for (int s = 0; s < nsplit; ++s) v += partial[((int64_t)s * a.R + row) * 16 + j];
+  const float v = ordered_sum(partial + (int64_t)row * 16 + j, (int64_t)a.R * 16, nsplit);
   lora_store(a, row, j, v);
 }
 
@@ -102,47 +101,108 @@ int64_t lora_mm_partial_floats(int R, int K) {
 // One workgroup of 16 waves owns 16 rows; wave w takes the 32-deep k steps
 // w, w + 16, ... for every adapter at once, so each x fragment (one 16-byte
 // load where rows are aligned) feeds n MFMAs; the waves' sums are added in
-// LDS in wave order.  No split-k: one launch per group.
+// LDS in wave order.  No split-k: one launch per group.  The launch has few
+// workgroups, so it is bound by load latency, not bandwidth: a wave issues
+// the loads of DB k steps (2 where it loads element by element) before their
+// MFMAs, which still run in k order.  Workgroups past the row blocks do the
+// launch's row conversion (ExtJob), one row per thread.
 constexpr int DW = 16;  // waves per workgroup of lora_down_k
+constexpr int DB = 4;   // k steps per batch of loads
 
-template <bool VEC>
-__global__ __launch_bounds__(DW * 64) void lora_down_k(const LoraDown a) {
+LSN_DEV void conv_row(const ExtJob& c, int64_t row) {
+  if (row < c.rows)
+    ext_row(buf_rsrc(c.W, c.wbytes), c.srow, c.sj, row, c.r, c.out + row * c.ld + c.c0, c.oj,
+            c.vec);
+}
+
+// blockIdx.y: the k range [y kchunk, (y + 1) kchunk) of a split launch, whose
+// sums go to part (lora_down_reduce_k adds them in split order)
+template <bool VEC, bool AF32>
+__global__ __launch_bounds__(DW * 64) void lora_down_k(const LoraDown a, int nrb, int kchunk,
+                                                       float* __restrict__ part) {
   __shared__ float red[DW][3][16][17];
+  if ((int)blockIdx.x >= nrb) {
+    conv_row(a.conv, (int64_t)(blockIdx.x - nrb) * (DW * 64) + threadIdx.x);
+    return;
+  }
+  const int kbeg = blockIdx.y * kchunk, kend = min(a.K, kbeg + kchunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row0 = blockIdx.x * 16;
   const int lr = lane & 15, lk = (lane >> 4) * 8;
-  const int row = row0 + lr;
-  const bool rin = row < a.R;
+  const bool jin = lr < a.r;
+  constexpr int NQ = AF32 ? 1 : 3;   // adapters (fp32 A: one)
+  constexpr int NB = VEC ? DB : 2;  // element-wise loads: fewer in flight
+  // Buffer loads: an element outside its operand reads 0 with no branch (a
+  // load under a divergent branch is waited for before the branch joins,
+  // which would serialize the batch).  X's resource covers this block's rows,
+  // so lanes past the last row read past its end.
+  const int nrow = min(16, a.R - row0);
+  const buf_t xr = buf_rsrc(a.X + (int64_t)row0 * a.ldx, (uint32_t)(nrow * a.ldx * 2));
+  const uint32_t xo = (uint32_t)(lr * a.ldx) * 2;
+  buf_t wr[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+    wr[q] = AF32 ? buf_rsrc(a.AF[q], (uint32_t)(a.K * a.r) * 4)
+                 : buf_rsrc(q < a.n ? a.AT[q] : a.AT[0], (uint32_t)(16 * a.K) * 2);
   f32x4 acc[3] = {};
-  for (int k0 = wave * KSTEP; k0 < a.K; k0 += DW * KSTEP) {
-    bf16x8 xf;
-    if (VEC) {
-      // K % 8 == 0: a lane's eight columns are all inside the row or all past it
-      xf = (rin && k0 + lk < a.K)
-               ? *reinterpret_cast<const bf16x8*>(a.X + (int64_t)row * a.ldx + k0 + lk)
-               : bf16x8{};
-    } else {
+  for (int kb = kbeg + wave * KSTEP; kb < kend; kb += NB * DW * KSTEP) {
+    // all loads of the batch first (raw values), then the conversions and
+    // MFMAs: the scheduling barrier keeps the compiler from interleaving
+    // them, which would wait for each k step's loads in turn
+    bf16x8 xf[NB], wf[NB][3];
+    float af[NB][8];                   // fp32 A
+    uint16_t xs[NB][8], ws[NB][3][8];  // element-wise loads
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = k0 + lk + i;
-        xf[i] = (bf16)((rin && k < a.K) ? bf16_to_f32(a.X[(int64_t)row * a.ldx + k]) : 0.f);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      if (q >= a.n) break;
-      bf16x8 wf;
+    for (int u = 0; u < NB; ++u) {
+      const int k0 = kb + u * DW * KSTEP;
+      // VEC: K and the k ranges are multiples of 8, so a lane's eight
+      // columns are all inside the range or all past it
+      const bool kin8 = k0 + lk < kend;
       if (VEC) {
-        wf = (k0 + lk < a.K) ? *reinterpret_cast<const bf16x8*>(a.AT[q] + (int64_t)lr * a.K + k0 + lk)
-                             : bf16x8{};
+        xf[u] = buf_bf16x8(xr, kin8 ? xo + (uint32_t)(k0 + lk) * 2 : BUF_OOB);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int k = k0 + lk + i;
-          wf[i] = (bf16)(k < a.K ? bf16_to_f32(a.AT[q][(int64_t)lr * a.K + k]) : 0.f);
+          xs[u][i] = buf_u16(xr, k < kend ? xo + (uint32_t)k * 2 : BUF_OOB);
         }
       }
-      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, wf, acc[q], 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        if (!AF32 && q >= a.n) break;  // fp32 A: n == 1
+        if (AF32) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int k = k0 + lk + i;
+            af[u][i] = buf_f32(wr[q], jin && k < kend ? (uint32_t)(k * a.r + lr) * 4 : BUF_OOB);
+          }
+        } else if (VEC) {
+          wf[u][q] = buf_bf16x8(wr[q], kin8 ? (uint32_t)(lr * a.K + k0 + lk) * 2 : BUF_OOB);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int k = k0 + lk + i;
+            ws[u][q][i] = buf_u16(wr[q], k < kend ? (uint32_t)(lr * a.K + k) * 2 : BUF_OOB);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (!VEC) xf[u][i] = __builtin_bit_cast(bf16, xs[u][i]);
+        if (AF32) wf[u][0][i] = (bf16)af[u][i];
+      }
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        if (!AF32 && q >= a.n) break;
+        if (!AF32 && !VEC)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wf[u][q][i] = __builtin_bit_cast(bf16, ws[u][q][i]);
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[u], wf[u][q], acc[q], 0, 0, 0);
+      }
     }
   }
   // lane holds column j = lane % 16, rows (lane / 16) * 4 + i
@@ -158,30 +218,122 @@ __global__ __launch_bounds__(DW * 64) void lora_down_k(const LoraDown a) {
   float v = 0.f;
 #pragma unroll
   for (int w = 0; w < DW; ++w) v += red[w][q][rr][j];
+  if (gridDim.y > 1) {
+    part[(((int64_t)blockIdx.y * a.n + q) * a.R + orow) * 16 + j] = v;
+    return;
+  }
   if (j < a.r) a.t[q][(int64_t)orow * a.r + j] = v;
-  a.ext[(int64_t)orow * a.ld_ext + 16 * q + j] = (j < a.r) ? f32_to_bf16_bits(a.ext_scale * v) : 0;
+  if (a.ext)
+    a.ext[(int64_t)orow * a.ld_ext + 16 * q + j] = (j < a.r) ? f32_to_bf16_bits(a.ext_scale * v) : 0;
 }
 
-__global__ void lora_at_k(const float* __restrict__ A, int K, int r, uint16_t* __restrict__ AT) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)16 * K) return;
-  const int j = (int)(i / K), k = (int)(i % K);
-  AT[i] = j < r ? f32_to_bf16_bits(A[(int64_t)k * r + j]) : 0;
+// the launcher's fields of a conversion job; false if W's extent does not
+// fit the 32-bit offsets of the buffer loads
+static bool prep_job(ExtJob& c) {
+  c.vec = c.oj == 1 && c.ld % 8 == 0 && c.c0 % 8 == 0 && ((uintptr_t)c.out & 15) == 0;
+  const int64_t ext =
+      c.rows > 0 && c.r > 0 ? ((int64_t)(c.rows - 1) * c.srow + (int64_t)(c.r - 1) * c.sj + 1) * 4 : 0;
+  if (ext >= BUF_OOB) return false;
+  c.wbytes = (uint32_t)ext;
+  return true;
 }
 
-void lora_at(const float* A, int K, int r, uint16_t* AT, hipStream_t s) {
-  const int64_t n = (int64_t)16 * K;
-  hipLaunchKernelGGL(lora_at_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, A, K, r, AT);
+__global__ __launch_bounds__(256) void lora_convert_k(const ExtBatch b) {
+  const ExtJob& c = b.job[blockIdx.y];
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row < c.rows)
+    ext_row(buf_rsrc(c.W, c.wbytes), c.srow, c.sj, row, c.r, c.out + row * c.ld + c.c0, c.oj,
+            c.vec);
 }
+
+hipError_t lora_convert(const ExtBatch& b0, hipStream_t s) {
+  if (b0.n < 0 || b0.n > 6) return hipErrorInvalidValue;
+  ExtBatch b = b0;
+  int rmax = 0;
+  for (int i = 0; i < b.n; ++i) {
+    if (b.job[i].r < 0 || b.job[i].r > 16 || !prep_job(b.job[i])) return hipErrorInvalidValue;
+    rmax = std::max(rmax, b.job[i].rows);
+  }
+  if (b.n == 0 || rmax <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lora_convert_k, dim3((unsigned)((rmax + 255) / 256), b.n), dim3(256), 0, s, b);
+  return hipGetLastError();
+}
+
+ExtJob lora_at_job(const float* A, int K, int r, uint16_t* AT) {
+  // row k of the job is column k of AT: AT[j*K + k] = bf16(A[k*r + j])
+  return ExtJob{A, r, 1, K, r, AT, 1, K, 0, 0};
+}
+
+// the split sums of a split lora_down_k, added in split order; workgroups
+// past nred do the launch's row conversion
+__global__ __launch_bounds__(256) void lora_down_reduce_k(const LoraDown a, int ns, int nred,
+                                                          const float* __restrict__ part) {
+  if ((int)blockIdx.x >= nred) {
+    conv_row(a.conv, (int64_t)(blockIdx.x - nred) * 256 + threadIdx.x);
+    return;
+  }
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (q, row, j)
+  if (i >= (int64_t)a.n * a.R * 16) return;
+  const int q = (int)(i / ((int64_t)a.R * 16)), j = (int)(i & 15);
+  const int64_t row = (i >> 4) % a.R;
+  const float v = ordered_sum(part + i, (int64_t)a.n * a.R * 16, ns);
+  if (j < a.r) a.t[q][row * a.r + j] = v;
+  if (a.ext) a.ext[row * a.ld_ext + 16 * q + j] = (j < a.r) ? f32_to_bf16_bits(a.ext_scale * v) : 0;
+}
+
+// k split of lora_down: about 256 workgroups, at least DW k steps per split
+static void down_split(int R, int K, int* ns, int* kchunk) {
+  const int nrb = (R + 15) / 16;
+  int s = std::max(1, std::min({8, 256 / std::max(nrb, 1), (K + DW * KSTEP - 1) / (DW * KSTEP)}));
+  int kc = (K + s - 1) / s;
+  kc = (kc + DW * KSTEP - 1) / (DW * KSTEP) * (DW * KSTEP);
+  *kchunk = kc;
+  *ns = (K + kc - 1) / kc;
+}
+
+int64_t lora_down_partial_floats(int R, int K, int n) {
+  int ns, kc;
+  down_split(R, K, &ns, &kc);
+  return ns > 1 ? (int64_t)ns * n * R * 16 : 0;
+}
+
+int64_t lora_down_partial_floats_max(int R, int n) { return (int64_t)8 * n * R * 16; }
 
 hipError_t lora_down(const LoraDown& a, hipStream_t s) {
-  if (a.R <= 0 || a.n <= 0) return hipSuccess;
-  if (a.n > 3 || a.r > 16) return hipErrorInvalidValue;
+  if (a.n < 0 || a.n > 3 || a.r > 16 || (a.n > 0 && a.R > 0 && a.r <= 0)) return hipErrorInvalidValue;
+  const bool af32 = a.n > 0 && a.AF[0] != nullptr;
+  if (af32 && a.n != 1) return hipErrorInvalidValue;
+  // byte offsets of the buffer loads are 32-bit
+  if ((int64_t)16 * a.ldx * 2 >= BUF_OOB || (int64_t)16 * a.K * 4 >= BUF_OOB)
+    return hipErrorInvalidValue;
   bool vec = a.K % 8 == 0 && a.ldx % 8 == 0 && ((uintptr_t)a.X & 15) == 0;
-  for (int q = 0; q < a.n; ++q) vec = vec && ((uintptr_t)a.AT[q] & 15) == 0;
-  const dim3 grid((a.R + 15) / 16);
-  if (vec) hipLaunchKernelGGL(lora_down_k<true>, grid, dim3(DW * 64), 0, s, a);
-  else hipLaunchKernelGGL(lora_down_k<false>, grid, dim3(DW * 64), 0, s, a);
+  for (int q = 0; q < a.n; ++q)
+    vec = vec && (af32 ? a.AF[q] != nullptr : ((uintptr_t)a.AT[q] & 15) == 0);
+  const int nrb = a.n > 0 && a.R > 0 ? (a.R + 15) / 16 : 0;
+  const int ncb = a.conv.rows > 0 ? (a.conv.rows + DW * 64 - 1) / (DW * 64) : 0;
+  if (nrb + ncb == 0) return hipSuccess;
+  LoraDown b = a;
+  if (b.conv.r < 0 || b.conv.r > 16 || !prep_job(b.conv)) return hipErrorInvalidValue;
+  int ns = 1, kc = std::max(a.K, 1);
+  if (nrb > 0 && a.part) {
+    down_split(a.R, a.K, &ns, &kc);
+    if ((int64_t)ns * a.n * a.R * 16 > a.part_floats) ns = 1, kc = std::max(a.K, 1);
+  }
+  // unsplit: the row conversion rides on this launch; split: on the reduction's
+  const dim3 grid(ns > 1 ? nrb : nrb + ncb, ns), blk(DW * 64);
+  if (af32) {
+    if (vec) hipLaunchKernelGGL((lora_down_k<true, true>), grid, blk, 0, s, b, nrb, kc, a.part);
+    else hipLaunchKernelGGL((lora_down_k<false, true>), grid, blk, 0, s, b, nrb, kc, a.part);
+  } else {
+    if (vec) hipLaunchKernelGGL((lora_down_k<true, false>), grid, blk, 0, s, b, nrb, kc, a.part);
+    else hipLaunchKernelGGL((lora_down_k<false, false>), grid, blk, 0, s, b, nrb, kc, a.part);
+  }
+  if (ns > 1) {
+    const int nred = (int)(((int64_t)a.n * a.R * 16 + 255) / 256);
+    const int ncr = a.conv.rows > 0 ? (a.conv.rows + 255) / 256 : 0;
+    hipLaunchKernelGGL(lora_down_reduce_k, dim3(nred + ncr), dim3(256), 0, s, b, ns, nred,
+                       (const float*)a.part);
+  }
   return hipGetLastError();
 }
 
@@ -206,36 +358,60 @@ __global__ __launch_bounds__(UW * 64) void lora_u_k(const LoraU a, const USplit 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row0 = blockIdx.x * 16;
   const int lr = lane & 15, lk = (lane >> 4) * 8;
-  const bool rin = row0 + lr < a.R, jin = lr < a.r;
+  const bool jin = lr < a.r;
   const int N = a.N[q];
   const int nb = rs * sp.cols, ne = min(N, nb + sp.cols);
-  const int64_t yo = a.col0[q] + (int64_t)(rin ? row0 + lr : 0) * a.lddy + lk;
-  const float* B = a.B[q] + (int64_t)(jin ? lr : 0) * N + lk;
+  // buffer loads (an element outside reads 0, no branch): dy over this
+  // block's rows from column col0, B over its r rows; the loads of UB
+  // column steps are issued before their MFMAs, which run in column order
+  constexpr int ES = DF32 ? 4 : 2;  // bytes per dy element
+  const int nrow = min(16, a.R - row0);
+  const buf_t yr = buf_rsrc(reinterpret_cast<const char*>(a.dy) +
+                                (a.col0[q] + (int64_t)row0 * a.lddy) * ES,
+                            (uint32_t)(nrow * a.lddy * ES));
+  const buf_t br = buf_rsrc(a.B[q], (uint32_t)(a.r * N) * 4);
+  const uint32_t yo = (uint32_t)(lr * a.lddy + lk) * ES;
+  const uint32_t bo = jin ? (uint32_t)(lr * N + lk) * 4 : BUF_OOB;
+  constexpr int UB = 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int n0 = nb + wave * 32; n0 < ne; n0 += UW * 32) {
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 af, bw;
-    if constexpr (DF32) {
-      const float* dy = reinterpret_cast<const float*>(a.dy) + yo + n0;
-      const f32x4 x0 = rin ? *reinterpret_cast<const f32x4*>(dy) : zero;
-      const f32x4 x1 = rin ? *reinterpret_cast<const f32x4*>(dy + 4) : zero;
+  for (int nb0 = nb + wave * 32; nb0 < ne; nb0 += UB * UW * 32) {
+    // N and the ranges are multiples of 32: a step is all inside or all past
+    f32x4 x[UB][2], b[UB][2];
+    bf16x8 xb[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int n0 = nb0 + u * UW * 32;
+      const bool in = n0 < ne;
+      if constexpr (DF32) {
+        x[u][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                yr, (int)(in ? yo + n0 * ES : BUF_OOB), 0, 0));
+        x[u][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                yr, (int)(in ? yo + (n0 + 4) * ES : BUF_OOB), 0, 0));
+      } else {
+        xb[u] = buf_bf16x8(yr, in ? yo + n0 * ES : BUF_OOB);
+      }
+      const uint32_t o = in && jin ? bo + n0 * 4 : BUF_OOB;
+      b[u][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(br, (int)o, 0, 0));
+      b[u][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              br, (int)(o == BUF_OOB ? o : o + 16), 0, 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      if (nb0 + u * UW * 32 >= ne) break;
+      bf16x8 af, bw;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        af[i] = (bf16)x0[i];
-        af[i + 4] = (bf16)x1[i];
+        if constexpr (DF32) {
+          af[i] = (bf16)x[u][0][i];
+          af[i + 4] = (bf16)x[u][1][i];
+        }
+        bw[i] = (bf16)b[u][0][i];
+        bw[i + 4] = (bf16)b[u][1][i];
       }
-    } else {
-      const uint16_t* dy = reinterpret_cast<const uint16_t*>(a.dy) + yo + n0;
-      af = rin ? *reinterpret_cast<const bf16x8*>(dy) : bf16x8{};
+      if constexpr (!DF32) af = xb[u];
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bw, acc, 0, 0, 0);
     }
-    const f32x4 b0 = jin ? *reinterpret_cast<const f32x4*>(B + n0) : zero;
-    const f32x4 b1 = jin ? *reinterpret_cast<const f32x4*>(B + n0 + 4) : zero;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bw[i] = (bf16)b0[i];
-      bw[i + 4] = (bf16)b1[i];
-    }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bw, acc, 0, 0, 0);
   }
   // lane holds column j = lane % 16, rows (lane / 16) * 4 + i
 #pragma unroll
@@ -261,8 +437,8 @@ __global__ void lora_u_reduce_k(const LoraU a, const USplit sp) {
   if (i >= (int64_t)a.n * a.R * 16) return;
   const int q = (int)(i / ((int64_t)a.R * 16));
   const int row = (int)((i >> 4) % a.R), j = (int)(i & 15);
-  float v = 0.f;
-  for (int s = 0; s < sp.S; ++s) v += sp.part[(((int64_t)q * sp.S + s) * a.R + row) * 16 + j];
+  const float v = ordered_sum(sp.part + ((int64_t)q * sp.S * a.R + row) * 16 + j,
+                              (int64_t)a.R * 16, sp.S);
   if (j < a.r) a.u[q][(int64_t)row * a.r + j] = v;
   if (a.ext)
     a.ext[(int64_t)row * a.ld_ext + 16 * q + j] = j < a.r ? f32_to_bf16_bits(a.ext_scale * v) : 0;
@@ -273,8 +449,12 @@ static bool al16(const void* q) { return ((uintptr_t)q & 15) == 0; }
 bool lora_u_ok(const LoraU& a) {
   const int v = a.dy_f32 ? 4 : 8;  // elements per 16 bytes
   if (a.n < 1 || a.n > 3 || a.r > 16 || a.lddy % v != 0 || !al16(a.dy)) return false;
+  // 32-bit byte offsets of the buffer loads
+  if ((int64_t)16 * a.lddy * 4 >= BUF_OOB) return false;
   for (int q = 0; q < a.n; ++q)
-    if (a.N[q] % 32 != 0 || a.col0[q] % v != 0 || !al16(a.B[q])) return false;
+    if (a.N[q] % 32 != 0 || a.col0[q] % v != 0 || !al16(a.B[q]) ||
+        (int64_t)16 * a.N[q] * 4 >= BUF_OOB)
+      return false;
   return true;
 }
 
@@ -332,31 +512,33 @@ __global__ __launch_bounds__(256) void lora_tgrad_k(const LoraTGrad a) {
   const bool cfull = c0 + cc + 8 <= jb.C;
   const bool yvec = cfull && (a.ldy % (YF32 ? 4 : 8)) == 0 &&
                     ((uintptr_t)jb.Y & 15) == 0 && ((c0 + cc) % (YF32 ? 4 : 8)) == 0;
+  constexpr int ES = YF32 ? 4 : 2;  // bytes per Y element
+  const int jz = 2 * (t & 7);
   for (int mb = mlo; mb < mhi; mb += TB) {
-    // every load of the block first (one round trip), then bf16 + LDS
+    // every load of the block first (one round trip), then bf16 + LDS.
+    // Buffer loads over the block's token rows: an element past the last
+    // row or column, or a Z column j >= r, reads 0 with no branch
     constexpr int NI = TB / 32;
+    const int nm = min(TB, mhi - mb);
+    const buf_t yr = buf_rsrc(reinterpret_cast<const char*>(jb.Y) + (int64_t)mb * a.ldy * ES,
+                              (uint32_t)((int64_t)nm * a.ldy * ES));
     float v[NI][8];
     float zv[3][NI][2];
     if (yvec) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int m = mb + mr + 32 * i;
-        const bool in = m < mhi;
+        const int ml = mr + 32 * i;
+        const uint32_t o = (uint32_t)((int64_t)ml * a.ldy + c0 + cc) * ES;
         if constexpr (YF32) {
-          const float* y = reinterpret_cast<const float*>(jb.Y) + (int64_t)(in ? m : 0) * a.ldy + c0 + cc;
-          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-          const f32x4 y0 = in ? *reinterpret_cast<const f32x4*>(y) : zero;
-          const f32x4 y1 = in ? *reinterpret_cast<const f32x4*>(y + 4) : zero;
+          const f32x4 y0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(yr, (int)o, 0, 0));
+          const f32x4 y1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(yr, (int)(o + 16), 0, 0));
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             v[i][e] = y0[e];
             v[i][e + 4] = y1[e];
           }
         } else {
-          const uint16_t* y =
-              reinterpret_cast<const uint16_t*>(jb.Y) + (int64_t)(in ? m : 0) * a.ldy + c0 + cc;
-          const u32x4 zero = {0u, 0u, 0u, 0u};
-          const u32x4 w4 = in ? *reinterpret_cast<const u32x4*>(y) : zero;
+          const u32x4 w4 = __builtin_amdgcn_raw_buffer_load_b128(yr, (int)o, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             v[i][2 * e] = bf16_to_f32((uint16_t)(w4[e] & 0xffff));
@@ -367,30 +549,25 @@ __global__ __launch_bounds__(256) void lora_tgrad_k(const LoraTGrad a) {
     } else {  // ragged column block or unaligned rows
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int m = mb + mr + 32 * i;
+        const int ml = mr + 32 * i;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int c = c0 + cc + e;
-          float y = 0.f;
-          if (m < mhi && c < jb.C) {
-            const int64_t o = (int64_t)m * a.ldy + c;
-            if constexpr (YF32) y = reinterpret_cast<const float*>(jb.Y)[o];
-            else y = bf16_to_f32(reinterpret_cast<const uint16_t*>(jb.Y)[o]);
-          }
-          v[i][e] = y;
+          const uint32_t o = c < jb.C ? (uint32_t)((int64_t)ml * a.ldy + c) * ES : BUF_OOB;
+          if constexpr (YF32) v[i][e] = buf_f32(yr, o);
+          else v[i][e] = bf16_to_f32(buf_u16(yr, o));
         }
       }
     }
-    const int jz = 2 * (t & 7);
 #pragma unroll
     for (int z = 0; z < 3; ++z) {
       if (z >= nz) break;
+      const buf_t zr = buf_rsrc(jb.Z[z] + (int64_t)mb * jb.ldz[z], (uint32_t)(nm * jb.ldz[z]) * 4);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int m = mb + mr + 32 * i;
-        const float* zr = jb.Z[z] + (int64_t)(m < mhi ? m : 0) * jb.ldz[z];
-        zv[z][i][0] = (m < mhi && jz < a.r) ? zr[jz] : 0.f;
-        zv[z][i][1] = (m < mhi && jz + 1 < a.r) ? zr[jz + 1] : 0.f;
+        const uint32_t o = (uint32_t)((mr + 32 * i) * jb.ldz[z] + jz) * 4;
+        zv[z][i][0] = buf_f32(zr, jz < a.r ? o : BUF_OOB);
+        zv[z][i][1] = buf_f32(zr, jz + 1 < a.r ? o + 4 : BUF_OOB);
       }
     }
 #pragma unroll
@@ -451,8 +628,7 @@ __global__ __launch_bounds__(256) void lora_tgrad_reduce_k(const LoraTGrad a) {
   const int c = (int)(e >> 4), j = (int)(e & 15);
   if (j >= a.r) return;
   const float* pp = a.part + a.poff[q][z] + e;
-  float sum = 0.f;
-  for (int sp = 0; sp < a.nsplit; ++sp) sum += pp[(int64_t)sp * jb.C * 16];
+  const float sum = ordered_sum(pp, (int64_t)jb.C * 16, a.nsplit);
   float* o = jb.out[z] + (int64_t)c * jb.so_c + (int64_t)j * jb.so_j;
   const float v = a.scale * sum;
   *o = a.accumulate ? *o + v : v;
@@ -462,6 +638,8 @@ hipError_t lora_tgrad(const LoraTGrad& a0, float* part, int64_t part_floats, hip
   LoraTGrad a = a0;
   if (a.R <= 0 || a.njobs <= 0) return hipSuccess;
   if (a.njobs > 3 || a.r > 16) return hipErrorInvalidValue;
+  // 32-bit byte offsets of the buffer loads
+  if ((int64_t)TB * a.ldy * 4 >= BUF_OOB) return hipErrorInvalidValue;
   int cmax = 0;
   int64_t per_split = 0;  // partial-sum floats of one token split
   for (int q = 0; q < a.njobs; ++q) {

@@ -47,8 +47,6 @@ void swiglu_bwd(const float* gu, const float* da, uint16_t* dgu, float* dguf, in
                 hipStream_t s);
 void embed(const int32_t* tok, const uint16_t* table, int T, int H, int V, float* h,
            hipStream_t s);
-void lora_ext(const float* W, int64_t srow, int64_t sj, int R, int r, uint16_t* out, int64_t ld,
-              int c0, hipStream_t s);
 void lse_chunk(const float* logits, int T, int Vc, int v0, const int32_t* tgt, float* run_m,
                float* run_s, float* tlogit, int first, hipStream_t s);
 // targets >= V give NaN log-probs (no vocabulary entry), negative ones 0

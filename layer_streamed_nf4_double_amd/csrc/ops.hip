@@ -192,16 +192,6 @@ __global__ void embed_k(const int32_t* __restrict__ tok, const uint16_t* __restr
     h[t * H + i] = ok ? bf16_to_f32(table[v * H + i]) : __builtin_nanf("");
 }
 
-// out[row*ld + c0 + j] = bf16(W(row, j)), W(row, j) = Wp[row*srow + j*sj], j < 16
-// (zero for j >= r); rows [0, R)
-__global__ void lora_ext_k(const float* __restrict__ Wp, int64_t srow, int64_t sj, int R, int r,
-                           uint16_t* __restrict__ out, int64_t ld, int c0) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)R * 16) return;
-  const int64_t row = i >> 4;
-  const int j = (int)(i & 15);
-  out[row * ld + c0 + j] = (j < r) ? f32_to_bf16_bits(Wp[row * srow + (int64_t)j * sj]) : 0;
-}
 
 // ---------------------------------------------------------------------------
 // vocabulary-chunk log-softmax (online max / sum) and target gather
@@ -905,11 +895,6 @@ void swiglu_bwd(const float* gu, const SplitSum& da, uint16_t* dgu, float* dguf,
 void embed(const int32_t* tok, const uint16_t* table, int T, int H, int V, float* h,
            hipStream_t s) {
   hipLaunchKernelGGL(embed_k, dim3(T), dim3(256), 0, s, tok, table, H, V, h);
-}
-void lora_ext(const float* W, int64_t srow, int64_t sj, int R, int r, uint16_t* out, int64_t ld,
-              int c0, hipStream_t s) {
-  hipLaunchKernelGGL(lora_ext_k, dim3(nb((int64_t)R * 16, 256)), dim3(256), 0, s, W, srow, sj, R,
-                     r, out, ld, c0);
 }
 void lse_chunk(const float* logits, int T, int Vc, int v0, const int32_t* tgt, float* run_m,
                float* run_s, float* tlogit, int first, hipStream_t s) {

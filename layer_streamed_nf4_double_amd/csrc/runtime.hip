@@ -482,7 +482,8 @@ static uint64_t carve(lsn_ctx* c, char* base) {
   c->dqkvb = (uint16_t*)P(T * std::max<int64_t>(QKV, H) * 2);
   c->hpart = (float*)P(T * QD * 4);  // per-q-head dV / dK before the group sum
   c->lt = (float*)P(NPROJ * T * 16 * 4);
-  c->lpart_floats = 0;
+  // the down-projections' split sums (any token count up to T)
+  c->lpart_floats = lora_down_partial_floats_max((int)T, 3);
   for (int p = 0; p < NPROJ; ++p)
     if (c->targeted(p))
       c->lpart_floats = std::max<int64_t>(
@@ -775,18 +776,20 @@ static int lora_fwd_ext(lsn_ctx* c, int layer, Group g, const uint16_t* x, int64
   if (c->fext_ver[ci] != c->lora_version) {  // rebuild the layer's bf16 copies
     // rows of one projection are zero in the other projections' slots
     if (g.count > 1) fill_u32(be, 0, group_rows(c, g) * kext / 2, c->cs);
+    ExtBatch eb;  // bf16(B_p^T) rows and bf16(A_p)^T of every adapter, one launch
     int slot = 0;
     int64_t row0 = 0;
     for (int p = g.first; p < g.first + g.count; ++p) {
       if (c->targeted(p)) {
-        lora_ext(c->B_of(layer, p), 1, c->N[p], (int)c->N[p], r, be + row0 * kext, kext,
-                 16 * slot, c->cs);
-        lora_at(c->A_of(layer, p), (int)c->K[p], r, c->fat + c->fat_off[(size_t)layer * NPROJ + p],
-                c->cs);
+        eb.job[eb.n++] = ExtJob{c->B_of(layer, p), 1, c->N[p], (int)c->N[p], r,
+                                be + row0 * kext, kext, 1, 16 * slot, 0};
+        eb.job[eb.n++] = lora_at_job(c->A_of(layer, p), (int)c->K[p], r,
+                                     c->fat + c->fat_off[(size_t)layer * NPROJ + p]);
         ++slot;
       }
       row0 += c->N[p];
     }
+    (void)lora_convert(eb, c->cs);
     c->fext_ver[ci] = c->lora_version;
   }
   for (int p = g.first; p < g.first + g.count; ++p)
@@ -795,6 +798,7 @@ static int lora_fwd_ext(lsn_ctx* c, int layer, Group g, const uint16_t* x, int64
       d.t[d.n] = c->lt + (int64_t)p * T * 16;
       ++d.n;
     }
+  d.part = c->lpart; d.part_floats = c->lpart_floats;
   (void)lora_down(d, c->cs);
   c->fwd_bext = be;
   return kext;
@@ -872,10 +876,13 @@ static int lora_bwd_ext(lsn_ctx* c, int layer, Group g, const float* dyf, int64_
       (void)lora_mm(mb, c->lpart, c->lpart_floats, c->cs);
     }
   }
-  int slot = 0;
+  ExtBatch eb;  // bext [K, kext]: bf16(A_p) of every adapter, one launch
   for (int p = g.first; p < g.first + g.count; ++p)
-    if (c->targeted(p))
-      lora_ext(c->A_of(layer, p), r, 1, (int)c->K[p], r, c->bext, kext, 16 * slot++, c->cs);
+    if (c->targeted(p)) {
+      eb.job[eb.n] = ExtJob{c->A_of(layer, p), r, 1, (int)c->K[p], r, c->bext, kext, 1, 16 * eb.n, 0};
+      ++eb.n;
+    }
+  (void)lora_convert(eb, c->cs);
   return kext;
 }
 
@@ -1217,7 +1224,8 @@ static LinScratch lin_scratch(char* base, int M, int K, int N) {
   Carver cv;
   auto P = [&](uint64_t b) -> char* { const uint64_t o = cv.take(b); return base ? base + o : nullptr; };
   L.lpf = std::max<int64_t>({lora_mm_partial_floats(M, K), lora_mm_partial_floats(M, N),
-                             lora_mm_partial_floats(K, M), lora_mm_partial_floats(N, M)});
+                             lora_mm_partial_floats(K, M), lora_mm_partial_floats(N, M),
+                             lora_down_partial_floats(M, K, 1)});
   L.gpf = std::max(gemm_partial_floats(M, N, K, 1, 1), gemm_partial_floats(M, K, N, 1, 1));
   L.t = (float*)P((uint64_t)M * 16 * 4);
   L.u = (float*)P((uint64_t)M * 16 * 4);
@@ -1268,13 +1276,17 @@ static lsn_status linear_fwd_core(const uint8_t* codes, const float* absmax, int
   p.C = Y; p.ldc = N;
   p.part = L.gpart; p.part_floats = L.gpf;
   if (r > 0) {
-    LoraMM m;  // t = X A, aext = bf16(s t)
-    m.X = X; m.ldx = K; m.R = M; m.K = K;
-    m.W = A; m.sk = r; m.sj = 1; m.r = r;
-    m.out = L.t; m.so_r = r; m.so_j = 1;
-    m.ext = L.aext; m.ld_ext = 16; m.ext_scale = s;
-    (void)lora_mm(m, L.lpart, L.lpf, hs);
-    lora_ext(B, 1, N, N, r, L.bext, 16, 0, hs);
+    // t = X A and aext = bf16(s t) from the fp32 A (split over k, then the
+    // ordered sum), and bext = bf16(B^T) [N, 16] from the fp32 B in the same
+    // launches
+    LoraDown d;
+    d.X = X; d.ldx = K; d.R = M; d.K = K; d.r = r; d.n = 1;
+    d.AF[0] = A; d.t[0] = L.t;
+    d.ext = L.aext; d.ld_ext = 16; d.ext_scale = s;
+    d.conv.W = B; d.conv.srow = 1; d.conv.sj = N; d.conv.rows = N; d.conv.r = r;
+    d.conv.out = L.bext; d.conv.ld = 16; d.conv.c0 = 0;
+    d.part = L.lpart; d.part_floats = L.lpf;
+    (void)lora_down(d, hs);
     p.Aext = L.aext; p.ldae = 16; p.Bext = L.bext; p.ldbe = 16; p.kext = 16;
   }
   const hipError_t e = gemm(p, A_BF16_K, B_NF4_K, 1, hs);
@@ -1313,13 +1325,13 @@ char* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
 }  // namespace
 
 // The forward's share of the stateless scratch: t, aext [M, 16], bext
-// [N, 16], the low-rank product's split partials and the NF4 GEMM's split-k
-// partials of this shape only (the same split the scratch-taking call uses).
+// [N, 16], the down-projection's and the NF4 GEMM's split-k partials of this
+// shape only (the same splits the scratch-taking call uses).
 static LinScratch lin_scratch_fwd(char* base, int M, int K, int N) {
   LinScratch L;
   Carver cv;
   auto P = [&](uint64_t b) -> char* { const uint64_t o = cv.take(b); return base ? base + o : nullptr; };
-  L.lpf = lora_mm_partial_floats(M, K);
+  L.lpf = lora_down_partial_floats(M, K, 1);
   L.gpf = gemm_partial_floats(M, N, K, 1, 1);
   L.t = (float*)P((uint64_t)M * 16 * 4);
   L.aext = (uint16_t*)P((uint64_t)M * 16 * 2);
@@ -1391,11 +1403,15 @@ lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t
   p.C = dX; p.ldc = K;
   p.part = L.gpart; p.part_floats = L.gpf;
   if (r > 0) {
-    LoraMM m;  // t = X A
-    m.X = X; m.ldx = K; m.R = M; m.K = K;
-    m.W = A; m.sk = r; m.sj = 1; m.r = r;
-    m.out = L.t; m.so_r = r; m.so_j = 1;
-    (void)lora_mm(m, L.lpart, L.lpf, hs);
+    // t = X A (the forward's bits) and bext = bf16(A) [K, 16] from the fp32
+    // A, in the same launches
+    LoraDown d;
+    d.X = X; d.ldx = K; d.R = M; d.K = K; d.r = r; d.n = 1;
+    d.AF[0] = A; d.t[0] = L.t;
+    d.conv.W = A; d.conv.srow = r; d.conv.sj = 1; d.conv.rows = K; d.conv.r = r;
+    d.conv.out = L.bext; d.conv.ld = 16; d.conv.c0 = 0;
+    d.part = L.lpart; d.part_floats = L.lpf;
+    (void)lora_down(d, hs);
     LoraU uu;  // u = dY B^T, aext = bf16(s u)
     uu.dy = dY; uu.dy_f32 = 0; uu.lddy = N; uu.R = M; uu.r = r; uu.n = 1;
     uu.N[0] = N; uu.B[0] = B; uu.u[0] = L.u;
@@ -1420,7 +1436,6 @@ lsn_status lsn_nf4_linear_bwd(const uint8_t* codes, const float* absmax, int32_t
     gb.job[0].Y = dY; gb.job[0].C = N; gb.job[0].nz = 1; gb.job[0].so_c = 1; gb.job[0].so_j = N;
     gb.job[0].Z[0] = L.t; gb.job[0].ldz[0] = r; gb.job[0].out[0] = dB;
     (void)lora_tgrad(gb, L.lpart, L.lpf, hs);
-    lora_ext(A, r, 1, K, r, L.bext, 16, 0, hs);  // bext = A
     p.Aext = L.aext; p.ldae = 16; p.Bext = L.bext; p.ldbe = 16; p.kext = 16;
   }
   const hipError_t e = gemm(p, A_BF16_K, B_NF4_R, 1, hs);
