@@ -431,6 +431,44 @@ def projection_kernels(torch, reps=20):
                              "frac": round(gbps / HBM_PEAK_GBPS, 4), "bound": "hbm"}}
 
 
+def library_bf16_context(torch, w, T, reps=30):
+    """The step's forward NF4 GEMM launches (per layer: q|k|v, o and gate|up
+    twice, in the forward and the backward's recompute, and down once) run as
+    plain bf16 GEMMs of the same shapes in the ROCm BLAS library
+    (torch.matmul, x [T, K] times W^T with W stored [N, K], the layout the NF4
+    kernel reads its weights in).  Context for the roofline fraction: the
+    library gets no dequantization to do.  Not part of the path."""
+    H, F = w["hidden"], w["ffn"]
+    d, nq, nkv = w["head_dim"], w["n_heads"], w["n_kv_heads"]
+    shapes = {"q|k|v": (H, (nq + 2 * nkv) * d, 2), "o": (nq * d, H, 2),
+              "gate|up": (H, 2 * F, 2), "down": (F, H, 1)}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    out, tot_us, tot_fl, n = {}, 0.0, 0.0, 0
+    for name, (K, N, per_layer) in shapes.items():
+        x = torch.randn(T, K, device="cuda", dtype=torch.bfloat16, generator=g)
+        wt = torch.randn(N, K, device="cuda", dtype=torch.bfloat16, generator=g)
+        for _ in range(5):
+            x @ wt.t()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            x @ wt.t()
+        e1.record()
+        e1.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        fl = 2.0 * T * K * N
+        out[name] = {"us": round(us, 2), "frac": round(fl / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        tot_us += per_layer * us
+        tot_fl += per_layer * fl
+        n += per_layer
+        del x, wt
+    torch.cuda.empty_cache()
+    return {"what": "torch.matmul bf16 (ROCm BLAS library), same shapes and launch mix",
+            "avg_us": round(tot_us / n, 2),
+            "frac": round(tot_fl / (tot_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "per_shape": out}
+
+
 def step_flops(w, T, n_seq):
     """Algorithmic flops of one SFT step: each projection 3 times (forward,
     recompute, dX), the LM head twice (log-probs, dX), attention scores and
@@ -658,12 +696,16 @@ def main():
         f"{loads_per_step:.1f} loads/step, peak {peak / 1e9:.2f} GB")
 
     achieved = flops / (ms / 1e3) / 1e12 if ms > 0 else 0.0
+    library = library_bf16_context(torch, w, S)
+    log(f"[bench] bf16 library GEMMs, same launch mix: {library['avg_us']} us per launch, "
+        f"frac {library['frac']}")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(args.workload, args.mode),
                 "kernel": "nf4f_kernel (fused NF4-dequant MFMA GEMM, 256x256 or 256x128 tile)",
                 "launches": int(n_gemm), "avg_us": round(ms / max(n_gemm, 1) * 1e3, 2),
-                "flop_per_launch": flops / max(n_gemm, 1)}
+                "flop_per_launch": flops / max(n_gemm, 1),
+                "library_bf16_same_launches": library}
     copy_gbps = cp_bytes / (cp_ms / 1e3) / 1e9 if cp_ms > 0 else 0.0
     alg = algorithmic_bytes(w, rec_bytes)
     link = {"bound": "host-link", "measured_peak_GBps": round(link_best, 2),
