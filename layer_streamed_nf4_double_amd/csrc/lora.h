@@ -25,6 +25,7 @@ struct LoraMM {
   uint16_t* ext = nullptr;   // optional bf16 copy
   int64_t ld_ext = 0;
   float ext_scale = 1.f;
+  uint32_t xbytes = 0, wbytes = 0;  // set by lora_mm: one block's operand extents
 };
 
 // The forward down-projections of all adapted projections of one group,

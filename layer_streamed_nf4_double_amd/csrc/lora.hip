@@ -22,15 +22,6 @@ namespace lsn {
 
 constexpr int KSTEP = 32;  // k per MFMA
 
-template <bool XF32, bool TRANS>
-LSN_DEV float load_x(const void* X, int64_t ldx, int row, int k) {
-  const int64_t o = TRANS ? (int64_t)k * ldx + row : (int64_t)row * ldx + k;
-  if constexpr (XF32)
-    return reinterpret_cast<const float*>(X)[o];
-  else
-    return bf16_to_f32(reinterpret_cast<const uint16_t*>(X)[o]);
-}
-
 LSN_DEV void lora_store(const LoraMM& a, int row, int j, float sum) {
   if (row >= a.R) return;
   if (j < a.r && a.out) {
@@ -48,18 +39,45 @@ __global__ __launch_bounds__(256) void lora_mm_k(const LoraMM a, int kchunk, flo
   const int row0 = blockIdx.x * 16;
   const int kb = blockIdx.y * kchunk, ke = min(a.K, kb + kchunk);
   const int lr = lane & 15, lk = (lane >> 4) * 8;
-  const int row = row0 + lr;
+  const bool rin = row0 + lr < a.R, jin = lr < a.r;
+  // buffer loads over this block's part of X and W (an element outside the
+  // rows, the k range or the r columns reads 0, with no branch); the loads
+  // of NB k steps are issued before their MFMAs, which run in k order
+  constexpr int ES = XF32 ? 4 : 2;
+  const char* xb = reinterpret_cast<const char*>(a.X) +
+                   (TRANS ? (int64_t)kb * a.ldx + row0 : (int64_t)row0 * a.ldx + kb) * ES;
+  const buf_t xr = buf_rsrc(xb, a.xbytes);
+  const buf_t wr = buf_rsrc(a.W + (int64_t)kb * a.sk, a.wbytes);
+  constexpr int NB = 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = kb + wave * KSTEP; k0 < ke; k0 += 4 * KSTEP) {
-    bf16x8 af, bw;
+  for (int kq = kb + wave * KSTEP; kq < ke; kq += NB * 4 * KSTEP) {
+    float xv[NB][8], wv[NB][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = k0 + lk + i;
-      const bool kin = k < ke;
-      af[i] = (bf16)((row < a.R && kin) ? load_x<XF32, TRANS>(a.X, a.ldx, row, k) : 0.f);
-      bw[i] = (bf16)((lr < a.r && kin) ? a.W[(int64_t)k * a.sk + (int64_t)lr * a.sj] : 0.f);
+    for (int u = 0; u < NB; ++u) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = kq + u * 4 * KSTEP + lk + i;
+        const int64_t kl = k - kb;
+        const uint32_t xo = rin && k < ke
+                                ? (uint32_t)((TRANS ? kl * a.ldx + lr : (int64_t)lr * a.ldx + kl) * ES)
+                                : BUF_OOB;
+        xv[u][i] = XF32 ? buf_f32(xr, xo) : bf16_to_f32(buf_u16(xr, xo));
+        wv[u][i] = buf_f32(wr, jin && k < ke ? (uint32_t)((kl * a.sk + (int64_t)lr * a.sj) * 4)
+                                             : BUF_OOB);
+      }
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bw, acc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      if (kq + u * 4 * KSTEP >= ke) break;  // the same for the whole wave
+      bf16x8 af, bw;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        af[i] = (bf16)xv[u][i];
+        bw[i] = (bf16)wv[u][i];
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bw, acc, 0, 0, 0);
+    }
   }
   // lane holds column j = lane % 16, rows (lane / 16) * 4 + i
 #pragma unroll
@@ -673,14 +691,24 @@ hipError_t lora_tgrad(const LoraTGrad& a0, float* part, int64_t part_floats, hip
   return hipGetLastError();
 }
 
-hipError_t lora_mm(const LoraMM& a, float* partial, int64_t partial_floats, hipStream_t s) {
-  if (a.R <= 0) return hipSuccess;
+hipError_t lora_mm(const LoraMM& a0, float* partial, int64_t partial_floats, hipStream_t s) {
+  if (a0.R <= 0) return hipSuccess;
+  if (a0.r > 16) return hipErrorInvalidValue;
+  LoraMM a = a0;
   int ns, kc;
   split_of(a.R, a.K, &ns, &kc);
   if ((int64_t)ns * a.R * 16 > partial_floats || !partial) {  // no room: one pass over k
     ns = 1;
     kc = std::max(a.K, 1);
   }
+  // extents of one block's buffer resources (every access outside them is
+  // masked to BUF_OOB); the offsets are 32-bit
+  const int64_t es = a.x_f32 ? 4 : 2;
+  const int64_t xb = (a.trans ? (int64_t)(kc - 1) * a.ldx + 16 : 15 * a.ldx + kc) * es;
+  const int64_t wb = ((int64_t)(kc - 1) * a.sk + (int64_t)std::max(a.r - 1, 0) * a.sj + 1) * 4;
+  if (xb >= BUF_OOB || wb >= BUF_OOB) return hipErrorInvalidValue;
+  a.xbytes = (uint32_t)xb;
+  a.wbytes = (uint32_t)wb;
   const dim3 grid((a.R + 15) / 16, ns);
   if (a.x_f32) {
     if (a.trans)
