@@ -8,6 +8,8 @@
 #include "common.h"
 #include "ops.h"
 
+#include <type_traits>
+
 namespace lsn {
 
 // ---------------------------------------------------------------------------
@@ -490,11 +492,28 @@ LSN_DEV bool al16(const void* q) { return ((uintptr_t)q & 15) == 0; }
 // four consecutive elements of a SplitSum operand: the buffers added in
 // split order from zero, as the split-k reduction adds them (one buffer: the
 // value itself)
+// value itself).  NS is the buffer count fixed at compile time (the
+// launchers instantiate 1..8), so the loads of all buffers are issued
+// before the first add; NS = 0 takes the run-time count a.ns, whose loop
+// waits for each load in turn.
+template <int NS>
 LSN_DEV f32x4 sum4(const SplitSum& a, int64_t off) {
-  if (a.ns == 1) return *reinterpret_cast<const f32x4*>(a.p + off);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int y = 0; y < a.ns; ++y) acc += *reinterpret_cast<const f32x4*>(a.p + y * a.stride + off);
-  return acc;
+  if constexpr (NS == 1) {
+    return *reinterpret_cast<const f32x4*>(a.p + off);
+  } else if constexpr (NS == 0) {
+    if (a.ns == 1) return *reinterpret_cast<const f32x4*>(a.p + off);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int y = 0; y < a.ns; ++y) acc += *reinterpret_cast<const f32x4*>(a.p + y * a.stride + off);
+    return acc;
+  } else {
+    f32x4 v[NS];
+#pragma unroll
+    for (int y = 0; y < NS; ++y) v[y] = *reinterpret_cast<const f32x4*>(a.p + y * a.stride + off);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int y = 0; y < NS; ++y) acc += v[y];
+    return acc;
+  }
 }
 
 __global__ __launch_bounds__(256) void rmsnorm_fwd4_k(const float* __restrict__ h,
@@ -525,6 +544,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd4_k(const float* __restrict__ 
 
 // h = res + src (the residual add of a projection whose split-k partial sums
 // src holds), written out, then RMSNorm of h as rmsnorm_fwd4_k
+template <int NS>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_res4_k(const float* __restrict__ res,
                                                           const SplitSum src,
                                                           const uint16_t* __restrict__ g, int H,
@@ -538,7 +558,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_res4_k(const float* __restric
   const int n4 = H >> 2;
   float ss = 0.f;
   for (int i = threadIdx.x; i < n4; i += 256) {
-    const f32x4 v = rr[i] + sum4(src, row * H + 4 * i);
+    const f32x4 v = rr[i] + sum4<NS>(src, row * H + 4 * i);
     x[i] = v;
     ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
@@ -559,6 +579,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_res4_k(const float* __restric
 // produced it, summed once: up to 8 chunks per thread stay in registers
 // between the two passes; outb, if given, also receives bf16(out))
 constexpr int RB_CACHE = 8;
+template <int NS>
 __global__ __launch_bounds__(256) void rmsnorm_bwd4_k(const float* __restrict__ h,
                                                       const uint16_t* __restrict__ g,
                                                       const float* __restrict__ rstd,
@@ -575,7 +596,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd4_k(const float* __restrict__ 
   for (int k = 0; k < RB_CACHE; ++k) {
     const int i = threadIdx.x + 256 * k;
     if (i < n4) {
-      const f32x4 xv = x[i], dv = sum4(dy, row * H + 4 * i);
+      const f32x4 xv = x[i], dv = sum4<NS>(dy, row * H + 4 * i);
       dc[k] = dv;
       const u32x2 w = gw[i];
       dot += bf_lo(w[0]) * dv[0] * xv[0] + bf_hi(w[0]) * dv[1] * xv[1] +
@@ -583,7 +604,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd4_k(const float* __restrict__ 
     }
   }
   for (int i = threadIdx.x + 256 * RB_CACHE; i < n4; i += 256) {
-    const f32x4 xv = x[i], dv = sum4(dy, row * H + 4 * i);
+    const f32x4 xv = x[i], dv = sum4<NS>(dy, row * H + 4 * i);
     const u32x2 w = gw[i];
     dot += bf_lo(w[0]) * dv[0] * xv[0] + bf_hi(w[0]) * dv[1] * xv[1] +
            bf_lo(w[1]) * dv[2] * xv[2] + bf_hi(w[1]) * dv[3] * xv[3];
@@ -608,13 +629,13 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd4_k(const float* __restrict__ 
     const int i = threadIdx.x + 256 * k;
     if (i < n4) emit(i, dc[k]);
   }
-  for (int i = threadIdx.x + 256 * RB_CACHE; i < n4; i += 256) emit(i, sum4(dy, row * H + 4 * i));
+  for (int i = threadIdx.x + 256 * RB_CACHE; i < n4; i += 256) emit(i, sum4<NS>(dy, row * H + 4 * i));
 }
 
 // RoPE with the token's d/2 angles computed once per block into LDS.
 // Forward: reads q|k|v from src (the projection's output or its split-k
 // partial sums); backward: rotates xin in place.
-template <bool FWD>
+template <bool FWD, int NS>
 __global__ __launch_bounds__(256) void rope4_k(const SplitSum src, float* __restrict__ xin,
                                                uint16_t* __restrict__ out, int S, int nq,
                                                int nkv, int d, float theta) {
@@ -626,7 +647,9 @@ __global__ __launch_bounds__(256) void rope4_k(const SplitSum src, float* __rest
   __syncthreads();
   float* x = FWD ? nullptr : xin + t * W;
   uint16_t* y = out + t * W;
-  auto ld4 = [&](int o) { return FWD ? sum4(src, t * W + o) : *reinterpret_cast<const f32x4*>(x + o); };
+  auto ld4 = [&](int o) {
+    return FWD ? sum4<NS>(src, t * W + o) : *reinterpret_cast<const f32x4*>(x + o);
+  };
   const int nrot = (nq + nkv) * h4;  // 4-wide groups of rotated pairs
   for (int i = threadIdx.x; i < nrot; i += 256) {
     const int head = i / h4, j = (i % h4) * 4;
@@ -756,6 +779,7 @@ __global__ __launch_bounds__(256) void swiglu_fwd4_k(const float* __restrict__ g
 
 // (da: the gradient of a, or the split-k partial sums of the GEMM that
 // produced it)
+template <int NS>
 __global__ __launch_bounds__(256) void swiglu_bwd4_k(const float* __restrict__ gu,
                                                      const SplitSum da,
                                                      uint16_t* __restrict__ dgu,
@@ -765,7 +789,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd4_k(const float* __restrict__ g
   const int64_t t = blockIdx.y;
   const f32x4 g = *reinterpret_cast<const f32x4*>(gu + t * 2 * F + f);
   const f32x4 u = *reinterpret_cast<const f32x4*>(gu + t * 2 * F + F + f);
-  const f32x4 d = sum4(da, t * F + f);
+  const f32x4 d = sum4<NS>(da, t * F + f);
   f32x4 dg, du;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -802,6 +826,22 @@ void rmsnorm_bwd(const float* h, const uint16_t* g, const float* rstd, const flo
   rmsnorm_bwd(h, g, rstd, SplitSum{dy, 1, 0}, dres, T, H, out, nullptr, s);
 }
 static bool split_vec(const SplitSum& a) { return a16(a.p) && a.stride % 4 == 0; }
+// calls f with std::integral_constant<int, NS>: the split count 1..8, or 0
+// (a run-time count) for more
+template <class F>
+static void with_splits(int ns, F&& f) {
+  switch (ns) {
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 3: f(std::integral_constant<int, 3>{}); break;
+    case 4: f(std::integral_constant<int, 4>{}); break;
+    case 5: f(std::integral_constant<int, 5>{}); break;
+    case 6: f(std::integral_constant<int, 6>{}); break;
+    case 7: f(std::integral_constant<int, 7>{}); break;
+    case 8: f(std::integral_constant<int, 8>{}); break;
+    default: f(std::integral_constant<int, 0>{}); break;
+  }
+}
 bool rmsnorm_bwd_fuses(int H, const float* h, const float* out, const float* dres,
                        const uint16_t* g) {
   return H % 4 == 0 && a16(h) && a16(out) && (!dres || a16(dres)) && ((uintptr_t)g & 7) == 0;
@@ -809,8 +849,10 @@ bool rmsnorm_bwd_fuses(int H, const float* h, const float* out, const float* dre
 void rmsnorm_bwd(const float* h, const uint16_t* g, const float* rstd, const SplitSum& dy,
                  const float* dres, int T, int H, float* out, uint16_t* outb, hipStream_t s) {
   if (rmsnorm_bwd_fuses(H, h, out, dres, g) && split_vec(dy) && ((uintptr_t)outb & 7) == 0) {
-    hipLaunchKernelGGL(rmsnorm_bwd4_k, dim3(T), dim3(256), 0, s, h, g, rstd, dy, dres, H, out,
-                       outb);
+    with_splits(dy.ns, [&](auto ns) {
+      hipLaunchKernelGGL((rmsnorm_bwd4_k<decltype(ns)::value>), dim3(T), dim3(256), 0, s, h, g,
+                         rstd, dy, dres, H, out, outb);
+    });
   } else if (dy.ns == 1) {
     hipLaunchKernelGGL(rmsnorm_bwd_k, dim3(T), dim3(256), 0, s, h, g, rstd, dy.p, dres, H, out);
     if (outb) f32_to_bf16(out, outb, (int64_t)T * H, s);
@@ -823,8 +865,10 @@ bool rmsnorm_fwd_res_fuses(int H, const float* res, const float* hout, const uin
 }
 void rmsnorm_fwd_res(const float* res, const SplitSum& src, const uint16_t* g, int T, int H,
                      float eps, float* hout, uint16_t* y, float* rstd, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_fwd_res4_k, dim3(T), dim3(256), 0, s, res, src, g, H, eps, hout, y,
-                     rstd);
+  with_splits(src.ns, [&](auto ns) {
+    hipLaunchKernelGGL((rmsnorm_fwd_res4_k<decltype(ns)::value>), dim3(T), dim3(256), 0, s, res,
+                       src, g, H, eps, hout, y, rstd);
+  });
 }
 static bool rope_vec(const void* x, const void* y, int d) {
   return d % 8 == 0 && d / 2 <= 128 && a16(x) && ((uintptr_t)y & 7) == 0;
@@ -837,16 +881,18 @@ void rope_fwd(const float* qkv, uint16_t* out, int T, int S, int nq, int nkv, in
 void rope_fwd(const SplitSum& qkv, uint16_t* out, int T, int S, int nq, int nkv, int d,
               float theta, hipStream_t s) {
   if (rope_vec(qkv.p, out, d) && split_vec(qkv))
-    hipLaunchKernelGGL(rope4_k<true>, dim3(T), dim3(256), 0, s, qkv, nullptr, out, S, nq, nkv, d,
-                       theta);
+    with_splits(qkv.ns, [&](auto ns) {
+      hipLaunchKernelGGL((rope4_k<true, decltype(ns)::value>), dim3(T), dim3(256), 0, s, qkv,
+                         nullptr, out, S, nq, nkv, d, theta);
+    });
   else if (qkv.ns == 1)
     hipLaunchKernelGGL(rope_fwd_k, dim3(T), dim3(256), 0, s, qkv.p, out, S, nq, nkv, d, theta);
 }
 void rope_bwd(float* dqkv, uint16_t* outb, int T, int S, int nq, int nkv, int d, float theta,
               hipStream_t s) {
   if (rope_vec(dqkv, outb, d))
-    hipLaunchKernelGGL(rope4_k<false>, dim3(T), dim3(256), 0, s, SplitSum{}, dqkv, outb, S, nq,
-                       nkv, d, theta);
+    hipLaunchKernelGGL((rope4_k<false, 1>), dim3(T), dim3(256), 0, s, SplitSum{}, dqkv, outb, S,
+                       nq, nkv, d, theta);
   else
     hipLaunchKernelGGL(rope_bwd_k, dim3(T), dim3(256), 0, s, dqkv, outb, S, nq, nkv, d, theta);
 }
@@ -885,7 +931,10 @@ void swiglu_bwd(const float* gu, const float* da, uint16_t* dgu, float* dguf, in
 void swiglu_bwd(const float* gu, const SplitSum& da, uint16_t* dgu, float* dguf, int T, int F,
                 hipStream_t s) {
   if (swiglu_bwd_fuses(T, F, gu, dgu, dguf) && split_vec(da)) {
-    hipLaunchKernelGGL(swiglu_bwd4_k, dim3(nb(F / 4, 256), T), dim3(256), 0, s, gu, da, dgu, dguf, F);
+    with_splits(da.ns, [&](auto ns) {
+      hipLaunchKernelGGL((swiglu_bwd4_k<decltype(ns)::value>), dim3(nb(F / 4, 256), T), dim3(256),
+                         0, s, gu, da, dgu, dguf, F);
+    });
     return;
   }
   if (da.ns != 1) return;
