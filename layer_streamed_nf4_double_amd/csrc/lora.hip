@@ -1,20 +1,23 @@
-// Low-rank (r <= 16) products of the LoRA branch on the matrix cores.
-//
+// Low-rank (r <= 16) products of the LoRA branch y = xW + s(xA)B on the
+// matrix cores:
+//   t  = x A            lora_down_k (every adapter of a projection group)
+//   u  = dy B^T         lora_u_k
+//   dA += s x^T u,  dB += s t^T dy    lora_tgrad_k
+// and lora_mm_k, the general product
 //   out(row, j) = scale * sum_k X(row, k) W(k, j)        j < r
+// with X bf16 or fp32, stored with the reduction contiguous (X[row*ld + k])
+// or transposed (X[k*ld + row]) and W(k, j) = W[k*sk + j*sj] fp32, for the
+// operands the others do not take (rows not 16-byte aligned);
+// lora_convert_k writes the bf16 adapter copies the GEMMs read as extra
+// k-columns.  Operands are rounded to bf16 and multiplied by
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  The sums of waves, and
+// of the k splits of a split launch, are added in fixed orders; no atomics:
+// results are bit-reproducible.
 //
-// X is bf16 or fp32, stored with the reduction contiguous (X[row*ld + k]) or
-// transposed (X[k*ld + row]); W(k, j) = W[k*sk + j*sj] is fp32.  This one
-// kernel serves the four products of an adapted projection y = xW + s(xA)B:
-//   t  = x A            (row = token, k = input feature)
-//   u  = dy B^T         (row = token, k = output feature)
-//   dA += s x^T u       (row = input feature, k = token; x transposed)
-//   dB += s t^T dy      (row = output feature, k = token; dy transposed,
-//                        written to dB[j*N + row])
-// Operands are rounded to bf16 and multiplied by v_mfma_f32_16x16x32_bf16
-// with fp32 accumulation.  One workgroup owns 16 rows; its four waves split
-// the k range and are summed in LDS in wave order; with split-k the partial
-// sums go to a buffer and a second kernel adds them in split order.  No
-// atomics: results are bit-reproducible.
+// These launches have few workgroups each, so they are bound by load
+// latency: operands are read through raw buffer loads (an element outside
+// its operand reads 0, without a branch) and a wave issues several k steps'
+// loads before their MFMAs.
 #include "common.h"
 #include "lora.h"
 
@@ -32,6 +35,10 @@ LSN_DEV void lora_store(const LoraMM& a, int row, int j, float sum) {
   if (a.ext) a.ext[(int64_t)row * a.ld_ext + j] = (j < a.r) ? f32_to_bf16_bits(a.ext_scale * sum) : 0;
 }
 
+// lora_mm_k: one workgroup owns 16 rows; its four waves take the 32-deep k
+// steps w, w + 4, ... of the block's k range and are summed in LDS in wave
+// order; with a split launch the partial sums go to a buffer and
+// lora_reduce_k adds them in split order.
 template <bool XF32, bool TRANS>
 __global__ __launch_bounds__(256) void lora_mm_k(const LoraMM a, int kchunk, float* partial) {
   __shared__ float red[4][16][17];
