@@ -417,6 +417,10 @@ struct Group {
   int first, count;
 };
 static const Group G_QKV{LSN_Q, 3}, G_O{LSN_O, 1}, G_GU{LSN_GATE, 2}, G_D{LSN_DOWN, 1};
+// a group's adapter conversions (two per adapter) fit one batch
+constexpr int MAX_GROUP = 3;
+static_assert(2 * MAX_GROUP <= (int)(sizeof(ExtBatch::job) / sizeof(ExtJob)),
+              "one conversion launch per group");
 
 static int64_t group_rows(const lsn_ctx* c, Group g) {
   int64_t n = 0;
