@@ -109,11 +109,15 @@ def _gpu_linear(torch, L, X, W, A, B, r, s, dY):
 # of four waves inside; (512, 4096, 256) 32 tiles of 4 slices; (300, 384,
 # 1024) ragged M, half a column tile, split 4 and the rank-16 extension;
 # (512, 640, 2048) split 8 x 4 slices.
+# The low-rank down projection t = x A splits k over up to 8 workgroups per
+# 16 rows: (40, 4096, 512, 8) takes 8 splits with a ragged last row block
+# and rank 8 (columns 8-15 of every fragment masked).
 @pytest.mark.parametrize("M,K,N,r", [(200, 688, 264, 8), (64, 256, 256, 16), (1, 16, 8, 4),
                                      (300, 1024, 2056, 16), (96, 512, 640, 0),
                                      (256, 64, 256, 0), (256, 832, 256, 16),
                                      (512, 4096, 256, 0), (257, 128, 296, 8),
-                                     (300, 384, 1024, 16), (512, 640, 2048, 0)])
+                                     (300, 384, 1024, 16), (512, 640, 2048, 0),
+                                     (40, 4096, 512, 8)])
 def test_linear_parity_small(torch, L, M, K, N, r):
     say(f"[linear] M={M} K={K} N={N} r={r}")
     s = 2.0
