@@ -123,13 +123,14 @@ def quantized_layers(w):
 
 
 def build_model(w, mode, max_tokens, max_seq_len, layers, head, store_path=None,
-                head_on_host=False, n_slots=0):
+                head_on_host=False, n_slots=0, layer_tokens=0):
     import numpy as np
 
     import synth
     from layer_streamed_nf4_double_amd.trainer import LayerStreamedLoRA
     m = LayerStreamedLoRA(w, mode, max_tokens=max_tokens, max_seq_len=max_seq_len,
-                          store_path=store_path, head_on_host=head_on_host, n_slots=n_slots)
+                          store_path=store_path, head_on_host=head_on_host, n_slots=n_slots,
+                          layer_tokens=layer_tokens)
     for layer, codes, absmax, g1, g2 in layers:
         m.load_layer(layer, codes, absmax, g1, g2)
     for layer in range(w["n_layers"]):
@@ -307,8 +308,10 @@ def sft_leg(torch, w, layers, head, tok, tgt, steps, warmup, n_slots=0, mode="st
 
 
 def dpo_leg(torch, w, layers, head, steps, warmup, sft_peak, sft_loads, link_best, rec_bytes,
-            n_slots=0):
-    """Streamed DPO steps on one preference pair (fused reference pass)."""
+            n_slots=0, layer_tokens=0):
+    """Streamed DPO steps on one preference pair (fused reference pass).
+    layer_tokens = seq_len: each layer runs the chosen and then the rejected
+    sequence on its record (half the activation workspace, same copies)."""
     import numpy as np
 
     import synth
@@ -319,7 +322,8 @@ def dpo_leg(torch, w, layers, head, steps, warmup, sft_peak, sft_loads, link_bes
     d_tok, d_tgt = device_batch(dtok, sft_targets(dtok), w["vocab"])
     torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats()
-    md = build_model(w, "stream_host", 2 * S, S, layers, head, n_slots=n_slots)
+    md = build_model(w, "stream_host", 2 * S, S, layers, head, n_slots=n_slots,
+                     layer_tokens=layer_tokens)
     P, beta = synth.dpo_prompt_len(w), synth.DPO_PAIR["beta"]
     for _ in range(max(1, warmup)):
         md.dpo_step(d_tok, d_tgt, S, P, beta, 1e-4)
@@ -340,6 +344,8 @@ def dpo_leg(torch, w, layers, head, steps, warmup, sft_peak, sft_loads, link_bes
     alg = algorithmic_bytes(w, rec_bytes, dpo=True)
     return {"tokens_per_s": round(2 * S / ddt, 2), "ms_per_step": round(ddt * 1e3, 2),
             "n_slots": n_slots or 2,
+            "layer_groups": ("one sequence per layer launch group (chosen, then rejected)"
+                             if layer_tokens else "the pair as one 2 x seq_len batch"),
             "reference_pass": "fused with the policy forward (one record copy per layer)",
             "tokens_per_step": 2 * S, "loss": float(out[0]),
             "layer_loads_per_step": (l1 - l0) / steps,
@@ -725,6 +731,13 @@ def main():
                       link_best, rec_bytes)
         log(f"[bench] DPO {dpo['ms_per_step']:.1f} ms/step, {dpo['tokens_per_s']:.1f} tok/s, "
             f"loss {dpo['loss']:.4f}")
+        if not args.no_extras:
+            dpo["seq_groups"] = dpo_leg(torch, w, layers, head, max(1, args.dpo_steps // 2),
+                                        args.warmup, peak, loads_per_step, link_best, rec_bytes,
+                                        layer_tokens=S)
+            log(f"[bench] DPO, one sequence per layer group: "
+                f"{dpo['seq_groups']['ms_per_step']:.1f} ms/step, peak "
+                f"{dpo['seq_groups']['peak_vram_bytes'] / 1e9:.2f} GB")
 
     # ---- three device slots (one more record resident: two fewer copies per step) ----
     slots3 = None
@@ -798,6 +811,10 @@ def main():
         dpo2_3 = dpo_leg(torch, w2, layers2, head2, max(1, args.second_steps // 2), args.warmup,
                          sft2["peak_vram_bytes"], sft2["layer_loads_per_step"], link_best, rec2,
                          n_slots=3)
+        dpo2["seq_groups"] = dpo_leg(torch, w2, layers2, head2, max(1, args.second_steps // 2),
+                                     args.warmup, sft2["peak_vram_bytes"],
+                                     sft2["layer_loads_per_step"], link_best, rec2,
+                                     layer_tokens=w2["seq_len"])
         second = {"workload": f"{args.second_workload} streamed LoRA-SFT step (seq "
                               f"{w2['seq_len']}) and DPO step (2 x {w2['seq_len']})",
                   "n_layers": w2["n_layers"], "hidden": w2["hidden"], "vocab": w2["vocab"],

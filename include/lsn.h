@@ -98,6 +98,17 @@ typedef struct {
    * again (2 * (n_slots - 2) fewer record copies per SFT step), at one
    * record of device memory per slot.  Ignored when resident. */
   int32_t n_slots;
+  /* 0: a layer call runs all of the pass's tokens as one batch.  Else the
+   * layer workspace holds max(layer_tokens, max_seq_len) tokens (at most
+   * max_tokens) and each layer call runs its sequences in groups of as many
+   * whole sequences as that holds, one group after the other on the same
+   * record (a DPO pair: the chosen and then the rejected sequence).  The
+   * record is still copied once per layer; the adapter gradients of the
+   * groups are added in group order.  Cuts the activation memory of a
+   * multi-sequence pass: the pages report streamed DPO below the SFT memory
+   * peak ("Show HN: Fine-tune an 8B model on a 4 GB laptop GPU", second
+   * paragraph). */
+  int32_t layer_tokens;
 } lsn_config;
 
 /* ---------------------------------------------------------------------------

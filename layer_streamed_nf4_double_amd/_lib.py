@@ -48,7 +48,7 @@ class lsn_config(ctypes.Structure):
                 ("max_seq_len", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("store_path", ctypes.c_char_p), ("vram_budget", ctypes.c_uint64),
                 ("head_on_host", ctypes.c_int32), ("head_chunk_rows", ctypes.c_int32),
-                ("n_slots", ctypes.c_int32)]
+                ("n_slots", ctypes.c_int32), ("layer_tokens", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p

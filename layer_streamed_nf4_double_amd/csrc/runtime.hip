@@ -138,7 +138,7 @@ struct lsn_ctx {
   std::vector<int64_t> lA, lB;  // float offsets of A and B per (layer, proj); -1 if none
   bool head_loaded = false;
 
-  // activation scratch (one layer at max_tokens)
+  // activation scratch (one layer at TL tokens)
   uint16_t *n1, *qkvb, *Pb, *O, *n2, *a, *dgu, *dO, *dqkvb, *aext, *bext, *nf, *dlog;
   float *rstd1, *qkv, *scores, *Pf, *h2, *rstd2, *gu, *da, *dguf, *dn, *dh2, *dqkv, *lt, *lu,
       *rstdf, *logits, *run_m, *run_s, *tlogit, *lse, *dnf, *lpart, *gpart, *hpart;
@@ -147,6 +147,7 @@ struct lsn_ctx {
 
   // pass state (the layer order and position live in sched)
   int pass_kind = -1, n_seq = 0, seq_len = 0, T = 0;
+  int64_t TL = 0;  // tokens the layer workspace holds (layer_tokens, else max_tokens)
   bool adapters_on = true;
   const float* lm_h = nullptr;
   int lm_T = 0;
@@ -353,6 +354,7 @@ static bool cfg_valid(const lsn_config* g, std::string* why) {
   if (g->head_chunk_rows < 0 || g->head_chunk_rows % 8) return bad("head_chunk_rows must be a multiple of 8");
   if (g->n_slots != 0 && (g->n_slots < 2 || g->n_slots > MAX_SLOTS))
     return bad("n_slots must be 0 (two) or 2..4");
+  if (g->layer_tokens < 0) return bad("layer_tokens must be >= 0");
   return true;
 }
 
@@ -431,8 +433,14 @@ static int64_t group_rows(const lsn_ctx* c, Group g) {
 // Carves the workspace; with base == nullptr only measures.
 static uint64_t carve(lsn_ctx* c, char* base) {
   const lsn_config& g = c->cfg;
-  const int64_t T = g.max_tokens, S = g.max_seq_len, H = g.hidden, F = g.ffn, V = g.vocab;
+  const int64_t TH = g.max_tokens, S = g.max_seq_len, H = g.hidden, F = g.ffn, V = g.vocab;
   const int64_t r = g.lora_rank;
+  // the layer buffers hold TL tokens (one group of whole sequences), the LM
+  // head's hold TH (all tokens of a pass)
+  const int64_t T = g.layer_tokens > 0
+                        ? std::min<int64_t>(TH, std::max<int64_t>(g.layer_tokens, S))
+                        : TH;
+  c->TL = T;
   c->vchunk = head_chunk_rows(c);
   Carver cv;
   auto P = [&](uint64_t bytes) -> char* { const uint64_t o = cv.take(bytes); return base ? base + o : nullptr; };
@@ -495,14 +503,16 @@ static uint64_t carve(lsn_ctx* c, char* base) {
            lora_mm_partial_floats((int)T, (int)c->N[p]), lora_mm_partial_floats((int)c->K[p], (int)T),
            lora_mm_partial_floats((int)c->N[p], (int)T)});
   c->lpart = (float*)P(std::max<int64_t>(c->lpart_floats, 1) * 4);
-  {  // split-k scratch of the largest single-problem GEMM at max_tokens
+  {  // split-k scratch of the largest single-problem GEMM: a layer's at TL
+     // tokens, the LM head's at max_tokens
     const int64_t Vc0 = std::min<int64_t>(V, c->vchunk);
-    const int64_t shapes[][3] = {{QKV, H}, {H, QD}, {2 * F, H}, {H, F}, {F, H},
-                                 {H, 2 * F}, {QD, H}, {H, QKV}, {Vc0, H}, {H, Vc0}};
+    const int64_t shapes[][3] = {{QKV, H, T},  {H, QD, T},  {2 * F, H, T}, {H, F, T},
+                                 {F, H, T},    {H, 2 * F, T}, {QD, H, T},  {H, QKV, T},
+                                 {Vc0, H, TH}, {H, Vc0, TH}};
     c->gpart_floats = 0;
     for (const auto& sh : shapes)
       c->gpart_floats = std::max<int64_t>(
-          c->gpart_floats, gemm_partial_floats((int)T, (int)sh[0], (int)sh[1], 1, 1));
+          c->gpart_floats, gemm_partial_floats((int)sh[2], (int)sh[0], (int)sh[1], 1, 1));
     c->gpart = (float*)P(std::max<int64_t>(c->gpart_floats, 1) * 4);
   }
   c->lu = (float*)P(3 * T * 16 * 4);  // u_p of up to three adapters of a group
@@ -536,16 +546,16 @@ static uint64_t carve(lsn_ctx* c, char* base) {
   }
   // LM head
   const int64_t Vc = std::min<int64_t>(V, c->vchunk);
-  c->nf = (uint16_t*)P(T * H * 2);
-  c->rstdf = (float*)P(T * 4);
-  c->logits = (float*)P(T * Vc * 4);
-  c->dlog = (uint16_t*)P(T * Vc * 2);
-  c->run_m = (float*)P(T * 4);
-  c->run_s = (float*)P(T * 4);
-  c->tlogit = (float*)P(T * 4);
-  c->lse = (float*)P(T * 4);
-  c->head_f = (float*)P(T * 4);
-  c->dnf = (float*)P(T * H * 4);
+  c->nf = (uint16_t*)P(TH * H * 2);
+  c->rstdf = (float*)P(TH * 4);
+  c->logits = (float*)P(TH * Vc * 4);
+  c->dlog = (uint16_t*)P(TH * Vc * 2);
+  c->run_m = (float*)P(TH * 4);
+  c->run_s = (float*)P(TH * 4);
+  c->tlogit = (float*)P(TH * 4);
+  c->lse = (float*)P(TH * 4);
+  c->head_f = (float*)P(TH * 4);
+  c->dnf = (float*)P(TH * H * 4);
   return align_up(cv.off, 256);
 }
 
@@ -1766,13 +1776,35 @@ lsn_status lsn_embed(lsn_ctx* c, const int32_t* tokens, float* h0) {
   return launch_check(c);
 }
 
+}  // extern "C"
+
+// Runs f(token offset) once per group of whole sequences of the pass that
+// the layer workspace holds (one group when it holds them all), with the
+// context's token and sequence counts set to the group's; groups in order.
+template <class Fn>
+static lsn_status for_groups(lsn_ctx* c, Fn f) {
+  const int n = c->n_seq, T = c->T;
+  const int per = (int)std::max<int64_t>(1, std::min<int64_t>(n, c->TL / c->seq_len));
+  lsn_status st = LSN_OK;
+  for (int s0 = 0; s0 < n && st == LSN_OK; s0 += per) {
+    c->n_seq = std::min(per, n - s0);
+    c->T = c->n_seq * c->seq_len;
+    st = f((int64_t)s0 * c->seq_len * c->cfg.hidden);
+  }
+  c->n_seq = n;
+  c->T = T;
+  return st;
+}
+
+extern "C" {
+
 lsn_status lsn_forward_layer(lsn_ctx* c, int32_t layer, const float* h_in, float* h_out) {
   CHECK_CTX(c);
   if (!h_in || !h_out) return fail(c, LSN_ERR_INVALID, "null activation");
   const uint8_t* rec;
   lsn_status st = layer_begin(c, LSN_PASS_FWD, layer, &rec);
   if (st != LSN_OK) return st;
-  st = layer_forward(c, layer, rec, h_in, h_out, true);
+  st = for_groups(c, [&](int64_t o) { return layer_forward(c, layer, rec, h_in + o, h_out + o, true); });
   if (st != LSN_OK) return st;
   return layer_end(c);
 }
@@ -1791,10 +1823,12 @@ lsn_status lsn_forward_layer_pair(lsn_ctx* c, int32_t layer, const float* h_ref_
   // then with them (policy); the kernels are the ones of lsn_forward_layer
   const bool on = c->adapters_on;
   c->adapters_on = false;
-  st = layer_forward(c, layer, rec, h_ref_in, h_ref_out, true);
+  st = for_groups(c, [&](int64_t o) {
+    return layer_forward(c, layer, rec, h_ref_in + o, h_ref_out + o, true);
+  });
   c->adapters_on = on;
   if (st != LSN_OK) return st;
-  st = layer_forward(c, layer, rec, h_in, h_out, true);
+  st = for_groups(c, [&](int64_t o) { return layer_forward(c, layer, rec, h_in + o, h_out + o, true); });
   if (st != LSN_OK) return st;
   return layer_end(c);
 }
@@ -1809,7 +1843,9 @@ lsn_status lsn_backward_layer(lsn_ctx* c, int32_t layer, const float* h_in, cons
   const uint8_t* rec;
   lsn_status st = layer_begin(c, LSN_PASS_BWD, layer, &rec);
   if (st != LSN_OK) return st;
-  st = layer_backward(c, layer, rec, h_in, dh_out, dh_in);
+  st = for_groups(c, [&](int64_t o) {
+    return layer_backward(c, layer, rec, h_in + o, dh_out + o, dh_in + o);
+  });
   if (st != LSN_OK) return st;
   return layer_end(c);
 }

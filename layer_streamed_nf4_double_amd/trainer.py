@@ -28,7 +28,7 @@ PREF_LOSSES = {"dpo": L.LSN_LOSS_DPO, "simpo": L.LSN_LOSS_SIMPO, "orpo": L.LSN_L
 
 def make_config(shape, mode="stream_host", max_tokens=None, max_seq_len=None,
                 lora_targets=("q", "v"), store_path=None, vram_budget=0, head_on_host=False,
-                head_chunk_rows=0, n_slots=0):
+                head_chunk_rows=0, n_slots=0, layer_tokens=0):
     """lsn_config from a shape dict (n_layers, hidden, n_heads, n_kv_heads,
     head_dim, ffn, vocab, rms_eps, rope_theta, lora_rank, lora_alpha, tied)."""
     cfg = L.lsn_config()
@@ -53,6 +53,7 @@ def make_config(shape, mode="stream_host", max_tokens=None, max_seq_len=None,
     cfg.head_on_host = int(bool(head_on_host))
     cfg.head_chunk_rows = head_chunk_rows
     cfg.n_slots = n_slots
+    cfg.layer_tokens = layer_tokens
     return cfg
 
 
@@ -61,7 +62,8 @@ class LayerStreamedLoRA:
 
     def __init__(self, shape, mode="stream_host", max_tokens=None, max_seq_len=None,
                  lora_targets=("q", "v"), store_path=None, device="cuda:0", stream=None,
-                 head_on_host=False, head_chunk_rows=0, n_slots=0, vram_budget=0):
+                 head_on_host=False, head_chunk_rows=0, n_slots=0, vram_budget=0,
+                 layer_tokens=0):
         """mode: resident | stream_host | stream_file | auto.  'auto' keeps the
         base in pinned RAM when it fits and in a file (store_path, or a file
         in $TMPDIR) when it does not; every mode is pre-flighted against the
@@ -69,7 +71,10 @@ class LayerStreamedLoRA:
         the embedding and LM-head tables stay in pinned host memory and W_lm
         streams through the layer slots.  n_slots: device slots of the layer
         stream (0: two).  vram_budget: lsn_create refuses a workspace larger
-        than this many bytes (0: no limit)."""
+        than this many bytes (0: no limit).  layer_tokens: tokens of one layer
+        launch group (0: the whole pass); a DPO pair with layer_tokens =
+        seq_len runs the chosen and the rejected sequence one after the other
+        on each record, with half the activation workspace."""
         import tempfile
 
         import torch
@@ -82,7 +87,7 @@ class LayerStreamedLoRA:
         probe = make_config(shape, "stream_host" if mode in ("auto", "stream_file") else mode,
                             max_tokens, max_seq_len, lora_targets, store_path,
                             head_on_host=head_on_host, head_chunk_rows=head_chunk_rows,
-                            n_slots=n_slots)
+                            n_slots=n_slots, layer_tokens=layer_tokens)
         free, _ = torch.cuda.mem_get_info(self.device)
         mode = adapter.plan_run(shape["n_layers"], L.lsn_config_record_bytes(probe),
                                 L.lsn_workspace_bytes(probe), free,
@@ -95,7 +100,8 @@ class LayerStreamedLoRA:
         self.mode = mode
         self.cfg = make_config(shape, mode, max_tokens, max_seq_len, lora_targets, store_path,
                                vram_budget=vram_budget, head_on_host=head_on_host,
-                               head_chunk_rows=head_chunk_rows, n_slots=n_slots)
+                               head_chunk_rows=head_chunk_rows, n_slots=n_slots,
+                               layer_tokens=layer_tokens)
         self.lora_targets = tuple(lora_targets)
         self.ws_bytes = L.lsn_workspace_bytes(self.cfg)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)

@@ -73,13 +73,13 @@ def layer_record(w, layer):
 
 def gpu_model(w, mode, b_zero, lora_targets=("q", "v"), store_path=None, max_tokens=None,
               max_seq_len=None, head_on_host=False, head_chunk_rows=0, n_slots=0,
-              vram_budget=0):
+              vram_budget=0, layer_tokens=0):
     from layer_streamed_nf4_double_amd import _lib as L
     from layer_streamed_nf4_double_amd.trainer import LayerStreamedLoRA
     m = LayerStreamedLoRA(w, mode, max_tokens=max_tokens, max_seq_len=max_seq_len,
                           head_on_host=head_on_host, head_chunk_rows=head_chunk_rows,
                           lora_targets=lora_targets, store_path=store_path, n_slots=n_slots,
-                          vram_budget=vram_budget)
+                          vram_budget=vram_budget, layer_tokens=layer_tokens)
     ones = np.full(w["hidden"], BF16_ONE, np.uint16)
     for layer in range(w["n_layers"]):
         codes, absmax = layer_record(w, layer)

@@ -217,3 +217,38 @@ def test_config_checks_without_a_gpu():
     # 64-wide stack whose slot holds fewer than 256 W_lm rows
     small = dict(w, hidden=64, n_heads=1, n_kv_heads=1, head_dim=64, ffn=64, vocab=4096)
     L.lsn_workspace_bytes(make_config(small, "stream_host", head_on_host=True))
+
+
+def test_sequence_groups_workspace_without_a_gpu():
+    """layer_tokens sizes the layer buffers for one group of whole sequences
+    and leaves the LM head's at max_tokens: a two-sequence (DPO pair)
+    workspace with layer_tokens = seq_len lies strictly between the
+    one-sequence workspace and the ungrouped two-sequence one, at least the
+    head's per-token buffers above the former; a single-sequence
+    config, or layer_tokens at or above max_tokens, changes nothing; a
+    negative value is refused."""
+    L = _lib()
+    import synth
+    from layer_streamed_nf4_double_amd.trainer import make_config
+    for name in ("tiny", "llama3.1-8b-shaped", "qwen2.5-3b-shaped"):
+        w = synth.WORKLOADS[name]
+        S = w["seq_len"]
+        one = L.lsn_workspace_bytes(make_config(w, "stream_host", S, S))
+        pair = L.lsn_workspace_bytes(make_config(w, "stream_host", 2 * S, S))
+        grouped = L.lsn_workspace_bytes(make_config(w, "stream_host", 2 * S, S, layer_tokens=S))
+        assert one < grouped < pair, (name, one, grouped, pair)
+        assert L.lsn_workspace_bytes(make_config(w, "stream_host", S, S, layer_tokens=S)) == one
+        assert L.lsn_workspace_bytes(make_config(w, "stream_host", 2 * S, S,
+                                                 layer_tokens=4 * S)) == pair
+        # below one sequence: still one sequence per group
+        assert L.lsn_workspace_bytes(make_config(w, "stream_host", 2 * S, S,
+                                                 layer_tokens=8)) == grouped
+        # the LM head's buffers (final norm bf16 + fp32 gradient, five fp32
+        # per-token scalars, its logits chunk and split-k scratch) keep all
+        # 2 S tokens
+        H = w["hidden"]
+        assert grouped - one >= S * (2 * H + 4 * H + 5 * 4), name
+    with pytest.raises(L.LsnError) as e:
+        L.lsn_workspace_bytes(make_config(synth.WORKLOADS["tiny"], "stream_host",
+                                          layer_tokens=-1))
+    assert e.value.status == L.LSN_ERR_INVALID

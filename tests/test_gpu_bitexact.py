@@ -6,7 +6,9 @@ Breakthrough"), also with the process capped to the streamed run's memory
 (the evermx page's notebook caps a T4 to 4 GB and asserts bit identity).
 
 * DPO steps, fused and separate reference pass, resident == host-streamed ==
-  file-streamed, bitwise; the fused form at the full 8B layer shape.
+  file-streamed, bitwise; the fused form at the full 8B layer shape; the
+  chosen and rejected sequences run one after the other on each record
+  (layer_tokens), also against the oracle.
 * SFT with 3 and 4 slots, and the exact record-copy counts.
 * Fault injection: slots filled with NaN bytes before every copy, copies
   delayed on the copy stream, layers delayed on the compute stream: the
@@ -144,6 +146,56 @@ def test_dpo_llama8b_layer_shape_streamed_equals_resident(torch):
         m.close()
         torch.cuda.empty_cache()
     _same(runs["resident"], runs["stream_host"], "8B DPO")
+
+
+@pytest.mark.parametrize("shape", ["tiny", "llama8b-layer"])
+def test_dpo_sequence_groups(torch, shape):
+    """layer_tokens = seq_len: each layer runs the chosen and then the
+    rejected sequence on its record (fused reference pass).  Resident ==
+    host-streamed bitwise over two steps, the record copies per step are
+    those of the ungrouped step, and (tiny) one step against the oracle:
+    losses and log-probs within 2e-2, adapter gradients within 5e-2."""
+    w = dict(TINY, n_layers=5) if shape == "tiny" else LLAMA8B_2L
+    S = w["seq_len"]
+    if shape == "tiny":
+        ch, rj, P = _pair(w)
+        beta = 0.1
+    else:
+        P, beta = synth.dpo_prompt_len(w), synth.DPO_PAIR["beta"]
+        ch, rj = synth.dpo_pair(w)
+    tok, tgt = _dev(torch, np.stack([ch, rj]), w["vocab"])
+    steps = 2 if shape == "tiny" else 1
+    runs, loads = {}, {}
+    for mode in ("resident", "stream_host"):
+        say(f"[dpo groups {shape}] {mode}")
+        m = gpu_model(w, mode, b_zero=False, max_tokens=2 * S, layer_tokens=S)
+        l0 = m.stats()[0]
+        runs[mode] = _dpo_steps(torch, m, w, tok, tgt, P, True, steps=steps, beta=beta)
+        loads[mode] = m.stats()[0] - l0
+        m.close()
+        torch.cuda.empty_cache()
+    _same(runs["resident"], runs["stream_host"], f"grouped DPO {shape}")
+    L_ = w["n_layers"]
+    assert loads["stream_host"] == (2 * L_ - 2) + (steps - 1) * (2 * L_ - 4), loads
+    if shape != "tiny":
+        return
+    say("[dpo groups tiny] vs oracle")
+    cfg, layers, lora, head = oracle_model(w, b_zero=False)
+    od = om.dpo_step(cfg, layers, lora, head, ch, rj, P, beta, LR)
+    m = gpu_model(w, "stream_host", b_zero=False, max_tokens=2 * S, layer_tokens=S)
+    out = m.dpo_step(tok, tgt, S, P, beta, LR)
+    m.sync()
+    o = out[:6].cpu().numpy().astype(np.float64)
+    assert abs(o[0] - od["loss"]) <= 2e-2 * abs(od["loss"]), (o[0], od["loss"])
+    assert_close(m.logp[:2 * S].cpu().numpy(), od["logp_policy"], 2e-2, "policy logp")
+    assert_close(m.logp_ref[:2 * S].cpu().numpy(), od["logp_ref"], 2e-2, "reference logp")
+    for layer in range(L_):
+        for p in ("q", "v"):
+            _, _, dA, dB = m.get_lora(layer, p)
+            odA, odB = od["grads"][layer][p]
+            assert_close(dA, odA, 5e-2, f"grouped dA L{layer} {p}")
+            assert_close(dB, odB, 5e-2, f"grouped dB L{layer} {p}")
+    m.close()
 
 
 @pytest.mark.parametrize("n_slots", [3, 4])
