@@ -343,7 +343,8 @@ def test_peak_memory_accounting(torch):
     (L - 2) records between resident and streamed runs (L - 3 with three
     slots), and so do the peaks; a DPO step's peak is the same account at
     2 x 512 tokens (the reference model is the same streamed base: no second
-    copy of the weights)."""
+    copy of the weights), also with one sequence per layer group, whose
+    workspace lies between the SFT and the one-batch DPO workspaces."""
     w = dict(synth.WORKLOADS["llama3.1-8b-shaped"], n_layers=4, vocab=1024)
     S = w["seq_len"]
     L_ = w["n_layers"]
@@ -371,6 +372,15 @@ def test_peak_memory_accounting(torch):
                                       lambda m: m.dpo_step(dtok, dtgt, S, P, 0.1, LR))
     assert peak == held, (peak, held)
     assert 0 <= held - (_r512(wd) + _trainer_bytes(w, 2 * S, L_)) < SEG_TAIL, (held, wd)
+    # one sequence per layer group: the same account with the smaller
+    # workspace, which the step does not exceed either
+    say("[memory] streamed DPO, one sequence per layer group")
+    held_g, peak_g, wg, _ = _peak_of_step(torch, w, "stream_host", 2 * S,
+                                          lambda m: m.dpo_step(dtok, dtgt, S, P, 0.1, LR),
+                                          layer_tokens=S)
+    assert peak_g == held_g, (peak_g, held_g)
+    assert 0 <= held_g - (_r512(wg) + _trainer_bytes(w, 2 * S, L_)) < SEG_TAIL, (held_g, wg)
+    assert ws < wg < wd and held_g < held, (ws, wg, wd, held_g, held)
 
 
 def test_capped_memory_run_equals_resident(torch):
