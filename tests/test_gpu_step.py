@@ -788,3 +788,45 @@ def test_dpo_qwen3b_layer_shape_vs_oracle_and_resident(torch):
         for p in ("q", "v"):
             for u, v in zip(g[layer][p], r[3][layer][p]):
                 assert np.array_equal(_bits(np.asarray(u)), _bits(np.asarray(v)))
+
+
+def test_sft_ragged_sequence_groups(torch):
+    """Three sequences with layer_tokens = 2 x seq_len: each layer runs a
+    group of two sequences, then a group of one, on its record.  Every
+    projection adapted (GQA).  Resident == host-streamed bitwise (loss,
+    log-probs, A, B, dA, dB), one step against the oracle (loss and log-probs
+    within 2e-2, adapter gradients within 5e-2), and the record copies are
+    those of the ungrouped step."""
+    w = dict(SMALL256, n_seq=3, seq_len=64)
+    S, n = w["seq_len"], w["n_seq"]
+    tokens = synth.sft_tokens(w)
+    runs, loads = {}, {}
+    for mode in ("resident", "stream_host"):
+        say(f"[sft groups] {mode}")
+        m = gpu_model(w, mode, b_zero=False, lora_targets=ALL7, layer_tokens=2 * S)
+        l0 = m.stats()[0]
+        loss, logp = _run_sft(torch, m, tokens)
+        loads[mode] = m.stats()[0] - l0
+        runs[mode] = (loss, logp, _grads(m, w, ALL7))
+        m.close()
+    a, b = runs["resident"], runs["stream_host"]
+    assert np.float32(a[0]).view(np.uint32) == np.float32(b[0]).view(np.uint32)
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    for la, lb in zip(a[2], b[2]):
+        for p in ALL7:
+            for x, y in zip(la[p], lb[p]):
+                assert np.array_equal(np.asarray(x, np.float32).view(np.uint32),
+                                      np.asarray(y, np.float32).view(np.uint32)), p
+    assert loads["stream_host"] == 2 * w["n_layers"] - 2, loads
+    say("[sft groups] oracle")
+    cfg, layers, lora, head = oracle_model(w, b_zero=False, lora_targets=ALL7)
+    o = om.sft_step(cfg, layers, lora, head, tokens, LR)
+    loss, logp, g = b
+    assert abs(loss - o["loss"]) <= 2e-2 * abs(o["loss"]), (loss, o["loss"])
+    assert_close(logp, o["logp"], 2e-2, "logp")
+    for layer in range(w["n_layers"]):
+        for p in ALL7:
+            _, _, dA, dB = g[layer][p]
+            odA, odB = o["grads"][layer][p]
+            assert_close(dA, odA, 5e-2, f"dA L{layer} {p}")
+            assert_close(dB, odB, 5e-2, f"dB L{layer} {p}")
