@@ -489,7 +489,6 @@ def step_flops(w, T, n_seq):
 
 def environment(torch, w, rec_bytes):
     import platform
-    import subprocess
     props = torch.cuda.get_device_properties(0)
     env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
            "gpu": torch.cuda.get_device_name(0), "gpu_arch": getattr(props, "gcnArchName", None),
@@ -497,11 +496,15 @@ def environment(torch, w, rec_bytes):
            "seed": 0, "pinned_store_bytes": int(rec_bytes) * w["n_layers"],
            "python": platform.python_version(), "host_threads": os.cpu_count(),
            "elapsed_s": round(time.perf_counter() - _T_START, 1)}
+    # the installed HIP headers' version (read from the header rather than by
+    # running hipcc: a child process of this one would start a second GPU
+    # runtime under a profiler's preloaded library)
     try:
-        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
-                             timeout=30).stdout
-        env["hipcc"] = next((l.strip() for l in out.splitlines() if "HIP version" in l), None)
-    except (OSError, subprocess.SubprocessError):
+        import re
+        with open("/opt/rocm/include/hip/hip_version.h") as f:
+            d = dict(re.findall(r"#define HIP_VERSION_(MAJOR|MINOR|PATCH|GITHASH)\s+\"?(\w+)", f.read()))
+        env["hipcc"] = f"HIP version: {d['MAJOR']}.{d['MINOR']}.{d['PATCH']}-{d['GITHASH']}"
+    except (OSError, KeyError):
         pass
     try:
         with open("/opt/rocm/.info/version") as f:
